@@ -1,0 +1,253 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics
+fix, each independent of the oracle's own code.
+
+Every pin is a function pin_*(orc) that raises AssertionError on a mismatch.
+test_oracle_pins.py runs them on the real oracle; test_oracle_mutants.py runs
+them on copies of the oracle with a planted mistake and requires that some pin
+fails for every planted mistake.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import os
+
+import numpy as np
+
+from ref_conv import conv_forward, dilate_flip_correlate
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand(rng, shape):
+    return rng.standard_normal(size=shape).astype(np.float32)
+
+
+def _forward(orc, x, w, bias=None, add=None, *, groups=1, stride, pad, out_pad, dilation):
+    nd = x.ndim - 2
+    return orc.forward(ndim=nd, N=x.shape[0], C_in=x.shape[1], C_out=w.shape[1] * groups,
+                       groups=groups, in_size=x.shape[2:], K=w.shape[2:], stride=stride, pad=pad,
+                       out_pad=out_pad, dilation=dilation, x=x, w=w, bias=bias, add=add)
+
+
+# Tiny random shapes covering 1D/2D/3D, groups, stride, padding (incl. p > d(K-1)),
+# output padding (incl. op >= s) and dilation.
+def tiny_cases():
+    cases = [
+        # ndim, N, Cin, Cout, G, in, K, s, p, op, d
+        (1, 2, 3, 4, 1, (7,), (3,), (2,), (1,), (0,), (2,)),
+        (1, 1, 4, 6, 2, (5,), (4,), (3,), (2,), (1,), (1,)),
+        (1, 2, 2, 2, 1, (6,), (2,), (1,), (0,), (0,), (3,)),
+        (1, 1, 2, 3, 1, (4,), (3,), (2,), (5,), (3,), (1,)),   # p > d(K-1), op >= s
+        (1, 1, 6, 3, 3, (9,), (5,), (4,), (3,), (2,), (2,)),
+        (2, 1, 2, 4, 2, (3, 4), (2, 3), (2, 1), (1, 0), (1, 0), (1, 2)),
+        (3, 1, 2, 2, 1, (3, 2, 4), (3, 2, 3), (2, 2, 1), (1, 0, 1), (1, 1, 0), (1, 2, 1)),
+        (3, 2, 4, 4, 2, (2, 3, 3), (3, 5, 3), (2, 1, 2), (1, 2, 1), (1, 0, 1), (1, 1, 1)),
+        (3, 1, 3, 6, 3, (2, 2, 3), (2, 2, 4), (2, 2, 2), (1, 1, 1), (0, 0, 0), (1, 1, 1)),
+    ]
+    return cases
+
+
+def _case_arrays(case, seed):
+    nd, N, Cin, Cout, G, ins, K, s, p, op, d = case
+    rng = np.random.default_rng(seed)
+    x = _rand(rng, (N, Cin) + ins)
+    w = _rand(rng, (Cin, Cout // G) + K)
+    b = _rand(rng, (Cout,))
+    return x, w, b
+
+
+# ---------------------------------------------------------------------------
+def pin_closed_form_pages(orc):
+    """E0: output sizes the pages print."""
+    for e in _load("closed_form_and_tap_counts.json")["output_sizes"]:
+        got = orc.output_size(len(e["in_size"]), e["in_size"], e["K"], e["stride"], e["pad"],
+                              e["out_pad"], e["dilation"])
+        assert list(got) == e["out_size"], (e["citation"], got)
+
+
+def pin_worked_examples(orc):
+    """E1-E4: symbolic outputs of the pages' worked examples."""
+    rng = np.random.default_rng(11)
+    for e in _load("worked_examples.json")["examples"]:
+        vals = {name: np.float32(rng.standard_normal()) for name in e["x"] + e["w"]}
+        x = np.array([[[vals[n] for n in e["x"]]]], dtype=np.float32)
+        w = np.array([[[vals[n] for n in e["w"]]]], dtype=np.float32)
+        y = _forward(orc, x, w, stride=e["stride"], pad=e["pad"], out_pad=e["out_pad"],
+                     dilation=e["dilation"])
+        assert list(y.shape[2:]) == e["out_size"], e["id"]
+        want = [sum(float(vals[a]) * float(vals[b]) for a, b in terms) for terms in e["y"]]
+        np.testing.assert_allclose(y[0, 0], want, rtol=1e-12, atol=1e-12, err_msg=e["id"])
+        # an empty term list is an exact zero
+        for o, terms in enumerate(e["y"]):
+            if not terms:
+                assert y[0, 0, o] == 0.0, (e["id"], o)
+
+
+def pin_numpy_convolve(orc):
+    """E5: one channel, stride 1, no padding, no dilation is the full linear
+    convolution ("Kimi-K2.6 l1_p72" transcript: stride 1 and padding 0 is a
+    full convolution).  Stride s, dilation d, padding 0: full convolution of
+    the zero-inserted input with the zero-inserted kernel; output padding
+    appends zeros."""
+    rng = np.random.default_rng(5)
+    for L, K in [(1, 1), (5, 3), (8, 4), (3, 6)]:
+        x = _rand(rng, (1, 1, L))
+        w = _rand(rng, (1, 1, K))
+        y = _forward(orc, x, w, stride=[1], pad=[0], out_pad=[0], dilation=[1])
+        np.testing.assert_allclose(y[0, 0], np.convolve(x[0, 0].astype(np.float64),
+                                                        w[0, 0].astype(np.float64), "full"),
+                                   rtol=1e-12, atol=1e-12)
+    for L, K, s, d, op in [(5, 3, 2, 1, 0), (4, 3, 3, 2, 1), (6, 2, 2, 3, 2)]:
+        x = _rand(rng, (1, 1, L))
+        w = _rand(rng, (1, 1, K))
+        xd = np.zeros((L - 1) * s + 1)
+        xd[::s] = x[0, 0]
+        wd = np.zeros((K - 1) * d + 1)
+        wd[::d] = w[0, 0]
+        want = np.concatenate([np.convolve(xd, wd, "full"), np.zeros(op)])
+        y = _forward(orc, x, w, stride=[s], pad=[0], out_pad=[op], dilation=[d])
+        np.testing.assert_allclose(y[0, 0], want, rtol=1e-12, atol=1e-12)
+
+
+def pin_odd_only(orc):
+    """I1: stride 2, padding 1, dilation 2, kernel 3: even outputs equal the
+    bias exactly; odd o = 2m-1 gets sum_k W[:, :, k]^T x[:, m-k] over the k with
+    0 <= m-k < L_in ("Kimi-K2.6 l1_p79" transcript, the odd-position analysis
+    and the boundary count)."""
+    rng = np.random.default_rng(7)
+    N, Cin, Cout, L = 2, 4, 6, 64
+    x = _rand(rng, (N, Cin, L))
+    w = _rand(rng, (Cin, Cout, 3))
+    b = _rand(rng, (Cout,))
+    y = _forward(orc, x, w, b, stride=[2], pad=[1], out_pad=[0], dilation=[2])
+    assert y.shape == (N, Cout, 129)
+    np.testing.assert_array_equal(y[:, :, 0::2], np.broadcast_to(b.astype(np.float64)[None, :, None],
+                                                                 y[:, :, 0::2].shape))
+    for m in range(1, L + 1):
+        want = b.astype(np.float64)[None, :].repeat(N, 0)
+        for k in range(3):
+            if 0 <= m - k < L:
+                want = want + x[:, :, m - k].astype(np.float64) @ w[:, :, k].astype(np.float64)
+        np.testing.assert_allclose(y[:, :, 2 * m - 1], want, rtol=1e-12, atol=1e-12)
+
+
+def pin_tap_counts(orc):
+    """I2: the per-position contribution counts the pages tabulate, both from
+    the pair-count routine and from the forward itself (all-ones input and
+    weight give, per output, the product of the per-axis counts)."""
+    for e in _load("closed_form_and_tap_counts.json")["tap_counts"]:
+        c = orc.axis_pair_counts(e["L_in"], e["K"], e["s"], e["p"], e["op"], e["d"])
+        assert [int(c[o]) for o in e["positions"]] == e["counts"], e["citation"]
+    # forward on ones: the page's 3D axes at reduced input size 4x5x6
+    L, K, s, p, op = (4, 5, 6), (3, 5, 7), (2, 2, 2), (1, 2, 3), (1, 1, 1)
+    x = np.ones((1, 1) + L, dtype=np.float32)
+    w = np.ones((1, 1) + K, dtype=np.float32)
+    y = _forward(orc, x, w, stride=s, pad=p, out_pad=op, dilation=(1, 1, 1))
+    cnt = [orc.axis_pair_counts(L[a], K[a], s[a], p[a], op[a], 1) for a in range(3)]
+    want = cnt[0][:, None, None] * cnt[1][None, :, None] * cnt[2][None, None, :]
+    np.testing.assert_array_equal(y[0, 0], want.astype(np.float64))
+    # first width counts of the page's table survive the smaller input
+    assert list(cnt[2][:8]) == [2, 3, 3, 4, 3, 4, 3, 4]
+
+
+def pin_adjoint(orc):
+    """I4: <convT(x), v> = <x, conv(v)> with bias 0, conv written separately
+    in gather form ("Kimi-K2.6 l1_p79" transcript, the adjoint derivation)."""
+    for ci, case in enumerate(tiny_cases()):
+        nd, N, Cin, Cout, G, ins, K, s, p, op, d = case
+        x, w, _ = _case_arrays(case, 100 + ci)
+        y = _forward(orc, x, w, groups=G, stride=s, pad=p, out_pad=op, dilation=d)
+        v = np.random.default_rng(200 + ci).standard_normal(size=y.shape)
+        lhs = float(np.sum(y * v))
+        rhs = float(np.sum(x.astype(np.float64) *
+                           conv_forward(v, w, groups=G, in_size=ins, stride=s, pad=p, dilation=d)))
+        assert abs(lhs - rhs) <= 1e-9 * (1 + abs(lhs)), (case, lhs, rhs)
+
+
+def pin_dilate_flip_correlate(orc):
+    """I5: a second derivation (zero-insert, pad, correlate with the flipped,
+    channel-swapped weight) gives the same tensor, bias included."""
+    for ci, case in enumerate(tiny_cases()):
+        nd, N, Cin, Cout, G, ins, K, s, p, op, d = case
+        x, w, b = _case_arrays(case, 300 + ci)
+        y = _forward(orc, x, w, b, groups=G, stride=s, pad=p, out_pad=op, dilation=d)
+        want = dilate_flip_correlate(x, w, b, groups=G, stride=s, pad=p, out_pad=op, dilation=d)
+        assert y.shape == want.shape, case
+        np.testing.assert_allclose(y, want, rtol=1e-11, atol=1e-11, err_msg=str(case))
+
+
+def pin_group_decomposition(orc):
+    """I6: groups = G is G independent single-group problems on channel slices
+    ("Kimi-K2.6 l1_p72" transcript, the per-group channel mapping)."""
+    for ci, case in enumerate(tiny_cases()):
+        nd, N, Cin, Cout, G, ins, K, s, p, op, d = case
+        if G == 1:
+            continue
+        x, w, b = _case_arrays(case, 400 + ci)
+        y = _forward(orc, x, w, b, groups=G, stride=s, pad=p, out_pad=op, dilation=d)
+        Cig, Cog = Cin // G, Cout // G
+        for g in range(G):
+            xs = np.ascontiguousarray(x[:, g * Cig:(g + 1) * Cig])
+            ws = np.ascontiguousarray(w[g * Cig:(g + 1) * Cig])
+            bs = np.ascontiguousarray(b[g * Cog:(g + 1) * Cog])
+            yg = _forward(orc, xs, ws, bs, groups=1, stride=s, pad=p, out_pad=op, dilation=d)
+            np.testing.assert_allclose(y[:, g * Cog:(g + 1) * Cog], yg, rtol=1e-12, atol=1e-12)
+
+
+def pin_epilogue_values(orc):
+    """I7: t*hardswish(t) = t^2*clamp(t+3,0,6)/6 ("Kimi-K2.6 l2_p26"
+    transcript, its statement of hardswish) at values with closed forms."""
+    t = np.array([-4.0, -3.0, -1.0, 0.0, 1.0, 3.0, 6.0, 10.0, -2.5])
+    want = np.array([0.0, 0.0, 1.0 / 3.0, 0.0, 2.0 / 3.0, 9.0, 36.0, 100.0, 6.25 * 0.5 / 6.0])
+    np.testing.assert_allclose(orc.times_hardswish(t), want, rtol=1e-15, atol=1e-15)
+
+
+def pin_fused_forward(orc):
+    """The fused forward equals the plain forward plus add_input, then the
+    epilogue; with add = 0 and t in the linear region it is t^2*(t+3)/6."""
+    for ci, case in enumerate(tiny_cases()[:6]):
+        nd, N, Cin, Cout, G, ins, K, s, p, op, d = case
+        x, w, b = _case_arrays(case, 500 + ci)
+        y0 = _forward(orc, x, w, b, groups=G, stride=s, pad=p, out_pad=op, dilation=d)
+        add = np.random.default_rng(600 + ci).standard_normal(size=y0.shape).astype(np.float32)
+        y1 = _forward(orc, x, w, b, add, groups=G, stride=s, pad=p, out_pad=op, dilation=d)
+        t = y0 + add.astype(np.float64)
+        np.testing.assert_allclose(y1, orc.times_hardswish(t), rtol=1e-12, atol=1e-12)
+    # second derivation in the region -3 < t < 3 where clamp is the identity
+    case = tiny_cases()[0]
+    nd, N, Cin, Cout, G, ins, K, s, p, op, d = case
+    x, w, b = _case_arrays(case, 700)
+    x *= np.float32(0.1)
+    t = dilate_flip_correlate(x, w, b, groups=G, stride=s, pad=p, out_pad=op, dilation=d)
+    zeros = np.zeros(t.shape, dtype=np.float32)
+    y1 = _forward(orc, x, w, b, zeros, groups=G, stride=s, pad=p, out_pad=op, dilation=d)
+    assert np.all(np.abs(t) < 3)
+    np.testing.assert_allclose(y1, t * t * (t + 3.0) / 6.0, rtol=1e-11, atol=1e-12)
+
+
+def pin_points_match_forward(orc):
+    """The one-by-one evaluation (used at full sizes) equals the full forward,
+    fused and not, on every element of the tiny cases."""
+    for ci, case in enumerate(tiny_cases()):
+        nd, N, Cin, Cout, G, ins, K, s, p, op, d = case
+        x, w, b = _case_arrays(case, 800 + ci)
+        kw = dict(ndim=nd, N=N, C_in=Cin, C_out=Cout, groups=G, in_size=ins, K=K, stride=s,
+                  pad=p, out_pad=op, dilation=d, x=x, w=w, bias=b)
+        y = orc.forward(**kw)
+        idx = np.arange(y.size, dtype=np.int64)
+        np.testing.assert_allclose(orc.points(idx, **kw), y.ravel(), rtol=1e-12, atol=1e-12)
+        add = np.random.default_rng(900 + ci).standard_normal(size=y.shape).astype(np.float32)
+        yf = orc.forward(add=add, **kw)
+        np.testing.assert_allclose(orc.points(idx, add=add, **kw), yf.ravel(), rtol=1e-12,
+                                   atol=1e-12)
+
+
+ALL_PINS = [pin_closed_form_pages, pin_worked_examples, pin_numpy_convolve, pin_odd_only,
+            pin_tap_counts, pin_adjoint, pin_dilate_flip_correlate, pin_group_decomposition,
+            pin_epilogue_values, pin_fused_forward, pin_points_match_forward]

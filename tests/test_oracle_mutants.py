@@ -1,0 +1,59 @@
+"""Planted mistakes in the oracle must each fail at least one pin (no GPU).
+
+Each mutant is a copy of oracle/convt_oracle.c with one textual change (a
+plausible mistake: flipped kernel, wrong padding sign, transposed weight
+operand, dropped bias, ...), compiled into a temporary directory with gcc.
+The real oracle is never modified.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+MUTATIONS = {
+    "flip_kernel": ("(double)wc[co_l * k_sp + (kd * KH + kh) * KW + kw]",
+                    "(double)wc[co_l * k_sp + ((KD - 1 - kd) * KH + (KH - 1 - kh)) * KW + (KW - 1 - kw)]"),
+    "pad_sign_w": ("iw * P->s[2] - P->p[2] + kw * P->d[2]", "iw * P->s[2] + P->p[2] + kw * P->d[2]"),
+    "stride_dilation_swapped": ("iw * P->s[2] - P->p[2] + kw * P->d[2]",
+                                "iw * P->d[2] - P->p[2] + kw * P->s[2]"),
+    "dilation_dropped": ("iw * P->s[2] - P->p[2] + kw * P->d[2]", "iw * P->s[2] - P->p[2] + kw"),
+    "depth_axis_pad_dropped": ("id * P->s[0] - P->p[0] + kd * P->d[0]", "id * P->s[0] + kd * P->d[0]"),
+    "closed_form_half_pad": ("return (L_in - 1) * s - 2 * p + d * (K - 1) + op + 1;",
+                             "return (L_in - 1) * s - p + d * (K - 1) + op + 1;"),
+    "closed_form_no_outpad": ("return (L_in - 1) * s - 2 * p + d * (K - 1) + op + 1;",
+                              "return (L_in - 1) * s - 2 * p + d * (K - 1) + 1;"),
+    "bias_dropped": ("double b = J->bias ? (double)J->bias[g * Cog + co_l] : 0.0;", "double b = 0.0;"),
+    "bias_wrong_channel": ("double b = J->bias ? (double)J->bias[g * Cog + co_l] : 0.0;",
+                           "double b = J->bias ? (double)J->bias[co_l] : 0.0;"),
+    "group_input_channel": ("const int64_t ci = g * Cig + ci_l;\n        const float *xc = J->x",
+                            "const int64_t ci = ci_l;\n        const float *xc = J->x"),
+    "weight_transposed": ("const double wv = (double)wc[co_l * k_sp + (kd * KH + kh) * KW + kw];",
+                          "const double wv = (double)J->w[((g * Cog + co_l) * Cig + ci_l) * k_sp"
+                          " + (kd * KH + kh) * KW + kw];"),
+    "epilogue_plain_hardswish": ("return t * (t * r / 6.0);", "return t * r / 6.0;"),
+    "epilogue_no_upper_clamp": ("if (r > 6.0) r = 6.0;", ""),
+    "epilogue_add_dropped": ("slab[e] = times_hardswish(slab[e] + (double)ad[e]);",
+                             "slab[e] = times_hardswish(slab[e]);"),
+    "points_pad_sign": ("if (i * s - p + k * d == o)", "if (i * s + p + k * d == o)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutant_fails_a_pin(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(oracle.SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    mpath = os.path.join(tmp_path, "mutant.c")
+    with open(mpath, "w") as f:
+        f.write(src.replace(old, new))
+    lib = oracle.build(mpath, os.path.join(tmp_path, "libmutant.so"), extra_flags=["-w"])
+    orc = oracle.Oracle(lib)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except Exception:  # any pin that does not pass counts
+            failed.append(pin.__name__)
+    assert failed, f"planted mistake {name} passed every pin"
