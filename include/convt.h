@@ -1,0 +1,138 @@
+/*
+ * convt.h -- transposed-convolution forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (the scatter definition the source pages settle on):
+ *   every input element x[n, ci, i] (i a position per spatial axis) times every
+ *   kernel tap w[ci, co_l, k] of its group is added to
+ *   y[n, g*(C_out/G) + co_l, o] at o = i*s - p + k*d on each axis; writes
+ *   outside [0, L_out) are dropped; bias[co] is added once to every output
+ *   element; input channel ci belongs to group g = ci / (C_in/G).
+ *   Sources: "Kimi-K2.6 l1_p79" transcript (ConvTranspose1d, dilation 2),
+ *   scatter-then-crop derivation and its two-input worked example;
+ *   "Kimi-K2.6 l1_p72" transcript (ConvTranspose3d, groups 4), the per-group
+ *   reference loop with bias.
+ *
+ * Output size per axis (closed form, all three pages):
+ *   L_out = (L_in - 1)*s - 2p + d*(K - 1) + out_pad + 1
+ *
+ * Layouts (all float32, contiguous, row-major, caller-owned DEVICE memory):
+ *   x         (N, C_in, L_in...)             NCL / NCHW / NCDHW
+ *   w         (C_in, C_out/groups, K...)     used as stored (no flip)
+ *   bias      (C_out)                        may be NULL (no bias)
+ *   add_input (N, C_out, L_out...)           same shape as y
+ *   y         (N, C_out, L_out...)           every element is written
+ * No alignment is required of any pointer beyond that of float.
+ *
+ * Ownership and threading: a plan holds host metadata only; it allocates no
+ * device memory, and no call allocates device memory.  Calls are asynchronous
+ * on the given HIP stream (hipStream_t passed as void*; NULL = null stream)
+ * and never synchronise.  A plan is immutable after creation apart from
+ * convt_plan_set_path; forward calls on one plan may run concurrently on any
+ * streams.
+ *
+ * Aliasing: x and w must not overlap y.  add_input == y (in place) is allowed:
+ * each element is read and then written by the same thread.
+ *
+ * Errors: status codes only; nothing is thrown across this boundary.
+ */
+#ifndef CONVT_H
+#define CONVT_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define CONVT_API __attribute__((visibility("default")))
+#else
+#define CONVT_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CONVT_OK = 0,
+    CONVT_ERR_INVALID_ARG = 1, /* NULL pointer, or a shape/parameter the closed form rejects */
+    CONVT_ERR_UNSUPPORTED = 2, /* valid, but beyond this library's limits or the forced path */
+    CONVT_ERR_HIP = 3,         /* the HIP runtime reported an error (launch or device) */
+    CONVT_ERR_NOMEM = 4        /* host allocation of the plan failed */
+} convt_status;
+
+typedef enum {
+    CONVT_PATH_AUTO = 0,     /* let the planner choose (the default) */
+    CONVT_PATH_GENERIC = 1,  /* output-stationary phase-table gather, any shape */
+    CONVT_PATH_STREAM1D = 2, /* 1D streaming kernel, MFMA channel contraction */
+    CONVT_PATH_IGEMM3D = 3   /* per-phase implicit GEMM on MFMA for 3D */
+} convt_path;
+
+typedef struct convt_plan convt_plan; /* opaque */
+
+/*
+ * Create a plan.  ndim is 1, 2 or 3; in_size, K, stride, pad, out_pad and
+ * dilation are arrays of ndim entries (outermost spatial axis first).
+ * Requirements (else CONVT_ERR_INVALID_ARG): N >= 1, C_in >= 1, C_out >= 1,
+ * groups >= 1 dividing both C_in and C_out; per axis L_in >= 1, K >= 1,
+ * stride >= 1, dilation >= 1, pad >= 0, out_pad >= 0, and L_out >= 1 by the
+ * closed form.  Any out_pad >= 0 is accepted (the pages state no upper
+ * bound).  Limits (else CONVT_ERR_UNSUPPORTED): K <= 32 and stride <= 32 per
+ * axis, every tensor below 2^31 elements per batch sample and below 2^40
+ * elements in total.  Host-only: makes no HIP call.  On success *plan owns a
+ * heap object released by convt_plan_destroy.
+ */
+CONVT_API convt_status convt_plan_create(convt_plan **plan, int ndim, int64_t N, int64_t C_in,
+                               int64_t C_out, int64_t groups, const int64_t *in_size,
+                               const int64_t *K, const int64_t *stride, const int64_t *pad,
+                               const int64_t *out_pad, const int64_t *dilation);
+
+/* Write the ndim output sizes (closed form) to out_size.  Host-only. */
+CONVT_API convt_status convt_plan_output_size(const convt_plan *plan, int64_t *out_size);
+
+/*
+ * y = conv_transpose(x, w) + bias.  bias may be NULL.  All pointers device
+ * memory, layouts above.  Returns CONVT_ERR_INVALID_ARG for NULL plan, x, w
+ * or y; CONVT_ERR_HIP if the launch fails.
+ */
+CONVT_API convt_status convt_forward(const convt_plan *plan, const float *x, const float *w,
+                           const float *bias, float *y, void *stream);
+
+/*
+ * Fused epilogue ("Kimi-K2.6 l2_p26" transcript, ConvTranspose3d + add +
+ * HardSwish, its forward and its statement of hardswish):
+ *   t = conv_transpose(x, w) + bias + add_input
+ *   y = t * hardswish(t) = t * t * min(max(t + 3, 0), 6) / 6
+ * computed in registers, one store per element.  bias may be NULL; add_input
+ * may equal y.  Errors as convt_forward (add_input NULL is INVALID_ARG).
+ */
+CONVT_API convt_status convt_forward_add_hswish(const convt_plan *plan, const float *x, const float *w,
+                                      const float *bias, const float *add_input, float *y,
+                                      void *stream);
+
+/* Release a plan.  NULL is a no-op. */
+CONVT_API void convt_plan_destroy(convt_plan *plan);
+
+/* Static, NUL-terminated description of a status code. */
+CONVT_API const char *convt_status_string(convt_status status);
+
+/*
+ * Force a kernel path (CONVT_PATH_AUTO restores the planner's choice).
+ * Returns CONVT_ERR_UNSUPPORTED, leaving the plan unchanged, if that path
+ * cannot run this plan.  Host-only; not safe concurrently with forward calls
+ * on the same plan.
+ */
+CONVT_API convt_status convt_plan_set_path(convt_plan *plan, convt_path path);
+
+/* The path forward calls will take (never CONVT_PATH_AUTO). */
+CONVT_API convt_path convt_plan_get_path(const convt_plan *plan);
+
+/*
+ * Human-readable summary of the plan (shapes, phase tables, chosen path and
+ * launch shape) into buf (NUL-terminated, truncated to len).  Returns the
+ * length the full text needs, excluding the NUL.  Host-only.
+ */
+CONVT_API int64_t convt_plan_describe(const convt_plan *plan, char *buf, int64_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVT_H */

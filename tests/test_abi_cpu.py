@@ -1,0 +1,138 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and its host-only calls (plan creation, validation, output size,
+path forcing, description) behave as documented.  No compute call is made."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import transposed_convolution_forward_amd as T
+from transposed_convolution_forward_amd import synthetic as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convt.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"CONVT_API\s+[\w\s\*]*?\b(convt_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    declared = header_functions()
+    assert len(declared) >= 9
+    L = T.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert sorted(T.EXPORTS) == declared
+
+
+def _create(ndim=1, N=1, C_in=2, C_out=2, groups=1, in_size=(4,), K=(3,), s=(2,), p=(1,), op=(0,),
+            d=(1,)):
+    L = T.lib()
+    h = ctypes.c_void_p()
+    arr = lambda v: (ctypes.c_int64 * len(v))(*v)
+    st = L.convt_plan_create(ctypes.byref(h), ndim, N, C_in, C_out, groups, arr(in_size), arr(K),
+                             arr(s), arr(p), arr(op), arr(d))
+    if st == 0:
+        L.convt_plan_destroy(h)
+    return st
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), T.CONVT_OK),
+    (dict(ndim=0), T.CONVT_ERR_INVALID_ARG),
+    (dict(ndim=4, in_size=(2,) * 4, K=(1,) * 4, s=(1,) * 4, p=(0,) * 4, op=(0,) * 4, d=(1,) * 4),
+     T.CONVT_ERR_INVALID_ARG),
+    (dict(N=0), T.CONVT_ERR_INVALID_ARG),
+    (dict(C_in=0), T.CONVT_ERR_INVALID_ARG),
+    (dict(C_in=3, groups=2), T.CONVT_ERR_INVALID_ARG),
+    (dict(C_out=3, groups=2), T.CONVT_ERR_INVALID_ARG),
+    (dict(groups=0), T.CONVT_ERR_INVALID_ARG),
+    (dict(K=(0,)), T.CONVT_ERR_INVALID_ARG),
+    (dict(s=(0,)), T.CONVT_ERR_INVALID_ARG),
+    (dict(d=(0,)), T.CONVT_ERR_INVALID_ARG),
+    (dict(p=(-1,)), T.CONVT_ERR_INVALID_ARG),
+    (dict(op=(-1,)), T.CONVT_ERR_INVALID_ARG),
+    (dict(in_size=(0,)), T.CONVT_ERR_INVALID_ARG),
+    # L_out = (1-1)*1 - 2*2 + 1*(3-1) + 0 + 1 = -1
+    (dict(in_size=(1,), s=(1,), p=(2,)), T.CONVT_ERR_INVALID_ARG),
+    # L_out = 1 exactly is valid
+    (dict(in_size=(1,), K=(1,), s=(1,), p=(0,)), T.CONVT_OK),
+    (dict(op=(7,)), T.CONVT_OK),          # out_pad >= stride is accepted
+    (dict(p=(9,), in_size=(16,)), T.CONVT_OK),  # p > d(K-1): crops real taps
+    (dict(K=(33,)), T.CONVT_ERR_UNSUPPORTED),
+    (dict(s=(33,)), T.CONVT_ERR_UNSUPPORTED),
+    (dict(in_size=(1 << 31,)), T.CONVT_ERR_UNSUPPORTED),
+])
+def test_plan_create_validation(kw, status):
+    assert _create(**kw) == status
+
+
+def test_null_arguments():
+    L = T.lib()
+    arr = (ctypes.c_int64 * 1)(4)
+    assert L.convt_plan_create(None, 1, 1, 1, 1, 1, arr, arr, arr, arr, arr, arr) == T.CONVT_ERR_INVALID_ARG
+    h = ctypes.c_void_p()
+    assert L.convt_plan_create(ctypes.byref(h), 1, 1, 1, 1, 1, None, arr, arr, arr, arr, arr) == T.CONVT_ERR_INVALID_ARG
+    L.convt_plan_destroy(None)  # no-op
+    assert L.convt_plan_output_size(None, arr) == T.CONVT_ERR_INVALID_ARG
+    assert L.convt_forward(None, None, None, None, None, None) == T.CONVT_ERR_INVALID_ARG
+    assert L.convt_forward_add_hswish(None, None, None, None, None, None, None) == T.CONVT_ERR_INVALID_ARG
+    assert L.convt_plan_set_path(None, 0) == T.CONVT_ERR_INVALID_ARG
+    assert L.convt_plan_describe(None, None, 0) == -1
+
+
+def test_forward_rejects_null_tensors_without_launch():
+    p = T.Plan(1, 1, 2, 2, 1, (4,), (3,), (2,), (1,), (0,), (1,))
+    L = T.lib()
+    fake = ctypes.c_void_p(16)  # never dereferenced: the NULL check comes first
+    assert L.convt_forward(p.handle, None, fake, None, fake, None) == T.CONVT_ERR_INVALID_ARG
+    assert L.convt_forward(p.handle, fake, None, None, fake, None) == T.CONVT_ERR_INVALID_ARG
+    assert L.convt_forward(p.handle, fake, fake, None, None, None) == T.CONVT_ERR_INVALID_ARG
+    assert L.convt_forward_add_hswish(p.handle, fake, fake, None, None, fake, None) == T.CONVT_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for s in range(5):
+        assert T.convt_status_string(s)
+    assert T.convt_status_string(99) == "unknown status"
+
+
+def test_output_sizes_match_pages():
+    data = json.load(open(os.path.join(ROOT, "tests", "golden", "closed_form_and_tap_counts.json")))
+    for e in data["output_sizes"]:
+        nd = len(e["in_size"])
+        p = T.Plan(nd, 1, 1, 1, 1, e["in_size"], e["K"], e["stride"], e["pad"], e["out_pad"],
+                   e["dilation"])
+        assert list(p.out_size) == e["out_size"], e["citation"]
+
+
+def test_workload_plans_and_paths():
+    want = {S.TINY_1D.name: (129,), S.LONG_1D.name: (262145,), S.GROUPED_3D.name: (32, 32, 64),
+            S.FUSED_3D.name: (32, 32, 32), S.HEAVY_3D.name: (64, 64, 64)}
+    for wl in S.WORKLOADS:
+        p = T.plan_for(wl)
+        assert p.out_size == want[wl.name]
+        assert T.convt_plan_get_path(p) in ("generic", "stream1d", "igemm3d")
+        T.convt_plan_set_path(p, "generic")
+        assert T.convt_plan_get_path(p) == "generic"
+        T.convt_plan_set_path(p, "auto")
+        text = T.convt_plan_describe(p)
+        assert "path=" in text and "r0:" in text
+
+
+def test_phase_table_description():
+    # stride 2, padding 1, dilation 2, kernel 3: residue 0 takes every tap, residue 1 none
+    p = T.Plan(1, 1, 1, 1, 1, (8,), (3,), (2,), (1,), (0,), (2,))
+    text = T.convt_plan_describe(p)
+    assert "r0:{k0/c0,k1/c1,k2/c2} r1:{}" in text
+
+
+def test_set_path_rejects_unsupported():
+    p = T.Plan(1, 1, 2, 3, 1, (8,), (3,), (2,), (1,), (0,), (1,))
+    assert T.lib().convt_plan_set_path(p.handle, 7) == T.CONVT_ERR_INVALID_ARG
+    assert T.convt_plan_get_path(p) == "generic"
+    assert T.lib().convt_plan_set_path(p.handle, T.PATHS["igemm3d"]) == T.CONVT_ERR_UNSUPPORTED

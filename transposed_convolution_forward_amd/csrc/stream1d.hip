@@ -1,0 +1,12 @@
+// 1D streaming path (placeholder until the MFMA kernel lands).
+#include <hip/hip_runtime.h>
+
+#include "convt_internal.h"
+
+namespace convt {
+bool stream1d_supports(const convt_plan &) { return false; }
+int launch_stream1d(const convt_plan &, const float *, const float *, const float *,
+                    const float *, float *, void *) {
+    return (int)hipErrorInvalidValue;
+}
+} // namespace convt
