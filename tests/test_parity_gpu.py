@@ -29,6 +29,20 @@ REDUCED = [
     reduced(S.FUSED_3D, N=1, in_size=(5, 7, 9)),
     reduced(S.HEAVY_3D, N=1, in_size=(6, 5, 9)),
     reduced(S.HEAVY_3D, N=2, in_size=(4, 4, 16)),
+    # 1D shapes for each streaming-kernel variant: groups, fused, several
+    # non-empty phases, empty phases, output padding, ragged lengths
+    S.Workload("s1d_g2_k3s2d2", 1, 2, 64, 128, 2, (517,), (3,), (2,), (1,), (0,), (2,), True, True,
+               wid=3001),
+    S.Workload("s1d_k3s2d1", 1, 2, 32, 64, 1, (1000,), (3,), (2,), (1,), (1,), (1,), True, False,
+               wid=3002),
+    S.Workload("s1d_k4s2d1", 1, 1, 32, 32, 1, (777,), (4,), (2,), (1,), (0,), (1,), False, True,
+               wid=3003),
+    S.Workload("s1d_k3s3d2", 1, 2, 16, 16, 1, (300,), (3,), (3,), (2,), (1,), (2,), True, False,
+               wid=3004),
+    S.Workload("s1d_k5s4d2", 1, 1, 16, 32, 1, (257,), (5,), (4,), (3,), (2,), (2,), True, True,
+               wid=3005),
+    S.Workload("s1d_short", 1, 3, 32, 64, 1, (5,), (3,), (2,), (1,), (0,), (2,), True, False,
+               wid=3006),
 ]
 
 
@@ -142,3 +156,15 @@ def test_full_size_long1d_even_outputs_exactly_zero():
     y = run_gpu(wl, dev)
     assert (y[:, :, 0::2] == 0).all().item()
     assert (y[:, :, 1::2] != 0).float().mean().item() > 0.99
+
+
+@pytest.mark.parametrize("wl", [S.LONG_1D, S.GROUPED_3D, S.FUSED_3D], ids=lambda w: w.name)
+def test_full_size_every_element(wl):
+    """Full size, planner's path, every element against the oracle's full
+    forward (these three finish in seconds on a many-core host; the
+    channel-heavy 3D layer is checked by sampling only)."""
+    inp = make(wl)
+    y = run_gpu(wl, to_dev(inp), "auto").cpu().numpy()
+    ref = oracle.get().forward(**oracle_kwargs(wl, inp))
+    err = check_close(y, ref, f"{wl.name} full")
+    log(f"  {wl.name}: every element, max abs err {err:.3e}")
