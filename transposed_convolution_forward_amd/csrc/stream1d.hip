@@ -84,128 +84,173 @@ struct Stream1dParams {
 constexpr int kRowF4 = (kTileQ + 4) / 4;
 constexpr int kPitch = kRowF4 * 4;
 
+// Fetch of one x tile into registers, branch-free so that the loads stay in
+// flight across the contraction of the current tile: every float4 is loaded
+// from a position clamped into the row (needs L_in >= 4); the shift back and
+// the zeroing of positions outside [0, L_in) happen when the tile is written
+// to LDS.
 template <int CIG, int NT>
 __device__ __forceinline__ void tile_fetch(f4 (&r)[(CIG * kRowF4 + NT - 1) / NT], const float *xrow,
                                            int L_in, int q0, int tid) {
     constexpr int NF = CIG * kRowF4;
     constexpr int PER = (NF + NT - 1) / NT;
-    const bool interior = (q0 - 4 >= 0) && (q0 + kTileQ <= L_in);
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int f = tid + u * NT;
-        if (f < NF) {
-            const int row = f / kRowF4, c4 = f % kRowF4;
-            const float *src = xrow + (int64_t)row * L_in;
-            const int pos = q0 - 4 + 4 * c4;
-            if (interior) {
-                r[u] = load4u(src + pos);
-            } else {
-                f4 v;
-                v.x = (pos + 0 >= 0 && pos + 0 < L_in) ? src[pos + 0] : 0.0f;
-                v.y = (pos + 1 >= 0 && pos + 1 < L_in) ? src[pos + 1] : 0.0f;
-                v.z = (pos + 2 >= 0 && pos + 2 < L_in) ? src[pos + 2] : 0.0f;
-                v.w = (pos + 3 >= 0 && pos + 3 < L_in) ? src[pos + 3] : 0.0f;
-                r[u] = v;
-            }
-        }
+        const int f = min(tid + u * NT, NF - 1);
+        const int row = f / kRowF4, c4 = f % kRowF4;
+        const int pos = q0 - 4 + 4 * c4;
+        const int cp = min(max(pos, 0), L_in - 4);
+        r[u] = load4u(xrow + (int64_t)row * L_in + cp);
     }
+}
+
+__device__ __forceinline__ float pick4(const f4 &v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
 template <int CIG, int NT>
 __device__ __forceinline__ void tile_store_lds(float *lds, const f4 (&r)[(CIG * kRowF4 + NT - 1) / NT],
-                                               int tid) {
+                                               int L_in, int q0, int tid) {
     constexpr int NF = CIG * kRowF4;
     constexpr int PER = (NF + NT - 1) / NT;
+    if (q0 - 4 >= 0 && q0 + kTileQ <= L_in) { // whole tile inside the row (uniform)
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int f = tid + u * NT;
+            if (f < NF) {
+                const int row = f / kRowF4, c4 = f % kRowF4;
+                *reinterpret_cast<f4 *>(lds + row * kPitch + 4 * c4) = r[u];
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const int f = tid + u * NT;
         if (f < NF) {
             const int row = f / kRowF4, c4 = f % kRowF4;
-            *reinterpret_cast<f4 *>(lds + row * kPitch + 4 * c4) = r[u];
+            const int pos = q0 - 4 + 4 * c4;
+            const int sh = pos - min(max(pos, 0), L_in - 4); // in [-3, 3]
+            f4 v;
+            v.x = (pos + 0 >= 0 && pos + 0 < L_in) ? pick4(r[u], sh + 0) : 0.0f;
+            v.y = (pos + 1 >= 0 && pos + 1 < L_in) ? pick4(r[u], sh + 1) : 0.0f;
+            v.z = (pos + 2 >= 0 && pos + 2 < L_in) ? pick4(r[u], sh + 2) : 0.0f;
+            v.w = (pos + 3 >= 0 && pos + 3 < L_in) ? pick4(r[u], sh + 3) : 0.0f;
+            *reinterpret_cast<f4 *>(lds + row * kPitch + 4 * c4) = v;
         }
     }
 }
+
+// Output staging: each wave passes its 16 x 64S output block through LDS in
+// two halves of 8 rows (e in {2h, 2h+1}), so that every global store
+// instruction writes whole contiguous runs of rows (16S float4 per row).
+template <int S> constexpr int out_pitch() { return 64 * S + 4; }
+
+// Tuning knobs: minimum waves per SIMD the register allocation must allow,
+// and resident workgroups aimed for per CU when sizing the grid.
+#ifndef CONVT_S1D_WAVES_PER_EU
+#define CONVT_S1D_WAVES_PER_EU 3
+#endif
+#ifndef CONVT_S1D_BLOCKS_PER_CU
+#define CONVT_S1D_BLOCKS_PER_CU 6
+#endif
 
 // One workgroup = COG/16 waves; wave w owns output channels 16w .. 16w+15 of
 // the group and all 64 positions of the work item; the waves share the x tile
 // through LDS, double-buffered: the tile of the next work item is fetched
 // from HBM into registers while the current one is contracted.
 template <int CIG, int COG, int K, int S, int D, bool FUSED>
-__global__ __launch_bounds__(COG * 4) void k_stream1d(const Stream1dParams P,
+__global__ __launch_bounds__(COG * 4)
+__attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(const Stream1dParams P,
                                                       const float *__restrict__ x,
                                                       const float *__restrict__ w,
                                                       const float *__restrict__ bias,
                                                       const float *add, float *y) {
     using Ph = Phases<K, S, D>;
     constexpr int NCIG = CIG / 4;
+    constexpr int COT = COG / 16;
     constexpr int NT = COG * 4; // threads per workgroup
     constexpr int NP = Ph::count() > 0 ? Ph::count() : 1;
     constexpr int PER = (CIG * kRowF4 + NT - 1) / NT;
+    constexpr int PO = out_pitch<S>();
+    constexpr int RUN4 = 16 * S;        // float4 per output row of one work item
+    constexpr int ROUNDS = 8 * RUN4 / 64; // read-back rounds per half (= 2S)
     static_assert(CIG % 4 == 0 && COG % 16 == 0, "tile shape");
     static_assert(Ph::cmax() <= 4, "input shift beyond the 4-position halo");
+    static_assert((8 * RUN4) % 64 == 0, "read-back rounds");
 
     __shared__ __attribute__((aligned(16))) float lds[2][CIG * kPitch];
+    __shared__ __attribute__((aligned(16))) float stage[COT][8 * PO];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int ct = tid >> 6; // this wave's co-tile
     const int j = lane & 15;
     const int g4 = lane >> 4;
-    int64_t it = (int64_t)blockIdx.x * P.per_block;
-    const int64_t it_end = it + P.per_block < P.total ? it + P.per_block : P.total;
-    if (it >= it_end) return;
+    const int64_t it0 = (int64_t)blockIdx.x * P.per_block;
+    const int64_t it_end = it0 + P.per_block < P.total ? it0 + P.per_block : P.total;
+    if (it0 >= it_end) return;
+    const int n_items = (int)(it_end - it0);
 
-    auto item_n_g_q0 = [&](int64_t item, int &n, int &g, int &q0) {
-        const int st = (int)(item % P.n_st);
-        const int64_t ng = item / P.n_st;
-        g = (int)(ng % P.G);
-        n = (int)(ng / P.G);
-        q0 = (P.st_lo + st) * kTileQ;
-    };
-    auto xrow_of = [&](int n, int g) {
-        return x + ((int64_t)n * P.C_in + (int64_t)g * CIG) * P.L_in;
-    };
+    // (n, g, tile) of the first item; later items advance incrementally
+    int st = (int)(it0 % P.n_st);
+    int ng = (int)(it0 / P.n_st);
+    auto xrow_of = [&](int ng_) { return x + (int64_t)ng_ * CIG * P.L_in; }; // (n*G+g)*CIG = n*C_in + g*CIG
 
     f4 pre[PER];
-    {
-        int n, g, q0;
-        item_n_g_q0(it, n, g, q0);
-        tile_fetch<CIG, NT>(pre, xrow_of(n, g), P.L_in, q0, tid);
-        tile_store_lds<CIG, NT>(lds[0], pre, tid);
-    }
+    tile_fetch<CIG, NT>(pre, xrow_of(ng), P.L_in, (P.st_lo + st) * kTileQ, tid);
+    tile_store_lds<CIG, NT>(lds[0], pre, P.L_in, (P.st_lo + st) * kTileQ, tid);
     __syncthreads();
 
-    float wr[K][NCIG]; // A operands: W[g*CIG + 4*cig + g4][16*ct + j][k]
-    float br[4];       // bias of co = 16*ct + 4*g4 + e
-    int cur_g = -1;
+    float wr[K][NCIG];   // A operands: W[g*CIG + 4*cig + g4][16*ct + j][k]
+    float bo[2][ROUNDS]; // bias of the rows this lane stores in read-back
     int buf = 0;
+    float *stg = stage[ct];
 
-    for (; it < it_end; ++it) {
-        int n, g, q0;
-        item_n_g_q0(it, n, g, q0);
-        const bool has_next = it + 1 < it_end;
-        if (has_next) {
-            int n1, g1, q1;
-            item_n_g_q0(it + 1, n1, g1, q1);
-            tile_fetch<CIG, NT>(pre, xrow_of(n1, g1), P.L_in, q1, tid);
-        }
-        if (g != cur_g) {
-            cur_g = g;
+    // Runs of consecutive items of one group share the weights: load them once
+    // per run, outside the loop that carries the prefetch.
+    for (int ii = 0; ii < n_items;) {
+        const int g = ng % P.G;
+        const int run = P.G == 1 ? n_items - ii : min(n_items - ii, P.n_st - st);
 #pragma unroll
-            for (int k = 0; k < K; ++k)
+        for (int k = 0; k < K; ++k)
 #pragma unroll
-                for (int cig = 0; cig < NCIG; ++cig)
-                    wr[k][cig] = w[((int64_t)(g * CIG + 4 * cig + g4) * COG + 16 * ct + j) * K + k];
+            for (int cig = 0; cig < NCIG; ++cig)
+                wr[k][cig] = w[((int64_t)(g * CIG + 4 * cig + g4) * COG + 16 * ct + j) * K + k];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                br[e] = bias ? bias[g * COG + 16 * ct + 4 * g4 + e] : 0.0f;
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int m = 0; m < ROUNDS; ++m) {
+                const int sr = (64 * m + lane) / RUN4; // staging row 0..7
+                const int col = 4 * (sr >> 1) + 2 * h + (sr & 1);
+                bo[h][m] = bias ? bias[g * COG + 16 * ct + col] : 0.0f;
+            }
+        // Wait for these loads here, before the loop: an empty asm that reads
+        // and redefines the registers puts the wait in the preheader, so the
+        // loop body never waits on them (which, vmcnt being in order, would
+        // also wait on the prefetch).
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+#pragma unroll
+            for (int cig = 0; cig < NCIG; ++cig) asm volatile("" : "+v"(wr[k][cig]));
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int m = 0; m < ROUNDS; ++m) asm volatile("" : "+v"(bo[h][m]));
+
+    for (int rr = 0; rr < run; ++rr, ++ii) {
+        const int n = ng / P.G;
+        const int q0 = (P.st_lo + st) * kTileQ;
+        int st1 = st + 1, ng1 = ng;
+        if (st1 == P.n_st) { st1 = 0; ++ng1; }
+        const bool has_next = ii + 1 < n_items;
+        if (has_next) tile_fetch<CIG, NT>(pre, xrow_of(ng1), P.L_in, (P.st_lo + st1) * kTileQ, tid);
 
         f4 acc[NP][4];
 #pragma unroll
-        for (int s = 0; s < NP; ++s)
+        for (int s2 = 0; s2 < NP; ++s2)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) acc[s][t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int t = 0; t < 4; ++t) acc[s2][t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
         if constexpr (Ph::count() > 0) {
             const float *tile = lds[buf];
@@ -230,50 +275,94 @@ __global__ __launch_bounds__(COG * 4) void k_stream1d(const Stream1dParams P,
             }
         }
 
-        // Epilogue: lane owns outputs o0 .. o0 + 4S - 1 of rows co = 16ct + 4g4 + e.
-        const int o0 = (q0 + 4 * j) * S - P.p;
-        const bool vec = (o0 >= 0) && (o0 + 4 * S <= P.L_out);
+        // Epilogue.  Lane (g4, j) holds, for row co_l = 4*g4 + e, the 4S
+        // outputs o = (q0 + 4j + t)*S + r - p (t = 0..3, r = 0..S-1).  They go
+        // to the staging rows, then come back as float4 runs of whole rows:
+        // the item's outputs of one row are o_t .. o_t + 64S - 1, o_t = q0*S - p.
+        const int o_t = q0 * S - P.p;
+        const int64_t row0 = ((int64_t)n * P.C_out + (int64_t)g * COG + 16 * ct) * P.L_out;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int co = g * COG + 16 * ct + 4 * g4 + e;
-            const int64_t row = ((int64_t)n * P.C_out + co) * P.L_out;
-            float v[4 * S];
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
+            for (int e2 = 0; e2 < 2; ++e2) {
+                const int e = 2 * h + e2;
+                float v[4 * S];
 #pragma unroll
-                for (int r = 0; r < S; ++r) {
-                    float a = 0.0f;
-                    if constexpr (Ph::count() > 0)
-                        if (Ph::nonempty(r)) a = acc[Ph::slot(r)][t][e];
-                    v[t * S + r] = a;
-                }
-            if (vec) {
+                for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int h = 0; h < S; ++h) {
-                    f4 a4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
-                    if constexpr (FUSED) a4 = load4u(add + row + o0 + 4 * h);
-                    f4 out;
-                    out.x = epilogue<FUSED>(v[4 * h + 0], br[e], a4.x);
-                    out.y = epilogue<FUSED>(v[4 * h + 1], br[e], a4.y);
-                    out.z = epilogue<FUSED>(v[4 * h + 2], br[e], a4.z);
-                    out.w = epilogue<FUSED>(v[4 * h + 3], br[e], a4.w);
-                    store4u(y + row + o0 + 4 * h, out);
-                }
-            } else {
+                    for (int r = 0; r < S; ++r) {
+                        float a = 0.0f;
+                        if constexpr (Ph::count() > 0)
+                            if (Ph::nonempty(r)) a = acc[Ph::slot(r)][t][e];
+                        v[t * S + r] = a;
+                    }
+                float *dst = stg + (2 * g4 + e2) * PO + 4 * S * j;
 #pragma unroll
-                for (int u = 0; u < 4 * S; ++u) {
-                    const int o = o0 + u;
-                    if (o >= 0 && o < P.L_out) {
-                        const float a1 = FUSED ? add[row + o] : 0.0f;
-                        y[row + o] = epilogue<FUSED>(v[u], br[e], a1);
+                for (int u = 0; u < S; ++u)
+                    *reinterpret_cast<f4 *>(dst + 4 * u) =
+                        f4{v[4 * u], v[4 * u + 1], v[4 * u + 2], v[4 * u + 3]};
+            }
+            // the same wave reads back what it wrote: LDS operations of one
+            // wave complete in order; keep the compiler from reordering them
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // Read-back: RUN4 lanes per staging row.  Rows have any length, so
+            // a row's run starts anywhere mod 16 bytes; the lanes store only the
+            // 16-byte-aligned float4 chunks inside the run (unaligned 16-byte
+            // stores stream far slower) and the last lane of the row stores the
+            // head and tail elements around them.
+            const bool interior = (o_t >= 0) && (o_t + 64 * S <= P.L_out);
+#pragma unroll
+            for (int m = 0; m < ROUNDS; ++m) {
+                const int f = 64 * m + lane;
+                const int sr = f / RUN4, c4 = f % RUN4;
+                const int col = 4 * (sr >> 1) + 2 * h + (sr & 1);
+                float *yr = y + row0 + (int64_t)col * P.L_out + o_t; // run start
+                const float *ar = FUSED ? add + row0 + (int64_t)col * P.L_out + o_t : nullptr;
+                const float *lr = stg + sr * PO;                    // run in LDS
+                const float bv = bo[h][m];
+                if (interior) {
+                    const int hd = (int)((0u - (unsigned)(uintptr_t)yr) >> 2) & 3; // head length
+                    if (hd == 0 || c4 < RUN4 - 1) {
+                        const int i = hd + 4 * c4;
+                        f4 a4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
+                        if constexpr (FUSED) a4 = load4u(ar + i);
+                        f4 out;
+                        out.x = epilogue<FUSED>(lr[i + 0], bv, a4.x);
+                        out.y = epilogue<FUSED>(lr[i + 1], bv, a4.y);
+                        out.z = epilogue<FUSED>(lr[i + 2], bv, a4.z);
+                        out.w = epilogue<FUSED>(lr[i + 3], bv, a4.w);
+                        store4u(yr + i, out);
+                    } else {
+                        // head [0, hd) and tail [hd + 4*(RUN4-1), 64S): 4 elements
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const int i = u < hd ? u : 4 * (RUN4 - 1) + u;
+                            yr[i] = epilogue<FUSED>(lr[i], bv, FUSED ? ar[i] : 0.0f);
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int i = 4 * c4 + u;
+                        const int o = o_t + i;
+                        if (o >= 0 && o < P.L_out)
+                            yr[i] = epilogue<FUSED>(lr[i], bv, FUSED ? ar[i] : 0.0f);
                     }
                 }
             }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
 
-        if (has_next) tile_store_lds<CIG, NT>(lds[buf ^ 1], pre, tid);
+        if (has_next) tile_store_lds<CIG, NT>(lds[buf ^ 1], pre, P.L_in, (P.st_lo + st1) * kTileQ, tid);
         __syncthreads();
         buf ^= 1;
+        st = st1;
+        ng = ng1;
+    }
     }
 }
 
@@ -331,7 +420,7 @@ int launch_variant(const convt_plan &Pl, const float *x, const float *w, const f
     P.n_st = (int)(st_hi - st_lo);
     P.total = Pl.N * Pl.G * P.n_st;
     // enough workgroups to fill every CU several times over
-    const int64_t blocks_target = (int64_t)num_cus() * 6;
+    const int64_t blocks_target = (int64_t)num_cus() * CONVT_S1D_BLOCKS_PER_CU;
     int64_t per_block = (P.total + blocks_target - 1) / blocks_target;
     if (per_block < 1) per_block = 1;
     P.per_block = (int)per_block;
@@ -350,8 +439,9 @@ int launch_variant(const convt_plan &Pl, const float *x, const float *w, const f
 
 bool stream1d_supports(const convt_plan &P) {
     if (find_variant(P) < 0) return false;
-    // 64-position tiles of one row must index within int range
-    return P.ax[2].L_out < (1 << 30) && P.ax[2].L_in < (1 << 30);
+    // 64-position tiles of one row must index within int range; the tile
+    // fetch reads whole float4 inside a row
+    return P.ax[2].L_out < (1 << 30) && P.ax[2].L_in < (1 << 30) && P.ax[2].L_in >= 4;
 }
 
 int launch_stream1d(const convt_plan &Pl, const float *x, const float *w, const float *bias,
