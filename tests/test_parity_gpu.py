@@ -43,6 +43,18 @@ REDUCED = [
                wid=3005),
     S.Workload("s1d_short", 1, 3, 32, 64, 1, (5,), (3,), (2,), (1,), (0,), (2,), True, False,
                wid=3006),
+    # 3D shapes for each implicit-GEMM variant: fused or not, two W-blocks per
+    # row, ragged last W-block, other paddings and output paddings
+    S.Workload("ig_k3s2_fused_w8", 3, 2, 32, 64, 1, (5, 7, 8), (3, 3, 3), (2, 2, 2), (1, 1, 1),
+               (1, 1, 1), (1, 1, 1), True, True, wid=3101),
+    S.Workload("ig_k3s2_w24", 3, 1, 32, 64, 1, (3, 4, 24), (3, 3, 3), (2, 2, 2), (1, 0, 1),
+               (0, 1, 1), (1, 1, 1), True, False, wid=3102),
+    S.Workload("ig_k4s2_c16", 3, 2, 16, 32, 1, (4, 5, 12), (4, 4, 4), (2, 2, 2), (1, 1, 1),
+               (0, 0, 0), (1, 1, 1), True, True, wid=3103),
+    S.Workload("ig_k3s2_p2", 3, 1, 32, 64, 1, (4, 4, 16), (3, 3, 3), (2, 2, 2), (2, 2, 2),
+               (1, 1, 1), (1, 1, 1), False, False, wid=3104),
+    S.Workload("ig_k3s2_w20", 3, 1, 32, 64, 1, (2, 3, 20), (3, 3, 3), (2, 2, 2), (1, 1, 1),
+               (1, 1, 1), (1, 1, 1), True, True, wid=3105),
 ]
 
 

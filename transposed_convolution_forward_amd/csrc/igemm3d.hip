@@ -1,12 +1,539 @@
-// 3D implicit-GEMM path (placeholder until the MFMA kernel lands).
+// 3D path: per-phase implicit GEMM on fp32 MFMA (v_mfma_f32_16x16x4_f32).
+//
+// Method.  On each axis the residue r of o + p mod s selects a dense tap set
+// T_r with input offsets c (convt_internal.h).  An output row (n, od, oh) has
+// one D phase and one H phase; together they form its class, whose taps
+// T_d x T_h are the same for every row of the class.  Along W the S_W phases
+// interleave inside the row.  Per class the work is a GEMM
+//   Y[co, (n, qd, qh, qw)] = sum_{ci, kd in T_d, kh in T_h, kw in T_w(rw)}
+//        W[ci, co, kd, kh, kw] * X[ci, qd - c_kd, qh - c_kh, qw - c_kw]
+// with M = C_out, N = positions, K = C_in * taps.
+// "Kimi-K2.6 l1_p72" transcript (ConvTranspose3d, groups 4): the parity-class
+// blocking (a block never mixes classes, so trip counts stay uniform) and the
+// reuse of one input value across all output channels of a position;
+// "Kimi-K2.6 l2_p26" transcript (ConvTranspose3d + add + HardSwish): outputs
+// with one or two taps per axis, and the fused epilogue.
+//
+// Mapping.  A workgroup holds one class and walks a run of its output rows.
+// Wave w owns output channels 16w .. 16w+15; the class's weights for those
+// channels stay in VGPRs (A operand, W^T: 16 co x 4 ci).  The input rows
+// x[n, :, qd - c_kd, qh - c_kh, :] of all D/H taps of the next output row are
+// fetched into registers during the current row's contraction, then written
+// to LDS (double buffer); B operands (4 ci x 16 positions) are read from
+// there, zero outside the input.  For W phase rw the first position
+// qw0(rw) = max(0, ceil((p_w - rw)/S_W)) gives output sigma(rw) =
+// qw0*S_W + rw - p_w in [0, S_W), so lane j of W-block t holds the outputs
+// ow = S_W*(16t + j) + sigma(rw): S_W consecutive outputs of one row per lane,
+// one vector store per channel.  Atomic-free: every output is stored once.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cstring>
+#include <utility>
+
 #include "convt_internal.h"
+#include "epilogue.hpp"
 
 namespace convt {
-bool igemm3d_supports(const convt_plan &) { return false; }
-int launch_igemm3d(const convt_plan &, const float *, const float *, const float *,
-                   const float *, float *, void *) {
-    return (int)hipErrorInvalidValue;
+namespace {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4 load4u(const float *p) {
+    f4 v;
+    __builtin_memcpy(&v, p, 16);
+    return v;
 }
+
+constexpr int kMaxClasses = 16;
+constexpr int kTapMax = 4; // per-axis taps per class the table holds
+constexpr int kMaxSW = 8;
+
+template <int K, int S, int D> struct WPhases {
+    static constexpr int r_of(int k) { return (k * D) % S; }
+    static constexpr int c_of(int k) { return (k * D) / S; }
+    static constexpr bool nonempty(int r) {
+        for (int k = 0; k < K; ++k)
+            if (r_of(k) == r) return true;
+        return false;
+    }
+    static constexpr int slot(int r) {
+        int n = 0;
+        for (int q = 0; q < r; ++q) n += nonempty(q) ? 1 : 0;
+        return n;
+    }
+    static constexpr int count() {
+        int n = 0;
+        for (int r = 0; r < S; ++r) n += nonempty(r) ? 1 : 0;
+        return n;
+    }
+    static constexpr int cmax() {
+        int m = 0;
+        for (int k = 0; k < K; ++k) m = c_of(k) > m ? c_of(k) : m;
+        return m;
+    }
+};
+
+struct Igemm3dParams {
+    int C_in, C_out;
+    int D_in, H_in, W_in, D_out, H_out, W_out;
+    int KD, KH;          // kernel extents along D and H (W is a template constant)
+    int s_d, s_h;
+    int n_class;
+    int rows_per_block;
+    int iw_lo;           // input position held at LDS offset 0 (multiple of 4, <= 0)
+    int nwb;             // W-blocks of 16*S_W outputs per row
+    int qw0[kMaxSW], sigma[kMaxSW];
+    int cls_block0[kMaxClasses + 1]; // classes ordered heaviest first
+    int cls_rows[kMaxClasses];
+    int cls_td[kMaxClasses], cls_th[kMaxClasses];
+    int cls_kd[kMaxClasses][kTapMax], cls_cd[kMaxClasses][kTapMax];
+    int cls_kh[kMaxClasses][kTapMax], cls_ch[kMaxClasses][kTapMax];
+    int cls_od0[kMaxClasses], cls_qd0[kMaxClasses], cls_nqd[kMaxClasses];
+    int cls_oh0[kMaxClasses], cls_qh0[kMaxClasses], cls_nqh[kMaxClasses];
+};
+
+struct RowPos {
+    int n, qd, qh, od, oh;
+};
+
+__device__ __forceinline__ RowPos decode_row(const Igemm3dParams &P, int cls, int r) {
+    const int nqh = P.cls_nqh[cls], nqd = P.cls_nqd[cls];
+    const int iqh = r % nqh;
+    const int t = r / nqh;
+    const int iqd = t % nqd;
+    RowPos R;
+    R.n = t / nqd;
+    R.qd = P.cls_qd0[cls] + iqd;
+    R.qh = P.cls_qh0[cls] + iqh;
+    R.od = P.cls_od0[cls] + iqd * P.s_d;
+    R.oh = P.cls_oh0[cls] + iqh * P.s_h;
+    return R;
+}
+
+// Input rows of one output row: SLOTS x CIG rows of W_in floats, W4 float4 each,
+// fetched branch-free (invalid rows read a safe address and are zeroed at the
+// LDS write).
+template <int CIG, int TDM, int THM, int NT, int PER>
+__device__ __forceinline__ void stage_fetch(f4 (&r)[PER], unsigned &valid, const Igemm3dParams &P,
+                                            const float *x, int cls, const RowPos &R, int tid) {
+    const int W4 = P.W_in >> 2;
+    const int nf = TDM * THM * CIG * W4;
+    valid = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int f = tid + u * NT;
+        const int slot = f / (CIG * W4);
+        const int rem = f - slot * (CIG * W4);
+        const int ci = rem / W4, c4 = rem - (rem / W4) * W4;
+        const int jd = slot / THM, jh = slot - (slot / THM) * THM;
+        const int id = R.qd - P.cls_cd[cls][jd < kTapMax ? jd : 0];
+        const int ih = R.qh - P.cls_ch[cls][jh < kTapMax ? jh : 0];
+        const bool ok = f < nf && jd < P.cls_td[cls] && jh < P.cls_th[cls] && id >= 0 &&
+                        id < P.D_in && ih >= 0 && ih < P.H_in;
+        const int64_t off =
+            ok ? ((((int64_t)R.n * P.C_in + ci) * P.D_in + id) * P.H_in + ih) * P.W_in + 4 * c4 : 0;
+        r[u] = load4u(x + off);
+        valid |= ok ? (1u << u) : 0u;
+    }
+}
+
+template <int CIG, int TDM, int THM, int NT, int PER, int PWM>
+__device__ __forceinline__ void stage_store(float *buf, const f4 (&r)[PER], unsigned valid,
+                                            const Igemm3dParams &P, int tid) {
+    const int W4 = P.W_in >> 2;
+    const int nf = TDM * THM * CIG * W4;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int f = tid + u * NT;
+        if (f < nf) {
+            const int slot = f / (CIG * W4);
+            const int rem = f - slot * (CIG * W4);
+            const int ci = rem / W4, c4 = rem - (rem / W4) * W4;
+            const f4 v = (valid >> u) & 1u ? r[u] : f4{0.0f, 0.0f, 0.0f, 0.0f};
+            *reinterpret_cast<f4 *>(buf + (slot * CIG + ci) * PWM + 4 * c4 - P.iw_lo) = v;
+        }
+    }
+}
+
+template <int CIG, int COG, int KW, int SW, int DW, int TDM, int THM, int NWBM, int PWM, int PER,
+          bool FUSED>
+__global__ __launch_bounds__(COG * 4) void k_igemm3d(const Igemm3dParams P,
+                                                     const float *__restrict__ x,
+                                                     const float *__restrict__ w,
+                                                     const float *__restrict__ bias,
+                                                     const float *add, float *y) {
+    using Ph = WPhases<KW, SW, DW>;
+    constexpr int NCIG = CIG / 4;
+    constexpr int NT = COG * 4;
+    constexpr int SLOTS = TDM * THM;
+    constexpr int NPH = Ph::count() > 0 ? Ph::count() : 1;
+    static_assert(CIG % 8 == 0 && COG % 16 == 0, "tile shape");
+    static_assert(SW <= kMaxSW, "W stride");
+
+    __shared__ __attribute__((aligned(16))) float lds[2][SLOTS * CIG * PWM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int ct = tid >> 6;
+    const int j = lane & 15;
+    const int g4 = lane >> 4;
+
+    int cls = 0;
+    while (cls + 1 < P.n_class && (int)blockIdx.x >= P.cls_block0[cls + 1]) ++cls;
+    const int r_begin = ((int)blockIdx.x - P.cls_block0[cls]) * P.rows_per_block;
+    const int r_end = min(r_begin + P.rows_per_block, P.cls_rows[cls]);
+    if (r_begin >= r_end) return;
+    const int td = P.cls_td[cls], th = P.cls_th[cls];
+
+    // zero both buffers once: halo columns and unused slots stay zero
+    for (int i = tid; i < 2 * SLOTS * CIG * PWM; i += NT) (&lds[0][0])[i] = 0.0f;
+
+    // the class's weights for this wave's channels: W[4cig + g4][16ct + j][kd][kh][kw]
+    float wr[TDM][THM][KW][NCIG];
+#pragma unroll
+    for (int jd = 0; jd < TDM; ++jd)
+#pragma unroll
+        for (int jh = 0; jh < THM; ++jh) {
+            const bool used = jd < td && jh < th;
+            const int kd = used ? P.cls_kd[cls][jd] : 0;
+            const int kh = used ? P.cls_kh[cls][jh] : 0;
+#pragma unroll
+            for (int kw = 0; kw < KW; ++kw)
+#pragma unroll
+                for (int cig = 0; cig < NCIG; ++cig) {
+                    const int64_t idx =
+                        ((((int64_t)(4 * cig + g4) * COG + 16 * ct + j) * P.KD + kd) * P.KH + kh) *
+                            KW + kw;
+                    const float v = w[idx];
+                    wr[jd][jh][kw][cig] = used ? v : 0.0f;
+                }
+        }
+    float bo[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) bo[e] = bias ? bias[16 * ct + 4 * g4 + e] : 0.0f;
+    // wait for these here, not inside the row loop (vmcnt is in order)
+#pragma unroll
+    for (int jd = 0; jd < TDM; ++jd)
+#pragma unroll
+        for (int jh = 0; jh < THM; ++jh)
+#pragma unroll
+            for (int kw = 0; kw < KW; ++kw)
+#pragma unroll
+                for (int cig = 0; cig < NCIG; ++cig) asm volatile("" : "+v"(wr[jd][jh][kw][cig]));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(bo[e]));
+
+    f4 pre[PER];
+    unsigned pvalid;
+    RowPos R = decode_row(P, cls, r_begin);
+    __syncthreads(); // LDS zeroed before the first row lands
+    stage_fetch<CIG, TDM, THM, NT, PER>(pre, pvalid, P, x, cls, R, tid);
+    stage_store<CIG, TDM, THM, NT, PER, PWM>(lds[0], pre, pvalid, P, tid);
+    __syncthreads();
+
+    int buf = 0;
+    for (int r = r_begin; r < r_end; ++r) {
+        const bool has_next = r + 1 < r_end;
+        // add_input of this row first (older than the prefetch in vmcnt order)
+        float av[NWBM][4][SW];
+        if constexpr (FUSED) {
+#pragma unroll
+            for (int t = 0; t < NWBM; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int co = 16 * ct + 4 * g4 + e;
+                    const int64_t row =
+                        (((int64_t)R.n * P.C_out + co) * P.D_out + R.od) * P.H_out + R.oh;
+#pragma unroll
+                    for (int rr = 0; rr < SW; ++rr) {
+                        const int ow = min(SW * (16 * t + j) + rr, P.W_out - 1);
+                        av[t][e][rr] = (t < P.nwb) ? add[row * P.W_out + ow] : 0.0f;
+                    }
+                }
+        }
+        RowPos Rn = R;
+        if (has_next) {
+            Rn = decode_row(P, cls, r + 1);
+            stage_fetch<CIG, TDM, THM, NT, PER>(pre, pvalid, P, x, cls, Rn, tid);
+        }
+
+        f4 acc[NPH][NWBM][2];
+#pragma unroll
+        for (int s = 0; s < NPH; ++s)
+#pragma unroll
+            for (int t = 0; t < NWBM; ++t) acc[s][t][0] = acc[s][t][1] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+        if constexpr (Ph::count() > 0) {
+            const float *tile = lds[buf];
+#pragma unroll
+            for (int jd = 0; jd < TDM; ++jd) {
+                if (jd >= td) break;
+#pragma unroll
+                for (int jh = 0; jh < THM; ++jh) {
+                    if (jh >= th) break;
+                    const int slot = jd * THM + jh;
+#pragma unroll
+                    for (int cig = 0; cig < NCIG; ++cig) {
+                        const float *rowp = tile + (slot * CIG + 4 * cig + g4) * PWM - P.iw_lo + j;
+#pragma unroll
+                        for (int kw = 0; kw < KW; ++kw) {
+                            const int rw = Ph::r_of(kw);
+                            const int sl = Ph::slot(rw);
+                            const int c = Ph::c_of(kw);
+#pragma unroll
+                            for (int t = 0; t < NWBM; ++t) {
+                                if (t >= P.nwb) break;
+                                const float bv = rowp[P.qw0[rw] + 16 * t - c];
+                                acc[sl][t][cig & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                    wr[jd][jh][kw][cig], bv, acc[sl][t][cig & 1], 0, 0, 0);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+
+        // epilogue: lane (g4, j) owns co = 16ct + 4g4 + e, ow = SW*(16t + j) + rr
+#pragma unroll
+        for (int t = 0; t < NWBM; ++t) {
+            if (t >= P.nwb) break;
+            const int ow0 = SW * (16 * t + j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int co = 16 * ct + 4 * g4 + e;
+                const int64_t row =
+                    (((int64_t)R.n * P.C_out + co) * P.D_out + R.od) * P.H_out + R.oh;
+                float v[SW];
+#pragma unroll
+                for (int rr = 0; rr < SW; ++rr) v[rr] = 0.0f;
+#pragma unroll
+                for (int rw = 0; rw < SW; ++rw) {
+                    if constexpr (Ph::count() > 0) {
+                        if (Ph::nonempty(rw)) {
+                            const int sl = Ph::slot(rw);
+                            const float a = acc[sl][t][0][e] + acc[sl][t][1][e];
+#pragma unroll
+                            for (int rr = 0; rr < SW; ++rr)
+                                if (P.sigma[rw] == rr) v[rr] = a;
+                        }
+                    }
+                }
+                float *yp = y + row * P.W_out + ow0;
+#pragma unroll
+                for (int rr = 0; rr < SW; ++rr) {
+                    const float a1 = FUSED ? av[t][e][rr] : 0.0f;
+                    v[rr] = epilogue<FUSED>(v[rr], bo[e], a1);
+                }
+                if (ow0 + SW <= P.W_out) {
+                    if constexpr (SW == 2) {
+                        typedef float f2u __attribute__((ext_vector_type(2)));
+                        f2u o2 = f2u{v[0], v[1]};
+                        __builtin_memcpy(yp, &o2, 8);
+                    } else {
+#pragma unroll
+                        for (int rr = 0; rr < SW; ++rr) yp[rr] = v[rr];
+                    }
+                } else {
+#pragma unroll
+                    for (int rr = 0; rr < SW; ++rr)
+                        if (ow0 + rr < P.W_out) yp[rr] = v[rr];
+                }
+            }
+        }
+
+        if (has_next) stage_store<CIG, TDM, THM, NT, PER, PWM>(lds[buf ^ 1], pre, pvalid, P, tid);
+        __syncthreads();
+        buf ^= 1;
+        R = Rn;
+    }
+}
+
+// ---------------------------------------------------------------- host side
+struct Variant {
+    int cig, cog, KW, SW, DW, TDM, THM, NWBM, PWM, W4M;
+};
+constexpr int kPW = 48; // LDS pitch: 16 mod 32 spreads the 4 ci rows of a B read over the banks
+constexpr Variant kVariants[] = {
+    {32, 64, 3, 2, 1, 2, 2, 1, kPW, 4}, // 32 -> 64 channels, kernel 3, stride 2 (the fused layer)
+    {32, 64, 3, 2, 1, 2, 2, 2, kPW, 8}, // same, input rows up to 32 wide
+    {16, 32, 4, 2, 1, 2, 2, 2, kPW, 8}, // 16 -> 32 channels, kernel 4, stride 2
+};
+constexpr int kNumVariants = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
+
+int ceil_div(int a, int b) { return a >= 0 ? (a + b - 1) / b : -((-a) / b); }
+
+struct Layout {
+    int iw_lo, need, nwb;
+    int qw0[kMaxSW], sigma[kMaxSW];
+    int cmax;
+};
+
+bool w_layout(const convt_plan &P, const Variant &v, Layout &L) {
+    const AxisPlan &A = P.ax[2];
+    if (A.K != v.KW || A.s != v.SW || A.d != v.DW) return false;
+    L.cmax = 0;
+    for (int k = 0; k < v.KW; ++k) L.cmax = std::max(L.cmax, (k * v.DW) / v.SW);
+    int qmax = 0;
+    for (int r = 0; r < v.SW; ++r) {
+        L.qw0[r] = std::max(0, ceil_div(A.p - r, v.SW));
+        L.sigma[r] = L.qw0[r] * v.SW + r - A.p;
+        qmax = std::max(qmax, L.qw0[r]);
+    }
+    L.nwb = (A.L_out + 16 * v.SW - 1) / (16 * v.SW);
+    L.iw_lo = -((L.cmax + 3) / 4) * 4;
+    const int iw_hi = std::max(qmax + 16 * L.nwb, A.L_in); // exclusive
+    L.need = iw_hi - L.iw_lo;
+    return L.nwb <= v.NWBM && L.need <= v.PWM;
+}
+
+int find_variant(const convt_plan &P, Layout *Lout = nullptr) {
+    if (P.ndim != 3 || P.G != 1) return -1;
+    const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
+    if (AW.L_in % 4 != 0) return -1;
+    const int W4 = AW.L_in / 4;
+    if (AD.s * AH.s > kMaxClasses) return -1;
+    // taps per class on D and H
+    int tdm = 0, thm = 0;
+    for (int r = 0; r < AD.s; ++r) tdm = std::max(tdm, AD.tap_start[r + 1] - AD.tap_start[r]);
+    for (int r = 0; r < AH.s; ++r) thm = std::max(thm, AH.tap_start[r + 1] - AH.tap_start[r]);
+    for (int i = 0; i < kNumVariants; ++i) {
+        const Variant &v = kVariants[i];
+        if (P.Cig != v.cig || P.Cog != v.cog || tdm > v.TDM || thm > v.THM || W4 > v.W4M) continue;
+        Layout L;
+        if (!w_layout(P, v, L)) continue;
+        if (Lout) *Lout = L;
+        return i;
+    }
+    return -1;
+}
+
+int num_cus() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+    }
+    return cus;
+}
+
+template <int CIG, int COG, int KW, int SW, int DW, int TDM, int THM, int NWBM, int PWM, int W4M>
+int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const float *w,
+                   const float *bias, const float *add, float *y, hipStream_t st) {
+    const AxisPlan &AD = Pl.ax[0], &AH = Pl.ax[1], &AW = Pl.ax[2];
+    Igemm3dParams P;
+    memset(&P, 0, sizeof(P));
+    P.C_in = (int)Pl.C_in;
+    P.C_out = (int)Pl.C_out;
+    P.D_in = AD.L_in;
+    P.H_in = AH.L_in;
+    P.W_in = AW.L_in;
+    P.D_out = AD.L_out;
+    P.H_out = AH.L_out;
+    P.W_out = AW.L_out;
+    P.KD = AD.K;
+    P.KH = AH.K;
+    P.s_d = AD.s;
+    P.s_h = AH.s;
+    P.iw_lo = L.iw_lo;
+    P.nwb = L.nwb;
+    for (int r = 0; r < SW; ++r) {
+        P.qw0[r] = L.qw0[r];
+        P.sigma[r] = L.sigma[r];
+    }
+    // classes (rd, rh) with at least one output row, heaviest first
+    struct Cls {
+        int rd, rh, taps;
+    } cl[kMaxClasses];
+    int nc = 0;
+    for (int rd = 0; rd < AD.s; ++rd)
+        for (int rh = 0; rh < AH.s; ++rh) {
+            const int td = AD.tap_start[rd + 1] - AD.tap_start[rd];
+            const int th = AH.tap_start[rh + 1] - AH.tap_start[rh];
+            cl[nc++] = {rd, rh, td * th};
+        }
+    for (int a = 0; a < nc; ++a)
+        for (int b = a + 1; b < nc; ++b)
+            if (cl[b].taps > cl[a].taps) std::swap(cl[a], cl[b]);
+    int64_t total_rows = 0;
+    int kept = 0;
+    for (int i = 0; i < nc; ++i) {
+        const int rd = cl[i].rd, rh = cl[i].rh;
+        const int qd0 = std::max(0, ceil_div(AD.p - rd, AD.s));
+        const int od0 = qd0 * AD.s + rd - AD.p;
+        const int nqd = od0 < AD.L_out ? (AD.L_out - 1 - od0) / AD.s + 1 : 0;
+        const int qh0 = std::max(0, ceil_div(AH.p - rh, AH.s));
+        const int oh0 = qh0 * AH.s + rh - AH.p;
+        const int nqh = oh0 < AH.L_out ? (AH.L_out - 1 - oh0) / AH.s + 1 : 0;
+        if (nqd == 0 || nqh == 0) continue;
+        const int c = kept++;
+        P.cls_td[c] = AD.tap_start[rd + 1] - AD.tap_start[rd];
+        P.cls_th[c] = AH.tap_start[rh + 1] - AH.tap_start[rh];
+        for (int t = 0; t < P.cls_td[c]; ++t) {
+            P.cls_kd[c][t] = AD.tap_k[AD.tap_start[rd] + t];
+            P.cls_cd[c][t] = AD.tap_c[AD.tap_start[rd] + t];
+        }
+        for (int t = 0; t < P.cls_th[c]; ++t) {
+            P.cls_kh[c][t] = AH.tap_k[AH.tap_start[rh] + t];
+            P.cls_ch[c][t] = AH.tap_c[AH.tap_start[rh] + t];
+        }
+        P.cls_qd0[c] = qd0;
+        P.cls_od0[c] = od0;
+        P.cls_nqd[c] = nqd;
+        P.cls_qh0[c] = qh0;
+        P.cls_oh0[c] = oh0;
+        P.cls_nqh[c] = nqh;
+        P.cls_rows[c] = (int)(Pl.N * nqd * nqh);
+        total_rows += P.cls_rows[c];
+    }
+    P.n_class = kept;
+    // rows per block: enough blocks to fill the CUs several times over
+    const int64_t target_blocks = (int64_t)num_cus() * 16;
+    int rpb = (int)std::max<int64_t>(1, std::min<int64_t>(64, total_rows / target_blocks));
+    P.rows_per_block = rpb;
+    int blocks = 0;
+    for (int c = 0; c < kept; ++c) {
+        P.cls_block0[c] = blocks;
+        blocks += (P.cls_rows[c] + rpb - 1) / rpb;
+    }
+    P.cls_block0[kept] = blocks;
+    if (blocks == 0) return 0;
+    constexpr int NT = COG * 4;
+    constexpr int PER = (TDM * THM * CIG * W4M + NT - 1) / NT; // W_in <= 4*W4M is checked
+    const int need_f = TDM * THM * CIG * (AW.L_in / 4);
+    if (need_f > PER * NT) return (int)hipErrorInvalidValue;
+    if (add)
+        hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, true>),
+                           dim3(blocks), dim3(NT), 0, st, P, x, w, bias, add, y);
+    else
+        hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, false>),
+                           dim3(blocks), dim3(NT), 0, st, P, x, w, bias, add, y);
+    return (int)hipGetLastError();
+}
+
+} // namespace
+
+bool igemm3d_supports(const convt_plan &P) {
+    if (P.ndim != 3) return false;
+    Layout L;
+    if (find_variant(P, &L) < 0) return false;
+    return P.N * P.ax[0].L_out * P.ax[1].L_out < (int64_t(1) << 31);
+}
+
+int launch_igemm3d(const convt_plan &Pl, const float *x, const float *w, const float *bias,
+                   const float *add, float *y, void *stream) {
+    Layout L;
+    const int v = find_variant(Pl, &L);
+    hipStream_t st = (hipStream_t)stream;
+    switch (v) {
+    case 0: return launch_variant<32, 64, 3, 2, 1, 2, 2, 1, kPW, 4>(Pl, L, x, w, bias, add, y, st);
+    case 1: return launch_variant<32, 64, 3, 2, 1, 2, 2, 2, kPW, 8>(Pl, L, x, w, bias, add, y, st);
+    case 2: return launch_variant<16, 32, 4, 2, 1, 2, 2, 2, kPW, 8>(Pl, L, x, w, bias, add, y, st);
+    default: return (int)hipErrorInvalidValue;
+    }
+}
+
 } // namespace convt
