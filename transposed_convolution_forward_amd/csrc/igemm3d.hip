@@ -82,7 +82,7 @@ struct Igemm3dParams {
     int n_class;
     int rows_per_block;
     int iw_lo;           // input position held at LDS offset 0 (multiple of 4, <= 0)
-    int nwb;             // W-blocks of 16*S_W outputs per row
+    int nwb;             // W-blocks of 16*S_W outputs per row (equals the template's NWBM)
     int qw0[kMaxSW], sigma[kMaxSW];
     int cls_block0[kMaxClasses + 1]; // classes ordered heaviest first
     int cls_rows[kMaxClasses];
@@ -111,47 +111,62 @@ __device__ __forceinline__ RowPos decode_row(const Igemm3dParams &P, int cls, in
     return R;
 }
 
-// Input rows of one output row: SLOTS x CIG rows of W_in floats, W4 float4 each,
-// fetched branch-free (invalid rows read a safe address and are zeroed at the
-// LDS write).
-template <int CIG, int TDM, int THM, int NT, int PER>
-__device__ __forceinline__ void stage_fetch(f4 (&r)[PER], unsigned &valid, const Igemm3dParams &P,
-                                            const float *x, int cls, const RowPos &R, int tid) {
+// Input rows of one output row: SLOTS x CIG rows of W_in floats (W4 float4
+// each).  Thread tid stages float4 number f = tid + u*NT; what f means does not
+// depend on the row, so it is decoded once (StageMap).  Fetches are
+// branch-free: invalid rows read a safe address and are zeroed at the LDS
+// write.
+template <int PER> struct StageMap {
+    int xoff[PER]; // ci*D_in*H_in*W_in + 4*c4
+    int loff[PER]; // LDS offset of the float4, -1 if f is past the last float4
+    int tap[PER];  // jd*4 + jh of the slot
+};
+
+template <int CIG, int THM, int NT, int PER, int PWM>
+__device__ __forceinline__ void stage_map(StageMap<PER> &M, const Igemm3dParams &P, int nslots,
+                                          int tid) {
     const int W4 = P.W_in >> 2;
-    const int nf = TDM * THM * CIG * W4;
-    valid = 0;
+    const int nf = nslots * CIG * W4;
+    const int dhw = P.D_in * P.H_in * P.W_in;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const int f = tid + u * NT;
         const int slot = f / (CIG * W4);
         const int rem = f - slot * (CIG * W4);
-        const int ci = rem / W4, c4 = rem - (rem / W4) * W4;
-        const int jd = slot / THM, jh = slot - (slot / THM) * THM;
-        const int id = R.qd - P.cls_cd[cls][jd < kTapMax ? jd : 0];
-        const int ih = R.qh - P.cls_ch[cls][jh < kTapMax ? jh : 0];
-        const bool ok = f < nf && jd < P.cls_td[cls] && jh < P.cls_th[cls] && id >= 0 &&
-                        id < P.D_in && ih >= 0 && ih < P.H_in;
-        const int64_t off =
-            ok ? ((((int64_t)R.n * P.C_in + ci) * P.D_in + id) * P.H_in + ih) * P.W_in + 4 * c4 : 0;
+        const int ci = rem / W4, c4 = rem - ci * W4;
+        M.xoff[u] = ci * dhw + 4 * c4;
+        M.loff[u] = f < nf ? (slot * CIG + ci) * PWM + 4 * c4 - P.iw_lo : -1;
+        M.tap[u] = (slot / THM) * 4 + slot % THM;
+    }
+}
+
+template <int PER>
+__device__ __forceinline__ void stage_fetch(f4 (&r)[PER], unsigned &valid, const StageMap<PER> &M,
+                                            const Igemm3dParams &P, const float *x, int td, int th,
+                                            int cd0, int cd1, int ch0, int ch1, const RowPos &R) {
+    const int64_t nbase = (int64_t)R.n * P.C_in * P.D_in * P.H_in * P.W_in;
+    valid = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int jd = M.tap[u] >> 2, jh = M.tap[u] & 3;
+        const int id = R.qd - (jd == 0 ? cd0 : cd1);
+        const int ih = R.qh - (jh == 0 ? ch0 : ch1);
+        const bool ok = M.loff[u] >= 0 && jd < td && jh < th && id >= 0 && id < P.D_in &&
+                        ih >= 0 && ih < P.H_in;
+        const int64_t off = ok ? nbase + M.xoff[u] + (id * P.H_in + ih) * P.W_in : 0;
         r[u] = load4u(x + off);
         valid |= ok ? (1u << u) : 0u;
     }
 }
 
-template <int CIG, int TDM, int THM, int NT, int PER, int PWM>
+template <int PER>
 __device__ __forceinline__ void stage_store(float *buf, const f4 (&r)[PER], unsigned valid,
-                                            const Igemm3dParams &P, int tid) {
-    const int W4 = P.W_in >> 2;
-    const int nf = TDM * THM * CIG * W4;
+                                            const StageMap<PER> &M) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int f = tid + u * NT;
-        if (f < nf) {
-            const int slot = f / (CIG * W4);
-            const int rem = f - slot * (CIG * W4);
-            const int ci = rem / W4, c4 = rem - (rem / W4) * W4;
+        if (M.loff[u] >= 0) {
             const f4 v = (valid >> u) & 1u ? r[u] : f4{0.0f, 0.0f, 0.0f, 0.0f};
-            *reinterpret_cast<f4 *>(buf + (slot * CIG + ci) * PWM + 4 * c4 - P.iw_lo) = v;
+            *reinterpret_cast<f4 *>(buf + M.loff[u]) = v;
         }
     }
 }
@@ -224,48 +239,63 @@ __global__ __launch_bounds__(COG * 4) void k_igemm3d(const Igemm3dParams P,
 #pragma unroll
     for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(bo[e]));
 
+    static_assert(TDM <= 2 && THM <= 2, "tap offsets are selected from two registers");
+    StageMap<PER> M;
+    stage_map<CIG, THM, NT, PER, PWM>(M, P, SLOTS, tid);
+    const int cd0 = P.cls_cd[cls][0], cd1 = P.cls_cd[cls][1];
+    const int ch0 = P.cls_ch[cls][0], ch1 = P.cls_ch[cls][1];
+    // output offset of this lane: channel 16ct + 4g4 (+ e), W position SW*j (+ 16 SW t)
+    const int64_t dhw_out = (int64_t)P.D_out * P.H_out * P.W_out;
+    const int64_t lane_out = (int64_t)(16 * ct + 4 * g4) * dhw_out + SW * j;
+
     f4 pre[PER];
     unsigned pvalid;
     RowPos R = decode_row(P, cls, r_begin);
     __syncthreads(); // LDS zeroed before the first row lands
-    stage_fetch<CIG, TDM, THM, NT, PER>(pre, pvalid, P, x, cls, R, tid);
-    stage_store<CIG, TDM, THM, NT, PER, PWM>(lds[0], pre, pvalid, P, tid);
+    stage_fetch<PER>(pre, pvalid, M, P, x, td, th, cd0, cd1, ch0, ch1, R);
+    stage_store<PER>(lds[0], pre, pvalid, M);
     __syncthreads();
 
     int buf = 0;
     for (int r = r_begin; r < r_end; ++r) {
         const bool has_next = r + 1 < r_end;
         // add_input of this row first (older than the prefetch in vmcnt order)
+        // this row's output base (uniform); lane adds lane_out + e*dhw_out + 16 SW t
+        const int64_t row_base = (int64_t)R.n * P.C_out * dhw_out +
+                                 ((int64_t)R.od * P.H_out + R.oh) * P.W_out;
         float av[NWBM][4][SW];
         if constexpr (FUSED) {
+            const float *arow = add + row_base + lane_out;
 #pragma unroll
             for (int t = 0; t < NWBM; ++t)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int co = 16 * ct + 4 * g4 + e;
-                    const int64_t row =
-                        (((int64_t)R.n * P.C_out + co) * P.D_out + R.od) * P.H_out + R.oh;
+                for (int e = 0; e < 4; ++e)
 #pragma unroll
                     for (int rr = 0; rr < SW; ++rr) {
-                        const int ow = min(SW * (16 * t + j) + rr, P.W_out - 1);
-                        av[t][e][rr] = (t < P.nwb) ? add[row * P.W_out + ow] : 0.0f;
+                        // clamp inside the row for lanes past its end
+                        const int ow = min(SW * (16 * t + j) + rr, P.W_out - 1) - SW * j;
+                        av[t][e][rr] = arow[e * dhw_out + ow];
                     }
-                }
         }
         RowPos Rn = R;
         if (has_next) {
             Rn = decode_row(P, cls, r + 1);
-            stage_fetch<CIG, TDM, THM, NT, PER>(pre, pvalid, P, x, cls, Rn, tid);
+            stage_fetch<PER>(pre, pvalid, M, P, x, td, th, cd0, cd1, ch0, ch1, Rn);
         }
 
-        f4 acc[NPH][NWBM][2];
+        f4 acc[NPH][NWBM];
 #pragma unroll
         for (int s = 0; s < NPH; ++s)
 #pragma unroll
-            for (int t = 0; t < NWBM; ++t) acc[s][t][0] = acc[s][t][1] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int t = 0; t < NWBM; ++t) acc[s][t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
         if constexpr (Ph::count() > 0) {
-            const float *tile = lds[buf];
+            // per W phase, this lane's B column in LDS: every read below is
+            // then this base plus a compile-time offset
+            const float *bcol[SW];
+#pragma unroll
+            for (int rw = 0; rw < SW; ++rw)
+                bcol[rw] = lds[buf] + g4 * PWM - P.iw_lo + j + P.qw0[rw];
 #pragma unroll
             for (int jd = 0; jd < TDM; ++jd) {
                 if (jd >= td) break;
@@ -275,7 +305,6 @@ __global__ __launch_bounds__(COG * 4) void k_igemm3d(const Igemm3dParams P,
                     const int slot = jd * THM + jh;
 #pragma unroll
                     for (int cig = 0; cig < NCIG; ++cig) {
-                        const float *rowp = tile + (slot * CIG + 4 * cig + g4) * PWM - P.iw_lo + j;
 #pragma unroll
                         for (int kw = 0; kw < KW; ++kw) {
                             const int rw = Ph::r_of(kw);
@@ -283,10 +312,9 @@ __global__ __launch_bounds__(COG * 4) void k_igemm3d(const Igemm3dParams P,
                             const int c = Ph::c_of(kw);
 #pragma unroll
                             for (int t = 0; t < NWBM; ++t) {
-                                if (t >= P.nwb) break;
-                                const float bv = rowp[P.qw0[rw] + 16 * t - c];
-                                acc[sl][t][cig & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                    wr[jd][jh][kw][cig], bv, acc[sl][t][cig & 1], 0, 0, 0);
+                                const float bv = bcol[rw][(slot * CIG + 4 * cig) * PWM + 16 * t - c];
+                                acc[sl][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                    wr[jd][jh][kw][cig], bv, acc[sl][t], 0, 0, 0);
                             }
                         }
                     }
@@ -297,13 +325,9 @@ __global__ __launch_bounds__(COG * 4) void k_igemm3d(const Igemm3dParams P,
         // epilogue: lane (g4, j) owns co = 16ct + 4g4 + e, ow = SW*(16t + j) + rr
 #pragma unroll
         for (int t = 0; t < NWBM; ++t) {
-            if (t >= P.nwb) break;
             const int ow0 = SW * (16 * t + j);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int co = 16 * ct + 4 * g4 + e;
-                const int64_t row =
-                    (((int64_t)R.n * P.C_out + co) * P.D_out + R.od) * P.H_out + R.oh;
                 float v[SW];
 #pragma unroll
                 for (int rr = 0; rr < SW; ++rr) v[rr] = 0.0f;
@@ -311,15 +335,14 @@ __global__ __launch_bounds__(COG * 4) void k_igemm3d(const Igemm3dParams P,
                 for (int rw = 0; rw < SW; ++rw) {
                     if constexpr (Ph::count() > 0) {
                         if (Ph::nonempty(rw)) {
-                            const int sl = Ph::slot(rw);
-                            const float a = acc[sl][t][0][e] + acc[sl][t][1][e];
+                            const float a = acc[Ph::slot(rw)][t][e];
 #pragma unroll
                             for (int rr = 0; rr < SW; ++rr)
                                 if (P.sigma[rw] == rr) v[rr] = a;
                         }
                     }
                 }
-                float *yp = y + row * P.W_out + ow0;
+                float *yp = y + row_base + lane_out + e * dhw_out + SW * 16 * t;
 #pragma unroll
                 for (int rr = 0; rr < SW; ++rr) {
                     const float a1 = FUSED ? av[t][e][rr] : 0.0f;
@@ -342,7 +365,7 @@ __global__ __launch_bounds__(COG * 4) void k_igemm3d(const Igemm3dParams P,
             }
         }
 
-        if (has_next) stage_store<CIG, TDM, THM, NT, PER, PWM>(lds[buf ^ 1], pre, pvalid, P, tid);
+        if (has_next) stage_store<PER>(lds[buf ^ 1], pre, pvalid, M);
         __syncthreads();
         buf ^= 1;
         R = Rn;
@@ -384,7 +407,7 @@ bool w_layout(const convt_plan &P, const Variant &v, Layout &L) {
     L.iw_lo = -((L.cmax + 3) / 4) * 4;
     const int iw_hi = std::max(qmax + 16 * L.nwb, A.L_in); // exclusive
     L.need = iw_hi - L.iw_lo;
-    return L.nwb <= v.NWBM && L.need <= v.PWM;
+    return L.nwb == v.NWBM && L.need <= v.PWM; // the W-block count is a compile-time constant
 }
 
 int find_variant(const convt_plan &P, Layout *Lout = nullptr) {
