@@ -45,6 +45,11 @@ __device__ __forceinline__ f4 load4u(const float *p) {
     return v;
 }
 
+// Tuning knob: minimum waves per SIMD the register allocation must allow.
+#ifndef CONVT_IG_WAVES_PER_EU
+#define CONVT_IG_WAVES_PER_EU 3
+#endif
+
 constexpr int kMaxClasses = 16;
 constexpr int kTapMax = 4; // per-axis taps per class the table holds
 constexpr int kMaxSW = 8;
@@ -173,7 +178,8 @@ __device__ __forceinline__ void stage_store(float *buf, const f4 (&r)[PER], unsi
 
 template <int CIG, int COG, int KW, int SW, int DW, int TDM, int THM, int NWBM, int PWM, int PER,
           bool FUSED>
-__global__ __launch_bounds__(COG * 4) void k_igemm3d(const Igemm3dParams P,
+__global__ __launch_bounds__(COG * 4)
+__attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const Igemm3dParams P,
                                                      const float *__restrict__ x,
                                                      const float *__restrict__ w,
                                                      const float *__restrict__ bias,
@@ -248,11 +254,29 @@ __global__ __launch_bounds__(COG * 4) void k_igemm3d(const Igemm3dParams P,
     const int64_t dhw_out = (int64_t)P.D_out * P.H_out * P.W_out;
     const int64_t lane_out = (int64_t)(16 * ct + 4 * g4) * dhw_out + SW * j;
 
+    // add_input of one row: lane_out + e*dhw_out + SW*(16t) + rr past the row base
+    auto fetch_add = [&](float (&a)[NWBM][4][SW], const RowPos &Q) {
+        const int64_t base = (int64_t)Q.n * P.C_out * dhw_out +
+                             ((int64_t)Q.od * P.H_out + Q.oh) * P.W_out + lane_out;
+#pragma unroll
+        for (int t = 0; t < NWBM; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int rr = 0; rr < SW; ++rr) {
+                    // clamp inside the row for lanes past its end
+                    const int ow = min(SW * (16 * t + j) + rr, P.W_out - 1) - SW * j;
+                    a[t][e][rr] = add[base + e * dhw_out + ow];
+                }
+    };
+
     f4 pre[PER];
     unsigned pvalid;
+    float av[NWBM][4][SW], avn[NWBM][4][SW];
     RowPos R = decode_row(P, cls, r_begin);
     __syncthreads(); // LDS zeroed before the first row lands
     stage_fetch<PER>(pre, pvalid, M, P, x, td, th, cd0, cd1, ch0, ch1, R);
+    if constexpr (FUSED) fetch_add(av, R);
     stage_store<PER>(lds[0], pre, pvalid, M);
     __syncthreads();
 
@@ -263,25 +287,11 @@ __global__ __launch_bounds__(COG * 4) void k_igemm3d(const Igemm3dParams P,
         // this row's output base (uniform); lane adds lane_out + e*dhw_out + 16 SW t
         const int64_t row_base = (int64_t)R.n * P.C_out * dhw_out +
                                  ((int64_t)R.od * P.H_out + R.oh) * P.W_out;
-        float av[NWBM][4][SW];
-        if constexpr (FUSED) {
-            const float *arow = add + row_base + lane_out;
-#pragma unroll
-            for (int t = 0; t < NWBM; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-#pragma unroll
-                    for (int rr = 0; rr < SW; ++rr) {
-                        // clamp inside the row for lanes past its end
-                        const int ow = min(SW * (16 * t + j) + rr, P.W_out - 1) - SW * j;
-                        av[t][e][rr] = arow[e * dhw_out + ow];
-                    }
-        }
-        RowPos Rn = R;
-        if (has_next) {
-            Rn = decode_row(P, cls, r + 1);
-            stage_fetch<PER>(pre, pvalid, M, P, x, td, th, cd0, cd1, ch0, ch1, Rn);
-        }
+        // inputs of the next row, issued unconditionally (the last row fetches
+        // itself again) so the wait counts stay exact: x rows, then add_input
+        const RowPos Rn = decode_row(P, cls, has_next ? r + 1 : r);
+        stage_fetch<PER>(pre, pvalid, M, P, x, td, th, cd0, cd1, ch0, ch1, Rn);
+        if constexpr (FUSED) fetch_add(avn, Rn);
 
         f4 acc[NPH][NWBM];
 #pragma unroll
@@ -369,6 +379,14 @@ __global__ __launch_bounds__(COG * 4) void k_igemm3d(const Igemm3dParams P,
         __syncthreads();
         buf ^= 1;
         R = Rn;
+        if constexpr (FUSED) {
+#pragma unroll
+            for (int t = 0; t < NWBM; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int rr = 0; rr < SW; ++rr) av[t][e][rr] = avn[t][e][rr];
+        }
     }
 }
 
