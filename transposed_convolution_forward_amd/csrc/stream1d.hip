@@ -141,10 +141,62 @@ __device__ __forceinline__ void tile_store_lds(float *lds, const f4 (&r)[(CIG * 
     }
 }
 
-// Output staging: each wave passes its 16 x 64S output block through LDS in
-// two halves of 8 rows (e in {2h, 2h+1}), so that every global store
-// instruction writes whole contiguous runs of rows (16S float4 per row).
-template <int S> constexpr int out_pitch() { return 64 * S + 4; }
+// Output run of one lane: for accumulator register e the lane holds the 4S
+// consecutive outputs run[4Sj, 4Sj + 4S) of row co = 16ct + 4g4 + e, where the
+// run of the work item starts at o_t = q0*S - p.  Rows may have any length, so
+// the run starts anywhere modulo 16 bytes; but the offset depends on the row
+// only through e (16ct + 4g4 is a multiple of 4), so it is uniform over the
+// wave.  The lane stores S float4 chunks aligned to 16 bytes,
+// run[4Sj + hd + 4c, +4) (hd = elements before the first aligned address),
+// taking the first hd values of lane j+1 through a row shift; lane 0 stores the
+// head run[0, hd) and lane 15 the tail instead of its last chunk.  Unaligned
+// 16-byte stores stream far slower than aligned ones on this part.
+__device__ __forceinline__ float shl1(float v) { // lane j gets lane j+1 of its row of 16
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x101, 0xf, 0xf, true));
+}
+
+template <int S, int HD, bool FUSED>
+__device__ __forceinline__ void store_run(float *yr, const float *ar, const float (&v)[4 * S],
+                                          int j) {
+    float nb[3];
+#pragma unroll
+    for (int u = 0; u < 3; ++u) nb[u] = HD > u ? shl1(v[u]) : 0.0f;
+    float *yl = yr + 4 * S * j;
+    const float *al = FUSED ? ar + 4 * S * j : nullptr;
+#pragma unroll
+    for (int c = 0; c < S; ++c) {
+        const int i0 = HD + 4 * c;
+        if (HD > 0 && c == S - 1 && j == 15) {
+            // tail of the run: its elements before the next item's run
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (i0 + u < 4 * S) {
+                    const float a = FUSED ? al[i0 + u] : 0.0f;
+                    yl[i0 + u] = FUSED ? times_hardswish(v[i0 + u] + a) : v[i0 + u];
+                }
+        } else {
+            float t[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) t[u] = i0 + u < 4 * S ? v[i0 + u] : nb[i0 + u - 4 * S];
+            f4 out = f4{t[0], t[1], t[2], t[3]};
+            if constexpr (FUSED) {
+                const f4 a4 = load4u(al + i0); // add_input may be aligned differently from y
+                out.x = times_hardswish(out.x + a4.x);
+                out.y = times_hardswish(out.y + a4.y);
+                out.z = times_hardswish(out.z + a4.z);
+                out.w = times_hardswish(out.w + a4.w);
+            }
+            *reinterpret_cast<f4 *>(yl + i0) = out; // 16-byte aligned
+        }
+    }
+    if (HD > 0 && j == 0) { // head of the run
+#pragma unroll
+        for (int u = 0; u < HD; ++u) {
+            const float a = FUSED ? ar[u] : 0.0f;
+            yr[u] = FUSED ? times_hardswish(v[u] + a) : v[u];
+        }
+    }
+}
 
 // Tuning knobs: minimum waves per SIMD the register allocation must allow,
 // and resident workgroups aimed for per CU when sizing the grid.
@@ -172,15 +224,10 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
     constexpr int NT = COG * 4; // threads per workgroup
     constexpr int NP = Ph::count() > 0 ? Ph::count() : 1;
     constexpr int PER = (CIG * kRowF4 + NT - 1) / NT;
-    constexpr int PO = out_pitch<S>();
-    constexpr int RUN4 = 16 * S;        // float4 per output row of one work item
-    constexpr int ROUNDS = 8 * RUN4 / 64; // read-back rounds per half (= 2S)
     static_assert(CIG % 4 == 0 && COG % 16 == 0, "tile shape");
     static_assert(Ph::cmax() <= 4, "input shift beyond the 4-position halo");
-    static_assert((8 * RUN4) % 64 == 0, "read-back rounds");
 
     __shared__ __attribute__((aligned(16))) float lds[2][CIG * kPitch];
-    __shared__ __attribute__((aligned(16))) float stage[COT][8 * PO];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -202,10 +249,9 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
     tile_store_lds<CIG, NT>(lds[0], pre, P.L_in, (P.st_lo + st) * kTileQ, tid);
     __syncthreads();
 
-    float wr[K][NCIG];   // A operands: W[g*CIG + 4*cig + g4][16*ct + j][k]
-    float bo[2][ROUNDS]; // bias of the rows this lane stores in read-back
+    float wr[K][NCIG]; // A operands: W[g*CIG + 4*cig + g4][16*ct + j][k]
+    float br[4];       // bias of rows co = 16ct + 4g4 + e
     int buf = 0;
-    float *stg = stage[ct];
 
     // Runs of consecutive items of one group share the weights: load them once
     // per run, outside the loop that carries the prefetch.
@@ -218,13 +264,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
             for (int cig = 0; cig < NCIG; ++cig)
                 wr[k][cig] = w[((int64_t)(g * CIG + 4 * cig + g4) * COG + 16 * ct + j) * K + k];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int m = 0; m < ROUNDS; ++m) {
-                const int sr = (64 * m + lane) / RUN4; // staging row 0..7
-                const int col = 4 * (sr >> 1) + 2 * h + (sr & 1);
-                bo[h][m] = bias ? bias[g * COG + 16 * ct + col] : 0.0f;
-            }
+        for (int e = 0; e < 4; ++e) br[e] = bias ? bias[g * COG + 16 * ct + 4 * g4 + e] : 0.0f;
         // Wait for these loads here, before the loop: an empty asm that reads
         // and redefines the registers puts the wait in the preheader, so the
         // loop body never waits on them (which, vmcnt being in order, would
@@ -234,9 +274,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
 #pragma unroll
             for (int cig = 0; cig < NCIG; ++cig) asm volatile("" : "+v"(wr[k][cig]));
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int m = 0; m < ROUNDS; ++m) asm volatile("" : "+v"(bo[h][m]));
+        for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(br[e]));
 
     for (int rr = 0; rr < run; ++rr, ++ii) {
         const int n = ng / P.G;
@@ -275,86 +313,46 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
             }
         }
 
-        // Epilogue.  Lane (g4, j) holds, for row co_l = 4*g4 + e, the 4S
-        // outputs o = (q0 + 4j + t)*S + r - p (t = 0..3, r = 0..S-1).  They go
-        // to the staging rows, then come back as float4 runs of whole rows:
-        // the item's outputs of one row are o_t .. o_t + 64S - 1, o_t = q0*S - p.
+        // Epilogue: see store_run.  Rows co = g*COG + 16ct + 4g4 + e; the item's
+        // outputs of a row are o_t .. o_t + 64S - 1, o_t = q0*S - p.
         const int o_t = q0 * S - P.p;
-        const int64_t row0 = ((int64_t)n * P.C_out + (int64_t)g * COG + 16 * ct) * P.L_out;
+        const bool interior = (o_t >= 0) && (o_t + 64 * S <= P.L_out);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int e = 0; e < 4; ++e) {
+            const int64_t row = ((int64_t)n * P.C_out + (int64_t)g * COG + 16 * ct + 4 * g4 + e) *
+                                P.L_out;
+            float *yr = y + row + o_t;
+            const float *ar = FUSED ? add + row + o_t : nullptr;
+            float v[4 * S];
 #pragma unroll
-            for (int e2 = 0; e2 < 2; ++e2) {
-                const int e = 2 * h + e2;
-                float v[4 * S];
+            for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+                for (int r = 0; r < S; ++r) {
+                    float a = 0.0f;
+                    if constexpr (Ph::count() > 0)
+                        if (Ph::nonempty(r)) a = acc[Ph::slot(r)][t][e];
+                    v[t * S + r] = a + br[e];
+                }
+            if (interior) {
+                // elements before the first 16-byte boundary (same on every lane)
+                const int hd = __builtin_amdgcn_readfirstlane(
+                    (int)((0u - (unsigned)(uintptr_t)yr) >> 2) & 3);
+                switch (hd) {
+                case 0: store_run<S, 0, FUSED>(yr, ar, v, j); break;
+                case 1: store_run<S, 1, FUSED>(yr, ar, v, j); break;
+                case 2: store_run<S, 2, FUSED>(yr, ar, v, j); break;
+                default: store_run<S, 3, FUSED>(yr, ar, v, j); break;
+                }
+            } else {
 #pragma unroll
-                    for (int r = 0; r < S; ++r) {
-                        float a = 0.0f;
-                        if constexpr (Ph::count() > 0)
-                            if (Ph::nonempty(r)) a = acc[Ph::slot(r)][t][e];
-                        v[t * S + r] = a;
-                    }
-                float *dst = stg + (2 * g4 + e2) * PO + 4 * S * j;
-#pragma unroll
-                for (int u = 0; u < S; ++u)
-                    *reinterpret_cast<f4 *>(dst + 4 * u) =
-                        f4{v[4 * u], v[4 * u + 1], v[4 * u + 2], v[4 * u + 3]};
-            }
-            // the same wave reads back what it wrote: LDS operations of one
-            // wave complete in order; keep the compiler from reordering them
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // Read-back: RUN4 lanes per staging row.  Rows have any length, so
-            // a row's run starts anywhere mod 16 bytes; the lanes store only the
-            // 16-byte-aligned float4 chunks inside the run (unaligned 16-byte
-            // stores stream far slower) and the last lane of the row stores the
-            // head and tail elements around them.
-            const bool interior = (o_t >= 0) && (o_t + 64 * S <= P.L_out);
-#pragma unroll
-            for (int m = 0; m < ROUNDS; ++m) {
-                const int f = 64 * m + lane;
-                const int sr = f / RUN4, c4 = f % RUN4;
-                const int col = 4 * (sr >> 1) + 2 * h + (sr & 1);
-                float *yr = y + row0 + (int64_t)col * P.L_out + o_t; // run start
-                const float *ar = FUSED ? add + row0 + (int64_t)col * P.L_out + o_t : nullptr;
-                const float *lr = stg + sr * PO;                    // run in LDS
-                const float bv = bo[h][m];
-                if (interior) {
-                    const int hd = (int)((0u - (unsigned)(uintptr_t)yr) >> 2) & 3; // head length
-                    if (hd == 0 || c4 < RUN4 - 1) {
-                        const int i = hd + 4 * c4;
-                        f4 a4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
-                        if constexpr (FUSED) a4 = load4u(ar + i);
-                        f4 out;
-                        out.x = epilogue<FUSED>(lr[i + 0], bv, a4.x);
-                        out.y = epilogue<FUSED>(lr[i + 1], bv, a4.y);
-                        out.z = epilogue<FUSED>(lr[i + 2], bv, a4.z);
-                        out.w = epilogue<FUSED>(lr[i + 3], bv, a4.w);
-                        store4u(yr + i, out);
-                    } else {
-                        // head [0, hd) and tail [hd + 4*(RUN4-1), 64S): 4 elements
-#pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            const int i = u < hd ? u : 4 * (RUN4 - 1) + u;
-                            yr[i] = epilogue<FUSED>(lr[i], bv, FUSED ? ar[i] : 0.0f);
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int i = 4 * c4 + u;
-                        const int o = o_t + i;
-                        if (o >= 0 && o < P.L_out)
-                            yr[i] = epilogue<FUSED>(lr[i], bv, FUSED ? ar[i] : 0.0f);
+                for (int u = 0; u < 4 * S; ++u) {
+                    const int o = o_t + 4 * S * j + u;
+                    if (o >= 0 && o < P.L_out) {
+                        const float a = FUSED ? ar[4 * S * j + u] : 0.0f;
+                        yr[4 * S * j + u] = FUSED ? times_hardswish(v[u] + a) : v[u];
                     }
                 }
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
 
         if (has_next) tile_store_lds<CIG, NT>(lds[buf ^ 1], pre, P.L_in, (P.st_lo + st1) * kTileQ, tid);
