@@ -55,6 +55,15 @@ REDUCED = [
                (1, 1, 1), (1, 1, 1), False, False, wid=3104),
     S.Workload("ig_k3s2_w20", 3, 1, 32, 64, 1, (2, 3, 20), (3, 3, 3), (2, 2, 2), (1, 1, 1),
                (1, 1, 1), (1, 1, 1), True, True, wid=3105),
+    # channel-heavy shapes (weights streamed through LDS): two W-blocks, a
+    # ragged last W-block, 64 input channels, fused
+    reduced(S.HEAVY_3D, N=1, in_size=(3, 4, 32)),
+    S.Workload("igw_c128_p2", 3, 1, 128, 64, 1, (3, 3, 32), (4, 4, 4), (2, 2, 2), (2, 1, 2),
+               (1, 0, 0), (1, 1, 1), True, False, wid=3201),
+    S.Workload("igw_c64_fused", 3, 2, 64, 64, 1, (2, 5, 32), (4, 4, 4), (2, 2, 2), (1, 1, 1),
+               (0, 0, 0), (1, 1, 1), True, True, wid=3202),
+    S.Workload("igw_c128_w16_nobias", 3, 1, 128, 64, 1, (5, 2, 16), (4, 4, 4), (2, 2, 2), (1, 1, 1),
+               (0, 1, 0), (1, 1, 1), False, False, wid=3203),
 ]
 
 

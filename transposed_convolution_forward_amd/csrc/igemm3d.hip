@@ -390,6 +390,229 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     }
 }
 
+// ---------------------------------------------------------------- wide variant
+// Channel-heavy layers: the class's weights (C_in x C_out x taps) do not fit in
+// VGPRs, so they stream through LDS.  A workgroup of 4 waves owns 4 output
+// rows of one class (wave w: row w, all 64 output channels x NWB W-blocks, 16
+// accumulator tiles).  The contraction runs over stages (D/H tap slot x chunk
+// of CC input channels); each stage stages the weight chunk, transposed to
+// [kw][ci][co] so the A operands (W^T: 16 co x 4 ci) read without bank
+// conflicts, and the 4 rows' input rows, double-buffered.  Per (ci quad, kw):
+// 4 A reads and NWB B reads feed 4*NWB MFMAs.
+constexpr int kWidePWC = 80; // co pitch of the staged weights (16 mod 32 spreads the ci rows)
+
+// Row q (0..3) of four held in separate variables, by selects (an array
+// indexed with a per-lane value would live in scratch memory).
+__device__ __forceinline__ int sel4(int q, int a, int b, int c, int d) {
+    return q == 0 ? a : q == 1 ? b : q == 2 ? c : d;
+}
+__device__ __forceinline__ RowPos pick_row(int q, const RowPos &A, const RowPos &B, const RowPos &C,
+                                           const RowPos &D) {
+    RowPos o;
+    o.n = sel4(q, A.n, B.n, C.n, D.n);
+    o.qd = sel4(q, A.qd, B.qd, C.qd, D.qd);
+    o.qh = sel4(q, A.qh, B.qh, C.qh, D.qh);
+    o.od = sel4(q, A.od, B.od, C.od, D.od);
+    o.oh = sel4(q, A.oh, B.oh, C.oh, D.oh);
+    return o;
+}
+
+template <int CIG, int KW, int SW, int DW, int NWB, int CC, int PWX, bool FUSED>
+__global__ __launch_bounds__(256) void k_igemm3d_wide(const Igemm3dParams P,
+                                                      const float *__restrict__ x,
+                                                      const float *__restrict__ w,
+                                                      const float *__restrict__ bias,
+                                                      const float *add, float *y) {
+    using Ph = WPhases<KW, SW, DW>;
+    constexpr int COG = 64;
+    constexpr int NT = 256;
+    constexpr int NCH = CIG / CC;          // channel chunks
+    constexpr int NPH = Ph::count() > 0 ? Ph::count() : 1;
+    constexpr int WPAIRS = CC * COG;       // (ci, co) pairs of a weight chunk
+    constexpr int WPER = WPAIRS / NT;      // per thread
+    constexpr int XPER = (4 * CC * 8 + NT - 1) / NT; // input rows: 4 rows x CC x (W_in/4 <= 8)
+    static_assert(CIG % CC == 0 && CC % 4 == 0 && WPAIRS % NT == 0, "chunking");
+    static_assert(KW <= 4, "kernel taps along W");
+
+    __shared__ __attribute__((aligned(16))) float Wl[2][KW][CC][kWidePWC];
+    __shared__ __attribute__((aligned(16))) float Xl[2][4][CC][PWX];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6; // wave = row of the block
+    const int j = lane & 15;
+    const int g4 = lane >> 4;
+
+    int cls = 0;
+    while (cls + 1 < P.n_class && (int)blockIdx.x >= P.cls_block0[cls + 1]) ++cls;
+    const int r0 = ((int)blockIdx.x - P.cls_block0[cls]) * 4;
+    const int nrows = min(4, P.cls_rows[cls] - r0);
+    if (nrows <= 0) return;
+    const int td = P.cls_td[cls], th = P.cls_th[cls];
+    const int nslots = td * th;
+    const int nstages = nslots * NCH;
+    const int W4 = P.W_in >> 2;
+
+    for (int i = tid; i < 2 * 4 * CC * PWX; i += NT) (&Xl[0][0][0][0])[i] = 0.0f;
+
+    const RowPos R0 = decode_row(P, cls, r0);
+    const RowPos R1 = decode_row(P, cls, r0 + min(1, nrows - 1));
+    const RowPos R2 = decode_row(P, cls, r0 + min(2, nrows - 1));
+    const RowPos R3 = decode_row(P, cls, r0 + min(3, nrows - 1));
+
+    f4 wpre[WPER][1];
+    float wsc[WPER][KW];
+    f4 xpre[XPER];
+    unsigned xvalid = 0;
+
+    auto fetch = [&](int sidx) {
+        const int slot = sidx / NCH, ch = sidx - slot * NCH;
+        const int jd = slot / th, jh = slot - jd * th;
+        const int kd = P.cls_kd[cls][jd], kh = P.cls_kh[cls][jh];
+        const int cd = P.cls_cd[cls][jd], chh = P.cls_ch[cls][jh];
+#pragma unroll
+        for (int u = 0; u < WPER; ++u) {
+            const int pr = tid + u * NT;
+            const int cil = pr / COG, co = pr - cil * COG;
+            const float *src =
+                w + ((((int64_t)(ch * CC + cil) * COG + co) * P.KD + kd) * P.KH + kh) * KW;
+            if constexpr (KW == 4) {
+                wpre[u][0] = load4u(src);
+            } else {
+#pragma unroll
+                for (int k = 0; k < KW; ++k) wsc[u][k] = src[k];
+            }
+        }
+        xvalid = 0;
+#pragma unroll
+        for (int u = 0; u < XPER; ++u) {
+            const int f = tid + u * NT;
+            const int rr = f / (CC * W4);
+            const int rem = f - rr * (CC * W4);
+            const int cil = rem / W4, c4 = rem - cil * W4;
+            const RowPos R = pick_row(rr, R0, R1, R2, R3);
+            const int id = R.qd - cd, ih = R.qh - chh;
+            const bool ok = f < 4 * CC * W4 && rr < nrows && id >= 0 && id < P.D_in && ih >= 0 &&
+                            ih < P.H_in;
+            const int64_t off =
+                ok ? ((((int64_t)R.n * P.C_in + ch * CC + cil) * P.D_in + id) * P.H_in + ih) *
+                             P.W_in + 4 * c4
+                   : 0;
+            xpre[u] = load4u(x + off);
+            xvalid |= ok ? (1u << u) : 0u;
+        }
+    };
+    auto stash = [&](int b) {
+#pragma unroll
+        for (int u = 0; u < WPER; ++u) {
+            const int pr = tid + u * NT;
+            const int cil = pr / COG, co = pr - cil * COG;
+            if constexpr (KW == 4) {
+                Wl[b][0][cil][co] = wpre[u][0].x;
+                Wl[b][1][cil][co] = wpre[u][0].y;
+                Wl[b][2][cil][co] = wpre[u][0].z;
+                Wl[b][3][cil][co] = wpre[u][0].w;
+            } else {
+#pragma unroll
+                for (int k = 0; k < KW; ++k) Wl[b][k][cil][co] = wsc[u][k];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < XPER; ++u) {
+            const int f = tid + u * NT;
+            if (f < 4 * CC * W4) {
+                const int rr = f / (CC * W4);
+                const int rem = f - rr * (CC * W4);
+                const int cil = rem / W4, c4 = rem - cil * W4;
+                const f4 v = (xvalid >> u) & 1u ? xpre[u] : f4{0.0f, 0.0f, 0.0f, 0.0f};
+                *reinterpret_cast<f4 *>(&Xl[b][rr][cil][4 * c4 - P.iw_lo]) = v;
+            }
+        }
+    };
+
+    f4 acc[4][NPH][NWB];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int ph = 0; ph < NPH; ++ph)
+#pragma unroll
+            for (int t = 0; t < NWB; ++t) acc[m][ph][t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    __syncthreads(); // halo zeros in place
+    if (nstages > 0) {
+        fetch(0);
+        stash(0);
+    }
+    __syncthreads();
+    const bool active = wv < nrows;
+    for (int sidx = 0; sidx < nstages; ++sidx) {
+        const int b = sidx & 1;
+        const bool has_next = sidx + 1 < nstages;
+        if (has_next) fetch(sidx + 1);
+        if (active && Ph::count() > 0) {
+#pragma unroll
+            for (int cig = 0; cig < CC / 4; ++cig) {
+#pragma unroll
+                for (int kw = 0; kw < KW; ++kw) {
+                    const int rw = Ph::r_of(kw);
+                    const int ph = Ph::slot(rw);
+                    const int c = Ph::c_of(kw);
+                    float a[4];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) a[m] = Wl[b][kw][4 * cig + g4][16 * m + j];
+#pragma unroll
+                    for (int t = 0; t < NWB; ++t) {
+                        const float bv = Xl[b][wv][4 * cig + g4][P.qw0[rw] + 16 * t + j - c - P.iw_lo];
+#pragma unroll
+                        for (int m = 0; m < 4; ++m)
+                            acc[m][ph][t] =
+                                __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], bv, acc[m][ph][t], 0, 0, 0);
+                    }
+                }
+            }
+        }
+        if (has_next) stash(b ^ 1);
+        __syncthreads();
+    }
+
+    if (!active) return;
+    const RowPos R = pick_row(__builtin_amdgcn_readfirstlane(wv), R0, R1, R2, R3);
+    const int64_t dhw_out = (int64_t)P.D_out * P.H_out * P.W_out;
+    const int64_t row_base =
+        (int64_t)R.n * COG * dhw_out + ((int64_t)R.od * P.H_out + R.oh) * P.W_out;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int co = 16 * m + 4 * g4 + e;
+            const float bco = bias ? bias[co] : 0.0f;
+#pragma unroll
+            for (int t = 0; t < NWB; ++t) {
+                const int ow0 = SW * (16 * t + j);
+                float v[SW];
+#pragma unroll
+                for (int rr = 0; rr < SW; ++rr) v[rr] = 0.0f;
+#pragma unroll
+                for (int rw = 0; rw < SW; ++rw)
+                    if constexpr (Ph::count() > 0)
+                        if (Ph::nonempty(rw)) {
+                            const float a = acc[m][Ph::slot(rw)][t][e];
+#pragma unroll
+                            for (int rr = 0; rr < SW; ++rr)
+                                if (P.sigma[rw] == rr) v[rr] = a;
+                        }
+                const int64_t o = row_base + (int64_t)co * dhw_out + ow0;
+#pragma unroll
+                for (int rr = 0; rr < SW; ++rr) {
+                    if (ow0 + rr < P.W_out) {
+                        const float a1 = FUSED ? add[o + rr] : 0.0f;
+                        y[o + rr] = epilogue<FUSED>(v[rr], bco, a1);
+                    }
+                }
+            }
+        }
+}
+
 // ---------------------------------------------------------------- host side
 struct Variant {
     int cig, cog, KW, SW, DW, TDM, THM, NWBM, PWM, W4M;
@@ -461,11 +684,10 @@ int num_cus() {
     return cus;
 }
 
-template <int CIG, int COG, int KW, int SW, int DW, int TDM, int THM, int NWBM, int PWM, int W4M>
-int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const float *w,
-                   const float *bias, const float *add, float *y, hipStream_t st) {
+// Fills P from the plan and the W layout: sizes, W phases and the class table
+// (classes ordered heaviest first).  Returns the total number of output rows.
+int64_t fill_params(const convt_plan &Pl, const Layout &L, int SW, Igemm3dParams &P) {
     const AxisPlan &AD = Pl.ax[0], &AH = Pl.ax[1], &AW = Pl.ax[2];
-    Igemm3dParams P;
     memset(&P, 0, sizeof(P));
     P.C_in = (int)Pl.C_in;
     P.C_out = (int)Pl.C_out;
@@ -485,7 +707,6 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
         P.qw0[r] = L.qw0[r];
         P.sigma[r] = L.sigma[r];
     }
-    // classes (rd, rh) with at least one output row, heaviest first
     struct Cls {
         int rd, rh, taps;
     } cl[kMaxClasses];
@@ -531,20 +752,34 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
         total_rows += P.cls_rows[c];
     }
     P.n_class = kept;
-    // rows per block: enough blocks to fill the CUs several times over
-    const int64_t target_blocks = (int64_t)num_cus() * 16;
-    int rpb = (int)std::max<int64_t>(1, std::min<int64_t>(64, total_rows / target_blocks));
+    return total_rows;
+}
+
+// Blocks of rpb rows per class; returns the grid size.
+int assign_blocks(Igemm3dParams &P, int rpb) {
     P.rows_per_block = rpb;
     int blocks = 0;
-    for (int c = 0; c < kept; ++c) {
+    for (int c = 0; c < P.n_class; ++c) {
         P.cls_block0[c] = blocks;
         blocks += (P.cls_rows[c] + rpb - 1) / rpb;
     }
-    P.cls_block0[kept] = blocks;
+    P.cls_block0[P.n_class] = blocks;
+    return blocks;
+}
+
+template <int CIG, int COG, int KW, int SW, int DW, int TDM, int THM, int NWBM, int PWM, int W4M>
+int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const float *w,
+                   const float *bias, const float *add, float *y, hipStream_t st) {
+    Igemm3dParams P;
+    const int64_t total_rows = fill_params(Pl, L, SW, P);
+    // rows per block: enough blocks to fill the CUs several times over
+    const int64_t target_blocks = (int64_t)num_cus() * 16;
+    const int rpb = (int)std::max<int64_t>(1, std::min<int64_t>(64, total_rows / target_blocks));
+    const int blocks = assign_blocks(P, rpb);
     if (blocks == 0) return 0;
     constexpr int NT = COG * 4;
     constexpr int PER = (TDM * THM * CIG * W4M + NT - 1) / NT; // W_in <= 4*W4M is checked
-    const int need_f = TDM * THM * CIG * (AW.L_in / 4);
+    const int need_f = TDM * THM * CIG * (Pl.ax[2].L_in / 4);
     if (need_f > PER * NT) return (int)hipErrorInvalidValue;
     if (add)
         hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, true>),
@@ -555,12 +790,59 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
     return (int)hipGetLastError();
 }
 
+struct WideVariant {
+    int cig, KW, SW, DW, NWB, CC, PWX;
+};
+constexpr WideVariant kWide[] = {
+    {128, 4, 2, 1, 2, 16, 48}, // 128 -> 64 channels, kernel 4, stride 2, rows of 64 outputs
+    {128, 4, 2, 1, 1, 16, 48}, // same, rows of 32 outputs
+    {64, 4, 2, 1, 2, 16, 48},  // 64 -> 64 channels
+};
+constexpr int kNumWide = (int)(sizeof(kWide) / sizeof(kWide[0]));
+
+int find_wide(const convt_plan &P, Layout *Lout) {
+    if (P.ndim != 3 || P.G != 1 || P.Cog != 64) return -1;
+    const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
+    if (AW.L_in % 4 != 0 || AW.L_in / 4 > 8) return -1;
+    if (AD.s * AH.s > kMaxClasses) return -1;
+    int tdm = 0, thm = 0;
+    for (int r = 0; r < AD.s; ++r) tdm = std::max(tdm, AD.tap_start[r + 1] - AD.tap_start[r]);
+    for (int r = 0; r < AH.s; ++r) thm = std::max(thm, AH.tap_start[r + 1] - AH.tap_start[r]);
+    if (tdm > 2 || thm > 2) return -1;
+    for (int i = 0; i < kNumWide; ++i) {
+        const WideVariant &v = kWide[i];
+        if (P.Cig != v.cig) continue;
+        const Variant vv = {v.cig, 64, v.KW, v.SW, v.DW, 2, 2, v.NWB, v.PWX, 8};
+        Layout L;
+        if (!w_layout(P, vv, L)) continue;
+        if (Lout) *Lout = L;
+        return i;
+    }
+    return -1;
+}
+
+template <int CIG, int KW, int SW, int DW, int NWB, int CC, int PWX>
+int launch_wide(const convt_plan &Pl, const Layout &L, const float *x, const float *w,
+                const float *bias, const float *add, float *y, hipStream_t st) {
+    Igemm3dParams P;
+    fill_params(Pl, L, SW, P);
+    const int blocks = assign_blocks(P, 4);
+    if (blocks == 0) return 0;
+    if (add)
+        hipLaunchKernelGGL((k_igemm3d_wide<CIG, KW, SW, DW, NWB, CC, PWX, true>), dim3(blocks),
+                           dim3(256), 0, st, P, x, w, bias, add, y);
+    else
+        hipLaunchKernelGGL((k_igemm3d_wide<CIG, KW, SW, DW, NWB, CC, PWX, false>), dim3(blocks),
+                           dim3(256), 0, st, P, x, w, bias, add, y);
+    return (int)hipGetLastError();
+}
+
 } // namespace
 
 bool igemm3d_supports(const convt_plan &P) {
     if (P.ndim != 3) return false;
     Layout L;
-    if (find_variant(P, &L) < 0) return false;
+    if (find_variant(P, &L) < 0 && find_wide(P, &L) < 0) return false;
     return P.N * P.ax[0].L_out * P.ax[1].L_out < (int64_t(1) << 31);
 }
 
@@ -573,6 +855,12 @@ int launch_igemm3d(const convt_plan &Pl, const float *x, const float *w, const f
     case 0: return launch_variant<32, 64, 3, 2, 1, 2, 2, 1, kPW, 4>(Pl, L, x, w, bias, add, y, st);
     case 1: return launch_variant<32, 64, 3, 2, 1, 2, 2, 2, kPW, 8>(Pl, L, x, w, bias, add, y, st);
     case 2: return launch_variant<16, 32, 4, 2, 1, 2, 2, 2, kPW, 8>(Pl, L, x, w, bias, add, y, st);
+    default: break;
+    }
+    switch (find_wide(Pl, &L)) {
+    case 0: return launch_wide<128, 4, 2, 1, 2, 16, 48>(Pl, L, x, w, bias, add, y, st);
+    case 1: return launch_wide<128, 4, 2, 1, 1, 16, 48>(Pl, L, x, w, bias, add, y, st);
+    case 2: return launch_wide<64, 4, 2, 1, 2, 16, 48>(Pl, L, x, w, bias, add, y, st);
     default: return (int)hipErrorInvalidValue;
     }
 }
