@@ -849,7 +849,7 @@ bool igemm3d_supports(const convt_plan &P) {
 int launch_igemm3d(const convt_plan &Pl, const float *x, const float *w, const float *bias,
                    const float *add, float *y, void *stream) {
     Layout L;
-    const int v = find_variant(Pl, &L);
+    const int v = find_variant(Pl, &L); // weights in VGPRs when they fit, else streamed
     hipStream_t st = (hipStream_t)stream;
     switch (v) {
     case 0: return launch_variant<32, 64, 3, 2, 1, 2, 2, 1, kPW, 4>(Pl, L, x, w, bias, add, y, st);
