@@ -141,62 +141,21 @@ __device__ __forceinline__ void tile_store_lds(float *lds, const f4 (&r)[(CIG * 
     }
 }
 
-// Output run of one lane: for accumulator register e the lane holds the 4S
-// consecutive outputs run[4Sj, 4Sj + 4S) of row co = 16ct + 4g4 + e, where the
-// run of the work item starts at o_t = q0*S - p.  Rows may have any length, so
-// the run starts anywhere modulo 16 bytes; but the offset depends on the row
-// only through e (16ct + 4g4 is a multiple of 4), so it is uniform over the
-// wave.  The lane stores S float4 chunks aligned to 16 bytes,
-// run[4Sj + hd + 4c, +4) (hd = elements before the first aligned address),
-// taking the first hd values of lane j+1 through a row shift; lane 0 stores the
-// head run[0, hd) and lane 15 the tail instead of its last chunk.  Unaligned
-// 16-byte stores stream far slower than aligned ones on this part.
-__device__ __forceinline__ float shl1(float v) { // lane j gets lane j+1 of its row of 16
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x101, 0xf, 0xf, true));
-}
-
-template <int S, int HD, bool FUSED>
-__device__ __forceinline__ void store_run(float *yr, const float *ar, const float (&v)[4 * S],
-                                          int j) {
-    float nb[3];
-#pragma unroll
-    for (int u = 0; u < 3; ++u) nb[u] = HD > u ? shl1(v[u]) : 0.0f;
-    float *yl = yr + 4 * S * j;
-    const float *al = FUSED ? ar + 4 * S * j : nullptr;
-#pragma unroll
-    for (int c = 0; c < S; ++c) {
-        const int i0 = HD + 4 * c;
-        if (HD > 0 && c == S - 1 && j == 15) {
-            // tail of the run: its elements before the next item's run
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (i0 + u < 4 * S) {
-                    const float a = FUSED ? al[i0 + u] : 0.0f;
-                    yl[i0 + u] = FUSED ? times_hardswish(v[i0 + u] + a) : v[i0 + u];
-                }
-        } else {
-            float t[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) t[u] = i0 + u < 4 * S ? v[i0 + u] : nb[i0 + u - 4 * S];
-            f4 out = f4{t[0], t[1], t[2], t[3]};
-            if constexpr (FUSED) {
-                const f4 a4 = load4u(al + i0); // add_input may be aligned differently from y
-                out.x = times_hardswish(out.x + a4.x);
-                out.y = times_hardswish(out.y + a4.y);
-                out.z = times_hardswish(out.z + a4.z);
-                out.w = times_hardswish(out.w + a4.w);
-            }
-            *reinterpret_cast<f4 *>(yl + i0) = out; // 16-byte aligned
-        }
-    }
-    if (HD > 0 && j == 0) { // head of the run
-#pragma unroll
-        for (int u = 0; u < HD; ++u) {
-            const float a = FUSED ? ar[u] : 0.0f;
-            yr[u] = FUSED ? times_hardswish(v[u] + a) : v[u];
-        }
-    }
-}
+// Output lines.  Rows may have any length, so the outputs o_t .. o_t + 64S - 1
+// of a work item start anywhere in a 64-byte line, at a different place in
+// every row; stored as they stand, the line at each end of the run is split
+// between two items written microseconds apart, and such partly written lines
+// drain to HBM far slower than whole ones.  So for each row an item stores the
+// 64S outputs from the line boundary at or before o_t: the first a of them
+// (0 <= a < 16, the offset of o_t in its line) are the previous item's last
+// outputs, carried over, and its own last a outputs are carried to the next
+// item.  The row-dependent shift by a and the carry pass through LDS that
+// belongs to one wave (no barrier): a staging row per accumulator row group,
+// holding the carry at [16 - a, 16) and the item's outputs at [16, 16 + 64S),
+// and a 16-float carry slot per output row.  Store c of lane j then writes
+// the 16 bytes at 64c + 4j of its row's segment, so one store instruction
+// covers four rows with 256 contiguous, line-aligned bytes each.
+template <int S> constexpr int stage_pitch() { return 16 + 64 * S + 4; } // +4: spread banks
 
 // Tuning knobs: minimum waves per SIMD the register allocation must allow,
 // and resident workgroups aimed for per CU when sizing the grid.
@@ -228,6 +187,8 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
     static_assert(Ph::cmax() <= 4, "input shift beyond the 4-position halo");
 
     __shared__ __attribute__((aligned(16))) float lds[2][CIG * kPitch];
+    __shared__ __attribute__((aligned(16))) float ostage[COT][4][stage_pitch<S>()];
+    __shared__ float ocarry[COT][16][16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -252,6 +213,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
     float wr[K][NCIG]; // A operands: W[g*CIG + 4*cig + g4][16*ct + j][k]
     float br[4];       // bias of rows co = 16ct + 4g4 + e
     int buf = 0;
+    bool chain = false; // the previous item left its last outputs of each row in ocarry
 
     // Runs of consecutive items of one group share the weights: load them once
     // per run, outside the loop that carries the prefetch.
@@ -313,10 +275,30 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
             }
         }
 
-        // Epilogue: see store_run.  Rows co = g*COG + 16ct + 4g4 + e; the item's
-        // outputs of a row are o_t .. o_t + 64S - 1, o_t = q0*S - p.
+        // The next tile goes to the other LDS buffer (free since the last
+        // barrier) before this item's stores are issued: the one vector-memory
+        // counter retires loads and stores in issue order, so the wait for the
+        // prefetch must not come after the stores.  The write is unconditional
+        // (after the last item it copies stale registers into a buffer nobody
+        // reads): were it conditional, the compiler would keep the prefetch
+        // pending along the skipping path and wait for it, and with it for every
+        // store, before the next fetch.
+#pragma unroll
+        for (int u = 0; u < PER; ++u) asm volatile("" : "+v"(pre[u])); // every prefetch landed here
+        tile_store_lds<CIG, NT>(lds[buf ^ 1], pre, P.L_in, (P.st_lo + st1) * kTileQ, tid);
+
+        // Epilogue (see stage_pitch).  Rows co = g*COG + 16ct + 4g4 + e; the
+        // item's outputs of a row are o_t .. o_t + 64S - 1, o_t = q0*S - p.
+        // Items touching a row end take a guarded element-wise path and break
+        // the carry chain: the item before flushes its carry itself, the one
+        // after leaves the first a outputs of its segment alone.
         const int o_t = q0 * S - P.p;
         const bool interior = (o_t >= 0) && (o_t + 64 * S <= P.L_out);
+        const bool chain_in = chain;
+        const bool chain_out =
+            interior && has_next && st1 != 0 && o_t + 128 * S <= P.L_out; // next: same rows, interior
+        chain = chain_out;
+        float *srow = &ostage[ct][g4][0];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int64_t row = ((int64_t)n * P.C_out + (int64_t)g * COG + 16 * ct + 4 * g4 + e) *
@@ -334,15 +316,42 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
                     v[t * S + r] = a + br[e];
                 }
             if (interior) {
-                // elements before the first 16-byte boundary (same on every lane)
-                const int hd = __builtin_amdgcn_readfirstlane(
-                    (int)((0u - (unsigned)(uintptr_t)yr) >> 2) & 3);
-                switch (hd) {
-                case 0: store_run<S, 0, FUSED>(yr, ar, v, j); break;
-                case 1: store_run<S, 1, FUSED>(yr, ar, v, j); break;
-                case 2: store_run<S, 2, FUSED>(yr, ar, v, j); break;
-                default: store_run<S, 3, FUSED>(yr, ar, v, j); break;
+                if constexpr (FUSED) {
+#pragma unroll
+                    for (int c = 0; c < S; ++c) {
+                        const f4 a4 = load4u(ar + 4 * S * j + 4 * c); // add_input: any alignment
+                        v[4 * c + 0] = times_hardswish(v[4 * c + 0] + a4.x);
+                        v[4 * c + 1] = times_hardswish(v[4 * c + 1] + a4.y);
+                        v[4 * c + 2] = times_hardswish(v[4 * c + 2] + a4.z);
+                        v[4 * c + 3] = times_hardswish(v[4 * c + 3] + a4.w);
+                    }
                 }
+                const int a = (int)(((uintptr_t)yr >> 2) & 15); // o_t's offset in its line
+                float *cr = &ocarry[ct][4 * g4 + e][0];
+                if (chain_in) srow[j] = cr[j];
+#pragma unroll
+                for (int c = 0; c < S; ++c)
+                    *reinterpret_cast<f4 *>(srow + 16 + 4 * S * j + 4 * c) =
+                        f4{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
+                if (chain_out) cr[j] = srow[64 * S + j];
+                float *ys = yr - a;               // line-aligned segment start
+                const float *ss = srow + 16 - a;  // segment in the staging row
+#pragma unroll
+                for (int c = 0; c < S; ++c) {
+                    const int s0 = 64 * c + 4 * j;
+                    const f4 val = f4{ss[s0], ss[s0 + 1], ss[s0 + 2], ss[s0 + 3]};
+                    if (c > 0 || chain_in) {
+                        *reinterpret_cast<f4 *>(ys + s0) = val;
+                    } else { // chain start: the segment's first a outputs are not this item's
+                        if (s0 >= a) *reinterpret_cast<f4 *>(ys + s0) = val;
+                        else {
+                            if (s0 + 1 >= a) ys[s0 + 1] = val.y;
+                            if (s0 + 2 >= a) ys[s0 + 2] = val.z;
+                            if (s0 + 3 >= a) ys[s0 + 3] = val.w;
+                        }
+                    }
+                }
+                if (!chain_out && j < a) ys[64 * S + j] = ss[64 * S + j]; // chain end: the carry
             } else {
 #pragma unroll
                 for (int u = 0; u < 4 * S; ++u) {
@@ -355,7 +364,6 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
             }
         }
 
-        if (has_next) tile_store_lds<CIG, NT>(lds[buf ^ 1], pre, P.L_in, (P.st_lo + st1) * kTileQ, tid);
         __syncthreads();
         buf ^= 1;
         st = st1;
