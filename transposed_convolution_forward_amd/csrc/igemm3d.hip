@@ -29,6 +29,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <type_traits>
 #include <utility>
 
 #include "convt_internal.h"
@@ -116,64 +117,29 @@ __device__ __forceinline__ RowPos decode_row(const Igemm3dParams &P, int cls, in
     return R;
 }
 
-// Input rows of one output row: SLOTS x CIG rows of W_in floats (W4 float4
-// each).  Thread tid stages float4 number f = tid + u*NT; what f means does not
-// depend on the row, so it is decoded once (StageMap).  Fetches are
-// branch-free: invalid rows read a safe address and are zeroed at the LDS
-// write.
-template <int PER> struct StageMap {
-    int xoff[PER]; // ci*D_in*H_in*W_in + 4*c4
-    int loff[PER]; // LDS offset of the float4, -1 if f is past the last float4
-    int tap[PER];  // jd*4 + jh of the slot
-};
+// Buffer resources: a load past num_records returns zeros and a store past it
+// is dropped, so input rows outside the input need no select, and lanes past
+// a row end read harmlessly.  One resource per sample keeps every byte offset
+// within 31 bits (checked on the host).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000; // raw (untyped) buffer access
+constexpr unsigned kOutOfRange = 0x80000000u;
 
-template <int CIG, int THM, int NT, int PER, int PWM>
-__device__ __forceinline__ void stage_map(StageMap<PER> &M, const Igemm3dParams &P, int nslots,
-                                          int tid) {
-    const int W4 = P.W_in >> 2;
-    const int nf = nslots * CIG * W4;
-    const int dhw = P.D_in * P.H_in * P.W_in;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int f = tid + u * NT;
-        const int slot = f / (CIG * W4);
-        const int rem = f - slot * (CIG * W4);
-        const int ci = rem / W4, c4 = rem - ci * W4;
-        M.xoff[u] = ci * dhw + 4 * c4;
-        M.loff[u] = f < nf ? (slot * CIG + ci) * PWM + 4 * c4 - P.iw_lo : -1;
-        M.tap[u] = (slot / THM) * 4 + slot % THM;
-    }
+__device__ __forceinline__ rsrc_t make_rsrc(const float *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, bytes, kRsrcWord3);
 }
-
-template <int PER>
-__device__ __forceinline__ void stage_fetch(f4 (&r)[PER], unsigned &valid, const StageMap<PER> &M,
-                                            const Igemm3dParams &P, const float *x, int td, int th,
-                                            int cd0, int cd1, int ch0, int ch1, const RowPos &R) {
-    const int64_t nbase = (int64_t)R.n * P.C_in * P.D_in * P.H_in * P.W_in;
-    valid = 0;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int jd = M.tap[u] >> 2, jh = M.tap[u] & 3;
-        const int id = R.qd - (jd == 0 ? cd0 : cd1);
-        const int ih = R.qh - (jh == 0 ? ch0 : ch1);
-        const bool ok = M.loff[u] >= 0 && jd < td && jh < th && id >= 0 && id < P.D_in &&
-                        ih >= 0 && ih < P.H_in;
-        const int64_t off = ok ? nbase + M.xoff[u] + (id * P.H_in + ih) * P.W_in : 0;
-        r[u] = load4u(x + off);
-        valid |= ok ? (1u << u) : 0u;
-    }
+__device__ __forceinline__ f4 buf_load4(rsrc_t r, unsigned voff) {
+    return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
-
-template <int PER>
-__device__ __forceinline__ void stage_store(float *buf, const f4 (&r)[PER], unsigned valid,
-                                            const StageMap<PER> &M) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        if (M.loff[u] >= 0) {
-            const f4 v = (valid >> u) & 1u ? r[u] : f4{0.0f, 0.0f, 0.0f, 0.0f};
-            *reinterpret_cast<f4 *>(buf + M.loff[u]) = v;
-        }
-    }
+__device__ __forceinline__ float buf_load1(rsrc_t r, unsigned voff, unsigned soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buf_store1(float v, rsrc_t r, unsigned voff, unsigned soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, voff, soff, 0);
+}
+typedef int i2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void buf_store2(float a, float b, rsrc_t r, unsigned voff, unsigned soff) {
+    __builtin_amdgcn_raw_buffer_store_b64(i2{__float_as_int(a), __float_as_int(b)}, r, voff, soff, 0);
 }
 
 template <int CIG, int COG, int KW, int SW, int DW, int TDM, int THM, int NWBM, int PWM, int PER,
@@ -246,58 +212,106 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(bo[e]));
 
     static_assert(TDM <= 2 && THM <= 2, "tap offsets are selected from two registers");
-    StageMap<PER> M;
-    stage_map<CIG, THM, NT, PER, PWM>(M, P, SLOTS, tid);
     const int cd0 = P.cls_cd[cls][0], cd1 = P.cls_cd[cls][1];
     const int ch0 = P.cls_ch[cls][0], ch1 = P.cls_ch[cls][1];
-    // output offset of this lane: channel 16ct + 4g4 (+ e), W position SW*j (+ 16 SW t)
+    const int dhw = P.D_in * P.H_in * P.W_in;
     const int64_t dhw_out = (int64_t)P.D_out * P.H_out * P.W_out;
-    const int64_t lane_out = (int64_t)(16 * ct + 4 * g4) * dhw_out + SW * j;
 
-    // add_input of one row: lane_out + e*dhw_out + SW*(16t) + rr past the row base
+    // Input rows of one output row: SLOTS x CIG rows of W_in floats.  Thread
+    // tid stages float4 number f = tid + u*NT, whose meaning does not depend on
+    // the row: tap slot (jd, jh), channel ci, float4 c4.  Its byte offset in
+    // the sample is 4*((qd*H_in + qh)*W_in) + xo4, valid when the slot's tap
+    // exists in the class and its input row lies inside the input (one bit per
+    // slot, the same for the whole workgroup).
+    int xo4[PER], lo[PER], tb[PER];
+    {
+        const int W4 = P.W_in >> 2;
+        const int nf = SLOTS * CIG * W4;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int f = tid + u * NT;
+            const int slot = f / (CIG * W4);
+            const int rem = f - slot * (CIG * W4);
+            const int ci = rem / W4, c4 = rem - ci * W4;
+            const int jd = slot / THM, jh = slot % THM;
+            const int cd = jd == 0 ? cd0 : cd1, ch = jh == 0 ? ch0 : ch1;
+            xo4[u] = 4 * (ci * dhw + 4 * c4 - (cd * P.H_in + ch) * P.W_in);
+            lo[u] = f < nf ? (slot * CIG + ci) * PWM + 4 * c4 - P.iw_lo : -1;
+            tb[u] = f < nf ? slot : 31;
+        }
+    }
+    const int xbytes = 4 * P.C_in * dhw;
+    auto fetch_rows = [&](f4 (&rv)[PER], const RowPos &Q) {
+        unsigned bad = 0xffffffffu; // bit slot clear: the slot's input row exists
+#pragma unroll
+        for (int jd = 0; jd < TDM; ++jd)
+#pragma unroll
+            for (int jh = 0; jh < THM; ++jh) {
+                const int id = Q.qd - (jd == 0 ? cd0 : cd1), ih = Q.qh - (jh == 0 ? ch0 : ch1);
+                if (jd < td && jh < th && id >= 0 && id < P.D_in && ih >= 0 && ih < P.H_in)
+                    bad &= ~(1u << (jd * THM + jh));
+            }
+        const rsrc_t rx = make_rsrc(x + (int64_t)Q.n * P.C_in * dhw, xbytes);
+        const int rowx4 = 4 * (Q.qd * P.H_in + Q.qh) * P.W_in;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            // an invalid slot gets bit 31 set: past num_records, the load returns zeros
+            const unsigned off = ((bad >> tb[u]) << 31) | (unsigned)(rowx4 + xo4[u]);
+            rv[u] = buf_load4(rx, off);
+        }
+    };
+    auto store_rows = [&](float *lbuf, const f4 (&rv)[PER]) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+            if (lo[u] >= 0) *reinterpret_cast<f4 *>(lbuf + lo[u]) = rv[u];
+    };
+
+    // Outputs of lane (g4, j): channel 16ct + 4g4 + e (scalar offset e*dhw_out),
+    // W position SW*(16t + j) + rr (immediate offset), at the row's offset
+    // (od*H_out + oh)*W_out.  Lanes past the row end read the next row or
+    // nothing and store nothing.
+    const int ybytes = (int)(4 * P.C_out * dhw_out);
+    const unsigned lane4 = 4u * (unsigned)((16 * ct + 4 * g4) * dhw_out + SW * j);
+    const unsigned e4 = 4u * (unsigned)dhw_out;
+    auto row_off4 = [&](const RowPos &Q) { return 4u * (unsigned)((Q.od * P.H_out + Q.oh) * P.W_out); };
     auto fetch_add = [&](float (&a)[NWBM][4][SW], const RowPos &Q) {
-        const int64_t base = (int64_t)Q.n * P.C_out * dhw_out +
-                             ((int64_t)Q.od * P.H_out + Q.oh) * P.W_out + lane_out;
+        const rsrc_t ra = make_rsrc(add + (int64_t)Q.n * P.C_out * dhw_out, ybytes);
+        const unsigned vo = lane4 + row_off4(Q);
 #pragma unroll
         for (int t = 0; t < NWBM; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
 #pragma unroll
-                for (int rr = 0; rr < SW; ++rr) {
-                    // clamp inside the row for lanes past its end
-                    const int ow = min(SW * (16 * t + j) + rr, P.W_out - 1) - SW * j;
-                    a[t][e][rr] = add[base + e * dhw_out + ow];
-                }
+                for (int rr = 0; rr < SW; ++rr)
+                    a[t][e][rr] = buf_load1(ra, vo + 4 * (SW * 16 * t + rr), e * e4);
     };
 
     f4 pre[PER];
-    unsigned pvalid;
     float av[NWBM][4][SW], avn[NWBM][4][SW];
     RowPos R = decode_row(P, cls, r_begin);
     __syncthreads(); // LDS zeroed before the first row lands
-    stage_fetch<PER>(pre, pvalid, M, P, x, td, th, cd0, cd1, ch0, ch1, R);
+    fetch_rows(pre, R);
     if constexpr (FUSED) fetch_add(av, R);
-    stage_store<PER>(lds[0], pre, pvalid, M);
+    store_rows(lds[0], pre);
     __syncthreads();
 
+    const f4 bias4 = f4{bo[0], bo[1], bo[2], bo[3]};
+    const bool swap2 = SW == 2 && P.sigma[0] != 0; // W phase 0 lands on the odd outputs
     int buf = 0;
     for (int r = r_begin; r < r_end; ++r) {
         const bool has_next = r + 1 < r_end;
-        // add_input of this row first (older than the prefetch in vmcnt order)
-        // this row's output base (uniform); lane adds lane_out + e*dhw_out + 16 SW t
-        const int64_t row_base = (int64_t)R.n * P.C_out * dhw_out +
-                                 ((int64_t)R.od * P.H_out + R.oh) * P.W_out;
         // inputs of the next row, issued unconditionally (the last row fetches
         // itself again) so the wait counts stay exact: x rows, then add_input
         const RowPos Rn = decode_row(P, cls, has_next ? r + 1 : r);
-        stage_fetch<PER>(pre, pvalid, M, P, x, td, th, cd0, cd1, ch0, ch1, Rn);
+        fetch_rows(pre, Rn);
         if constexpr (FUSED) fetch_add(avn, Rn);
 
+        // the bias enters as the accumulators' start value
         f4 acc[NPH][NWBM];
 #pragma unroll
         for (int s = 0; s < NPH; ++s)
 #pragma unroll
-            for (int t = 0; t < NWBM; ++t) acc[s][t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int t = 0; t < NWBM; ++t) acc[s][t] = bias4;
 
         if constexpr (Ph::count() > 0) {
             // per W phase, this lane's B column in LDS: every read below is
@@ -332,50 +346,66 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
             }
         }
 
+        // The next row's inputs go to the other LDS buffer (free since the last
+        // barrier) before this row's stores: the vector-memory counter retires
+        // in issue order, so the wait for them must not follow the stores.
+        // Unconditional, so that no path leaves them pending into the next
+        // row's fetch.
+#pragma unroll
+        for (int u = 0; u < PER; ++u) asm volatile("" : "+v"(pre[u]));
+        store_rows(lds[buf ^ 1], pre);
+
         // epilogue: lane (g4, j) owns co = 16ct + 4g4 + e, ow = SW*(16t + j) + rr
+        const rsrc_t ry = make_rsrc(y + (int64_t)R.n * P.C_out * dhw_out, ybytes);
+        const unsigned vo = lane4 + row_off4(R);
+        auto epi = [&](auto swapped) {
 #pragma unroll
-        for (int t = 0; t < NWBM; ++t) {
-            const int ow0 = SW * (16 * t + j);
+            for (int t = 0; t < NWBM; ++t) {
+                const int ow0 = SW * (16 * t + j);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float v[SW];
-#pragma unroll
-                for (int rr = 0; rr < SW; ++rr) v[rr] = 0.0f;
-#pragma unroll
-                for (int rw = 0; rw < SW; ++rw) {
-                    if constexpr (Ph::count() > 0) {
-                        if (Ph::nonempty(rw)) {
-                            const float a = acc[Ph::slot(rw)][t][e];
-#pragma unroll
-                            for (int rr = 0; rr < SW; ++rr)
-                                if (P.sigma[rw] == rr) v[rr] = a;
-                        }
-                    }
-                }
-                float *yp = y + row_base + lane_out + e * dhw_out + SW * 16 * t;
-#pragma unroll
-                for (int rr = 0; rr < SW; ++rr) {
-                    const float a1 = FUSED ? av[t][e][rr] : 0.0f;
-                    v[rr] = epilogue<FUSED>(v[rr], bo[e], a1);
-                }
-                if (ow0 + SW <= P.W_out) {
-                    if constexpr (SW == 2) {
-                        typedef float f2u __attribute__((ext_vector_type(2)));
-                        f2u o2 = f2u{v[0], v[1]};
-                        __builtin_memcpy(yp, &o2, 8);
+                for (int e = 0; e < 4; ++e) {
+                    float v[SW];
+                    if constexpr (SW == 2 && NPH == 2) {
+                        v[0] = acc[decltype(swapped)::value ? 1 : 0][t][e];
+                        v[1] = acc[decltype(swapped)::value ? 0 : 1][t][e];
                     } else {
 #pragma unroll
-                        for (int rr = 0; rr < SW; ++rr) yp[rr] = v[rr];
-                    }
-                } else {
+                        for (int rr = 0; rr < SW; ++rr) v[rr] = bo[e];
 #pragma unroll
-                    for (int rr = 0; rr < SW; ++rr)
-                        if (ow0 + rr < P.W_out) yp[rr] = v[rr];
+                        for (int rw = 0; rw < SW; ++rw) {
+                            if constexpr (Ph::count() > 0) {
+                                if (Ph::nonempty(rw)) {
+                                    const float a = acc[Ph::slot(rw)][t][e];
+#pragma unroll
+                                    for (int rr = 0; rr < SW; ++rr)
+                                        if (P.sigma[rw] == rr) v[rr] = a;
+                                }
+                            }
+                        }
+                    }
+                    if constexpr (FUSED) {
+#pragma unroll
+                        for (int rr = 0; rr < SW; ++rr) v[rr] = times_hardswish(v[rr] + av[t][e][rr]);
+                    }
+                    const unsigned o = vo + 4 * SW * 16 * t;
+                    if (ow0 + SW <= P.W_out) {
+                        if constexpr (SW == 2) {
+                            buf_store2(v[0], v[1], ry, o, e * e4);
+                        } else {
+#pragma unroll
+                            for (int rr = 0; rr < SW; ++rr) buf_store1(v[rr], ry, o + 4 * rr, e * e4);
+                        }
+                    } else {
+#pragma unroll
+                        for (int rr = 0; rr < SW; ++rr)
+                            if (ow0 + rr < P.W_out) buf_store1(v[rr], ry, o + 4 * rr, e * e4);
+                    }
                 }
             }
-        }
+        };
+        if (swap2) epi(std::true_type{});
+        else epi(std::false_type{});
 
-        if (has_next) stage_store<PER>(lds[buf ^ 1], pre, pvalid, M);
         __syncthreads();
         buf ^= 1;
         R = Rn;
@@ -655,6 +685,10 @@ int find_variant(const convt_plan &P, Layout *Lout = nullptr) {
     if (P.ndim != 3 || P.G != 1) return -1;
     const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
     if (AW.L_in % 4 != 0) return -1;
+    // per-sample byte offsets of x, y and add_input stay below 2^31 (buffer addressing)
+    if ((int64_t)P.C_in * AD.L_in * AH.L_in * AW.L_in * 4 >= INT32_MAX ||
+        (int64_t)P.C_out * AD.L_out * AH.L_out * AW.L_out * 4 >= INT32_MAX)
+        return -1;
     const int W4 = AW.L_in / 4;
     if (AD.s * AH.s > kMaxClasses) return -1;
     // taps per class on D and H

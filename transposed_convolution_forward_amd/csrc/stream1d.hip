@@ -188,7 +188,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
 
     __shared__ __attribute__((aligned(16))) float lds[2][CIG * kPitch];
     __shared__ __attribute__((aligned(16))) float ostage[COT][4][stage_pitch<S>()];
-    __shared__ float ocarry[COT][16][16];
+    __shared__ __attribute__((aligned(16))) float ocarry[COT][4][4][16]; // [wave][g4][e][slot]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -246,19 +246,28 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
         const bool has_next = ii + 1 < n_items;
         if (has_next) tile_fetch<CIG, NT>(pre, xrow_of(ng1), P.L_in, (P.st_lo + st1) * kTileQ, tid);
 
+        // The bias enters as the accumulators' start value.
+        const f4 bias4 = f4{br[0], br[1], br[2], br[3]};
         f4 acc[NP][4];
 #pragma unroll
         for (int s2 = 0; s2 < NP; ++s2)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) acc[s2][t] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int t = 0; t < 4; ++t) acc[s2][t] = bias4;
 
         if constexpr (Ph::count() > 0) {
-            const float *tile = lds[buf];
+            // B operands of input-channel step cig+1 are read from LDS while the
+            // MFMAs of step cig run.
+            const float *tp = lds[buf] + g4 * kPitch + 4 * j;
+            f4 pv = *reinterpret_cast<const f4 *>(tp);     // q0+4j-4 .. -1
+            f4 cv = *reinterpret_cast<const f4 *>(tp + 4); // q0+4j .. +3
 #pragma unroll
             for (int cig = 0; cig < NCIG; ++cig) {
-                const float *rowp = tile + (4 * cig + g4) * kPitch + 4 * j;
-                const f4 pv = *reinterpret_cast<const f4 *>(rowp);     // q0+4j-4 .. -1
-                const f4 cv = *reinterpret_cast<const f4 *>(rowp + 4); // q0+4j .. +3
+                f4 pn = pv, cn = cv;
+                if (cig + 1 < NCIG) {
+                    pn = *reinterpret_cast<const f4 *>(tp + (cig + 1) * 4 * kPitch);
+                    cn = *reinterpret_cast<const f4 *>(tp + (cig + 1) * 4 * kPitch + 4);
+                }
+                __builtin_amdgcn_sched_barrier(0); // keep these reads ahead of the step's MFMAs
                 const float cur[4] = {cv.x, cv.y, cv.z, cv.w};
                 const float prv[4] = {pv.x, pv.y, pv.z, pv.w};
 #pragma unroll
@@ -272,6 +281,8 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
                                                                           acc[sl][t], 0, 0, 0);
                     }
                 }
+                pv = pn;
+                cv = cn;
             }
         }
 
@@ -299,21 +310,26 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
             interior && has_next && st1 != 0 && o_t + 128 * S <= P.L_out; // next: same rows, interior
         chain = chain_out;
         float *srow = &ostage[ct][g4][0];
+        float cin[4] = {0.0f, 0.0f, 0.0f, 0.0f}; // carried outputs, slot j of each row
+        if (chain_in) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cin[e] = ocarry[ct][g4][e][j];
+        }
+        float *yrow = y + ((int64_t)n * P.C_out + (int64_t)g * COG + 16 * ct + 4 * g4) * P.L_out + o_t;
+        const float *arow = FUSED ? add + (yrow - y) : nullptr;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int64_t row = ((int64_t)n * P.C_out + (int64_t)g * COG + 16 * ct + 4 * g4 + e) *
-                                P.L_out;
-            float *yr = y + row + o_t;
-            const float *ar = FUSED ? add + row + o_t : nullptr;
+            float *yr = yrow + (int64_t)e * P.L_out;
+            const float *ar = FUSED ? arow + (int64_t)e * P.L_out : nullptr;
             float v[4 * S];
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
                 for (int r = 0; r < S; ++r) {
-                    float a = 0.0f;
+                    float a = br[e];
                     if constexpr (Ph::count() > 0)
                         if (Ph::nonempty(r)) a = acc[Ph::slot(r)][t][e];
-                    v[t * S + r] = a + br[e];
+                    v[t * S + r] = a;
                 }
             if (interior) {
                 if constexpr (FUSED) {
@@ -327,13 +343,20 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
                     }
                 }
                 const int a = (int)(((uintptr_t)yr >> 2) & 15); // o_t's offset in its line
-                float *cr = &ocarry[ct][4 * g4 + e][0];
-                if (chain_in) srow[j] = cr[j];
+                if (chain_in) srow[j] = cin[e]; // the previous run's last 16 outputs
 #pragma unroll
                 for (int c = 0; c < S; ++c)
                     *reinterpret_cast<f4 *>(srow + 16 + 4 * S * j + 4 * c) =
                         f4{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
-                if (chain_out) cr[j] = srow[64 * S + j];
+                if (chain_out) { // this run's last 16 outputs, straight from the lanes holding them
+#pragma unroll
+                    for (int c = 0; c < S; ++c) {
+                        const int i0 = 4 * S * j + 4 * c - (64 * S - 16);
+                        if (i0 >= 0)
+                            *reinterpret_cast<f4 *>(&ocarry[ct][g4][e][i0]) =
+                                f4{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
+                    }
+                }
                 float *ys = yr - a;               // line-aligned segment start
                 const float *ss = srow + 16 - a;  // segment in the staging row
 #pragma unroll
