@@ -24,6 +24,7 @@ import argparse
 import glob
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -196,7 +197,8 @@ def main():
     gbs = nbytes / (ms_per_step * 1e-3) / 1e9
     t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
     t_fp32 = flops / (PEAK_FP32_TFLOPS * 1e12)
-    kernel = KERNEL_NAMES[path]
+    m = re.search(r"kernel=(\S+)", T.convt_plan_describe(plan))
+    kernel = m.group(1) if m else KERNEL_NAMES[path]
     if t_hbm >= t_fp32:
         ach = nbytes / (ms_launch * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

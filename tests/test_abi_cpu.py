@@ -122,6 +122,11 @@ def test_workload_plans_and_paths():
         T.convt_plan_set_path(p, "auto")
         text = T.convt_plan_describe(p)
         assert "path=" in text and "r0:" in text
+        kern = {"generic": "k_generic", "stream1d": "k_stream1d"}.get(T.convt_plan_get_path(p))
+        assert ("kernel=" + kern) in text if kern else ("kernel=k_igemm3d" in text)
+    # the channel-heavy layer streams its weights through LDS
+    assert "kernel=k_igemm3d_wide" in T.convt_plan_describe(T.plan_for(S.HEAVY_3D))
+    assert "kernel=k_igemm3d\n" in T.convt_plan_describe(T.plan_for(S.FUSED_3D))
 
 
 def test_phase_table_description():

@@ -222,9 +222,13 @@ int64_t convt_plan_describe(const convt_plan *plan, char *buf, int64_t len) {
     if (!plan) return -1;
     std::string s;
     char tmp[256];
-    snprintf(tmp, sizeof tmp, "convt plan: ndim=%d N=%lld C_in=%lld C_out=%lld groups=%lld path=%s\n",
+    const char *kernel = plan->path == CONVT_PATH_STREAM1D ? "k_stream1d"
+                         : plan->path == CONVT_PATH_IGEMM3D ? convt::igemm3d_kernel_name(*plan)
+                                                            : "k_generic";
+    snprintf(tmp, sizeof tmp,
+             "convt plan: ndim=%d N=%lld C_in=%lld C_out=%lld groups=%lld path=%s kernel=%s\n",
              plan->ndim, (long long)plan->N, (long long)plan->C_in, (long long)plan->C_out,
-             (long long)plan->G, path_name(plan->path));
+             (long long)plan->G, path_name(plan->path), kernel);
     s += tmp;
     for (int a = kAxes - plan->ndim; a < kAxes; ++a) {
         const AxisPlan &A = plan->ax[a];

@@ -56,6 +56,8 @@ int launch_stream1d(const convt_plan &P, const float *x, const float *w, const f
                     const float *add, float *y, void *stream);
 
 bool igemm3d_supports(const convt_plan &P);
+// Name of the kernel launch_igemm3d runs for P (weights in VGPRs or streamed).
+const char *igemm3d_kernel_name(const convt_plan &P);
 int launch_igemm3d(const convt_plan &P, const float *x, const float *w, const float *bias,
                    const float *add, float *y, void *stream);
 

@@ -880,6 +880,12 @@ bool igemm3d_supports(const convt_plan &P) {
     return P.N * P.ax[0].L_out * P.ax[1].L_out < (int64_t(1) << 31);
 }
 
+const char *igemm3d_kernel_name(const convt_plan &P) {
+    Layout L;
+    if (find_variant(P, &L) >= 0) return "k_igemm3d";
+    return find_wide(P, &L) >= 0 ? "k_igemm3d_wide" : "none";
+}
+
 int launch_igemm3d(const convt_plan &Pl, const float *x, const float *w, const float *bias,
                    const float *add, float *y, void *stream) {
     Layout L;
