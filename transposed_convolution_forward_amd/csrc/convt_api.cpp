@@ -224,7 +224,7 @@ int64_t convt_plan_describe(const convt_plan *plan, char *buf, int64_t len) {
     char tmp[256];
     const char *kernel = plan->path == CONVT_PATH_STREAM1D ? "k_stream1d"
                          : plan->path == CONVT_PATH_IGEMM3D ? convt::igemm3d_kernel_name(*plan)
-                                                            : "k_generic";
+                                                            : convt::generic_kernel_name(*plan);
     snprintf(tmp, sizeof tmp,
              "convt plan: ndim=%d N=%lld C_in=%lld C_out=%lld groups=%lld path=%s kernel=%s\n",
              plan->ndim, (long long)plan->N, (long long)plan->C_in, (long long)plan->C_out,

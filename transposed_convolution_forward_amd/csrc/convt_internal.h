@@ -48,6 +48,9 @@ namespace convt {
 // Kernel launchers, one per path.  add != nullptr selects the fused epilogue.
 // Each returns hipSuccess or the launch error (as int, to keep HIP types out).
 bool generic_supports(const convt_plan &P);
+// Name of the kernel launch_generic runs for P (phase-class variant when the
+// shape has at most 32 phase classes).
+const char *generic_kernel_name(const convt_plan &P);
 int launch_generic(const convt_plan &P, const float *x, const float *w, const float *bias,
                    const float *add, float *y, void *stream);
 

@@ -93,6 +93,186 @@ __global__ __launch_bounds__(kBlock) void k_generic(const GenericParams P,
     }
 }
 
+// ------------------------------------------------------- phase-class variant
+// Same gather, but a workgroup covers output positions of one phase class
+// (one residue per axis) only, consecutive lanes taking consecutive positions q
+// along W.  All lanes of a wave then walk the same tap list, the weights they
+// use are the same for the whole wave (scalar loads, broadcast), and each
+// input load, coalesced along W, feeds CPT FMAs.  P1's parity-class blocking
+// ("Kimi-K2.6 l1_p72" transcript, ConvTranspose3d): a block never mixes
+// classes, so trip counts stay uniform.
+constexpr int kMaxPhaseCls = 32;
+
+int pick_cpt(int64_t Cog) { return Cog >= 8 ? 8 : Cog >= 4 ? 4 : Cog >= 2 ? 2 : 1; }
+
+struct PhaseParams {
+    AxisPlan ax[kAxes];
+    int C_in, C_out, Cig, Cog, k_vol;
+    int in_sp, out_sp;
+    int co_chunks;
+    int n0;
+    int n_cls;
+    int cls_r[kMaxPhaseCls][kAxes];  // residue per axis
+    int cls_q0[kMaxPhaseCls][kAxes]; // first q per axis (its output lies in [0, L_out))
+    int cls_nq[kMaxPhaseCls][kAxes]; // number of q per axis
+    int cls_blk0[kMaxPhaseCls + 1];  // first workgroup (grid x) of each class
+    int max_taps;                    // taps of the class with the most
+};
+constexpr int kMaxPhaseLds = 32768; // bytes of staged weights per workgroup
+
+template <int CPT, bool FUSED>
+__global__ __launch_bounds__(kBlock) void k_generic_phase(const PhaseParams P,
+                                                          const float *__restrict__ x,
+                                                          const float *__restrict__ w,
+                                                          const float *__restrict__ bias,
+                                                          const float *add, float *y) {
+    int c = 0;
+    while (c + 1 < P.n_cls && (int)blockIdx.x >= P.cls_blk0[c + 1]) ++c;
+    const int l = ((int)blockIdx.x - P.cls_blk0[c]) * kBlock + (int)threadIdx.x;
+    const int nqd = P.cls_nq[c][0], nqh = P.cls_nq[c][1], nqw = P.cls_nq[c][2];
+    const bool live = l < nqd * nqh * nqw;
+    const int iqw = l % nqw;
+    const int t2 = l / nqw;
+    const int iqh = t2 % nqh;
+    const int iqd = t2 / nqh;
+    const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
+    const int rd = P.cls_r[c][0], rh = P.cls_r[c][1], rw = P.cls_r[c][2];
+    const int qd = P.cls_q0[c][0] + iqd, qh = P.cls_q0[c][1] + iqh, qw = P.cls_q0[c][2] + iqw;
+
+    const int g = blockIdx.y / P.co_chunks;
+    const int co0 = (blockIdx.y % P.co_chunks) * CPT;
+    const int n = P.n0 + blockIdx.z;
+    const int ncol = min(CPT, P.Cog - co0);
+
+    float acc[CPT];
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) acc[j] = 0.0f;
+
+    // The workgroup's weights, [class tap][input channel][column], staged once:
+    // every lane reads the same ones, so the reads below are broadcasts.
+    // Columns past the group's last channel repeat it (never stored).
+    extern __shared__ __attribute__((aligned(16))) float wl[];
+    const int Td = AD.tap_start[rd + 1] - AD.tap_start[rd];
+    const int Th = AH.tap_start[rh + 1] - AH.tap_start[rh];
+    const int Tw = AW.tap_start[rw + 1] - AW.tap_start[rw];
+    {
+        const float *wg = w + ((int64_t)g * P.Cig * P.Cog + co0) * P.k_vol;
+        const int nw = Td * Th * Tw * P.Cig * CPT;
+        for (int i = threadIdx.x; i < nw; i += kBlock) {
+            const int j = i % CPT, t = i / CPT;
+            const int ci = t % P.Cig, tap = t / P.Cig;
+            const int tw = tap % Tw, tdh = tap / Tw;
+            const int th = tdh % Th, td = tdh / Th;
+            const int kidx = (AD.tap_k[AD.tap_start[rd] + td] * AH.K + AH.tap_k[AH.tap_start[rh] + th]) *
+                                 AW.K + AW.tap_k[AW.tap_start[rw] + tw];
+            wl[i] = wg[((int64_t)ci * P.Cog + min(j, ncol - 1)) * P.k_vol + kidx];
+        }
+    }
+    __syncthreads();
+
+    const float *xg = x + ((int64_t)n * P.C_in + (int64_t)g * P.Cig) * P.in_sp;
+    const float *wt = wl;
+    for (int jd = AD.tap_start[rd]; jd < AD.tap_start[rd + 1]; ++jd) {
+        const int id = qd - AD.tap_c[jd];
+        const bool okd = id >= 0 && id < AD.L_in;
+        for (int jh = AH.tap_start[rh]; jh < AH.tap_start[rh + 1]; ++jh) {
+            const int ih = qh - AH.tap_c[jh];
+            const bool okh = okd && ih >= 0 && ih < AH.L_in;
+            for (int jw = AW.tap_start[rw]; jw < AW.tap_start[rw + 1]; ++jw, wt += P.Cig * CPT) {
+                const int iw = qw - AW.tap_c[jw];
+                const bool ok = live && okh && iw >= 0 && iw < AW.L_in;
+                // lanes outside the input read the group's first element and use 0
+                const float *xp = xg + (ok ? (id * AH.L_in + ih) * AW.L_in + iw : 0);
+#pragma unroll 4
+                for (int ci = 0; ci < P.Cig; ++ci) {
+                    const float xr = xp[(int64_t)ci * P.in_sp];
+                    const float xv = ok ? xr : 0.0f;
+                    const float *wc = wt + ci * CPT;
+#pragma unroll
+                    for (int j = 0; j < CPT; ++j) acc[j] = fmaf(xv, wc[j], acc[j]);
+                }
+            }
+        }
+    }
+    if (!live) return;
+
+    const int od = qd * AD.s + rd - AD.p, oh = qh * AH.s + rh - AH.p, ow = qw * AW.s + rw - AW.p;
+    const int sp = (od * AH.L_out + oh) * AW.L_out + ow;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+        if (j >= ncol) break;
+        const int co = g * P.Cog + co0 + j;
+        const int64_t idx = ((int64_t)n * P.C_out + co) * P.out_sp + sp;
+        const float b = bias ? bias[co] : 0.0f;
+        const float a = FUSED ? add[idx] : 0.0f;
+        y[idx] = epilogue<FUSED>(acc[j], b, a);
+    }
+}
+
+// Fills the class table; false when the shape has more classes than it holds.
+bool phase_classes(const convt_plan &Pl, PhaseParams &P) {
+    P.n_cls = 0;
+    P.max_taps = 1;
+    int blocks = 0;
+    const AxisPlan *A = Pl.ax;
+    for (int rd = 0; rd < A[0].s; ++rd)
+        for (int rh = 0; rh < A[1].s; ++rh)
+            for (int rw = 0; rw < A[2].s; ++rw) {
+                const int r[kAxes] = {rd, rh, rw};
+                int q0[kAxes], nq[kAxes];
+                bool empty = false;
+                for (int a = 0; a < kAxes; ++a) {
+                    // q with 0 <= q*s + r - p < L_out
+                    const int lo = A[a].p - r[a];
+                    q0[a] = lo <= 0 ? 0 : (lo + A[a].s - 1) / A[a].s;
+                    const int o0 = q0[a] * A[a].s + r[a] - A[a].p;
+                    nq[a] = o0 < A[a].L_out ? (A[a].L_out - 1 - o0) / A[a].s + 1 : 0;
+                    empty |= nq[a] == 0;
+                }
+                if (empty) continue;
+                if (P.n_cls == kMaxPhaseCls) return false;
+                const int c = P.n_cls++;
+                for (int a = 0; a < kAxes; ++a) {
+                    P.cls_r[c][a] = r[a];
+                    P.cls_q0[c][a] = q0[a];
+                    P.cls_nq[c][a] = nq[a];
+                }
+                P.cls_blk0[c] = blocks;
+                int taps = 1;
+                for (int a = 0; a < kAxes; ++a) taps *= A[a].tap_start[r[a] + 1] - A[a].tap_start[r[a]];
+                P.max_taps = taps > P.max_taps ? taps : P.max_taps;
+                const int64_t pos = (int64_t)nq[0] * nq[1] * nq[2];
+                blocks += (int)((pos + kBlock - 1) / kBlock);
+            }
+    P.cls_blk0[P.n_cls] = blocks;
+    // the staged weights of the class with the most taps must fit in LDS
+    return (int64_t)P.max_taps * Pl.Cig * pick_cpt(Pl.Cog) * 4 <= kMaxPhaseLds;
+}
+
+template <int CPT>
+int launch_phase(const convt_plan &Pl, PhaseParams &P, const float *x, const float *w,
+                 const float *bias, const float *add, float *y, hipStream_t st) {
+    P.co_chunks = (int)((Pl.Cog + CPT - 1) / CPT);
+    const unsigned gx = (unsigned)P.cls_blk0[P.n_cls];
+    const unsigned gy = (unsigned)(Pl.G * P.co_chunks);
+    if (gx == 0) return 0;
+    for (int64_t n0 = 0; n0 < Pl.N; n0 += 65535) {
+        P.n0 = (int)n0;
+        const unsigned gz = (unsigned)(Pl.N - n0 < 65535 ? Pl.N - n0 : 65535);
+        dim3 grid(gx, gy, gz);
+        const size_t lds = (size_t)P.max_taps * Pl.Cig * CPT * sizeof(float);
+        if (add)
+            hipLaunchKernelGGL((k_generic_phase<CPT, true>), grid, dim3(kBlock), lds, st, P, x, w,
+                               bias, add, y);
+        else
+            hipLaunchKernelGGL((k_generic_phase<CPT, false>), grid, dim3(kBlock), lds, st, P, x, w,
+                               bias, add, y);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+    }
+    return 0;
+}
+
 template <int CPT>
 int launch_cpt(const convt_plan &Pl, const GenericParams &base, const float *x, const float *w,
                const float *bias, const float *add, float *y, hipStream_t st) {
@@ -116,9 +296,13 @@ int launch_cpt(const convt_plan &Pl, const GenericParams &base, const float *x, 
     return 0;
 }
 
-int pick_cpt(int64_t Cog) { return Cog >= 8 ? 8 : Cog >= 4 ? 4 : Cog >= 2 ? 2 : 1; }
 
 } // namespace
+
+const char *generic_kernel_name(const convt_plan &Pl) {
+    PhaseParams P;
+    return phase_classes(Pl, P) ? "k_generic_phase" : "k_generic";
+}
 
 bool generic_supports(const convt_plan &P) {
     const int cpt = pick_cpt(P.Cog);
@@ -127,6 +311,26 @@ bool generic_supports(const convt_plan &P) {
 
 int launch_generic(const convt_plan &Pl, const float *x, const float *w, const float *bias,
                    const float *add, float *y, void *stream) {
+    {
+        PhaseParams Q;
+        if (phase_classes(Pl, Q)) {
+            for (int a = 0; a < kAxes; ++a) Q.ax[a] = Pl.ax[a];
+            Q.C_in = (int)Pl.C_in;
+            Q.C_out = (int)Pl.C_out;
+            Q.Cig = (int)Pl.Cig;
+            Q.Cog = (int)Pl.Cog;
+            Q.k_vol = (int)Pl.k_vol;
+            Q.in_sp = (int)Pl.in_sp;
+            Q.out_sp = (int)Pl.out_sp;
+            hipStream_t st = (hipStream_t)stream;
+            switch (pick_cpt(Pl.Cog)) {
+            case 8: return launch_phase<8>(Pl, Q, x, w, bias, add, y, st);
+            case 4: return launch_phase<4>(Pl, Q, x, w, bias, add, y, st);
+            case 2: return launch_phase<2>(Pl, Q, x, w, bias, add, y, st);
+            default: return launch_phase<1>(Pl, Q, x, w, bias, add, y, st);
+            }
+        }
+    }
     GenericParams P;
     for (int a = 0; a < kAxes; ++a) P.ax[a] = Pl.ax[a];
     P.C_in = (int)Pl.C_in;

@@ -134,6 +134,10 @@ __device__ __forceinline__ f4 buf_load4(rsrc_t r, unsigned voff) {
 __device__ __forceinline__ float buf_load1(rsrc_t r, unsigned voff, unsigned soff) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
 }
+typedef float fl2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ fl2 buf_load2(rsrc_t r, unsigned voff, unsigned soff) {
+    return __builtin_bit_cast(fl2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
 __device__ __forceinline__ void buf_store1(float v, rsrc_t r, unsigned voff, unsigned soff) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, voff, soff, 0);
 }
@@ -280,10 +284,17 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
 #pragma unroll
         for (int t = 0; t < NWBM; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (SW == 2) { // the lane's two outputs are adjacent: one 8-byte load
+                    const fl2 v = buf_load2(ra, vo + 4 * SW * 16 * t, e * e4);
+                    a[t][e][0] = v.x;
+                    a[t][e][1] = v.y;
+                } else {
 #pragma unroll
-                for (int rr = 0; rr < SW; ++rr)
-                    a[t][e][rr] = buf_load1(ra, vo + 4 * (SW * 16 * t + rr), e * e4);
+                    for (int rr = 0; rr < SW; ++rr)
+                        a[t][e][rr] = buf_load1(ra, vo + 4 * (SW * 16 * t + rr), e * e4);
+                }
+            }
     };
 
     f4 pre[PER];
