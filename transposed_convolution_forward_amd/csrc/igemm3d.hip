@@ -78,6 +78,11 @@ template <int K, int S, int D> struct WPhases {
         for (int k = 0; k < K; ++k) m = c_of(k) > m ? c_of(k) : m;
         return m;
     }
+    static constexpr int first_k(int r) { // first tap of phase r
+        for (int k = 0; k < K; ++k)
+            if (r_of(k) == r) return k;
+        return -1;
+    }
 };
 
 struct Igemm3dParams {
@@ -309,7 +314,9 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     const f4 bias4 = f4{bo[0], bo[1], bo[2], bo[3]};
     const bool swap2 = SW == 2 && P.sigma[0] != 0; // W phase 0 lands on the odd outputs
     int buf = 0;
-    for (int r = r_begin; r < r_end; ++r) {
+    // One output row; the loop below runs it twice per trip with the two
+    // add_input register sets swapped, so the prefetched set needs no copy.
+    auto row_step = [&](const int r, const auto &av, auto &avn) {
         const bool has_next = r + 1 < r_end;
         // inputs of the next row, issued unconditionally (the last row fetches
         // itself again) so the wait counts stay exact: x rows, then add_input
@@ -317,14 +324,16 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
         fetch_rows(pre, Rn);
         if constexpr (FUSED) fetch_add(avn, Rn);
 
-        // the bias enters as the accumulators' start value
+        // The bias enters as the accumulators' start value: the first MFMA of
+        // each W phase takes it as its accumulator input.  Rows of a class
+        // without taps keep the bias.
         f4 acc[NPH][NWBM];
+        if (Ph::count() == 0 || td == 0 || th == 0) {
 #pragma unroll
-        for (int s = 0; s < NPH; ++s)
+            for (int s = 0; s < NPH; ++s)
 #pragma unroll
-            for (int t = 0; t < NWBM; ++t) acc[s][t] = bias4;
-
-        if constexpr (Ph::count() > 0) {
+                for (int t = 0; t < NWBM; ++t) acc[s][t] = bias4;
+        } else if constexpr (Ph::count() > 0) {
             // per W phase, this lane's B column in LDS: every read below is
             // then this base plus a compile-time offset
             const float *bcol[SW];
@@ -333,10 +342,10 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
                 bcol[rw] = lds[buf] + g4 * PWM - P.iw_lo + j + P.qw0[rw];
 #pragma unroll
             for (int jd = 0; jd < TDM; ++jd) {
-                if (jd >= td) break;
+                if (jd > 0 && jd >= td) break;
 #pragma unroll
                 for (int jh = 0; jh < THM; ++jh) {
-                    if (jh >= th) break;
+                    if (jh > 0 && jh >= th) break;
                     const int slot = jd * THM + jh;
 #pragma unroll
                     for (int cig = 0; cig < NCIG; ++cig) {
@@ -348,8 +357,9 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
 #pragma unroll
                             for (int t = 0; t < NWBM; ++t) {
                                 const float bv = bcol[rw][(slot * CIG + 4 * cig) * PWM + 16 * t - c];
+                                const bool first = jd == 0 && jh == 0 && cig == 0 && kw == Ph::first_k(rw);
                                 acc[sl][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                    wr[jd][jh][kw][cig], bv, acc[sl][t], 0, 0, 0);
+                                    wr[jd][jh][kw][cig], bv, first ? bias4 : acc[sl][t], 0, 0, 0);
                             }
                         }
                     }
@@ -420,14 +430,10 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
         __syncthreads();
         buf ^= 1;
         R = Rn;
-        if constexpr (FUSED) {
-#pragma unroll
-            for (int t = 0; t < NWBM; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-#pragma unroll
-                    for (int rr = 0; rr < SW; ++rr) av[t][e][rr] = avn[t][e][rr];
-        }
+    };
+    for (int r = r_begin; r < r_end; r += 2) {
+        row_step(r, av, avn);
+        if (r + 1 < r_end) row_step(r + 1, avn, av);
     }
 }
 
