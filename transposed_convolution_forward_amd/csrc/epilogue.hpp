@@ -4,7 +4,7 @@
 // Plain:  y = acc + bias
 // Fused ("Kimi-K2.6 l2_p26" transcript, ConvTranspose3d + add + HardSwish: its
 // forward, then hardswish(t) = t * clamp(t + 3, 0, 6) / 6):
-//   t = acc + bias + add_input,  y = t * hardswish(t) = t * (t * clamp(t+3,0,6) / 6)
+//   t = acc + bias + add_input,  y = t * hardswish(t) = t * t * clamp(t+3,0,6) / 6
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,8 +12,10 @@
 namespace convt {
 
 __device__ __forceinline__ float times_hardswish(float t) {
-    const float r = fminf(fmaxf(t + 3.0f, 0.0f), 6.0f);
-    return t * (t * r * (1.0f / 6.0f)); // times 1/6 rounded: within an ulp of dividing by 6
+    // clamp(t+3, 0, 6)/6 = clamp(t/6 + 1/2, 0, 1): one FMA and one clamp (1/6
+    // rounded to fp32: within an ulp of dividing), then t*t times it
+    const float r = fminf(fmaxf(fmaf(t, 1.0f / 6.0f, 0.5f), 0.0f), 1.0f);
+    return (t * t) * r;
 }
 
 template <bool FUSED>
