@@ -336,10 +336,21 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
         } else if constexpr (Ph::count() > 0) {
             // per W phase, this lane's B column in LDS: every read below is
             // then this base plus a compile-time offset
-            const float *bcol[SW];
+            // one base per (W phase, tap shift): the reads below are then the
+            // base plus multiples of 64 floats (channel and slot pitches), which
+            // paired LDS reads reach without address arithmetic
+            // (the empty asm hides how the bases relate, or the compiler would pair
+            // reads one float apart and rebuild a base for every pair)
+            typedef const __attribute__((address_space(3))) float *lds_ptr;
+            constexpr int CM = Ph::cmax() + 1;
+            lds_ptr bcol[SW][CM];
 #pragma unroll
             for (int rw = 0; rw < SW; ++rw)
-                bcol[rw] = lds[buf] + g4 * PWM - P.iw_lo + j + P.qw0[rw];
+#pragma unroll
+                for (int c = 0; c < CM; ++c) {
+                    bcol[rw][c] = (lds_ptr)(lds[buf] + g4 * PWM - P.iw_lo + j + P.qw0[rw] - c);
+                    asm volatile("" : "+v"(bcol[rw][c]));
+                }
 #pragma unroll
             for (int jd = 0; jd < TDM; ++jd) {
                 if (jd > 0 && jd >= td) break;
@@ -356,7 +367,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
                             const int c = Ph::c_of(kw);
 #pragma unroll
                             for (int t = 0; t < NWBM; ++t) {
-                                const float bv = bcol[rw][(slot * CIG + 4 * cig) * PWM + 16 * t - c];
+                                const float bv = bcol[rw][c][(slot * CIG + 4 * cig) * PWM + 16 * t];
                                 const bool first = jd == 0 && jh == 0 && cig == 0 && kw == Ph::first_k(rw);
                                 acc[sl][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
                                     wr[jd][jh][kw][cig], bv, first ? bias4 : acc[sl][t], 0, 0, 0);
