@@ -46,12 +46,18 @@ __device__ __forceinline__ f4 load4u(const float *p) {
     return v;
 }
 
+// Tuning knob: each XCD walks a contiguous range of a class's row chunks.
+#ifndef CONVT_IG_XCD_ORDER
+#define CONVT_IG_XCD_ORDER 1
+#endif
+
 // Tuning knob: minimum waves per SIMD the register allocation must allow.
 #ifndef CONVT_IG_WAVES_PER_EU
 #define CONVT_IG_WAVES_PER_EU 3
 #endif
 
 constexpr int kMaxClasses = 16;
+constexpr int kXcds = 8; // accelerator complex dies (each with its own L2) per device
 constexpr int kTapMax = 4; // per-axis taps per class the table holds
 constexpr int kMaxSW = 8;
 
@@ -96,6 +102,8 @@ struct Igemm3dParams {
     int nwb;             // W-blocks of 16*S_W outputs per row (equals the template's NWBM)
     int qw0[kMaxSW], sigma[kMaxSW];
     int cls_block0[kMaxClasses + 1]; // classes ordered heaviest first
+    int cls_chunks[kMaxClasses];     // row chunks (rows_per_block rows each) per class
+    int xcd_order;                   // 1: each XCD walks a contiguous range of a class's chunks
     int cls_rows[kMaxClasses];
     int cls_td[kMaxClasses], cls_th[kMaxClasses];
     int cls_kd[kMaxClasses][kTapMax], cls_cd[kMaxClasses][kTapMax];
@@ -177,7 +185,16 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
 
     int cls = 0;
     while (cls + 1 < P.n_class && (int)blockIdx.x >= P.cls_block0[cls + 1]) ++cls;
-    const int r_begin = ((int)blockIdx.x - P.cls_block0[cls]) * P.rows_per_block;
+    int chunk = (int)blockIdx.x - P.cls_block0[cls];
+    if (P.xcd_order) {
+        // Blocks go to the XCDs round robin, so block k of the class runs on XCD
+        // (k mod 8) up to a fixed rotation; give each XCD a contiguous range of
+        // chunks, walked in order, so blocks running together on one L2 share
+        // the input rows at their chunk boundaries.
+        const int per = (P.cls_chunks[cls] + kXcds - 1) / kXcds;
+        chunk = (chunk % kXcds) * per + chunk / kXcds;
+    }
+    const int r_begin = chunk * P.rows_per_block;
     const int r_end = min(r_begin + P.rows_per_block, P.cls_rows[cls]);
     if (r_begin >= r_end) return;
     const int td = P.cls_td[cls], th = P.cls_th[cls];
@@ -817,13 +834,17 @@ int64_t fill_params(const convt_plan &Pl, const Layout &L, int SW, Igemm3dParams
     return total_rows;
 }
 
-// Blocks of rpb rows per class; returns the grid size.
-int assign_blocks(Igemm3dParams &P, int rpb) {
+// Blocks of rpb rows per class; returns the grid size.  With xcd_order the
+// block count of each class is a multiple of the XCD count (blocks whose chunk
+// lies past the class's rows exit at once).
+int assign_blocks(Igemm3dParams &P, int rpb, bool xcd_order = false) {
     P.rows_per_block = rpb;
+    P.xcd_order = xcd_order ? 1 : 0;
     int blocks = 0;
     for (int c = 0; c < P.n_class; ++c) {
         P.cls_block0[c] = blocks;
-        blocks += (P.cls_rows[c] + rpb - 1) / rpb;
+        P.cls_chunks[c] = (P.cls_rows[c] + rpb - 1) / rpb;
+        blocks += xcd_order ? (P.cls_chunks[c] + kXcds - 1) / kXcds * kXcds : P.cls_chunks[c];
     }
     P.cls_block0[P.n_class] = blocks;
     return blocks;
@@ -837,7 +858,7 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
     // rows per block: enough blocks to fill the CUs several times over
     const int64_t target_blocks = (int64_t)num_cus() * 16;
     const int rpb = (int)std::max<int64_t>(1, std::min<int64_t>(64, total_rows / target_blocks));
-    const int blocks = assign_blocks(P, rpb);
+    const int blocks = assign_blocks(P, rpb, CONVT_IG_XCD_ORDER != 0);
     if (blocks == 0) return 0;
     constexpr int NT = COG * 4;
     constexpr int PER = (TDM * THM * CIG * W4M + NT - 1) / NT; // W_in <= 4*W4M is checked
