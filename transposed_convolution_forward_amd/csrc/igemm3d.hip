@@ -46,6 +46,15 @@ __device__ __forceinline__ f4 load4u(const float *p) {
     return v;
 }
 
+// Tuning knobs: workgroups aimed for per CU when sizing the rows per block,
+// and the most rows one block walks.
+#ifndef CONVT_IG_BLOCKS_PER_CU
+#define CONVT_IG_BLOCKS_PER_CU 8
+#endif
+#ifndef CONVT_IG_MAX_ROWS
+#define CONVT_IG_MAX_ROWS 256
+#endif
+
 // Tuning knob: each XCD walks a contiguous range of a class's row chunks.
 #ifndef CONVT_IG_XCD_ORDER
 #define CONVT_IG_XCD_ORDER 1
@@ -856,8 +865,8 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
     Igemm3dParams P;
     const int64_t total_rows = fill_params(Pl, L, SW, P);
     // rows per block: enough blocks to fill the CUs several times over
-    const int64_t target_blocks = (int64_t)num_cus() * 16;
-    const int rpb = (int)std::max<int64_t>(1, std::min<int64_t>(64, total_rows / target_blocks));
+    const int64_t target_blocks = (int64_t)num_cus() * CONVT_IG_BLOCKS_PER_CU;
+    const int rpb = (int)std::max<int64_t>(1, std::min<int64_t>(CONVT_IG_MAX_ROWS, total_rows / target_blocks));
     const int blocks = assign_blocks(P, rpb, CONVT_IG_XCD_ORDER != 0);
     if (blocks == 0) return 0;
     constexpr int NT = COG * 4;
