@@ -44,6 +44,18 @@ __device__ __forceinline__ f4 load4u(const float *p) {
 }
 __device__ __forceinline__ void store4u(float *p, f4 v) { __builtin_memcpy(p, &v, 16); }
 
+// A buffer resource over one batch sample of y: the common-path stores then
+// take a row-invariant lane offset plus a uniform item offset (no 64-bit
+// address arithmetic per store).  Per-sample byte offsets stay below 2^31.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(float *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void buf_store4(f4 v, rsrc_t r, unsigned voff, unsigned soff) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, v),
+                                           r, voff, soff, 0);
+}
+
 // Compile-time phase table of one axis.
 template <int K, int S, int D> struct Phases {
     static constexpr int r_of(int k) { return (k * D) % S; }
@@ -67,6 +79,11 @@ template <int K, int S, int D> struct Phases {
         int m = 0;
         for (int k = 0; k < K; ++k) m = c_of(k) > m ? c_of(k) : m;
         return m;
+    }
+    static constexpr int first_k(int r) { // first tap of phase r
+        for (int k = 0; k < K; ++k)
+            if (r_of(k) == r) return k;
+        return -1;
     }
 };
 
@@ -214,6 +231,14 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
     float br[4];       // bias of rows co = 16ct + 4g4 + e
     int buf = 0;
     bool chain = false; // the previous item left its last outputs of each row in ocarry
+    // Per row set (n, g): the sample's y resource, and per row group e the
+    // lane's byte offset of its segment relative to the item offset 4*o_t,
+    // folding in a (the run's offset in its 64-byte line, the same for every
+    // item of a row since items advance 64S floats).
+    int rs_ng = -1;
+    rsrc_t ry = make_rsrc(y, 0);
+    unsigned lane_off[4] = {0u, 0u, 0u, 0u};
+    int a_row[4] = {0, 0, 0, 0};
 
     // Runs of consecutive items of one group share the weights: load them once
     // per run, outside the loop that carries the prefetch.
@@ -246,43 +271,35 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
         const bool has_next = ii + 1 < n_items;
         if (has_next) tile_fetch<CIG, NT>(pre, xrow_of(ng1), P.L_in, (P.st_lo + st1) * kTileQ, tid);
 
-        // The bias enters as the accumulators' start value.
+        // The bias enters as the accumulators' start value: the first MFMA of
+        // each phase takes it as its accumulator input.
         const f4 bias4 = f4{br[0], br[1], br[2], br[3]};
         f4 acc[NP][4];
+        if constexpr (Ph::count() == 0) {
 #pragma unroll
-        for (int s2 = 0; s2 < NP; ++s2)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc[s2][t] = bias4;
-
-        if constexpr (Ph::count() > 0) {
-            // B operands of input-channel step cig+1 are read from LDS while the
-            // MFMAs of step cig run.
+            for (int t = 0; t < 4; ++t) acc[0][t] = bias4;
+        } else {
             const float *tp = lds[buf] + g4 * kPitch + 4 * j;
-            f4 pv = *reinterpret_cast<const f4 *>(tp);     // q0+4j-4 .. -1
-            f4 cv = *reinterpret_cast<const f4 *>(tp + 4); // q0+4j .. +3
 #pragma unroll
             for (int cig = 0; cig < NCIG; ++cig) {
-                f4 pn = pv, cn = cv;
-                if (cig + 1 < NCIG) {
-                    pn = *reinterpret_cast<const f4 *>(tp + (cig + 1) * 4 * kPitch);
-                    cn = *reinterpret_cast<const f4 *>(tp + (cig + 1) * 4 * kPitch + 4);
-                }
-                __builtin_amdgcn_sched_barrier(0); // keep these reads ahead of the step's MFMAs
+                const float *rowp = tp + cig * 4 * kPitch;
+                const f4 pv = *reinterpret_cast<const f4 *>(rowp);     // q0+4j-4 .. -1
+                const f4 cv = *reinterpret_cast<const f4 *>(rowp + 4); // q0+4j .. +3
                 const float cur[4] = {cv.x, cv.y, cv.z, cv.w};
                 const float prv[4] = {pv.x, pv.y, pv.z, pv.w};
 #pragma unroll
                 for (int k = 0; k < K; ++k) {
                     const int c = Ph::c_of(k);
-                    const int sl = Ph::slot(Ph::r_of(k));
+                    const int r = Ph::r_of(k);
+                    const int sl = Ph::slot(r);
+                    const bool first = cig == 0 && k == Ph::first_k(r);
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const float bv = (t >= c) ? cur[(t - c) & 3] : prv[(t - c + 4) & 3];
-                        acc[sl][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(wr[k][cig], bv,
-                                                                          acc[sl][t], 0, 0, 0);
+                        acc[sl][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            wr[k][cig], bv, first ? bias4 : acc[sl][t], 0, 0, 0);
                     }
                 }
-                pv = pn;
-                cv = cn;
             }
         }
 
@@ -315,6 +332,50 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
 #pragma unroll
             for (int e = 0; e < 4; ++e) cin[e] = ocarry[ct][g4][e][j];
         }
+        if (rs_ng != ng) { // a new row set
+            rs_ng = ng;
+            ry = make_rsrc(y + (int64_t)n * P.C_out * P.L_out, (int)(4 * (int64_t)P.C_out * P.L_out));
+            const unsigned yel = (unsigned)((uintptr_t)y >> 2) + (unsigned)((int64_t)n * P.C_out * P.L_out);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = g * COG + 16 * ct + 4 * g4 + e;
+                a_row[e] = (int)((yel + (unsigned)row * (unsigned)P.L_out + (unsigned)o_t) & 15u);
+                lane_off[e] = 4u * ((unsigned)row * (unsigned)P.L_out + (unsigned)(4 * j - a_row[e]));
+            }
+        }
+        if (!FUSED && interior && chain_in && chain_out) {
+            // The common item: staging, carry and whole-line stores, with no
+            // per-store address arithmetic.
+            const unsigned item4 = 4u * (unsigned)o_t;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float v[4 * S];
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int r = 0; r < S; ++r) {
+                        float a = br[e];
+                        if constexpr (Ph::count() > 0)
+                            if (Ph::nonempty(r)) a = acc[Ph::slot(r)][t][e];
+                        v[t * S + r] = a;
+                    }
+                srow[j] = cin[e]; // the previous run's last 16 outputs
+#pragma unroll
+                for (int u = 0; u < 4 * S; ++u) srow[16 + 4 * S * j + u] = v[u];
+#pragma unroll
+                for (int u = 0; u < 4 * S; ++u) { // this run's last 16, from the lanes holding them
+                    const int i0 = 4 * S * j + u - (64 * S - 16);
+                    if (i0 >= 0) ocarry[ct][g4][e][i0] = v[u];
+                }
+                const float *ss = srow + 16 - a_row[e]; // the line-aligned segment
+#pragma unroll
+                for (int c = 0; c < S; ++c) {
+                    const int s0 = 64 * c + 4 * j;
+                    buf_store4(f4{ss[s0], ss[s0 + 1], ss[s0 + 2], ss[s0 + 3]}, ry,
+                               lane_off[e] + item4 + 256u * c, 0u);
+                }
+            }
+        } else {
         float *yrow = y + ((int64_t)n * P.C_out + (int64_t)g * COG + 16 * ct + 4 * g4) * P.L_out + o_t;
         const float *arow = FUSED ? add + (yrow - y) : nullptr;
 #pragma unroll
@@ -385,6 +446,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
                     }
                 }
             }
+        }
         }
 
         __syncthreads();
@@ -470,7 +532,9 @@ bool stream1d_supports(const convt_plan &P) {
     if (find_variant(P) < 0) return false;
     // 64-position tiles of one row must index within int range; the tile
     // fetch reads whole float4 inside a row
-    return P.ax[2].L_out < (1 << 30) && P.ax[2].L_in < (1 << 30) && P.ax[2].L_in >= 4;
+    // (and one sample of y below 2 GiB: the common-path stores use 31-bit offsets)
+    return P.ax[2].L_out < (1 << 30) && P.ax[2].L_in < (1 << 30) && P.ax[2].L_in >= 4 &&
+           4 * P.C_out * P.ax[2].L_out < INT32_MAX;
 }
 
 int launch_stream1d(const convt_plan &Pl, const float *x, const float *w, const float *bias,
