@@ -113,6 +113,7 @@ struct Igemm3dParams {
     int cls_block0[kMaxClasses + 1]; // classes ordered heaviest first
     int cls_chunks[kMaxClasses];     // row chunks (rows_per_block rows each) per class
     int xcd_order;                   // 1: each XCD walks a contiguous range of a class's chunks
+    int x_bytes;                     // bytes of x (wide variant: one buffer resource over it)
     int cls_rows[kMaxClasses];
     int cls_td[kMaxClasses], cls_th[kMaxClasses];
     int cls_kd[kMaxClasses][kTapMax], cls_cd[kMaxClasses][kTapMax];
@@ -479,11 +480,19 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
 // VGPRs, so they stream through LDS.  A workgroup of 4 waves owns 4 output
 // rows of one class (wave w: row w, all 64 output channels x NWB W-blocks, 16
 // accumulator tiles).  The contraction runs over stages (D/H tap slot x chunk
-// of CC input channels); each stage stages the weight chunk, transposed to
-// [kw][ci][co] so the A operands (W^T: 16 co x 4 ci) read without bank
-// conflicts, and the 4 rows' input rows, double-buffered.  Per (ci quad, kw):
-// 4 A reads and NWB B reads feed 4*NWB MFMAs.
-constexpr int kWidePWC = 80; // co pitch of the staged weights (16 mod 32 spreads the ci rows)
+// of CC input channels); each stage stages the weight chunk and the 4 rows'
+// input rows, double-buffered.  The weights are staged as [kw][ci][j][m] for
+// channel co = 16m + j, so one 16-byte read gives a lane its four A operands
+// (W^T: 16 co x 4 ci for m = 0..3).  Per (ci quad, kw): 1 A read and NWB B
+// reads feed 4*NWB MFMAs.  Staging offsets are fixed per thread for the
+// block; per stage only a uniform offset changes, and input rows outside the
+// input load as zeros through the buffer resource's range check.
+constexpr int kWidePWC = 64; // staged weights per (kw, ci): 64 channels as [j][m]
+// Two workgroups fit a CU's LDS, so two waves per SIMD: the register budget
+// that target allows keeps the accumulators in place across stages.
+#ifndef CONVT_IGW_WAVES_PER_EU
+#define CONVT_IGW_WAVES_PER_EU 2
+#endif
 
 // Row q (0..3) of four held in separate variables, by selects (an array
 // indexed with a per-lane value would live in scratch memory).
@@ -502,7 +511,8 @@ __device__ __forceinline__ RowPos pick_row(int q, const RowPos &A, const RowPos 
 }
 
 template <int CIG, int KW, int SW, int DW, int NWB, int CC, int PWX, bool FUSED>
-__global__ __launch_bounds__(256) void k_igemm3d_wide(const Igemm3dParams P,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CONVT_IGW_WAVES_PER_EU)))
+void k_igemm3d_wide(const Igemm3dParams P,
                                                       const float *__restrict__ x,
                                                       const float *__restrict__ w,
                                                       const float *__restrict__ bias,
@@ -516,7 +526,7 @@ __global__ __launch_bounds__(256) void k_igemm3d_wide(const Igemm3dParams P,
     constexpr int WPER = WPAIRS / NT;      // per thread
     constexpr int XPER = (4 * CC * 8 + NT - 1) / NT; // input rows: 4 rows x CC x (W_in/4 <= 8)
     static_assert(CIG % CC == 0 && CC % 4 == 0 && WPAIRS % NT == 0, "chunking");
-    static_assert(KW <= 4, "kernel taps along W");
+    static_assert(KW == 4, "one 16-byte weight load covers the W taps");
 
     __shared__ __attribute__((aligned(16))) float Wl[2][KW][CC][kWidePWC];
     __shared__ __attribute__((aligned(16))) float Xl[2][4][CC][PWX];
@@ -544,74 +554,74 @@ __global__ __launch_bounds__(256) void k_igemm3d_wide(const Igemm3dParams P,
     const RowPos R2 = decode_row(P, cls, r0 + min(2, nrows - 1));
     const RowPos R3 = decode_row(P, cls, r0 + min(3, nrows - 1));
 
-    f4 wpre[WPER][1];
-    float wsc[WPER][KW];
+    // Per-thread staging offsets, fixed for the block.
+    const int KDHW = P.KD * P.KH * KW;
+    const int dhw = P.D_in * P.H_in * P.W_in;
+    unsigned wo4[WPER]; // weight byte offset of (ci in chunk, co), tap part excluded
+    int wlo[WPER];      // its LDS index in a [kw] plane: ci*64 + 4*(co mod 16) + co/16
+#pragma unroll
+    for (int u = 0; u < WPER; ++u) {
+        const int pr = tid + u * NT;
+        const int cil = pr / COG, co = pr - cil * COG;
+        wo4[u] = 4u * (unsigned)((cil * COG + co) * KDHW);
+        wlo[u] = cil * kWidePWC + 4 * (co & 15) + (co >> 4);
+    }
+    int xo[XPER];  // input element offset of (row, ci in chunk, float4) at the row's (qd, qh)
+    int xlo[XPER]; // its LDS index, -1 past the staged float4s
+    int xrw[XPER]; // its row, 31 past the staged float4s
+#pragma unroll
+    for (int u = 0; u < XPER; ++u) {
+        const int f = tid + u * NT;
+        const bool in = f < 4 * CC * W4;
+        const int rr = in ? f / (CC * W4) : 3;
+        const int rem = f - rr * (CC * W4);
+        const int cil = rem / W4, c4 = rem - cil * W4;
+        const RowPos R = pick_row(rr, R0, R1, R2, R3);
+        xo[u] = (((R.n * P.C_in + cil) * P.D_in + R.qd) * P.H_in + R.qh) * P.W_in + 4 * c4;
+        xlo[u] = in ? (rr * CC + cil) * PWX + 4 * c4 - P.iw_lo : -1;
+        xrw[u] = in ? rr : 31;
+    }
+    const rsrc_t rw_ = make_rsrc(w, 4 * P.C_in * COG * KDHW);
+    const rsrc_t rx = make_rsrc(x, P.x_bytes);
+
+    f4 wpre[WPER];
     f4 xpre[XPER];
-    unsigned xvalid = 0;
 
     auto fetch = [&](int sidx) {
         const int slot = sidx / NCH, ch = sidx - slot * NCH;
         const int jd = slot / th, jh = slot - jd * th;
         const int kd = P.cls_kd[cls][jd], kh = P.cls_kh[cls][jh];
         const int cd = P.cls_cd[cls][jd], chh = P.cls_ch[cls][jh];
+        const unsigned wst = 4u * (unsigned)(ch * CC * COG * KDHW + (kd * P.KH + kh) * KW);
 #pragma unroll
-        for (int u = 0; u < WPER; ++u) {
-            const int pr = tid + u * NT;
-            const int cil = pr / COG, co = pr - cil * COG;
-            const float *src =
-                w + ((((int64_t)(ch * CC + cil) * COG + co) * P.KD + kd) * P.KH + kh) * KW;
-            if constexpr (KW == 4) {
-                wpre[u][0] = load4u(src);
-            } else {
+        for (int u = 0; u < WPER; ++u)
+            wpre[u] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rw_, wo4[u], wst, 0));
+        // rows whose input row (qd - cd, qh - ch) lies inside the input: one bit each
+        unsigned bad = 0xffffffffu;
 #pragma unroll
-                for (int k = 0; k < KW; ++k) wsc[u][k] = src[k];
-            }
+        for (int q = 0; q < 4; ++q) {
+            const RowPos &R = q == 0 ? R0 : q == 1 ? R1 : q == 2 ? R2 : R3;
+            const int id = R.qd - cd, ih = R.qh - chh;
+            if (q < nrows && id >= 0 && id < P.D_in && ih >= 0 && ih < P.H_in) bad &= ~(1u << q);
         }
-        xvalid = 0;
+        const int xst = ch * CC * dhw - (cd * P.H_in + chh) * P.W_in;
 #pragma unroll
         for (int u = 0; u < XPER; ++u) {
-            const int f = tid + u * NT;
-            const int rr = f / (CC * W4);
-            const int rem = f - rr * (CC * W4);
-            const int cil = rem / W4, c4 = rem - cil * W4;
-            const RowPos R = pick_row(rr, R0, R1, R2, R3);
-            const int id = R.qd - cd, ih = R.qh - chh;
-            const bool ok = f < 4 * CC * W4 && rr < nrows && id >= 0 && id < P.D_in && ih >= 0 &&
-                            ih < P.H_in;
-            const int64_t off =
-                ok ? ((((int64_t)R.n * P.C_in + ch * CC + cil) * P.D_in + id) * P.H_in + ih) *
-                             P.W_in + 4 * c4
-                   : 0;
-            xpre[u] = load4u(x + off);
-            xvalid |= ok ? (1u << u) : 0u;
+            const unsigned off = ((bad >> xrw[u]) << 31) | (4u * (unsigned)(xo[u] + xst));
+            xpre[u] = buf_load4(rx, off);
         }
     };
     auto stash = [&](int b) {
 #pragma unroll
         for (int u = 0; u < WPER; ++u) {
-            const int pr = tid + u * NT;
-            const int cil = pr / COG, co = pr - cil * COG;
-            if constexpr (KW == 4) {
-                Wl[b][0][cil][co] = wpre[u][0].x;
-                Wl[b][1][cil][co] = wpre[u][0].y;
-                Wl[b][2][cil][co] = wpre[u][0].z;
-                Wl[b][3][cil][co] = wpre[u][0].w;
-            } else {
-#pragma unroll
-                for (int k = 0; k < KW; ++k) Wl[b][k][cil][co] = wsc[u][k];
-            }
+            (&Wl[b][0][0][0])[wlo[u]] = wpre[u].x;
+            (&Wl[b][1][0][0])[wlo[u]] = wpre[u].y;
+            (&Wl[b][2][0][0])[wlo[u]] = wpre[u].z;
+            (&Wl[b][3][0][0])[wlo[u]] = wpre[u].w;
         }
 #pragma unroll
-        for (int u = 0; u < XPER; ++u) {
-            const int f = tid + u * NT;
-            if (f < 4 * CC * W4) {
-                const int rr = f / (CC * W4);
-                const int rem = f - rr * (CC * W4);
-                const int cil = rem / W4, c4 = rem - cil * W4;
-                const f4 v = (xvalid >> u) & 1u ? xpre[u] : f4{0.0f, 0.0f, 0.0f, 0.0f};
-                *reinterpret_cast<f4 *>(&Xl[b][rr][cil][4 * c4 - P.iw_lo]) = v;
-            }
-        }
+        for (int u = 0; u < XPER; ++u)
+            if (xlo[u] >= 0) *reinterpret_cast<f4 *>(&Xl[b][0][0][0] + xlo[u]) = xpre[u];
     };
 
     f4 acc[4][NPH][NWB];
@@ -634,6 +644,19 @@ __global__ __launch_bounds__(256) void k_igemm3d_wide(const Igemm3dParams P,
         const bool has_next = sidx + 1 < nstages;
         if (has_next) fetch(sidx + 1);
         if (active && Ph::count() > 0) {
+            typedef const __attribute__((address_space(3))) float *lds_ptr;
+            typedef const __attribute__((address_space(3))) f4 *lds_f4ptr;
+            const lds_ptr abase = (lds_ptr)(&Wl[b][0][g4][4 * j]);
+            // one base per (W phase, tap shift), relations hidden (see k_igemm3d)
+            constexpr int CM = Ph::cmax() + 1;
+            lds_ptr bb[SW][CM];
+#pragma unroll
+            for (int rw = 0; rw < SW; ++rw)
+#pragma unroll
+                for (int c = 0; c < CM; ++c) {
+                    bb[rw][c] = (lds_ptr)(&Xl[b][wv][g4][0] + P.qw0[rw] + j - c - P.iw_lo);
+                    asm volatile("" : "+v"(bb[rw][c]));
+                }
 #pragma unroll
             for (int cig = 0; cig < CC / 4; ++cig) {
 #pragma unroll
@@ -641,12 +664,11 @@ __global__ __launch_bounds__(256) void k_igemm3d_wide(const Igemm3dParams P,
                     const int rw = Ph::r_of(kw);
                     const int ph = Ph::slot(rw);
                     const int c = Ph::c_of(kw);
-                    float a[4];
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) a[m] = Wl[b][kw][4 * cig + g4][16 * m + j];
+                    const f4 a4 = *(lds_f4ptr)(abase + (kw * CC + 4 * cig) * kWidePWC);
+                    const float a[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
                     for (int t = 0; t < NWB; ++t) {
-                        const float bv = Xl[b][wv][4 * cig + g4][P.qw0[rw] + 16 * t + j - c - P.iw_lo];
+                        const float bv = bb[rw][c][4 * cig * PWX + 16 * t];
 #pragma unroll
                         for (int m = 0; m < 4; ++m)
                             acc[m][ph][t] =
@@ -894,6 +916,8 @@ constexpr int kNumWide = (int)(sizeof(kWide) / sizeof(kWide[0]));
 
 int find_wide(const convt_plan &P, Layout *Lout) {
     if (P.ndim != 3 || P.G != 1 || P.Cog != 64) return -1;
+    // one buffer resource spans x (31-bit byte offsets); per-sample y as in the VGPR variant
+    if (4 * P.N * P.C_in * P.in_sp >= INT32_MAX || 4 * P.C_out * P.out_sp >= INT32_MAX) return -1;
     const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
     if (AW.L_in % 4 != 0 || AW.L_in / 4 > 8) return -1;
     if (AD.s * AH.s > kMaxClasses) return -1;
@@ -918,6 +942,7 @@ int launch_wide(const convt_plan &Pl, const Layout &L, const float *x, const flo
                 const float *bias, const float *add, float *y, hipStream_t st) {
     Igemm3dParams P;
     fill_params(Pl, L, SW, P);
+    P.x_bytes = (int)(4 * Pl.N * Pl.C_in * Pl.in_sp);
     const int blocks = assign_blocks(P, 4);
     if (blocks == 0) return 0;
     if (add)
