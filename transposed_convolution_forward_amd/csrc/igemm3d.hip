@@ -170,7 +170,7 @@ __device__ __forceinline__ void buf_store2(float a, float b, rsrc_t r, unsigned 
 }
 
 template <int CIG, int COG, int KW, int SW, int DW, int TDM, int THM, int NWBM, int PWM, int PER,
-          bool FUSED>
+          bool FUSED, bool FULLW>
 __global__ __launch_bounds__(COG * 4)
 __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const Igemm3dParams P,
                                                      const float *__restrict__ x,
@@ -329,13 +329,20 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
             }
     };
 
-    f4 pre[PER];
+    // Input rows are fetched two rows ahead, before the current row's stores:
+    // the vector-memory counter retires in issue order, so the wait for them
+    // then covers only stores issued two rows earlier.  (With rows that
+    // every lane fills, FULLW, each path issues the same stores and the
+    // compiler's wait counts stay exact.)  Past the block's last row the last
+    // row is fetched again, never used.
+    f4 pre0[PER], pre1[PER];
     float av[NWBM][4][SW], avn[NWBM][4][SW];
     RowPos R = decode_row(P, cls, r_begin);
     __syncthreads(); // LDS zeroed before the first row lands
-    fetch_rows(pre, R);
+    fetch_rows(pre0, R);
+    store_rows(lds[0], pre0);
+    fetch_rows(pre0, decode_row(P, cls, min(r_begin + 1, r_end - 1)));
     if constexpr (FUSED) fetch_add(av, R);
-    store_rows(lds[0], pre);
     __syncthreads();
 
     const f4 bias4 = f4{bo[0], bo[1], bo[2], bo[3]};
@@ -343,12 +350,12 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     int buf = 0;
     // One output row; the loop below runs it twice per trip with the two
     // add_input register sets swapped, so the prefetched set needs no copy.
-    auto row_step = [&](const int r, const auto &av, auto &avn) {
+    auto row_step = [&](const int r, const auto &av, auto &avn, auto &pre, auto &pre2) {
         const bool has_next = r + 1 < r_end;
-        // inputs of the next row, issued unconditionally (the last row fetches
-        // itself again) so the wait counts stay exact: x rows, then add_input
+        // x rows of row r+2 (into pre2), then add_input of row r+1; pre holds
+        // the x rows of row r+1, fetched a row earlier
         const RowPos Rn = decode_row(P, cls, has_next ? r + 1 : r);
-        fetch_rows(pre, Rn);
+        fetch_rows(pre2, decode_row(P, cls, min(r + 2, r_end - 1)));
         if constexpr (FUSED) fetch_add(avn, Rn);
 
         // The bias enters as the accumulators' start value: the first MFMA of
@@ -447,7 +454,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
                         for (int rr = 0; rr < SW; ++rr) v[rr] = times_hardswish(v[rr] + av[t][e][rr]);
                     }
                     const unsigned o = vo + 4 * SW * 16 * t;
-                    if (ow0 + SW <= P.W_out) {
+                    if (FULLW || ow0 + SW <= P.W_out) {
                         if constexpr (SW == 2) {
                             buf_store2(v[0], v[1], ry, o, e * e4);
                         } else {
@@ -470,8 +477,8 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
         R = Rn;
     };
     for (int r = r_begin; r < r_end; r += 2) {
-        row_step(r, av, avn);
-        if (r + 1 < r_end) row_step(r + 1, avn, av);
+        row_step(r, av, avn, pre0, pre1);
+        if (r + 1 < r_end) row_step(r + 1, avn, av, pre1, pre0);
     }
 }
 
@@ -895,11 +902,19 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
     constexpr int PER = (TDM * THM * CIG * W4M + NT - 1) / NT; // W_in <= 4*W4M is checked
     const int need_f = TDM * THM * CIG * (Pl.ax[2].L_in / 4);
     if (need_f > PER * NT) return (int)hipErrorInvalidValue;
-    if (add)
-        hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, true>),
+    // every lane of every W-block inside the row
+    const bool fullw = Pl.ax[2].L_out == SW * 16 * NWBM;
+    if (add && fullw)
+        hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, true, true>),
+                           dim3(blocks), dim3(NT), 0, st, P, x, w, bias, add, y);
+    else if (add)
+        hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, true, false>),
+                           dim3(blocks), dim3(NT), 0, st, P, x, w, bias, add, y);
+    else if (fullw)
+        hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, false, true>),
                            dim3(blocks), dim3(NT), 0, st, P, x, w, bias, add, y);
     else
-        hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, false>),
+        hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, false, false>),
                            dim3(blocks), dim3(NT), 0, st, P, x, w, bias, add, y);
     return (int)hipGetLastError();
 }
