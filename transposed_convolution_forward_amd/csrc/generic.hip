@@ -102,6 +102,10 @@ __global__ __launch_bounds__(kBlock) void k_generic(const GenericParams P,
 // ("Kimi-K2.6 l1_p72" transcript, ConvTranspose3d): a block never mixes
 // classes, so trip counts stay uniform.
 constexpr int kMaxPhaseCls = 32;
+#ifndef CONVT_GEN_POS
+#define CONVT_GEN_POS 2
+#endif
+constexpr int kPhasePos = CONVT_GEN_POS; // positions per thread
 
 int pick_cpt(int64_t Cog) { return Cog >= 8 ? 8 : Cog >= 4 ? 4 : Cog >= 2 ? 2 : 1; }
 
@@ -120,33 +124,45 @@ struct PhaseParams {
 };
 constexpr int kMaxPhaseLds = 32768; // bytes of staged weights per workgroup
 
-template <int CPT, bool FUSED>
+template <int CPT, int NPOS, bool FUSED>
 __global__ __launch_bounds__(kBlock) void k_generic_phase(const PhaseParams P,
                                                           const float *__restrict__ x,
                                                           const float *__restrict__ w,
                                                           const float *__restrict__ bias,
                                                           const float *add, float *y) {
+    // Each thread computes NPOS positions of the class, kBlock apart (so each
+    // of its loads still coalesces with the neighbouring lanes'), sharing
+    // every weight read among NPOS*CPT FMAs.
     int c = 0;
     while (c + 1 < P.n_cls && (int)blockIdx.x >= P.cls_blk0[c + 1]) ++c;
-    const int l = ((int)blockIdx.x - P.cls_blk0[c]) * kBlock + (int)threadIdx.x;
     const int nqd = P.cls_nq[c][0], nqh = P.cls_nq[c][1], nqw = P.cls_nq[c][2];
-    const bool live = l < nqd * nqh * nqw;
-    const int iqw = l % nqw;
-    const int t2 = l / nqw;
-    const int iqh = t2 % nqh;
-    const int iqd = t2 / nqh;
     const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
     const int rd = P.cls_r[c][0], rh = P.cls_r[c][1], rw = P.cls_r[c][2];
-    const int qd = P.cls_q0[c][0] + iqd, qh = P.cls_q0[c][1] + iqh, qw = P.cls_q0[c][2] + iqw;
+    bool live[NPOS];
+    int qd[NPOS], qh[NPOS], qw[NPOS];
+#pragma unroll
+    for (int u = 0; u < NPOS; ++u) {
+        const int l = ((int)blockIdx.x - P.cls_blk0[c]) * (kBlock * NPOS) + u * kBlock + (int)threadIdx.x;
+        live[u] = l < nqd * nqh * nqw;
+        const int iqw = l % nqw;
+        const int t2 = l / nqw;
+        const int iqh = t2 % nqh;
+        const int iqd = t2 / nqh;
+        qd[u] = P.cls_q0[c][0] + iqd;
+        qh[u] = P.cls_q0[c][1] + iqh;
+        qw[u] = P.cls_q0[c][2] + iqw;
+    }
 
     const int g = blockIdx.y / P.co_chunks;
     const int co0 = (blockIdx.y % P.co_chunks) * CPT;
     const int n = P.n0 + blockIdx.z;
     const int ncol = min(CPT, P.Cog - co0);
 
-    float acc[CPT];
+    float acc[NPOS][CPT];
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) acc[j] = 0.0f;
+    for (int u = 0; u < NPOS; ++u)
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) acc[u][j] = 0.0f;
 
     // The workgroup's weights, [class tap][input channel][column], staged once:
     // every lane reads the same ones, so the reads below are broadcasts.
@@ -173,39 +189,52 @@ __global__ __launch_bounds__(kBlock) void k_generic_phase(const PhaseParams P,
     const float *xg = x + ((int64_t)n * P.C_in + (int64_t)g * P.Cig) * P.in_sp;
     const float *wt = wl;
     for (int jd = AD.tap_start[rd]; jd < AD.tap_start[rd + 1]; ++jd) {
-        const int id = qd - AD.tap_c[jd];
-        const bool okd = id >= 0 && id < AD.L_in;
         for (int jh = AH.tap_start[rh]; jh < AH.tap_start[rh + 1]; ++jh) {
-            const int ih = qh - AH.tap_c[jh];
-            const bool okh = okd && ih >= 0 && ih < AH.L_in;
             for (int jw = AW.tap_start[rw]; jw < AW.tap_start[rw + 1]; ++jw, wt += P.Cig * CPT) {
-                const int iw = qw - AW.tap_c[jw];
-                const bool ok = live && okh && iw >= 0 && iw < AW.L_in;
-                // lanes outside the input read the group's first element and use 0
-                const float *xp = xg + (ok ? (id * AH.L_in + ih) * AW.L_in + iw : 0);
+                bool ok[NPOS];
+                const float *xp[NPOS];
+#pragma unroll
+                for (int u = 0; u < NPOS; ++u) {
+                    const int id = qd[u] - AD.tap_c[jd], ih = qh[u] - AH.tap_c[jh], iw = qw[u] - AW.tap_c[jw];
+                    ok[u] = live[u] && id >= 0 && id < AD.L_in && ih >= 0 && ih < AH.L_in && iw >= 0 &&
+                            iw < AW.L_in;
+                    // lanes outside the input read the group's first element and use 0
+                    xp[u] = xg + (ok[u] ? (id * AH.L_in + ih) * AW.L_in + iw : 0);
+                }
 #pragma unroll 4
                 for (int ci = 0; ci < P.Cig; ++ci) {
-                    const float xr = xp[(int64_t)ci * P.in_sp];
-                    const float xv = ok ? xr : 0.0f;
+                    float xv[NPOS];
+#pragma unroll
+                    for (int u = 0; u < NPOS; ++u) {
+                        const float xr = xp[u][(int64_t)ci * P.in_sp];
+                        xv[u] = ok[u] ? xr : 0.0f;
+                    }
                     const float *wc = wt + ci * CPT;
 #pragma unroll
-                    for (int j = 0; j < CPT; ++j) acc[j] = fmaf(xv, wc[j], acc[j]);
+                    for (int j = 0; j < CPT; ++j) {
+                        const float wv = wc[j];
+#pragma unroll
+                        for (int u = 0; u < NPOS; ++u) acc[u][j] = fmaf(xv[u], wv, acc[u][j]);
+                    }
                 }
             }
         }
     }
-    if (!live) return;
 
-    const int od = qd * AD.s + rd - AD.p, oh = qh * AH.s + rh - AH.p, ow = qw * AW.s + rw - AW.p;
-    const int sp = (od * AH.L_out + oh) * AW.L_out + ow;
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) {
-        if (j >= ncol) break;
-        const int co = g * P.Cog + co0 + j;
-        const int64_t idx = ((int64_t)n * P.C_out + co) * P.out_sp + sp;
-        const float b = bias ? bias[co] : 0.0f;
-        const float a = FUSED ? add[idx] : 0.0f;
-        y[idx] = epilogue<FUSED>(acc[j], b, a);
+    for (int u = 0; u < NPOS; ++u) {
+        if (!live[u]) continue;
+        const int od = qd[u] * AD.s + rd - AD.p, oh = qh[u] * AH.s + rh - AH.p, ow = qw[u] * AW.s + rw - AW.p;
+        const int sp = (od * AH.L_out + oh) * AW.L_out + ow;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            if (j >= ncol) break;
+            const int co = g * P.Cog + co0 + j;
+            const int64_t idx = ((int64_t)n * P.C_out + co) * P.out_sp + sp;
+            const float b = bias ? bias[co] : 0.0f;
+            const float a = FUSED ? add[idx] : 0.0f;
+            y[idx] = epilogue<FUSED>(acc[u][j], b, a);
+        }
     }
 }
 
@@ -242,7 +271,7 @@ bool phase_classes(const convt_plan &Pl, PhaseParams &P) {
                 for (int a = 0; a < kAxes; ++a) taps *= A[a].tap_start[r[a] + 1] - A[a].tap_start[r[a]];
                 P.max_taps = taps > P.max_taps ? taps : P.max_taps;
                 const int64_t pos = (int64_t)nq[0] * nq[1] * nq[2];
-                blocks += (int)((pos + kBlock - 1) / kBlock);
+                blocks += (int)((pos + kBlock * kPhasePos - 1) / (kBlock * kPhasePos));
             }
     P.cls_blk0[P.n_cls] = blocks;
     // the staged weights of the class with the most taps must fit in LDS
@@ -262,10 +291,10 @@ int launch_phase(const convt_plan &Pl, PhaseParams &P, const float *x, const flo
         dim3 grid(gx, gy, gz);
         const size_t lds = (size_t)P.max_taps * Pl.Cig * CPT * sizeof(float);
         if (add)
-            hipLaunchKernelGGL((k_generic_phase<CPT, true>), grid, dim3(kBlock), lds, st, P, x, w,
+            hipLaunchKernelGGL((k_generic_phase<CPT, kPhasePos, true>), grid, dim3(kBlock), lds, st, P, x, w,
                                bias, add, y);
         else
-            hipLaunchKernelGGL((k_generic_phase<CPT, false>), grid, dim3(kBlock), lds, st, P, x, w,
+            hipLaunchKernelGGL((k_generic_phase<CPT, kPhasePos, false>), grid, dim3(kBlock), lds, st, P, x, w,
                                bias, add, y);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
