@@ -56,6 +56,10 @@ __device__ __forceinline__ void buf_store4(f4 v, rsrc_t r, unsigned voff, unsign
                                            r, voff, soff, 0);
 }
 
+__device__ __forceinline__ f4 buf_load4(rsrc_t r, unsigned voff, unsigned soff) {
+    return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
 // Compile-time phase table of one axis.
 template <int K, int S, int D> struct Phases {
     static constexpr int r_of(int k) { return (k * D) % S; }
@@ -125,6 +129,19 @@ __device__ __forceinline__ float pick4(const f4 &v, int i) {
     return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
+// The same fetch for a tile wholly inside the row (q0 >= 4, q0 + 64 <= L_in),
+// through a buffer resource over the row set's CIG input rows: per thread a
+// fixed byte offset xo[u] (row and float4 column) plus the uniform
+// 4*(q0 - 4) in the scalar offset, so no address arithmetic per tile.
+template <int CIG, int NT>
+__device__ __forceinline__ void tile_fetch_inner(f4 (&r)[(CIG * kRowF4 + NT - 1) / NT], rsrc_t rx,
+                                                 const unsigned (&xo)[(CIG * kRowF4 + NT - 1) / NT],
+                                                 int q0) {
+    constexpr int PER = (CIG * kRowF4 + NT - 1) / NT;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) r[u] = buf_load4(rx, xo[u], 4u * (unsigned)(q0 - 4));
+}
+
 template <int CIG, int NT>
 __device__ __forceinline__ void tile_store_lds(float *lds, const f4 (&r)[(CIG * kRowF4 + NT - 1) / NT],
                                                int L_in, int q0, int tid) {
@@ -159,20 +176,22 @@ __device__ __forceinline__ void tile_store_lds(float *lds, const f4 (&r)[(CIG * 
 }
 
 // Output lines.  Rows may have any length, so the outputs o_t .. o_t + 64S - 1
-// of a work item start anywhere in a 64-byte line, at a different place in
-// every row; stored as they stand, the line at each end of the run is split
+// of a work item start anywhere in a 128-byte cache line, at a different place
+// in every row; stored as they stand, the line at each end of the run is split
 // between two items written microseconds apart, and such partly written lines
-// drain to HBM far slower than whole ones.  So for each row an item stores the
-// 64S outputs from the line boundary at or before o_t: the first a of them
-// (0 <= a < 16, the offset of o_t in its line) are the previous item's last
+// drain to HBM far slower than whole ones (runs aligned to 64 bytes only are
+// still 15% slower than runs aligned to 128).  So for each row an item stores
+// the 64S outputs from the line boundary at or before o_t: the first a of them
+// (0 <= a < 32, the offset of o_t in its line) are the previous item's last
 // outputs, carried over, and its own last a outputs are carried to the next
 // item.  The row-dependent shift by a and the carry pass through LDS that
 // belongs to one wave (no barrier): a staging row per accumulator row group,
-// holding the carry at [16 - a, 16) and the item's outputs at [16, 16 + 64S),
-// and a 16-float carry slot per output row.  Store c of lane j then writes
+// holding the carry at [32 - a, 32) and the item's outputs at [32, 32 + 64S),
+// and a 32-float carry slot per output row.  Store c of lane j then writes
 // the 16 bytes at 64c + 4j of its row's segment, so one store instruction
 // covers four rows with 256 contiguous, line-aligned bytes each.
-template <int S> constexpr int stage_pitch() { return 16 + 64 * S + 4; } // +4: spread banks
+constexpr int kLineF = 32; // floats per 128-byte line
+template <int S> constexpr int stage_pitch() { return kLineF + 64 * S + 4; } // +4: spread banks
 
 // Tuning knobs: minimum waves per SIMD the register allocation must allow,
 // and resident workgroups aimed for per CU when sizing the grid.
@@ -205,7 +224,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
 
     __shared__ __attribute__((aligned(16))) float lds[2][CIG * kPitch];
     __shared__ __attribute__((aligned(16))) float ostage[COT][4][stage_pitch<S>()];
-    __shared__ __attribute__((aligned(16))) float ocarry[COT][4][4][16]; // [wave][g4][e][slot]
+    __shared__ __attribute__((aligned(16))) float ocarry[COT][4][4][kLineF]; // [wave][g4][e][slot]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -222,8 +241,23 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
     int ng = (int)(it0 / P.n_st);
     auto xrow_of = [&](int ng_) { return x + (int64_t)ng_ * CIG * P.L_in; }; // (n*G+g)*CIG = n*C_in + g*CIG
 
+    unsigned xo[PER]; // byte offsets of this thread's float4 in a tile wholly inside the row
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int f = min(tid + u * NT, CIG * kRowF4 - 1);
+        xo[u] = 4u * (unsigned)((f / kRowF4) * P.L_in + 4 * (f % kRowF4));
+    }
+    const int x_bytes = 4 * CIG * P.L_in; // one row set's input rows (below 2 GiB)
+    // Tiles inside the row take buffer loads at fixed offsets; the others clamp.
+    auto fetch = [&](f4 (&r)[PER], int ng_, int q0_) {
+        if (q0_ - 4 >= 0 && q0_ + kTileQ <= P.L_in)
+            tile_fetch_inner<CIG, NT>(r, make_rsrc(const_cast<float *>(xrow_of(ng_)), x_bytes), xo, q0_);
+        else
+            tile_fetch<CIG, NT>(r, xrow_of(ng_), P.L_in, q0_, tid);
+    };
+
     f4 pre[PER];
-    tile_fetch<CIG, NT>(pre, xrow_of(ng), P.L_in, (P.st_lo + st) * kTileQ, tid);
+    fetch(pre, ng, (P.st_lo + st) * kTileQ);
     tile_store_lds<CIG, NT>(lds[0], pre, P.L_in, (P.st_lo + st) * kTileQ, tid);
     __syncthreads();
 
@@ -232,13 +266,28 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
     int buf = 0;
     bool chain = false; // the previous item left its last outputs of each row in ocarry
     // Per row set (n, g): the sample's y resource, and per row group e the
-    // lane's byte offset of its segment relative to the item offset 4*o_t,
-    // folding in a (the run's offset in its 64-byte line, the same for every
-    // item of a row since items advance 64S floats).
+    // lane's byte offset of its segment relative to the item offset
+    // 4*(o_t - 32), folding in a (the run's offset in its 128-byte line, the
+    // same for every item of a row since items advance 64S floats).
     int rs_ng = -1;
     rsrc_t ry = make_rsrc(y, 0);
     unsigned lane_off[4] = {0u, 0u, 0u, 0u};
     int a_row[4] = {0, 0, 0, 0};
+    float *srow = &ostage[ct][g4][0];
+    // Common-path staging: this lane's outputs of phase r go to
+    // sph[r][S*t] (t = 0..3), written straight from the accumulators (dword
+    // LDS writes, no register packing: the empty asm hides the pointers'
+    // relation, so the compiler cannot merge the phases into 16-byte writes
+    // that need the values gathered first); the segment of row group e is
+    // read from seg[e][64c].
+    typedef __attribute__((address_space(3))) float *lds_fptr;
+    lds_fptr sph[S];
+#pragma unroll
+    for (int r = 0; r < S; ++r) {
+        sph[r] = (lds_fptr)(srow + kLineF + 4 * S * j + r);
+        asm volatile("" : "+v"(sph[r]));
+    }
+    const float *seg[4] = {srow, srow, srow, srow};
 
     // Runs of consecutive items of one group share the weights: load them once
     // per run, outside the loop that carries the prefetch.
@@ -269,7 +318,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
         int st1 = st + 1, ng1 = ng;
         if (st1 == P.n_st) { st1 = 0; ++ng1; }
         const bool has_next = ii + 1 < n_items;
-        if (has_next) tile_fetch<CIG, NT>(pre, xrow_of(ng1), P.L_in, (P.st_lo + st1) * kTileQ, tid);
+        if (has_next) fetch(pre, ng1, (P.st_lo + st1) * kTileQ);
 
         // The bias enters as the accumulators' start value: the first MFMA of
         // each phase takes it as its accumulator input.
@@ -326,12 +375,6 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
         const bool chain_out =
             interior && has_next && st1 != 0 && o_t + 128 * S <= P.L_out; // next: same rows, interior
         chain = chain_out;
-        float *srow = &ostage[ct][g4][0];
-        float cin[4] = {0.0f, 0.0f, 0.0f, 0.0f}; // carried outputs, slot j of each row
-        if (chain_in) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) cin[e] = ocarry[ct][g4][e][j];
-        }
         if (rs_ng != ng) { // a new row set
             rs_ng = ng;
             ry = make_rsrc(y + (int64_t)n * P.C_out * P.L_out, (int)(4 * (int64_t)P.C_out * P.L_out));
@@ -339,41 +382,42 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = g * COG + 16 * ct + 4 * g4 + e;
-                a_row[e] = (int)((yel + (unsigned)row * (unsigned)P.L_out + (unsigned)o_t) & 15u);
-                lane_off[e] = 4u * ((unsigned)row * (unsigned)P.L_out + (unsigned)(4 * j - a_row[e]));
+                a_row[e] = (int)((yel + (unsigned)row * (unsigned)P.L_out + (unsigned)o_t) & (kLineF - 1u));
+                // non-negative (the range check drops a store whose vector
+                // offset wraps): kLineF floats are moved out of the scalar
+                // item offset, which stays >= 0 since a chained item has
+                // o_t >= 64S
+                lane_off[e] = 4u * ((unsigned)row * (unsigned)P.L_out + (unsigned)(4 * j + kLineF - a_row[e]));
+                seg[e] = srow + kLineF - a_row[e] + 4 * j;
             }
         }
         if (!FUSED && interior && chain_in && chain_out) {
             // The common item: staging, carry and whole-line stores, with no
             // per-store address arithmetic.
-            const unsigned item4 = 4u * (unsigned)o_t;
+            const unsigned item4 = 4u * (unsigned)(o_t - kLineF);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                float v[4 * S];
+                // The previous run's last 32 outputs, then this run's outputs.
+                srow[j] = ocarry[ct][g4][e][j];
+                srow[j + 16] = ocarry[ct][g4][e][j + 16];
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
+                for (int r = 0; r < S; ++r)
 #pragma unroll
-                    for (int r = 0; r < S; ++r) {
+                    for (int t = 0; t < 4; ++t) {
                         float a = br[e];
                         if constexpr (Ph::count() > 0)
                             if (Ph::nonempty(r)) a = acc[Ph::slot(r)][t][e];
-                        v[t * S + r] = a;
+                        sph[r][S * t] = a;
                     }
-                srow[j] = cin[e]; // the previous run's last 16 outputs
+                // This run's last 32 outputs become the next run's carry (one
+                // wave's LDS accesses are performed in order).
+                ocarry[ct][g4][e][j] = srow[64 * S + j];
+                ocarry[ct][g4][e][j + 16] = srow[64 * S + j + 16];
+                const float *ss = seg[e]; // the line-aligned segment
 #pragma unroll
-                for (int u = 0; u < 4 * S; ++u) srow[16 + 4 * S * j + u] = v[u];
-#pragma unroll
-                for (int u = 0; u < 4 * S; ++u) { // this run's last 16, from the lanes holding them
-                    const int i0 = 4 * S * j + u - (64 * S - 16);
-                    if (i0 >= 0) ocarry[ct][g4][e][i0] = v[u];
-                }
-                const float *ss = srow + 16 - a_row[e]; // the line-aligned segment
-#pragma unroll
-                for (int c = 0; c < S; ++c) {
-                    const int s0 = 64 * c + 4 * j;
-                    buf_store4(f4{ss[s0], ss[s0 + 1], ss[s0 + 2], ss[s0 + 3]}, ry,
-                               lane_off[e] + item4 + 256u * c, 0u);
-                }
+                for (int c = 0; c < S; ++c)
+                    buf_store4(f4{ss[64 * c], ss[64 * c + 1], ss[64 * c + 2], ss[64 * c + 3]}, ry,
+                               lane_off[e] + 256u * c, item4);
             }
         } else {
         float *yrow = y + ((int64_t)n * P.C_out + (int64_t)g * COG + 16 * ct + 4 * g4) * P.L_out + o_t;
@@ -403,23 +447,26 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
                         v[4 * c + 3] = times_hardswish(v[4 * c + 3] + a4.w);
                     }
                 }
-                const int a = (int)(((uintptr_t)yr >> 2) & 15); // o_t's offset in its line
-                if (chain_in) srow[j] = cin[e]; // the previous run's last 16 outputs
+                const int a = (int)(((uintptr_t)yr >> 2) & (kLineF - 1)); // o_t's offset in its line
+                if (chain_in) { // the previous run's last 32 outputs
+                    srow[j] = ocarry[ct][g4][e][j];
+                    srow[j + 16] = ocarry[ct][g4][e][j + 16];
+                }
 #pragma unroll
                 for (int c = 0; c < S; ++c)
-                    *reinterpret_cast<f4 *>(srow + 16 + 4 * S * j + 4 * c) =
+                    *reinterpret_cast<f4 *>(srow + kLineF + 4 * S * j + 4 * c) =
                         f4{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
-                if (chain_out) { // this run's last 16 outputs, straight from the lanes holding them
+                if (chain_out) { // this run's last 32 outputs, straight from the lanes holding them
 #pragma unroll
                     for (int c = 0; c < S; ++c) {
-                        const int i0 = 4 * S * j + 4 * c - (64 * S - 16);
+                        const int i0 = 4 * S * j + 4 * c - (64 * S - kLineF);
                         if (i0 >= 0)
                             *reinterpret_cast<f4 *>(&ocarry[ct][g4][e][i0]) =
                                 f4{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
                     }
                 }
                 float *ys = yr - a;               // line-aligned segment start
-                const float *ss = srow + 16 - a;  // segment in the staging row
+                const float *ss = srow + kLineF - a; // segment in the staging row
 #pragma unroll
                 for (int c = 0; c < S; ++c) {
                     const int s0 = 64 * c + 4 * j;
@@ -435,7 +482,10 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
                         }
                     }
                 }
-                if (!chain_out && j < a) ys[64 * S + j] = ss[64 * S + j]; // chain end: the carry
+                if (!chain_out) { // chain end: the carry
+                    if (j < a) ys[64 * S + j] = ss[64 * S + j];
+                    if (j + 16 < a) ys[64 * S + j + 16] = ss[64 * S + j + 16];
+                }
             } else {
 #pragma unroll
                 for (int u = 0; u < 4 * S; ++u) {
@@ -532,9 +582,10 @@ bool stream1d_supports(const convt_plan &P) {
     if (find_variant(P) < 0) return false;
     // 64-position tiles of one row must index within int range; the tile
     // fetch reads whole float4 inside a row
-    // (and one sample of y below 2 GiB: the common-path stores use 31-bit offsets)
+    // (one sample of y and one row set of x below 2 GiB: the common-path
+    // stores and the inner-tile loads use 31-bit offsets)
     return P.ax[2].L_out < (1 << 30) && P.ax[2].L_in < (1 << 30) && P.ax[2].L_in >= 4 &&
-           4 * P.C_out * P.ax[2].L_out < INT32_MAX;
+           4 * P.C_out * P.ax[2].L_out < INT32_MAX && 4 * P.Cig * P.ax[2].L_in < INT32_MAX;
 }
 
 int launch_stream1d(const convt_plan &Pl, const float *x, const float *w, const float *bias,
