@@ -191,7 +191,10 @@ __device__ __forceinline__ void tile_store_lds(float *lds, const f4 (&r)[(CIG * 
 // the 16 bytes at 64c + 4j of its row's segment, so one store instruction
 // covers four rows with 256 contiguous, line-aligned bytes each.
 constexpr int kLineF = 32; // floats per 128-byte line
-template <int S> constexpr int stage_pitch() { return kLineF + 64 * S + 4; } // +4: spread banks
+// A multiple of 64 dwords, so the four rows a store instruction reads start
+// on the same LDS bank (16-byte reads of such rows are conflict-free); it
+// holds the common path's layout (up to 31 + 32 + 64S floats).
+template <int S> constexpr int stage_pitch() { return (kLineF + 64 * S + kLineF + 63) / 64 * 64; }
 
 // Tuning knobs: minimum waves per SIMD the register allocation must allow,
 // and resident workgroups aimed for per CU when sizing the grid.
@@ -274,20 +277,17 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
     unsigned lane_off[4] = {0u, 0u, 0u, 0u};
     int a_row[4] = {0, 0, 0, 0};
     float *srow = &ostage[ct][g4][0];
-    // Common-path staging: this lane's outputs of phase r go to
-    // sph[r][S*t] (t = 0..3), written straight from the accumulators (dword
-    // LDS writes, no register packing: the empty asm hides the pointers'
-    // relation, so the compiler cannot merge the phases into 16-byte writes
-    // that need the values gathered first); the segment of row group e is
-    // read from seg[e][64c].
+    // Common-path staging of row group e: run output m (m = -32 .. 64S-1,
+    // negative = carried) at srow[32 + a + m].  The line-aligned segment then
+    // starts at srow[32] in every row, whatever a is, so chunk c of lane j is
+    // the aligned float4 at srow[32 + 4j + 64c].  cb[e] points at the lane's
+    // carry slot srow[a + j]; the lane's own outputs m = 4Sj + u are written
+    // at cb[e][32 + (4S - 1)j + u] straight from the accumulators (dword
+    // writes, no register packing).
     typedef __attribute__((address_space(3))) float *lds_fptr;
-    lds_fptr sph[S];
-#pragma unroll
-    for (int r = 0; r < S; ++r) {
-        sph[r] = (lds_fptr)(srow + kLineF + 4 * S * j + r);
-        asm volatile("" : "+v"(sph[r]));
-    }
-    const float *seg[4] = {srow, srow, srow, srow};
+    lds_fptr cb[4];
+    const int own = kLineF + (4 * S - 1) * j;
+    const f4 *segp = reinterpret_cast<const f4 *>(srow + kLineF + 4 * j);
 
     // Runs of consecutive items of one group share the weights: load them once
     // per run, outside the loop that carries the prefetch.
@@ -388,7 +388,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
                 // item offset, which stays >= 0 since a chained item has
                 // o_t >= 64S
                 lane_off[e] = 4u * ((unsigned)row * (unsigned)P.L_out + (unsigned)(4 * j + kLineF - a_row[e]));
-                seg[e] = srow + kLineF - a_row[e] + 4 * j;
+                cb[e] = (lds_fptr)(srow + a_row[e] + j);
             }
         }
         if (!FUSED && interior && chain_in && chain_out) {
@@ -397,27 +397,26 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
             const unsigned item4 = 4u * (unsigned)(o_t - kLineF);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
+                const lds_fptr c = cb[e];
                 // The previous run's last 32 outputs, then this run's outputs.
-                srow[j] = ocarry[ct][g4][e][j];
-                srow[j + 16] = ocarry[ct][g4][e][j + 16];
+                c[0] = ocarry[ct][g4][e][j];
+                c[16] = ocarry[ct][g4][e][j + 16];
+                const lds_fptr o = c + own;
 #pragma unroll
-                for (int r = 0; r < S; ++r)
+                for (int t = 0; t < 4; ++t)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
+                    for (int r = 0; r < S; ++r) {
                         float a = br[e];
                         if constexpr (Ph::count() > 0)
                             if (Ph::nonempty(r)) a = acc[Ph::slot(r)][t][e];
-                        sph[r][S * t] = a;
+                        o[S * t + r] = a;
                     }
-                // This run's last 32 outputs become the next run's carry (one
-                // wave's LDS accesses are performed in order).
-                ocarry[ct][g4][e][j] = srow[64 * S + j];
-                ocarry[ct][g4][e][j + 16] = srow[64 * S + j + 16];
-                const float *ss = seg[e]; // the line-aligned segment
+                // This run's last 32 outputs (m = 64S - 32 + i) become the next
+                // run's carry (one wave's LDS accesses are performed in order).
+                ocarry[ct][g4][e][j] = c[64 * S];
+                ocarry[ct][g4][e][j + 16] = c[64 * S + 16];
 #pragma unroll
-                for (int c = 0; c < S; ++c)
-                    buf_store4(f4{ss[64 * c], ss[64 * c + 1], ss[64 * c + 2], ss[64 * c + 3]}, ry,
-                               lane_off[e] + 256u * c, item4);
+                for (int q = 0; q < S; ++q) buf_store4(segp[16 * q], ry, lane_off[e] + 256u * q, item4);
             }
         } else {
         float *yrow = y + ((int64_t)n * P.C_out + (int64_t)g * COG + 16 * ct + 4 * g4) * P.L_out + o_t;
