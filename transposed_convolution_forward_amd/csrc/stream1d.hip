@@ -100,10 +100,21 @@ struct Stream1dParams {
     int64_t total; // N * G * n_st
 };
 
-// The x tile of one work item in LDS: CIG rows (input channels of the group)
-// of positions q0-4 .. q0+63, i.e. 17 float4 per row (pitch 68 floats).
+// The x tile of one work item: CIG rows (input channels of the group) of
+// positions q0-4 .. q0+63, 17 float4 per row.  In LDS the rows go in groups
+// of four (the channels one MFMA step reads): positions q0 .. q0+63 of row
+// 4g + i at group g, offset 64i, so the four rows of one 16-byte operand read
+// start on the same bank (conflict-free), and the four halo float4s
+// (q0-4 .. q0-1) after them at offset 256 + 4i.
 constexpr int kRowF4 = (kTileQ + 4) / 4;
-constexpr int kPitch = kRowF4 * 4;
+constexpr int kGrpF = 4 * kTileQ + 16; // floats per group of four rows
+
+// LDS float offset of float4 f (row f / 17, column f % 17) of the tile.
+__device__ __forceinline__ int tile_lds_off(int f) {
+    const int row = f / kRowF4, c4 = f % kRowF4;
+    const int grp = row >> 2, i = row & 3;
+    return grp * kGrpF + (c4 == 0 ? 4 * kTileQ + 4 * i : 64 * i + 4 * (c4 - 1));
+}
 
 // Fetch of one x tile into registers, branch-free so that the loads stay in
 // flight across the contraction of the current tile: every float4 is loaded
@@ -144,7 +155,8 @@ __device__ __forceinline__ void tile_fetch_inner(f4 (&r)[(CIG * kRowF4 + NT - 1)
 
 template <int CIG, int NT>
 __device__ __forceinline__ void tile_store_lds(float *lds, const f4 (&r)[(CIG * kRowF4 + NT - 1) / NT],
-                                               int L_in, int q0, int tid) {
+                                               const int (&lo)[(CIG * kRowF4 + NT - 1) / NT], int L_in,
+                                               int q0, int tid) {
     constexpr int NF = CIG * kRowF4;
     constexpr int PER = (NF + NT - 1) / NT;
     if (q0 - 4 >= 0 && q0 + kTileQ <= L_in) { // whole tile inside the row (uniform)
@@ -152,8 +164,7 @@ __device__ __forceinline__ void tile_store_lds(float *lds, const f4 (&r)[(CIG * 
         for (int u = 0; u < PER; ++u) {
             const int f = tid + u * NT;
             if (f < NF) {
-                const int row = f / kRowF4, c4 = f % kRowF4;
-                *reinterpret_cast<f4 *>(lds + row * kPitch + 4 * c4) = r[u];
+                *reinterpret_cast<f4 *>(lds + lo[u]) = r[u];
             }
         }
         return;
@@ -162,7 +173,7 @@ __device__ __forceinline__ void tile_store_lds(float *lds, const f4 (&r)[(CIG * 
     for (int u = 0; u < PER; ++u) {
         const int f = tid + u * NT;
         if (f < NF) {
-            const int row = f / kRowF4, c4 = f % kRowF4;
+            const int c4 = f % kRowF4;
             const int pos = q0 - 4 + 4 * c4;
             const int sh = pos - min(max(pos, 0), L_in - 4); // in [-3, 3]
             f4 v;
@@ -170,7 +181,7 @@ __device__ __forceinline__ void tile_store_lds(float *lds, const f4 (&r)[(CIG * 
             v.y = (pos + 1 >= 0 && pos + 1 < L_in) ? pick4(r[u], sh + 1) : 0.0f;
             v.z = (pos + 2 >= 0 && pos + 2 < L_in) ? pick4(r[u], sh + 2) : 0.0f;
             v.w = (pos + 3 >= 0 && pos + 3 < L_in) ? pick4(r[u], sh + 3) : 0.0f;
-            *reinterpret_cast<f4 *>(lds + row * kPitch + 4 * c4) = v;
+            *reinterpret_cast<f4 *>(lds + lo[u]) = v;
         }
     }
 }
@@ -197,12 +208,14 @@ constexpr int kLineF = 32; // floats per 128-byte line
 template <int S> constexpr int stage_pitch() { return (kLineF + 64 * S + kLineF + 63) / 64 * 64; }
 
 // Tuning knobs: minimum waves per SIMD the register allocation must allow,
-// and resident workgroups aimed for per CU when sizing the grid.
+// and how many rounds of resident workgroups the grid holds (one round: every
+// workgroup starts at once and walks a long run of items, so the per-workgroup
+// start-up is paid once per CU slot; measured 2.5% faster than two rounds).
 #ifndef CONVT_S1D_WAVES_PER_EU
 #define CONVT_S1D_WAVES_PER_EU 3
 #endif
-#ifndef CONVT_S1D_BLOCKS_PER_CU
-#define CONVT_S1D_BLOCKS_PER_CU 6
+#ifndef CONVT_S1D_ROUNDS
+#define CONVT_S1D_ROUNDS 1
 #endif
 
 // One workgroup = COG/16 waves; wave w owns output channels 16w .. 16w+15 of
@@ -225,7 +238,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
     static_assert(CIG % 4 == 0 && COG % 16 == 0, "tile shape");
     static_assert(Ph::cmax() <= 4, "input shift beyond the 4-position halo");
 
-    __shared__ __attribute__((aligned(16))) float lds[2][CIG * kPitch];
+    __shared__ __attribute__((aligned(16))) float lds[2][CIG / 4 * kGrpF];
     __shared__ __attribute__((aligned(16))) float ostage[COT][4][stage_pitch<S>()];
     __shared__ __attribute__((aligned(16))) float ocarry[COT][4][4][kLineF]; // [wave][g4][e][slot]
 
@@ -250,6 +263,9 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
         const int f = min(tid + u * NT, CIG * kRowF4 - 1);
         xo[u] = 4u * (unsigned)((f / kRowF4) * P.L_in + 4 * (f % kRowF4));
     }
+    int lo[PER]; // LDS offsets of this thread's float4 of the tile
+#pragma unroll
+    for (int u = 0; u < PER; ++u) lo[u] = tile_lds_off(min(tid + u * NT, CIG * kRowF4 - 1));
     const int x_bytes = 4 * CIG * P.L_in; // one row set's input rows (below 2 GiB)
     // Tiles inside the row take buffer loads at fixed offsets; the others clamp.
     auto fetch = [&](f4 (&r)[PER], int ng_, int q0_) {
@@ -261,7 +277,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
 
     f4 pre[PER];
     fetch(pre, ng, (P.st_lo + st) * kTileQ);
-    tile_store_lds<CIG, NT>(lds[0], pre, P.L_in, (P.st_lo + st) * kTileQ, tid);
+    tile_store_lds<CIG, NT>(lds[0], pre, lo, P.L_in, (P.st_lo + st) * kTileQ, tid);
     __syncthreads();
 
     float wr[K][NCIG]; // A operands: W[g*CIG + 4*cig + g4][16*ct + j][k]
@@ -328,12 +344,14 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[0][t] = bias4;
         } else {
-            const float *tp = lds[buf] + g4 * kPitch + 4 * j;
+            // lane j's float4 at q0+4j (row 4cig+g4) and the one before it
+            // (the halo float4 for lane 0)
+            const float *cp = lds[buf] + 64 * g4 + 4 * j;
+            const float *pp = lds[buf] + (j > 0 ? 64 * g4 + 4 * j - 4 : 4 * kTileQ + 4 * g4);
 #pragma unroll
             for (int cig = 0; cig < NCIG; ++cig) {
-                const float *rowp = tp + cig * 4 * kPitch;
-                const f4 pv = *reinterpret_cast<const f4 *>(rowp);     // q0+4j-4 .. -1
-                const f4 cv = *reinterpret_cast<const f4 *>(rowp + 4); // q0+4j .. +3
+                const f4 pv = *reinterpret_cast<const f4 *>(pp + cig * kGrpF); // q0+4j-4 .. -1
+                const f4 cv = *reinterpret_cast<const f4 *>(cp + cig * kGrpF); // q0+4j .. +3
                 const float cur[4] = {cv.x, cv.y, cv.z, cv.w};
                 const float prv[4] = {pv.x, pv.y, pv.z, pv.w};
 #pragma unroll
@@ -362,7 +380,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
         // store, before the next fetch.
 #pragma unroll
         for (int u = 0; u < PER; ++u) asm volatile("" : "+v"(pre[u])); // every prefetch landed here
-        tile_store_lds<CIG, NT>(lds[buf ^ 1], pre, P.L_in, (P.st_lo + st1) * kTileQ, tid);
+        tile_store_lds<CIG, NT>(lds[buf ^ 1], pre, lo, P.L_in, (P.st_lo + st1) * kTileQ, tid);
 
         // Epilogue (see stage_pitch).  Rows co = g*COG + 16ct + 4g4 + e; the
         // item's outputs of a row are o_t .. o_t + 64S - 1, o_t = q0*S - p.
@@ -559,8 +577,11 @@ int launch_variant(const convt_plan &Pl, const float *x, const float *w, const f
     P.st_lo = (int)st_lo;
     P.n_st = (int)(st_hi - st_lo);
     P.total = Pl.N * Pl.G * P.n_st;
-    // enough workgroups to fill every CU several times over
-    const int64_t blocks_target = (int64_t)num_cus() * CONVT_S1D_BLOCKS_PER_CU;
+    // one round of resident workgroups (see CONVT_S1D_ROUNDS)
+    // workgroups resident per CU: CONVT_S1D_WAVES_PER_EU waves on each of the
+    // 4 SIMDs, COG/16 waves per workgroup
+    const int64_t blocks_target =
+        (int64_t)num_cus() * CONVT_S1D_ROUNDS * (4 * CONVT_S1D_WAVES_PER_EU / (COG / 16));
     int64_t per_block = (P.total + blocks_target - 1) / blocks_target;
     if (per_block < 1) per_block = 1;
     P.per_block = (int)per_block;
