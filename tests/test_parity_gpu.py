@@ -141,6 +141,42 @@ def test_degenerate_shapes(wl):
         _full_check(wl, path)
 
 
+# Workgroups walking chains of several items (the 1D kernel's common path,
+# with each row's first outputs carried from the item before), and the output
+# placed 0..3 floats past an allocation's start so that other row alignments
+# occur: one non-empty phase with three paddings and an output padding, and
+# both phases non-empty.
+CHAINED_1D = [
+    S.Workload("s1d_chain_p1", 1, 2, 32, 64, 1, (65553,), (3,), (2,), (1,), (0,), (2,), True, False,
+               wid=3007),
+    S.Workload("s1d_chain_p2_op1", 1, 2, 32, 64, 1, (65553,), (3,), (2,), (2,), (1,), (2,), True,
+               False, wid=3008),
+    S.Workload("s1d_chain_p3", 1, 1, 32, 64, 1, (65553,), (3,), (2,), (3,), (0,), (2,), False, False,
+               wid=3009),
+    S.Workload("s1d_chain_d1", 1, 2, 32, 64, 1, (65553,), (3,), (2,), (1,), (1,), (1,), True, False,
+               wid=3010),
+]
+
+
+@pytest.mark.parametrize("shift", [0, 1, 3])
+@pytest.mark.parametrize("wl", CHAINED_1D, ids=lambda w: w.name)
+def test_chained_1d_offset_output(wl, shift):
+    import torch
+    inp = make(wl)
+    dev = to_dev(inp)
+    plan = T.plan_for(wl)
+    assert T.convt_plan_get_path(plan) == "stream1d"
+    numel = wl.N * wl.C_out * plan.out_size[0]
+    base = torch.full((numel + 4,), float("nan"), device="cuda")
+    y = base[shift:shift + numel].view((wl.N, wl.C_out) + plan.out_size)
+    y = run_gpu(wl, dev, "auto", y=y)
+    assert torch.isnan(base[:shift]).all().item() and torch.isnan(base[shift + numel:]).all().item(), \
+        "written outside the output"
+    ref = oracle.get().forward(**oracle_kwargs(wl, inp))
+    err = check_close(y.cpu().numpy(), ref, f"{wl.name} output at +{shift} floats")
+    log(f"  {wl.name} +{shift}: max abs err {err:.3e}")
+
+
 FULL = [S.TINY_1D, S.LONG_1D, S.GROUPED_3D, S.FUSED_3D, S.HEAVY_3D]
 
 
