@@ -170,7 +170,7 @@ __device__ __forceinline__ void buf_store2(float a, float b, rsrc_t r, unsigned 
 }
 
 template <int CIG, int COG, int KW, int SW, int DW, int TDM, int THM, int NWBM, int PWM, int PER,
-          bool FUSED, bool FULLW>
+          bool FUSED, bool FULLW, bool SWAP>
 __global__ __launch_bounds__(COG * 4)
 __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const Igemm3dParams P,
                                                      const float *__restrict__ x,
@@ -346,7 +346,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     __syncthreads();
 
     const f4 bias4 = f4{bo[0], bo[1], bo[2], bo[3]};
-    const bool swap2 = SW == 2 && P.sigma[0] != 0; // W phase 0 lands on the odd outputs
+    static_assert(!SWAP || SW == 2, "the phase swap is for two W phases");
     int buf = 0;
     // One output row; the loop below runs it twice per trip with the two
     // add_input register sets swapped, so the prefetched set needs no copy.
@@ -469,8 +469,10 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
                 }
             }
         };
-        if (swap2) epi(std::true_type{});
-        else epi(std::false_type{});
+        // W phase 0 on the odd outputs: fixed for the launch, so a template
+        // flag (as a runtime flag the compiler turns the two orders into
+        // per-element selects)
+        epi(std::integral_constant<bool, SWAP>{});
 
         __syncthreads();
         buf ^= 1;
@@ -904,18 +906,26 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
     if (need_f > PER * NT) return (int)hipErrorInvalidValue;
     // every lane of every W-block inside the row
     const bool fullw = Pl.ax[2].L_out == SW * 16 * NWBM;
-    if (add && fullw)
-        hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, true, true>),
+    auto launch = [&](auto fused, auto full, auto swap) {
+        hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, decltype(fused)::value,
+                                      decltype(full)::value, decltype(swap)::value>),
                            dim3(blocks), dim3(NT), 0, st, P, x, w, bias, add, y);
-    else if (add)
-        hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, true, false>),
-                           dim3(blocks), dim3(NT), 0, st, P, x, w, bias, add, y);
-    else if (fullw)
-        hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, false, true>),
-                           dim3(blocks), dim3(NT), 0, st, P, x, w, bias, add, y);
-    else
-        hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, false, false>),
-                           dim3(blocks), dim3(NT), 0, st, P, x, w, bias, add, y);
+    };
+    auto with_swap = [&](auto fused, auto full) {
+        if constexpr (SW == 2) {
+            if (P.sigma[0] != 0) { // W phase 0 lands on the odd outputs
+                launch(fused, full, std::true_type{});
+                return;
+            }
+        }
+        launch(fused, full, std::false_type{});
+    };
+    auto with_full = [&](auto fused) {
+        if (fullw) with_swap(fused, std::true_type{});
+        else with_swap(fused, std::false_type{});
+    };
+    if (add) with_full(std::true_type{});
+    else with_full(std::false_type{});
     return (int)hipGetLastError();
 }
 
