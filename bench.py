@@ -192,6 +192,23 @@ def main():
     launches = np.array([a.elapsed_time(b) for a, b in ev])
     ms_launch = float(launches.mean())
 
+    # Launches with the 256 MB last-level (Infinity) cache evicted first: a
+    # 512 MB buffer is read before each timed launch, outside its events
+    # (read, not written, so that no dirty lines are written back during the
+    # launch; the warm, back-to-back figure above stays the headline).
+    n_cold = min(args.steps, 20)
+    evict = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+    ev_cold = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_cold)]
+    for i in range(n_cold):
+        evict.sum()
+        ev_cold[i][0].record(stream)
+        step()
+        ev_cold[i][1].record(stream)
+    torch.cuda.synchronize()
+    del evict
+    cold = np.array([a.elapsed_time(b) for a, b in ev_cold])
+
     nbytes = algorithmic_bytes(wl)
     flops = 2 * valid_macs(wl)
     gbs = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -210,6 +227,12 @@ def main():
     roof["traffic"] = traffic_for(wl.name, kernel)
     roof["kernel"] = kernel
     roof["launch_ms"] = round(ms_launch, 5)
+    stats = lambda a: {"median": round(float(np.median(a)), 5), "min": round(float(a.min()), 5),
+                       "max": round(float(a.max()), 5)}
+    roof["launch_ms_stats"] = stats(launches)
+    cold_ms = float(np.median(cold))
+    roof["cold_cache"] = dict(stats(cold), launches=int(n_cold), frac=round(
+        (t_hbm if t_hbm >= t_fp32 else t_fp32) / (cold_ms * 1e-3), 4))
 
     cpu = None
     if not args.no_cpu_baseline:
