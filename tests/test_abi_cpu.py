@@ -133,6 +133,12 @@ def test_workload_plans_and_paths():
     # more classes than the table holds (4*3*3 = 36): the per-position gather
     big = T.Plan(3, 1, 2, 2, 1, (4, 4, 4), (4, 3, 3), (4, 3, 3), (0, 0, 0), (0, 0, 0), (1, 1, 1))
     assert "kernel=k_generic\n" in T.convt_plan_describe(big)
+    # 2D plans with the implicit-GEMM channel counts take those kernels
+    p2 = T.Plan(2, 2, 32, 64, 1, (16, 16), (3, 3), (2, 2), (1, 1), (1, 1), (1, 1))
+    assert T.convt_plan_get_path(p2) == "igemm3d"
+    assert "kernel=k_igemm3d\n" in T.convt_plan_describe(p2)
+    p2w = T.Plan(2, 2, 128, 64, 1, (9, 32), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1))
+    assert "kernel=k_igemm3d_wide" in T.convt_plan_describe(p2w)
 
 
 def test_phase_table_description():

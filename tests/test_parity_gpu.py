@@ -64,6 +64,14 @@ REDUCED = [
                (0, 0, 0), (1, 1, 1), True, True, wid=3202),
     S.Workload("igw_c128_w16_nobias", 3, 1, 128, 64, 1, (5, 2, 16), (4, 4, 4), (2, 2, 2), (1, 1, 1),
                (0, 1, 0), (1, 1, 1), False, False, wid=3203),
+    # ConvTranspose2d on the implicit-GEMM kernels (depth-1 3D problems):
+    # weights in registers, fused or not, and weights streamed
+    S.Workload("ig2d_k3s2_fused", 2, 2, 32, 64, 1, (16, 16), (3, 3), (2, 2), (1, 1), (1, 1), (1, 1),
+               True, True, wid=3301),
+    S.Workload("ig2d_k3s2_w24", 2, 3, 32, 64, 1, (7, 24), (3, 3), (2, 2), (1, 0), (0, 1), (1, 1),
+               True, False, wid=3302),
+    S.Workload("igw2d_c128_k4", 2, 2, 128, 64, 1, (9, 32), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1),
+               True, False, wid=3303),
 ]
 
 

@@ -767,7 +767,9 @@ bool w_layout(const convt_plan &P, const Variant &v, Layout &L) {
 }
 
 int find_variant(const convt_plan &P, Layout *Lout = nullptr) {
-    if (P.ndim != 3 || P.G != 1) return -1;
+    // 2D plans run as depth-1 3D problems (their leading axis has one position
+    // and one tap)
+    if (P.ndim < 2 || P.G != 1) return -1;
     const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
     if (AW.L_in % 4 != 0) return -1;
     // per-sample byte offsets of x, y and add_input stay below 2^31 (buffer addressing)
@@ -940,7 +942,7 @@ constexpr WideVariant kWide[] = {
 constexpr int kNumWide = (int)(sizeof(kWide) / sizeof(kWide[0]));
 
 int find_wide(const convt_plan &P, Layout *Lout) {
-    if (P.ndim != 3 || P.G != 1 || P.Cog != 64) return -1;
+    if (P.ndim < 2 || P.G != 1 || P.Cog != 64) return -1;
     // one buffer resource spans x (31-bit byte offsets); per-sample y as in the VGPR variant
     if (4 * P.N * P.C_in * P.in_sp >= INT32_MAX || 4 * P.C_out * P.out_sp >= INT32_MAX) return -1;
     const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
@@ -982,7 +984,7 @@ int launch_wide(const convt_plan &Pl, const Layout &L, const float *x, const flo
 } // namespace
 
 bool igemm3d_supports(const convt_plan &P) {
-    if (P.ndim != 3) return false;
+    if (P.ndim < 2) return false;
     Layout L;
     if (find_variant(P, &L) < 0 && find_wide(P, &L) < 0) return false;
     return P.N * P.ax[0].L_out * P.ax[1].L_out < (int64_t(1) << 31);
