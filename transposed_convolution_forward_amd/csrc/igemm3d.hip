@@ -259,6 +259,9 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     // the sample is 4*((qd*H_in + qh)*W_in) + xo4, valid when the slot's tap
     // exists in the class and its input row lies inside the input (one bit per
     // slot, the same for the whole workgroup).
+    // The float4s are numbered H tap slot first (jh, then jd, channel, float4),
+    // so that when they split evenly the second half of a thread's float4s are
+    // all of the second H tap (see the sliding rows below).
     int xo4[PER], lo[PER], tb[PER];
     {
         const int W4 = P.W_in >> 2;
@@ -266,10 +269,11 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
             const int f = tid + u * NT;
-            const int slot = f / (CIG * W4);
-            const int rem = f - slot * (CIG * W4);
+            const int sq = f / (CIG * W4); // jh * TDM + jd
+            const int rem = f - sq * (CIG * W4);
             const int ci = rem / W4, c4 = rem - ci * W4;
-            const int jd = slot / THM, jh = slot % THM;
+            const int jh = sq / TDM, jd = sq % TDM;
+            const int slot = jd * THM + jh;
             const int cd = jd == 0 ? cd0 : cd1, ch = jh == 0 ? ch0 : ch1;
             xo4[u] = 4 * (ci * dhw + 4 * c4 - (cd * P.H_in + ch) * P.W_in);
             lo[u] = f < nf ? (slot * CIG + ci) * PWM + 4 * c4 - P.iw_lo : -1;
@@ -277,14 +281,27 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
         }
     }
     const int xbytes = 4 * P.C_in * dhw;
-    auto fetch_rows = [&](f4 (&rv)[PER], const RowPos &Q) {
+    // Sliding rows: when the class has two H taps at offsets c and c+1 and
+    // the float4s split evenly by H tap, a row that follows the previous row
+    // of its chunk along H (same sample and D position, qh one higher) needs
+    // as its second H tap's input rows the first H tap's rows of that
+    // previous row, which are still in the other LDS buffer when the row is
+    // staged: they are copied from there, and their loads are issued out of
+    // range (no traffic; the number of loads per row stays fixed, which keeps
+    // the compiler's wait counts exact).
+    const bool slide_ok = THM == 2 && PER % 2 == 0 && th == 2 && ch1 == ch0 + 1 &&
+                          SLOTS * CIG * (P.W_in >> 2) == PER * NT;
+    const int nqh = P.cls_nqh[cls];
+    auto slide_of = [&](int k) { return slide_ok && k > r_begin && k % nqh != 0; };
+    auto fetch_rows = [&](f4 (&rv)[PER], const RowPos &Q, bool slide) {
         unsigned bad = 0xffffffffu; // bit slot clear: the slot's input row exists
 #pragma unroll
         for (int jd = 0; jd < TDM; ++jd)
 #pragma unroll
             for (int jh = 0; jh < THM; ++jh) {
                 const int id = Q.qd - (jd == 0 ? cd0 : cd1), ih = Q.qh - (jh == 0 ? ch0 : ch1);
-                if (jd < td && jh < th && id >= 0 && id < P.D_in && ih >= 0 && ih < P.H_in)
+                if (jd < td && jh < th && id >= 0 && id < P.D_in && ih >= 0 && ih < P.H_in &&
+                    !(slide && jh == 1))
                     bad &= ~(1u << (jd * THM + jh));
             }
         const rsrc_t rx = make_rsrc(x + (int64_t)Q.n * P.C_in * dhw, xbytes);
@@ -296,10 +313,14 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
             rv[u] = buf_load4(rx, off);
         }
     };
-    auto store_rows = [&](float *lbuf, const f4 (&rv)[PER]) {
+    auto store_rows = [&](float *lbuf, const f4 (&rv)[PER], bool slide, const float *lprev) {
 #pragma unroll
-        for (int u = 0; u < PER; ++u)
-            if (lo[u] >= 0) *reinterpret_cast<f4 *>(lbuf + lo[u]) = rv[u];
+        for (int u = 0; u < PER; ++u) {
+            f4 v = rv[u];
+            if (u >= PER / 2 && slide && lo[u] >= 0) // second H tap: the previous row's first (one slot back)
+                v = *reinterpret_cast<const f4 *>(lprev + lo[u] - CIG * PWM);
+            if (lo[u] >= 0) *reinterpret_cast<f4 *>(lbuf + lo[u]) = v;
+        }
     };
 
     // Outputs of lane (g4, j): channel 16ct + 4g4 + e (scalar offset e*dhw_out),
@@ -339,9 +360,9 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     float av[NWBM][4][SW], avn[NWBM][4][SW];
     RowPos R = decode_row(P, cls, r_begin);
     __syncthreads(); // LDS zeroed before the first row lands
-    fetch_rows(pre0, R);
-    store_rows(lds[0], pre0);
-    fetch_rows(pre0, decode_row(P, cls, min(r_begin + 1, r_end - 1)));
+    fetch_rows(pre0, R, false);
+    store_rows(lds[0], pre0, false, lds[1]);
+    fetch_rows(pre0, decode_row(P, cls, min(r_begin + 1, r_end - 1)), slide_of(min(r_begin + 1, r_end - 1)));
     if constexpr (FUSED) fetch_add(av, R);
     __syncthreads();
 
@@ -355,7 +376,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
         // x rows of row r+2 (into pre2), then add_input of row r+1; pre holds
         // the x rows of row r+1, fetched a row earlier
         const RowPos Rn = decode_row(P, cls, has_next ? r + 1 : r);
-        fetch_rows(pre2, decode_row(P, cls, min(r + 2, r_end - 1)));
+        fetch_rows(pre2, decode_row(P, cls, min(r + 2, r_end - 1)), slide_of(min(r + 2, r_end - 1)));
         if constexpr (FUSED) fetch_add(avn, Rn);
 
         // The bias enters as the accumulators' start value: the first MFMA of
@@ -419,7 +440,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
         // row's fetch.
 #pragma unroll
         for (int u = 0; u < PER; ++u) asm volatile("" : "+v"(pre[u]));
-        store_rows(lds[buf ^ 1], pre);
+        store_rows(lds[buf ^ 1], pre, slide_of(min(r + 1, r_end - 1)), lds[buf]);
 
         // epilogue: lane (g4, j) owns co = 16ct + 4g4 + e, ow = SW*(16t + j) + rr
         const rsrc_t ry = make_rsrc(y + (int64_t)R.n * P.C_out * dhw_out, ybytes);
