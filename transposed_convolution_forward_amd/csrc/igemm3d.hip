@@ -368,10 +368,12 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
 
     const f4 bias4 = f4{bo[0], bo[1], bo[2], bo[3]};
     static_assert(!SWAP || SW == 2, "the phase swap is for two W phases");
-    int buf = 0;
     // One output row; the loop below runs it twice per trip with the two
-    // add_input register sets swapped, so the prefetched set needs no copy.
-    auto row_step = [&](const int r, const auto &av, auto &avn, auto &pre, auto &pre2) {
+    // add_input register sets swapped, so the prefetched set needs no copy,
+    // and with the LDS buffer as a compile-time index (rows alternate between
+    // the two buffers), so buffer addresses are immediate offsets.
+    auto row_step = [&](const int r, const auto &av, auto &avn, auto &pre, auto &pre2, auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
         const bool has_next = r + 1 < r_end;
         // x rows of row r+2 (into pre2), then add_input of row r+1; pre holds
         // the x rows of row r+1, fetched a row earlier
@@ -496,12 +498,11 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
         epi(std::integral_constant<bool, SWAP>{});
 
         __syncthreads();
-        buf ^= 1;
         R = Rn;
     };
     for (int r = r_begin; r < r_end; r += 2) {
-        row_step(r, av, avn, pre0, pre1);
-        if (r + 1 < r_end) row_step(r + 1, avn, av, pre1, pre0);
+        row_step(r, av, avn, pre0, pre1, std::integral_constant<int, 0>{});
+        if (r + 1 < r_end) row_step(r + 1, avn, av, pre1, pre0, std::integral_constant<int, 1>{});
     }
 }
 
