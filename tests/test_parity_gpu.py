@@ -64,6 +64,25 @@ REDUCED = [
                (0, 0, 0), (1, 1, 1), True, True, wid=3202),
     S.Workload("igw_c128_w16_nobias", 3, 1, 128, 64, 1, (5, 2, 16), (4, 4, 4), (2, 2, 2), (1, 1, 1),
                (0, 1, 0), (1, 1, 1), False, False, wid=3203),
+    # generic path on the matrix cores with input rows shared along H: two H
+    # tap counts (one launch each) and a ragged last row block, a partial
+    # input-channel chunk, 4-channel blocks with a partial chunk, bias-only
+    # classes (H stride above K), two channel chunks, 2D, and an H dilation
+    # that sends the shape to the FMA phase kernel instead
+    S.Workload("rows_hs2_g2", 3, 2, 16, 16, 2, (3, 7, 9), (3, 3, 3), (2, 2, 2), (1, 1, 1),
+               (1, 0, 1), (1, 1, 1), True, False, wid=3401),
+    S.Workload("rows_cig4", 3, 1, 8, 16, 2, (4, 9, 10), (2, 5, 3), (2, 1, 2), (0, 2, 1),
+               (0, 0, 1), (1, 1, 1), True, True, wid=3402),
+    S.Workload("rows_cpt4_cig12", 3, 2, 24, 8, 2, (2, 11, 6), (3, 4, 2), (1, 1, 2), (1, 1, 0),
+               (0, 0, 1), (1, 1, 1), False, False, wid=3403),
+    S.Workload("rows_bias_only", 3, 1, 8, 8, 1, (3, 6, 5), (1, 2, 3), (1, 3, 2), (0, 0, 1),
+               (0, 2, 0), (1, 1, 1), True, True, wid=3404),
+    S.Workload("rows_cig16", 3, 1, 32, 16, 2, (2, 8, 12), (3, 5, 3), (1, 1, 2), (1, 2, 1),
+               (0, 0, 1), (1, 1, 1), True, False, wid=3405),
+    S.Workload("rows_2d", 2, 3, 16, 24, 2, (13, 17), (5, 4), (1, 2), (2, 1), (0, 1), (1, 1),
+               True, True, wid=3406),
+    S.Workload("rows_hdil2", 3, 1, 8, 8, 1, (3, 9, 8), (3, 3, 3), (2, 1, 2), (1, 2, 1),
+               (1, 0, 1), (1, 2, 1), True, False, wid=3407),
     # ConvTranspose2d on the implicit-GEMM kernels (depth-1 3D problems):
     # weights in registers, fused or not, and weights streamed
     S.Workload("ig2d_k3s2_fused", 2, 2, 32, 64, 1, (16, 16), (3, 3), (2, 2), (1, 1), (1, 1), (1, 1),
