@@ -130,7 +130,7 @@ def test_workload_plans_and_paths():
     # few stride-phase classes: the phase-class gather, on the matrix cores with
     # input rows shared along H where the shape has H extent; the tiny 1D layer
     # (two classes, no H) takes the FMA variant
-    assert "kernel=k_generic_rows" in T.convt_plan_describe(T.plan_for(S.GROUPED_3D))
+    assert "kernel=k_generic_pairs" in T.convt_plan_describe(T.plan_for(S.GROUPED_3D))
     assert "kernel=k_generic_phase" in T.convt_plan_describe(T.plan_for(S.TINY_1D))
     # more classes than the table holds (4*3*3 = 36): the per-position gather
     big = T.Plan(3, 1, 2, 2, 1, (4, 4, 4), (4, 3, 3), (4, 3, 3), (0, 0, 0), (0, 0, 0), (1, 1, 1))

@@ -64,11 +64,12 @@ REDUCED = [
                (0, 0, 0), (1, 1, 1), True, True, wid=3202),
     S.Workload("igw_c128_w16_nobias", 3, 1, 128, 64, 1, (5, 2, 16), (4, 4, 4), (2, 2, 2), (1, 1, 1),
                (0, 1, 0), (1, 1, 1), False, False, wid=3203),
-    # generic path on the matrix cores with input rows shared along H: two H
-    # tap counts (one launch each) and a ragged last row block, a partial
-    # input-channel chunk, 4-channel blocks with a partial chunk, bias-only
-    # classes (H stride above K), two channel chunks, 2D, and an H dilation
-    # that sends the shape to the FMA phase kernel instead
+    # generic path on the matrix cores with input rows shared along H (the
+    # 4x4x1 rows kernel or, for groups of 8k output and 4k input channels, the
+    # 16x16x4 row-pair kernel): two H tap counts (one launch each) and a ragged
+    # last row block, a partial input-channel chunk, 4-channel blocks with a
+    # partial chunk, bias-only classes (H stride above K), two channel chunks,
+    # 2D, and an H dilation that sends the shape to the FMA phase kernel
     S.Workload("rows_hs2_g2", 3, 2, 16, 16, 2, (3, 7, 9), (3, 3, 3), (2, 2, 2), (1, 1, 1),
                (1, 0, 1), (1, 1, 1), True, False, wid=3401),
     S.Workload("rows_cig4", 3, 1, 8, 16, 2, (4, 9, 10), (2, 5, 3), (2, 1, 2), (0, 2, 1),
@@ -83,6 +84,14 @@ REDUCED = [
                True, True, wid=3406),
     S.Workload("rows_hdil2", 3, 1, 8, 8, 1, (3, 9, 8), (3, 3, 3), (2, 1, 2), (1, 2, 1),
                (1, 0, 1), (1, 2, 1), True, False, wid=3407),
+    S.Workload("rows_cig6", 3, 2, 12, 16, 2, (3, 10, 7), (2, 3, 3), (2, 1, 2), (0, 1, 1),
+               (1, 0, 1), (1, 1, 1), True, True, wid=3408),
+    # 8-channel groups on 16x16x4 tiles of two output rows: two channel
+    # chunks, ragged position and row blocks, fused
+    S.Workload("pairs_co16_ragged", 3, 2, 8, 32, 2, (3, 13, 21), (3, 5, 3), (2, 1, 2), (1, 2, 1),
+               (1, 0, 0), (1, 1, 1), True, True, wid=3409),
+    S.Workload("pairs_2d_k4", 2, 2, 16, 8, 1, (15, 40), (4, 3), (1, 2), (1, 1), (0, 1), (1, 1),
+               False, False, wid=3410),
     # ConvTranspose2d on the implicit-GEMM kernels (depth-1 3D problems):
     # weights in registers, fused or not, and weights streamed
     S.Workload("ig2d_k3s2_fused", 2, 2, 32, 64, 1, (16, 16), (3, 3), (2, 2), (1, 1), (1, 1), (1, 1),

@@ -19,6 +19,7 @@ namespace convt {
 namespace {
 
 constexpr int kBlock = 256;
+static_assert(kBlock == 4 * 64, "weight staging deals rows to four waves");
 
 struct GenericParams {
     AxisPlan ax[kAxes];
@@ -122,6 +123,7 @@ struct PhaseParams {
     int cls_blk0[kMaxPhaseCls + 1];  // first workgroup (grid x) of each class
     int max_taps;                    // taps of the class with the most
     int tap_stride;                  // staged floats per tap (see tap_stride())
+    int lds_bytes;                   // dynamic LDS of a workgroup
 };
 constexpr int kMaxPhaseLds = 32768; // bytes of staged weights per workgroup
 
@@ -273,6 +275,42 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000; // raw (untyped) buffer access
 constexpr unsigned kOutOfRange = 0x80000000u;
 
+// Weight staging shared by the row kernels.  Row r of the staged operand is
+// 64 floats; src(r) names, for this lane, the weight w[g*Cig + ci][co0 + c]
+// [kidx] of the workgroup's group and channel chunk, or none (a zero).
+struct WSrc {
+    int ci, c, kidx;
+    bool ok;
+};
+
+// Rows r dealt to wave r % 4: each wave issues kStageBatch loads (out of
+// range, so zero, for none) before it writes any of them to LDS, so their
+// latencies overlap.
+constexpr int kStageBatch = 8;
+
+template <typename Src>
+__device__ __forceinline__ void stage_weight_rows(float *wl, rsrc_t rw, int64_t w_base, int Cog, int k_vol,
+                                                  int nrows, Src &&src) {
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    for (int r0 = wv; r0 < nrows; r0 += 4 * kStageBatch) {
+        float v[kStageBatch];
+#pragma unroll
+        for (int u = 0; u < kStageBatch; ++u) {
+            const int r = r0 + 4 * u;
+            unsigned o = kOutOfRange;
+            if (r < nrows) {
+                const WSrc q = src(r);
+                if (q.ok) o = 4u * (unsigned)(w_base + ((int64_t)q.ci * Cog + q.c) * k_vol + q.kidx);
+            }
+            v[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, o, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < kStageBatch; ++u)
+            if (r0 + 4 * u < nrows) wl[(r0 + 4 * u) * 64 + lane] = v[u];
+    }
+}
+
 // One window row (u = ih - (qh0 - TH + 1)), channels ci0 + CL: one MFMA per
 // (output row r whose tap j = r + TH-1-U exists, 4-channel block h).  The
 // block index is an instruction immediate, hence the compile-time recursion.
@@ -364,26 +402,28 @@ __global__ __launch_bounds__(kBlock) void k_generic_rows(const PhaseParams P,
         // stored).  Th == TH here.
         extern __shared__ __attribute__((aligned(16))) float wl[];
         const int TS = P.tap_stride;
+        const int lane = threadIdx.x & 63;
         {
-            const float *wg = w + ((int64_t)g * P.Cig * P.Cog + co0) * P.k_vol;
-            const int nw = Td * TH * Tw * TS;
-            for (int i = threadIdx.x; i < nw; i += kBlock) {
-                const int tap = i / TS, rem = i % TS;
-                const int j = rem % CPT, ci = rem / CPT;
-                float v = 0.0f;
-                if (ci < P.Cig) {
-                    const int tw = tap % Tw, tdh = tap / Tw;
-                    const int th = tdh % TH, td = tdh / TH;
-                    const int kidx = (AD.tap_k[AD.tap_start[rd] + td] * AH.K + AH.tap_k[AH.tap_start[rh] + th]) *
-                                         AW.K + AW.tap_k[AW.tap_start[rw] + tw];
-                    v = wg[((int64_t)ci * P.Cog + min(j, ncol - 1)) * P.k_vol + kidx];
-                }
-                wl[i] = v;
-            }
+            // one 64-float row per (tap (d, h, w), 64/CPT channels): lane l
+            // holds w[ci = part*64/CPT + l/CPT][co0 + l%CPT] (the group's last
+            // channel for columns past it; zero past Cig)
+            const rsrc_t rwt = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(w), (short)0,
+                                                                 (int)(4 * P.C_in * P.Cog * P.k_vol), kRsrcWord3);
+            const int64_t w_base = ((int64_t)g * P.Cig * P.Cog + co0) * P.k_vol;
+            const int c = min(lane % CPT, ncol - 1);
+            const int parts = TS / 64;
+            stage_weight_rows(wl, rwt, w_base, P.Cog, P.k_vol, Td * TH * Tw * parts, [&](int r) -> WSrc {
+                const int part = r % parts, tap = r / parts;
+                const int tw = tap % Tw, tdh = tap / Tw;
+                const int th = tdh % TH, td = tdh / TH;
+                const int kidx = (AD.tap_k[AD.tap_start[rd] + td] * AH.K + AH.tap_k[AH.tap_start[rh] + th]) *
+                                     AW.K + AW.tap_k[AW.tap_start[rw] + tw];
+                const int ci = part * (64 / CPT) + lane / CPT;
+                return WSrc{ci, c, kidx, ci < P.Cig};
+            });
         }
         __syncthreads();
 
-        const int lane = threadIdx.x & 63;
         const rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<float *>(x + ((int64_t)n * P.C_in + (int64_t)g * P.Cig) * P.in_sp), (short)0,
             (int)(4 * P.Cig * P.in_sp), kRsrcWord3);
@@ -428,15 +468,188 @@ __global__ __launch_bounds__(kBlock) void k_generic_rows(const PhaseParams P,
     }
 }
 
+// ------------------------------------------------ 8-channel groups, row pairs
+// For groups of 8 output channels a 16-row matrix tile holds two output rows
+// along H: row i = dh*8 + co of v_mfma_f32_16x16x4f32 is channel co of output
+// row qh0 + dh, its columns are 16 consecutive positions along W of the class,
+// and its K is 4 input channels.  With the H taps of every residue at offsets
+// 0..TH-1, output row q takes tap j from input row q - j, so input row ih
+// feeds row qh0 + dh through tap j = delta + dh with delta = qh0 - ih: one
+// B operand (4 channels x 16 positions of input row ih) serves every row pair
+// whose window contains ih, each with the A operand of its delta (TH + 1 of
+// them per (D tap, W tap, channel quad); the entries with delta + dh outside
+// [0, TH) are zero: 2 of the 2(TH + 1) half-tiles).  Lane layouts:
+// A[i][k] at lane i + 16k, B[k][j] at lane j + 16k, D[i][j] at lane
+// j + 16(i/4), accumulator register i%4.
+//
+// A wave owns NP row pairs x PB blocks of 16 positions of one (class, qd).
+typedef float v4f_p __attribute__((ext_vector_type(4)));
+
+template <int NP, int PB, int TH, bool FUSED>
+__global__ __launch_bounds__(kBlock) void k_generic_pairs(const PhaseParams P,
+                                                          const float *__restrict__ x,
+                                                          const float *__restrict__ w,
+                                                          const float *__restrict__ bias,
+                                                          const float *add, float *y) {
+    constexpr int ND = TH + 1;          // delta = qh0 - ih in [-1, TH - 1]
+    constexpr int NR = 2 * NP + TH - 1; // input rows of a wave's window
+    int c = 0;
+    while (c + 1 < P.n_cls && (int)blockIdx.x >= P.cls_blk0[c + 1]) ++c;
+    const int nqd = P.cls_nq[c][0], nqh = P.cls_nq[c][1], nqw = P.cls_nq[c][2];
+    const int nrb = (nqh + 2 * NP - 1) / (2 * NP);
+    const int nwb = (nqw + 16 * PB - 1) / (16 * PB);
+    const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
+    const int rd = P.cls_r[c][0], rh = P.cls_r[c][1], rw = P.cls_r[c][2];
+    const int wave = ((int)blockIdx.x - P.cls_blk0[c]) * (kBlock / 64) + (int)(threadIdx.x >> 6);
+    const bool wlive = wave < nqd * nrb * nwb;
+    const int iwb = wave % nwb;
+    const int t2 = wave / nwb;
+    const int irb = t2 % nrb;
+    const int iqd = t2 / nrb;
+    const int lane = threadIdx.x & 63;
+    const int j16 = lane & 15, k4 = lane >> 4;
+    const int qd = P.cls_q0[c][0] + iqd;
+    const int qh0 = P.cls_q0[c][1] + irb * 2 * NP;
+    int iqw[PB];
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) iqw[pb] = iwb * 16 * PB + pb * 16 + j16;
+
+    const int g = blockIdx.y / P.co_chunks;
+    const int co0 = (blockIdx.y % P.co_chunks) * 8;
+    const int n = P.n0 + blockIdx.z;
+
+    v4f_p acc[NP][PB];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) acc[p][pb] = v4f_p{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int Td = AD.tap_start[rd + 1] - AD.tap_start[rd];
+    const int Th = AH.tap_start[rh + 1] - AH.tap_start[rh];
+    const int Tw = AW.tap_start[rw + 1] - AW.tap_start[rw];
+    if (Td * Th * Tw > 0) {
+        // Staged weights as in k_generic_rows with CPT = 8: [class tap (d, h,
+        // w)][input channel][8 columns], tap_stride floats per tap.  Th == TH.
+        extern __shared__ __attribute__((aligned(16))) float wl[];
+        const int NQ = P.Cig / 4;
+        const int TS = P.tap_stride;
+        {
+            const rsrc_t rwt = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(w), (short)0,
+                                                                 (int)(4 * P.C_in * P.Cog * P.k_vol), kRsrcWord3);
+            const int64_t w_base = ((int64_t)g * P.Cig * P.Cog + co0) * P.k_vol;
+            const int parts = TS / 64;
+            stage_weight_rows(wl, rwt, w_base, P.Cog, P.k_vol, Td * TH * Tw * parts, [&](int r) -> WSrc {
+                const int part = r % parts, tap = r / parts;
+                const int tw = tap % Tw, tdh = tap / Tw;
+                const int th = tdh % TH, td = tdh / TH;
+                const int kidx = (AD.tap_k[AD.tap_start[rd] + td] * AH.K + AH.tap_k[AH.tap_start[rh] + th]) *
+                                     AW.K + AW.tap_k[AW.tap_start[rw] + tw];
+                const int ci = part * 8 + lane / 8;
+                return WSrc{ci, lane % 8, kidx, ci < P.Cig};
+            });
+        }
+        __syncthreads();
+
+        const rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float *>(x + ((int64_t)n * P.C_in + (int64_t)g * P.Cig) * P.in_sp), (short)0,
+            (int)(4 * P.Cig * P.in_sp), kRsrcWord3);
+        const unsigned ch_bytes = 4u * (unsigned)P.in_sp;
+        const unsigned lane_ch = (unsigned)k4 * (unsigned)P.in_sp; // this lane's channel in the quad
+        const int ih0 = qh0 - (TH - 1);
+        const int a_dh = (lane >> 3) & 1;
+        const int a_lane = 8 * k4 + (lane & 7);
+        for (int td = 0; td < Td; ++td) {
+            const int id = qd - AD.tap_c[AD.tap_start[rd] + td];
+            const bool okd = wlive && id >= 0 && id < AD.L_in;
+            for (int tw = 0; tw < Tw; ++tw) {
+                const int cw = AW.tap_c[AW.tap_start[rw] + tw];
+                unsigned base[PB];
+                bool ok[PB];
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb) {
+                    const int iw = P.cls_q0[c][2] + iqw[pb] - cw;
+                    ok[pb] = okd && iqw[pb] < nqw && iw >= 0 && iw < AW.L_in;
+                    base[pb] = lane_ch + (unsigned)(id * AH.L_in * AW.L_in + iw);
+                }
+                for (int q = 0; q < NQ; ++q) {
+                    // A of delta = di - 1: lane i + 16k takes channel 4q + k,
+                    // column i%8, H tap di - 1 + i/8 (zero outside [0, TH))
+                    float a[ND];
+                    const float *wq = wl + (td * TH * Tw + tw) * TS + 32 * q + a_lane;
+#pragma unroll
+                    for (int di = 0; di < ND; ++di) {
+                        const int th = di - 1 + a_dh;
+                        const float v = wq[min(max(th, 0), TH - 1) * Tw * TS];
+                        a[di] = th >= 0 && th < TH ? v : 0.0f;
+                    }
+                    const unsigned soff = (unsigned)(4 * q) * ch_bytes;
+#pragma unroll
+                    for (int u = 0; u < NR; ++u) {
+                        const int ih = ih0 + u;
+                        const bool okh = ih >= 0 && ih < AH.L_in;
+                        float b[PB];
+#pragma unroll
+                        for (int pb = 0; pb < PB; ++pb) {
+                            const unsigned vo = ok[pb] && okh ? 4u * (base[pb] + (unsigned)(ih * AW.L_in)) : kOutOfRange;
+                            b[pb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, vo, soff, 0));
+                        }
+#pragma unroll
+                        for (int p = 0; p < NP; ++p) {
+                            // delta = qh0 + 2p - ih = 2p + TH - 1 - u
+                            const int di = 2 * p + TH - u; // delta + 1
+                            if (di < 0 || di >= ND) continue;
+#pragma unroll
+                            for (int pb = 0; pb < PB; ++pb)
+                                acc[p][pb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[di], b[pb], acc[p][pb], 0, 0, 0);
+                        }
+                    }
+                }
+            }
+        }
+    }
+
+    if (!wlive) return;
+    // lane j16 + 16*k4, register v: position j16, output row dh = k4/2,
+    // channel 4*(k4%2) + v
+    const int dh = k4 >> 1;
+    const int cb = co0 + 4 * (k4 & 1);
+    const int od = qd * AD.s + rd - AD.p;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int iqh = irb * 2 * NP + 2 * p + dh;
+        if (iqh >= nqh) continue;
+        const int oh = (P.cls_q0[c][1] + iqh) * AH.s + rh - AH.p;
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) {
+            if (iqw[pb] >= nqw) continue;
+            const int ow = (P.cls_q0[c][2] + iqw[pb]) * AW.s + rw - AW.p;
+            const int sp = (od * AH.L_out + oh) * AW.L_out + ow;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int co = g * P.Cog + cb + v;
+                const int64_t idx = ((int64_t)n * P.C_out + co) * P.out_sp + sp;
+                const float bb = bias ? bias[co] : 0.0f;
+                const float aa = FUSED ? add[idx] : 0.0f;
+                y[idx] = epilogue<FUSED>(acc[p][pb][v], bb, aa);
+            }
+        }
+    }
+}
+
+constexpr int kPairs = 4;      // row pairs per wave in k_generic_pairs
+constexpr int kPairBlocks = 1; // 16-position blocks per wave
+constexpr int kMaxPairsLds = 65536;
+
 constexpr int kRows = 4;     // H rows per thread in k_generic_rows
 constexpr int kRowsMaxTH = 5; // largest H tap count instantiated
 
 // Largest H tap count of the shape if k_generic_rows applies, else 0: 4-channel
-// blocks, a group's input below 2 GiB, at least kRows outputs along H, and on H
-// every residue's taps at offsets 0, 1, .., T-1.
+// blocks, a group's input and the weights below 2 GiB, at least kRows outputs
+// along H, and on H every residue's taps at offsets 0, 1, .., T-1.
 int rows_th(const convt_plan &Pl) {
     if (pick_cpt(Pl.Cog) < 4) return 0;
-    if (4 * Pl.Cig * Pl.in_sp > 0x7fffffff) return 0; // byte offsets in the buffer resource
+    if (4 * Pl.Cig * Pl.in_sp > 0x7fffffff) return 0;           // byte offsets in the buffer
+    if (4 * Pl.C_in * Pl.Cog * Pl.k_vol > 0x7fffffff) return 0; // resources over x and w
     const AxisPlan &A = Pl.ax[1];
     if (A.L_out < kRows) return 0; // nothing to share along H (1D shapes)
     int th = 1;
@@ -457,17 +670,23 @@ int tap_stride(int64_t Cig, int cpt, bool rows) {
 }
 
 // Fills the class table; false when the shape has more classes than it holds.
-// rows > 0 lays the class out for k_generic_rows (rows q along H per thread),
-// else for k_generic_phase (kPhasePos positions per thread).
-// th_only > 0 keeps only the classes whose launch key (below) is th_only.
+// Launch key of a class for the row kernels: its H tap count, with bias-only
+// classes (no tap on some axis) in the 1-tap launch, which skips their
+// contraction.
 int rows_key(const AxisPlan *A, const int r[kAxes]) {
     int taps = 1;
     for (int a = 0; a < kAxes; ++a) taps *= A[a].tap_start[r[a] + 1] - A[a].tap_start[r[a]];
-    // bias-only classes go with the 1-tap launch, which skips their contraction
     return taps == 0 ? 1 : A[1].tap_start[r[1] + 1] - A[1].tap_start[r[1]];
 }
 
-bool phase_classes(const convt_plan &Pl, PhaseParams &P, int rows, int th_only = 0) {
+// How a launch lays out the positions of a class.
+enum class Layout { kFma, kRows, kPairs };
+
+// The class table of a launch: every class with output positions (th_only > 0
+// keeps those whose rows_key is th_only), the first workgroup of each, and the
+// LDS the staged weights take.  False when the shape has more classes than the
+// table holds or the weights do not fit.
+bool phase_classes(const convt_plan &Pl, PhaseParams &P, Layout lay, int th_only = 0) {
     P.n_cls = 0;
     P.max_taps = 1;
     int blocks = 0;
@@ -499,14 +718,29 @@ bool phase_classes(const convt_plan &Pl, PhaseParams &P, int rows, int th_only =
                 int taps = 1;
                 for (int a = 0; a < kAxes; ++a) taps *= A[a].tap_start[r[a] + 1] - A[a].tap_start[r[a]];
                 P.max_taps = taps > P.max_taps ? taps : P.max_taps;
-                const int64_t per_thread = rows > 0 ? 1 : kPhasePos;
-                const int64_t pos = (int64_t)nq[0] * (rows > 0 ? (nq[1] + rows - 1) / rows : nq[1]) * nq[2];
-                blocks += (int)((pos + kBlock * per_thread - 1) / (kBlock * per_thread));
+                int64_t units, per_block; // threads (or waves) and units per workgroup
+                if (lay == Layout::kPairs) {
+                    units = (int64_t)nq[0] * ((nq[1] + 2 * kPairs - 1) / (2 * kPairs)) *
+                            ((nq[2] + 16 * kPairBlocks - 1) / (16 * kPairBlocks));
+                    per_block = kBlock / 64;
+                } else if (lay == Layout::kRows) {
+                    units = (int64_t)nq[0] * ((nq[1] + kRows - 1) / kRows) * nq[2];
+                    per_block = kBlock;
+                } else {
+                    units = (int64_t)nq[0] * nq[1] * nq[2];
+                    per_block = kBlock * kPhasePos;
+                }
+                blocks += (int)((units + per_block - 1) / per_block);
             }
     P.cls_blk0[P.n_cls] = blocks;
     // the staged weights of the class with the most taps must fit in LDS
-    P.tap_stride = tap_stride(Pl.Cig, pick_cpt(Pl.Cog), rows > 0);
-    return (int64_t)P.max_taps * P.tap_stride * 4 <= kMaxPhaseLds;
+    P.tap_stride = tap_stride(Pl.Cig, lay == Layout::kPairs ? 8 : pick_cpt(Pl.Cog), lay != Layout::kFma);
+    int64_t bytes;
+    bytes = (int64_t)P.max_taps * P.tap_stride * 4;
+    const int64_t limit = lay == Layout::kPairs ? kMaxPairsLds : kMaxPhaseLds;
+    if (bytes > limit) return false;
+    P.lds_bytes = (int)bytes;
+    return true;
 }
 
 template <typename Launch>
@@ -518,8 +752,7 @@ int launch_classes(const convt_plan &Pl, PhaseParams &P, int cpt, Launch &&launc
     for (int64_t n0 = 0; n0 < Pl.N; n0 += 65535) {
         P.n0 = (int)n0;
         const unsigned gz = (unsigned)(Pl.N - n0 < 65535 ? Pl.N - n0 : 65535);
-        const size_t lds = (size_t)P.max_taps * P.tap_stride * sizeof(float);
-        launch(dim3(gx, gy, gz), lds);
+        launch(dim3(gx, gy, gz), (size_t)P.lds_bytes);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }
@@ -571,7 +804,7 @@ int launch_rows_all(int th_max, const convt_plan &Pl, PhaseParams &Q, const floa
     static_assert(kRowsMaxTH == 5, "one case per instantiated H tap count");
     for (int th = 1; th <= th_max; ++th) {
         PhaseParams P = Q;
-        if (!phase_classes(Pl, P, kRows, th)) return (int)hipErrorInvalidValue; // checked in rows_plan
+        if (!phase_classes(Pl, P, Layout::kRows, th)) return (int)hipErrorInvalidValue; // checked in rows_plan
         if (P.n_cls == 0) continue;
         int e = 0;
         switch (th) {
@@ -592,9 +825,56 @@ int rows_plan(const convt_plan &Pl) {
     if (th == 0) return 0;
     for (int t = 1; t <= th; ++t) {
         PhaseParams P;
-        if (!phase_classes(Pl, P, kRows, t)) return 0;
+        if (!phase_classes(Pl, P, Layout::kRows, t)) return 0;
     }
     return th;
+}
+
+// k_generic_pairs applies: groups of a multiple of 8 output channels and of 4
+// input channels, the conditions of the rows kernel, and per H tap count a
+// class table whose A operands fit in LDS.  Returns the largest H tap count.
+int pairs_plan(const convt_plan &Pl) {
+    if (Pl.Cog % 8 != 0 || Pl.Cig % 4 != 0) return 0;
+    const int th = rows_th(Pl);
+    if (th == 0) return 0;
+    for (int t = 1; t <= th; ++t) {
+        PhaseParams P;
+        if (!phase_classes(Pl, P, Layout::kPairs, t)) return 0;
+    }
+    return th;
+}
+
+template <int TH>
+int launch_pairs(const convt_plan &Pl, PhaseParams &P, const float *x, const float *w,
+                 const float *bias, const float *add, float *y, hipStream_t st) {
+    return launch_classes(Pl, P, 8, [&](dim3 grid, size_t lds) {
+        if (add)
+            hipLaunchKernelGGL((k_generic_pairs<kPairs, kPairBlocks, TH, true>), grid, dim3(kBlock), lds, st, P,
+                               x, w, bias, add, y);
+        else
+            hipLaunchKernelGGL((k_generic_pairs<kPairs, kPairBlocks, TH, false>), grid, dim3(kBlock), lds, st, P,
+                               x, w, bias, add, y);
+    });
+}
+
+int launch_pairs_all(int th_max, const convt_plan &Pl, PhaseParams &Q, const float *x, const float *w,
+                     const float *bias, const float *add, float *y, hipStream_t st) {
+    static_assert(kRowsMaxTH == 5, "one case per instantiated H tap count");
+    for (int th = 1; th <= th_max; ++th) {
+        PhaseParams P = Q;
+        if (!phase_classes(Pl, P, Layout::kPairs, th)) return (int)hipErrorInvalidValue; // checked in pairs_plan
+        if (P.n_cls == 0) continue;
+        int e = 0;
+        switch (th) {
+        case 1: e = launch_pairs<1>(Pl, P, x, w, bias, add, y, st); break;
+        case 2: e = launch_pairs<2>(Pl, P, x, w, bias, add, y, st); break;
+        case 3: e = launch_pairs<3>(Pl, P, x, w, bias, add, y, st); break;
+        case 4: e = launch_pairs<4>(Pl, P, x, w, bias, add, y, st); break;
+        default: e = launch_pairs<5>(Pl, P, x, w, bias, add, y, st); break;
+        }
+        if (e) return e;
+    }
+    return 0;
 }
 
 template <int CPT>
@@ -624,8 +904,9 @@ int launch_cpt(const convt_plan &Pl, const GenericParams &base, const float *x, 
 
 const char *generic_kernel_name(const convt_plan &Pl) {
     PhaseParams P;
+    if (pairs_plan(Pl) > 0) return "k_generic_pairs";
     if (rows_plan(Pl) > 0) return "k_generic_rows";
-    if (phase_classes(Pl, P, 0)) return "k_generic_phase";
+    if (phase_classes(Pl, P, Layout::kFma)) return "k_generic_phase";
     return "k_generic";
 }
 
@@ -638,9 +919,10 @@ int launch_generic(const convt_plan &Pl, const float *x, const float *w, const f
                    const float *add, float *y, void *stream) {
     {
         PhaseParams Q;
-        const int th = rows_plan(Pl);
+        const int thp = pairs_plan(Pl);
+        const int th = thp > 0 ? 0 : rows_plan(Pl);
         const bool rows = th > 0;
-        if (rows || phase_classes(Pl, Q, 0)) {
+        if (thp > 0 || rows || phase_classes(Pl, Q, Layout::kFma)) {
             for (int a = 0; a < kAxes; ++a) Q.ax[a] = Pl.ax[a];
             Q.C_in = (int)Pl.C_in;
             Q.C_out = (int)Pl.C_out;
@@ -650,6 +932,7 @@ int launch_generic(const convt_plan &Pl, const float *x, const float *w, const f
             Q.in_sp = (int)Pl.in_sp;
             Q.out_sp = (int)Pl.out_sp;
             hipStream_t st = (hipStream_t)stream;
+            if (thp > 0) return launch_pairs_all(thp, Pl, Q, x, w, bias, add, y, st);
             if (rows) {
                 if (pick_cpt(Pl.Cog) == 8) return launch_rows_all<8>(th, Pl, Q, x, w, bias, add, y, st);
                 return launch_rows_all<4>(th, Pl, Q, x, w, bias, add, y, st);
