@@ -278,18 +278,22 @@ constexpr unsigned kOutOfRange = 0x80000000u;
 // Weight staging shared by the row kernels.  Row r of the staged operand is
 // 64 floats; src(r) names, for this lane, the weight w[g*Cig + ci][co0 + c]
 // [kidx] of the workgroup's group and channel chunk, or none (a zero).
-struct WSrc {
-    int ci, c, kidx;
-    bool ok;
-};
-
 // Rows r dealt to wave r % 4: each wave issues kStageBatch loads (out of
 // range, so zero, for none) before it writes any of them to LDS, so their
-// latencies overlap.
+// latencies overlap.  Row r holds, in lane l, the weight at element offset
+// lane_off + src(r) of w, where src(r) is uniform (the tap's offset plus the
+// row's first input channel times ci_stride) and lane_off is the lane's
+// channel and column; rows past a lane's last channel (lane_ci + part_ci(r) >=
+// Cig) are zero.
 constexpr int kStageBatch = 8;
 
+struct WRow {
+    unsigned off; // uniform element offset of the row (tap and channel part)
+    int ci0;      // first input channel of the row
+};
+
 template <typename Src>
-__device__ __forceinline__ void stage_weight_rows(float *wl, rsrc_t rw, int64_t w_base, int Cog, int k_vol,
+__device__ __forceinline__ void stage_weight_rows(float *wl, rsrc_t rw, unsigned lane_off, int lane_ci, int Cig,
                                                   int nrows, Src &&src) {
     const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
@@ -300,8 +304,8 @@ __device__ __forceinline__ void stage_weight_rows(float *wl, rsrc_t rw, int64_t 
             const int r = r0 + 4 * u;
             unsigned o = kOutOfRange;
             if (r < nrows) {
-                const WSrc q = src(r);
-                if (q.ok) o = 4u * (unsigned)(w_base + ((int64_t)q.ci * Cog + q.c) * k_vol + q.kidx);
+                const WRow q = src(r);
+                if (q.ci0 + lane_ci < Cig) o = 4u * (lane_off + q.off);
             }
             v[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, o, 0, 0));
         }
@@ -409,17 +413,20 @@ __global__ __launch_bounds__(kBlock) void k_generic_rows(const PhaseParams P,
             // channel for columns past it; zero past Cig)
             const rsrc_t rwt = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(w), (short)0,
                                                                  (int)(4 * P.C_in * P.Cog * P.k_vol), kRsrcWord3);
-            const int64_t w_base = ((int64_t)g * P.Cig * P.Cog + co0) * P.k_vol;
             const int c = min(lane % CPT, ncol - 1);
+            const int lane_ci = lane / CPT;
+            const unsigned lane_off =
+                (unsigned)(((int64_t)g * P.Cig * P.Cog + co0 + (int64_t)lane_ci * P.Cog + c) * P.k_vol);
             const int parts = TS / 64;
-            stage_weight_rows(wl, rwt, w_base, P.Cog, P.k_vol, Td * TH * Tw * parts, [&](int r) -> WSrc {
+            const unsigned ci_stride = (unsigned)(P.Cog * P.k_vol);
+            stage_weight_rows(wl, rwt, lane_off, lane_ci, P.Cig, Td * TH * Tw * parts, [&](int r) -> WRow {
                 const int part = r % parts, tap = r / parts;
                 const int tw = tap % Tw, tdh = tap / Tw;
                 const int th = tdh % TH, td = tdh / TH;
                 const int kidx = (AD.tap_k[AD.tap_start[rd] + td] * AH.K + AH.tap_k[AH.tap_start[rh] + th]) *
                                      AW.K + AW.tap_k[AW.tap_start[rw] + tw];
-                const int ci = part * (64 / CPT) + lane / CPT;
-                return WSrc{ci, c, kidx, ci < P.Cig};
+                const int ci0 = part * (64 / CPT);
+                return WRow{(unsigned)ci0 * ci_stride + (unsigned)kidx, ci0};
             });
         }
         __syncthreads();
@@ -536,16 +543,18 @@ __global__ __launch_bounds__(kBlock) void k_generic_pairs(const PhaseParams P,
         {
             const rsrc_t rwt = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(w), (short)0,
                                                                  (int)(4 * P.C_in * P.Cog * P.k_vol), kRsrcWord3);
-            const int64_t w_base = ((int64_t)g * P.Cig * P.Cog + co0) * P.k_vol;
+            const int lane_ci = lane / 8;
+            const unsigned lane_off =
+                (unsigned)(((int64_t)g * P.Cig * P.Cog + co0 + (int64_t)lane_ci * P.Cog + lane % 8) * P.k_vol);
             const int parts = TS / 64;
-            stage_weight_rows(wl, rwt, w_base, P.Cog, P.k_vol, Td * TH * Tw * parts, [&](int r) -> WSrc {
+            const unsigned ci_stride = (unsigned)(P.Cog * P.k_vol);
+            stage_weight_rows(wl, rwt, lane_off, lane_ci, P.Cig, Td * TH * Tw * parts, [&](int r) -> WRow {
                 const int part = r % parts, tap = r / parts;
                 const int tw = tap % Tw, tdh = tap / Tw;
                 const int th = tdh % TH, td = tdh / TH;
                 const int kidx = (AD.tap_k[AD.tap_start[rd] + td] * AH.K + AH.tap_k[AH.tap_start[rh] + th]) *
                                      AW.K + AW.tap_k[AW.tap_start[rw] + tw];
-                const int ci = part * 8 + lane / 8;
-                return WSrc{ci, lane % 8, kidx, ci < P.Cig};
+                return WRow{(unsigned)(part * 8) * ci_stride + (unsigned)kidx, part * 8};
             });
         }
         __syncthreads();
@@ -571,6 +580,16 @@ __global__ __launch_bounds__(kBlock) void k_generic_pairs(const PhaseParams P,
                     ok[pb] = okd && iqw[pb] < nqw && iw >= 0 && iw < AW.L_in;
                     base[pb] = lane_ch + (unsigned)(id * AH.L_in * AW.L_in + iw);
                 }
+                // the window's row offsets, shared by every channel quad
+                unsigned vo[NR][PB];
+#pragma unroll
+                for (int u = 0; u < NR; ++u) {
+                    const int ih = ih0 + u;
+                    const bool okh = ih >= 0 && ih < AH.L_in;
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb)
+                        vo[u][pb] = ok[pb] && okh ? 4u * (base[pb] + (unsigned)(ih * AW.L_in)) : kOutOfRange;
+                }
                 for (int q = 0; q < NQ; ++q) {
                     // A of delta = di - 1: lane i + 16k takes channel 4q + k,
                     // column i%8, H tap di - 1 + i/8 (zero outside [0, TH))
@@ -585,14 +604,10 @@ __global__ __launch_bounds__(kBlock) void k_generic_pairs(const PhaseParams P,
                     const unsigned soff = (unsigned)(4 * q) * ch_bytes;
 #pragma unroll
                     for (int u = 0; u < NR; ++u) {
-                        const int ih = ih0 + u;
-                        const bool okh = ih >= 0 && ih < AH.L_in;
                         float b[PB];
 #pragma unroll
-                        for (int pb = 0; pb < PB; ++pb) {
-                            const unsigned vo = ok[pb] && okh ? 4u * (base[pb] + (unsigned)(ih * AW.L_in)) : kOutOfRange;
-                            b[pb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, vo, soff, 0));
-                        }
+                        for (int pb = 0; pb < PB; ++pb)
+                            b[pb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, vo[u][pb], soff, 0));
 #pragma unroll
                         for (int p = 0; p < NP; ++p) {
                             // delta = qh0 + 2p - ih = 2p + TH - 1 - u
@@ -610,27 +625,39 @@ __global__ __launch_bounds__(kBlock) void k_generic_pairs(const PhaseParams P,
 
     if (!wlive) return;
     // lane j16 + 16*k4, register v: position j16, output row dh = k4/2,
-    // channel 4*(k4%2) + v
+    // channel 4*(k4%2) + v.  Stores (and add_input loads) through a resource
+    // over the sample's output: the lane's byte offset of channel cb, the
+    // channel step v*out_sp in the scalar offset; rows and positions past the
+    // class's end take an out-of-range offset and are dropped.
     const int dh = k4 >> 1;
-    const int cb = co0 + 4 * (k4 & 1);
+    const int cb = g * P.Cog + co0 + 4 * (k4 & 1);
     const int od = qd * AD.s + rd - AD.p;
+    const int ybytes = 4 * P.C_out * P.out_sp;
+    const rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(y + (int64_t)n * P.C_out * P.out_sp, (short)0, ybytes,
+                                                        kRsrcWord3);
+    const rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(FUSED ? add + (int64_t)n * P.C_out * P.out_sp : y), (short)0, ybytes, kRsrcWord3);
+    float bb[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) bb[v] = bias ? bias[cb + v] : 0.0f;
+    const unsigned ch_step = 4u * (unsigned)P.out_sp;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const int iqh = irb * 2 * NP + 2 * p + dh;
-        if (iqh >= nqh) continue;
         const int oh = (P.cls_q0[c][1] + iqh) * AH.s + rh - AH.p;
 #pragma unroll
         for (int pb = 0; pb < PB; ++pb) {
-            if (iqw[pb] >= nqw) continue;
             const int ow = (P.cls_q0[c][2] + iqw[pb]) * AW.s + rw - AW.p;
-            const int sp = (od * AH.L_out + oh) * AW.L_out + ow;
+            const bool in = iqh < nqh && iqw[pb] < nqw;
+            const unsigned vo =
+                in ? 4u * (unsigned)(cb * P.out_sp + (od * AH.L_out + oh) * AW.L_out + ow) : kOutOfRange;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const int co = g * P.Cog + cb + v;
-                const int64_t idx = ((int64_t)n * P.C_out + co) * P.out_sp + sp;
-                const float bb = bias ? bias[co] : 0.0f;
-                const float aa = FUSED ? add[idx] : 0.0f;
-                y[idx] = epilogue<FUSED>(acc[p][pb][v], bb, aa);
+                const float aa = FUSED ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                                       ra, vo, v * ch_step, 0))
+                                       : 0.0f;
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, epilogue<FUSED>(acc[p][pb][v], bb[v], aa)),
+                                                      ry, vo, v * ch_step, 0);
             }
         }
     }
@@ -644,12 +671,14 @@ constexpr int kRows = 4;     // H rows per thread in k_generic_rows
 constexpr int kRowsMaxTH = 5; // largest H tap count instantiated
 
 // Largest H tap count of the shape if k_generic_rows applies, else 0: 4-channel
-// blocks, a group's input and the weights below 2 GiB, at least kRows outputs
+// blocks, a group's input, the weights and a sample's output below 2 GiB
+// (byte offsets of buffer resources), at least kRows outputs
 // along H, and on H every residue's taps at offsets 0, 1, .., T-1.
 int rows_th(const convt_plan &Pl) {
     if (pick_cpt(Pl.Cog) < 4) return 0;
     if (4 * Pl.Cig * Pl.in_sp > 0x7fffffff) return 0;           // byte offsets in the buffer
     if (4 * Pl.C_in * Pl.Cog * Pl.k_vol > 0x7fffffff) return 0; // resources over x and w
+    if (4 * Pl.C_out * Pl.out_sp > 0x7fffffff) return 0;        // and a sample's output
     const AxisPlan &A = Pl.ax[1];
     if (A.L_out < kRows) return 0; // nothing to share along H (1D shapes)
     int th = 1;
