@@ -72,12 +72,26 @@ def valid_macs(wl, N=None):
     return N * wl.C_in * (wl.C_out // wl.groups) * P
 
 
-def source_sha():
+# The source file each kernel is built from; with the headers every kernel
+# includes, it decides whether a stored counter record still describes the
+# kernel that runs.
+KERNEL_SOURCES = {"k_stream1d": "stream1d.hip", "k_igemm3d": "igemm3d.hip", "k_igemm3d_wide": "igemm3d.hip",
+                  "k_generic": "generic.hip", "k_generic_phase": "generic.hip", "k_generic_rows": "generic.hip",
+                  "k_generic_pairs": "generic.hip"}
+SHARED_SOURCES = ("convt_internal.h", "epilogue.hpp")
+
+
+def source_sha(kernel=None):
+    """Hash of the kernel's own source and the shared headers (of every
+    kernel source when kernel is None)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "transposed_convolution_forward_amd", "csrc")
-    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
-        if f.endswith((".hip", ".cpp", ".h", ".hpp")):
-            h.update(open(f, "rb").read())
+    if kernel is None:
+        files = sorted(f for f in glob.glob(os.path.join(csrc, "*")) if f.endswith((".hip", ".cpp", ".h", ".hpp")))
+    else:
+        files = [os.path.join(csrc, f) for f in (KERNEL_SOURCES[kernel],) + SHARED_SOURCES]
+    for f in files:
+        h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -91,7 +105,7 @@ def traffic_for(wl_name, kernel):
         rec = json.load(open(path)).get(wl_name)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha") != source_sha() or rec.get("kernel") != kernel:
+    if not rec or rec.get("kernel") != kernel or rec.get("source_sha") != source_sha(kernel):
         return None
     return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
 
