@@ -64,6 +64,9 @@ class Oracle:
         lib.oracle_axis_pair_counts.restype = ctypes.c_int
         lib.oracle_times_hardswish.argtypes = [_f64p, _f64p, ctypes.c_int64]
         lib.oracle_times_hardswish.restype = None
+        lib.oracle_convt_backward_data.argtypes = ([ctypes.c_int] + [ctypes.c_int64] * 4 + [_i64p] * 6 +
+                                                   [_f32p] * 2 + [_f64p, ctypes.c_int])
+        lib.oracle_convt_backward_data.restype = ctypes.c_int
         self.lib = lib
 
     # -- shapes -----------------------------------------------------------
@@ -111,6 +114,18 @@ class Oracle:
         if rc:
             raise ValueError("bad arguments")
         return out
+
+    def backward_data(self, *, ndim, N, C_in, C_out, groups, in_size, K, stride, pad, out_pad, dilation,
+                      dy, w, nthreads: int = 0) -> np.ndarray:
+        """Input gradient dx (adjoint of the forward's linear part) as float64,
+        shape (N, C_in, *in_size); dy has the forward output's shape."""
+        dx = np.empty((N, C_in) + tuple(int(v) for v in in_size), dtype=np.float64)
+        rc = self.lib.oracle_convt_backward_data(
+            ndim, N, C_in, C_out, groups, _arr(in_size), _arr(K), _arr(stride), _arr(pad),
+            _arr(out_pad), _arr(dilation), _f32(dy), _f32(w), dx.ctypes.data_as(_f64p), int(nthreads))
+        if rc:
+            raise ValueError("bad arguments")
+        return dx
 
     def times_hardswish(self, t: np.ndarray) -> np.ndarray:
         t = np.ascontiguousarray(t, dtype=np.float64)

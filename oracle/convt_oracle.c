@@ -298,3 +298,98 @@ void oracle_times_hardswish(const double *in, double *out, int64_t n)
 {
     for (int64_t e = 0; e < n; ++e) out[e] = times_hardswish(in[e]);
 }
+
+/* ---------------------------------------------------------------------------
+ * Input gradient: the adjoint of the forward's linear part (no bias, no
+ * epilogue).  The forward scatter adds x[n, ci, i] * w[ci, co_l, k] to
+ * y[n, g*Cog + co_l, o] with o = i*s - p + k*d; its transpose therefore sends
+ * dy[n, g*Cog + co_l, o] * w[ci, co_l, k] back to dx[n, ci, i], over the same
+ * (i, k) pairs, dropping those whose o leaves [0, L_out) on some axis.
+ * "Kimi-K2.6 l1_p79" transcript: the adjoint derivation that defines the
+ * transposed convolution as the transpose of the strided convolution; "Kimi-K2.6
+ * l2_p26" transcript: the convolution matrix C and its transpose C^T.
+ */
+typedef struct {
+    const problem *P;
+    const float *dy, *w;
+    double *dx;
+    int64_t next_slab, n_slabs;
+    pthread_mutex_t lock;
+} adjoint_job;
+
+/* One (n, g) slab: the scatter loop of the forward, read backwards. */
+static void adjoint_slab(const adjoint_job *J, int64_t n, int64_t g)
+{
+    const problem *P = J->P;
+    const int64_t Cig = P->C_in / P->G, Cog = P->C_out / P->G;
+    const int64_t ID = P->L_in[0], IH = P->L_in[1], IW = P->L_in[2];
+    const int64_t OD = P->L_out[0], OH = P->L_out[1], OW = P->L_out[2];
+    const int64_t KD = P->K[0], KH = P->K[1], KW = P->K[2];
+    const int64_t in_sp = ID * IH * IW, out_sp = OD * OH * OW, k_sp = KD * KH * KW;
+
+    for (int64_t ci_l = 0; ci_l < Cig; ++ci_l) {
+        const int64_t ci = g * Cig + ci_l;
+        double *dxc = J->dx + (n * P->C_in + ci) * in_sp;
+        const float *wci = J->w + ci * Cog * k_sp;      /* w[ci][co_l][kd][kh][kw] */
+        for (int64_t id = 0; id < ID; ++id)
+        for (int64_t ih = 0; ih < IH; ++ih)
+        for (int64_t iw = 0; iw < IW; ++iw) {
+            double acc = 0.0;
+            for (int64_t co_l = 0; co_l < Cog; ++co_l) {
+                const float *dyc = J->dy + (n * P->C_out + g * Cog + co_l) * out_sp;
+                for (int64_t kd = 0; kd < KD; ++kd) {
+                    const int64_t zd = id * P->s[0] + kd * P->d[0] - P->p[0];
+                    if (zd < 0 || zd >= OD) continue;
+                    for (int64_t kh = 0; kh < KH; ++kh) {
+                        const int64_t zh = ih * P->s[1] + kh * P->d[1] - P->p[1];
+                        if (zh < 0 || zh >= OH) continue;
+                        for (int64_t kw = 0; kw < KW; ++kw) {
+                            const int64_t zw = iw * P->s[2] + kw * P->d[2] - P->p[2];
+                            if (zw < 0 || zw >= OW) continue;
+                            acc += (double)dyc[(zd * OH + zh) * OW + zw] *
+                                   (double)wci[((co_l * KD + kd) * KH + kh) * KW + kw];
+                        }
+                    }
+                }
+            }
+            dxc[(id * IH + ih) * IW + iw] = acc;
+        }
+    }
+}
+
+static void *adjoint_worker(void *arg)
+{
+    adjoint_job *J = (adjoint_job *)arg;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        int64_t t = J->next_slab++;
+        pthread_mutex_unlock(&J->lock);
+        if (t >= J->n_slabs) break;
+        adjoint_slab(J, t / J->P->G, t % J->P->G);
+    }
+    return NULL;
+}
+
+/* dx (N*C_in*prod(L_in) doubles) from dy (N*C_out*prod(L_out) floats).
+ * Returns 0, or 1 on bad arguments. */
+int oracle_convt_backward_data(int ndim, int64_t N, int64_t C_in, int64_t C_out, int64_t G,
+                               const int64_t *in_size, const int64_t *K, const int64_t *s,
+                               const int64_t *p, const int64_t *op, const int64_t *d,
+                               const float *dy, const float *w, double *dx, int nthreads)
+{
+    problem P;
+    if (set_problem(&P, ndim, N, C_in, C_out, G, in_size, K, s, p, op, d)) return 1;
+    adjoint_job J;
+    J.P = &P; J.dy = dy; J.w = w; J.dx = dx;
+    J.next_slab = 0; J.n_slabs = N * G;
+    pthread_mutex_init(&J.lock, NULL);
+    int nt = resolve_threads(nthreads);
+    if (nt > J.n_slabs) nt = (int)(J.n_slabs > 0 ? J.n_slabs : 1);
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nt);
+    if (!th) return 1;
+    for (int t = 0; t < nt; ++t) pthread_create(&th[t], NULL, adjoint_worker, &J);
+    for (int t = 0; t < nt; ++t) pthread_join(th[t], NULL);
+    free(th);
+    pthread_mutex_destroy(&J.lock);
+    return 0;
+}

@@ -248,6 +248,60 @@ def pin_points_match_forward(orc):
                                    atol=1e-12)
 
 
+def _backward(orc, dy, w, *, groups=1, in_size, stride, pad, out_pad, dilation):
+    nd = dy.ndim - 2
+    return orc.backward_data(ndim=nd, N=dy.shape[0], C_in=w.shape[0], C_out=dy.shape[1],
+                             groups=groups, in_size=in_size, K=w.shape[2:], stride=stride, pad=pad,
+                             out_pad=out_pad, dilation=dilation, dy=dy, w=w)
+
+
+def pin_backward_worked_examples(orc):
+    """B1: the input gradient of the pages' worked examples E1-E4 is their
+    symbolic matrix read transposed: output o holds terms w_k * x_i, so dx_i
+    collects w_k * dy_o over those terms ("Kimi-K2.6 l2_p26" transcript: the
+    transposed convolution is C^T, so its adjoint is C)."""
+    rng = np.random.default_rng(13)
+    for e in _load("worked_examples.json")["examples"]:
+        vals = {name: np.float32(rng.standard_normal()) for name in e["w"]}
+        dy = rng.standard_normal(size=(1, 1) + tuple(e["out_size"])).astype(np.float32)
+        w = np.array([[[vals[n] for n in e["w"]]]], dtype=np.float32)
+        dx = _backward(orc, dy, w, in_size=e["in_size"], stride=e["stride"], pad=e["pad"],
+                       out_pad=e["out_pad"], dilation=e["dilation"])
+        want = np.zeros(len(e["x"]))
+        for o, terms in enumerate(e["y"]):
+            for wname, xname in terms:
+                want[e["x"].index(xname)] += float(vals[wname]) * float(dy[0, 0, o])
+        np.testing.assert_allclose(dx[0, 0], want, rtol=1e-12, atol=1e-12, err_msg=e["id"])
+
+
+def pin_backward_gather(orc):
+    """B2: the input gradient equals the strided forward convolution written
+    separately in gather form (tests/ref_conv.py) on the tiny shapes."""
+    for ci, case in enumerate(tiny_cases()):
+        nd, N, Cin, Cout, G, ins, K, s, p, op, d = case
+        _, w, _ = _case_arrays(case, 1100 + ci)
+        out = orc.output_size(nd, ins, K, s, p, op, d)
+        dy = _rand(np.random.default_rng(1200 + ci), (N, Cout) + out)
+        got = _backward(orc, dy, w, groups=G, in_size=ins, stride=s, pad=p, out_pad=op, dilation=d)
+        want = conv_forward(dy, w, groups=G, in_size=ins, stride=s, pad=p, dilation=d)
+        np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-11, err_msg=str(case))
+
+
+def pin_backward_adjoint(orc):
+    """B3: <convT(x), v> = <x, dx(v)> between the oracle's forward (bias 0) and
+    its input gradient."""
+    for ci, case in enumerate(tiny_cases()):
+        nd, N, Cin, Cout, G, ins, K, s, p, op, d = case
+        x, w, _ = _case_arrays(case, 1300 + ci)
+        y = _forward(orc, x, w, groups=G, stride=s, pad=p, out_pad=op, dilation=d)
+        v = _rand(np.random.default_rng(1400 + ci), y.shape)
+        dx = _backward(orc, v, w, groups=G, in_size=ins, stride=s, pad=p, out_pad=op, dilation=d)
+        lhs = float(np.sum(y * v.astype(np.float64)))
+        rhs = float(np.sum(x.astype(np.float64) * dx))
+        assert abs(lhs - rhs) <= 1e-9 * (1 + abs(lhs)), (case, lhs, rhs)
+
+
 ALL_PINS = [pin_closed_form_pages, pin_worked_examples, pin_numpy_convolve, pin_odd_only,
             pin_tap_counts, pin_adjoint, pin_dilate_flip_correlate, pin_group_decomposition,
-            pin_epilogue_values, pin_fused_forward, pin_points_match_forward]
+            pin_epilogue_values, pin_fused_forward, pin_points_match_forward,
+            pin_backward_worked_examples, pin_backward_gather, pin_backward_adjoint]

@@ -37,6 +37,14 @@ MUTATIONS = {
     "epilogue_add_dropped": ("slab[e] = times_hardswish(slab[e] + (double)ad[e]);",
                              "slab[e] = times_hardswish(slab[e]);"),
     "points_pad_sign": ("if (i * s - p + k * d == o)", "if (i * s + p + k * d == o)"),
+    # input gradient
+    "bwd_pad_sign_w": ("iw * P->s[2] + kw * P->d[2] - P->p[2]", "iw * P->s[2] + kw * P->d[2] + P->p[2]"),
+    "bwd_flip_kernel": ("(double)wci[((co_l * KD + kd) * KH + kh) * KW + kw]",
+                        "(double)wci[((co_l * KD + (KD - 1 - kd)) * KH + (KH - 1 - kh)) * KW + (KW - 1 - kw)]"),
+    "bwd_group_output_channel": ("J->dy + (n * P->C_out + g * Cog + co_l) * out_sp",
+                                 "J->dy + (n * P->C_out + co_l) * out_sp"),
+    "bwd_stride_dilation_swapped": ("ih * P->s[1] + kh * P->d[1] - P->p[1]",
+                                    "ih * P->d[1] + kh * P->s[1] - P->p[1]"),
 }
 
 
