@@ -107,6 +107,26 @@ CONVT_API convt_status convt_forward_add_hswish(const convt_plan *plan, const fl
                                       const float *bias, const float *add_input, float *y,
                                       void *stream);
 
+/*
+ * Input gradient: dx = the adjoint of the forward's linear part applied to dy
+ * (no bias or epilogue term), i.e. for every input position i and channel ci
+ * of group g
+ *   dx[n, ci, i] = sum over co_l < C_out/G and taps k whose o = i*s - p + k*d
+ *                  lies in [0, L_out) on every axis of w[ci, co_l, k] * dy[n, g*(C_out/G) + co_l, o].
+ * "Kimi-K2.6 l1_p79" transcript (ConvTranspose1d, dilation 2): the adjoint
+ * derivation, the transposed convolution being the transpose of the strided
+ * convolution; "Kimi-K2.6 l2_p26" transcript: the matrix C and its transpose.
+ * dy has y's layout (N, C_out, L_out...), dx has x's (N, C_in, L_in...), w as
+ * in the forward; all device memory, caller-owned; every dx element is
+ * written.  dy and w must not overlap dx.  Asynchronous on stream like the
+ * forward.  Returns CONVT_ERR_INVALID_ARG for NULL plan, dy, w or dx;
+ * CONVT_ERR_UNSUPPORTED if one output channel group's weights for a single
+ * input channel exceed 32 KB (C_out/G * prod(K) > 8192); CONVT_ERR_HIP if the
+ * launch fails.
+ */
+CONVT_API convt_status convt_backward_data(const convt_plan *plan, const float *dy, const float *w,
+                                           float *dx, void *stream);
+
 /* Release a plan.  NULL is a no-op. */
 CONVT_API void convt_plan_destroy(convt_plan *plan);
 

@@ -1,0 +1,60 @@
+"""Input gradient (convt_backward_data) through the C ABI against the oracle's
+adjoint loop (oracle_convt_backward_data), element by element, on seeded
+inputs: reduced shapes of every workload, the seeded random and degenerate
+shapes of the forward tests, full spatial sizes at a reduced batch, and the
+properties that every dx element is written and the inputs are untouched.
+Tolerance as the forward: |got - ref| <= 1e-4 + 1e-4 |ref|."""
+import numpy as np
+import pytest
+
+import oracle
+import transposed_convolution_forward_amd as T
+from transposed_convolution_forward_amd import synthetic as S
+
+from gpu_util import check_close, log, reduced
+from test_parity_gpu import DEGENERATE, REDUCED, _random_cases
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(wl, seed):
+    """dy ~ N(0, 1) in the forward output's shape and w as the workload's,
+    from the seeded generators both sides use."""
+    out = oracle.get().output_size(wl.ndim, wl.in_size, wl.K, wl.stride, wl.pad, wl.out_pad, wl.dilation)
+    inp = S.make_inputs(wl, seed, (wl.N, wl.C_out) + out)
+    return S.make_grad_output(wl, seed, (wl.N, wl.C_out) + out), inp["w"]
+
+
+def _check(wl, seed=0):
+    import torch
+    dy, w = _inputs(wl, seed)
+    ref = oracle.get().backward_data(ndim=wl.ndim, N=wl.N, C_in=wl.C_in, C_out=wl.C_out, groups=wl.groups,
+                                     in_size=wl.in_size, K=wl.K, stride=wl.stride, pad=wl.pad,
+                                     out_pad=wl.out_pad, dilation=wl.dilation, dy=dy, w=w)
+    plan = T.plan_for(wl)
+    log(f"  gpu backward_data: {wl.name} N={wl.N} in={wl.in_size}")
+    ddy, dw = torch.from_numpy(dy).cuda(), torch.from_numpy(w).cuda()
+    dx = torch.full(plan.x_shape(), float("nan"), dtype=torch.float32, device="cuda")
+    T.convt_backward_data(plan, ddy, dw, dx=dx)
+    torch.cuda.synchronize()
+    err = check_close(dx.cpu().numpy(), ref, f"backward_data {wl.name}")
+    log(f"  max abs err {err:.3e}")
+    # the inputs are left as they were
+    assert np.array_equal(ddy.cpu().numpy(), dy) and np.array_equal(dw.cpu().numpy(), w)
+
+
+@pytest.mark.parametrize("wl", REDUCED, ids=lambda w: f"{w.name}-N{w.N}-in{'x'.join(map(str, w.in_size))}")
+def test_backward_reduced(wl):
+    _check(wl)
+
+
+@pytest.mark.parametrize("wl", _random_cases(24) + DEGENERATE, ids=lambda w: w.name)
+def test_backward_random_and_degenerate(wl):
+    _check(wl)
+
+
+@pytest.mark.parametrize("wl", [reduced(S.LONG_1D, N=2), reduced(S.GROUPED_3D, N=1), reduced(S.FUSED_3D, N=2),
+                                reduced(S.HEAVY_3D, N=1, in_size=(8, 32, 32))],
+                         ids=lambda w: f"{w.name}-N{w.N}")
+def test_backward_full_spatial(wl):
+    _check(wl)

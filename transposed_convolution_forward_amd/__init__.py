@@ -20,7 +20,7 @@ PATH_NAMES = {v: k for k, v in PATHS.items()}
 
 # Every symbol include/convt.h declares.
 EXPORTS = ("convt_plan_create", "convt_plan_output_size", "convt_forward",
-           "convt_forward_add_hswish", "convt_plan_destroy", "convt_status_string",
+           "convt_forward_add_hswish", "convt_backward_data", "convt_plan_destroy", "convt_status_string",
            "convt_plan_set_path", "convt_plan_get_path", "convt_plan_describe")
 
 _lib_handle = None
@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
     L.convt_forward.restype = ctypes.c_int
     L.convt_forward_add_hswish.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     L.convt_forward_add_hswish.restype = ctypes.c_int
+    L.convt_backward_data.argtypes = [vp, vp, vp, vp, vp]
+    L.convt_backward_data.restype = ctypes.c_int
     L.convt_plan_destroy.argtypes = [vp]
     L.convt_plan_destroy.restype = None
     L.convt_status_string.argtypes = [ctypes.c_int]
@@ -168,6 +170,19 @@ def convt_forward_add_hswish(plan: Plan, x, w, bias, add_input, y=None, stream=N
     if st != CONVT_OK:
         raise ConvtError(st, "convt_forward_add_hswish")
     return y
+
+
+def convt_backward_data(plan: Plan, dy, w, dx=None, stream=None):
+    """dx = the input gradient of the forward's linear part, applied to dy."""
+    import torch
+    if dx is None:
+        dx = torch.empty(plan.x_shape(), dtype=torch.float32, device=dy.device)
+    args = (_dev_ptr(dy, plan.y_shape(), "dy"), _dev_ptr(w, plan.w_shape(), "w"),
+            _dev_ptr(dx, plan.x_shape(), "dx"))
+    st = lib().convt_backward_data(plan.handle, *args, _stream_ptr(stream))
+    if st != CONVT_OK:
+        raise ConvtError(st, "convt_backward_data")
+    return dx
 
 
 def convt_plan_destroy(plan: Plan) -> None:

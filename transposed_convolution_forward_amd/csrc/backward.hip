@@ -1,0 +1,156 @@
+// Input gradient of the transposed convolution: the adjoint of the forward's
+// linear part (no bias, no epilogue).  The forward adds x[n, ci, i] *
+// w[ci, co_l, k] to y[n, g*Cog + co_l, o] at o = i*s - p + k*d per axis, so
+//   dx[n, ci, i] = sum_{co_l, k : o in [0, L_out) on every axis}
+//                  w[ci, co_l, k] * dy[n, g*Cog + co_l, o].
+// "Kimi-K2.6 l1_p79" transcript (ConvTranspose1d, dilation 2): the adjoint
+// derivation that defines the transposed convolution as the transpose of the
+// strided convolution; "Kimi-K2.6 l2_p26" transcript: the convolution matrix C
+// and C^T.  Unlike the forward there are no stride phases here: every input
+// position meets every tap, and only taps that leave the output are skipped.
+//
+// Gather, input-stationary: a thread owns one input position and CPI
+// consecutive input channels of one group; consecutive lanes take consecutive
+// positions along W, so dx stores coalesce and dy loads step by the W stride.
+// The workgroup's weights, [tap][co_l][CPI], are staged once in LDS and read
+// as broadcasts, so each dy value loaded feeds CPI FMAs.  Every dx element is
+// written once by one thread; no atomics.
+#include <hip/hip_runtime.h>
+
+#include "backward.h"
+
+namespace convt {
+namespace {
+
+constexpr int kBwdBlock = 256;
+constexpr int kBwdMaxLds = 32768; // bytes of staged weights per workgroup
+
+struct BwdParams {
+    AxisPlan ax[kAxes];
+    int C_in, C_out, Cig, Cog, k_vol;
+    int in_sp, out_sp;
+    int ci_chunks;
+    int n0; // first batch index of this launch
+};
+
+template <int CPI>
+__global__ __launch_bounds__(kBwdBlock) void k_backward_data(const BwdParams P, const float *__restrict__ dy,
+                                                             const float *__restrict__ w,
+                                                             float *__restrict__ dx) {
+    const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
+    const int sp = blockIdx.x * kBwdBlock + threadIdx.x;
+    const bool live = sp < P.in_sp;
+    const int g = blockIdx.y / P.ci_chunks;
+    const int ci0 = (blockIdx.y % P.ci_chunks) * CPI;
+    const int n = P.n0 + blockIdx.z;
+    const int nci = min(CPI, P.Cig - ci0);
+
+    // ws[(k*Cog + co_l)*CPI + j] = w[g*Cig + ci0 + j][co_l][k]; channels past
+    // the group's last repeat it (their sums are never stored)
+    extern __shared__ __attribute__((aligned(16))) float ws[];
+    {
+        const float *wg = w + (int64_t)(g * P.Cig + ci0) * P.Cog * P.k_vol;
+        const int nw = P.k_vol * P.Cog * CPI;
+        for (int e = threadIdx.x; e < nw; e += kBwdBlock) {
+            const int j = e % CPI, t = e / CPI;
+            const int co_l = t % P.Cog, k = t / P.Cog;
+            ws[e] = wg[((int64_t)min(j, nci - 1) * P.Cog + co_l) * P.k_vol + k];
+        }
+    }
+    __syncthreads();
+
+    const int iw = sp % AW.L_in;
+    const int t2 = sp / AW.L_in;
+    const int ih = t2 % AH.L_in;
+    const int id = t2 / AH.L_in;
+
+    float acc[CPI];
+#pragma unroll
+    for (int j = 0; j < CPI; ++j) acc[j] = 0.0f;
+
+    const float *dyg = dy + ((int64_t)n * P.C_out + (int64_t)g * P.Cog) * P.out_sp;
+    for (int kd = 0; kd < AD.K; ++kd) {
+        const int od = id * AD.s - AD.p + kd * AD.d;
+        const bool okd = live && od >= 0 && od < AD.L_out;
+        for (int kh = 0; kh < AH.K; ++kh) {
+            const int oh = ih * AH.s - AH.p + kh * AH.d;
+            const bool okh = okd && oh >= 0 && oh < AH.L_out;
+            for (int kw = 0; kw < AW.K; ++kw) {
+                const int ow = iw * AW.s - AW.p + kw * AW.d;
+                const bool ok = okh && ow >= 0 && ow < AW.L_out;
+                // lanes whose tap leaves the output read the slab's first
+                // element and use 0
+                const float *dyo = dyg + (ok ? (od * AH.L_out + oh) * AW.L_out + ow : 0);
+                const float *wk = ws + ((kd * AH.K + kh) * AW.K + kw) * P.Cog * CPI;
+#pragma unroll 4
+                for (int co_l = 0; co_l < P.Cog; ++co_l) {
+                    const float v0 = dyo[(int64_t)co_l * P.out_sp];
+                    const float v = ok ? v0 : 0.0f;
+                    const float *wc = wk + co_l * CPI;
+#pragma unroll
+                    for (int j = 0; j < CPI; ++j) acc[j] = fmaf(v, wc[j], acc[j]);
+                }
+            }
+        }
+    }
+
+    if (!live) return;
+#pragma unroll
+    for (int j = 0; j < CPI; ++j) {
+        if (j >= nci) break;
+        dx[((int64_t)n * P.C_in + g * P.Cig + ci0 + j) * P.in_sp + sp] = acc[j];
+    }
+}
+
+// Input channels per thread: as many as the group has, up to 16, while the
+// staged weights fit in LDS.
+int pick_cpi(const convt_plan &P) {
+    for (int c = 16; c >= 1; c /= 2)
+        if ((c <= P.Cig || c == 1) && (int64_t)P.k_vol * P.Cog * c * 4 <= kBwdMaxLds) return c;
+    return 0;
+}
+
+template <int CPI>
+int launch(const convt_plan &Pl, BwdParams &P, const float *dy, const float *w, float *dx, hipStream_t st) {
+    P.ci_chunks = (int)((Pl.Cig + CPI - 1) / CPI);
+    const unsigned gx = (unsigned)((Pl.in_sp + kBwdBlock - 1) / kBwdBlock);
+    const unsigned gy = (unsigned)(Pl.G * P.ci_chunks);
+    const size_t lds = (size_t)Pl.k_vol * Pl.Cog * CPI * sizeof(float);
+    for (int64_t n0 = 0; n0 < Pl.N; n0 += 65535) {
+        P.n0 = (int)n0;
+        const unsigned gz = (unsigned)(Pl.N - n0 < 65535 ? Pl.N - n0 : 65535);
+        hipLaunchKernelGGL((k_backward_data<CPI>), dim3(gx, gy, gz), dim3(kBwdBlock), lds, st, P, dy, w, dx);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+    }
+    return 0;
+}
+
+} // namespace
+
+bool backward_data_supports(const convt_plan &P) {
+    const int c = pick_cpi(P);
+    return c > 0 && P.G * ((P.Cig + c - 1) / c) <= 65535;
+}
+
+int launch_backward_data(const convt_plan &Pl, const float *dy, const float *w, float *dx, void *stream) {
+    BwdParams P;
+    for (int a = 0; a < kAxes; ++a) P.ax[a] = Pl.ax[a];
+    P.C_in = (int)Pl.C_in;
+    P.C_out = (int)Pl.C_out;
+    P.Cig = (int)Pl.Cig;
+    P.Cog = (int)Pl.Cog;
+    P.k_vol = (int)Pl.k_vol;
+    P.in_sp = (int)Pl.in_sp;
+    P.out_sp = (int)Pl.out_sp;
+    hipStream_t st = (hipStream_t)stream;
+    switch (pick_cpi(Pl)) {
+    case 16: return launch<16>(Pl, P, dy, w, dx, st);
+    case 8: return launch<8>(Pl, P, dy, w, dx, st);
+    case 4: return launch<4>(Pl, P, dy, w, dx, st);
+    case 2: return launch<2>(Pl, P, dy, w, dx, st);
+    default: return launch<1>(Pl, P, dy, w, dx, st);
+    }
+}
+
+} // namespace convt

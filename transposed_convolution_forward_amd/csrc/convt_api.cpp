@@ -8,6 +8,7 @@
 #include <new>
 #include <string>
 
+#include "backward.h"
 #include "convt_internal.h"
 
 using convt::AxisPlan;
@@ -186,6 +187,13 @@ convt_status convt_forward_add_hswish(const convt_plan *plan, const float *x, co
                                       void *stream) {
     if (!plan || !x || !w || !y || !add_input) return CONVT_ERR_INVALID_ARG;
     return dispatch(plan, x, w, bias, add_input, y, stream);
+}
+
+convt_status convt_backward_data(const convt_plan *plan, const float *dy, const float *w, float *dx,
+                                 void *stream) {
+    if (!plan || !dy || !w || !dx) return CONVT_ERR_INVALID_ARG;
+    if (!convt::backward_data_supports(*plan)) return CONVT_ERR_UNSUPPORTED;
+    return convt::launch_backward_data(*plan, dy, w, dx, stream) == 0 ? CONVT_OK : CONVT_ERR_HIP;
 }
 
 void convt_plan_destroy(convt_plan *plan) { delete plan; }

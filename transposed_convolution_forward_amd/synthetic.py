@@ -20,6 +20,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 TENSOR_X, TENSOR_W, TENSOR_BIAS, TENSOR_ADD = 0, 1, 2, 3
+TENSOR_DY = 4  # the output gradient fed to the input-gradient pass
 
 
 @dataclasses.dataclass(frozen=True)
@@ -91,6 +92,11 @@ def make_inputs(wl: Workload, seed: int = 0, out_shape: Optional[Sequence[int]] 
             raise ValueError("fused workload needs out_shape for add_input")
         d["add"] = normal(tuple(out_shape), seed, wl.wid, TENSOR_ADD)
     return d
+
+
+def make_grad_output(wl: Workload, seed: int, out_shape: Sequence[int]):
+    """dy ~ N(0, 1) in the forward output's shape, for the input gradient."""
+    return normal(tuple(out_shape), seed, wl.wid, TENSOR_DY)
 
 
 # The five workloads: a tiny 1D case, the long-sequence 1D case, a grouped
