@@ -15,6 +15,10 @@ N=16, 32->64 channels, L=131072, K=3, stride 2, padding 1, dilation 2):
   cpu_baseline  the fp64 CPU oracle, untuned, on a bounded sample of the same
              workload, in the same unit.
 
+--op backward_data times the input gradient (convt_backward_data: dy and w in,
+dx out) on the same workload instead of the forward; its bytes are dy + w + dx
+and its valid MACs those of the forward.
+
 --copy-calibration instead times a plain 1 GiB device copy (used to scale the
 HBM byte counters of a profiler run).
 """
@@ -56,6 +60,13 @@ def algorithmic_bytes(wl, N=None):
     if wl.fused:
         b += ys
     return 4 * b
+
+
+def algorithmic_bytes_backward(wl, N=None):
+    """Input gradient: dy + w + dx, each once."""
+    N = wl.N if N is None else N
+    return 4 * (N * wl.C_out * int(np.prod(out_size(wl))) + int(np.prod(wl.w_shape())) +
+                N * wl.C_in * int(np.prod(wl.in_size)))
 
 
 def valid_macs(wl, N=None):
@@ -110,24 +121,30 @@ def traffic_for(wl_name, kernel):
     return int(rec["fetch_bytes"]) + int(rec["write_bytes"])
 
 
-def cpu_baseline(wl, inp, budget_slabs=None):
+def cpu_baseline(wl, inp, budget_slabs=None, op="forward"):
     """The oracle (as it stands) on the first n_s batch samples."""
     import oracle
     orc = oracle.get()
     cores = min(16, os.cpu_count() or 1)
     n_s = budget_slabs or max(1, min(wl.N, cores // max(1, wl.groups)))
-    sub = dict(x=np.ascontiguousarray(inp["x"][:n_s]), w=inp["w"], bias=inp["bias"],
-               add=None if inp["add"] is None else np.ascontiguousarray(inp["add"][:n_s]))
     threads = min(cores, n_s * wl.groups)
+    shape = dict(ndim=wl.ndim, N=n_s, C_in=wl.C_in, C_out=wl.C_out, groups=wl.groups,
+                 in_size=wl.in_size, K=wl.K, stride=wl.stride, pad=wl.pad, out_pad=wl.out_pad,
+                 dilation=wl.dilation, nthreads=threads)
     t0 = time.perf_counter()
-    orc.forward(ndim=wl.ndim, N=n_s, C_in=wl.C_in, C_out=wl.C_out, groups=wl.groups,
-                in_size=wl.in_size, K=wl.K, stride=wl.stride, pad=wl.pad, out_pad=wl.out_pad,
-                dilation=wl.dilation, nthreads=threads, **sub)
+    if op == "backward_data":
+        orc.backward_data(dy=np.ascontiguousarray(inp["dy"][:n_s]), w=inp["w"], **shape)
+        nbytes = algorithmic_bytes_backward(wl, n_s)
+    else:
+        orc.forward(x=np.ascontiguousarray(inp["x"][:n_s]), w=inp["w"], bias=inp["bias"],
+                    add=None if inp["add"] is None else np.ascontiguousarray(inp["add"][:n_s]), **shape)
+        nbytes = algorithmic_bytes(wl, n_s)
     dt = time.perf_counter() - t0
-    return {"value": algorithmic_bytes(wl, n_s) / dt / 1e9, "unit": "GB/s", "cores": threads,
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"first {n_s} of {wl.N} batch samples (all channels and positions), "
-                      f"{dt:.2f} s wall; fp64 scatter, {threads} threads",
+                      f"{dt:.2f} s wall; fp64 {'adjoint' if op == 'backward_data' else 'scatter'} loop, "
+                      f"{threads} threads",
             "valid_mac_gflops": 2 * valid_macs(wl, n_s) / dt / 1e9}
 
 
@@ -150,6 +167,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=S.LONG_1D.name, choices=sorted(S.BY_NAME))
     ap.add_argument("--path", default="auto", choices=sorted(T.PATHS))
+    ap.add_argument("--op", default="forward", choices=["forward", "backward_data"],
+                    help="forward (the hot path, default) or the input gradient")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -167,16 +186,21 @@ def main():
 
     wl = S.BY_NAME[args.workload]
     print(f"[bench] workload {wl.name}: generating seeded inputs", file=sys.stderr, flush=True)
+    bwd = args.op == "backward_data"
     inp = S.make_inputs(wl, 0, (wl.N, wl.C_out) + out_size(wl))
+    if bwd:
+        inp = {"dy": S.make_grad_output(wl, 0, (wl.N, wl.C_out) + out_size(wl)), "w": inp["w"]}
     dev = {k: (None if v is None else torch.from_numpy(v).cuda()) for k, v in inp.items()}
     plan = T.plan_for(wl)
     if args.path != "auto":
         T.convt_plan_set_path(plan, args.path)
     path = T.convt_plan_get_path(plan)
-    y = torch.empty(plan.y_shape(), dtype=torch.float32, device="cuda")
+    y = torch.empty(plan.x_shape() if bwd else plan.y_shape(), dtype=torch.float32, device="cuda")
 
     def step():
-        if wl.fused:
+        if bwd:
+            T.convt_backward_data(plan, dev["dy"], dev["w"], dx=y)
+        elif wl.fused:
             T.convt_forward_add_hswish(plan, dev["x"], dev["w"], dev["bias"], dev["add"], y=y)
         else:
             T.convt_forward(plan, dev["x"], dev["w"], dev["bias"], y=y)
@@ -223,13 +247,13 @@ def main():
     del evict
     cold = np.array([a.elapsed_time(b) for a, b in ev_cold])
 
-    nbytes = algorithmic_bytes(wl)
+    nbytes = algorithmic_bytes_backward(wl) if bwd else algorithmic_bytes(wl)
     flops = 2 * valid_macs(wl)
     gbs = nbytes / (ms_per_step * 1e-3) / 1e9
     t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
     t_fp32 = flops / (PEAK_FP32_TFLOPS * 1e12)
     m = re.search(r"kernel=(\S+)", T.convt_plan_describe(plan))
-    kernel = m.group(1) if m else KERNEL_NAMES[path]
+    kernel = "k_backward_data" if bwd else (m.group(1) if m else KERNEL_NAMES[path])
     if t_hbm >= t_fp32:
         ach = nbytes / (ms_launch * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -251,10 +275,11 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, inp)
+        cpu = cpu_baseline(wl, inp, op=args.op)
 
     line = {
-        "metric": "ConvTranspose fwd GB/s and valid-MAC TFLOP/s, % of roofline, 1x MI355X",
+        "metric": ("ConvTranspose input-gradient GB/s and valid-MAC TFLOP/s, % of roofline, 1x MI355X" if bwd
+                   else "ConvTranspose fwd GB/s and valid-MAC TFLOP/s, % of roofline, 1x MI355X"),
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32",
@@ -264,7 +289,8 @@ def main():
                    "out_size": list(out_size(wl)), "K": list(wl.K), "stride": list(wl.stride),
                    "pad": list(wl.pad), "out_pad": list(wl.out_pad),
                    "dilation": list(wl.dilation), "bias": wl.bias, "fused": wl.fused,
-                   "path": path, "parallelism": "single GPU"},
+                   "path": "backward_data" if bwd else path, "op": args.op,
+                   "parallelism": "single GPU"},
         "valid_mac_tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
         "hbm_frac": round(t_hbm / (ms_per_step * 1e-3), 4),
         "fp32_frac": round(t_fp32 / (ms_per_step * 1e-3), 4),

@@ -120,9 +120,8 @@ CONVT_API convt_status convt_forward_add_hswish(const convt_plan *plan, const fl
  * in the forward; all device memory, caller-owned; every dx element is
  * written.  dy and w must not overlap dx.  Asynchronous on stream like the
  * forward.  Returns CONVT_ERR_INVALID_ARG for NULL plan, dy, w or dx;
- * CONVT_ERR_UNSUPPORTED if one output channel group's weights for a single
- * input channel exceed 32 KB (C_out/G * prod(K) > 8192); CONVT_ERR_HIP if the
- * launch fails.
+ * CONVT_ERR_UNSUPPORTED if C_out/G > 8192; CONVT_ERR_HIP if the launch
+ * fails.
  */
 CONVT_API convt_status convt_backward_data(const convt_plan *plan, const float *dy, const float *w,
                                            float *dx, void *stream);

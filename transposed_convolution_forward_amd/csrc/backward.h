@@ -5,8 +5,8 @@
 
 namespace convt {
 
-// The kernel can run P: one input channel's weights for a group (C_out/G x
-// prod(K) floats) fit in the 32 KB it stages per workgroup.
+// The kernel can run P: one tap's weights of one input channel for a group
+// (C_out/G floats) fit in the 32 KB it stages per workgroup.
 bool backward_data_supports(const convt_plan &P);
 // dx = the adjoint of the forward's linear part applied to dy; hipSuccess or
 // the launch error (as int).

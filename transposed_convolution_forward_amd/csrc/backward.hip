@@ -12,9 +12,9 @@
 // Gather, input-stationary: a thread owns one input position and CPI
 // consecutive input channels of one group; consecutive lanes take consecutive
 // positions along W, so dx stores coalesce and dy loads step by the W stride.
-// The workgroup's weights, [tap][co_l][CPI], are staged once in LDS and read
-// as broadcasts, so each dy value loaded feeds CPI FMAs.  Every dx element is
-// written once by one thread; no atomics.
+// The workgroup's weights, [tap][co_l][CPI], are staged in LDS a chunk of
+// taps at a time and read as broadcasts, so each dy value loaded feeds CPI
+// FMAs.  Every dx element is written once by one thread; no atomics.
 #include <hip/hip_runtime.h>
 
 #include "backward.h"
@@ -30,7 +30,8 @@ struct BwdParams {
     int C_in, C_out, Cig, Cog, k_vol;
     int in_sp, out_sp;
     int ci_chunks;
-    int n0; // first batch index of this launch
+    int taps_per_chunk; // taps whose weights are staged at once
+    int n0;             // first batch index of this launch
 };
 
 template <int CPI>
@@ -45,20 +46,6 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data(const BwdParams P, 
     const int n = P.n0 + blockIdx.z;
     const int nci = min(CPI, P.Cig - ci0);
 
-    // ws[(k*Cog + co_l)*CPI + j] = w[g*Cig + ci0 + j][co_l][k]; channels past
-    // the group's last repeat it (their sums are never stored)
-    extern __shared__ __attribute__((aligned(16))) float ws[];
-    {
-        const float *wg = w + (int64_t)(g * P.Cig + ci0) * P.Cog * P.k_vol;
-        const int nw = P.k_vol * P.Cog * CPI;
-        for (int e = threadIdx.x; e < nw; e += kBwdBlock) {
-            const int j = e % CPI, t = e / CPI;
-            const int co_l = t % P.Cog, k = t / P.Cog;
-            ws[e] = wg[((int64_t)min(j, nci - 1) * P.Cog + co_l) * P.k_vol + k];
-        }
-    }
-    __syncthreads();
-
     const int iw = sp % AW.L_in;
     const int t2 = sp / AW.L_in;
     const int ih = t2 % AH.L_in;
@@ -68,28 +55,42 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data(const BwdParams P, 
 #pragma unroll
     for (int j = 0; j < CPI; ++j) acc[j] = 0.0f;
 
+    // ws[(t*Cog + co_l)*CPI + j] = w[g*Cig + ci0 + j][co_l][t0 + t] for the
+    // chunk's taps t; channels past the group's last repeat it (their sums are
+    // never stored)
+    extern __shared__ __attribute__((aligned(16))) float ws[];
+    const float *wg = w + (int64_t)(g * P.Cig + ci0) * P.Cog * P.k_vol;
     const float *dyg = dy + ((int64_t)n * P.C_out + (int64_t)g * P.Cog) * P.out_sp;
-    for (int kd = 0; kd < AD.K; ++kd) {
-        const int od = id * AD.s - AD.p + kd * AD.d;
-        const bool okd = live && od >= 0 && od < AD.L_out;
-        for (int kh = 0; kh < AH.K; ++kh) {
+    for (int t0 = 0; t0 < P.k_vol; t0 += P.taps_per_chunk) {
+        const int tc = min(P.taps_per_chunk, P.k_vol - t0);
+        if (t0 > 0) __syncthreads(); // the previous chunk is consumed
+        const int nw = tc * P.Cog * CPI;
+        for (int e = threadIdx.x; e < nw; e += kBwdBlock) {
+            const int j = e % CPI, t = e / CPI;
+            const int co_l = t % P.Cog, tap = t / P.Cog;
+            ws[e] = wg[((int64_t)min(j, nci - 1) * P.Cog + co_l) * P.k_vol + t0 + tap];
+        }
+        __syncthreads();
+        for (int t = 0; t < tc; ++t) {
+            const int k = t0 + t;
+            const int kw = k % AW.K, kdh = k / AW.K;
+            const int kh = kdh % AH.K, kd = kdh / AH.K;
+            const int od = id * AD.s - AD.p + kd * AD.d;
             const int oh = ih * AH.s - AH.p + kh * AH.d;
-            const bool okh = okd && oh >= 0 && oh < AH.L_out;
-            for (int kw = 0; kw < AW.K; ++kw) {
-                const int ow = iw * AW.s - AW.p + kw * AW.d;
-                const bool ok = okh && ow >= 0 && ow < AW.L_out;
-                // lanes whose tap leaves the output read the slab's first
-                // element and use 0
-                const float *dyo = dyg + (ok ? (od * AH.L_out + oh) * AW.L_out + ow : 0);
-                const float *wk = ws + ((kd * AH.K + kh) * AW.K + kw) * P.Cog * CPI;
+            const int ow = iw * AW.s - AW.p + kw * AW.d;
+            const bool ok = live && od >= 0 && od < AD.L_out && oh >= 0 && oh < AH.L_out && ow >= 0 &&
+                            ow < AW.L_out;
+            // lanes whose tap leaves the output read the slab's first element
+            // and use 0
+            const float *dyo = dyg + (ok ? (od * AH.L_out + oh) * AW.L_out + ow : 0);
+            const float *wk = ws + t * P.Cog * CPI;
 #pragma unroll 4
-                for (int co_l = 0; co_l < P.Cog; ++co_l) {
-                    const float v0 = dyo[(int64_t)co_l * P.out_sp];
-                    const float v = ok ? v0 : 0.0f;
-                    const float *wc = wk + co_l * CPI;
+            for (int co_l = 0; co_l < P.Cog; ++co_l) {
+                const float v0 = dyo[(int64_t)co_l * P.out_sp];
+                const float v = ok ? v0 : 0.0f;
+                const float *wc = wk + co_l * CPI;
 #pragma unroll
-                    for (int j = 0; j < CPI; ++j) acc[j] = fmaf(v, wc[j], acc[j]);
-                }
+                for (int j = 0; j < CPI; ++j) acc[j] = fmaf(v, wc[j], acc[j]);
             }
         }
     }
@@ -102,20 +103,22 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data(const BwdParams P, 
     }
 }
 
-// Input channels per thread: as many as the group has, up to 16, while the
-// staged weights fit in LDS.
+// Input channels per thread: as many as the group has, up to 16, while one
+// tap's weights for them (C_out/G x CPI floats) fit in LDS.
 int pick_cpi(const convt_plan &P) {
     for (int c = 16; c >= 1; c /= 2)
-        if ((c <= P.Cig || c == 1) && (int64_t)P.k_vol * P.Cog * c * 4 <= kBwdMaxLds) return c;
+        if ((c <= P.Cig || c == 1) && (int64_t)P.Cog * c * 4 <= kBwdMaxLds) return c;
     return 0;
 }
 
 template <int CPI>
 int launch(const convt_plan &Pl, BwdParams &P, const float *dy, const float *w, float *dx, hipStream_t st) {
     P.ci_chunks = (int)((Pl.Cig + CPI - 1) / CPI);
+    const int64_t per_tap = Pl.Cog * CPI * (int64_t)sizeof(float);
+    P.taps_per_chunk = (int)(kBwdMaxLds / per_tap < Pl.k_vol ? kBwdMaxLds / per_tap : Pl.k_vol);
     const unsigned gx = (unsigned)((Pl.in_sp + kBwdBlock - 1) / kBwdBlock);
     const unsigned gy = (unsigned)(Pl.G * P.ci_chunks);
-    const size_t lds = (size_t)Pl.k_vol * Pl.Cog * CPI * sizeof(float);
+    const size_t lds = (size_t)(P.taps_per_chunk * per_tap);
     for (int64_t n0 = 0; n0 < Pl.N; n0 += 65535) {
         P.n0 = (int)n0;
         const unsigned gz = (unsigned)(Pl.N - n0 < 65535 ? Pl.N - n0 : 65535);
