@@ -88,7 +88,8 @@ def valid_macs(wl, N=None):
 # kernel that runs.
 KERNEL_SOURCES = {"k_stream1d": "stream1d.hip", "k_igemm3d": "igemm3d.hip", "k_igemm3d_wide": "igemm3d.hip",
                   "k_generic": "generic.hip", "k_generic_phase": "generic.hip", "k_generic_rows": "generic.hip",
-                  "k_generic_pairs": "generic.hip", "k_backward_data": "backward.hip"}
+                  "k_generic_pairs": "generic.hip", "k_backward_data": "backward.hip",
+                  "k_backward_data_mfma": "backward.hip"}
 SHARED_SOURCES = ("convt_internal.h", "epilogue.hpp")
 
 
@@ -253,7 +254,9 @@ def main():
     t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
     t_fp32 = flops / (PEAK_FP32_TFLOPS * 1e12)
     m = re.search(r"kernel=(\S+)", T.convt_plan_describe(plan))
-    kernel = "k_backward_data" if bwd else (m.group(1) if m else KERNEL_NAMES[path])
+    if bwd:
+        m = re.search(r"input gradient: kernel=(\S+)", T.convt_plan_describe(plan))
+    kernel = m.group(1) if m else KERNEL_NAMES[path]
     if t_hbm >= t_fp32:
         ach = nbytes / (ms_launch * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

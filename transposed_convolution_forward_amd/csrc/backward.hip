@@ -103,6 +103,130 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data(const BwdParams P, 
     }
 }
 
+// ----------------------------------------------------------- matrix cores
+// For groups of 16k input channels and 4k output channels the same sum is an
+// implicit GEMM per tap on v_mfma_f32_16x16x4_f32: rows = 16 input channels,
+// columns = 16 input positions, K = 4 output channels of the group.  A (lane
+// i + 16c) = w[ci0 + i][4q + c][tap], B (lane j + 16c) = dy[4q + c][o(j, tap)],
+// D (lane j + 16(i/4), register i%4) = dx[ci0 + i][position j].  A wave owns
+// MT row tiles x PB position blocks, so each B it loads feeds MT MFMAs and each
+// A feeds PB.  The A operands of a chunk of taps, [tap][q][m][64 lanes], are
+// staged in LDS (one 64-float row each, conflict-free lane reads); dy goes
+// through a buffer resource over the group's channels of one sample, the
+// channel quad in the scalar offset, and a tap that leaves the output gets an
+// out-of-range offset (the hardware returns zero).
+typedef float bwd_v4f __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t bwd_rsrc_t;
+constexpr int kBwdRsrcWord3 = 0x00020000; // raw (untyped) buffer access
+constexpr unsigned kBwdOutOfRange = 0x80000000u;
+
+template <int MT, int PB>
+__global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma(const BwdParams P, const float *__restrict__ dy,
+                                                                  const float *__restrict__ w,
+                                                                  float *__restrict__ dx) {
+    const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j16 = lane & 15, c4 = lane >> 4;
+    const int g = blockIdx.y / P.ci_chunks;
+    const int ci0 = (blockIdx.y % P.ci_chunks) * 16 * MT; // first input channel of the group
+    const int n = P.n0 + blockIdx.z;
+    const int NQ = P.Cog / 4;
+
+    int id[PB], ih[PB], iw[PB], sp[PB];
+    bool live[PB];
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) {
+        sp[pb] = (blockIdx.x * 4 + wave) * 16 * PB + pb * 16 + j16;
+        live[pb] = sp[pb] < P.in_sp;
+        iw[pb] = sp[pb] % AW.L_in;
+        const int t2 = sp[pb] / AW.L_in;
+        ih[pb] = t2 % AH.L_in;
+        id[pb] = t2 / AH.L_in;
+    }
+
+    bwd_v4f acc[MT][PB];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) acc[m][pb] = bwd_v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const bwd_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(dy + ((int64_t)n * P.C_out + (int64_t)g * P.Cog) * P.out_sp), (short)0,
+        (int)(4 * P.Cog * P.out_sp), kBwdRsrcWord3);
+    const unsigned quad_bytes = 16u * (unsigned)P.out_sp; // 4 channels
+    const unsigned lane_ch = (unsigned)c4 * (unsigned)P.out_sp;
+
+    extern __shared__ __attribute__((aligned(16))) float wa[];
+    // lane l of row (t, q, m): w[g*Cig + ci0 + 16m + l%16][4q + l/16][t0 + t]
+    const float *wl_ = w + ((int64_t)(g * P.Cig + ci0 + j16) * P.Cog + c4) * P.k_vol;
+    for (int t0 = 0; t0 < P.k_vol; t0 += P.taps_per_chunk) {
+        const int tc = min(P.taps_per_chunk, P.k_vol - t0);
+        if (t0 > 0) __syncthreads(); // the previous chunk is consumed
+        const int nrows = tc * NQ * MT;
+        for (int r = wave; r < nrows; r += 4) {
+            const int m = r % MT, t = r / MT;
+            const int q = t % NQ, tap = t / NQ;
+            wa[r * 64 + lane] = wl_[((int64_t)(16 * m) * P.Cog + 4 * q) * P.k_vol + t0 + tap];
+        }
+        __syncthreads();
+        for (int t = 0; t < tc; ++t) {
+            const int k = t0 + t;
+            const int kw = k % AW.K, kdh = k / AW.K;
+            const int kh = kdh % AH.K, kd = kdh / AH.K;
+            unsigned vo[PB];
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) {
+                const int od = id[pb] * AD.s - AD.p + kd * AD.d;
+                const int oh = ih[pb] * AH.s - AH.p + kh * AH.d;
+                const int ow = iw[pb] * AW.s - AW.p + kw * AW.d;
+                const bool ok = live[pb] && od >= 0 && od < AD.L_out && oh >= 0 && oh < AH.L_out && ow >= 0 &&
+                                ow < AW.L_out;
+                vo[pb] = ok ? 4u * (lane_ch + (unsigned)((od * AH.L_out + oh) * AW.L_out + ow)) : kBwdOutOfRange;
+            }
+            const float *wt = wa + t * NQ * MT * 64 + lane;
+            for (int q = 0; q < NQ; ++q) {
+                float b[PB], a[MT];
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb)
+                    b[pb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdy, vo[pb], q * quad_bytes, 0));
+#pragma unroll
+                for (int m = 0; m < MT; ++m) a[m] = wt[(q * MT + m) * 64];
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb)
+                        acc[m][pb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], b[pb], acc[m][pb], 0, 0, 0);
+            }
+        }
+    }
+
+    // lane j16 + 16*c4, register v: position j16, input channel 16m + 4*c4 + v
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) {
+        if (!live[pb]) continue;
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int ci = g * P.Cig + ci0 + 16 * m + 4 * c4 + v;
+                dx[((int64_t)n * P.C_in + ci) * P.in_sp + sp[pb]] = acc[m][pb][v];
+            }
+    }
+}
+
+constexpr int kBwdPB = 2; // 16-position blocks per wave
+
+// Row tiles per wave for the matrix kernel (0: it does not apply).  Needs
+// groups of 16k input and 4k output channels, one tap's A rows within the
+// staging budget, and a group's dy below 2 GiB (buffer offsets).
+int pick_mt(const convt_plan &P) {
+    if (P.Cig % 16 != 0 || P.Cog % 4 != 0) return 0;
+    if (4 * P.Cog * P.out_sp > 0x7fffffff) return 0;
+    for (int mt = 4; mt >= 1; mt /= 2)
+        if ((P.Cig / 16) % mt == 0 && (int64_t)(P.Cog / 4) * mt * 64 * 4 <= kBwdMaxLds) return mt;
+    return 0;
+}
+
 // Input channels per thread: as many as the group has, up to 16, while one
 // tap's weights for them (C_out/G x CPI floats) fit in LDS.
 int pick_cpi(const convt_plan &P) {
@@ -129,7 +253,30 @@ int launch(const convt_plan &Pl, BwdParams &P, const float *dy, const float *w, 
     return 0;
 }
 
+template <int MT>
+int launch_mfma(const convt_plan &Pl, BwdParams &P, const float *dy, const float *w, float *dx, hipStream_t st) {
+    P.ci_chunks = (int)(Pl.Cig / (16 * MT));
+    const int64_t per_tap = (Pl.Cog / 4) * MT * 64 * (int64_t)sizeof(float);
+    P.taps_per_chunk = (int)(kBwdMaxLds / per_tap < Pl.k_vol ? kBwdMaxLds / per_tap : Pl.k_vol);
+    const unsigned gx = (unsigned)((Pl.in_sp + 64 * kBwdPB - 1) / (64 * kBwdPB));
+    const unsigned gy = (unsigned)(Pl.G * P.ci_chunks);
+    const size_t lds = (size_t)(P.taps_per_chunk * per_tap);
+    for (int64_t n0 = 0; n0 < Pl.N; n0 += 65535) {
+        P.n0 = (int)n0;
+        const unsigned gz = (unsigned)(Pl.N - n0 < 65535 ? Pl.N - n0 : 65535);
+        hipLaunchKernelGGL((k_backward_data_mfma<MT, kBwdPB>), dim3(gx, gy, gz), dim3(kBwdBlock), lds, st, P, dy,
+                           w, dx);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+    }
+    return 0;
+}
+
 } // namespace
+
+const char *backward_data_kernel_name(const convt_plan &P) {
+    return pick_mt(P) > 0 ? "k_backward_data_mfma" : "k_backward_data";
+}
 
 bool backward_data_supports(const convt_plan &P) {
     const int c = pick_cpi(P);
@@ -147,6 +294,12 @@ int launch_backward_data(const convt_plan &Pl, const float *dy, const float *w, 
     P.in_sp = (int)Pl.in_sp;
     P.out_sp = (int)Pl.out_sp;
     hipStream_t st = (hipStream_t)stream;
+    switch (pick_mt(Pl)) {
+    case 4: return launch_mfma<4>(Pl, P, dy, w, dx, st);
+    case 2: return launch_mfma<2>(Pl, P, dy, w, dx, st);
+    case 1: return launch_mfma<1>(Pl, P, dy, w, dx, st);
+    default: break;
+    }
     switch (pick_cpi(Pl)) {
     case 16: return launch<16>(Pl, P, dy, w, dx, st);
     case 8: return launch<8>(Pl, P, dy, w, dx, st);
