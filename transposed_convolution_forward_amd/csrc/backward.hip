@@ -184,6 +184,7 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma(const BwdParam
                 vo[pb] = ok ? 4u * (lane_ch + (unsigned)((od * AH.L_out + oh) * AW.L_out + ow)) : kBwdOutOfRange;
             }
             const float *wt = wa + t * NQ * MT * 64 + lane;
+#pragma unroll 4
             for (int q = 0; q < NQ; ++q) {
                 float b[PB], a[MT];
 #pragma unroll
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma(const BwdParam
     }
 }
 
-constexpr int kBwdPB = 2; // 16-position blocks per wave
+constexpr int kBwdPB = 4; // 16-position blocks per wave
 
 // Row tiles per wave for the matrix kernel (0: it does not apply).  Needs
 // groups of 16k input and 4k output channels, one tap's A rows within the
