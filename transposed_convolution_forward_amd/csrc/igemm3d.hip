@@ -161,12 +161,15 @@ typedef float fl2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ fl2 buf_load2(rsrc_t r, unsigned voff, unsigned soff) {
     return __builtin_bit_cast(fl2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
+// Output stores are non-temporal (cache policy nt): y is written once and
+// not read back here (fused layer 0.673 -> 0.666 ms).
+constexpr int kStoreNT = 2;
 __device__ __forceinline__ void buf_store1(float v, rsrc_t r, unsigned voff, unsigned soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, voff, soff, kStoreNT);
 }
 typedef int i2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void buf_store2(float a, float b, rsrc_t r, unsigned voff, unsigned soff) {
-    __builtin_amdgcn_raw_buffer_store_b64(i2{__float_as_int(a), __float_as_int(b)}, r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(i2{__float_as_int(a), __float_as_int(b)}, r, voff, soff, kStoreNT);
 }
 
 template <int CIG, int COG, int KW, int SW, int DW, int TDM, int THM, int NWBM, int PWM, int PER,
