@@ -67,6 +67,9 @@ class Oracle:
         lib.oracle_convt_backward_data.argtypes = ([ctypes.c_int] + [ctypes.c_int64] * 4 + [_i64p] * 6 +
                                                    [_f32p] * 2 + [_f64p, ctypes.c_int])
         lib.oracle_convt_backward_data.restype = ctypes.c_int
+        lib.oracle_convt_backward_weight.argtypes = ([ctypes.c_int] + [ctypes.c_int64] * 4 + [_i64p] * 6 +
+                                                     [_f32p] * 2 + [_f64p, _f64p, ctypes.c_int])
+        lib.oracle_convt_backward_weight.restype = ctypes.c_int
         self.lib = lib
 
     # -- shapes -----------------------------------------------------------
@@ -126,6 +129,19 @@ class Oracle:
         if rc:
             raise ValueError("bad arguments")
         return dx
+
+    def backward_weight(self, *, ndim, N, C_in, C_out, groups, in_size, K, stride, pad, out_pad,
+                        dilation, x, dy, nthreads: int = 0):
+        """(dw, db) as float64: dw (C_in, C_out/groups, *K), db (C_out,)."""
+        dw = np.empty((C_in, C_out // groups) + tuple(int(v) for v in K), dtype=np.float64)
+        db = np.empty((C_out,), dtype=np.float64)
+        rc = self.lib.oracle_convt_backward_weight(
+            ndim, N, C_in, C_out, groups, _arr(in_size), _arr(K), _arr(stride), _arr(pad),
+            _arr(out_pad), _arr(dilation), _f32(x), _f32(dy), dw.ctypes.data_as(_f64p),
+            db.ctypes.data_as(_f64p), int(nthreads))
+        if rc:
+            raise ValueError("bad arguments")
+        return dw, db
 
     def times_hardswish(self, t: np.ndarray) -> np.ndarray:
         t = np.ascontiguousarray(t, dtype=np.float64)

@@ -393,3 +393,102 @@ int oracle_convt_backward_data(int ndim, int64_t N, int64_t C_in, int64_t C_out,
     pthread_mutex_destroy(&J.lock);
     return 0;
 }
+
+/* ---------------------------------------------------------------------------
+ * Weight and bias gradients.  The forward is linear in w: y depends on
+ * w[ci, co_l, k] through the terms x[n, ci, i] * w[ci, co_l, k] landing on
+ * y[n, g*Cog + co_l, o], o = i*s - p + k*d.  So for an output gradient dy
+ *   dw[ci, co_l, k] = sum over n and the inputs i whose o lies in [0, L_out)
+ *                     of x[n, ci, i] * dy[n, g*Cog + co_l, o]
+ *   db[co]          = sum over n and every output position of dy[n, co, o]
+ * (the bias is added once to every output element).  Same sources as the
+ * forward; one thread per input channel, the sums in fp64.
+ */
+typedef struct {
+    const problem *P;
+    const float *x, *dy;
+    double *dw;
+    int64_t next, total;
+    pthread_mutex_t lock;
+} wgrad_job;
+
+static void wgrad_channel(const wgrad_job *J, int64_t ci)
+{
+    const problem *P = J->P;
+    const int64_t Cig = P->C_in / P->G, Cog = P->C_out / P->G, g = ci / Cig;
+    const int64_t ID = P->L_in[0], IH = P->L_in[1], IW = P->L_in[2];
+    const int64_t OD = P->L_out[0], OH = P->L_out[1], OW = P->L_out[2];
+    const int64_t KD = P->K[0], KH = P->K[1], KW = P->K[2];
+    const int64_t in_sp = ID * IH * IW, out_sp = OD * OH * OW;
+    double *dwc = J->dw + ci * Cog * KD * KH * KW;   /* dw[ci][co_l][kd][kh][kw] */
+    for (int64_t co_l = 0; co_l < Cog; ++co_l)
+    for (int64_t kd = 0; kd < KD; ++kd)
+    for (int64_t kh = 0; kh < KH; ++kh)
+    for (int64_t kw = 0; kw < KW; ++kw) {
+        double sum = 0.0;
+        for (int64_t n = 0; n < P->N; ++n) {
+            const float *xc = J->x + (n * P->C_in + ci) * in_sp;
+            const float *dyc = J->dy + (n * P->C_out + (g * Cog + co_l)) * out_sp;
+            for (int64_t id = 0; id < ID; ++id) {
+                const int64_t vd = kd * P->d[0] + id * P->s[0] - P->p[0];
+                if (vd < 0 || vd >= OD) continue;
+                for (int64_t ih = 0; ih < IH; ++ih) {
+                    const int64_t vh = kh * P->d[1] + ih * P->s[1] - P->p[1];
+                    if (vh < 0 || vh >= OH) continue;
+                    for (int64_t iw = 0; iw < IW; ++iw) {
+                        const int64_t vw = kw * P->d[2] + iw * P->s[2] - P->p[2];
+                        if (vw < 0 || vw >= OW) continue;
+                        sum += (double)xc[(id * IH + ih) * IW + iw] * (double)dyc[(vd * OH + vh) * OW + vw];
+                    }
+                }
+            }
+        }
+        dwc[((co_l * KD + kd) * KH + kh) * KW + kw] = sum;
+    }
+}
+
+static void *wgrad_worker(void *arg)
+{
+    wgrad_job *J = (wgrad_job *)arg;
+    for (;;) {
+        pthread_mutex_lock(&J->lock);
+        int64_t t = J->next++;
+        pthread_mutex_unlock(&J->lock);
+        if (t >= J->total) break;
+        wgrad_channel(J, t);
+    }
+    return NULL;
+}
+
+/* dw (C_in*(C_out/G)*prod(K) doubles) and, if db != NULL, db (C_out doubles)
+ * from x and dy.  Returns 0, or 1 on bad arguments. */
+int oracle_convt_backward_weight(int ndim, int64_t N, int64_t C_in, int64_t C_out, int64_t G,
+                                 const int64_t *in_size, const int64_t *K, const int64_t *s,
+                                 const int64_t *p, const int64_t *op, const int64_t *d,
+                                 const float *x, const float *dy, double *dw, double *db, int nthreads)
+{
+    problem P;
+    if (set_problem(&P, ndim, N, C_in, C_out, G, in_size, K, s, p, op, d)) return 1;
+    wgrad_job J;
+    J.P = &P; J.x = x; J.dy = dy; J.dw = dw;
+    J.next = 0; J.total = C_in;
+    pthread_mutex_init(&J.lock, NULL);
+    int nt = resolve_threads(nthreads);
+    if (nt > J.total) nt = (int)J.total;
+    pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nt);
+    if (!th) return 1;
+    for (int t = 0; t < nt; ++t) pthread_create(&th[t], NULL, wgrad_worker, &J);
+    for (int t = 0; t < nt; ++t) pthread_join(th[t], NULL);
+    free(th);
+    pthread_mutex_destroy(&J.lock);
+    if (db) {
+        const int64_t out_sp = P.L_out[0] * P.L_out[1] * P.L_out[2];
+        for (int64_t co = 0; co < C_out; ++co) {
+            double sum = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                for (int64_t e = 0; e < out_sp; ++e) sum += (double)dy[(n * C_out + co) * out_sp + e];
+            db[co] = sum;
+        }
+    }
+    return 0;
+}

@@ -301,7 +301,52 @@ def pin_backward_adjoint(orc):
         assert abs(lhs - rhs) <= 1e-9 * (1 + abs(lhs)), (case, lhs, rhs)
 
 
+def _wgrad(orc, x, dy, K, *, groups=1, stride, pad, out_pad, dilation):
+    nd = x.ndim - 2
+    return orc.backward_weight(ndim=nd, N=x.shape[0], C_in=x.shape[1], C_out=dy.shape[1], groups=groups,
+                               in_size=x.shape[2:], K=K, stride=stride, pad=pad, out_pad=out_pad,
+                               dilation=dilation, x=x, dy=dy)
+
+
+def pin_wgrad_worked_examples(orc):
+    """W1: in the pages' worked examples E1-E4 every output element is a list of
+    w_k * x_i terms, so the gradient of <y, dy> in w_k collects x_i * dy_o over
+    the terms that hold w_k."""
+    rng = np.random.default_rng(17)
+    for e in _load("worked_examples.json")["examples"]:
+        vals = {name: np.float32(rng.standard_normal()) for name in e["x"]}
+        x = np.array([[[vals[n] for n in e["x"]]]], dtype=np.float32)
+        dy = rng.standard_normal(size=(1, 1) + tuple(e["out_size"])).astype(np.float32)
+        dw, db = _wgrad(orc, x, dy, e["K"], stride=e["stride"], pad=e["pad"], out_pad=e["out_pad"],
+                        dilation=e["dilation"])
+        want = np.zeros(len(e["w"]))
+        for o, terms in enumerate(e["y"]):
+            for wname, xname in terms:
+                want[e["w"].index(wname)] += float(vals[xname]) * float(dy[0, 0, o])
+        np.testing.assert_allclose(dw[0, 0], want, rtol=1e-12, atol=1e-12, err_msg=e["id"])
+        np.testing.assert_allclose(db, [float(dy.astype(np.float64).sum())], rtol=1e-12, err_msg=e["id"])
+
+
+def pin_wgrad_adjoint(orc):
+    """W2: the forward is linear in w, so <convT(x, u), v> = <u, dw(x, v)> for
+    any weight-shaped u; and adding a bias b adds <b, db(v)> to <y, v>."""
+    for ci, case in enumerate(tiny_cases()):
+        nd, N, Cin, Cout, G, ins, K, s, p, op, d = case
+        x, u, b = _case_arrays(case, 1500 + ci)
+        y = _forward(orc, x, u, groups=G, stride=s, pad=p, out_pad=op, dilation=d)
+        v = _rand(np.random.default_rng(1600 + ci), y.shape)
+        dw, db = _wgrad(orc, x, v, K, groups=G, stride=s, pad=p, out_pad=op, dilation=d)
+        lhs = float(np.sum(y * v.astype(np.float64)))
+        rhs = float(np.sum(u.astype(np.float64) * dw))
+        assert abs(lhs - rhs) <= 1e-9 * (1 + abs(lhs)), (case, lhs, rhs)
+        yb = _forward(orc, x, u, b, groups=G, stride=s, pad=p, out_pad=op, dilation=d)
+        lhs_b = float(np.sum((yb - y) * v.astype(np.float64)))
+        rhs_b = float(np.sum(b.astype(np.float64) * db))
+        assert abs(lhs_b - rhs_b) <= 1e-9 * (1 + abs(lhs_b)), (case, lhs_b, rhs_b)
+
+
 ALL_PINS = [pin_closed_form_pages, pin_worked_examples, pin_numpy_convolve, pin_odd_only,
             pin_tap_counts, pin_adjoint, pin_dilate_flip_correlate, pin_group_decomposition,
             pin_epilogue_values, pin_fused_forward, pin_points_match_forward,
-            pin_backward_worked_examples, pin_backward_gather, pin_backward_adjoint]
+            pin_backward_worked_examples, pin_backward_gather, pin_backward_adjoint,
+            pin_wgrad_worked_examples, pin_wgrad_adjoint]

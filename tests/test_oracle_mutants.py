@@ -45,6 +45,12 @@ MUTATIONS = {
                                  "J->dy + (n * P->C_out + co_l) * out_sp"),
     "bwd_stride_dilation_swapped": ("ih * P->s[1] + kh * P->d[1] - P->p[1]",
                                     "ih * P->d[1] + kh * P->s[1] - P->p[1]"),
+    # weight and bias gradients
+    "wgrad_pad_sign_w": ("kw * P->d[2] + iw * P->s[2] - P->p[2]", "kw * P->d[2] + iw * P->s[2] + P->p[2]"),
+    "wgrad_group_output_channel": ("J->dy + (n * P->C_out + (g * Cog + co_l)) * out_sp;",
+                                   "J->dy + (n * P->C_out + (co_l)) * out_sp;"),
+    "wgrad_batch_dropped": ("for (int64_t n = 0; n < P->N; ++n) {", "for (int64_t n = 0; n < 1; ++n) {"),
+    "bgrad_first_sample_only": ("for (int64_t n = 0; n < N; ++n)\n", "for (int64_t n = 0; n < 1; ++n)\n"),
 }
 
 
