@@ -126,6 +126,28 @@ CONVT_API convt_status convt_forward_add_hswish(const convt_plan *plan, const fl
 CONVT_API convt_status convt_backward_data(const convt_plan *plan, const float *dy, const float *w,
                                            float *dx, void *stream);
 
+/*
+ * Weight and bias gradients for an output gradient dy.  The forward is linear
+ * in w and b (the scatter definition above), so
+ *   dw[ci, co_l, k] = sum over n and the input positions i whose
+ *                     o = i*s - p + k*d lies in [0, L_out) on every axis of
+ *                     x[n, ci, i] * dy[n, g*(C_out/G) + co_l, o]
+ *   db[co]          = sum over n and every output position of dy[n, co, o]
+ * Sources as the forward ("Kimi-K2.6 l1_p79" transcript, the scatter
+ * definition; "Kimi-K2.6 l1_p72" transcript, the per-group loop with bias).
+ * x and dy as in the forward and the input gradient; dw has w's layout
+ * (C_in, C_out/groups, K...), db is (C_out) or NULL (not computed).  dw and db
+ * are overwritten (the call clears them, then adds partial sums over ranges
+ * of positions with fp32 atomics, so the low bits of the result vary from run
+ * to run).  All device memory, caller-owned; dw and db must not overlap x or
+ * dy.  Asynchronous on stream; no device allocation.  Returns
+ * CONVT_ERR_INVALID_ARG for NULL plan, x, dy or dw; CONVT_ERR_UNSUPPORTED if a
+ * group's slice of x or dy for one sample is 2 GiB or more; CONVT_ERR_HIP if
+ * a launch fails.
+ */
+CONVT_API convt_status convt_backward_weight(const convt_plan *plan, const float *x, const float *dy,
+                                             float *dw, float *db, void *stream);
+
 /* Release a plan.  NULL is a no-op. */
 CONVT_API void convt_plan_destroy(convt_plan *plan);
 

@@ -82,6 +82,7 @@ def test_null_arguments():
     assert L.convt_forward(None, None, None, None, None, None) == T.CONVT_ERR_INVALID_ARG
     assert L.convt_forward_add_hswish(None, None, None, None, None, None, None) == T.CONVT_ERR_INVALID_ARG
     assert L.convt_backward_data(None, None, None, None, None) == T.CONVT_ERR_INVALID_ARG
+    assert L.convt_backward_weight(None, None, None, None, None, None) == T.CONVT_ERR_INVALID_ARG
     assert L.convt_plan_set_path(None, 0) == T.CONVT_ERR_INVALID_ARG
     assert L.convt_plan_describe(None, None, 0) == -1
 

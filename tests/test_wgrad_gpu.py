@@ -1,0 +1,87 @@
+"""Weight and bias gradients (convt_backward_weight) through the C ABI against
+the oracle (oracle_convt_backward_weight), element by element, on seeded
+inputs: reduced shapes of every workload, the seeded random and degenerate
+shapes of the forward tests, and full spatial sizes at a reduced batch.
+
+Tolerance, derived from the arithmetic: each dw element is a sum of products
+accumulated in fp32, first along a chain of at most 256 four-product MFMA
+steps per range of 1024 positions, then across the N x ceil(positions/1024)
+ranges by atomic adds.  With u = 2^-24 and S = the sum of |x * dy| over the
+same terms (the oracle's gradient of |x| and |dy|), the rounding error is
+within (chain length) * u * S; the test allows
+  |got - ref| <= 1e-4 + (256 + 4 + ranges + 8) * 2^-24 * S.
+db sums N * L_out values: per (co, n) a thread adds L_out/256 of them, a wave
+tree of 8 levels and N atomic adds, so chain = L_out/256 + 8 + N with
+S = sum |dy|."""
+import numpy as np
+import pytest
+
+import oracle
+import transposed_convolution_forward_amd as T
+from transposed_convolution_forward_amd import synthetic as S
+
+from gpu_util import log, reduced
+from test_parity_gpu import DEGENERATE, REDUCED, _random_cases
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+def _kw(wl):
+    return dict(ndim=wl.ndim, N=wl.N, C_in=wl.C_in, C_out=wl.C_out, groups=wl.groups, in_size=wl.in_size,
+                K=wl.K, stride=wl.stride, pad=wl.pad, out_pad=wl.out_pad, dilation=wl.dilation)
+
+
+def _check(wl, seed=0):
+    import torch
+    orc = oracle.get()
+    out = orc.output_size(wl.ndim, wl.in_size, wl.K, wl.stride, wl.pad, wl.out_pad, wl.dilation)
+    x = S.make_inputs(wl, seed, (wl.N, wl.C_out) + out)["x"]
+    dy = S.make_grad_output(wl, seed, (wl.N, wl.C_out) + out)
+    ref_w, ref_b = orc.backward_weight(x=x, dy=dy, **_kw(wl))
+    abs_w, abs_b = orc.backward_weight(x=np.abs(x), dy=np.abs(dy), **_kw(wl))
+    plan = T.plan_for(wl)
+    log(f"  gpu backward_weight: {wl.name} N={wl.N} in={wl.in_size}")
+    dx_, ddy = torch.from_numpy(x).cuda(), torch.from_numpy(dy).cuda()
+    dw = torch.full(plan.w_shape(), float("nan"), dtype=torch.float32, device="cuda")
+    db = torch.full((wl.C_out,), float("nan"), dtype=torch.float32, device="cuda")
+    T.convt_backward_weight(plan, dx_, ddy, dw=dw, db=db)
+    torch.cuda.synchronize()
+    in_sp = int(np.prod(wl.in_size))
+    out_sp = int(np.prod(out))
+    chain_w = 256 + 4 + wl.N * -(-in_sp // 1024) + 8
+    chain_b = -(-out_sp // 256) + 8 + wl.N
+    for what, got, ref, s_abs, chain in (("dw", dw, ref_w, abs_w, chain_w), ("db", db, ref_b, abs_b, chain_b)):
+        g = got.cpu().numpy().astype(np.float64)
+        assert g.shape == ref.shape and np.all(np.isfinite(g)), (what, g.shape, ref.shape)
+        err = np.abs(g - ref)
+        bound = 1e-4 + chain * U * s_abs
+        bad = err > bound
+        assert not bad.any(), (f"{wl.name} {what}: {int(bad.sum())} of {bad.size} outside; worst "
+                               f"{float((err - bound).max())}")
+        log(f"  {what} max abs err {err.max():.3e} (bound min {bound.min():.3e})")
+    # the inputs are left as they were
+    assert np.array_equal(dx_.cpu().numpy(), x) and np.array_equal(ddy.cpu().numpy(), dy)
+    # without db the call leaves any bias tensor alone and computes the same dw
+    dw2, none = T.convt_backward_weight(plan, dx_, ddy, with_bias=False)
+    torch.cuda.synchronize()
+    assert none is None
+    assert np.all(np.abs(dw2.cpu().numpy() - ref_w) <= 1e-4 + chain_w * U * abs_w)
+
+
+@pytest.mark.parametrize("wl", REDUCED, ids=lambda w: f"{w.name}-N{w.N}-in{'x'.join(map(str, w.in_size))}")
+def test_wgrad_reduced(wl):
+    _check(wl)
+
+
+@pytest.mark.parametrize("wl", _random_cases(24) + DEGENERATE, ids=lambda w: w.name)
+def test_wgrad_random_and_degenerate(wl):
+    _check(wl)
+
+
+@pytest.mark.parametrize("wl", [reduced(S.LONG_1D, N=2), reduced(S.GROUPED_3D, N=1), reduced(S.FUSED_3D, N=2),
+                                reduced(S.HEAVY_3D, N=1, in_size=(8, 16, 16))],
+                         ids=lambda w: f"{w.name}-N{w.N}")
+def test_wgrad_full_spatial(wl):
+    _check(wl)

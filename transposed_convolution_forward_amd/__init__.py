@@ -20,7 +20,8 @@ PATH_NAMES = {v: k for k, v in PATHS.items()}
 
 # Every symbol include/convt.h declares.
 EXPORTS = ("convt_plan_create", "convt_plan_output_size", "convt_forward",
-           "convt_forward_add_hswish", "convt_backward_data", "convt_plan_destroy", "convt_status_string",
+           "convt_forward_add_hswish", "convt_backward_data", "convt_backward_weight",
+           "convt_plan_destroy", "convt_status_string",
            "convt_plan_set_path", "convt_plan_get_path", "convt_plan_describe")
 
 _lib_handle = None
@@ -53,6 +54,8 @@ def lib() -> ctypes.CDLL:
     L.convt_forward_add_hswish.restype = ctypes.c_int
     L.convt_backward_data.argtypes = [vp, vp, vp, vp, vp]
     L.convt_backward_data.restype = ctypes.c_int
+    L.convt_backward_weight.argtypes = [vp, vp, vp, vp, vp, vp]
+    L.convt_backward_weight.restype = ctypes.c_int
     L.convt_plan_destroy.argtypes = [vp]
     L.convt_plan_destroy.restype = None
     L.convt_status_string.argtypes = [ctypes.c_int]
@@ -183,6 +186,22 @@ def convt_backward_data(plan: Plan, dy, w, dx=None, stream=None):
     if st != CONVT_OK:
         raise ConvtError(st, "convt_backward_data")
     return dx
+
+
+def convt_backward_weight(plan: Plan, x, dy, dw=None, db=None, with_bias: bool = True, stream=None):
+    """(dw, db): weight and bias gradients for the output gradient dy (db is
+    None when with_bias is False and no db tensor is given)."""
+    import torch
+    if dw is None:
+        dw = torch.empty(plan.w_shape(), dtype=torch.float32, device=x.device)
+    if db is None and with_bias:
+        db = torch.empty((plan.C_out,), dtype=torch.float32, device=x.device)
+    args = (_dev_ptr(x, plan.x_shape(), "x"), _dev_ptr(dy, plan.y_shape(), "dy"),
+            _dev_ptr(dw, plan.w_shape(), "dw"), None if db is None else _dev_ptr(db, (plan.C_out,), "db"))
+    st = lib().convt_backward_weight(plan.handle, *args, _stream_ptr(stream))
+    if st != CONVT_OK:
+        raise ConvtError(st, "convt_backward_weight")
+    return dw, db
 
 
 def convt_plan_destroy(plan: Plan) -> None:

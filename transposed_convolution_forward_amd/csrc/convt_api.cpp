@@ -9,6 +9,7 @@
 #include <string>
 
 #include "backward.h"
+#include "wgrad.h"
 #include "convt_internal.h"
 
 using convt::AxisPlan;
@@ -194,6 +195,13 @@ convt_status convt_backward_data(const convt_plan *plan, const float *dy, const 
     if (!plan || !dy || !w || !dx) return CONVT_ERR_INVALID_ARG;
     if (!convt::backward_data_supports(*plan)) return CONVT_ERR_UNSUPPORTED;
     return convt::launch_backward_data(*plan, dy, w, dx, stream) == 0 ? CONVT_OK : CONVT_ERR_HIP;
+}
+
+convt_status convt_backward_weight(const convt_plan *plan, const float *x, const float *dy, float *dw,
+                                   float *db, void *stream) {
+    if (!plan || !x || !dy || !dw) return CONVT_ERR_INVALID_ARG;
+    if (!convt::backward_weight_supports(*plan)) return CONVT_ERR_UNSUPPORTED;
+    return convt::launch_backward_weight(*plan, x, dy, dw, db, stream) == 0 ? CONVT_OK : CONVT_ERR_HIP;
 }
 
 void convt_plan_destroy(convt_plan *plan) { delete plan; }

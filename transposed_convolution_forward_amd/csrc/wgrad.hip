@@ -1,0 +1,247 @@
+// Weight and bias gradients of the transposed convolution.  The forward is
+// linear in w: x[n, ci, i] * w[ci, co_l, k] lands on y[n, g*Cog + co_l, o]
+// with o = i*s - p + k*d per axis, so for an output gradient dy
+//   dw[ci, co_l, k] = sum over n and the inputs i whose o lies in [0, L_out)
+//                     of x[n, ci, i] * dy[n, g*Cog + co_l, o]
+//   db[co]          = sum over n and every output position of dy[n, co, o].
+// Same sources as the forward ("Kimi-K2.6 l1_p79" transcript, the scatter
+// definition; "Kimi-K2.6 l1_p72" transcript, the per-group loop with bias).
+//
+// Per tap k the weight gradient is a GEMM over positions: dW_k = X * DY_k^T
+// with X (C_in/G x positions) and DY_k[p][co] = dy[co][o(p, k)].  It runs on
+// v_mfma_f32_16x16x4_f32 with K = 4 input positions: A (lane i + 16c) =
+// x[ci0 + i][p_c], B (lane j + 16c) = dy[co0 + j][o(p_c, k)], D (lane
+// j + 16(i/4), register i%4) = the partial dW_k[ci0 + i][co0 + j].  A wave
+// owns CTW input-channel tiles x OTW output-channel tiles x up to TK taps over
+// one range of positions of one batch sample; each lane walks its own
+// position four at a time, so the tap offsets need no division.  Tiles past
+// the group's channels load zeros and are not stored, so any channel counts
+// run.  The partial sums of all ranges are added into dw with fp32 atomics
+// (dw is cleared first, in the same call): the result is the sum in some order,
+// so it varies in the last bits from run to run.
+#include <hip/hip_runtime.h>
+
+#include "wgrad.h"
+
+namespace convt {
+namespace {
+
+typedef float wg_v4f __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t wg_rsrc_t;
+constexpr int kWgRsrcWord3 = 0x00020000; // raw (untyped) buffer access
+constexpr unsigned kWgOutOfRange = 0x80000000u;
+constexpr int kWgBlock = 256;  // four waves, each its own unit
+constexpr int kWgRange = 1024; // input positions per wave (256 steps of 4)
+
+struct WgradParams {
+    AxisPlan ax[kAxes];
+    int C_in, C_out, Cig, Cog, k_vol;
+    int in_sp, out_sp;
+    int CT, OT;        // 16-channel tiles of the group (input, output)
+    int kchunks;       // chunks of TK taps
+    int nranges;       // position ranges per sample
+    int64_t units;     // waves of work
+};
+
+template <int CTW, int OTW, int TK>
+__global__ __launch_bounds__(kWgBlock) void k_backward_weight(const WgradParams P, const float *__restrict__ x,
+                                                              const float *__restrict__ dy, float *dw) {
+    const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * (kWgBlock / 64) + (threadIdx.x >> 6);
+    if (unit >= P.units) return; // no barrier in this kernel: a wave may leave early
+    int64_t t = unit;
+    const int range = (int)(t % P.nranges);
+    t /= P.nranges;
+    const int kc = (int)(t % P.kchunks);
+    t /= P.kchunks;
+    const int otw = (int)(t % (P.OT / OTW));
+    t /= P.OT / OTW;
+    const int ctw = (int)(t % (P.CT / CTW));
+    t /= P.CT / CTW;
+    const int g = (int)(t % (P.C_in / P.Cig));
+    const int n = (int)(t / (P.C_in / P.Cig));
+    const int ci0 = ctw * CTW * 16, co0 = otw * OTW * 16;
+    const int k0 = kc * TK, tk = min(TK, P.k_vol - k0);
+
+    const int i16 = lane & 15, c4 = lane >> 4;
+    // this lane's A rows (input channel ci0 + 16m + i16) and B columns
+    // (output channel co0 + 16o + i16); c4 is its position within the step
+    const wg_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(x + ((int64_t)n * P.C_in + (int64_t)g * P.Cig) * P.in_sp), (short)0,
+        (int)(4 * P.Cig * P.in_sp), kWgRsrcWord3);
+    const wg_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(dy + ((int64_t)n * P.C_out + (int64_t)g * P.Cog) * P.out_sp), (short)0,
+        (int)(4 * P.Cog * P.out_sp), kWgRsrcWord3);
+    bool a_ok[CTW], b_ok[OTW];
+    unsigned a_ch[CTW], b_ch[OTW];
+#pragma unroll
+    for (int m = 0; m < CTW; ++m) {
+        a_ok[m] = ci0 + 16 * m + i16 < P.Cig;
+        a_ch[m] = (unsigned)(ci0 + 16 * m + i16) * (unsigned)P.in_sp;
+    }
+#pragma unroll
+    for (int o = 0; o < OTW; ++o) {
+        b_ok[o] = co0 + 16 * o + i16 < P.Cog;
+        b_ch[o] = (unsigned)(co0 + 16 * o + i16) * (unsigned)P.out_sp;
+    }
+    // the taps of this chunk: output offset and per-axis tap shifts
+    int tkd[TK], tkh[TK], tkw[TK];
+#pragma unroll
+    for (int u = 0; u < TK; ++u) {
+        const int k = k0 + min(u, tk - 1);
+        const int kw = k % AW.K, kdh = k / AW.K;
+        tkw[u] = kw * AW.d;
+        tkh[u] = (kdh % AH.K) * AH.d;
+        tkd[u] = (kdh / AH.K) * AD.d;
+    }
+
+    wg_v4f acc[TK][CTW][OTW];
+#pragma unroll
+    for (int u = 0; u < TK; ++u)
+#pragma unroll
+        for (int m = 0; m < CTW; ++m)
+#pragma unroll
+            for (int o = 0; o < OTW; ++o) acc[u][m][o] = wg_v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // this lane's position: p = range*kWgRange + 4*step + c4
+    const int p_begin = range * kWgRange;
+    const int p_end = min(p_begin + kWgRange, P.in_sp);
+    int p = p_begin + c4;
+    int iw = p % AW.L_in, ih = (p / AW.L_in) % AH.L_in, id = p / (AW.L_in * AH.L_in);
+    for (int step = p_begin; step < p_end; step += 4) {
+        const bool live = p < p_end;
+        // A: x[ci][p]
+        float a[CTW];
+#pragma unroll
+        for (int m = 0; m < CTW; ++m) {
+            const unsigned vo = live && a_ok[m] ? 4u * (a_ch[m] + (unsigned)p) : kWgOutOfRange;
+            a[m] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, vo, 0, 0));
+        }
+        const int bd = id * AD.s - AD.p, bh = ih * AH.s - AH.p, bw = iw * AW.s - AW.p;
+#pragma unroll
+        for (int u = 0; u < TK; ++u) {
+            if (u >= tk) break;
+            const int od = bd + tkd[u], oh = bh + tkh[u], ow = bw + tkw[u];
+            const bool ok = live && od >= 0 && od < AD.L_out && oh >= 0 && oh < AH.L_out && ow >= 0 &&
+                            ow < AW.L_out;
+            const unsigned o_sp = (unsigned)((od * AH.L_out + oh) * AW.L_out + ow);
+            float b[OTW];
+#pragma unroll
+            for (int o = 0; o < OTW; ++o) {
+                const unsigned vo = ok && b_ok[o] ? 4u * (b_ch[o] + o_sp) : kWgOutOfRange;
+                b[o] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdy, vo, 0, 0));
+            }
+#pragma unroll
+            for (int m = 0; m < CTW; ++m)
+#pragma unroll
+                for (int o = 0; o < OTW; ++o)
+                    acc[u][m][o] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], b[o], acc[u][m][o], 0, 0, 0);
+        }
+        // next position, four along
+        p += 4;
+        iw += 4;
+        while (iw >= AW.L_in) {
+            iw -= AW.L_in;
+            if (++ih == AH.L_in) {
+                ih = 0;
+                ++id;
+            }
+        }
+    }
+
+    // lane j + 16*c4, register v: dW_k[ci0 + 16m + 4*c4 + v][co0 + 16o + j]
+#pragma unroll
+    for (int u = 0; u < TK; ++u) {
+        if (u >= tk) break;
+#pragma unroll
+        for (int m = 0; m < CTW; ++m)
+#pragma unroll
+            for (int o = 0; o < OTW; ++o) {
+                const int co = co0 + 16 * o + i16;
+                if (co >= P.Cog) continue;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int ci = ci0 + 16 * m + 4 * c4 + v;
+                    if (ci >= P.Cig) continue;
+                    atomicAdd(dw + ((int64_t)(g * P.Cig + ci) * P.Cog + co) * P.k_vol + k0 + u, acc[u][m][o][v]);
+                }
+            }
+    }
+}
+
+// db[co] += the sum of dy[n, co, :] for one (co, n) per workgroup.
+__global__ __launch_bounds__(kWgBlock) void k_backward_bias(const float *__restrict__ dy, float *db, int C_out,
+                                                            int out_sp) {
+    const int co = blockIdx.x, n = blockIdx.y;
+    const float *row = dy + ((int64_t)n * C_out + co) * out_sp;
+    float s = 0.0f;
+    for (int e = threadIdx.x; e < out_sp; e += kWgBlock) s += row[e];
+    __shared__ float part[kWgBlock / 64];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicAdd(db + co, part[0] + part[1] + part[2] + part[3]);
+}
+
+__global__ void k_fill_zero(float *p, int64_t n) {
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x)
+        p[e] = 0.0f;
+}
+
+constexpr int kWgTaps = 2; // taps per wave
+
+template <int CTW, int OTW>
+int launch_w(const convt_plan &Pl, WgradParams &P, const float *x, const float *dy, float *dw, hipStream_t st) {
+    P.kchunks = (int)((Pl.k_vol + kWgTaps - 1) / kWgTaps);
+    P.units = Pl.N * Pl.G * (int64_t)(P.CT / CTW) * (P.OT / OTW) * P.kchunks * P.nranges;
+    const int64_t blocks = (P.units + kWgBlock / 64 - 1) / (kWgBlock / 64);
+    hipLaunchKernelGGL((k_backward_weight<CTW, OTW, kWgTaps>), dim3((unsigned)blocks), dim3(kWgBlock), 0, st, P, x,
+                       dy, dw);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? 0 : (int)e;
+}
+
+} // namespace
+
+bool backward_weight_supports(const convt_plan &P) {
+    if (4 * P.Cig * P.in_sp > 0x7fffffff || 4 * P.Cog * P.out_sp > 0x7fffffff) return false;
+    const int64_t CT = (P.Cig + 15) / 16, OT = (P.Cog + 15) / 16;
+    const int64_t units = P.N * P.G * CT * OT * ((P.k_vol + kWgTaps - 1) / kWgTaps) *
+                          ((P.in_sp + kWgRange - 1) / kWgRange);
+    return units / (kWgBlock / 64) < 0x7fffffff && P.N <= 65535 && P.C_out <= 0x7fffffff;
+}
+
+int launch_backward_weight(const convt_plan &Pl, const float *x, const float *dy, float *dw, float *db,
+                           void *stream) {
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t nw = Pl.C_in * Pl.Cog * Pl.k_vol;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)((nw + 255) / 256 < 4096 ? (nw + 255) / 256 : 4096)), dim3(256), 0,
+                       st, dw, nw);
+    if (db) hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(256), 0, st, db, Pl.C_out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+
+    WgradParams P;
+    for (int a = 0; a < kAxes; ++a) P.ax[a] = Pl.ax[a];
+    P.C_in = (int)Pl.C_in;
+    P.C_out = (int)Pl.C_out;
+    P.Cig = (int)Pl.Cig;
+    P.Cog = (int)Pl.Cog;
+    P.k_vol = (int)Pl.k_vol;
+    P.in_sp = (int)Pl.in_sp;
+    P.out_sp = (int)Pl.out_sp;
+    P.CT = (int)((Pl.Cig + 15) / 16);
+    P.OT = (int)((Pl.Cog + 15) / 16);
+    P.nranges = (int)((Pl.in_sp + kWgRange - 1) / kWgRange);
+    int rc = (P.CT % 2 == 0 && P.OT % 4 == 0) ? launch_w<2, 4>(Pl, P, x, dy, dw, st)
+                                              : launch_w<1, 1>(Pl, P, x, dy, dw, st);
+    if (rc || !db) return rc;
+    hipLaunchKernelGGL(k_backward_bias, dim3((unsigned)Pl.C_out, (unsigned)Pl.N), dim3(kWgBlock), 0, st, dy, db,
+                       (int)Pl.C_out, (int)Pl.out_sp);
+    e = hipGetLastError();
+    return e == hipSuccess ? 0 : (int)e;
+}
+
+} // namespace convt
