@@ -17,7 +17,9 @@ N=16, 32->64 channels, L=131072, K=3, stride 2, padding 1, dilation 2):
 
 --op backward_data times the input gradient (convt_backward_data: dy and w in,
 dx out) on the same workload instead of the forward; its bytes are dy + w + dx
-and its valid MACs those of the forward.
+and its valid MACs those of the forward.  --op backward_weight times the
+weight and bias gradients (convt_backward_weight: x and dy in, dw and db out;
+bytes x + dy + dw + db, the same valid MACs).
 
 --copy-calibration instead times a plain 1 GiB device copy (used to scale the
 HBM byte counters of a profiler run).
@@ -67,6 +69,13 @@ def algorithmic_bytes_backward(wl, N=None):
     N = wl.N if N is None else N
     return 4 * (N * wl.C_out * int(np.prod(out_size(wl))) + int(np.prod(wl.w_shape())) +
                 N * wl.C_in * int(np.prod(wl.in_size)))
+
+
+def algorithmic_bytes_weight(wl, N=None):
+    """Weight and bias gradients: x + dy + dw + db, each once."""
+    N = wl.N if N is None else N
+    return 4 * (N * wl.C_in * int(np.prod(wl.in_size)) + N * wl.C_out * int(np.prod(out_size(wl))) +
+                int(np.prod(wl.w_shape())) + wl.C_out)
 
 
 def valid_macs(wl, N=None):
@@ -136,6 +145,12 @@ def cpu_baseline(wl, inp, budget_slabs=None, op="forward"):
     if op == "backward_data":
         orc.backward_data(dy=np.ascontiguousarray(inp["dy"][:n_s]), w=inp["w"], **shape)
         nbytes = algorithmic_bytes_backward(wl, n_s)
+    elif op == "backward_weight":
+        shape["nthreads"] = min(cores, wl.C_in)
+        threads = shape["nthreads"]
+        orc.backward_weight(x=np.ascontiguousarray(inp["x"][:n_s]), dy=np.ascontiguousarray(inp["dy"][:n_s]),
+                            **shape)
+        nbytes = algorithmic_bytes_weight(wl, n_s)
     else:
         orc.forward(x=np.ascontiguousarray(inp["x"][:n_s]), w=inp["w"], bias=inp["bias"],
                     add=None if inp["add"] is None else np.ascontiguousarray(inp["add"][:n_s]), **shape)
@@ -144,7 +159,7 @@ def cpu_baseline(wl, inp, budget_slabs=None, op="forward"):
     return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": f"first {n_s} of {wl.N} batch samples (all channels and positions), "
-                      f"{dt:.2f} s wall; fp64 {'adjoint' if op == 'backward_data' else 'scatter'} loop, "
+                      f"{dt:.2f} s wall; fp64 {dict(backward_data='adjoint', backward_weight='weight-gradient').get(op, 'scatter')} loop, "
                       f"{threads} threads",
             "valid_mac_gflops": 2 * valid_macs(wl, n_s) / dt / 1e9}
 
@@ -168,8 +183,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=S.LONG_1D.name, choices=sorted(S.BY_NAME))
     ap.add_argument("--path", default="auto", choices=sorted(T.PATHS))
-    ap.add_argument("--op", default="forward", choices=["forward", "backward_data"],
-                    help="forward (the hot path, default) or the input gradient")
+    ap.add_argument("--op", default="forward", choices=["forward", "backward_data", "backward_weight"],
+                    help="forward (the hot path, default), the input gradient, or the weight and bias gradients")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -188,19 +203,26 @@ def main():
     wl = S.BY_NAME[args.workload]
     print(f"[bench] workload {wl.name}: generating seeded inputs", file=sys.stderr, flush=True)
     bwd = args.op == "backward_data"
+    wgr = args.op == "backward_weight"
     inp = S.make_inputs(wl, 0, (wl.N, wl.C_out) + out_size(wl))
     if bwd:
         inp = {"dy": S.make_grad_output(wl, 0, (wl.N, wl.C_out) + out_size(wl)), "w": inp["w"]}
+    elif wgr:
+        inp = {"dy": S.make_grad_output(wl, 0, (wl.N, wl.C_out) + out_size(wl)), "x": inp["x"]}
     dev = {k: (None if v is None else torch.from_numpy(v).cuda()) for k, v in inp.items()}
     plan = T.plan_for(wl)
     if args.path != "auto":
         T.convt_plan_set_path(plan, args.path)
     path = T.convt_plan_get_path(plan)
-    y = torch.empty(plan.x_shape() if bwd else plan.y_shape(), dtype=torch.float32, device="cuda")
+    y = torch.empty(plan.x_shape() if bwd else plan.w_shape() if wgr else plan.y_shape(), dtype=torch.float32,
+                    device="cuda")
+    db = torch.empty((wl.C_out,), dtype=torch.float32, device="cuda")
 
     def step():
         if bwd:
             T.convt_backward_data(plan, dev["dy"], dev["w"], dx=y)
+        elif wgr:
+            T.convt_backward_weight(plan, dev["x"], dev["dy"], dw=y, db=db)
         elif wl.fused:
             T.convt_forward_add_hswish(plan, dev["x"], dev["w"], dev["bias"], dev["add"], y=y)
         else:
@@ -248,7 +270,8 @@ def main():
     del evict
     cold = np.array([a.elapsed_time(b) for a, b in ev_cold])
 
-    nbytes = algorithmic_bytes_backward(wl) if bwd else algorithmic_bytes(wl)
+    nbytes = (algorithmic_bytes_backward(wl) if bwd else algorithmic_bytes_weight(wl) if wgr
+              else algorithmic_bytes(wl))
     flops = 2 * valid_macs(wl)
     gbs = nbytes / (ms_per_step * 1e-3) / 1e9
     t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
@@ -256,7 +279,7 @@ def main():
     m = re.search(r"kernel=(\S+)", T.convt_plan_describe(plan))
     if bwd:
         m = re.search(r"input gradient: kernel=(\S+)", T.convt_plan_describe(plan))
-    kernel = m.group(1) if m else KERNEL_NAMES[path]
+    kernel = "k_backward_weight" if wgr else (m.group(1) if m else KERNEL_NAMES[path])
     if t_hbm >= t_fp32:
         ach = nbytes / (ms_launch * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -282,6 +305,7 @@ def main():
 
     line = {
         "metric": ("ConvTranspose input-gradient GB/s and valid-MAC TFLOP/s, % of roofline, 1x MI355X" if bwd
+                   else "ConvTranspose weight-gradient GB/s and valid-MAC TFLOP/s, % of roofline, 1x MI355X" if wgr
                    else "ConvTranspose fwd GB/s and valid-MAC TFLOP/s, % of roofline, 1x MI355X"),
         "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
@@ -292,7 +316,7 @@ def main():
                    "out_size": list(out_size(wl)), "K": list(wl.K), "stride": list(wl.stride),
                    "pad": list(wl.pad), "out_pad": list(wl.out_pad),
                    "dilation": list(wl.dilation), "bias": wl.bias, "fused": wl.fused,
-                   "path": "backward_data" if bwd else path, "op": args.op,
+                   "path": args.op if (bwd or wgr) else path, "op": args.op,
                    "parallelism": "single GPU"},
         "valid_mac_tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
         "hbm_frac": round(t_hbm / (ms_per_step * 1e-3), 4),
