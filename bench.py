@@ -98,7 +98,8 @@ def valid_macs(wl, N=None):
 KERNEL_SOURCES = {"k_stream1d": "stream1d.hip", "k_igemm3d": "igemm3d.hip", "k_igemm3d_wide": "igemm3d.hip",
                   "k_generic": "generic.hip", "k_generic_phase": "generic.hip", "k_generic_rows": "generic.hip",
                   "k_generic_pairs": "generic.hip", "k_backward_data": "backward.hip",
-                  "k_backward_data_mfma": "backward.hip", "k_backward_weight": "wgrad.hip"}
+                  "k_backward_data_mfma": "backward.hip", "k_backward_weight": "wgrad.hip",
+                  "k_backward_weight_lds": "wgrad.hip"}
 SHARED_SOURCES = ("convt_internal.h", "epilogue.hpp")
 
 
@@ -279,7 +280,9 @@ def main():
     m = re.search(r"kernel=(\S+)", T.convt_plan_describe(plan))
     if bwd:
         m = re.search(r"input gradient: kernel=(\S+)", T.convt_plan_describe(plan))
-    kernel = "k_backward_weight" if wgr else (m.group(1) if m else KERNEL_NAMES[path])
+    if wgr:
+        m = re.search(r"weight gradient: kernel=(\S+)", T.convt_plan_describe(plan))
+    kernel = m.group(1) if m else KERNEL_NAMES[path]
     if t_hbm >= t_fp32:
         ach = nbytes / (ms_launch * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -167,7 +167,7 @@ CONVT_API convt_path convt_plan_get_path(const convt_plan *plan);
 
 /*
  * Human-readable summary of the plan (shapes, phase tables, chosen path and
- * the kernel that path runs, and the input-gradient kernel) into buf (NUL-terminated, truncated to len).  Returns the
+ * the kernel that path runs, and the gradient kernels) into buf (NUL-terminated, truncated to len).  Returns the
  * length the full text needs, excluding the NUL.  Host-only.
  */
 CONVT_API int64_t convt_plan_describe(const convt_plan *plan, char *buf, int64_t len);

@@ -267,6 +267,11 @@ int64_t convt_plan_describe(const convt_plan *plan, char *buf, int64_t len) {
         s += convt::backward_data_kernel_name(*plan);
         s += "\n";
     }
+    if (convt::backward_weight_supports(*plan)) {
+        s += "  weight gradient: kernel=";
+        s += convt::backward_weight_kernel_name(*plan);
+        s += "\n";
+    }
     if (buf && len > 0) {
         const size_t n = s.size() < (size_t)(len - 1) ? s.size() : (size_t)(len - 1);
         memcpy(buf, s.data(), n);

@@ -170,6 +170,121 @@ __global__ __launch_bounds__(kWgBlock) void k_backward_weight(const WgradParams 
     }
 }
 
+// Channel-rich groups (32k input, 64k output channels): the same GEMM with
+// both operands staged through LDS, so that global loads run along positions
+// (coalesced) instead of gathering 16 channel rows per instruction.  A
+// workgroup owns 32 input x 64 output channels x up to kWlTaps taps over a
+// range of positions of one sample; per tile of 64 positions it stages x as
+// [position][ci] once and, per tap, dy at o(p, k) as [position][co] (rows
+// padded by one float: the transposed writes do not collide on a bank); wave
+// w then runs the 16 K-steps of its output-channel tile for both input-channel
+// tiles.  Partial sums go to dw with atomics as above.
+constexpr int kWlTaps = 4;      // taps per workgroup
+constexpr int kWlTile = 64;     // positions per staged tile
+constexpr int kWlRange = 2048;  // positions per workgroup
+constexpr int kWlApitch = 33;   // floats per staged x position row (32 channels + 1)
+constexpr int kWlBpitch = 65;   // floats per staged dy position row (64 channels + 1)
+
+struct WlParams {
+    AxisPlan ax[kAxes];
+    int C_in, C_out, Cig, Cog, k_vol;
+    int in_sp, out_sp;
+    int cib, cob;      // 32- and 64-channel blocks of the group
+    int kchunks;       // chunks of kWlTaps taps
+    int nranges;       // position ranges per sample
+};
+
+__global__ __launch_bounds__(kWgBlock) void k_backward_weight_lds(const WlParams P, const float *__restrict__ x,
+                                                                  const float *__restrict__ dy, float *dw) {
+    const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int64_t t = blockIdx.x;
+    const int range = (int)(t % P.nranges);
+    t /= P.nranges;
+    const int kc = (int)(t % P.kchunks);
+    t /= P.kchunks;
+    const int cb = (int)(t % P.cob);
+    t /= P.cob;
+    const int ib = (int)(t % P.cib);
+    t /= P.cib;
+    const int g = (int)(t % (P.C_in / P.Cig));
+    const int n = (int)(t / (P.C_in / P.Cig));
+    const int ci0 = 32 * ib, co0 = 64 * cb;
+    const int k0 = kc * kWlTaps, tk = min(kWlTaps, P.k_vol - k0);
+
+    __shared__ float As[kWlTile * kWlApitch];
+    __shared__ float Bs[kWlTile * kWlBpitch];
+
+    const float *xg = x + ((int64_t)n * P.C_in + (int64_t)g * P.Cig + ci0) * P.in_sp;
+    const float *dyg = dy + ((int64_t)n * P.C_out + (int64_t)g * P.Cog + co0) * P.out_sp;
+
+    wg_v4f acc[kWlTaps][2];
+#pragma unroll
+    for (int u = 0; u < kWlTaps; ++u) acc[u][0] = acc[u][1] = wg_v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int i16 = lane & 15, c4 = lane >> 4;
+    const int p_begin = range * kWlRange;
+    const int p_end = min(p_begin + kWlRange, P.in_sp);
+    for (int p0 = p_begin; p0 < p_end; p0 += kWlTile) {
+        // this lane's position of the tile
+        const int p = p0 + lane;
+        const bool live = p < p_end;
+        const int iw = p % AW.L_in, ih = (p / AW.L_in) % AH.L_in, id = p / (AW.L_in * AH.L_in);
+        __syncthreads(); // the previous tile's operands are consumed
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int ci = wave + 4 * r;
+            As[lane * kWlApitch + ci] = live ? xg[(int64_t)ci * P.in_sp + p] : 0.0f;
+        }
+        for (int u = 0; u < tk; ++u) {
+            const int k = k0 + u;
+            const int kw = k % AW.K, kdh = k / AW.K;
+            const int od = id * AD.s - AD.p + (kdh / AH.K) * AD.d;
+            const int oh = ih * AH.s - AH.p + (kdh % AH.K) * AH.d;
+            const int ow = iw * AW.s - AW.p + kw * AW.d;
+            const bool ok = live && od >= 0 && od < AD.L_out && oh >= 0 && oh < AH.L_out && ow >= 0 &&
+                            ow < AW.L_out;
+            const int o = ok ? (od * AH.L_out + oh) * AW.L_out + ow : 0;
+            if (u > 0) __syncthreads(); // the previous tap's dy tile is consumed
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int co = wave + 4 * r;
+                const float v = dyg[(int64_t)co * P.out_sp + o];
+                Bs[lane * kWlBpitch + co] = ok ? v : 0.0f;
+            }
+            __syncthreads();
+            // wave: output-channel tile `wave`, both input-channel tiles
+#pragma unroll 4
+            for (int q = 0; q < kWlTile / 4; ++q) {
+                const int pp = 4 * q + c4;
+                const float b = Bs[pp * kWlBpitch + 16 * wave + i16];
+                const float a0 = As[pp * kWlApitch + i16];
+                const float a1 = As[pp * kWlApitch + 16 + i16];
+#pragma unroll
+                for (int uu = 0; uu < kWlTaps; ++uu) {
+                    if (uu != u) continue;
+                    acc[uu][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b, acc[uu][0], 0, 0, 0);
+                    acc[uu][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b, acc[uu][1], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // lane j + 16*c4, register v: dW_k[ci0 + 16m + 4*c4 + v][co0 + 16*wave + j]
+    const int co = co0 + 16 * wave + i16;
+#pragma unroll
+    for (int u = 0; u < kWlTaps; ++u) {
+        if (u >= tk) break;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int ci = ci0 + 16 * m + 4 * c4 + v;
+                atomicAdd(dw + ((int64_t)(g * P.Cig + ci) * P.Cog + co) * P.k_vol + k0 + u, acc[u][m][v]);
+            }
+    }
+}
+
 // db[co] += the sum of dy[n, co, :] for one (co, n) per workgroup.
 __global__ __launch_bounds__(kWgBlock) void k_backward_bias(const float *__restrict__ dy, float *db, int C_out,
                                                             int out_sp) {
@@ -205,6 +320,10 @@ int launch_w(const convt_plan &Pl, WgradParams &P, const float *x, const float *
 
 } // namespace
 
+const char *backward_weight_kernel_name(const convt_plan &P) {
+    return P.Cig % 32 == 0 && P.Cog % 64 == 0 ? "k_backward_weight_lds" : "k_backward_weight";
+}
+
 bool backward_weight_supports(const convt_plan &P) {
     if (4 * P.Cig * P.in_sp > 0x7fffffff || 4 * P.Cog * P.out_sp > 0x7fffffff) return false;
     const int64_t CT = (P.Cig + 15) / 16, OT = (P.Cog + 15) / 16;
@@ -235,8 +354,24 @@ int launch_backward_weight(const convt_plan &Pl, const float *x, const float *dy
     P.CT = (int)((Pl.Cig + 15) / 16);
     P.OT = (int)((Pl.Cog + 15) / 16);
     P.nranges = (int)((Pl.in_sp + kWgRange - 1) / kWgRange);
-    int rc = (P.CT % 2 == 0 && P.OT % 4 == 0) ? launch_w<2, 4>(Pl, P, x, dy, dw, st)
+    int rc;
+    if (Pl.Cig % 32 == 0 && Pl.Cog % 64 == 0) {
+        WlParams L;
+        for (int a = 0; a < kAxes; ++a) L.ax[a] = Pl.ax[a];
+        L.C_in = P.C_in, L.C_out = P.C_out, L.Cig = P.Cig, L.Cog = P.Cog, L.k_vol = P.k_vol;
+        L.in_sp = P.in_sp, L.out_sp = P.out_sp;
+        L.cib = (int)(Pl.Cig / 32);
+        L.cob = (int)(Pl.Cog / 64);
+        L.kchunks = (int)((Pl.k_vol + kWlTaps - 1) / kWlTaps);
+        L.nranges = (int)((Pl.in_sp + kWlRange - 1) / kWlRange);
+        const int64_t blocks = Pl.N * Pl.G * (int64_t)L.cib * L.cob * L.kchunks * L.nranges;
+        hipLaunchKernelGGL(k_backward_weight_lds, dim3((unsigned)blocks), dim3(kWgBlock), 0, st, L, x, dy, dw);
+        e = hipGetLastError();
+        rc = e == hipSuccess ? 0 : (int)e;
+    } else {
+        rc = (P.CT % 2 == 0 && P.OT % 4 == 0) ? launch_w<2, 4>(Pl, P, x, dy, dw, st)
                                               : launch_w<1, 1>(Pl, P, x, dy, dw, st);
+    }
     if (rc || !db) return rc;
     hipLaunchKernelGGL(k_backward_bias, dim3((unsigned)Pl.C_out, (unsigned)Pl.N), dim3(kWgBlock), 0, st, dy, db,
                        (int)Pl.C_out, (int)Pl.out_sp);
