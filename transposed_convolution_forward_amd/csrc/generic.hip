@@ -275,16 +275,15 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000; // raw (untyped) buffer access
 constexpr unsigned kOutOfRange = 0x80000000u;
 
-// Weight staging shared by the row kernels.  Row r of the staged operand is
-// 64 floats; src(r) names, for this lane, the weight w[g*Cig + ci][co0 + c]
-// [kidx] of the workgroup's group and channel chunk, or none (a zero).
-// Rows r dealt to wave r % 4: each wave issues kStageBatch loads (out of
-// range, so zero, for none) before it writes any of them to LDS, so their
-// latencies overlap.  Row r holds, in lane l, the weight at element offset
-// lane_off + src(r) of w, where src(r) is uniform (the tap's offset plus the
-// row's first input channel times ci_stride) and lane_off is the lane's
-// channel and column; rows past a lane's last channel (lane_ci + part_ci(r) >=
-// Cig) are zero.
+// Weight staging shared by the row kernels.  The staged operand is nrows rows
+// of 64 floats; row r holds, in lane l, the weight at element offset
+// lane_off + src(r).off of w, where src(r).off is uniform (the tap's offset
+// plus the row's first input channel times the channel stride) and lane_off
+// is the lane's own channel and column.  A lane whose channel lies past the
+// group's last (lane_ci + src(r).ci0 >= Cig) gets zero.  Rows are dealt to
+// wave r % 4, and each wave issues kStageBatch loads (out of range, so zero,
+// where there is no weight) before it writes any of them to LDS, so their
+// latencies overlap.
 constexpr int kStageBatch = 8;
 
 struct WRow {
