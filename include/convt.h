@@ -142,8 +142,8 @@ CONVT_API convt_status convt_backward_data(const convt_plan *plan, const float *
  * to run).  All device memory, caller-owned; dw and db must not overlap x or
  * dy.  Asynchronous on stream; no device allocation.  Returns
  * CONVT_ERR_INVALID_ARG for NULL plan, x, dy or dw; CONVT_ERR_UNSUPPORTED if a
- * group's slice of x or dy for one sample is 2 GiB or more; CONVT_ERR_HIP if
- * a launch fails.
+ * group's slice of x or dy for one sample is 2 GiB or more, or N > 65535;
+ * CONVT_ERR_HIP if a launch fails.
  */
 CONVT_API convt_status convt_backward_weight(const convt_plan *plan, const float *x, const float *dy,
                                              float *dw, float *db, void *stream);
