@@ -169,35 +169,61 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma(const BwdParam
             wa[r * 64 + lane] = wl_[((int64_t)(16 * m) * P.Cog + 4 * q) * P.k_vol + t0 + tap];
         }
         __syncthreads();
-        for (int t = 0; t < tc; ++t) {
-            const int k = t0 + t;
+        // Steps (t, q) of the chunk, t-major.  The B operands of the next step
+        // are loaded while this step's MFMAs run (two register sets, the loop
+        // unrolled by two so they swap roles without copies); past the last
+        // step the offsets are out of range (zeros, no traffic) and an odd
+        // count ends with a step that adds nothing.  The loads are
+        // unconditional, so every path issues the same ones and the waits for
+        // a step's operands leave the next step's loads in flight.
+        unsigned vo[PB];
+        auto tap_offsets = [&](int t) {
+            const int k = t0 + min(t, tc - 1);
             const int kw = k % AW.K, kdh = k / AW.K;
             const int kh = kdh % AH.K, kd = kdh / AH.K;
-            unsigned vo[PB];
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb) {
                 const int od = id[pb] * AD.s - AD.p + kd * AD.d;
                 const int oh = ih[pb] * AH.s - AH.p + kh * AH.d;
                 const int ow = iw[pb] * AW.s - AW.p + kw * AW.d;
-                const bool ok = live[pb] && od >= 0 && od < AD.L_out && oh >= 0 && oh < AH.L_out && ow >= 0 &&
-                                ow < AW.L_out;
+                const bool ok = t < tc && live[pb] && od >= 0 && od < AD.L_out && oh >= 0 && oh < AH.L_out &&
+                                ow >= 0 && ow < AW.L_out;
                 vo[pb] = ok ? 4u * (lane_ch + (unsigned)((od * AH.L_out + oh) * AW.L_out + ow)) : kBwdOutOfRange;
             }
-            const float *wt = wa + t * NQ * MT * 64 + lane;
-#pragma unroll 4
-            for (int q = 0; q < NQ; ++q) {
-                float b[PB], a[MT];
+        };
+        auto load = [&](float (&b)[PB], int q) {
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb)
+                b[pb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdy, vo[pb], q * quad_bytes, 0));
+        };
+        auto contract = [&](const float (&b)[PB], int t, int q) {
+            const float *wt = wa + min(t, tc - 1) * NQ * MT * 64 + lane;
+            float a[MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) a[m] = wt[(q * MT + m) * 64];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int pb = 0; pb < PB; ++pb)
-                    b[pb] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdy, vo[pb], q * quad_bytes, 0));
-#pragma unroll
-                for (int m = 0; m < MT; ++m) a[m] = wt[(q * MT + m) * 64];
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-#pragma unroll
-                    for (int pb = 0; pb < PB; ++pb)
-                        acc[m][pb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], b[pb], acc[m][pb], 0, 0, 0);
-            }
+                    acc[m][pb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], b[pb], acc[m][pb], 0, 0, 0);
+        };
+        const int nsteps = tc * NQ;
+        int t = 0, q = 0;
+        float b0[PB], b1[PB];
+        tap_offsets(0);
+        load(b0, 0);
+        for (int st = 0; st < nsteps; st += 2) {
+            int t1 = t, q1 = q + 1;
+            if (q1 == NQ) q1 = 0, ++t1;
+            if (q1 == 0) tap_offsets(t1);
+            load(b1, q1);
+            contract(b0, t, q);
+            t = t1, q = q1;
+            if (++q1 == NQ) q1 = 0, ++t1;
+            if (q1 == 0) tap_offsets(t1);
+            load(b0, q1);
+            contract(b1, t, q);
+            t = t1, q = q1;
         }
     }
 
