@@ -147,6 +147,10 @@ __device__ __forceinline__ RowPos decode_row(const Igemm3dParams &P, int cls, in
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000; // raw (untyped) buffer access
 constexpr unsigned kOutOfRange = 0x80000000u;
+// Cache policy nt (non-temporal) for the output stores, as y is written once
+// and not read back here (fused layer 0.673 -> 0.666 ms), and for the
+// add_input loads below.
+constexpr int kNonTemporal = 2;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const float *base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, bytes, kRsrcWord3);
@@ -154,22 +158,23 @@ __device__ __forceinline__ rsrc_t make_rsrc(const float *base, int bytes) {
 __device__ __forceinline__ f4 buf_load4(rsrc_t r, unsigned voff) {
     return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
+// add_input loads (buf_load1/2) are non-temporal as well: each element is
+// read once, and keeping it out of the caches leaves them to the input rows
+// that other classes read again (fused layer 0.678 -> 0.667 ms warm, cold
+// cache 0.72 -> 0.70 ms).
 __device__ __forceinline__ float buf_load1(rsrc_t r, unsigned voff, unsigned soff) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNonTemporal));
 }
 typedef float fl2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ fl2 buf_load2(rsrc_t r, unsigned voff, unsigned soff) {
-    return __builtin_bit_cast(fl2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    return __builtin_bit_cast(fl2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNonTemporal));
 }
-// Output stores are non-temporal (cache policy nt): y is written once and
-// not read back here (fused layer 0.673 -> 0.666 ms).
-constexpr int kStoreNT = 2;
 __device__ __forceinline__ void buf_store1(float v, rsrc_t r, unsigned voff, unsigned soff) {
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, voff, soff, kStoreNT);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, voff, soff, kNonTemporal);
 }
 typedef int i2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void buf_store2(float a, float b, rsrc_t r, unsigned voff, unsigned soff) {
-    __builtin_amdgcn_raw_buffer_store_b64(i2{__float_as_int(a), __float_as_int(b)}, r, voff, soff, kStoreNT);
+    __builtin_amdgcn_raw_buffer_store_b64(i2{__float_as_int(a), __float_as_int(b)}, r, voff, soff, kNonTemporal);
 }
 
 template <int CIG, int COG, int KW, int SW, int DW, int TDM, int THM, int NWBM, int PWM, int PER,
