@@ -58,3 +58,20 @@ def test_backward_random_and_degenerate(wl):
                          ids=lambda w: f"{w.name}-N{w.N}")
 def test_backward_full_spatial(wl):
     _check(wl)
+
+
+# One-axis shapes whose grids are large enough that a workgroup of the
+# window-staged matrix kernel walks several position tiles: 3 tiles per
+# workgroup with a last workgroup of 2 and a ragged last tile; 4 with two
+# groups and unit stride; the cap of 8.
+ROW_TILES = [
+    S.Workload("bwd_row_tiles3_ragged", 1, 300, 16, 4, 1, (5669,), (3,), (2,), (1,), (1,), (2,), False, False, 41),
+    S.Workload("bwd_row_tiles4_g2", 1, 140, 32, 8, 2, (7683,), (4,), (1,), (2,), (0,), (3,), False, False, 42),
+    S.Workload("bwd_row_tiles8", 1, 700, 16, 4, 1, (5889,), (3,), (2,), (0,), (0,), (1,), False, False, 43),
+]
+
+
+@pytest.mark.parametrize("wl", ROW_TILES, ids=lambda w: w.name)
+def test_backward_row_multitile(wl):
+    assert "input gradient: kernel=k_backward_data_mfma_row" in T.convt_plan_describe(T.plan_for(wl))
+    _check(wl)

@@ -31,6 +31,8 @@ struct BwdParams {
     int in_sp, out_sp;
     int ci_chunks;
     int taps_per_chunk; // taps whose weights are staged at once
+    int win_pitch;      // floats per staged dy window row (the one-axis matrix kernel)
+    int tiles_per_wg;   // position tiles a workgroup of the one-axis matrix kernel walks
     int n0;             // first batch index of this launch
 };
 
@@ -119,6 +121,10 @@ typedef float bwd_v4f __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t bwd_rsrc_t;
 constexpr int kBwdRsrcWord3 = 0x00020000; // raw (untyped) buffer access
 constexpr unsigned kBwdOutOfRange = 0x80000000u;
+constexpr int kRowMaxT = 10; // 64-column steps of the one-axis kernel's dy window (640 columns)
+constexpr int kRowMinWgs = 2048;       // the one-axis kernel's grid, at least (8 per CU)
+constexpr int kRowMaxTilesPerWg = 8;
+constexpr int kRowCh = 4; // output channels per staged window chunk (a multiple of 4, <= 16)
 
 template <int MT, int PB>
 __global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma(const BwdParams P, const float *__restrict__ dy,
@@ -241,6 +247,145 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma(const BwdParam
     }
 }
 
+// Along one axis only (1D plans: the leading axes are unit), the dy values
+// that a tile of 64*PB consecutive input positions needs for all taps form one
+// window [p0*s - p, (p0 + 64*PB - 1)*s - p + (K-1)*d] of each output channel
+// row.  This variant stages that window, kRowCh output channels at a time,
+// into LDS with loads along the row (coalesced) and reads the B operands from it,
+// instead of gathering 4 channel rows per load instruction.  Every tap's A
+// rows are staged once per workgroup, and a workgroup walks tiles_per_wg
+// consecutive tiles; the next (tile, chunk) window is loaded into registers
+// while the current one's MFMAs run.  Window columns outside [0, L_out) are
+// zero.
+template <int MT, int PB>
+__global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma_row(const BwdParams P,
+                                                                      const float *__restrict__ dy,
+                                                                      const float *__restrict__ w,
+                                                                      float *__restrict__ dx) {
+    const AxisPlan &AW = P.ax[2];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j16 = lane & 15, c4 = lane >> 4;
+    const int g = blockIdx.y / P.ci_chunks;
+    const int ci0 = (blockIdx.y % P.ci_chunks) * 16 * MT;
+    const int n = P.n0 + blockIdx.z;
+    const int NQ = P.Cog / 4;
+    const int NC = P.Cog / kRowCh; // window chunks per tile
+    const int K = P.k_vol;      // taps along W
+    const int TP = 64 * PB;     // positions per tile
+    const int Wp = P.win_pitch; // floats per staged row (odd)
+    const int Wn = (TP - 1) * AW.s + (K - 1) * AW.d + 1;
+    const int tile0 = blockIdx.x * P.tiles_per_wg;
+    const int ntiles = min(P.tiles_per_wg, (P.in_sp + TP - 1) / TP - tile0);
+    const int nsteps = ntiles * NC; // (tile, chunk) steps, chunk-minor
+
+    extern __shared__ __attribute__((aligned(16))) float wa[];
+    float *bw = wa + K * NQ * MT * 64; // the window, [kRowCh channels][Wp]
+
+    // every tap's A rows, [tap][q][m][64 lanes]; rows dealt to waves, eight
+    // loads in flight per wave (indexes past the last row repeat it)
+    {
+        const float *wl_ = w + ((int64_t)(g * P.Cig + ci0 + j16) * P.Cog + c4) * P.k_vol;
+        const int nrows = K * NQ * MT;
+        for (int r0 = wave; r0 < nrows; r0 += 32) {
+            float t8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int r = min(r0 + 4 * u, nrows - 1);
+                const int m = r % MT, t = r / MT;
+                const int q = t % NQ, tap = t / NQ;
+                t8[u] = wl_[((int64_t)(16 * m) * P.Cog + 4 * q) * P.k_vol + tap];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (r0 + 4 * u < nrows) wa[(r0 + 4 * u) * 64 + lane] = t8[u];
+        }
+    }
+
+    bwd_v4f acc[MT][PB];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) acc[m][pb] = bwd_v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const bwd_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(dy + ((int64_t)n * P.C_out + (int64_t)g * P.Cog) * P.out_sp), (short)0,
+        (int)(4 * P.Cog * P.out_sp), kBwdRsrcWord3);
+    // this lane's window column for position block pb at tap 0
+    int col[PB];
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) col[pb] = (wave * 16 * PB + pb * 16 + j16) * AW.s;
+    // wave v stages window rows RW*v .. RW*v + RW-1 of a chunk, lane l the
+    // columns l + 64t (t < T <= kRowMaxT); past the last step every load is
+    // out of range (zeros, no traffic)
+    constexpr int RW = kRowCh / 4;
+    const int T = (Wn + 63) >> 6;
+    float v[RW][kRowMaxT];
+    auto load_window = [&](int st) {
+        const int tile = tile0 + st / NC, c0 = (st % NC) * kRowCh;
+        const int o0 = tile * TP * AW.s - AW.p;
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) {
+            const unsigned ch = 4u * (unsigned)((c0 + RW * wave + rr) * P.out_sp);
+#pragma unroll
+            for (int t = 0; t < kRowMaxT; ++t) {
+                const int e = t * 64 + lane;
+                const int o = o0 + e;
+                const bool ok = st < nsteps && e < Wn && o >= 0 && o < AW.L_out;
+                v[rr][t] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(rdy, ok ? 4u * (unsigned)o : kBwdOutOfRange, ch, 0));
+            }
+        }
+    };
+    load_window(0);
+    for (int st = 0; st < nsteps; ++st) {
+        __syncthreads(); // the previous window is consumed
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr)
+#pragma unroll
+            for (int t = 0; t < kRowMaxT; ++t) {
+                const int e = t * 64 + lane;
+                if (t < T && e < Wn) bw[(RW * wave + rr) * Wp + e] = v[rr][t];
+            }
+        __syncthreads();
+        load_window(st + 1);
+        const int c0 = (st % NC) * kRowCh;
+        for (int k = 0; k < K; ++k) {
+            const int kd = k * AW.d;
+            const float *wt = wa + (k * NQ + c0 / 4) * MT * 64 + lane;
+#pragma unroll
+            for (int qq = 0; qq < kRowCh / 4; ++qq) {
+                float a[MT], b[PB];
+#pragma unroll
+                for (int m = 0; m < MT; ++m) a[m] = wt[(qq * MT + m) * 64];
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb) b[pb] = bw[(4 * qq + c4) * Wp + col[pb] + kd];
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb)
+                        acc[m][pb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], b[pb], acc[m][pb], 0, 0, 0);
+            }
+        }
+        if (st % NC != NC - 1) continue;
+        // the tile is complete: lane j16 + 16*c4, register v holds position
+        // j16, input channel 16m + 4*c4 + v
+        const int p0 = (tile0 + st / NC) * TP;
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb) {
+            const int sp = p0 + wave * 16 * PB + pb * 16 + j16;
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int ci = g * P.Cig + ci0 + 16 * m + 4 * c4 + r;
+                    if (sp < P.in_sp) dx[((int64_t)n * P.C_in + ci) * P.in_sp + sp] = acc[m][pb][r];
+                }
+                acc[m][pb] = bwd_v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        }
+    }
+}
+
 constexpr int kBwdPB = 4; // 16-position blocks per wave
 
 // Row tiles per wave for the matrix kernel (0: it does not apply).  Needs
@@ -299,10 +444,54 @@ int launch_mfma(const convt_plan &Pl, BwdParams &P, const float *dy, const float
     return 0;
 }
 
+// The one-axis window variant applies: a 1D plan (unit leading axes), the
+// matrix kernel's channel counts, output channels in whole window chunks, and
+// every tap's A rows plus a kRowCh-row window within 64 KB of LDS.  Returns the
+// window row pitch (odd, so the four rows one MFMA operand reads start on
+// different banks), or 0.
+int row_window_pitch(const convt_plan &P, int mt) {
+    if (mt == 0 || P.Cog % kRowCh != 0) return 0;
+    if (P.ax[0].L_in != 1 || P.ax[1].L_in != 1 || P.ax[0].K != 1 || P.ax[1].K != 1) return 0;
+    const AxisPlan &A = P.ax[2];
+    const int64_t wn = (int64_t)(64 * kBwdPB - 1) * A.s + (int64_t)(A.K - 1) * A.d + 1;
+    if (wn > 64 * kRowMaxT) return 0;
+    const int64_t wp = wn | 1;
+    const int64_t a_bytes = (int64_t)P.k_vol * (P.Cog / 4) * mt * 64 * 4;
+    if (a_bytes > kBwdMaxLds || a_bytes + kRowCh * wp * 4 > 65536) return 0;
+    return (int)wp;
+}
+
+template <int MT>
+int launch_mfma_row(const convt_plan &Pl, BwdParams &P, int wp, const float *dy, const float *w, float *dx,
+                    hipStream_t st) {
+    P.ci_chunks = (int)(Pl.Cig / (16 * MT));
+    P.win_pitch = wp;
+    // enough tiles per workgroup to amortise staging the A rows, while the
+    // grid keeps at least kRowMinWgs workgroups
+    const int64_t ntiles = (Pl.in_sp + 64 * kBwdPB - 1) / (64 * kBwdPB);
+    const int64_t per_tile = Pl.N * Pl.G * P.ci_chunks;
+    int64_t tpw = ntiles * per_tile / kRowMinWgs;
+    P.tiles_per_wg = (int)(tpw < 1 ? 1 : tpw > kRowMaxTilesPerWg ? kRowMaxTilesPerWg : tpw);
+    const unsigned gx = (unsigned)((ntiles + P.tiles_per_wg - 1) / P.tiles_per_wg);
+    const unsigned gy = (unsigned)(Pl.G * P.ci_chunks);
+    const size_t lds = (size_t)(Pl.k_vol * (Pl.Cog / 4) * MT * 64 + kRowCh * wp) * sizeof(float);
+    for (int64_t n0 = 0; n0 < Pl.N; n0 += 65535) {
+        P.n0 = (int)n0;
+        const unsigned gz = (unsigned)(Pl.N - n0 < 65535 ? Pl.N - n0 : 65535);
+        hipLaunchKernelGGL((k_backward_data_mfma_row<MT, kBwdPB>), dim3(gx, gy, gz), dim3(kBwdBlock), lds, st, P,
+                           dy, w, dx);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return (int)e;
+    }
+    return 0;
+}
+
 } // namespace
 
 const char *backward_data_kernel_name(const convt_plan &P) {
-    return pick_mt(P) > 0 ? "k_backward_data_mfma" : "k_backward_data";
+    const int mt = pick_mt(P);
+    if (row_window_pitch(P, mt) > 0) return "k_backward_data_mfma_row";
+    return mt > 0 ? "k_backward_data_mfma" : "k_backward_data";
 }
 
 bool backward_data_supports(const convt_plan &P) {
@@ -321,7 +510,16 @@ int launch_backward_data(const convt_plan &Pl, const float *dy, const float *w, 
     P.in_sp = (int)Pl.in_sp;
     P.out_sp = (int)Pl.out_sp;
     hipStream_t st = (hipStream_t)stream;
-    switch (pick_mt(Pl)) {
+    const int mt = pick_mt(Pl);
+    const int wp = row_window_pitch(Pl, mt);
+    if (wp > 0) {
+        switch (mt) {
+        case 4: return launch_mfma_row<4>(Pl, P, wp, dy, w, dx, st);
+        case 2: return launch_mfma_row<2>(Pl, P, wp, dy, w, dx, st);
+        default: return launch_mfma_row<1>(Pl, P, wp, dy, w, dx, st);
+        }
+    }
+    switch (mt) {
     case 4: return launch_mfma<4>(Pl, P, dy, w, dx, st);
     case 2: return launch_mfma<2>(Pl, P, dy, w, dx, st);
     case 1: return launch_mfma<1>(Pl, P, dy, w, dx, st);
