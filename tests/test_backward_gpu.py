@@ -60,14 +60,18 @@ def test_backward_full_spatial(wl):
     _check(wl)
 
 
-# One-axis shapes whose grids are large enough that a workgroup of the
-# window-staged matrix kernel walks several position tiles: 3 tiles per
-# workgroup with a last workgroup of 2 and a ragged last tile; 4 with two
-# groups and unit stride; the cap of 8.
+# One-axis shapes for the window-staged matrix kernel.  Grids large enough
+# that a workgroup walks several position tiles: 3 tiles per workgroup with a
+# last workgroup of 2 and a ragged last tile (d a multiple of s: the window
+# keeps every s-th column); 4 with two groups and unit stride; the cap of 8
+# (d = 1 < s: the full window).  Then strides 3 and 4 with d a multiple of s,
+# which the compressed window brings within its column limit.
 ROW_TILES = [
     S.Workload("bwd_row_tiles3_ragged", 1, 300, 16, 4, 1, (5669,), (3,), (2,), (1,), (1,), (2,), False, False, 41),
     S.Workload("bwd_row_tiles4_g2", 1, 140, 32, 8, 2, (7683,), (4,), (1,), (2,), (0,), (3,), False, False, 42),
     S.Workload("bwd_row_tiles8", 1, 700, 16, 4, 1, (5889,), (3,), (2,), (0,), (0,), (1,), False, False, 43),
+    S.Workload("bwd_row_s3d3", 1, 2, 16, 8, 1, (700,), (3,), (3,), (2,), (1,), (3,), False, False, 44),
+    S.Workload("bwd_row_s4d8_g2", 1, 3, 32, 16, 2, (301,), (5,), (4,), (7,), (2,), (8,), False, False, 45),
 ]
 
 

@@ -33,6 +33,9 @@ struct BwdParams {
     int taps_per_chunk; // taps whose weights are staged at once
     int win_pitch;      // floats per staged dy window row (the one-axis matrix kernel)
     int tiles_per_wg;   // position tiles a workgroup of the one-axis matrix kernel walks
+    int win_cols;       // columns of that kernel's dy window
+    int win_cs;         // output step per window column (s when s divides d, else 1)
+    int win_js, win_kd; // window columns per input position (s/cs) and per tap (d/cs)
     int n0;             // first batch index of this launch
 };
 
@@ -248,15 +251,19 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma(const BwdParam
 }
 
 // Along one axis only (1D plans: the leading axes are unit), the dy values
-// that a tile of 64*PB consecutive input positions needs for all taps form one
-// window [p0*s - p, (p0 + 64*PB - 1)*s - p + (K-1)*d] of each output channel
-// row.  This variant stages that window, kRowCh output channels at a time,
-// into LDS with loads along the row (coalesced) and reads the B operands from it,
-// instead of gathering 4 channel rows per load instruction.  Every tap's A
-// rows are staged once per workgroup, and a workgroup walks tiles_per_wg
-// consecutive tiles; the next (tile, chunk) window is loaded into registers
-// while the current one's MFMAs run.  Window columns outside [0, L_out) are
-// zero.
+// that a tile of 64*PB consecutive input positions needs for all taps lie in
+// one window [p0*s - p, (p0 + 64*PB - 1)*s - p + (K-1)*d] of each output
+// channel row.  When d is a multiple of s only every s-th column of it is ever
+// read (position j, tap k: column j*s + k*d), so the window keeps those
+// columns alone: column e holds output o0 + cs*e with cs = s then, else 1.
+// This variant stages the window, kRowCh output channels at a time, into LDS
+// with loads along the row and reads the B operands from it, instead of
+// gathering 4 channel rows per load instruction.  Every tap's A rows are
+// staged once per workgroup, and a workgroup walks tiles_per_wg consecutive
+// tiles.  The next (tile, chunk) window is loaded into registers while the
+// current one's MFMAs run.  (A second LDS buffer, to save one of the two
+// barriers per step, costs a workgroup per CU and is slower.)  Columns
+// outside [0, L_out) are zero.
 template <int MT, int PB>
 __global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma_row(const BwdParams P,
                                                                       const float *__restrict__ dy,
@@ -270,10 +277,11 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma_row(const BwdP
     const int n = P.n0 + blockIdx.z;
     const int NQ = P.Cog / 4;
     const int NC = P.Cog / kRowCh; // window chunks per tile
-    const int K = P.k_vol;      // taps along W
-    const int TP = 64 * PB;     // positions per tile
-    const int Wp = P.win_pitch; // floats per staged row (odd)
-    const int Wn = (TP - 1) * AW.s + (K - 1) * AW.d + 1;
+    const int K = P.k_vol;         // taps along W
+    const int TP = 64 * PB;        // positions per tile
+    const int Wp = P.win_pitch;    // floats per staged row (odd)
+    const int Wn = P.win_cols;     // columns of the window
+    const int cs = P.win_cs;       // output step per window column
     const int tile0 = blockIdx.x * P.tiles_per_wg;
     const int ntiles = min(P.tiles_per_wg, (P.in_sp + TP - 1) / TP - tile0);
     const int nsteps = ntiles * NC; // (tile, chunk) steps, chunk-minor
@@ -313,7 +321,7 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma_row(const BwdP
     // this lane's window column for position block pb at tap 0
     int col[PB];
 #pragma unroll
-    for (int pb = 0; pb < PB; ++pb) col[pb] = (wave * 16 * PB + pb * 16 + j16) * AW.s;
+    for (int pb = 0; pb < PB; ++pb) col[pb] = (wave * 16 * PB + pb * 16 + j16) * P.win_js;
     // wave v stages window rows RW*v .. RW*v + RW-1 of a chunk, lane l the
     // columns l + 64t (t < T <= kRowMaxT); past the last step every load is
     // out of range (zeros, no traffic)
@@ -328,8 +336,9 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma_row(const BwdP
             const unsigned ch = 4u * (unsigned)((c0 + RW * wave + rr) * P.out_sp);
 #pragma unroll
             for (int t = 0; t < kRowMaxT; ++t) {
+                if (t >= T) break; // wave-uniform
                 const int e = t * 64 + lane;
-                const int o = o0 + e;
+                const int o = o0 + cs * e;
                 const bool ok = st < nsteps && e < Wn && o >= 0 && o < AW.L_out;
                 v[rr][t] = __builtin_bit_cast(
                     float, __builtin_amdgcn_raw_buffer_load_b32(rdy, ok ? 4u * (unsigned)o : kBwdOutOfRange, ch, 0));
@@ -350,7 +359,7 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma_row(const BwdP
         load_window(st + 1);
         const int c0 = (st % NC) * kRowCh;
         for (int k = 0; k < K; ++k) {
-            const int kd = k * AW.d;
+            const int kd = k * P.win_kd;
             const float *wt = wa + (k * NQ + c0 / 4) * MT * 64 + lane;
 #pragma unroll
             for (int qq = 0; qq < kRowCh / 4; ++qq) {
@@ -366,21 +375,22 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma_row(const BwdP
                         acc[m][pb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], b[pb], acc[m][pb], 0, 0, 0);
             }
         }
-        if (st % NC != NC - 1) continue;
-        // the tile is complete: lane j16 + 16*c4, register v holds position
-        // j16, input channel 16m + 4*c4 + v
-        const int p0 = (tile0 + st / NC) * TP;
+        if (st % NC == NC - 1) {
+            // the tile is complete: lane j16 + 16*c4, register r holds
+            // position j16, input channel 16m + 4*c4 + r
+            const int p0 = (tile0 + st / NC) * TP;
 #pragma unroll
-        for (int pb = 0; pb < PB; ++pb) {
-            const int sp = p0 + wave * 16 * PB + pb * 16 + j16;
+            for (int pb = 0; pb < PB; ++pb) {
+                const int sp = p0 + wave * 16 * PB + pb * 16 + j16;
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
+                for (int m = 0; m < MT; ++m) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int ci = g * P.Cig + ci0 + 16 * m + 4 * c4 + r;
-                    if (sp < P.in_sp) dx[((int64_t)n * P.C_in + ci) * P.in_sp + sp] = acc[m][pb][r];
+                    for (int r = 0; r < 4; ++r) {
+                        const int ci = g * P.Cig + ci0 + 16 * m + 4 * c4 + r;
+                        if (sp < P.in_sp) dx[((int64_t)n * P.C_in + ci) * P.in_sp + sp] = acc[m][pb][r];
+                    }
+                    acc[m][pb] = bwd_v4f{0.0f, 0.0f, 0.0f, 0.0f};
                 }
-                acc[m][pb] = bwd_v4f{0.0f, 0.0f, 0.0f, 0.0f};
             }
         }
     }
@@ -446,26 +456,31 @@ int launch_mfma(const convt_plan &Pl, BwdParams &P, const float *dy, const float
 
 // The one-axis window variant applies: a 1D plan (unit leading axes), the
 // matrix kernel's channel counts, output channels in whole window chunks, and
-// every tap's A rows plus a kRowCh-row window within 64 KB of LDS.  Returns the
-// window row pitch (odd, so the four rows one MFMA operand reads start on
-// different banks), or 0.
-int row_window_pitch(const convt_plan &P, int mt) {
-    if (mt == 0 || P.Cog % kRowCh != 0) return 0;
-    if (P.ax[0].L_in != 1 || P.ax[1].L_in != 1 || P.ax[0].K != 1 || P.ax[1].K != 1) return 0;
-    const AxisPlan &A = P.ax[2];
-    const int64_t wn = (int64_t)(64 * kBwdPB - 1) * A.s + (int64_t)(A.K - 1) * A.d + 1;
-    if (wn > 64 * kRowMaxT) return 0;
+// every tap's A rows plus a kRowCh-row window within 64 KB of LDS.  Fills
+// the window fields of P and returns true when it applies.  The row pitch is
+// odd, so the rows one MFMA operand reads start on different banks.
+bool row_window(const convt_plan &Pl, int mt, BwdParams &P) {
+    if (mt == 0 || Pl.Cog % kRowCh != 0) return false;
+    if (Pl.ax[0].L_in != 1 || Pl.ax[1].L_in != 1 || Pl.ax[0].K != 1 || Pl.ax[1].K != 1) return false;
+    const AxisPlan &A = Pl.ax[2];
+    const int cs = A.d % A.s == 0 ? A.s : 1;
+    const int64_t wn = (int64_t)(64 * kBwdPB - 1) * (A.s / cs) + (int64_t)(A.K - 1) * (A.d / cs) + 1;
+    if (wn > 64 * kRowMaxT) return false;
     const int64_t wp = wn | 1;
-    const int64_t a_bytes = (int64_t)P.k_vol * (P.Cog / 4) * mt * 64 * 4;
-    if (a_bytes > kBwdMaxLds || a_bytes + kRowCh * wp * 4 > 65536) return 0;
-    return (int)wp;
+    const int64_t a_bytes = (int64_t)Pl.k_vol * (Pl.Cog / 4) * mt * 64 * 4;
+    if (a_bytes > kBwdMaxLds || a_bytes + kRowCh * wp * 4 > 65536) return false;
+    P.win_pitch = (int)wp;
+    P.win_cols = (int)wn;
+    P.win_cs = cs;
+    P.win_js = A.s / cs;
+    P.win_kd = A.d / cs;
+    return true;
 }
 
 template <int MT>
-int launch_mfma_row(const convt_plan &Pl, BwdParams &P, int wp, const float *dy, const float *w, float *dx,
+int launch_mfma_row(const convt_plan &Pl, BwdParams &P, const float *dy, const float *w, float *dx,
                     hipStream_t st) {
     P.ci_chunks = (int)(Pl.Cig / (16 * MT));
-    P.win_pitch = wp;
     // enough tiles per workgroup to amortise staging the A rows, while the
     // grid keeps at least kRowMinWgs workgroups
     const int64_t ntiles = (Pl.in_sp + 64 * kBwdPB - 1) / (64 * kBwdPB);
@@ -474,7 +489,7 @@ int launch_mfma_row(const convt_plan &Pl, BwdParams &P, int wp, const float *dy,
     P.tiles_per_wg = (int)(tpw < 1 ? 1 : tpw > kRowMaxTilesPerWg ? kRowMaxTilesPerWg : tpw);
     const unsigned gx = (unsigned)((ntiles + P.tiles_per_wg - 1) / P.tiles_per_wg);
     const unsigned gy = (unsigned)(Pl.G * P.ci_chunks);
-    const size_t lds = (size_t)(Pl.k_vol * (Pl.Cog / 4) * MT * 64 + kRowCh * wp) * sizeof(float);
+    const size_t lds = (size_t)(Pl.k_vol * (Pl.Cog / 4) * MT * 64 + kRowCh * P.win_pitch) * sizeof(float);
     for (int64_t n0 = 0; n0 < Pl.N; n0 += 65535) {
         P.n0 = (int)n0;
         const unsigned gz = (unsigned)(Pl.N - n0 < 65535 ? Pl.N - n0 : 65535);
@@ -490,7 +505,8 @@ int launch_mfma_row(const convt_plan &Pl, BwdParams &P, int wp, const float *dy,
 
 const char *backward_data_kernel_name(const convt_plan &P) {
     const int mt = pick_mt(P);
-    if (row_window_pitch(P, mt) > 0) return "k_backward_data_mfma_row";
+    BwdParams W;
+    if (row_window(P, mt, W)) return "k_backward_data_mfma_row";
     return mt > 0 ? "k_backward_data_mfma" : "k_backward_data";
 }
 
@@ -511,12 +527,11 @@ int launch_backward_data(const convt_plan &Pl, const float *dy, const float *w, 
     P.out_sp = (int)Pl.out_sp;
     hipStream_t st = (hipStream_t)stream;
     const int mt = pick_mt(Pl);
-    const int wp = row_window_pitch(Pl, mt);
-    if (wp > 0) {
+    if (row_window(Pl, mt, P)) {
         switch (mt) {
-        case 4: return launch_mfma_row<4>(Pl, P, wp, dy, w, dx, st);
-        case 2: return launch_mfma_row<2>(Pl, P, wp, dy, w, dx, st);
-        default: return launch_mfma_row<1>(Pl, P, wp, dy, w, dx, st);
+        case 4: return launch_mfma_row<4>(Pl, P, dy, w, dx, st);
+        case 2: return launch_mfma_row<2>(Pl, P, dy, w, dx, st);
+        default: return launch_mfma_row<1>(Pl, P, dy, w, dx, st);
         }
     }
     switch (mt) {
