@@ -124,6 +124,11 @@ typedef float bwd_v4f __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t bwd_rsrc_t;
 constexpr int kBwdRsrcWord3 = 0x00020000; // raw (untyped) buffer access
 constexpr unsigned kBwdOutOfRange = 0x80000000u;
+// A-row loads in flight per wave while the matrix kernel stages a chunk of
+// taps.  Eight is measured faster with up to 2 row tiles per wave (the
+// fused-layer shape, 1.17 -> 1.14 ms) and slower with 4 (the channel-heavy
+// shape, 3.52 -> 3.71 ms; 2 and 4 in flight lie between), where one is kept.
+template <int MT> constexpr int stage_depth() { return MT >= 4 ? 1 : 8; }
 constexpr int kRowMaxT = 10; // 64-column steps of the one-axis kernel's dy window (640 columns)
 constexpr int kRowMinWgs = 2048;       // the one-axis kernel's grid, at least (8 per CU)
 constexpr int kRowMaxTilesPerWg = 8;
@@ -140,6 +145,7 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma(const BwdParam
     const int ci0 = (blockIdx.y % P.ci_chunks) * 16 * MT; // first input channel of the group
     const int n = P.n0 + blockIdx.z;
     const int NQ = P.Cog / 4;
+    constexpr int SD = stage_depth<MT>();
 
     int id[PB], ih[PB], iw[PB], sp[PB];
     bool live[PB];
@@ -171,11 +177,21 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma(const BwdParam
     for (int t0 = 0; t0 < P.k_vol; t0 += P.taps_per_chunk) {
         const int tc = min(P.taps_per_chunk, P.k_vol - t0);
         if (t0 > 0) __syncthreads(); // the previous chunk is consumed
+        // rows dealt to waves, SD loads in flight per wave (indexes past the
+        // last row repeat it)
         const int nrows = tc * NQ * MT;
-        for (int r = wave; r < nrows; r += 4) {
-            const int m = r % MT, t = r / MT;
-            const int q = t % NQ, tap = t / NQ;
-            wa[r * 64 + lane] = wl_[((int64_t)(16 * m) * P.Cog + 4 * q) * P.k_vol + t0 + tap];
+        for (int r0 = wave; r0 < nrows; r0 += 4 * SD) {
+            float t8[SD];
+#pragma unroll
+            for (int u = 0; u < SD; ++u) {
+                const int r = min(r0 + 4 * u, nrows - 1);
+                const int m = r % MT, t = r / MT;
+                const int q = t % NQ, tap = t / NQ;
+                t8[u] = wl_[((int64_t)(16 * m) * P.Cog + 4 * q) * P.k_vol + t0 + tap];
+            }
+#pragma unroll
+            for (int u = 0; u < SD; ++u)
+                if (r0 + 4 * u < nrows) wa[(r0 + 4 * u) * 64 + lane] = t8[u];
         }
         __syncthreads();
         // Steps (t, q) of the chunk, t-major.  The B operands of the next step
