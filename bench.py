@@ -100,7 +100,7 @@ KERNEL_SOURCES = {"k_stream1d": "stream1d.hip", "k_igemm3d": "igemm3d.hip", "k_i
                   "k_generic_pairs": "generic.hip", "k_backward_data": "backward.hip",
                   "k_backward_data_mfma": "backward.hip", "k_backward_data_mfma_row": "backward.hip",
                   "k_backward_weight": "wgrad.hip",
-                  "k_backward_weight_lds": "wgrad.hip"}
+                  "k_backward_weight_lds": "wgrad.hip", "k_backward_weight_row": "wgrad.hip"}
 SHARED_SOURCES = ("convt_internal.h", "epilogue.hpp")
 
 

@@ -85,3 +85,20 @@ def test_wgrad_random_and_degenerate(wl):
                          ids=lambda w: f"{w.name}-N{w.N}")
 def test_wgrad_full_spatial(wl):
     _check(wl)
+
+
+# One-axis shapes for the window-staged weight-gradient kernel: 6 taps in two
+# chunks of up to 4 (d = 1 < s: the full window); stride 3 with d = 3 and
+# stride 4 with d = 8 and two groups (d a multiple of s: the window keeps
+# every s-th column).  Ragged last tiles and ranges throughout.
+ROW_WINDOW = [
+    S.Workload("wgrad_row_k6_chunks", 1, 3, 32, 64, 1, (1000,), (6,), (2,), (2,), (1,), (1,), True, False, 51),
+    S.Workload("wgrad_row_s3d3", 1, 2, 32, 64, 1, (777,), (5,), (3,), (4,), (2,), (3,), True, False, 52),
+    S.Workload("wgrad_row_s4d8_g2", 1, 2, 64, 128, 2, (301,), (3,), (4,), (3,), (0,), (8,), True, False, 53),
+]
+
+
+@pytest.mark.parametrize("wl", ROW_WINDOW, ids=lambda w: w.name)
+def test_wgrad_row_window(wl):
+    assert "weight gradient: kernel=k_backward_weight_row" in T.convt_plan_describe(T.plan_for(wl))
+    _check(wl)

@@ -285,6 +285,139 @@ __global__ __launch_bounds__(kWgBlock) void k_backward_weight_lds(const WlParams
     }
 }
 
+// One-axis plans (unit leading axes) with the same channel blocks: for a tile
+// of 64 consecutive positions the dy values of every tap of the chunk lie in
+// one window of each output-channel row, columns e <-> o = p0*s - p + k0*d +
+// cs*e, where cs = s when s divides d (then only every s-th column is read:
+// position pp, tap u at column pp*js + u*kd with js = s/cs, kd = d/cs), else
+// 1.  The window is staged once per tile for all taps, transposed to
+// [column][co] (pitch 65), with loads along the row, so the tile takes two
+// barriers instead of one per tap, and each A read from LDS feeds every tap.
+// Partial sums go to dw with atomics as above.
+struct WrParams {
+    WlParams L;
+    int win_cols;            // columns of the staged window
+    int win_cs, win_js, win_kd;
+    float inv_cols;          // 1 / win_cols (exact quotients for the staged index range)
+};
+
+__global__ __launch_bounds__(kWgBlock) void k_backward_weight_row(const WrParams R, const float *__restrict__ x,
+                                                                  const float *__restrict__ dy, float *dw) {
+    const WlParams &P = R.L;
+    const AxisPlan &AW = P.ax[2];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int64_t t = blockIdx.x;
+    const int range = (int)(t % P.nranges);
+    t /= P.nranges;
+    const int kc = (int)(t % P.kchunks);
+    t /= P.kchunks;
+    const int cb = (int)(t % P.cob);
+    t /= P.cob;
+    const int ib = (int)(t % P.cib);
+    t /= P.cib;
+    const int g = (int)(t % (P.C_in / P.Cig));
+    const int n = (int)(t / (P.C_in / P.Cig));
+    const int ci0 = 32 * ib, co0 = 64 * cb;
+    const int k0 = kc * kWlTaps, tk = min(kWlTaps, P.k_vol - k0);
+    const int Wn = R.win_cols, cs = R.win_cs;
+
+    extern __shared__ __attribute__((aligned(16))) float wr_lds[];
+    float *As = wr_lds;                     // [position][ci], pitch kWlApitch
+    float *Bw = wr_lds + kWlTile * kWlApitch; // [column][co], pitch kWlBpitch
+
+    const float *xg = x + ((int64_t)n * P.C_in + (int64_t)g * P.Cig + ci0) * P.in_sp;
+    const float *dyg = dy + ((int64_t)n * P.C_out + (int64_t)g * P.Cog + co0) * P.out_sp;
+
+    wg_v4f acc[kWlTaps][2];
+#pragma unroll
+    for (int u = 0; u < kWlTaps; ++u) acc[u][0] = acc[u][1] = wg_v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int i16 = lane & 15, c4 = lane >> 4;
+    const int p_begin = range * kWlRange;
+    const int p_end = min(p_begin + kWlRange, P.in_sp);
+    const int nwin = Wn * 64;
+    for (int p0 = p_begin; p0 < p_end; p0 += kWlTile) {
+        const int p = p0 + lane;
+        const bool live = p < p_end;
+        const int obase = p0 * AW.s - AW.p + k0 * AW.d;
+        __syncthreads(); // the previous tile's operands are consumed
+        // x tile, [position][ci]; positions past the range are zero, so the
+        // window's columns for them add nothing
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int ci = wave + 4 * r;
+            As[lane * kWlApitch + ci] = live ? xg[(int64_t)ci * P.in_sp + p] : 0.0f;
+        }
+        // dy window: element idx = co*Wn + e, consecutive threads along e
+        for (int i0 = 0; i0 < nwin; i0 += 8 * kWgBlock) {
+            float v[8];
+            int slot[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int idx = i0 + u * kWgBlock + threadIdx.x;
+                const int co = (int)(((float)idx + 0.5f) * R.inv_cols);
+                const int e = idx - co * Wn;
+                const int o = obase + cs * e;
+                const bool ok = idx < nwin && o >= 0 && o < AW.L_out;
+                v[u] = ok ? dyg[(int64_t)co * P.out_sp + o] : 0.0f;
+                slot[u] = idx < nwin ? e * kWlBpitch + co : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (slot[u] >= 0) Bw[slot[u]] = v[u];
+        }
+        __syncthreads();
+        // wave: output-channel tile `wave`, both input-channel tiles, every tap
+#pragma unroll 2
+        for (int q = 0; q < kWlTile / 4; ++q) {
+            const int pp = 4 * q + c4;
+            const float a0 = As[pp * kWlApitch + i16];
+            const float a1 = As[pp * kWlApitch + 16 + i16];
+            const float *bcol = Bw + pp * R.win_js * kWlBpitch + 16 * wave + i16;
+#pragma unroll
+            for (int u = 0; u < kWlTaps; ++u) {
+                if (u >= tk) break;
+                const float b = bcol[u * R.win_kd * kWlBpitch];
+                acc[u][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, b, acc[u][0], 0, 0, 0);
+                acc[u][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, b, acc[u][1], 0, 0, 0);
+            }
+        }
+    }
+
+    // lane j + 16*c4, register v: dW_k[ci0 + 16m + 4*c4 + v][co0 + 16*wave + j]
+    const int co = co0 + 16 * wave + i16;
+#pragma unroll
+    for (int u = 0; u < kWlTaps; ++u) {
+        if (u >= tk) break;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int ci = ci0 + 16 * m + 4 * c4 + v;
+                atomicAdd(dw + ((int64_t)(g * P.Cig + ci) * P.Cog + co) * P.k_vol + k0 + u, acc[u][m][v]);
+            }
+    }
+}
+
+// The one-axis window kernel applies: unit leading axes, the LDS kernel's
+// channel blocks, and the x tile plus the window within 64 KB.  Fills the
+// window fields of R and returns true when it applies.
+bool weight_row_window(const convt_plan &Pl, WrParams &R) {
+    if (Pl.Cig % 32 != 0 || Pl.Cog % 64 != 0) return false;
+    if (Pl.ax[0].L_in != 1 || Pl.ax[1].L_in != 1 || Pl.ax[0].K != 1 || Pl.ax[1].K != 1) return false;
+    const AxisPlan &A = Pl.ax[2];
+    const int cs = A.d % A.s == 0 ? A.s : 1;
+    const int tk = Pl.k_vol < kWlTaps ? (int)Pl.k_vol : kWlTaps;
+    const int64_t wn = (int64_t)(kWlTile - 1) * (A.s / cs) + (int64_t)(tk - 1) * (A.d / cs) + 1;
+    if ((kWlTile * kWlApitch + wn * kWlBpitch) * 4 > 65536) return false;
+    R.win_cols = (int)wn;
+    R.win_cs = cs;
+    R.win_js = A.s / cs;
+    R.win_kd = A.d / cs;
+    R.inv_cols = 1.0f / (float)wn;
+    return true;
+}
+
 // db[co] += the sum of dy[n, co, :] for one (co, n) per workgroup.
 __global__ __launch_bounds__(kWgBlock) void k_backward_bias(const float *__restrict__ dy, float *db, int C_out,
                                                             int out_sp) {
@@ -321,6 +454,8 @@ int launch_w(const convt_plan &Pl, WgradParams &P, const float *x, const float *
 } // namespace
 
 const char *backward_weight_kernel_name(const convt_plan &P) {
+    WrParams R;
+    if (weight_row_window(P, R)) return "k_backward_weight_row";
     return P.Cig % 32 == 0 && P.Cog % 64 == 0 ? "k_backward_weight_lds" : "k_backward_weight";
 }
 
@@ -365,7 +500,14 @@ int launch_backward_weight(const convt_plan &Pl, const float *x, const float *dy
         L.kchunks = (int)((Pl.k_vol + kWlTaps - 1) / kWlTaps);
         L.nranges = (int)((Pl.in_sp + kWlRange - 1) / kWlRange);
         const int64_t blocks = Pl.N * Pl.G * (int64_t)L.cib * L.cob * L.kchunks * L.nranges;
-        hipLaunchKernelGGL(k_backward_weight_lds, dim3((unsigned)blocks), dim3(kWgBlock), 0, st, L, x, dy, dw);
+        WrParams R;
+        if (weight_row_window(Pl, R)) {
+            R.L = L;
+            const size_t lds = (size_t)(kWlTile * kWlApitch + R.win_cols * kWlBpitch) * sizeof(float);
+            hipLaunchKernelGGL(k_backward_weight_row, dim3((unsigned)blocks), dim3(kWgBlock), lds, st, R, x, dy, dw);
+        } else {
+            hipLaunchKernelGGL(k_backward_weight_lds, dim3((unsigned)blocks), dim3(kWgBlock), 0, st, L, x, dy, dw);
+        }
         e = hipGetLastError();
         rc = e == hipSuccess ? 0 : (int)e;
     } else {
