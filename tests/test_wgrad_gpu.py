@@ -10,9 +10,12 @@ ranges by atomic adds.  With u = 2^-24 and S = the sum of |x * dy| over the
 same terms (the oracle's gradient of |x| and |dy|), the rounding error is
 within (chain length) * u * S; the test allows
   |got - ref| <= 1e-4 + (256 + 4 + ranges + 8) * 2^-24 * S.
-db sums N * L_out values: per (co, n) a thread adds L_out/256 of them, a wave
-tree of 8 levels and N atomic adds, so chain = L_out/256 + 8 + N with
-S = sum |dy|."""
+db sums N * L_out values in chunks of 16384 positions: a thread adds up to 4
+values into each of 16 partial sums, which a 4-level tree, a wave tree of 6
+levels and a 2-level tree across the 4 waves combine, and the N * chunks
+partial sums meet by atomic adds, so
+chain = ceil(min(L_out, 16384) / 4096) + 4 + 8 + N * ceil(L_out / 16384)
+with S = sum |dy|."""
 import numpy as np
 import pytest
 
@@ -51,7 +54,7 @@ def _check(wl, seed=0):
     in_sp = int(np.prod(wl.in_size))
     out_sp = int(np.prod(out))
     chain_w = 256 + 4 + wl.N * -(-in_sp // 1024) + 8
-    chain_b = -(-out_sp // 256) + 8 + wl.N
+    chain_b = -(-min(out_sp, 16384) // 4096) + 4 + 8 + wl.N * -(-out_sp // 16384)
     for what, got, ref, s_abs, chain in (("dw", dw, ref_w, abs_w, chain_w), ("db", db, ref_b, abs_b, chain_b)):
         g = got.cpu().numpy().astype(np.float64)
         assert g.shape == ref.shape and np.all(np.isfinite(g)), (what, g.shape, ref.shape)

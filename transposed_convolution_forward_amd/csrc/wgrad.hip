@@ -418,19 +418,42 @@ bool weight_row_window(const convt_plan &Pl, WrParams &R) {
     return true;
 }
 
-// db[co] += the sum of dy[n, co, :] for one (co, n) per workgroup.
+// db[co] += the sum of dy[n, co, e] over one chunk of kBiasChunk positions e
+// per workgroup, grid (co, chunk, n).  Each thread keeps kBiasDepth partial
+// sums, so that many loads are in flight; a pairwise tree, a wave tree and an
+// atomic add finish the chunk.
+constexpr int kBiasChunk = 16384;
+constexpr int kBiasDepth = 16;
 __global__ __launch_bounds__(kWgBlock) void k_backward_bias(const float *__restrict__ dy, float *db, int C_out,
                                                             int out_sp) {
-    const int co = blockIdx.x, n = blockIdx.y;
+    const int co = blockIdx.x, n = blockIdx.z;
     const float *row = dy + ((int64_t)n * C_out + co) * out_sp;
-    float s = 0.0f;
-    for (int e = threadIdx.x; e < out_sp; e += kWgBlock) s += row[e];
+    const int e0 = blockIdx.y * kBiasChunk;
+    const int e1 = min(e0 + kBiasChunk, out_sp);
+    float sp[kBiasDepth];
+#pragma unroll
+    for (int u = 0; u < kBiasDepth; ++u) sp[u] = 0.0f;
+    for (int e = e0 + threadIdx.x; e < e1; e += kBiasDepth * kWgBlock) {
+#pragma unroll
+        for (int u = 0; u < kBiasDepth; ++u) {
+            // unconditional loads (a clamped index; past the chunk the value
+            // is dropped), so all of them are in flight at once
+            const int i = e + u * kWgBlock;
+            const float v = row[min(i, e1 - 1)];
+            sp[u] += i < e1 ? v : 0.0f;
+        }
+    }
+#pragma unroll
+    for (int h = kBiasDepth / 2; h >= 1; h /= 2)
+#pragma unroll
+        for (int u = 0; u < h; ++u) sp[u] += sp[u + h];
+    float s = sp[0];
     __shared__ float part[kWgBlock / 64];
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = s;
     __syncthreads();
-    if (threadIdx.x == 0) atomicAdd(db + co, part[0] + part[1] + part[2] + part[3]);
+    if (threadIdx.x == 0) atomicAdd(db + co, (part[0] + part[1]) + (part[2] + part[3]));
 }
 
 __global__ void k_fill_zero(float *p, int64_t n) {
@@ -515,8 +538,9 @@ int launch_backward_weight(const convt_plan &Pl, const float *x, const float *dy
                                               : launch_w<1, 1>(Pl, P, x, dy, dw, st);
     }
     if (rc || !db) return rc;
-    hipLaunchKernelGGL(k_backward_bias, dim3((unsigned)Pl.C_out, (unsigned)Pl.N), dim3(kWgBlock), 0, st, dy, db,
-                       (int)Pl.C_out, (int)Pl.out_sp);
+    const unsigned chunks = (unsigned)((Pl.out_sp + kBiasChunk - 1) / kBiasChunk);
+    hipLaunchKernelGGL(k_backward_bias, dim3((unsigned)Pl.C_out, chunks, (unsigned)Pl.N), dim3(kWgBlock), 0, st, dy,
+                       db, (int)Pl.C_out, (int)Pl.out_sp);
     e = hipGetLastError();
     return e == hipSuccess ? 0 : (int)e;
 }
