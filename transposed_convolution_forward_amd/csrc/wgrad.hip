@@ -231,10 +231,15 @@ __global__ __launch_bounds__(kWgBlock) void k_backward_weight_lds(const WlParams
         const bool live = p < p_end;
         const int iw = p % AW.L_in, ih = (p / AW.L_in) % AH.L_in, id = p / (AW.L_in * AH.L_in);
         __syncthreads(); // the previous tile's operands are consumed
+        {
+            // unconditional loads (positions past the range read its last one
+            // and store zero), so all eight are in flight at once
+            const int pc = min(p, p_end - 1);
+            float xv[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int ci = wave + 4 * r;
-            As[lane * kWlApitch + ci] = live ? xg[(int64_t)ci * P.in_sp + p] : 0.0f;
+            for (int r = 0; r < 8; ++r) xv[r] = xg[(int64_t)(wave + 4 * r) * P.in_sp + pc];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) As[lane * kWlApitch + wave + 4 * r] = live ? xv[r] : 0.0f;
         }
         for (int u = 0; u < tk; ++u) {
             const int k = k0 + u;
@@ -343,10 +348,15 @@ __global__ __launch_bounds__(kWgBlock) void k_backward_weight_row(const WrParams
         __syncthreads(); // the previous tile's operands are consumed
         // x tile, [position][ci]; positions past the range are zero, so the
         // window's columns for them add nothing
+        {
+            // unconditional loads (positions past the range read its last one
+            // and store zero), so all eight are in flight at once
+            const int pc = min(p, p_end - 1);
+            float xv[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int ci = wave + 4 * r;
-            As[lane * kWlApitch + ci] = live ? xg[(int64_t)ci * P.in_sp + p] : 0.0f;
+            for (int r = 0; r < 8; ++r) xv[r] = xg[(int64_t)(wave + 4 * r) * P.in_sp + pc];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) As[lane * kWlApitch + wave + 4 * r] = live ? xv[r] : 0.0f;
         }
         // dy window: element idx = co*Wn + e, consecutive threads along e
         for (int i0 = 0; i0 < nwin; i0 += 8 * kWgBlock) {
