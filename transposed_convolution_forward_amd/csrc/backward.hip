@@ -69,11 +69,21 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data(const BwdParams P, 
     for (int t0 = 0; t0 < P.k_vol; t0 += P.taps_per_chunk) {
         const int tc = min(P.taps_per_chunk, P.k_vol - t0);
         if (t0 > 0) __syncthreads(); // the previous chunk is consumed
+        // eight loads in flight per thread (indexes past the last element
+        // repeat it)
         const int nw = tc * P.Cog * CPI;
-        for (int e = threadIdx.x; e < nw; e += kBwdBlock) {
-            const int j = e % CPI, t = e / CPI;
-            const int co_l = t % P.Cog, tap = t / P.Cog;
-            ws[e] = wg[((int64_t)min(j, nci - 1) * P.Cog + co_l) * P.k_vol + t0 + tap];
+        for (int e0 = threadIdx.x; e0 < nw; e0 += 8 * kBwdBlock) {
+            float t8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = min(e0 + u * kBwdBlock, nw - 1);
+                const int j = e % CPI, t = e / CPI;
+                const int co_l = t % P.Cog, tap = t / P.Cog;
+                t8[u] = wg[((int64_t)min(j, nci - 1) * P.Cog + co_l) * P.k_vol + t0 + tap];
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (e0 + u * kBwdBlock < nw) ws[e0 + u * kBwdBlock] = t8[u];
         }
         __syncthreads();
         for (int t = 0; t < tc; ++t) {
