@@ -145,6 +145,38 @@ def test_workload_plans_and_paths():
     assert "kernel=k_igemm3d_wide" in T.convt_plan_describe(p2w)
 
 
+def _gradient_kernels(plan):
+    text = T.convt_plan_describe(plan)
+    return tuple(line.split("=")[1] for line in text.splitlines() if "gradient: kernel=" in line)
+
+
+def test_gradient_kernel_routing():
+    """The describe text names the kernels the gradient calls run; the
+    choices follow the kernels' documented conditions."""
+    want = {S.TINY_1D.name: ("k_backward_data", "k_backward_weight"),
+            S.LONG_1D.name: ("k_backward_data_mfma_row", "k_backward_weight_row"),
+            S.GROUPED_3D.name: ("k_backward_data", "k_backward_weight"),
+            S.FUSED_3D.name: ("k_backward_data_mfma", "k_backward_weight_lds"),
+            S.HEAVY_3D.name: ("k_backward_data_mfma", "k_backward_weight_lds")}
+    for wl in S.WORKLOADS:
+        assert _gradient_kernels(T.plan_for(wl)) == want[wl.name], wl.name
+    # one axis, s = 3 and d = 2: the input gradient's full window (765 + 5
+    # columns) exceeds its 640-column limit, the weight gradient's (194) fits
+    p = T.Plan(1, 2, 32, 64, 1, (1000,), (3,), (3,), (1,), (0,), (2,))
+    assert _gradient_kernels(p) == ("k_backward_data_mfma", "k_backward_weight_row")
+    # d a multiple of s: only every s-th column is kept, and both windows fit
+    p = T.Plan(1, 2, 32, 64, 1, (1000,), (3,), (3,), (1,), (0,), (3,))
+    assert _gradient_kernels(p) == ("k_backward_data_mfma_row", "k_backward_weight_row")
+    # s = 4, d = 1, K = 5: the weight gradient's window (256 columns) does not
+    # fit 64 KB of LDS beside the x tile
+    p = T.Plan(1, 2, 32, 64, 1, (1000,), (5,), (4,), (1,), (0,), (1,))
+    assert _gradient_kernels(p) == ("k_backward_data_mfma", "k_backward_weight_lds")
+    # 4 output channels per group: the window kernel's 4-channel chunks still
+    # apply; the weight gradient's channel blocks do not
+    p = T.Plan(1, 2, 16, 4, 1, (1000,), (3,), (2,), (1,), (0,), (2,))
+    assert _gradient_kernels(p) == ("k_backward_data_mfma_row", "k_backward_weight")
+
+
 def test_phase_table_description():
     # stride 2, padding 1, dilation 2, kernel 3: residue 0 takes every tap, residue 1 none
     p = T.Plan(1, 1, 1, 1, 1, (8,), (3,), (2,), (1,), (0,), (2,))
