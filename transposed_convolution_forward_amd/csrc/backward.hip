@@ -290,8 +290,12 @@ __global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma(const BwdParam
 // current one's MFMAs run.  (A second LDS buffer, to save one of the two
 // barriers per step, costs a workgroup per CU and is slower.)  Columns
 // outside [0, L_out) are zero.
+// Five waves per SIMD (at most 102 VGPRs) for up to 2 row tiles per wave: the
+// long 1D shape 0.406 -> 0.384 ms; with 4 row tiles the bound would spill.
+template <int MT> constexpr int row_waves_per_simd() { return MT >= 4 ? 1 : 5; }
+
 template <int MT, int PB>
-__global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma_row(const BwdParams P,
+__global__ __launch_bounds__(kBwdBlock, row_waves_per_simd<MT>()) void k_backward_data_mfma_row(const BwdParams P,
                                                                       const float *__restrict__ dy,
                                                                       const float *__restrict__ w,
                                                                       float *__restrict__ dx) {
