@@ -139,13 +139,18 @@ constexpr unsigned kBwdOutOfRange = 0x80000000u;
 // fused-layer shape, 1.17 -> 1.14 ms) and slower with 4 (the channel-heavy
 // shape, 3.52 -> 3.71 ms; 2 and 4 in flight lie between), where one is kept.
 template <int MT> constexpr int stage_depth() { return MT >= 4 ? 1 : 8; }
+// Four waves per SIMD for the matrix kernel: the 4-row-tile instantiation then
+// keeps its accumulators in AGPRs instead of holding 168 VGPRs (three waves);
+// channel-heavy shape 3.52 -> 3.36 ms, fused-layer shape unchanged, five no better.
+constexpr int kMfmaWavesPerSimd = 4;
 constexpr int kRowMaxT = 10; // 64-column steps of the one-axis kernel's dy window (640 columns)
 constexpr int kRowMinWgs = 2048;       // the one-axis kernel's grid, at least (8 per CU)
 constexpr int kRowMaxTilesPerWg = 8;
 constexpr int kRowCh = 4; // output channels per staged window chunk (a multiple of 4, <= 16)
 
 template <int MT, int PB>
-__global__ __launch_bounds__(kBwdBlock) void k_backward_data_mfma(const BwdParams P, const float *__restrict__ dy,
+__global__ __launch_bounds__(kBwdBlock, kMfmaWavesPerSimd) void k_backward_data_mfma(const BwdParams P,
+                                                                                      const float *__restrict__ dy,
                                                                   const float *__restrict__ w,
                                                                   float *__restrict__ dx) {
     const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
