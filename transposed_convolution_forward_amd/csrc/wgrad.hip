@@ -378,7 +378,7 @@ __global__ __launch_bounds__(kWgBlock) void k_backward_weight_row(const WrParams
         }
         __syncthreads();
         // wave: output-channel tile `wave`, both input-channel tiles, every tap
-#pragma unroll 2
+#pragma unroll
         for (int q = 0; q < kWlTile / 4; ++q) {
             const int pp = 4 * q + c4;
             const float a0 = As[pp * kWlApitch + i16];
