@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kWgBlock) void k_backward_weight_lds(const WlParams
             }
             __syncthreads();
             // wave: output-channel tile `wave`, both input-channel tiles
-#pragma unroll 4
+#pragma unroll
             for (int q = 0; q < kWlTile / 4; ++q) {
                 const int pp = 4 * q + c4;
                 const float b = Bs[pp * kWlBpitch + 16 * wave + i16];
