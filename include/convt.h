@@ -75,8 +75,9 @@ typedef struct convt_plan convt_plan; /* opaque */
  * stride >= 1, dilation >= 1, pad >= 0, out_pad >= 0, and L_out >= 1 by the
  * closed form.  Any out_pad >= 0 is accepted (the pages state no upper
  * bound).  Limits (else CONVT_ERR_UNSUPPORTED): K <= 32 and stride <= 32 per
- * axis, every tensor below 2^31 elements per batch sample and below 2^40
- * elements in total.  Host-only: makes no HIP call.  On success *plan owns a
+ * axis, the uncropped length (L_in - 1)*s + d*(K - 1) + out_pad + 1 below
+ * 2^31 per axis, every tensor below 2^31 elements per batch sample and below
+ * 2^40 elements in total.  Host-only: makes no HIP call.  On success *plan owns a
  * heap object released by convt_plan_destroy.
  */
 CONVT_API convt_status convt_plan_create(convt_plan **plan, int ndim, int64_t N, int64_t C_in,

@@ -66,6 +66,11 @@ def _create(ndim=1, N=1, C_in=2, C_out=2, groups=1, in_size=(4,), K=(3,), s=(2,)
     (dict(K=(33,)), T.CONVT_ERR_UNSUPPORTED),
     (dict(s=(33,)), T.CONVT_ERR_UNSUPPORTED),
     (dict(in_size=(1 << 31,)), T.CONVT_ERR_UNSUPPORTED),
+    # a huge dilation cancelled by a huge padding: L_out = 3, but the
+    # uncropped length 2*(2^31 - 1) + 1 overflows the kernels' int indices
+    (dict(K=(3,), d=((1 << 31) - 1,), p=((1 << 31) - 1,), in_size=(2,), s=(1,)), T.CONVT_ERR_UNSUPPORTED),
+    # the same uncropped length just within the limit is accepted
+    (dict(K=(3,), d=((1 << 30) - 2,), p=((1 << 30) - 2,), in_size=(2,), s=(1,)), T.CONVT_OK),
 ])
 def test_plan_create_validation(kw, status):
     assert _create(**kw) == status
@@ -175,6 +180,12 @@ def test_gradient_kernel_routing():
     # apply; the weight gradient's channel blocks do not
     p = T.Plan(1, 2, 16, 4, 1, (1000,), (3,), (2,), (1,), (0,), (2,))
     assert _gradient_kernels(p) == ("k_backward_data_mfma_row", "k_backward_weight")
+    # a 2D plan whose leading axis has one input and one tap but a padding
+    # that drops that tap (L_out = 1) or more than one output: the window
+    # kernels index only the last axis, so neither may take it
+    for lead_p, lead_op in ((1, 2), (0, 2)):
+        p = T.Plan(2, 2, 32, 64, 1, (1, 1000), (1, 3), (3, 2), (lead_p, 1), (lead_op, 0), (1, 2))
+        assert _gradient_kernels(p) == ("k_backward_data_mfma", "k_backward_weight_lds"), (lead_p, lead_op)
 
 
 def test_phase_table_description():

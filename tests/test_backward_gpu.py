@@ -79,3 +79,19 @@ ROW_TILES = [
 def test_backward_row_multitile(wl):
     assert "input gradient: kernel=k_backward_data_mfma_row" in T.convt_plan_describe(T.plan_for(wl))
     _check(wl)
+
+
+# 2D shapes whose leading axis has one input position and one tap, with a
+# padding that drops that tap (p = 1, out_pad 2: one output, no contribution,
+# so the gradients of x and w are zero) or leaves it at output 0 of three
+# (p = 0, out_pad 2).  They must not take the one-axis window kernels.
+LEADING_UNIT_AXIS = [
+    S.Workload("lead_unit_p1_op2", 2, 2, 32, 64, 1, (1, 1000), (1, 3), (3, 2), (1, 1), (2, 0), (1, 2), True, False, 61),
+    S.Workload("lead_unit_p0_op2", 2, 2, 32, 64, 1, (1, 1000), (1, 3), (3, 2), (0, 1), (2, 0), (1, 2), True, False, 62),
+]
+
+
+@pytest.mark.parametrize("wl", LEADING_UNIT_AXIS, ids=lambda w: w.name)
+def test_backward_leading_unit_axis(wl):
+    assert "_row" not in T.convt_plan_describe(T.plan_for(wl))
+    _check(wl)

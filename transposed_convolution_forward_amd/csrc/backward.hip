@@ -496,7 +496,10 @@ int launch_mfma(const convt_plan &Pl, BwdParams &P, const float *dy, const float
 // odd, so the rows one MFMA operand reads start on different banks.
 bool row_window(const convt_plan &Pl, int mt, BwdParams &P) {
     if (mt == 0 || Pl.Cog % kRowCh != 0) return false;
-    if (Pl.ax[0].L_in != 1 || Pl.ax[1].L_in != 1 || Pl.ax[0].K != 1 || Pl.ax[1].K != 1) return false;
+    // A leading axis must be a unit axis whose one tap lands on its one output
+    // (p = 0 and L_out = 1): the window kernels index only the last axis.
+    for (int a = 0; a < 2; ++a)
+        if (Pl.ax[a].L_in != 1 || Pl.ax[a].K != 1 || Pl.ax[a].p != 0 || Pl.ax[a].L_out != 1) return false;
     const AxisPlan &A = Pl.ax[2];
     const int cs = A.d % A.s == 0 ? A.s : 1;
     const int64_t wn = (int64_t)(64 * kBwdPB - 1) * (A.s / cs) + (int64_t)(A.K - 1) * (A.d / cs) + 1;

@@ -105,6 +105,11 @@ convt_status convt_plan_create(convt_plan **plan, int ndim, int64_t N, int64_t C
             dilation[a] > kMaxAxisParam)
             return CONVT_ERR_UNSUPPORTED;
         if (K[a] > convt::kMaxK || stride[a] > convt::kMaxStride) return CONVT_ERR_UNSUPPORTED;
+        // The uncropped scatter length (L_in - 1)*s + d*(K - 1) + out_pad + 1
+        // bounds every index i*s - p + k*d the kernels form in int; a large
+        // padding can cancel it in the closed form, so it is bounded itself.
+        if ((in_size[a] - 1) * stride[a] + dilation[a] * (K[a] - 1) + out_pad[a] + 1 > kMaxAxisParam)
+            return CONVT_ERR_UNSUPPORTED;
     }
     if (N > kMaxAxisParam || C_in > kMaxAxisParam || C_out > kMaxAxisParam)
         return CONVT_ERR_UNSUPPORTED;

@@ -414,7 +414,10 @@ __global__ __launch_bounds__(kWgBlock) void k_backward_weight_row(const WrParams
 // window fields of R and returns true when it applies.
 bool weight_row_window(const convt_plan &Pl, WrParams &R) {
     if (Pl.Cig % 32 != 0 || Pl.Cog % 64 != 0) return false;
-    if (Pl.ax[0].L_in != 1 || Pl.ax[1].L_in != 1 || Pl.ax[0].K != 1 || Pl.ax[1].K != 1) return false;
+    // A leading axis must be a unit axis whose one tap lands on its one output
+    // (p = 0 and L_out = 1): the window kernels index only the last axis.
+    for (int a = 0; a < 2; ++a)
+        if (Pl.ax[a].L_in != 1 || Pl.ax[a].K != 1 || Pl.ax[a].p != 0 || Pl.ax[a].L_out != 1) return false;
     const AxisPlan &A = Pl.ax[2];
     const int cs = A.d % A.s == 0 ? A.s : 1;
     const int tk = Pl.k_vol < kWlTaps ? (int)Pl.k_vol : kWlTaps;

@@ -74,6 +74,14 @@ def uniform(shape: Sequence[int], bound: float, seed: int, wid: int, tensor_id: 
     return ((u * np.float32(2.0) - np.float32(1.0)) * np.float32(bound)).astype(np.float32)
 
 
+def small_integers(shape: Sequence[int], bound: int, seed: int, wid: int, tensor_id: int) -> np.ndarray:
+    """Integers drawn uniformly from [-bound, bound], as float32.  Sums of
+    products of such values stay exact in fp32 while below 2^24, so a result
+    computed from them does not depend on the order of its additions."""
+    v = _rng(seed, wid, tensor_id).integers(-bound, bound + 1, size=tuple(shape))
+    return v.astype(np.float32)
+
+
 def make_inputs(wl: Workload, seed: int = 0, out_shape: Optional[Sequence[int]] = None):
     """Return dict(x, w, bias|None, add|None) of float32 arrays.
 
