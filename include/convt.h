@@ -65,6 +65,17 @@ typedef enum {
     CONVT_PATH_IGEMM3D = 3   /* per-phase implicit GEMM on MFMA for 3D */
 } convt_path;
 
+/*
+ * Activations of the selectable epilogue ("Kimi-K2.6 l2_p26" transcript,
+ * ConvTranspose3d + add + HardSwish: its statement of hardswish and of the
+ * forward, which multiplies the sum by its hardswish).
+ */
+typedef enum {
+    CONVT_ACT_NONE = 0,       /* y = t */
+    CONVT_ACT_HARDSWISH = 1,  /* y = hardswish(t) = t * min(max(t + 3, 0), 6) / 6 */
+    CONVT_ACT_X_HARDSWISH = 2 /* y = t * hardswish(t) */
+} convt_activation;
+
 typedef struct convt_plan convt_plan; /* opaque */
 
 /*
@@ -107,6 +118,22 @@ CONVT_API convt_status convt_forward(const convt_plan *plan, const float *x, con
 CONVT_API convt_status convt_forward_add_hswish(const convt_plan *plan, const float *x, const float *w,
                                       const float *bias, const float *add_input, float *y,
                                       void *stream);
+
+/*
+ * Forward with a selectable epilogue, computed in registers before the one
+ * store of each output element:
+ *   t = conv_transpose(x, w) + bias [+ add_input]
+ *   y = t, hardswish(t) or t * hardswish(t)   (activation, see above)
+ * bias may be NULL (no bias); add_input may be NULL (no residual add) and may
+ * equal y (in place).  convt_forward is this call with add_input NULL and
+ * CONVT_ACT_NONE; convt_forward_add_hswish with add_input and
+ * CONVT_ACT_X_HARDSWISH.  Every path runs every mode.  Errors as
+ * convt_forward, and CONVT_ERR_INVALID_ARG for an activation outside the
+ * enum.
+ */
+CONVT_API convt_status convt_forward_epilogue(const convt_plan *plan, const float *x, const float *w,
+                                              const float *bias, const float *add_input, int activation,
+                                              float *y, void *stream);
 
 /*
  * Input gradient: dx = the adjoint of the forward's linear part applied to dy

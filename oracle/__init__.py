@@ -60,6 +60,13 @@ class Oracle:
         lib.oracle_convt_forward.restype = ctypes.c_int
         lib.oracle_convt_points.argtypes = conv_args + [_i64p, ctypes.c_int64, _f64p]
         lib.oracle_convt_points.restype = ctypes.c_int
+        lib.oracle_convt_forward_ex.argtypes = conv_args + [ctypes.c_int, ctypes.c_int, _f64p, ctypes.c_int]
+        lib.oracle_convt_forward_ex.restype = ctypes.c_int
+        lib.oracle_convt_points_ex.argtypes = conv_args + [ctypes.c_int, ctypes.c_int, _i64p, ctypes.c_int64,
+                                                           _f64p]
+        lib.oracle_convt_points_ex.restype = ctypes.c_int
+        lib.oracle_activate.argtypes = [_f64p, _f64p, ctypes.c_int64, ctypes.c_int]
+        lib.oracle_activate.restype = None
         lib.oracle_axis_pair_counts.argtypes = [ctypes.c_int64] * 6 + [_i64p]
         lib.oracle_axis_pair_counts.restype = ctypes.c_int
         lib.oracle_times_hardswish.argtypes = [_f64p, _f64p, ctypes.c_int64]
@@ -93,26 +100,36 @@ class Oracle:
 
     # -- values -----------------------------------------------------------
     def forward(self, *, ndim, N, C_in, C_out, groups, in_size, K, stride, pad, out_pad, dilation,
-                x, w, bias=None, add=None, nthreads: int = 0) -> np.ndarray:
-        """Whole output as float64, shape (N, C_out, *L_out)."""
+                x, w, bias=None, add=None, act=None, layout=0, nthreads: int = 0) -> np.ndarray:
+        """Whole output as float64, shape (N, C_out, *L_out) for layout 0
+        (channels first) or (N, *L_out, C_out) for layout 1 (channels last),
+        x and add in the same layout.  act: 0 none, 1 hardswish, 2 t *
+        hardswish(t); None means 2 with add and 0 without (the two forwards
+        of the pages)."""
         out_size = self.output_size(ndim, in_size, K, stride, pad, out_pad, dilation)
-        y = np.empty((N, C_out) + out_size, dtype=np.float64)
-        rc = self.lib.oracle_convt_forward(
+        if act is None:
+            act = 2 if add is not None else 0
+        shape = (N,) + out_size + (C_out,) if layout else (N, C_out) + out_size
+        y = np.empty(shape, dtype=np.float64)
+        rc = self.lib.oracle_convt_forward_ex(
             ndim, N, C_in, C_out, groups, _arr(in_size), _arr(K), _arr(stride), _arr(pad),
-            _arr(out_pad), _arr(dilation), _f32(x), _f32(w), _f32(bias), _f32(add),
+            _arr(out_pad), _arr(dilation), _f32(x), _f32(w), _f32(bias), _f32(add), int(act), int(layout),
             y.ctypes.data_as(_f64p), int(nthreads))
         if rc:
             raise ValueError("bad arguments")
         return y
 
     def points(self, idx: np.ndarray, *, ndim, N, C_in, C_out, groups, in_size, K, stride, pad,
-               out_pad, dilation, x, w, bias=None, add=None) -> np.ndarray:
-        """Output values at flat indices idx, computed one by one, float64."""
+               out_pad, dilation, x, w, bias=None, add=None, act=None, layout=0) -> np.ndarray:
+        """Output values at flat indices idx (of the layout's output shape),
+        computed one by one, float64; act and layout as forward()."""
         idx = np.ascontiguousarray(idx, dtype=np.int64)
         out = np.empty(idx.shape, dtype=np.float64)
-        rc = self.lib.oracle_convt_points(
+        if act is None:
+            act = 2 if add is not None else 0
+        rc = self.lib.oracle_convt_points_ex(
             ndim, N, C_in, C_out, groups, _arr(in_size), _arr(K), _arr(stride), _arr(pad),
-            _arr(out_pad), _arr(dilation), _f32(x), _f32(w), _f32(bias), _f32(add),
+            _arr(out_pad), _arr(dilation), _f32(x), _f32(w), _f32(bias), _f32(add), int(act), int(layout),
             idx.ctypes.data_as(_i64p), idx.size, out.ctypes.data_as(_f64p))
         if rc:
             raise ValueError("bad arguments")
@@ -142,6 +159,12 @@ class Oracle:
         if rc:
             raise ValueError("bad arguments")
         return dw, db
+
+    def activate(self, t: np.ndarray, act: int) -> np.ndarray:
+        t = np.ascontiguousarray(t, dtype=np.float64)
+        out = np.empty_like(t)
+        self.lib.oracle_activate(t.ctypes.data_as(_f64p), out.ctypes.data_as(_f64p), t.size, int(act))
+        return out
 
     def times_hardswish(self, t: np.ndarray) -> np.ndarray:
         t = np.ascontiguousarray(t, dtype=np.float64)

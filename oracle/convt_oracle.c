@@ -29,6 +29,15 @@
  *   HardSwish, its statement of the forward and of hardswish):
  *     t = conv_transpose(x) + bias + add_input
  *     y = t * hardswish(t),  hardswish(t) = t * min(max(t + 3, 0), 6) / 6
+ *   The selectable epilogue takes the parts of that forward singly or
+ *   together: the add of add_input or not, then y = t, hardswish(t) or
+ *   t * hardswish(t) (act 0, 1, 2).
+ *
+ *   Layouts: channels first (layout 0: x (N, C_in, L_in...), y and add_input
+ *   (N, C_out, L_out...)) or channels last (layout 1: x (N, L_in..., C_in),
+ *   y and add_input (N, L_out..., C_out)); the weight is (C_in, C_out/G, K...)
+ *   in both.  The layout changes where each element sits, nothing of the
+ *   arithmetic.
  *
  * Readings taken where the pages leave a point open: output_padding only
  * lengthens the output at the high end and those positions receive whatever
@@ -96,18 +105,40 @@ static int set_problem(problem *P, int ndim, int64_t N, int64_t C_in, int64_t C_
     return 0;
 }
 
-/* y = t * hardswish(t) with hardswish(t) = t * clamp(t + 3, 0, 6) / 6. */
-static double times_hardswish(double t)
+/* hardswish(t) = t * clamp(t + 3, 0, 6) / 6. */
+static double hardswish(double t)
 {
     double r = t + 3.0;
     if (r < 0.0) r = 0.0;
     if (r > 6.0) r = 6.0;
-    return t * (t * r / 6.0);
+    return t * r / 6.0;
+}
+
+/* The fused forward's epilogue: t * hardswish(t). */
+static double times_hardswish(double t)
+{
+    return t * hardswish(t);
+}
+
+/* Activation act: 0 none, 1 hardswish, 2 t * hardswish(t). */
+static double activate(double t, int act)
+{
+    if (act == 1) return hardswish(t);
+    if (act == 2) return times_hardswish(t);
+    return t;
+}
+
+/* Flat index of element (n, c, e) (e the flat spatial position, sp of them
+ * per channel, C channels) in layout 0 (channels first) or 1 (channels last). */
+static int64_t at(int layout, int64_t n, int64_t c, int64_t e, int64_t C, int64_t sp)
+{
+    return layout ? (n * sp + e) * C + c : (n * C + c) * sp + e;
 }
 
 typedef struct {
     const problem *P;
     const float *x, *w, *bias, *add;
+    int act, layout;
     double *y;
     int64_t next_slab, n_slabs;
     pthread_mutex_t lock;
@@ -123,8 +154,14 @@ static void scatter_slab(const scatter_job *J, int64_t n, int64_t g)
     const int64_t KD = P->K[0], KH = P->K[1], KW = P->K[2];
     const int64_t in_sp = ID * IH * IW, out_sp = OD * OH * OW, k_sp = KD * KH * KW;
 
-    /* slab[co_l][od][oh][ow], starting from the bias */
-    double *slab = J->y + (n * P->C_out + g * Cog) * out_sp;
+    /* slab[co_l][od][oh][ow], starting from the bias: in y itself for
+     * channels first, else in a scratch slab written out at the end */
+    double *own = NULL;
+    if (J->layout) {
+        own = (double *)malloc(sizeof(double) * (size_t)(Cog * out_sp));
+        if (!own) abort();
+    }
+    double *slab = J->layout ? own : J->y + (n * P->C_out + g * Cog) * out_sp;
     for (int64_t co_l = 0; co_l < Cog; ++co_l) {
         double b = J->bias ? (double)J->bias[g * Cog + co_l] : 0.0;
         for (int64_t e = 0; e < out_sp; ++e) slab[co_l * out_sp + e] = b;
@@ -132,12 +169,13 @@ static void scatter_slab(const scatter_job *J, int64_t n, int64_t g)
 
     for (int64_t ci_l = 0; ci_l < Cig; ++ci_l) {
         const int64_t ci = g * Cig + ci_l;
-        const float *xc = J->x + (n * P->C_in + ci) * in_sp;
+        const float *xc = J->x + at(J->layout, n, ci, 0, P->C_in, in_sp);
+        const int64_t xs = J->layout ? P->C_in : 1; /* step between positions */
         const float *wc = J->w + ci * Cog * k_sp;
         for (int64_t id = 0; id < ID; ++id)
         for (int64_t ih = 0; ih < IH; ++ih)
         for (int64_t iw = 0; iw < IW; ++iw) {
-            const double xv = (double)xc[(id * IH + ih) * IW + iw];
+            const double xv = (double)xc[((id * IH + ih) * IW + iw) * xs];
             for (int64_t co_l = 0; co_l < Cog; ++co_l)
             for (int64_t kd = 0; kd < KD; ++kd) {
                 const int64_t od = id * P->s[0] - P->p[0] + kd * P->d[0];
@@ -156,11 +194,16 @@ static void scatter_slab(const scatter_job *J, int64_t n, int64_t g)
         }
     }
 
-    if (J->add) {
-        const float *ad = J->add + (n * P->C_out + g * Cog) * out_sp;
-        for (int64_t e = 0; e < Cog * out_sp; ++e)
-            slab[e] = times_hardswish(slab[e] + (double)ad[e]);
-    }
+    /* epilogue: t = slab (+ add_input), then the activation, stored at the
+     * element's place in the layout */
+    for (int64_t co_l = 0; co_l < Cog; ++co_l)
+        for (int64_t e = 0; e < out_sp; ++e) {
+            const int64_t yi = at(J->layout, n, g * Cog + co_l, e, P->C_out, out_sp);
+            double t = slab[co_l * out_sp + e];
+            if (J->add) t += (double)J->add[yi];
+            J->y[yi] = activate(t, J->act);
+        }
+    free(own);
 }
 
 static void *scatter_worker(void *arg)
@@ -183,18 +226,21 @@ static int resolve_threads(int nthreads)
     return c > 0 ? (int)c : 1;
 }
 
-/* Full forward.  y has N*C_out*prod(L_out) doubles.  bias and add may be NULL
- * (add != NULL selects the fused epilogue).  Returns 0, or 1 on bad arguments. */
-int oracle_convt_forward(int ndim, int64_t N, int64_t C_in, int64_t C_out, int64_t G,
-                         const int64_t *in_size, const int64_t *K, const int64_t *s,
-                         const int64_t *p, const int64_t *op, const int64_t *d,
-                         const float *x, const float *w, const float *bias, const float *add,
-                         double *y, int nthreads)
+/* Full forward with the selectable epilogue and layout.  y has
+ * N*C_out*prod(L_out) doubles.  bias and add may be NULL.  act is 0, 1 or 2,
+ * layout 0 or 1.  Returns 0, or 1 on bad arguments. */
+int oracle_convt_forward_ex(int ndim, int64_t N, int64_t C_in, int64_t C_out, int64_t G,
+                            const int64_t *in_size, const int64_t *K, const int64_t *s,
+                            const int64_t *p, const int64_t *op, const int64_t *d,
+                            const float *x, const float *w, const float *bias, const float *add,
+                            int act, int layout, double *y, int nthreads)
 {
     problem P;
     if (set_problem(&P, ndim, N, C_in, C_out, G, in_size, K, s, p, op, d)) return 1;
+    if (act < 0 || act > 2 || layout < 0 || layout > 1) return 1;
     scatter_job J;
     J.P = &P; J.x = x; J.w = w; J.bias = bias; J.add = add; J.y = y;
+    J.act = act; J.layout = layout;
     J.next_slab = 0; J.n_slabs = N * G;
     pthread_mutex_init(&J.lock, NULL);
     int nt = resolve_threads(nthreads);
@@ -206,6 +252,18 @@ int oracle_convt_forward(int ndim, int64_t N, int64_t C_in, int64_t C_out, int64
     free(th);
     pthread_mutex_destroy(&J.lock);
     return 0;
+}
+
+/* Full forward, channels first: the plain forward, or with add != NULL the
+ * fused one (t * hardswish(t) of conv + bias + add). */
+int oracle_convt_forward(int ndim, int64_t N, int64_t C_in, int64_t C_out, int64_t G,
+                         const int64_t *in_size, const int64_t *K, const int64_t *s,
+                         const int64_t *p, const int64_t *op, const int64_t *d,
+                         const float *x, const float *w, const float *bias, const float *add,
+                         double *y, int nthreads)
+{
+    return oracle_convt_forward_ex(ndim, N, C_in, C_out, G, in_size, K, s, p, op, d, x, w, bias, add,
+                                   add ? 2 : 0, 0, y, nthreads);
 }
 
 /* The (i, k) pairs of one axis whose scatter lands on output position o:
@@ -238,17 +296,19 @@ int oracle_axis_pair_counts(int64_t L_in, int64_t K, int64_t s, int64_t p, int64
 }
 
 /* Selected outputs, one by one: idx holds flat indices into y (N, C_out,
- * L_out...).  Each value is the sum of the scatter contributions that land on
- * that element (per axis, every (i, k) pair is tried), plus bias, then the
- * fused epilogue if add != NULL.  Returns 0, or 1 on bad arguments. */
-int oracle_convt_points(int ndim, int64_t N, int64_t C_in, int64_t C_out, int64_t G,
-                        const int64_t *in_size, const int64_t *K, const int64_t *s,
-                        const int64_t *p, const int64_t *op, const int64_t *d,
-                        const float *x, const float *w, const float *bias, const float *add,
-                        const int64_t *idx, int64_t npts, double *out)
+ * L_out...) in the given layout.  Each value is the sum of the scatter
+ * contributions that land on that element (per axis, every (i, k) pair is
+ * tried), plus bias, plus add_input if add != NULL, then the activation act.
+ * Returns 0, or 1 on bad arguments. */
+int oracle_convt_points_ex(int ndim, int64_t N, int64_t C_in, int64_t C_out, int64_t G,
+                           const int64_t *in_size, const int64_t *K, const int64_t *s,
+                           const int64_t *p, const int64_t *op, const int64_t *d,
+                           const float *x, const float *w, const float *bias, const float *add,
+                           int act, int layout, const int64_t *idx, int64_t npts, double *out)
 {
     problem P;
     if (set_problem(&P, ndim, N, C_in, C_out, G, in_size, K, s, p, op, d)) return 1;
+    if (act < 0 || act > 2 || layout < 0 || layout > 1) return 1;
     const int64_t Cig = C_in / G, Cog = C_out / G;
     const int64_t in_sp = P.L_in[0] * P.L_in[1] * P.L_in[2];
     const int64_t out_sp = P.L_out[0] * P.L_out[1] * P.L_out[2];
@@ -264,11 +324,13 @@ int oracle_convt_points(int ndim, int64_t N, int64_t C_in, int64_t C_out, int64_
     for (int64_t t = 0; t < npts; ++t) {
         int64_t e = idx[t];
         if (e < 0 || e >= N * C_out * out_sp) { rc = 1; break; }
-        int64_t o[ORACLE_MAX_AXES];
+        int64_t o[ORACLE_MAX_AXES], co;
+        if (layout) { co = e % C_out; e /= C_out; }
         o[2] = e % P.L_out[2]; e /= P.L_out[2];
         o[1] = e % P.L_out[1]; e /= P.L_out[1];
         o[0] = e % P.L_out[0]; e /= P.L_out[0];
-        const int64_t co = e % C_out, n = e / C_out;
+        if (!layout) { co = e % C_out; e /= C_out; }
+        const int64_t n = e;
         const int64_t g = co / Cog, co_l = co % Cog;
         int64_t np[ORACLE_MAX_AXES];
         for (int a = 0; a < ORACLE_MAX_AXES; ++a)
@@ -276,27 +338,44 @@ int oracle_convt_points(int ndim, int64_t N, int64_t C_in, int64_t C_out, int64_
         double acc = bias ? (double)bias[co] : 0.0;
         for (int64_t ci_l = 0; ci_l < Cig; ++ci_l) {
             const int64_t ci = g * Cig + ci_l;
-            const float *xc = x + (n * C_in + ci) * in_sp;
             const float *wc = w + (ci * Cog + co_l) * k_sp;
             for (int64_t a0 = 0; a0 < np[0]; ++a0)
             for (int64_t a1 = 0; a1 < np[1]; ++a1)
             for (int64_t a2 = 0; a2 < np[2]; ++a2) {
-                double xv = (double)xc[(pi[0][a0] * P.L_in[1] + pi[1][a1]) * P.L_in[2] + pi[2][a2]];
+                const int64_t ie = (pi[0][a0] * P.L_in[1] + pi[1][a1]) * P.L_in[2] + pi[2][a2];
+                double xv = (double)x[at(layout, n, ci, ie, C_in, in_sp)];
                 double wv = (double)wc[(pk[0][a0] * P.K[1] + pk[1][a1]) * P.K[2] + pk[2][a2]];
                 acc += xv * wv;
             }
         }
-        if (add) acc = times_hardswish(acc + (double)add[idx[t]]);
-        out[t] = acc;
+        if (add) acc += (double)add[idx[t]];
+        out[t] = activate(acc, act);
     }
     for (int a = 0; a < ORACLE_MAX_AXES; ++a) { free(pi[a]); free(pk[a]); }
     return rc;
+}
+
+/* Channels-first points, plain or (add != NULL) fused. */
+int oracle_convt_points(int ndim, int64_t N, int64_t C_in, int64_t C_out, int64_t G,
+                        const int64_t *in_size, const int64_t *K, const int64_t *s,
+                        const int64_t *p, const int64_t *op, const int64_t *d,
+                        const float *x, const float *w, const float *bias, const float *add,
+                        const int64_t *idx, int64_t npts, double *out)
+{
+    return oracle_convt_points_ex(ndim, N, C_in, C_out, G, in_size, K, s, p, op, d, x, w, bias, add,
+                                  add ? 2 : 0, 0, idx, npts, out);
 }
 
 /* The fused epilogue alone, elementwise: out[e] = t * hardswish(t), t = in[e]. */
 void oracle_times_hardswish(const double *in, double *out, int64_t n)
 {
     for (int64_t e = 0; e < n; ++e) out[e] = times_hardswish(in[e]);
+}
+
+/* An activation alone, elementwise: out[e] = activation act of in[e]. */
+void oracle_activate(const double *in, double *out, int64_t n, int act)
+{
+    for (int64_t e = 0; e < n; ++e) out[e] = activate(in[e], act);
 }
 
 /* ---------------------------------------------------------------------------

@@ -231,6 +231,69 @@ def pin_fused_forward(orc):
     np.testing.assert_allclose(y1, t * t * (t + 3.0) / 6.0, rtol=1e-11, atol=1e-12)
 
 
+def pin_activation_values(orc):
+    """hardswish(t) = t*clamp(t+3,0,6)/6 ("Kimi-K2.6 l2_p26" transcript, its
+    statement of hardswish) at values with closed forms; act 0 is the
+    identity and act 2 is t*hardswish(t) (the values of pin_epilogue_values)."""
+    t = np.array([-4.0, -3.0, -1.0, 0.0, 1.0, 3.0, 6.0, 10.0, -2.5, 1.5])
+    want = np.array([0.0, 0.0, -1.0 / 3.0, 0.0, 2.0 / 3.0, 3.0, 6.0, 10.0, -2.5 * 0.5 / 6.0, 1.5 * 4.5 / 6.0])
+    np.testing.assert_allclose(orc.activate(t, 1), want, rtol=1e-15, atol=1e-15)
+    np.testing.assert_array_equal(orc.activate(t, 0), t)
+    np.testing.assert_allclose(orc.activate(t, 2), t * want, rtol=1e-15, atol=1e-15)
+
+
+def pin_epilogue_modes(orc):
+    """Every epilogue mode is the plain forward (conv + bias), plus add_input
+    when given, then the activation, elementwise; in the region -3 < t < 3
+    hardswish is t*(t+3)/6, checked against the second derivation."""
+    for ci, case in enumerate(tiny_cases()[:5]):
+        nd, N, Cin, Cout, G, ins, K, s, p, op, d = case
+        x, w, b = _case_arrays(case, 1500 + ci)
+        kw = dict(ndim=nd, N=N, C_in=Cin, C_out=Cout, groups=G, in_size=ins, K=K, stride=s, pad=p,
+                  out_pad=op, dilation=d, x=x, w=w, bias=b)
+        y0 = orc.forward(**kw)
+        add = (3 * np.random.default_rng(1600 + ci).standard_normal(size=y0.shape)).astype(np.float32)
+        for act in (0, 1, 2):
+            np.testing.assert_allclose(orc.forward(act=act, **kw), orc.activate(y0, act), rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(orc.forward(add=add, act=act, **kw),
+                                       orc.activate(y0 + add.astype(np.float64), act), rtol=1e-12, atol=1e-12)
+    case = tiny_cases()[1]
+    nd, N, Cin, Cout, G, ins, K, s, p, op, d = case
+    x, w, b = _case_arrays(case, 1700)
+    x *= np.float32(0.1)
+    t = dilate_flip_correlate(x, w, b, groups=G, stride=s, pad=p, out_pad=op, dilation=d)
+    assert np.all(np.abs(t) < 3)
+    y1 = orc.forward(ndim=nd, N=N, C_in=Cin, C_out=Cout, groups=G, in_size=ins, K=K, stride=s, pad=p,
+                     out_pad=op, dilation=d, x=x, w=w, bias=b, act=1)
+    np.testing.assert_allclose(y1, t * (t + 3.0) / 6.0, rtol=1e-11, atol=1e-12)
+
+
+def _to_last(a):
+    return np.ascontiguousarray(np.moveaxis(a, 1, -1))
+
+
+def pin_channels_last(orc):
+    """Channels last (x (N, L..., C_in), y and add (N, L..., C_out)) holds the
+    same values as channels first, moved: the layout places elements and
+    changes no arithmetic.  The one-by-one evaluation agrees in that layout."""
+    for ci, case in enumerate(tiny_cases()):
+        nd, N, Cin, Cout, G, ins, K, s, p, op, d = case
+        x, w, b = _case_arrays(case, 1800 + ci)
+        kw = dict(ndim=nd, N=N, C_in=Cin, C_out=Cout, groups=G, in_size=ins, K=K, stride=s, pad=p,
+                  out_pad=op, dilation=d, w=w, bias=b)
+        y0 = orc.forward(x=x, **kw)
+        add = np.random.default_rng(1900 + ci).standard_normal(size=y0.shape).astype(np.float32)
+        for a, act in ((None, 0), (add, 2), (add, 1)):
+            ref = orc.forward(x=x, add=a, act=act, **kw)
+            a_l = None if a is None else _to_last(a)
+            got = orc.forward(x=_to_last(x), add=a_l, act=act, layout=1, **kw)
+            assert got.shape == (N,) + ref.shape[2:] + (Cout,)
+            np.testing.assert_array_equal(got, np.moveaxis(ref, 1, -1))
+            idx = np.arange(got.size, dtype=np.int64)
+            np.testing.assert_allclose(orc.points(idx, x=_to_last(x), add=a_l, act=act, layout=1, **kw),
+                                       got.ravel(), rtol=1e-12, atol=1e-12)
+
+
 def pin_points_match_forward(orc):
     """The one-by-one evaluation (used at full sizes) equals the full forward,
     fused and not, on every element of the tiny cases."""
@@ -347,6 +410,7 @@ def pin_wgrad_adjoint(orc):
 
 ALL_PINS = [pin_closed_form_pages, pin_worked_examples, pin_numpy_convolve, pin_odd_only,
             pin_tap_counts, pin_adjoint, pin_dilate_flip_correlate, pin_group_decomposition,
-            pin_epilogue_values, pin_fused_forward, pin_points_match_forward,
+            pin_epilogue_values, pin_fused_forward, pin_activation_values, pin_epilogue_modes,
+            pin_channels_last, pin_points_match_forward,
             pin_backward_worked_examples, pin_backward_gather, pin_backward_adjoint,
             pin_wgrad_worked_examples, pin_wgrad_adjoint]

@@ -86,6 +86,7 @@ def test_null_arguments():
     assert L.convt_plan_output_size(None, arr) == T.CONVT_ERR_INVALID_ARG
     assert L.convt_forward(None, None, None, None, None, None) == T.CONVT_ERR_INVALID_ARG
     assert L.convt_forward_add_hswish(None, None, None, None, None, None, None) == T.CONVT_ERR_INVALID_ARG
+    assert L.convt_forward_epilogue(None, None, None, None, None, 0, None, None) == T.CONVT_ERR_INVALID_ARG
     assert L.convt_backward_data(None, None, None, None, None) == T.CONVT_ERR_INVALID_ARG
     assert L.convt_backward_weight(None, None, None, None, None, None) == T.CONVT_ERR_INVALID_ARG
     assert L.convt_plan_set_path(None, 0) == T.CONVT_ERR_INVALID_ARG
@@ -100,6 +101,11 @@ def test_forward_rejects_null_tensors_without_launch():
     assert L.convt_forward(p.handle, fake, None, None, fake, None) == T.CONVT_ERR_INVALID_ARG
     assert L.convt_forward(p.handle, fake, fake, None, None, None) == T.CONVT_ERR_INVALID_ARG
     assert L.convt_forward_add_hswish(p.handle, fake, fake, None, None, fake, None) == T.CONVT_ERR_INVALID_ARG
+    # the selectable epilogue: NULL x, w or y, or an activation outside the enum
+    assert L.convt_forward_epilogue(p.handle, None, fake, None, None, 0, fake, None) == T.CONVT_ERR_INVALID_ARG
+    assert L.convt_forward_epilogue(p.handle, fake, fake, None, None, 0, None, None) == T.CONVT_ERR_INVALID_ARG
+    for bad in (-1, 3, 99):
+        assert L.convt_forward_epilogue(p.handle, fake, fake, None, None, bad, fake, None) == T.CONVT_ERR_INVALID_ARG
 
 
 def test_status_strings():

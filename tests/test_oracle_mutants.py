@@ -32,10 +32,26 @@ MUTATIONS = {
     "weight_transposed": ("const double wv = (double)wc[co_l * k_sp + (kd * KH + kh) * KW + kw];",
                           "const double wv = (double)J->w[((g * Cog + co_l) * Cig + ci_l) * k_sp"
                           " + (kd * KH + kh) * KW + kw];"),
-    "epilogue_plain_hardswish": ("return t * (t * r / 6.0);", "return t * r / 6.0;"),
+    "epilogue_plain_hardswish": ("return t * hardswish(t);", "return hardswish(t);"),
     "epilogue_no_upper_clamp": ("if (r > 6.0) r = 6.0;", ""),
-    "epilogue_add_dropped": ("slab[e] = times_hardswish(slab[e] + (double)ad[e]);",
-                             "slab[e] = times_hardswish(slab[e]);"),
+    "epilogue_add_dropped": ("            if (J->add) t += (double)J->add[yi];\n", ""),
+    # selectable epilogue
+    "hardswish_scale": ("return t * r / 6.0;", "return t * r / 3.0;"),
+    "act_modes_swapped": ("if (act == 1) return hardswish(t);", "if (act == 1) return times_hardswish(t);"),
+    "act_before_add": ("            if (J->add) t += (double)J->add[yi];\n            J->y[yi] = activate(t, J->act);",
+                       "            t = activate(t, J->act);\n            if (J->add) t += (double)J->add[yi];\n"
+                       "            J->y[yi] = t;"),
+    "points_act_dropped": ("        out[t] = activate(acc, act);", "        out[t] = acc;"),
+    # channels last
+    "channels_last_x_stride": ("const int64_t xs = J->layout ? P->C_in : 1;", "const int64_t xs = 1;"),
+    "channels_last_y_index": ("return layout ? (n * sp + e) * C + c : (n * C + c) * sp + e;",
+                              "return layout ? (n * sp + e) * C + (C - 1 - c) : (n * C + c) * sp + e;"),
+    "points_channels_last_decoded_first": (
+        "        if (layout) { co = e % C_out; e /= C_out; }\n        o[2] = e % P.L_out[2]; e /= P.L_out[2];\n"
+        "        o[1] = e % P.L_out[1]; e /= P.L_out[1];\n        o[0] = e % P.L_out[0]; e /= P.L_out[0];\n"
+        "        if (!layout) { co = e % C_out; e /= C_out; }",
+        "        o[2] = e % P.L_out[2]; e /= P.L_out[2];\n        o[1] = e % P.L_out[1]; e /= P.L_out[1];\n"
+        "        o[0] = e % P.L_out[0]; e /= P.L_out[0];\n        co = e % C_out; e /= C_out;"),
     "points_pad_sign": ("if (i * s - p + k * d == o)", "if (i * s + p + k * d == o)"),
     # input gradient
     "bwd_pad_sign_w": ("iw * P->s[2] + kw * P->d[2] - P->p[2]", "iw * P->s[2] + kw * P->d[2] + P->p[2]"),

@@ -16,11 +16,12 @@ LIB_PATH = os.path.join(_HERE, "libconvt.so")
 
 CONVT_OK, CONVT_ERR_INVALID_ARG, CONVT_ERR_UNSUPPORTED, CONVT_ERR_HIP, CONVT_ERR_NOMEM = range(5)
 PATHS = {"auto": 0, "generic": 1, "stream1d": 2, "igemm3d": 3}
+ACTIVATIONS = {"none": 0, "hardswish": 1, "x_hardswish": 2}  # convt_activation
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 
 # Every symbol include/convt.h declares.
 EXPORTS = ("convt_plan_create", "convt_plan_output_size", "convt_forward",
-           "convt_forward_add_hswish", "convt_backward_data", "convt_backward_weight",
+           "convt_forward_add_hswish", "convt_forward_epilogue", "convt_backward_data", "convt_backward_weight",
            "convt_plan_destroy", "convt_status_string",
            "convt_plan_set_path", "convt_plan_get_path", "convt_plan_describe")
 
@@ -52,6 +53,8 @@ def lib() -> ctypes.CDLL:
     L.convt_forward.restype = ctypes.c_int
     L.convt_forward_add_hswish.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     L.convt_forward_add_hswish.restype = ctypes.c_int
+    L.convt_forward_epilogue.argtypes = [vp, vp, vp, vp, vp, ctypes.c_int, vp, vp]
+    L.convt_forward_epilogue.restype = ctypes.c_int
     L.convt_backward_data.argtypes = [vp, vp, vp, vp, vp]
     L.convt_backward_data.restype = ctypes.c_int
     L.convt_backward_weight.argtypes = [vp, vp, vp, vp, vp, vp]
@@ -172,6 +175,25 @@ def convt_forward_add_hswish(plan: Plan, x, w, bias, add_input, y=None, stream=N
     st = lib().convt_forward_add_hswish(plan.handle, *args, _stream_ptr(stream))
     if st != CONVT_OK:
         raise ConvtError(st, "convt_forward_add_hswish")
+    return y
+
+
+def convt_forward_epilogue(plan: Plan, x, w, bias=None, add_input=None, activation="none", y=None,
+                           stream=None):
+    """t = conv_transpose(x, w) + bias [+ add_input]; y = t, hardswish(t) or
+    t * hardswish(t) (activation "none", "hardswish" or "x_hardswish", or the
+    enum's integer)."""
+    import torch
+    act = ACTIVATIONS[activation] if isinstance(activation, str) else int(activation)
+    if y is None:
+        y = torch.empty(plan.y_shape(), dtype=torch.float32, device=x.device)
+    args = (_dev_ptr(x, plan.x_shape(), "x"), _dev_ptr(w, plan.w_shape(), "w"),
+            None if bias is None else _dev_ptr(bias, (plan.C_out,), "bias"),
+            None if add_input is None else _dev_ptr(add_input, plan.y_shape(), "add_input"))
+    st = lib().convt_forward_epilogue(plan.handle, *args, act, _dev_ptr(y, plan.y_shape(), "y"),
+                                      _stream_ptr(stream))
+    if st != CONVT_OK:
+        raise ConvtError(st, "convt_forward_epilogue")
     return y
 
 

@@ -70,12 +70,12 @@ const char *path_name(convt_path p) {
 }
 
 convt_status dispatch(const convt_plan *plan, const float *x, const float *w, const float *bias,
-                      const float *add, float *y, void *stream) {
+                      const float *add, int act, float *y, void *stream) {
     int e = 0;
     switch (plan->path) {
-    case CONVT_PATH_STREAM1D: e = convt::launch_stream1d(*plan, x, w, bias, add, y, stream); break;
-    case CONVT_PATH_IGEMM3D: e = convt::launch_igemm3d(*plan, x, w, bias, add, y, stream); break;
-    case CONVT_PATH_GENERIC: e = convt::launch_generic(*plan, x, w, bias, add, y, stream); break;
+    case CONVT_PATH_STREAM1D: e = convt::launch_stream1d(*plan, x, w, bias, add, act, y, stream); break;
+    case CONVT_PATH_IGEMM3D: e = convt::launch_igemm3d(*plan, x, w, bias, add, act, y, stream); break;
+    case CONVT_PATH_GENERIC: e = convt::launch_generic(*plan, x, w, bias, add, act, y, stream); break;
     default: return CONVT_ERR_UNSUPPORTED;
     }
     return e == 0 ? CONVT_OK : CONVT_ERR_HIP;
@@ -185,14 +185,23 @@ convt_status convt_plan_output_size(const convt_plan *plan, int64_t *out_size) {
 convt_status convt_forward(const convt_plan *plan, const float *x, const float *w,
                            const float *bias, float *y, void *stream) {
     if (!plan || !x || !w || !y) return CONVT_ERR_INVALID_ARG;
-    return dispatch(plan, x, w, bias, nullptr, y, stream);
+    return dispatch(plan, x, w, bias, nullptr, CONVT_ACT_NONE, y, stream);
 }
 
 convt_status convt_forward_add_hswish(const convt_plan *plan, const float *x, const float *w,
                                       const float *bias, const float *add_input, float *y,
                                       void *stream) {
     if (!plan || !x || !w || !y || !add_input) return CONVT_ERR_INVALID_ARG;
-    return dispatch(plan, x, w, bias, add_input, y, stream);
+    return dispatch(plan, x, w, bias, add_input, CONVT_ACT_X_HARDSWISH, y, stream);
+}
+
+convt_status convt_forward_epilogue(const convt_plan *plan, const float *x, const float *w,
+                                    const float *bias, const float *add_input, int activation, float *y,
+                                    void *stream) {
+    if (!plan || !x || !w || !y) return CONVT_ERR_INVALID_ARG;
+    if (activation != CONVT_ACT_NONE && activation != CONVT_ACT_HARDSWISH && activation != CONVT_ACT_X_HARDSWISH)
+        return CONVT_ERR_INVALID_ARG;
+    return dispatch(plan, x, w, bias, add_input, activation, y, stream);
 }
 
 convt_status convt_backward_data(const convt_plan *plan, const float *dy, const float *w, float *dx,

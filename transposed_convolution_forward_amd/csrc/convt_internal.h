@@ -45,23 +45,25 @@ struct convt_plan {
 
 namespace convt {
 
-// Kernel launchers, one per path.  add != nullptr selects the fused epilogue.
-// Each returns hipSuccess or the launch error (as int, to keep HIP types out).
+// Kernel launchers, one per path.  The epilogue is t = acc + bias, plus
+// add_input when add != nullptr, then the activation act (kActNone,
+// kActHardswish or kActXHardswish, epilogue.hpp).  Each returns hipSuccess or
+// the launch error (as int, to keep HIP types out).
 bool generic_supports(const convt_plan &P);
 // Name of the kernel launch_generic runs for P (phase-class variant when the
 // shape has at most 32 phase classes).
 const char *generic_kernel_name(const convt_plan &P);
 int launch_generic(const convt_plan &P, const float *x, const float *w, const float *bias,
-                   const float *add, float *y, void *stream);
+                   const float *add, int act, float *y, void *stream);
 
 bool stream1d_supports(const convt_plan &P);
 int launch_stream1d(const convt_plan &P, const float *x, const float *w, const float *bias,
-                    const float *add, float *y, void *stream);
+                    const float *add, int act, float *y, void *stream);
 
 bool igemm3d_supports(const convt_plan &P);
 // Name of the kernel launch_igemm3d runs for P (weights in VGPRs or streamed).
 const char *igemm3d_kernel_name(const convt_plan &P);
 int launch_igemm3d(const convt_plan &P, const float *x, const float *w, const float *bias,
-                   const float *add, float *y, void *stream);
+                   const float *add, int act, float *y, void *stream);
 
 } // namespace convt

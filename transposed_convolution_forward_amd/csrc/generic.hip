@@ -29,7 +29,7 @@ struct GenericParams {
     int n0; // first batch index of this launch
 };
 
-template <int CPT, bool FUSED>
+template <int CPT, int EPI>
 __global__ __launch_bounds__(kBlock) void k_generic(const GenericParams P,
                                                     const float *__restrict__ x,
                                                     const float *__restrict__ w,
@@ -89,8 +89,8 @@ __global__ __launch_bounds__(kBlock) void k_generic(const GenericParams P,
         const int co = g * P.Cog + co0 + j;
         const int64_t idx = ((int64_t)n * P.C_out + co) * P.out_sp + sp;
         const float b = bias ? bias[co] : 0.0f;
-        const float a = FUSED ? add[idx] : 0.0f;
-        y[idx] = epilogue<FUSED>(acc[j], b, a);
+        const float a = epi_add(EPI) ? add[idx] : 0.0f;
+        y[idx] = epilogue<EPI>(acc[j], b, a);
     }
 }
 
@@ -127,7 +127,7 @@ struct PhaseParams {
 };
 constexpr int kMaxPhaseLds = 32768; // bytes of staged weights per workgroup
 
-template <int CPT, int NPOS, bool FUSED>
+template <int CPT, int NPOS, int EPI>
 __global__ __launch_bounds__(kBlock) void k_generic_phase(const PhaseParams P,
                                                           const float *__restrict__ x,
                                                           const float *__restrict__ w,
@@ -235,8 +235,8 @@ __global__ __launch_bounds__(kBlock) void k_generic_phase(const PhaseParams P,
             const int co = g * P.Cog + co0 + j;
             const int64_t idx = ((int64_t)n * P.C_out + co) * P.out_sp + sp;
             const float b = bias ? bias[co] : 0.0f;
-            const float a = FUSED ? add[idx] : 0.0f;
-            y[idx] = epilogue<FUSED>(acc[u][j], b, a);
+            const float a = epi_add(EPI) ? add[idx] : 0.0f;
+            y[idx] = epilogue<EPI>(acc[u][j], b, a);
         }
     }
 }
@@ -359,7 +359,7 @@ __device__ __forceinline__ void rows_window(const float (&wa)[TH], rsrc_t rx, un
 
 // Every class of a launch has exactly TH taps on H (or none on some axis: then
 // it only takes the bias).  FULLCH: Cig is a multiple of the channel chunk.
-template <int CPT, int R, int TH, bool FULLCH, bool FUSED>
+template <int CPT, int R, int TH, bool FULLCH, int EPI>
 __global__ __launch_bounds__(kBlock) void k_generic_rows(const PhaseParams P,
                                                          const float *__restrict__ x,
                                                          const float *__restrict__ w,
@@ -468,8 +468,8 @@ __global__ __launch_bounds__(kBlock) void k_generic_rows(const PhaseParams P,
             const int co = g * P.Cog + co0 + j;
             const int64_t idx = ((int64_t)n * P.C_out + co) * P.out_sp + sp;
             const float b = bias ? bias[co] : 0.0f;
-            const float a = FUSED ? add[idx] : 0.0f;
-            y[idx] = epilogue<FUSED>(acc[r][j / 4][j % 4], b, a);
+            const float a = epi_add(EPI) ? add[idx] : 0.0f;
+            y[idx] = epilogue<EPI>(acc[r][j / 4][j % 4], b, a);
         }
     }
 }
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(kBlock) void k_generic_rows(const PhaseParams P,
 // A wave owns NP row pairs x PB blocks of 16 positions of one (class, qd).
 typedef float v4f_p __attribute__((ext_vector_type(4)));
 
-template <int NP, int PB, int TH, bool FUSED>
+template <int NP, int PB, int TH, int EPI>
 __global__ __launch_bounds__(kBlock) void k_generic_pairs(const PhaseParams P,
                                                           const float *__restrict__ x,
                                                           const float *__restrict__ w,
@@ -635,7 +635,7 @@ __global__ __launch_bounds__(kBlock) void k_generic_pairs(const PhaseParams P,
     const rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(y + (int64_t)n * P.C_out * P.out_sp, (short)0, ybytes,
                                                         kRsrcWord3);
     const rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float *>(FUSED ? add + (int64_t)n * P.C_out * P.out_sp : y), (short)0, ybytes, kRsrcWord3);
+        const_cast<float *>(epi_add(EPI) ? add + (int64_t)n * P.C_out * P.out_sp : y), (short)0, ybytes, kRsrcWord3);
     float bb[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) bb[v] = bias ? bias[cb + v] : 0.0f;
@@ -652,10 +652,10 @@ __global__ __launch_bounds__(kBlock) void k_generic_pairs(const PhaseParams P,
                 in ? 4u * (unsigned)(cb * P.out_sp + (od * AH.L_out + oh) * AW.L_out + ow) : kOutOfRange;
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const float aa = FUSED ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                const float aa = epi_add(EPI) ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                                        ra, vo, v * ch_step, 0))
                                        : 0.0f;
-                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, epilogue<FUSED>(acc[p][pb][v], bb[v], aa)),
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, epilogue<EPI>(acc[p][pb][v], bb[v], aa)),
                                                       ry, vo, v * ch_step, 0);
             }
         }
@@ -789,37 +789,31 @@ int launch_classes(const convt_plan &Pl, PhaseParams &P, int cpt, Launch &&launc
 
 template <int CPT>
 int launch_phase(const convt_plan &Pl, PhaseParams &P, const float *x, const float *w,
-                 const float *bias, const float *add, float *y, hipStream_t st) {
+                 const float *bias, const float *add, int act, float *y, hipStream_t st) {
     return launch_classes(Pl, P, CPT, [&](dim3 grid, size_t lds) {
-        if (add)
-            hipLaunchKernelGGL((k_generic_phase<CPT, kPhasePos, true>), grid, dim3(kBlock), lds, st, P, x, w,
-                               bias, add, y);
-        else
-            hipLaunchKernelGGL((k_generic_phase<CPT, kPhasePos, false>), grid, dim3(kBlock), lds, st, P, x, w,
-                               bias, add, y);
+        with_epi(add != nullptr, act, [&](auto E) {
+            hipLaunchKernelGGL((k_generic_phase<CPT, kPhasePos, decltype(E)::value>),
+                               grid, dim3(kBlock), lds, st, P, x, w, bias, add, y);
+        });
     });
 }
 
 template <int CPT, int TH>
 int launch_rows(const convt_plan &Pl, PhaseParams &P, const float *x, const float *w,
-                const float *bias, const float *add, float *y, hipStream_t st) {
+                const float *bias, const float *add, int act, float *y, hipStream_t st) {
     constexpr int CH = 64 / CPT;
     const bool full = Pl.Cig % CH == 0;
     return launch_classes(Pl, P, CPT, [&](dim3 grid, size_t lds) {
         if (full) {
-            if (add)
-                hipLaunchKernelGGL((k_generic_rows<CPT, kRows, TH, true, true>), grid, dim3(kBlock), lds, st, P,
-                                   x, w, bias, add, y);
-            else
-                hipLaunchKernelGGL((k_generic_rows<CPT, kRows, TH, true, false>), grid, dim3(kBlock), lds, st, P,
-                                   x, w, bias, add, y);
+            with_epi(add != nullptr, act, [&](auto E) {
+                hipLaunchKernelGGL((k_generic_rows<CPT, kRows, TH, true, decltype(E)::value>),
+                                   grid, dim3(kBlock), lds, st, P, x, w, bias, add, y);
+            });
         } else {
-            if (add)
-                hipLaunchKernelGGL((k_generic_rows<CPT, kRows, TH, false, true>), grid, dim3(kBlock), lds, st, P,
-                                   x, w, bias, add, y);
-            else
-                hipLaunchKernelGGL((k_generic_rows<CPT, kRows, TH, false, false>), grid, dim3(kBlock), lds, st, P,
-                                   x, w, bias, add, y);
+            with_epi(add != nullptr, act, [&](auto E) {
+                hipLaunchKernelGGL((k_generic_rows<CPT, kRows, TH, false, decltype(E)::value>),
+                                   grid, dim3(kBlock), lds, st, P, x, w, bias, add, y);
+            });
         }
     });
 }
@@ -828,7 +822,7 @@ int launch_rows(const convt_plan &Pl, PhaseParams &P, const float *x, const floa
 // over the classes with exactly that many H taps.
 template <int CPT>
 int launch_rows_all(int th_max, const convt_plan &Pl, PhaseParams &Q, const float *x, const float *w,
-                    const float *bias, const float *add, float *y, hipStream_t st) {
+                    const float *bias, const float *add, int act, float *y, hipStream_t st) {
     static_assert(kRowsMaxTH == 5, "one case per instantiated H tap count");
     for (int th = 1; th <= th_max; ++th) {
         PhaseParams P = Q;
@@ -836,11 +830,11 @@ int launch_rows_all(int th_max, const convt_plan &Pl, PhaseParams &Q, const floa
         if (P.n_cls == 0) continue;
         int e = 0;
         switch (th) {
-        case 1: e = launch_rows<CPT, 1>(Pl, P, x, w, bias, add, y, st); break;
-        case 2: e = launch_rows<CPT, 2>(Pl, P, x, w, bias, add, y, st); break;
-        case 3: e = launch_rows<CPT, 3>(Pl, P, x, w, bias, add, y, st); break;
-        case 4: e = launch_rows<CPT, 4>(Pl, P, x, w, bias, add, y, st); break;
-        default: e = launch_rows<CPT, 5>(Pl, P, x, w, bias, add, y, st); break;
+        case 1: e = launch_rows<CPT, 1>(Pl, P, x, w, bias, add, act, y, st); break;
+        case 2: e = launch_rows<CPT, 2>(Pl, P, x, w, bias, add, act, y, st); break;
+        case 3: e = launch_rows<CPT, 3>(Pl, P, x, w, bias, add, act, y, st); break;
+        case 4: e = launch_rows<CPT, 4>(Pl, P, x, w, bias, add, act, y, st); break;
+        default: e = launch_rows<CPT, 5>(Pl, P, x, w, bias, add, act, y, st); break;
         }
         if (e) return e;
     }
@@ -874,19 +868,17 @@ int pairs_plan(const convt_plan &Pl) {
 
 template <int TH>
 int launch_pairs(const convt_plan &Pl, PhaseParams &P, const float *x, const float *w,
-                 const float *bias, const float *add, float *y, hipStream_t st) {
+                 const float *bias, const float *add, int act, float *y, hipStream_t st) {
     return launch_classes(Pl, P, 8, [&](dim3 grid, size_t lds) {
-        if (add)
-            hipLaunchKernelGGL((k_generic_pairs<kPairs, kPairBlocks, TH, true>), grid, dim3(kBlock), lds, st, P,
-                               x, w, bias, add, y);
-        else
-            hipLaunchKernelGGL((k_generic_pairs<kPairs, kPairBlocks, TH, false>), grid, dim3(kBlock), lds, st, P,
-                               x, w, bias, add, y);
+        with_epi(add != nullptr, act, [&](auto E) {
+            hipLaunchKernelGGL((k_generic_pairs<kPairs, kPairBlocks, TH, decltype(E)::value>),
+                               grid, dim3(kBlock), lds, st, P, x, w, bias, add, y);
+        });
     });
 }
 
 int launch_pairs_all(int th_max, const convt_plan &Pl, PhaseParams &Q, const float *x, const float *w,
-                     const float *bias, const float *add, float *y, hipStream_t st) {
+                     const float *bias, const float *add, int act, float *y, hipStream_t st) {
     static_assert(kRowsMaxTH == 5, "one case per instantiated H tap count");
     for (int th = 1; th <= th_max; ++th) {
         PhaseParams P = Q;
@@ -894,11 +886,11 @@ int launch_pairs_all(int th_max, const convt_plan &Pl, PhaseParams &Q, const flo
         if (P.n_cls == 0) continue;
         int e = 0;
         switch (th) {
-        case 1: e = launch_pairs<1>(Pl, P, x, w, bias, add, y, st); break;
-        case 2: e = launch_pairs<2>(Pl, P, x, w, bias, add, y, st); break;
-        case 3: e = launch_pairs<3>(Pl, P, x, w, bias, add, y, st); break;
-        case 4: e = launch_pairs<4>(Pl, P, x, w, bias, add, y, st); break;
-        default: e = launch_pairs<5>(Pl, P, x, w, bias, add, y, st); break;
+        case 1: e = launch_pairs<1>(Pl, P, x, w, bias, add, act, y, st); break;
+        case 2: e = launch_pairs<2>(Pl, P, x, w, bias, add, act, y, st); break;
+        case 3: e = launch_pairs<3>(Pl, P, x, w, bias, add, act, y, st); break;
+        case 4: e = launch_pairs<4>(Pl, P, x, w, bias, add, act, y, st); break;
+        default: e = launch_pairs<5>(Pl, P, x, w, bias, add, act, y, st); break;
         }
         if (e) return e;
     }
@@ -907,7 +899,7 @@ int launch_pairs_all(int th_max, const convt_plan &Pl, PhaseParams &Q, const flo
 
 template <int CPT>
 int launch_cpt(const convt_plan &Pl, const GenericParams &base, const float *x, const float *w,
-               const float *bias, const float *add, float *y, hipStream_t st) {
+               const float *bias, const float *add, int act, float *y, hipStream_t st) {
     GenericParams P = base;
     P.co_chunks = (int)((Pl.Cog + CPT - 1) / CPT);
     const unsigned gx = (unsigned)((Pl.out_sp + kBlock - 1) / kBlock);
@@ -916,12 +908,10 @@ int launch_cpt(const convt_plan &Pl, const GenericParams &base, const float *x, 
         P.n0 = (int)n0;
         const unsigned gz = (unsigned)(Pl.N - n0 < 65535 ? Pl.N - n0 : 65535);
         dim3 grid(gx, gy, gz);
-        if (add)
-            hipLaunchKernelGGL((k_generic<CPT, true>), grid, dim3(kBlock), 0, st, P, x, w, bias,
-                               add, y);
-        else
-            hipLaunchKernelGGL((k_generic<CPT, false>), grid, dim3(kBlock), 0, st, P, x, w, bias,
-                               add, y);
+        with_epi(add != nullptr, act, [&](auto E) {
+            hipLaunchKernelGGL((k_generic<CPT, decltype(E)::value>),
+                               grid, dim3(kBlock), 0, st, P, x, w, bias, add, y);
+        });
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return (int)e;
     }
@@ -944,7 +934,7 @@ bool generic_supports(const convt_plan &P) {
 }
 
 int launch_generic(const convt_plan &Pl, const float *x, const float *w, const float *bias,
-                   const float *add, float *y, void *stream) {
+                   const float *add, int act, float *y, void *stream) {
     {
         PhaseParams Q;
         const int thp = pairs_plan(Pl);
@@ -960,16 +950,16 @@ int launch_generic(const convt_plan &Pl, const float *x, const float *w, const f
             Q.in_sp = (int)Pl.in_sp;
             Q.out_sp = (int)Pl.out_sp;
             hipStream_t st = (hipStream_t)stream;
-            if (thp > 0) return launch_pairs_all(thp, Pl, Q, x, w, bias, add, y, st);
+            if (thp > 0) return launch_pairs_all(thp, Pl, Q, x, w, bias, add, act, y, st);
             if (rows) {
-                if (pick_cpt(Pl.Cog) == 8) return launch_rows_all<8>(th, Pl, Q, x, w, bias, add, y, st);
-                return launch_rows_all<4>(th, Pl, Q, x, w, bias, add, y, st);
+                if (pick_cpt(Pl.Cog) == 8) return launch_rows_all<8>(th, Pl, Q, x, w, bias, add, act, y, st);
+                return launch_rows_all<4>(th, Pl, Q, x, w, bias, add, act, y, st);
             }
             switch (pick_cpt(Pl.Cog)) {
-            case 8: return launch_phase<8>(Pl, Q, x, w, bias, add, y, st);
-            case 4: return launch_phase<4>(Pl, Q, x, w, bias, add, y, st);
-            case 2: return launch_phase<2>(Pl, Q, x, w, bias, add, y, st);
-            default: return launch_phase<1>(Pl, Q, x, w, bias, add, y, st);
+            case 8: return launch_phase<8>(Pl, Q, x, w, bias, add, act, y, st);
+            case 4: return launch_phase<4>(Pl, Q, x, w, bias, add, act, y, st);
+            case 2: return launch_phase<2>(Pl, Q, x, w, bias, add, act, y, st);
+            default: return launch_phase<1>(Pl, Q, x, w, bias, add, act, y, st);
             }
         }
     }
@@ -986,10 +976,10 @@ int launch_generic(const convt_plan &Pl, const float *x, const float *w, const f
     P.n0 = 0;
     hipStream_t st = (hipStream_t)stream;
     switch (pick_cpt(Pl.Cog)) {
-    case 8: return launch_cpt<8>(Pl, P, x, w, bias, add, y, st);
-    case 4: return launch_cpt<4>(Pl, P, x, w, bias, add, y, st);
-    case 2: return launch_cpt<2>(Pl, P, x, w, bias, add, y, st);
-    default: return launch_cpt<1>(Pl, P, x, w, bias, add, y, st);
+    case 8: return launch_cpt<8>(Pl, P, x, w, bias, add, act, y, st);
+    case 4: return launch_cpt<4>(Pl, P, x, w, bias, add, act, y, st);
+    case 2: return launch_cpt<2>(Pl, P, x, w, bias, add, act, y, st);
+    default: return launch_cpt<1>(Pl, P, x, w, bias, add, act, y, st);
     }
 }
 

@@ -178,7 +178,7 @@ __device__ __forceinline__ void buf_store2(float a, float b, rsrc_t r, unsigned 
 }
 
 template <int CIG, int COG, int KW, int SW, int DW, int TDM, int THM, int NWBM, int PWM, int PER,
-          bool FUSED, bool FULLW, bool SWAP>
+          int EPI, bool FULLW, bool SWAP>
 __global__ __launch_bounds__(COG * 4)
 __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const Igemm3dParams P,
                                                      const float *__restrict__ x,
@@ -186,6 +186,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
                                                      const float *__restrict__ bias,
                                                      const float *add, float *y) {
     using Ph = WPhases<KW, SW, DW>;
+    constexpr bool FUSED = epi_add(EPI); // add_input is read
     constexpr int NCIG = CIG / 4;
     constexpr int NT = COG * 4;
     constexpr int SLOTS = TDM * THM;
@@ -480,10 +481,8 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
                             }
                         }
                     }
-                    if constexpr (FUSED) {
 #pragma unroll
-                        for (int rr = 0; rr < SW; ++rr) v[rr] = times_hardswish(v[rr] + av[t][e][rr]);
-                    }
+                    for (int rr = 0; rr < SW; ++rr) v[rr] = finish<EPI>(v[rr], FUSED ? av[t][e][rr] : 0.0f);
                     const unsigned o = vo + 4 * SW * 16 * t;
                     if (FULLW || ow0 + SW <= P.W_out) {
                         if constexpr (SW == 2) {
@@ -549,7 +548,7 @@ __device__ __forceinline__ RowPos pick_row(int q, const RowPos &A, const RowPos 
     return o;
 }
 
-template <int CIG, int KW, int SW, int DW, int NWB, int CC, int PWX, bool FUSED>
+template <int CIG, int KW, int SW, int DW, int NWB, int CC, int PWX, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CONVT_IGW_WAVES_PER_EU)))
 void k_igemm3d_wide(const Igemm3dParams P,
                                                       const float *__restrict__ x,
@@ -750,8 +749,8 @@ void k_igemm3d_wide(const Igemm3dParams P,
 #pragma unroll
                 for (int rr = 0; rr < SW; ++rr) {
                     if (ow0 + rr < P.W_out) {
-                        const float a1 = FUSED ? add[o + rr] : 0.0f;
-                        y[o + rr] = epilogue<FUSED>(v[rr], bco, a1);
+                        const float a1 = epi_add(EPI) ? add[o + rr] : 0.0f;
+                        y[o + rr] = epilogue<EPI>(v[rr], bco, a1);
                     }
                 }
             }
@@ -924,7 +923,7 @@ int assign_blocks(Igemm3dParams &P, int rpb, bool xcd_order = false) {
 
 template <int CIG, int COG, int KW, int SW, int DW, int TDM, int THM, int NWBM, int PWM, int W4M>
 int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const float *w,
-                   const float *bias, const float *add, float *y, hipStream_t st) {
+                   const float *bias, const float *add, int act, float *y, hipStream_t st) {
     Igemm3dParams P;
     const int64_t total_rows = fill_params(Pl, L, SW, P);
     // rows per block: enough blocks to fill the CUs several times over
@@ -938,8 +937,8 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
     if (need_f > PER * NT) return (int)hipErrorInvalidValue;
     // every lane of every W-block inside the row
     const bool fullw = Pl.ax[2].L_out == SW * 16 * NWBM;
-    auto launch = [&](auto fused, auto full, auto swap) {
-        hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, decltype(fused)::value,
+    auto launch = [&](auto epi, auto full, auto swap) {
+        hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, decltype(epi)::value,
                                       decltype(full)::value, decltype(swap)::value>),
                            dim3(blocks), dim3(NT), 0, st, P, x, w, bias, add, y);
     };
@@ -956,8 +955,7 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
         if (fullw) with_swap(fused, std::true_type{});
         else with_swap(fused, std::false_type{});
     };
-    if (add) with_full(std::true_type{});
-    else with_full(std::false_type{});
+    with_epi(add != nullptr, act, with_full);
     return (int)hipGetLastError();
 }
 
@@ -996,18 +994,16 @@ int find_wide(const convt_plan &P, Layout *Lout) {
 
 template <int CIG, int KW, int SW, int DW, int NWB, int CC, int PWX>
 int launch_wide(const convt_plan &Pl, const Layout &L, const float *x, const float *w,
-                const float *bias, const float *add, float *y, hipStream_t st) {
+                const float *bias, const float *add, int act, float *y, hipStream_t st) {
     Igemm3dParams P;
     fill_params(Pl, L, SW, P);
     P.x_bytes = (int)(4 * Pl.N * Pl.C_in * Pl.in_sp);
     const int blocks = assign_blocks(P, 4);
     if (blocks == 0) return 0;
-    if (add)
-        hipLaunchKernelGGL((k_igemm3d_wide<CIG, KW, SW, DW, NWB, CC, PWX, true>), dim3(blocks),
+    with_epi(add != nullptr, act, [&](auto E) {
+        hipLaunchKernelGGL((k_igemm3d_wide<CIG, KW, SW, DW, NWB, CC, PWX, decltype(E)::value>), dim3(blocks),
                            dim3(256), 0, st, P, x, w, bias, add, y);
-    else
-        hipLaunchKernelGGL((k_igemm3d_wide<CIG, KW, SW, DW, NWB, CC, PWX, false>), dim3(blocks),
-                           dim3(256), 0, st, P, x, w, bias, add, y);
+    });
     return (int)hipGetLastError();
 }
 
@@ -1027,20 +1023,20 @@ const char *igemm3d_kernel_name(const convt_plan &P) {
 }
 
 int launch_igemm3d(const convt_plan &Pl, const float *x, const float *w, const float *bias,
-                   const float *add, float *y, void *stream) {
+                   const float *add, int act, float *y, void *stream) {
     Layout L;
     const int v = find_variant(Pl, &L); // weights in VGPRs when they fit, else streamed
     hipStream_t st = (hipStream_t)stream;
     switch (v) {
-    case 0: return launch_variant<32, 64, 3, 2, 1, 2, 2, 1, kPW, 4>(Pl, L, x, w, bias, add, y, st);
-    case 1: return launch_variant<32, 64, 3, 2, 1, 2, 2, 2, kPW, 8>(Pl, L, x, w, bias, add, y, st);
-    case 2: return launch_variant<16, 32, 4, 2, 1, 2, 2, 2, kPW, 8>(Pl, L, x, w, bias, add, y, st);
+    case 0: return launch_variant<32, 64, 3, 2, 1, 2, 2, 1, kPW, 4>(Pl, L, x, w, bias, add, act, y, st);
+    case 1: return launch_variant<32, 64, 3, 2, 1, 2, 2, 2, kPW, 8>(Pl, L, x, w, bias, add, act, y, st);
+    case 2: return launch_variant<16, 32, 4, 2, 1, 2, 2, 2, kPW, 8>(Pl, L, x, w, bias, add, act, y, st);
     default: break;
     }
     switch (find_wide(Pl, &L)) {
-    case 0: return launch_wide<128, 4, 2, 1, 2, 16, 48>(Pl, L, x, w, bias, add, y, st);
-    case 1: return launch_wide<128, 4, 2, 1, 1, 16, 48>(Pl, L, x, w, bias, add, y, st);
-    case 2: return launch_wide<64, 4, 2, 1, 2, 16, 48>(Pl, L, x, w, bias, add, y, st);
+    case 0: return launch_wide<128, 4, 2, 1, 2, 16, 48>(Pl, L, x, w, bias, add, act, y, st);
+    case 1: return launch_wide<128, 4, 2, 1, 1, 16, 48>(Pl, L, x, w, bias, add, act, y, st);
+    case 2: return launch_wide<64, 4, 2, 1, 2, 16, 48>(Pl, L, x, w, bias, add, act, y, st);
     default: return (int)hipErrorInvalidValue;
     }
 }

@@ -226,7 +226,7 @@ template <int S> constexpr int stage_pitch() { return (kLineF + 64 * S + kLineF 
 // the group and all 64 positions of the work item; the waves share the x tile
 // through LDS, double-buffered: the tile of the next work item is fetched
 // from HBM into registers while the current one is contracted.
-template <int CIG, int COG, int K, int S, int D, bool FUSED>
+template <int CIG, int COG, int K, int S, int D, int EPI>
 __global__ __launch_bounds__(COG * 4)
 __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(const Stream1dParams P,
                                                       const float *__restrict__ x,
@@ -234,6 +234,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
                                                       const float *__restrict__ bias,
                                                       const float *add, float *y) {
     using Ph = Phases<K, S, D>;
+    constexpr bool ADD = epi_add(EPI);
     constexpr int NCIG = CIG / 4;
     constexpr int COT = COG / 16;
     constexpr int NT = COG * 4; // threads per workgroup
@@ -413,7 +414,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
                 cb[e] = (lds_fptr)(srow + a_row[e] + j);
             }
         }
-        if (!FUSED && interior && chain_in && chain_out) {
+        if (!ADD && interior && chain_in && chain_out) {
             // The common item: staging, carry and whole-line stores, with no
             // per-store address arithmetic.
             const unsigned item4 = 4u * (unsigned)(o_t - kLineF);
@@ -431,7 +432,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
                         float a = br[e];
                         if constexpr (Ph::count() > 0)
                             if (Ph::nonempty(r)) a = acc[Ph::slot(r)][t][e];
-                        o[S * t + r] = a;
+                        o[S * t + r] = activate<EPI>(a);
                     }
                 // This run's last 32 outputs (m = 64S - 32 + i) become the next
                 // run's carry (one wave's LDS accesses are performed in order).
@@ -442,11 +443,11 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
             }
         } else {
         float *yrow = y + ((int64_t)n * P.C_out + (int64_t)g * COG + 16 * ct + 4 * g4) * P.L_out + o_t;
-        const float *arow = FUSED ? add + (yrow - y) : nullptr;
+        const float *arow = ADD ? add + (yrow - y) : nullptr;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float *yr = yrow + (int64_t)e * P.L_out;
-            const float *ar = FUSED ? arow + (int64_t)e * P.L_out : nullptr;
+            const float *ar = ADD ? arow + (int64_t)e * P.L_out : nullptr;
             float v[4 * S];
 #pragma unroll
             for (int t = 0; t < 4; ++t)
@@ -458,15 +459,18 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
                     v[t * S + r] = a;
                 }
             if (interior) {
-                if constexpr (FUSED) {
+                if constexpr (ADD) {
 #pragma unroll
                     for (int c = 0; c < S; ++c) {
                         const f4 a4 = load4u(ar + 4 * S * j + 4 * c); // add_input: any alignment
-                        v[4 * c + 0] = times_hardswish(v[4 * c + 0] + a4.x);
-                        v[4 * c + 1] = times_hardswish(v[4 * c + 1] + a4.y);
-                        v[4 * c + 2] = times_hardswish(v[4 * c + 2] + a4.z);
-                        v[4 * c + 3] = times_hardswish(v[4 * c + 3] + a4.w);
+                        v[4 * c + 0] = finish<EPI>(v[4 * c + 0], a4.x);
+                        v[4 * c + 1] = finish<EPI>(v[4 * c + 1], a4.y);
+                        v[4 * c + 2] = finish<EPI>(v[4 * c + 2], a4.z);
+                        v[4 * c + 3] = finish<EPI>(v[4 * c + 3], a4.w);
                     }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4 * S; ++u) v[u] = activate<EPI>(v[u]);
                 }
                 const int a = (int)(((uintptr_t)yr >> 2) & (kLineF - 1)); // o_t's offset in its line
                 if (chain_in) { // the previous run's last 32 outputs
@@ -512,8 +516,8 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
                 for (int u = 0; u < 4 * S; ++u) {
                     const int o = o_t + 4 * S * j + u;
                     if (o >= 0 && o < P.L_out) {
-                        const float a = FUSED ? ar[4 * S * j + u] : 0.0f;
-                        yr[4 * S * j + u] = FUSED ? times_hardswish(v[u] + a) : v[u];
+                        const float a = ADD ? ar[4 * S * j + u] : 0.0f;
+                        yr[4 * S * j + u] = finish<EPI>(v[u], a);
                     }
                 }
             }
@@ -564,7 +568,7 @@ int num_cus() {
 
 template <int CIG, int COG, int K, int S, int D>
 int launch_variant(const convt_plan &Pl, const float *x, const float *w, const float *bias,
-                   const float *add, float *y, hipStream_t st) {
+                   const float *add, int act, float *y, hipStream_t st) {
     const AxisPlan &A = Pl.ax[2];
     Stream1dParams P;
     P.C_in = (int)Pl.C_in;
@@ -591,12 +595,10 @@ int launch_variant(const convt_plan &Pl, const float *x, const float *w, const f
     P.per_block = (int)per_block;
     const unsigned grid = (unsigned)((P.total + per_block - 1) / per_block);
     constexpr int NT = COG * 4;
-    if (add)
-        hipLaunchKernelGGL((k_stream1d<CIG, COG, K, S, D, true>), dim3(grid), dim3(NT), 0, st, P,
+    with_epi(add != nullptr, act, [&](auto E) {
+        hipLaunchKernelGGL((k_stream1d<CIG, COG, K, S, D, decltype(E)::value>), dim3(grid), dim3(NT), 0, st, P,
                            x, w, bias, add, y);
-    else
-        hipLaunchKernelGGL((k_stream1d<CIG, COG, K, S, D, false>), dim3(grid), dim3(NT), 0, st, P,
-                           x, w, bias, add, y);
+    });
     return (int)hipGetLastError();
 }
 
@@ -613,14 +615,14 @@ bool stream1d_supports(const convt_plan &P) {
 }
 
 int launch_stream1d(const convt_plan &Pl, const float *x, const float *w, const float *bias,
-                    const float *add, float *y, void *stream) {
+                    const float *add, int act, float *y, void *stream) {
     hipStream_t st = (hipStream_t)stream;
     switch (find_variant(Pl)) {
-    case 0: return launch_variant<32, 64, 3, 2, 2>(Pl, x, w, bias, add, y, st);
-    case 1: return launch_variant<32, 64, 3, 2, 1>(Pl, x, w, bias, add, y, st);
-    case 2: return launch_variant<32, 32, 4, 2, 1>(Pl, x, w, bias, add, y, st);
-    case 3: return launch_variant<16, 16, 3, 3, 2>(Pl, x, w, bias, add, y, st);
-    case 4: return launch_variant<16, 32, 5, 4, 2>(Pl, x, w, bias, add, y, st);
+    case 0: return launch_variant<32, 64, 3, 2, 2>(Pl, x, w, bias, add, act, y, st);
+    case 1: return launch_variant<32, 64, 3, 2, 1>(Pl, x, w, bias, add, act, y, st);
+    case 2: return launch_variant<32, 32, 4, 2, 1>(Pl, x, w, bias, add, act, y, st);
+    case 3: return launch_variant<16, 16, 3, 3, 2>(Pl, x, w, bias, add, act, y, st);
+    case 4: return launch_variant<16, 32, 5, 4, 2>(Pl, x, w, bias, add, act, y, st);
     default: return (int)hipErrorInvalidValue;
     }
 }
