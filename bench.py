@@ -171,10 +171,12 @@ def host_cpu():
             "affinity_cpus": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
-def _oracle_run(orc, wl, inp, op, n_s, threads):
+def _oracle_run(orc, wl, inp, op, n_s, threads, layout=0):
     shape = dict(ndim=wl.ndim, N=n_s, C_in=wl.C_in, C_out=wl.C_out, groups=wl.groups,
                  in_size=wl.in_size, K=wl.K, stride=wl.stride, pad=wl.pad, out_pad=wl.out_pad,
                  dilation=wl.dilation, nthreads=threads)
+    if layout:
+        shape["layout"] = layout
     t0 = time.perf_counter()
     if op == "backward_data":
         orc.backward_data(dy=np.ascontiguousarray(inp["dy"][:n_s]), w=inp["w"], **shape)
@@ -187,7 +189,7 @@ def _oracle_run(orc, wl, inp, op, n_s, threads):
     return time.perf_counter() - t0
 
 
-def cpu_baseline(wl, inp, op="forward", single_thread=False):
+def cpu_baseline(wl, inp, op="forward", single_thread=False, layout=0):
     """The oracle (as it stands) on the first n_s batch samples, with as many
     threads as it can use there (it splits the work by (sample, group), or by
     input channel for the weight gradient), at most 16; optionally also with
@@ -197,7 +199,7 @@ def cpu_baseline(wl, inp, op="forward", single_thread=False):
     cores = min(16, os.cpu_count() or 1)
     n_s = max(1, min(wl.N, cores // max(1, wl.groups)))
     threads = min(cores, wl.C_in) if op == "backward_weight" else min(cores, n_s * wl.groups)
-    dt = _oracle_run(orc, wl, inp, op, n_s, threads)
+    dt = _oracle_run(orc, wl, inp, op, n_s, threads, layout)
     nbytes = op_bytes(wl, op, n_s)
     kind = dict(backward_data="adjoint", backward_weight="weight-gradient").get(op, "scatter")
     res = {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
@@ -206,7 +208,7 @@ def cpu_baseline(wl, inp, op="forward", single_thread=False):
            "valid_mac_gflops": 2 * valid_macs(wl, n_s) / dt / 1e9, "wall_s": round(dt, 3)}
     res.update(host_cpu())
     if single_thread:
-        dt1 = _oracle_run(orc, wl, inp, op, 1, 1)
+        dt1 = _oracle_run(orc, wl, inp, op, 1, 1, layout)
         res["single_thread"] = {"value": op_bytes(wl, op, 1) / dt1 / 1e9, "unit": "GB/s",
                                 "sample": f"first 1 of {wl.N} batch samples, 1 thread",
                                 "wall_s": round(dt1, 3)}
@@ -371,20 +373,27 @@ def kernel_of(plan, op, path):
     return m.group(1) if m else KERNEL_NAMES.get(path, path)
 
 
-def measure(wl, op, steps, warmup, path="auto", flushed=20, flusher=None, cpu=True, single_thread=False):
+def measure(wl, op, steps, warmup, path="auto", flushed=20, flusher=None, cpu=True, single_thread=False,
+            layout="channels_first"):
     """One workload: warm-up, K back-to-back timed launches, then `flushed`
     launches each after the cache flush; roofline figures and the CPU
-    baseline.  Returns (record, ms_per_step, timed wall seconds)."""
+    baseline.  Channels last takes the seeded channels-first draws with the
+    channel axis moved last.  Returns (record, ms_per_step, timed wall
+    seconds)."""
     import torch
-    log(f"workload {wl.name} ({op}): generating seeded inputs")
+    log(f"workload {wl.name} ({op}, {layout}): generating seeded inputs")
     bwd, wgr = op == "backward_data", op == "backward_weight"
     inp = S.make_inputs(wl, 0, (wl.N, wl.C_out) + out_size(wl))
     if bwd:
         inp = {"dy": S.make_grad_output(wl, 0, (wl.N, wl.C_out) + out_size(wl)), "w": inp["w"]}
     elif wgr:
         inp = {"dy": S.make_grad_output(wl, 0, (wl.N, wl.C_out) + out_size(wl)), "x": inp["x"]}
+    if layout == "channels_last":
+        for k in ("x", "add"):
+            if inp.get(k) is not None:
+                inp[k] = np.ascontiguousarray(np.moveaxis(inp[k], 1, -1))
     dev = {k: (None if v is None else torch.from_numpy(v).cuda()) for k, v in inp.items()}
-    plan = T.plan_for(wl)
+    plan = T.plan_for(wl, layout)
     if path != "auto":
         T.convt_plan_set_path(plan, path)
     path = T.convt_plan_get_path(plan)
@@ -440,7 +449,7 @@ def measure(wl, op, steps, warmup, path="auto", flushed=20, flusher=None, cpu=Tr
         roof["flushed"] = dict(stats(cold), launches=int(flushed),
                                achieved=round(rate(cold_ms), 2 if roof["bound"] == "mfma" else 1),
                                frac=round(rate(cold_ms) / roof["peak"], 4))
-    rec = {"workload": wl.name, "op": op, "path": path, "kernel": kernel,
+    rec = {"workload": wl.name, "op": op, "layout": layout, "path": path, "kernel": kernel,
            "ms_per_step": round(ms_per_step, 5), "gbs": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1),
            "valid_mac_tflops": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
            "hbm_frac": round(t_hbm / (ms_per_step * 1e-3), 4), "fp32_frac": round(t_fp32 / (ms_per_step * 1e-3), 4),
@@ -449,7 +458,8 @@ def measure(wl, op, steps, warmup, path="auto", flushed=20, flusher=None, cpu=Tr
     torch.cuda.empty_cache()
     if cpu:
         log(f"timing the CPU oracle on a bounded sample of {wl.name}")
-        rec["cpu_baseline"] = cpu_baseline(wl, inp, op=op, single_thread=single_thread)
+        rec["cpu_baseline"] = cpu_baseline(wl, inp, op=op, single_thread=single_thread,
+                                           layout=1 if layout == "channels_last" else 0)
     return rec, ms_per_step, wall
 
 
@@ -481,6 +491,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=S.LONG_1D.name, choices=sorted(S.BY_NAME))
     ap.add_argument("--path", default="auto", choices=sorted(T.PATHS))
+    ap.add_argument("--layout", default="channels_first", choices=sorted(T.LAYOUTS),
+                    help="layout of x, y and add_input for the headline workload")
     ap.add_argument("--op", default="forward", choices=["forward", "backward_data", "backward_weight"],
                     help="forward (the hot path, default), the input gradient, or the weight and bias gradients")
     ap.add_argument("--flushed", type=int, default=20, help="cache-flushed launches per workload")
@@ -510,18 +522,24 @@ def main():
     flusher = Flusher() if args.flushed > 0 else None
     head, ms_per_step, wall = measure(wl, args.op, args.steps, args.warmup, args.path, args.flushed, flusher,
                                       cpu=not args.no_cpu_baseline, single_thread=wl.name != S.HEAVY_3D.name and
-                                      wl.name != S.FUSED_3D.name)
+                                      wl.name != S.FUSED_3D.name, layout=args.layout)
     configs = {}
     if not args.no_configs:
         for other in S.WORKLOADS:
             key = CONFIG_KEYS[other.name]
-            if other.name == wl.name:
+            if other.name == wl.name and args.layout == "channels_first":
                 configs[key] = head
                 continue
             rec, _, _ = measure(other, args.op, args.steps, args.warmup, "auto", args.flushed, flusher,
                                 cpu=not args.no_cpu_baseline,
                                 single_thread=other.name in (S.TINY_1D.name, S.LONG_1D.name, S.GROUPED_3D.name))
             configs[key] = rec
+        if args.op == "forward":
+            # the channels-last layout of the long 1D and fused 3D layers
+            for other in (S.LONG_1D, S.FUSED_3D):
+                rec, _, _ = measure(other, args.op, args.steps, args.warmup, "auto", args.flushed, flusher,
+                                    cpu=not args.no_cpu_baseline, layout="channels_last")
+                configs[CONFIG_KEYS[other.name] + "_channels_last"] = rec
     del flusher
     torch.cuda.empty_cache()
     log("calibration kernels")
@@ -550,7 +568,7 @@ def main():
                    "out_size": list(out_size(wl)), "K": list(wl.K), "stride": list(wl.stride),
                    "pad": list(wl.pad), "out_pad": list(wl.out_pad),
                    "dilation": list(wl.dilation), "bias": wl.bias, "fused": wl.fused,
-                   "path": head["path"], "op": args.op, "parallelism": "single GPU"},
+                   "path": head["path"], "op": args.op, "layout": args.layout, "parallelism": "single GPU"},
         "valid_mac_tflops": head["valid_mac_tflops"], "hbm_frac": head["hbm_frac"], "fp32_frac": head["fp32_frac"],
         "algorithmic_bytes": head["algorithmic_bytes"], "valid_macs": head["valid_macs"],
         "timed_wall_s": round(wall, 4), "source_sha": source_sha(),

@@ -21,6 +21,8 @@
  *   bias      (C_out)                        may be NULL (no bias)
  *   add_input (N, C_out, L_out...)           same shape as y
  *   y         (N, C_out, L_out...)           every element is written
+ * or, after convt_plan_set_layout(plan, CONVT_LAYOUT_CHANNELS_LAST), x as
+ * (N, L_in..., C_in) and y and add_input as (N, L_out..., C_out).
  * No alignment is required of any pointer beyond that of float.
  *
  * Ownership and threading: a plan holds host metadata only; it allocates no
@@ -75,6 +77,19 @@ typedef enum {
     CONVT_ACT_HARDSWISH = 1,  /* y = hardswish(t) = t * min(max(t + 3, 0), 6) / 6 */
     CONVT_ACT_X_HARDSWISH = 2 /* y = t * hardswish(t) */
 } convt_activation;
+
+/*
+ * Memory layout of x, y and add_input (the weight is always
+ * (C_in, C_out/groups, K...)).  Channels last makes the C_out values of one
+ * output position contiguous ("Kimi-K2.6 l1_p79" transcript: its fast-kernel
+ * section finds the channels-first output stores of neighbouring threads far
+ * apart; "Kimi-K2.6 l2_p26" transcript: its note on channels-last 3D
+ * tensors for library convolutions).
+ */
+typedef enum {
+    CONVT_LAYOUT_CHANNELS_FIRST = 0, /* NCL / NCHW / NCDHW (the default) */
+    CONVT_LAYOUT_CHANNELS_LAST = 1   /* NLC / NHWC / NDHWC */
+} convt_layout;
 
 typedef struct convt_plan convt_plan; /* opaque */
 
@@ -189,6 +204,21 @@ CONVT_API const char *convt_status_string(convt_status status);
  * on the same plan.
  */
 CONVT_API convt_status convt_plan_set_path(convt_plan *plan, convt_path path);
+
+/*
+ * Set the layout of x, y and add_input for the plan's calls (convt_layout;
+ * a new plan is CONVT_LAYOUT_CHANNELS_FIRST).  The planner's path is chosen
+ * again for the layout and any forced path is dropped.  Every forward call
+ * and every epilogue mode takes both layouts; the gradient calls take
+ * channels first only (CONVT_ERR_UNSUPPORTED otherwise).  Returns
+ * CONVT_ERR_INVALID_ARG for a NULL plan or a value outside the enum,
+ * CONVT_ERR_UNSUPPORTED (plan unchanged) if the shape is beyond the layout's
+ * limits.  Host-only; not safe concurrently with calls on the same plan.
+ */
+CONVT_API convt_status convt_plan_set_layout(convt_plan *plan, int layout);
+
+/* The plan's layout (convt_layout), or -1 for a NULL plan. */
+CONVT_API int convt_plan_get_layout(const convt_plan *plan);
 
 /* The path forward calls will take (never CONVT_PATH_AUTO). */
 CONVT_API convt_path convt_plan_get_path(const convt_plan *plan);

@@ -206,3 +206,23 @@ def test_set_path_rejects_unsupported():
     assert T.lib().convt_plan_set_path(p.handle, 7) == T.CONVT_ERR_INVALID_ARG
     assert T.convt_plan_get_path(p) == "generic"
     assert T.lib().convt_plan_set_path(p.handle, T.PATHS["igemm3d"]) == T.CONVT_ERR_UNSUPPORTED
+
+
+def test_layout_selection():
+    """channels last re-plans: the long 1D layer takes its channels-last
+    streaming kernel, other shapes the channels-last generic kernel; the
+    gradient kernels are not offered; bad values are rejected."""
+    p = T.plan_for(S.LONG_1D)
+    assert T.convt_plan_get_layout(p) == "channels_first"
+    T.convt_plan_set_layout(p, "channels_last")
+    assert T.convt_plan_get_layout(p) == "channels_last"
+    text = T.convt_plan_describe(p)
+    assert "layout=channels_last" in text and "kernel=k_stream1d_nlc" in text and "gradient" not in text
+    assert p.x_shape() == (16, 131072, 32) and p.y_shape() == (16, 262145, 64)
+    q = T.plan_for(S.GROUPED_3D, "channels_last")
+    assert "kernel=k_generic_nxc" in T.convt_plan_describe(q)
+    assert T.lib().convt_plan_set_layout(q.handle, 2) == T.CONVT_ERR_INVALID_ARG
+    assert T.lib().convt_plan_set_layout(None, 1) == T.CONVT_ERR_INVALID_ARG
+    assert T.lib().convt_plan_get_layout(None) == -1
+    T.convt_plan_set_layout(p, "channels_first")
+    assert "kernel=k_stream1d\n" in T.convt_plan_describe(p)

@@ -17,13 +17,16 @@ LIB_PATH = os.path.join(_HERE, "libconvt.so")
 CONVT_OK, CONVT_ERR_INVALID_ARG, CONVT_ERR_UNSUPPORTED, CONVT_ERR_HIP, CONVT_ERR_NOMEM = range(5)
 PATHS = {"auto": 0, "generic": 1, "stream1d": 2, "igemm3d": 3}
 ACTIVATIONS = {"none": 0, "hardswish": 1, "x_hardswish": 2}  # convt_activation
+LAYOUTS = {"channels_first": 0, "channels_last": 1}  # convt_layout
+LAYOUT_NAMES = {v: k for k, v in LAYOUTS.items()}
 PATH_NAMES = {v: k for k, v in PATHS.items()}
 
 # Every symbol include/convt.h declares.
 EXPORTS = ("convt_plan_create", "convt_plan_output_size", "convt_forward",
            "convt_forward_add_hswish", "convt_forward_epilogue", "convt_backward_data", "convt_backward_weight",
            "convt_plan_destroy", "convt_status_string",
-           "convt_plan_set_path", "convt_plan_get_path", "convt_plan_describe")
+           "convt_plan_set_path", "convt_plan_get_path", "convt_plan_set_layout", "convt_plan_get_layout",
+           "convt_plan_describe")
 
 _lib_handle = None
 _i64p = ctypes.POINTER(ctypes.c_int64)
@@ -67,6 +70,10 @@ def lib() -> ctypes.CDLL:
     L.convt_plan_set_path.restype = ctypes.c_int
     L.convt_plan_get_path.argtypes = [vp]
     L.convt_plan_get_path.restype = ctypes.c_int
+    L.convt_plan_set_layout.argtypes = [vp, ctypes.c_int]
+    L.convt_plan_set_layout.restype = ctypes.c_int
+    L.convt_plan_get_layout.argtypes = [vp]
+    L.convt_plan_get_layout.restype = ctypes.c_int
     L.convt_plan_describe.argtypes = [vp, ctypes.c_char_p, ctypes.c_int64]
     L.convt_plan_describe.restype = ctypes.c_int64
     _lib_handle = L
@@ -95,6 +102,7 @@ class Plan:
         if st != CONVT_OK:
             raise ConvtError(st, "convt_plan_create")
         self._h = h
+        self.layout = "channels_first"
         self.ndim, self.N, self.C_in, self.C_out, self.groups = ndim, N, C_in, C_out, groups
         self.in_size, self.K = tuple(in_size), tuple(K)
         out = (ctypes.c_int64 * ndim)()
@@ -114,12 +122,16 @@ class Plan:
             self._h = None
 
     def x_shape(self):
+        if self.layout == "channels_last":
+            return (self.N,) + self.in_size + (self.C_in,)
         return (self.N, self.C_in) + self.in_size
 
     def w_shape(self):
         return (self.C_in, self.C_out // self.groups) + self.K
 
     def y_shape(self):
+        if self.layout == "channels_last":
+            return (self.N,) + self.out_size + (self.C_out,)
         return (self.N, self.C_out) + self.out_size
 
 
@@ -247,6 +259,19 @@ def convt_plan_get_path(plan: Plan) -> str:
     return PATH_NAMES[lib().convt_plan_get_path(plan.handle)]
 
 
+def convt_plan_set_layout(plan: Plan, layout: str) -> None:
+    """"channels_first" (N, C, L...) or "channels_last" (N, L..., C) for x, y
+    and add_input; the tensor shapes the calls expect follow."""
+    st = lib().convt_plan_set_layout(plan.handle, LAYOUTS[layout])
+    if st != CONVT_OK:
+        raise ConvtError(st, f"convt_plan_set_layout({layout})")
+    plan.layout = layout
+
+
+def convt_plan_get_layout(plan: Plan) -> str:
+    return LAYOUT_NAMES[lib().convt_plan_get_layout(plan.handle)]
+
+
 def convt_plan_describe(plan: Plan) -> str:
     n = lib().convt_plan_describe(plan.handle, None, 0)
     buf = ctypes.create_string_buffer(int(n) + 1)
@@ -254,7 +279,10 @@ def convt_plan_describe(plan: Plan) -> str:
     return buf.value.decode()
 
 
-def plan_for(wl) -> Plan:
-    """Plan for a synthetic.Workload description."""
-    return Plan(wl.ndim, wl.N, wl.C_in, wl.C_out, wl.groups, wl.in_size, wl.K, wl.stride, wl.pad,
-                wl.out_pad, wl.dilation)
+def plan_for(wl, layout: str = "channels_first") -> Plan:
+    """Plan for a synthetic.Workload description, in the given layout."""
+    p = Plan(wl.ndim, wl.N, wl.C_in, wl.C_out, wl.groups, wl.in_size, wl.K, wl.stride, wl.pad,
+             wl.out_pad, wl.dilation)
+    if layout != "channels_first":
+        convt_plan_set_layout(p, layout)
+    return p

@@ -69,6 +69,21 @@ const char *path_name(convt_path p) {
     return "?";
 }
 
+// The planner's path for the plan's shape and layout, then the CONVT_PATH
+// environment override (generic, stream1d or igemm3d) where that path applies.
+void select_path(convt_plan &P) {
+    P.auto_path = choose_path(P);
+    P.path = P.auto_path;
+    const char *env = getenv("CONVT_PATH");
+    if (env && *env && strcmp(env, "auto") != 0) {
+        convt_path want = CONVT_PATH_AUTO;
+        if (!strcmp(env, "generic")) want = CONVT_PATH_GENERIC;
+        else if (!strcmp(env, "stream1d")) want = CONVT_PATH_STREAM1D;
+        else if (!strcmp(env, "igemm3d")) want = CONVT_PATH_IGEMM3D;
+        if (want != CONVT_PATH_AUTO && path_supports(P, want)) P.path = want;
+    }
+}
+
 convt_status dispatch(const convt_plan *plan, const float *x, const float *w, const float *bias,
                       const float *add, int act, float *y, void *stream) {
     int e = 0;
@@ -161,19 +176,25 @@ convt_status convt_plan_create(convt_plan **plan, int ndim, int64_t N, int64_t C
         return CONVT_ERR_UNSUPPORTED;
     }
     if (!convt::generic_supports(*P)) { delete P; return CONVT_ERR_UNSUPPORTED; }
-    P->auto_path = choose_path(*P);
-    P->path = P->auto_path;
-    const char *env = getenv("CONVT_PATH");
-    if (env && *env && strcmp(env, "auto") != 0) {
-        convt_path want = CONVT_PATH_AUTO;
-        if (!strcmp(env, "generic")) want = CONVT_PATH_GENERIC;
-        else if (!strcmp(env, "stream1d")) want = CONVT_PATH_STREAM1D;
-        else if (!strcmp(env, "igemm3d")) want = CONVT_PATH_IGEMM3D;
-        if (want != CONVT_PATH_AUTO && path_supports(*P, want)) P->path = want;
-    }
+    select_path(*P);
     *plan = P;
     return CONVT_OK;
 }
+
+convt_status convt_plan_set_layout(convt_plan *plan, int layout) {
+    if (!plan) return CONVT_ERR_INVALID_ARG;
+    if (layout != CONVT_LAYOUT_CHANNELS_FIRST && layout != CONVT_LAYOUT_CHANNELS_LAST) return CONVT_ERR_INVALID_ARG;
+    const int old = plan->layout;
+    plan->layout = layout;
+    if (!convt::generic_supports(*plan)) {
+        plan->layout = old;
+        return CONVT_ERR_UNSUPPORTED;
+    }
+    select_path(*plan);
+    return CONVT_OK;
+}
+
+int convt_plan_get_layout(const convt_plan *plan) { return plan ? plan->layout : -1; }
 
 convt_status convt_plan_output_size(const convt_plan *plan, int64_t *out_size) {
     if (!plan || !out_size) return CONVT_ERR_INVALID_ARG;
@@ -207,14 +228,16 @@ convt_status convt_forward_epilogue(const convt_plan *plan, const float *x, cons
 convt_status convt_backward_data(const convt_plan *plan, const float *dy, const float *w, float *dx,
                                  void *stream) {
     if (!plan || !dy || !w || !dx) return CONVT_ERR_INVALID_ARG;
-    if (!convt::backward_data_supports(*plan)) return CONVT_ERR_UNSUPPORTED;
+    if (plan->layout != CONVT_LAYOUT_CHANNELS_FIRST || !convt::backward_data_supports(*plan))
+        return CONVT_ERR_UNSUPPORTED;
     return convt::launch_backward_data(*plan, dy, w, dx, stream) == 0 ? CONVT_OK : CONVT_ERR_HIP;
 }
 
 convt_status convt_backward_weight(const convt_plan *plan, const float *x, const float *dy, float *dw,
                                    float *db, void *stream) {
     if (!plan || !x || !dy || !dw) return CONVT_ERR_INVALID_ARG;
-    if (!convt::backward_weight_supports(*plan)) return CONVT_ERR_UNSUPPORTED;
+    if (plan->layout != CONVT_LAYOUT_CHANNELS_FIRST || !convt::backward_weight_supports(*plan))
+        return CONVT_ERR_UNSUPPORTED;
     return convt::launch_backward_weight(*plan, x, dy, dw, db, stream) == 0 ? CONVT_OK : CONVT_ERR_HIP;
 }
 
@@ -252,13 +275,14 @@ int64_t convt_plan_describe(const convt_plan *plan, char *buf, int64_t len) {
     if (!plan) return -1;
     std::string s;
     char tmp[256];
-    const char *kernel = plan->path == CONVT_PATH_STREAM1D ? "k_stream1d"
+    const bool last = plan->layout == CONVT_LAYOUT_CHANNELS_LAST;
+    const char *kernel = plan->path == CONVT_PATH_STREAM1D ? (last ? "k_stream1d_nlc" : "k_stream1d")
                          : plan->path == CONVT_PATH_IGEMM3D ? convt::igemm3d_kernel_name(*plan)
                                                             : convt::generic_kernel_name(*plan);
     snprintf(tmp, sizeof tmp,
-             "convt plan: ndim=%d N=%lld C_in=%lld C_out=%lld groups=%lld path=%s kernel=%s\n",
+             "convt plan: ndim=%d N=%lld C_in=%lld C_out=%lld groups=%lld layout=%s path=%s kernel=%s\n",
              plan->ndim, (long long)plan->N, (long long)plan->C_in, (long long)plan->C_out,
-             (long long)plan->G, path_name(plan->path), kernel);
+             (long long)plan->G, last ? "channels_last" : "channels_first", path_name(plan->path), kernel);
     s += tmp;
     for (int a = kAxes - plan->ndim; a < kAxes; ++a) {
         const AxisPlan &A = plan->ax[a];
@@ -276,12 +300,12 @@ int64_t convt_plan_describe(const convt_plan *plan, char *buf, int64_t len) {
         }
         s += "\n";
     }
-    if (convt::backward_data_supports(*plan)) {
+    if (!last && convt::backward_data_supports(*plan)) {
         s += "  input gradient: kernel=";
         s += convt::backward_data_kernel_name(*plan);
         s += "\n";
     }
-    if (convt::backward_weight_supports(*plan)) {
+    if (!last && convt::backward_weight_supports(*plan)) {
         s += "  weight gradient: kernel=";
         s += convt::backward_weight_kernel_name(*plan);
         s += "\n";

@@ -41,6 +41,7 @@ struct convt_plan {
     int64_t in_sp, out_sp, k_vol;     // spatial volumes
     convt_path auto_path;             // planner's choice
     convt_path path;                  // path the forward calls take
+    int layout;                       // convt_layout of x, y and add_input
 };
 
 namespace convt {

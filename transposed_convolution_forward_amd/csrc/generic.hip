@@ -94,6 +94,60 @@ __global__ __launch_bounds__(kBlock) void k_generic(const GenericParams P,
     }
 }
 
+// --------------------------------------------------------- channels last
+// Any shape with x (N, L_in..., C_in) and y, add_input (N, L_out..., C_out):
+// one thread per output element, the channel fastest, so a wave's stores
+// cover contiguous channels of consecutive positions, and the threads of one
+// position read the same input value (one broadcast load per tap and input
+// channel).  The gather walks the element's phase taps as k_generic does.
+template <int EPI>
+__global__ __launch_bounds__(kBlock) void k_generic_nxc(const GenericParams P, int64_t total,
+                                                        const float *__restrict__ x,
+                                                        const float *__restrict__ w,
+                                                        const float *__restrict__ bias,
+                                                        const float *add, float *y) {
+    const int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (idx >= total) return;
+    const int co = (int)(idx % P.C_out);
+    const int64_t t = idx / P.C_out;
+    const int sp = (int)(t % P.out_sp);
+    const int64_t n = t / P.out_sp;
+    const int g = co / P.Cog, co_l = co - g * P.Cog;
+
+    const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
+    const int ow = sp % AW.L_out;
+    const int t2 = sp / AW.L_out;
+    const int oh = t2 % AH.L_out;
+    const int od = t2 / AH.L_out;
+    const int td = od + AD.p, th = oh + AH.p, tw = ow + AW.p;
+    const int rd = td % AD.s, qd = td / AD.s;
+    const int rh = th % AH.s, qh = th / AH.s;
+    const int rw = tw % AW.s, qw = tw / AW.s;
+
+    float acc = 0.0f;
+    const float *xn = x + n * P.in_sp * P.C_in + (int64_t)g * P.Cig;
+    const float *wg = w + ((int64_t)g * P.Cig * P.Cog + co_l) * P.k_vol;
+    for (int jd = AD.tap_start[rd]; jd < AD.tap_start[rd + 1]; ++jd) {
+        const int id = qd - AD.tap_c[jd];
+        if (id < 0 || id >= AD.L_in) continue;
+        for (int jh = AH.tap_start[rh]; jh < AH.tap_start[rh + 1]; ++jh) {
+            const int ih = qh - AH.tap_c[jh];
+            if (ih < 0 || ih >= AH.L_in) continue;
+            for (int jw = AW.tap_start[rw]; jw < AW.tap_start[rw + 1]; ++jw) {
+                const int iw = qw - AW.tap_c[jw];
+                if (iw < 0 || iw >= AW.L_in) continue;
+                const int kidx = (AD.tap_k[jd] * AH.K + AH.tap_k[jh]) * AW.K + AW.tap_k[jw];
+                const float *xp = xn + (int64_t)((id * AH.L_in + ih) * AW.L_in + iw) * P.C_in;
+                const float *wp = wg + kidx;
+                for (int ci = 0; ci < P.Cig; ++ci)
+                    acc = fmaf(xp[ci], wp[(int64_t)ci * P.Cog * P.k_vol], acc);
+            }
+        }
+    }
+    const float a = epi_add(EPI) ? add[idx] : 0.0f;
+    y[idx] = epilogue<EPI>(acc, bias ? bias[co] : 0.0f, a);
+}
+
 // ------------------------------------------------------- phase-class variant
 // Same gather, but a workgroup covers output positions of one phase class
 // (one residue per axis) only, consecutive lanes taking consecutive positions q
@@ -921,6 +975,7 @@ int launch_cpt(const convt_plan &Pl, const GenericParams &base, const float *x, 
 } // namespace
 
 const char *generic_kernel_name(const convt_plan &Pl) {
+    if (Pl.layout == CONVT_LAYOUT_CHANNELS_LAST) return "k_generic_nxc";
     PhaseParams P;
     if (pairs_plan(Pl) > 0) return "k_generic_pairs";
     if (rows_plan(Pl) > 0) return "k_generic_rows";
@@ -929,12 +984,34 @@ const char *generic_kernel_name(const convt_plan &Pl) {
 }
 
 bool generic_supports(const convt_plan &P) {
+    // channels last: one thread per output element, a grid of at most 2^31 - 1 blocks
+    if (P.layout == CONVT_LAYOUT_CHANNELS_LAST) return (P.N * P.out_sp * P.C_out + kBlock - 1) / kBlock < INT32_MAX;
     const int cpt = pick_cpt(P.Cog);
     return P.G * ((P.Cog + cpt - 1) / cpt) <= 65535;
 }
 
 int launch_generic(const convt_plan &Pl, const float *x, const float *w, const float *bias,
                    const float *add, int act, float *y, void *stream) {
+    if (Pl.layout == CONVT_LAYOUT_CHANNELS_LAST) {
+        GenericParams P;
+        for (int a = 0; a < kAxes; ++a) P.ax[a] = Pl.ax[a];
+        P.C_in = (int)Pl.C_in;
+        P.C_out = (int)Pl.C_out;
+        P.Cig = (int)Pl.Cig;
+        P.Cog = (int)Pl.Cog;
+        P.k_vol = (int)Pl.k_vol;
+        P.in_sp = (int)Pl.in_sp;
+        P.out_sp = (int)Pl.out_sp;
+        P.co_chunks = 1;
+        P.n0 = 0;
+        const int64_t total = Pl.N * Pl.out_sp * Pl.C_out;
+        const unsigned grid = (unsigned)((total + kBlock - 1) / kBlock);
+        with_epi(add != nullptr, act, [&](auto E) {
+            hipLaunchKernelGGL((k_generic_nxc<decltype(E)::value>), dim3(grid), dim3(kBlock), 0, (hipStream_t)stream,
+                               P, total, x, w, bias, add, y);
+        });
+        return (int)hipGetLastError();
+    }
     {
         PhaseParams Q;
         const int thp = pairs_plan(Pl);

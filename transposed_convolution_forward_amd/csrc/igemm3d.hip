@@ -1010,7 +1010,7 @@ int launch_wide(const convt_plan &Pl, const Layout &L, const float *x, const flo
 } // namespace
 
 bool igemm3d_supports(const convt_plan &P) {
-    if (P.ndim < 2) return false;
+    if (P.ndim < 2 || P.layout != CONVT_LAYOUT_CHANNELS_FIRST) return false;
     Layout L;
     if (find_variant(P, &L) < 0 && find_wide(P, &L) < 0) return false;
     return P.N * P.ax[0].L_out * P.ax[1].L_out < (int64_t(1) << 31);

@@ -221,6 +221,19 @@ template <int S> constexpr int stage_pitch() { return (kLineF + 64 * S + kLineF 
 #ifndef CONVT_S1D_ROUNDS
 #define CONVT_S1D_ROUNDS 1
 #endif
+// Channels-last kernel: waves per SIMD the register allocation must allow;
+// whether a wave stages its outputs in LDS so that each store instruction
+// writes 1 KB of whole lines (1) or stores the accumulator tiles directly
+// (0); the cache policy of its output stores (2: non-temporal, 0: default).
+#ifndef CONVT_NLC_WAVES_PER_EU
+#define CONVT_NLC_WAVES_PER_EU 2
+#endif
+#ifndef CONVT_NLC_STAGE
+#define CONVT_NLC_STAGE 1
+#endif
+#ifndef CONVT_NLC_STORE_POLICY
+#define CONVT_NLC_STORE_POLICY 2
+#endif
 
 // One workgroup = COG/16 waves; wave w owns output channels 16w .. 16w+15 of
 // the group and all 64 positions of the work item; the waves share the x tile
@@ -532,6 +545,226 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
     }
 }
 
+// ------------------------------------------------------------ channels last
+// The same phase decomposition for x (N, L_in, C_in) and y (N, L_out, C_out).
+// The output of one position is C_out contiguous floats, so an
+// output-stationary tile stores whole lines without any staging: a wave owns
+// 16 consecutive positions q0 .. q0+15 of one (n, g) and all COG output
+// channels (COG/16 accumulator tiles per phase), with every weight of the
+// group in VGPRs.  Waves are independent: no LDS, no barrier.
+//
+// MFMA D[co][col] = sum_k A[co][k] B[k][col], A = W^T (16 co x 4 ci), B = X
+// (4 ci x 16 positions), column j = position q0 + j.  At step kk the lane
+// (g4, j) supplies input channel 16*(kk/4) + 4*g4 + kk%4, so for one position
+// and one tap shift c it loads its CIG/4 channels as CIG/16 float4s at
+// channel offsets 16u + 4g4: one load instruction covers 16 positions x 64
+// contiguous bytes.  Positions outside [0, L_in) read zeros through the
+// buffer resource's range check (a negative offset wraps past it).  The
+// accumulator of lane (g4, j), register e, holds channel 16ct + 4g4 + e at
+// position q0 + j: one 16-byte store per (tile, phase), and the tiles ct of
+// one position fill its C_out floats; outputs outside [0, L_out) are dropped
+// by the same range check.
+template <int CIG, int COG, int K, int S, int D, int EPI>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(CONVT_NLC_WAVES_PER_EU))) void k_stream1d_nlc(const Stream1dParams P,
+                                                          const float *__restrict__ x,
+                                                          const float *__restrict__ w,
+                                                          const float *__restrict__ bias,
+                                                          const float *add, float *y) {
+    using Ph = Phases<K, S, D>;
+    constexpr bool ADD = epi_add(EPI);
+    constexpr int NKK = CIG / 4;   // MFMA steps per tap
+    constexpr int NU = CIG / 16;   // float4 per lane per (position, shift)
+    constexpr int COT = COG / 16;  // accumulator tiles
+    constexpr int NC = Ph::cmax() + 1;
+    constexpr int NP = Ph::count() > 0 ? Ph::count() : 1;
+    static_assert(CIG % 16 == 0 && COG % 16 == 0, "tile shape");
+
+    const int lane = threadIdx.x & 63;
+    const int j = lane & 15;
+    const int g4 = lane >> 4;
+    // uniform across the wave: the item walk and the buffer resources stay in
+    // scalar registers
+    const int64_t wave = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t it0 = wave * P.per_block;
+    const int64_t it_end = it0 + P.per_block < P.total ? it0 + P.per_block : P.total;
+    if (it0 >= it_end) return;
+
+    int st = (int)(it0 % P.n_st);
+    int ng = (int)(it0 / P.n_st);
+    const unsigned xrow = 4u * (unsigned)P.C_in, yrow = 4u * (unsigned)P.C_out;
+    const int x_bytes = 4 * P.L_in * P.C_in, y_bytes = 4 * P.L_out * P.C_out;
+
+    // the lane's part of one input position: channel 16u + 4g4 of the group
+    auto fetch = [&](f4 (&xb)[NC][NU], int ng_, int st_) {
+        const int n = ng_ / P.G, g = ng_ - n * P.G;
+        const rsrc_t rx = make_rsrc(const_cast<float *>(x) + (int64_t)n * P.L_in * P.C_in, x_bytes);
+        const int q = (P.st_lo + st_) * 16 + j;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+                xb[c][u] = buf_load4(rx, (unsigned)(q - c) * xrow + 4u * (unsigned)(g * CIG + 16 * u + 4 * g4), 0u);
+    };
+
+    // Output staging (CONVT_NLC_STAGE): the wave's 16*S outputs x COG channels
+    // of one item, row p = output offset in the item, float4 column c4 stored
+    // at c4 ^ key(p), key(p) = (p/S) mod (COG/4).  The accumulator writes
+    // (lanes j = 0..15 of one g4: rows S*j + r, one column) and the reads
+    // for the stores (16 consecutive float4 of one row) then hit distinct
+    // banks.  Private to the wave: one wave's LDS accesses are performed in
+    // order, so no barrier.
+    constexpr int C4 = COG / 4;
+    constexpr int SROWS = 16 * S;
+    __shared__ __attribute__((aligned(16))) float ostage[CONVT_NLC_STAGE ? 4 : 1][CONVT_NLC_STAGE ? SROWS * COG : 4];
+    float *stg = &ostage[CONVT_NLC_STAGE ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0][0];
+
+    float wr[COT][K][NKK]; // A operands: W[g*CIG + ci(kk)][16ct + j][k]
+    f4 b4[COT];            // bias of channels 16ct + 4g4 .. +3
+    f4 xa[NC][NU], xb[NC][NU];
+    fetch(xa, ng, st);
+
+    // One item with its inputs in xc; the next item's inputs (the current
+    // one's again after the wave's last item, so that every step issues the
+    // same loads and the compiler's wait counts stay exact) go to xnx.
+    int64_t it = it0;
+    auto step = [&](const f4 (&xc)[NC][NU], f4 (&xnx)[NC][NU]) {
+        const int n = ng / P.G, g = ng - n * P.G;
+        int st1 = st + 1, ng1 = ng;
+        if (st1 == P.n_st) { st1 = 0; ++ng1; }
+        const bool has_next = it + 1 < it_end;
+        fetch(xnx, has_next ? ng1 : ng, has_next ? st1 : st);
+        // nothing moves across the steps: the scheduler would otherwise pull
+        // the next item's MFMAs up to its just-issued loads and wait for them
+        __builtin_amdgcn_sched_barrier(0);
+
+        f4 acc[NP][COT];
+        if constexpr (Ph::count() > 0) {
+#pragma unroll
+            for (int k = 0; k < K; ++k) {
+                const int c = Ph::c_of(k);
+                const int sl = Ph::slot(Ph::r_of(k));
+                const bool first = k == Ph::first_k(Ph::r_of(k));
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const float bv = xc[c][kk / 4][kk % 4];
+#pragma unroll
+                    for (int ct = 0; ct < COT; ++ct)
+                        acc[sl][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(wr[ct][k][kk], bv,
+                                                                         (first && kk == 0) ? b4[ct] : acc[sl][ct],
+                                                                         0, 0, 0);
+                }
+            }
+        }
+
+        // epilogue: phase r of position q0 + j is output o = (q0 + j)*S + r - p
+        const rsrc_t ry = make_rsrc(y + (int64_t)n * P.L_out * P.C_out, y_bytes);
+        const rsrc_t ra = make_rsrc(const_cast<float *>(ADD ? add : y) + (int64_t)n * P.L_out * P.C_out, y_bytes);
+        if constexpr (CONVT_NLC_STAGE != 0) {
+#pragma unroll
+            for (int r = 0; r < S; ++r)
+#pragma unroll
+                for (int ct = 0; ct < COT; ++ct) {
+                    f4 v = b4[ct];
+                    if constexpr (Ph::count() > 0)
+                        if (Ph::nonempty(r)) v = acc[Ph::slot(r)][ct];
+                    const int c4 = (4 * ct + g4) ^ (j & (C4 - 1));
+                    *reinterpret_cast<f4 *>(stg + (S * j + r) * COG + 4 * c4) = v;
+                }
+            // float4 number f = 64u + lane of the item's outputs: row f / C4,
+            // column f % C4; the stores of one instruction are contiguous
+            const int o0 = (P.st_lo + st) * 16 * S - P.p;
+#pragma unroll
+            for (int u = 0; u < SROWS * C4 / 64; ++u) {
+                const int f = 64 * u + lane;
+                const int row = f / C4, c4 = f % C4;
+                f4 v = *reinterpret_cast<const f4 *>(stg + row * COG + 4 * (c4 ^ ((row / S) & (C4 - 1))));
+                const unsigned off = (unsigned)(o0 + row) * yrow + 4u * (unsigned)(g * COG + 4 * c4);
+                if constexpr (ADD) {
+                    const f4 a = buf_load4(ra, off, 0u);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = finish<EPI>(v[e], a[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = activate<EPI>(v[e]);
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, v),
+                                                       ry, off, 0u, CONVT_NLC_STORE_POLICY);
+            }
+        } else {
+        const int q = (P.st_lo + st) * 16 + j;
+#pragma unroll
+        for (int r = 0; r < S; ++r) {
+            const unsigned o4 = (unsigned)(q * S + r - P.p) * yrow;
+#pragma unroll
+            for (int ct = 0; ct < COT; ++ct) {
+                const unsigned off = o4 + 4u * (unsigned)(g * COG + 16 * ct + 4 * g4);
+                f4 v = b4[ct];
+                if constexpr (Ph::count() > 0)
+                    if (Ph::nonempty(r)) v = acc[Ph::slot(r)][ct];
+                if constexpr (ADD) {
+                    const f4 a = buf_load4(ra, off, 0u);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = finish<EPI>(v[e], a[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = activate<EPI>(v[e]);
+                }
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, v),
+                                                       ry, off, 0u, CONVT_NLC_STORE_POLICY);
+            }
+        }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        st = st1;
+        ng = ng1;
+        ++it;
+    };
+
+    // Runs of consecutive items of one group share the weights: load them
+    // once per run, before the loop that carries the prefetch.
+    while (it < it_end) {
+        const int g = ng % P.G;
+        const int64_t left = P.G == 1 ? it_end - it : min(it_end - it, (int64_t)(P.n_st - st));
+#pragma unroll
+        for (int ct = 0; ct < COT; ++ct) {
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) {
+                    const int ci = g * CIG + 16 * (kk / 4) + 4 * g4 + kk % 4;
+                    wr[ct][k][kk] = w[((int64_t)ci * COG + 16 * ct + j) * K + k];
+                }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) b4[ct][e] = bias ? bias[g * COG + 16 * ct + 4 * g4 + e] : 0.0f;
+        }
+        // wait for these here (an empty asm that reads and redefines them
+        // puts the wait before the loop, whose waits then cover only the
+        // prefetch)
+#pragma unroll
+        for (int ct = 0; ct < COT; ++ct) {
+#pragma unroll
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+v"(wr[ct][k][kk]));
+            asm volatile("" : "+v"(b4[ct]));
+        }
+        const int64_t run_end = it + left;
+        // two items per trip with the input buffers swapped (no copies)
+        while (it + 1 < run_end) {
+            step(xa, xb);
+            step(xb, xa);
+        }
+        if (it < run_end) { // an odd item: its prefetch lands in xb; move it
+            step(xa, xb);
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int u = 0; u < NU; ++u) xa[c][u] = xb[c][u];
+        }
+    }
+}
+
 // Instantiated shapes: (C_in/g, C_out/g, K, S, D).
 struct Variant {
     int cig, cog, K, S, D;
@@ -602,10 +835,47 @@ int launch_variant(const convt_plan &Pl, const float *x, const float *w, const f
     return (int)hipGetLastError();
 }
 
+template <int CIG, int COG, int K, int S, int D>
+int launch_variant_nlc(const convt_plan &Pl, const float *x, const float *w, const float *bias,
+                       const float *add, int act, float *y, hipStream_t st) {
+    const AxisPlan &A = Pl.ax[2];
+    Stream1dParams P;
+    P.C_in = (int)Pl.C_in;
+    P.C_out = (int)Pl.C_out;
+    P.G = (int)Pl.G;
+    P.L_in = A.L_in;
+    P.L_out = A.L_out;
+    P.p = A.p;
+    // positions q with some output o = q*S + r - p in [0, L_out), in tiles of 16
+    const int64_t q_lo = A.p / S;
+    const int64_t q_hi = ((int64_t)A.L_out - 1 + A.p) / S + 1;
+    const int64_t st_lo = q_lo / 16;
+    P.st_lo = (int)st_lo;
+    P.n_st = (int)((q_hi + 15) / 16 - st_lo);
+    P.total = Pl.N * Pl.G * P.n_st;
+    // one round of resident waves, each walking a run of consecutive tiles
+    const int64_t waves = (int64_t)num_cus() * 4 * CONVT_NLC_WAVES_PER_EU;
+    int64_t per_wave = (P.total + waves - 1) / waves;
+    if (per_wave < 1) per_wave = 1;
+    P.per_block = (int)per_wave;
+    const int64_t nw = (P.total + per_wave - 1) / per_wave;
+    const unsigned grid = (unsigned)((nw + 3) / 4);
+    with_epi(add != nullptr, act, [&](auto E) {
+        hipLaunchKernelGGL((k_stream1d_nlc<CIG, COG, K, S, D, decltype(E)::value>), dim3(grid), dim3(256), 0, st,
+                           P, x, w, bias, add, y);
+    });
+    return (int)hipGetLastError();
+}
+
 } // namespace
 
 bool stream1d_supports(const convt_plan &P) {
     if (find_variant(P) < 0) return false;
+    if (P.layout == CONVT_LAYOUT_CHANNELS_LAST)
+        // per-sample x and y below 2 GiB (31-bit buffer offsets); positions
+        // and outputs index within int
+        return P.ax[2].L_out < (1 << 30) && P.ax[2].L_in < (1 << 30) &&
+               4 * P.C_out * P.ax[2].L_out < INT32_MAX && 4 * P.C_in * P.ax[2].L_in < INT32_MAX;
     // 64-position tiles of one row must index within int range; the tile
     // fetch reads whole float4 inside a row
     // (one sample of y and one row set of x below 2 GiB: the common-path
@@ -617,6 +887,16 @@ bool stream1d_supports(const convt_plan &P) {
 int launch_stream1d(const convt_plan &Pl, const float *x, const float *w, const float *bias,
                     const float *add, int act, float *y, void *stream) {
     hipStream_t st = (hipStream_t)stream;
+    if (Pl.layout == CONVT_LAYOUT_CHANNELS_LAST) {
+        switch (find_variant(Pl)) {
+        case 0: return launch_variant_nlc<32, 64, 3, 2, 2>(Pl, x, w, bias, add, act, y, st);
+        case 1: return launch_variant_nlc<32, 64, 3, 2, 1>(Pl, x, w, bias, add, act, y, st);
+        case 2: return launch_variant_nlc<32, 32, 4, 2, 1>(Pl, x, w, bias, add, act, y, st);
+        case 3: return launch_variant_nlc<16, 16, 3, 3, 2>(Pl, x, w, bias, add, act, y, st);
+        case 4: return launch_variant_nlc<16, 32, 5, 4, 2>(Pl, x, w, bias, add, act, y, st);
+        default: return (int)hipErrorInvalidValue;
+        }
+    }
     switch (find_variant(Pl)) {
     case 0: return launch_variant<32, 64, 3, 2, 2>(Pl, x, w, bias, add, act, y, st);
     case 1: return launch_variant<32, 64, 3, 2, 1>(Pl, x, w, bias, add, act, y, st);
