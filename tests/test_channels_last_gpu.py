@@ -95,6 +95,33 @@ def test_channels_last_1d_fast_kernel(wl):
     _check(wl, paths=["stream1d"])
 
 
+# Shapes for the channels-last implicit-GEMM kernel (weights in registers):
+# fused or not, one or two W-blocks per row, a ragged last W-block, other
+# paddings, 16 -> 32 channels with kernel 4, 2D.
+NDHWC_3D = [
+    reduced(S.FUSED_3D, N=2),
+    S.Workload("ndhwc_k3s2_fused_w8", 3, 2, 32, 64, 1, (5, 7, 8), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1),
+               (1, 1, 1), True, True, wid=5201),
+    S.Workload("ndhwc_k3s2_w24", 3, 1, 32, 64, 1, (3, 4, 24), (3, 3, 3), (2, 2, 2), (1, 0, 1), (0, 1, 1),
+               (1, 1, 1), True, False, wid=5202),
+    S.Workload("ndhwc_k4s2_c16", 3, 2, 16, 32, 1, (4, 5, 20), (4, 4, 4), (2, 2, 2), (1, 1, 1), (0, 0, 0),
+               (1, 1, 1), True, True, wid=5203),
+    S.Workload("ndhwc_k3s2_p2", 3, 1, 32, 64, 1, (4, 4, 16), (3, 3, 3), (2, 2, 2), (2, 2, 2), (1, 1, 1),
+               (1, 1, 1), False, False, wid=5204),
+    S.Workload("ndhwc_k3s2_w20", 3, 1, 32, 64, 1, (2, 3, 20), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1),
+               (1, 1, 1), True, True, wid=5205),
+    S.Workload("nhwc_2d_k3s2", 2, 2, 32, 64, 1, (16, 16), (3, 3), (2, 2), (1, 1), (1, 1), (1, 1), True, True,
+               wid=5206),
+]
+
+
+@pytest.mark.parametrize("wl", NDHWC_3D, ids=lambda w: f"{w.name}-N{w.N}-in{'x'.join(map(str, w.in_size))}")
+def test_channels_last_3d_fast_kernel(wl):
+    plan = T.plan_for(wl, "channels_last")
+    assert "kernel=k_igemm3d" in T.convt_plan_describe(plan)
+    _check(wl, paths=["igemm3d"])
+
+
 MODES = [(add, act) for add in (False, True) for act in ("none", "hardswish", "x_hardswish")]
 
 

@@ -176,9 +176,16 @@ typedef int i2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void buf_store2(float a, float b, rsrc_t r, unsigned voff, unsigned soff) {
     __builtin_amdgcn_raw_buffer_store_b64(i2{__float_as_int(a), __float_as_int(b)}, r, voff, soff, kNonTemporal);
 }
+__device__ __forceinline__ f4 buf_load4nt(rsrc_t r, unsigned voff) {
+    return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, kNonTemporal));
+}
+__device__ __forceinline__ void buf_store4(f4 v, rsrc_t r, unsigned voff) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, v), r, voff,
+                                           0, kNonTemporal);
+}
 
 template <int CIG, int COG, int KW, int SW, int DW, int TDM, int THM, int NWBM, int PWM, int PER,
-          int EPI, bool FULLW, bool SWAP>
+          int EPI, bool FULLW, bool SWAP, bool LAST>
 __global__ __launch_bounds__(COG * 4)
 __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const Igemm3dParams P,
                                                      const float *__restrict__ x,
@@ -193,8 +200,25 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     constexpr int NPH = Ph::count() > 0 ? Ph::count() : 1;
     static_assert(CIG % 8 == 0 && COG % 16 == 0, "tile shape");
     static_assert(SW <= kMaxSW, "W stride");
-
-    __shared__ __attribute__((aligned(16))) float lds[2][SLOTS * CIG * PWM];
+    // Staged input rows.  Channels first: [slot][ci][w] with a pitch of PWM
+    // floats per channel row.  Channels last (LAST): [slot][w][ci] with a
+    // pitch of CIG + 4 floats per position (the 16 positions x 4 channels of
+    // one B read then fall on distinct banks, and an input float4 of 4
+    // channels is one aligned LDS store), PWN positions per slot.
+    constexpr int PCL = CIG + 4;
+    constexpr int PWN = 16 * NWBM + 8;
+    constexpr int SLOT_SZ = LAST ? PWN * PCL : CIG * PWM;
+    __shared__ __attribute__((aligned(16))) float lds[2][SLOTS * SLOT_SZ];
+    // Channels last: the output row's 16*SW*NWBM positions x COG channels,
+    // staged across the waves so that one store instruction writes 1 KB of
+    // whole lines; float4 column c4 of position row p sits at c4 ^ key(p),
+    // key(p) = (p / SW) mod (COG/4), so the accumulator writes (16 lanes j of
+    // one g4: rows SW*j + const) and the row reads hit distinct banks.
+    constexpr int OPOS = 16 * SW * NWBM;
+    constexpr int OC4 = COG / 4;
+    constexpr int NSO = LAST ? OPOS * OC4 / NT : 1; // staged float4 each thread stores
+    static_assert(!LAST || (OPOS * OC4) % NT == 0, "output staging split");
+    __shared__ __attribute__((aligned(16))) float ost[LAST ? OPOS * COG : 4];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -219,7 +243,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     const int td = P.cls_td[cls], th = P.cls_th[cls];
 
     // zero both buffers once: halo columns and unused slots stay zero
-    for (int i = tid; i < 2 * SLOTS * CIG * PWM; i += NT) (&lds[0][0])[i] = 0.0f;
+    for (int i = tid; i < 2 * SLOTS * SLOT_SZ; i += NT) (&lds[0][0])[i] = 0.0f;
 
     // the class's weights for this wave's channels: W[4cig + g4][16ct + j][kd][kh][kw]
     float wr[TDM][THM][KW][NCIG];
@@ -272,7 +296,25 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     // so that when they split evenly the second half of a thread's float4s are
     // all of the second H tap (see the sliding rows below).
     int xo4[PER], lo[PER], tb[PER];
-    {
+    if constexpr (LAST) {
+        // channels last: float4 f is 4 channels (CIG/4 of them per position,
+        // fastest) of one input position of one tap slot's row
+        constexpr int CQ = CIG / 4;
+        const int nf = SLOTS * CQ * P.W_in;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int f = tid + u * NT;
+            const int sq = f / (CQ * P.W_in); // jh * TDM + jd
+            const int rem = f - sq * (CQ * P.W_in);
+            const int iw = rem / CQ, cq = rem - iw * CQ;
+            const int jh = sq / TDM, jd = sq % TDM;
+            const int slot = jd * THM + jh;
+            const int cd = jd == 0 ? cd0 : cd1, ch = jh == 0 ? ch0 : ch1;
+            xo4[u] = 4 * ((iw - (cd * P.H_in + ch) * P.W_in) * CIG + 4 * cq);
+            lo[u] = f < nf ? slot * SLOT_SZ + (iw - P.iw_lo) * PCL + 4 * cq : -1;
+            tb[u] = f < nf ? slot : 31;
+        }
+    } else {
         const int W4 = P.W_in >> 2;
         const int nf = SLOTS * CIG * W4;
 #pragma unroll
@@ -299,7 +341,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     // range (no traffic; the number of loads per row stays fixed, which keeps
     // the compiler's wait counts exact).
     const bool slide_ok = THM == 2 && PER % 2 == 0 && th == 2 && ch1 == ch0 + 1 &&
-                          SLOTS * CIG * (P.W_in >> 2) == PER * NT;
+                          SLOTS * (CIG / 4) * P.W_in == PER * NT;
     const int nqh = P.cls_nqh[cls];
     auto slide_of = [&](int k) { return slide_ok && k > r_begin && k % nqh != 0; };
     auto fetch_rows = [&](f4 (&rv)[PER], const RowPos &Q, bool slide) {
@@ -314,7 +356,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
                     bad &= ~(1u << (jd * THM + jh));
             }
         const rsrc_t rx = make_rsrc(x + (int64_t)Q.n * P.C_in * dhw, xbytes);
-        const int rowx4 = 4 * (Q.qd * P.H_in + Q.qh) * P.W_in;
+        const int rowx4 = 4 * (Q.qd * P.H_in + Q.qh) * P.W_in * (LAST ? CIG : 1);
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
             // an invalid slot gets bit 31 set: past num_records, the load returns zeros
@@ -327,7 +369,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
         for (int u = 0; u < PER; ++u) {
             f4 v = rv[u];
             if (u >= PER / 2 && slide && lo[u] >= 0) // second H tap: the previous row's first (one slot back)
-                v = *reinterpret_cast<const f4 *>(lprev + lo[u] - CIG * PWM);
+                v = *reinterpret_cast<const f4 *>(lprev + lo[u] - SLOT_SZ);
             if (lo[u] >= 0) *reinterpret_cast<f4 *>(lbuf + lo[u]) = v;
         }
     };
@@ -339,9 +381,28 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     const int ybytes = (int)(4 * P.C_out * dhw_out);
     const unsigned lane4 = 4u * (unsigned)((16 * ct + 4 * g4) * dhw_out + SW * j);
     const unsigned e4 = 4u * (unsigned)dhw_out;
-    auto row_off4 = [&](const RowPos &Q) { return 4u * (unsigned)((Q.od * P.H_out + Q.oh) * P.W_out); };
-    auto fetch_add = [&](float (&a)[NWBM][4][SW], const RowPos &Q) {
+    auto row_off4 = [&](const RowPos &Q) {
+        return 4u * (unsigned)((Q.od * P.H_out + Q.oh) * P.W_out * (LAST ? COG : 1));
+    };
+    // Channels last: the staged float4 f = NT*u + tid of an output row is
+    // position f / OC4, channels 4*(f % OC4) .. +3; its byte offset in the row,
+    // or past the resource for positions beyond the row end.
+    unsigned lst[NSO];
+    if constexpr (LAST) {
+#pragma unroll
+        for (int u = 0; u < NSO; ++u) {
+            const int f = NT * u + tid, pp = f / OC4, c4 = f % OC4;
+            lst[u] = pp < P.W_out ? 4u * (unsigned)(pp * COG + 4 * c4) : kOutOfRange;
+        }
+    }
+    using AddRegs = std::conditional_t<LAST, f4[NSO], float[NWBM][4][SW]>;
+    auto fetch_add = [&](AddRegs &a, const RowPos &Q) {
         const rsrc_t ra = make_rsrc(add + (int64_t)Q.n * P.C_out * dhw_out, ybytes);
+        if constexpr (LAST) {
+#pragma unroll
+            for (int u = 0; u < NSO; ++u) a[u] = buf_load4nt(ra, row_off4(Q) + lst[u]);
+            return;
+        } else {
         const unsigned vo = lane4 + row_off4(Q);
 #pragma unroll
         for (int t = 0; t < NWBM; ++t)
@@ -357,6 +418,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
                         a[t][e][rr] = buf_load1(ra, vo + 4 * (SW * 16 * t + rr), e * e4);
                 }
             }
+        }
     };
 
     // Input rows are fetched two rows ahead, before the current row's stores:
@@ -366,7 +428,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     // compiler's wait counts stay exact.)  Past the block's last row the last
     // row is fetched again, never used.
     f4 pre0[PER], pre1[PER];
-    float av[NWBM][4][SW], avn[NWBM][4][SW];
+    AddRegs av, avn;
     RowPos R = decode_row(P, cls, r_begin);
     __syncthreads(); // LDS zeroed before the first row lands
     fetch_rows(pre0, R, false);
@@ -414,7 +476,8 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
             for (int rw = 0; rw < SW; ++rw)
 #pragma unroll
                 for (int c = 0; c < CM; ++c) {
-                    bcol[rw][c] = (lds_ptr)(lds[buf] + g4 * PWM - P.iw_lo + j + P.qw0[rw] - c);
+                    bcol[rw][c] = LAST ? (lds_ptr)(lds[buf] + (j + P.qw0[rw] - c - P.iw_lo) * PCL + g4)
+                                       : (lds_ptr)(lds[buf] + g4 * PWM - P.iw_lo + j + P.qw0[rw] - c);
                     asm volatile("" : "+v"(bcol[rw][c]));
                 }
 #pragma unroll
@@ -433,7 +496,8 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
                             const int c = Ph::c_of(kw);
 #pragma unroll
                             for (int t = 0; t < NWBM; ++t) {
-                                const float bv = bcol[rw][c][(slot * CIG + 4 * cig) * PWM + 16 * t];
+                                const float bv = LAST ? bcol[rw][c][slot * SLOT_SZ + 4 * cig + 16 * t * PCL]
+                                                      : bcol[rw][c][(slot * CIG + 4 * cig) * PWM + 16 * t];
                                 const bool first = jd == 0 && jh == 0 && cig == 0 && kw == Ph::first_k(rw);
                                 acc[sl][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
                                     wr[jd][jh][kw][cig], bv, first ? bias4 : acc[sl][t], 0, 0, 0);
@@ -456,6 +520,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
         // epilogue: lane (g4, j) owns co = 16ct + 4g4 + e, ow = SW*(16t + j) + rr
         const rsrc_t ry = make_rsrc(y + (int64_t)R.n * P.C_out * dhw_out, ybytes);
         const unsigned vo = lane4 + row_off4(R);
+        const unsigned vo_row = row_off4(R);
         auto epi = [&](auto swapped) {
 #pragma unroll
             for (int t = 0; t < NWBM; ++t) {
@@ -481,8 +546,15 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
                             }
                         }
                     }
+                    if constexpr (LAST) { // staged as they are; the epilogue follows the read back
+                        const int c4 = (4 * ct + g4) ^ ((16 * t + j) & (OC4 - 1));
+#pragma unroll
+                        for (int rr = 0; rr < SW; ++rr) ost[(ow0 + rr) * COG + 4 * c4 + e] = v[rr];
+                        continue;
+                    } else {
 #pragma unroll
                     for (int rr = 0; rr < SW; ++rr) v[rr] = finish<EPI>(v[rr], FUSED ? av[t][e][rr] : 0.0f);
+                    }
                     const unsigned o = vo + 4 * SW * 16 * t;
                     if (FULLW || ow0 + SW <= P.W_out) {
                         if constexpr (SW == 2) {
@@ -503,6 +575,17 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
         // flag (as a runtime flag the compiler turns the two orders into
         // per-element selects)
         epi(std::integral_constant<bool, SWAP>{});
+        if constexpr (LAST) {
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < NSO; ++u) {
+                const int f = NT * u + tid, pp = f / OC4, c4 = f % OC4;
+                f4 v = *reinterpret_cast<const f4 *>(&ost[pp * COG + 4 * (c4 ^ ((pp / SW) & (OC4 - 1)))]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = finish<EPI>(v[e], FUSED ? av[u][e] : 0.0f);
+                buf_store4(v, ry, vo_row + lst[u]);
+            }
+        }
 
         __syncthreads();
         R = Rn;
@@ -777,7 +860,7 @@ struct Layout {
     int cmax;
 };
 
-bool w_layout(const convt_plan &P, const Variant &v, Layout &L) {
+bool w_layout(const convt_plan &P, const Variant &v, Layout &L, bool last = false) {
     const AxisPlan &A = P.ax[2];
     if (A.K != v.KW || A.s != v.SW || A.d != v.DW) return false;
     L.cmax = 0;
@@ -792,7 +875,9 @@ bool w_layout(const convt_plan &P, const Variant &v, Layout &L) {
     L.iw_lo = -((L.cmax + 3) / 4) * 4;
     const int iw_hi = std::max(qmax + 16 * L.nwb, A.L_in); // exclusive
     L.need = iw_hi - L.iw_lo;
-    return L.nwb == v.NWBM && L.need <= v.PWM; // the W-block count is a compile-time constant
+    // the W-block count is a compile-time constant; channels last stages
+    // 16*NWBM + 8 positions per tap row
+    return L.nwb == v.NWBM && L.need <= (last ? 16 * v.NWBM + 8 : v.PWM);
 }
 
 int find_variant(const convt_plan &P, Layout *Lout = nullptr) {
@@ -815,7 +900,7 @@ int find_variant(const convt_plan &P, Layout *Lout = nullptr) {
         const Variant &v = kVariants[i];
         if (P.Cig != v.cig || P.Cog != v.cog || tdm > v.TDM || thm > v.THM || W4 > v.W4M) continue;
         Layout L;
-        if (!w_layout(P, v, L)) continue;
+        if (!w_layout(P, v, L, P.layout == CONVT_LAYOUT_CHANNELS_LAST)) continue;
         if (Lout) *Lout = L;
         return i;
     }
@@ -937,9 +1022,17 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
     if (need_f > PER * NT) return (int)hipErrorInvalidValue;
     // every lane of every W-block inside the row
     const bool fullw = Pl.ax[2].L_out == SW * 16 * NWBM;
+    const bool last = Pl.layout == CONVT_LAYOUT_CHANNELS_LAST;
     auto launch = [&](auto epi, auto full, auto swap) {
+        if (last) { // channels last: the staged epilogue guards the row end itself
+            if constexpr (!decltype(full)::value)
+                hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, decltype(epi)::value,
+                                              false, decltype(swap)::value, true>),
+                                   dim3(blocks), dim3(NT), 0, st, P, x, w, bias, add, y);
+            return;
+        }
         hipLaunchKernelGGL((k_igemm3d<CIG, COG, KW, SW, DW, TDM, THM, NWBM, PWM, PER, decltype(epi)::value,
-                                      decltype(full)::value, decltype(swap)::value>),
+                                      decltype(full)::value, decltype(swap)::value, false>),
                            dim3(blocks), dim3(NT), 0, st, P, x, w, bias, add, y);
     };
     auto with_swap = [&](auto fused, auto full) {
@@ -952,7 +1045,7 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
         launch(fused, full, std::false_type{});
     };
     auto with_full = [&](auto fused) {
-        if (fullw) with_swap(fused, std::true_type{});
+        if (fullw && !last) with_swap(fused, std::true_type{});
         else with_swap(fused, std::false_type{});
     };
     with_epi(add != nullptr, act, with_full);
@@ -970,7 +1063,7 @@ constexpr WideVariant kWide[] = {
 constexpr int kNumWide = (int)(sizeof(kWide) / sizeof(kWide[0]));
 
 int find_wide(const convt_plan &P, Layout *Lout) {
-    if (P.ndim < 2 || P.G != 1 || P.Cog != 64) return -1;
+    if (P.ndim < 2 || P.G != 1 || P.Cog != 64 || P.layout != CONVT_LAYOUT_CHANNELS_FIRST) return -1;
     // one buffer resource spans x (31-bit byte offsets); per-sample y as in the VGPR variant
     if (4 * P.N * P.C_in * P.in_sp >= INT32_MAX || 4 * P.C_out * P.out_sp >= INT32_MAX) return -1;
     const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
@@ -1010,7 +1103,7 @@ int launch_wide(const convt_plan &Pl, const Layout &L, const float *x, const flo
 } // namespace
 
 bool igemm3d_supports(const convt_plan &P) {
-    if (P.ndim < 2 || P.layout != CONVT_LAYOUT_CHANNELS_FIRST) return false;
+    if (P.ndim < 2) return false;
     Layout L;
     if (find_variant(P, &L) < 0 && find_wide(P, &L) < 0) return false;
     return P.N * P.ax[0].L_out * P.ax[1].L_out < (int64_t(1) << 31);
