@@ -498,6 +498,8 @@ def main():
     ap.add_argument("--flushed", type=int, default=20, help="cache-flushed launches per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the calibration kernels (e.g. under a profiler)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--memory-floor", action="store_true",
                     help="run only the calibration kernels and print their figures")
@@ -542,11 +544,13 @@ def main():
                 configs[CONFIG_KEYS[other.name] + "_channels_last"] = rec
     del flusher
     torch.cuda.empty_cache()
-    log("calibration kernels")
-    cal = calibration()
-    for rec in [head] + list(configs.values()):
-        against_measured(rec, cal)
-    if wl.name == S.LONG_1D.name and args.op == "forward":
+    cal = None
+    if not args.no_calibration:
+        log("calibration kernels")
+        cal = calibration()
+        for rec in [head] + list(configs.values()):
+            against_measured(rec, cal)
+    if cal is not None and wl.name == S.LONG_1D.name and args.op == "forward":
         floor = cal["long_1d_layer_pattern"]["ms"]
         head["roofline"]["vs_memory_floor"] = {
             "floor_ms": floor, "floor_what": "the layer's own memory pattern without arithmetic",

@@ -36,6 +36,12 @@
  * each element is read and then written by the same thread.
  *
  * Errors: status codes only; nothing is thrown across this boundary.
+ *
+ * Environment: CONVT_LOG=1 prints one line on stderr per planning decision
+ * (plan creation, convt_plan_set_layout, convt_plan_set_path): the shape,
+ * the path and kernel chosen, and whether the shape fell to a generic kernel
+ * because no specialised one takes it.  CONVT_PATH=generic|stream1d|igemm3d
+ * forces that path on every plan it applies to.
  */
 #ifndef CONVT_H
 #define CONVT_H

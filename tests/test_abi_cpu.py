@@ -226,3 +226,25 @@ def test_layout_selection():
     assert T.lib().convt_plan_get_layout(None) == -1
     T.convt_plan_set_layout(p, "channels_first")
     assert "kernel=k_stream1d\n" in T.convt_plan_describe(p)
+
+
+def test_convt_log_names_kernel_and_fallback():
+    """CONVT_LOG=1: one stderr line per plan with the chosen kernel, and the
+    generic fallback called out (a subprocess, so the variable is read at
+    plan creation)."""
+    import subprocess
+    import sys
+    code = ("import transposed_convolution_forward_amd as T; from transposed_convolution_forward_amd import "
+            "synthetic as S; T.plan_for(S.LONG_1D); T.plan_for(S.GROUPED_3D); "
+            "T.Plan(1, 1, 64, 64, 1, (100,), (3,), (2,), (1,), (0,), (1,))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                       env={**os.environ, "CONVT_LOG": "1"})
+    assert r.returncode == 0, r.stderr
+    lines = [l for l in r.stderr.splitlines() if l.startswith("convt: plan:")]
+    assert len(lines) == 3, r.stderr
+    assert "kernel=k_stream1d" in lines[0] and "fallback" not in lines[0]
+    assert "kernel=k_generic_pairs" in lines[1] and "generic fallback" in lines[1]
+    assert "generic fallback" in lines[2]
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                       env={k: v for k, v in os.environ.items() if k != "CONVT_LOG"})
+    assert "convt:" not in r.stderr

@@ -69,6 +69,36 @@ const char *path_name(convt_path p) {
     return "?";
 }
 
+const char *kernel_name(const convt_plan &P) {
+    const bool last = P.layout == CONVT_LAYOUT_CHANNELS_LAST;
+    return P.path == CONVT_PATH_STREAM1D ? (last ? "k_stream1d_nlc" : "k_stream1d")
+           : P.path == CONVT_PATH_IGEMM3D ? convt::igemm3d_kernel_name(P)
+                                          : convt::generic_kernel_name(P);
+}
+
+// With CONVT_LOG set (to anything but 0), one line on stderr per planning
+// decision: the shape, layout, path and kernel, and whether the shape fell to
+// a generic kernel because no specialised one takes it.
+void log_plan(const convt_plan &P, const char *why) {
+    const char *env = getenv("CONVT_LOG");
+    if (!env || !*env || !strcmp(env, "0")) return;
+    std::string axes;
+    char tmp[160];
+    for (int a = kAxes - P.ndim; a < kAxes; ++a) {
+        const AxisPlan &A = P.ax[a];
+        snprintf(tmp, sizeof tmp, "%s[L=%d K=%d s=%d p=%d op=%d d=%d]", axes.empty() ? "" : " ", A.L_in, A.K, A.s,
+                 A.p, A.op, A.d);
+        axes += tmp;
+    }
+    fprintf(stderr, "convt: %s: ndim=%d N=%lld C_in=%lld C_out=%lld groups=%lld %s layout=%s -> path=%s kernel=%s%s\n",
+            why, P.ndim, (long long)P.N, (long long)P.C_in, (long long)P.C_out, (long long)P.G, axes.c_str(),
+            P.layout == CONVT_LAYOUT_CHANNELS_LAST ? "channels_last" : "channels_first", path_name(P.path),
+            kernel_name(P),
+            P.path == CONVT_PATH_GENERIC && P.auto_path == CONVT_PATH_GENERIC
+                ? " (generic fallback: no specialised kernel takes this shape)"
+                : P.path != P.auto_path ? " (forced)" : "");
+}
+
 // The planner's path for the plan's shape and layout, then the CONVT_PATH
 // environment override (generic, stream1d or igemm3d) where that path applies.
 void select_path(convt_plan &P) {
@@ -177,6 +207,7 @@ convt_status convt_plan_create(convt_plan **plan, int ndim, int64_t N, int64_t C
     }
     if (!convt::generic_supports(*P)) { delete P; return CONVT_ERR_UNSUPPORTED; }
     select_path(*P);
+    log_plan(*P, "plan");
     *plan = P;
     return CONVT_OK;
 }
@@ -191,6 +222,7 @@ convt_status convt_plan_set_layout(convt_plan *plan, int layout) {
         return CONVT_ERR_UNSUPPORTED;
     }
     select_path(*plan);
+    log_plan(*plan, "layout");
     return CONVT_OK;
 }
 
@@ -264,6 +296,7 @@ convt_status convt_plan_set_path(convt_plan *plan, convt_path path) {
         return CONVT_ERR_INVALID_ARG;
     if (!path_supports(*plan, path)) return CONVT_ERR_UNSUPPORTED;
     plan->path = path;
+    log_plan(*plan, "set_path");
     return CONVT_OK;
 }
 
@@ -276,9 +309,7 @@ int64_t convt_plan_describe(const convt_plan *plan, char *buf, int64_t len) {
     std::string s;
     char tmp[256];
     const bool last = plan->layout == CONVT_LAYOUT_CHANNELS_LAST;
-    const char *kernel = plan->path == CONVT_PATH_STREAM1D ? (last ? "k_stream1d_nlc" : "k_stream1d")
-                         : plan->path == CONVT_PATH_IGEMM3D ? convt::igemm3d_kernel_name(*plan)
-                                                            : convt::generic_kernel_name(*plan);
+    const char *kernel = kernel_name(*plan);
     snprintf(tmp, sizeof tmp,
              "convt plan: ndim=%d N=%lld C_in=%lld C_out=%lld groups=%lld layout=%s path=%s kernel=%s\n",
              plan->ndim, (long long)plan->N, (long long)plan->C_in, (long long)plan->C_out,

@@ -221,18 +221,13 @@ template <int S> constexpr int stage_pitch() { return (kLineF + 64 * S + kLineF 
 #ifndef CONVT_S1D_ROUNDS
 #define CONVT_S1D_ROUNDS 1
 #endif
-// Channels-last kernel: waves per SIMD the register allocation must allow;
-// whether a wave stages its outputs in LDS so that each store instruction
-// writes 1 KB of whole lines (1) or stores the accumulator tiles directly
-// (0); the cache policy of its output stores (2: non-temporal, 0: default).
+// Channels-last kernel: waves per SIMD the register allocation must allow,
+// and how many items ahead a wave loads its inputs (1 or 2).
 #ifndef CONVT_NLC_WAVES_PER_EU
 #define CONVT_NLC_WAVES_PER_EU 2
 #endif
-#ifndef CONVT_NLC_STAGE
-#define CONVT_NLC_STAGE 1
-#endif
-#ifndef CONVT_NLC_STORE_POLICY
-#define CONVT_NLC_STORE_POLICY 2
+#ifndef CONVT_NLC_PREFETCH
+#define CONVT_NLC_PREFETCH 2
 #endif
 
 // One workgroup = COG/16 waves; wave w owns output channels 16w .. 16w+15 of
@@ -548,10 +543,10 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
 // ------------------------------------------------------------ channels last
 // The same phase decomposition for x (N, L_in, C_in) and y (N, L_out, C_out).
 // The output of one position is C_out contiguous floats, so an
-// output-stationary tile stores whole lines without any staging: a wave owns
-// 16 consecutive positions q0 .. q0+15 of one (n, g) and all COG output
-// channels (COG/16 accumulator tiles per phase), with every weight of the
-// group in VGPRs.  Waves are independent: no LDS, no barrier.
+// output-stationary tile can store whole lines: a wave owns 16 consecutive
+// positions q0 .. q0+15 of one (n, g) and all COG output channels (COG/16
+// accumulator tiles per phase), with every weight of the group in VGPRs.
+// Waves are independent: no barrier.
 //
 // MFMA D[co][col] = sum_k A[co][k] B[k][col], A = W^T (16 co x 4 ci), B = X
 // (4 ci x 16 positions), column j = position q0 + j.  At step kk the lane
@@ -560,10 +555,21 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
 // channel offsets 16u + 4g4: one load instruction covers 16 positions x 64
 // contiguous bytes.  Positions outside [0, L_in) read zeros through the
 // buffer resource's range check (a negative offset wraps past it).  The
-// accumulator of lane (g4, j), register e, holds channel 16ct + 4g4 + e at
-// position q0 + j: one 16-byte store per (tile, phase), and the tiles ct of
-// one position fill its C_out floats; outputs outside [0, L_out) are dropped
-// by the same range check.
+// inputs of an item are loaded PF items ahead (CONVT_NLC_PREFETCH), in
+// rotating register sets.
+//
+// The accumulator of lane (g4, j), register e, holds channel 16ct + 4g4 + e at
+// position q0 + j.  Stored as they are, one instruction would write half
+// lines (64 of each 128 bytes), which costs HBM bandwidth when the lines are
+// not in the cache (0.44 against 0.30 ms on the long 1D layer after a cache
+// flush).  So each wave stages its item's 16*S outputs x COG channels in its
+// own LDS region (row p = output offset in the item, float4 column c4 stored
+// at c4 ^ key(p), key(p) = (p/S) mod (COG/4): the accumulator writes, 16 lanes
+// j of one g4 on rows S*j + r, and the row reads fall on distinct banks), and
+// each store instruction writes 1 KB of whole lines; add_input is read at the
+// same contiguous offsets.  One wave's LDS accesses are performed in order,
+// so the region needs no barrier.  Outputs outside [0, L_out) are dropped by
+// the range check.
 template <int CIG, int COG, int K, int S, int D, int EPI>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(CONVT_NLC_WAVES_PER_EU))) void k_stream1d_nlc(const Stream1dParams P,
@@ -578,62 +584,73 @@ __attribute__((amdgpu_waves_per_eu(CONVT_NLC_WAVES_PER_EU))) void k_stream1d_nlc
     constexpr int COT = COG / 16;  // accumulator tiles
     constexpr int NC = Ph::cmax() + 1;
     constexpr int NP = Ph::count() > 0 ? Ph::count() : 1;
+    constexpr int PF = CONVT_NLC_PREFETCH;
+    constexpr int C4 = COG / 4;
+    constexpr int SROWS = 16 * S;
+    constexpr int NST = SROWS * C4 / 64; // stores per lane and item
     static_assert(CIG % 16 == 0 && COG % 16 == 0, "tile shape");
+    static_assert(PF == 1 || PF == 2, "prefetch distance");
 
     const int lane = threadIdx.x & 63;
     const int j = lane & 15;
     const int g4 = lane >> 4;
     // uniform across the wave: the item walk and the buffer resources stay in
     // scalar registers
-    const int64_t wave = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t it0 = wave * P.per_block;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t it0 = ((int64_t)blockIdx.x * 4 + wv) * P.per_block;
     const int64_t it_end = it0 + P.per_block < P.total ? it0 + P.per_block : P.total;
     if (it0 >= it_end) return;
 
-    int st = (int)(it0 % P.n_st);
-    int ng = (int)(it0 / P.n_st);
+    __shared__ __attribute__((aligned(16))) float ostage[4][SROWS * COG];
+    float *stg = &ostage[wv][0];
+
     const unsigned xrow = 4u * (unsigned)P.C_in, yrow = 4u * (unsigned)P.C_out;
     const int x_bytes = 4 * P.L_in * P.C_in, y_bytes = 4 * P.L_out * P.C_out;
+    // lane-invariant parts of the load offsets: position j, channel 16u + 4g4
+    unsigned xl[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) xl[u] = (unsigned)j * xrow + 4u * (unsigned)(16 * u + 4 * g4);
 
-    // the lane's part of one input position: channel 16u + 4g4 of the group
+    // the inputs of item (ng_ = n*G + g, tile st_) into xb: per shift c the
+    // uniform offset of position q0 - c and channel g*CIG
     auto fetch = [&](f4 (&xb)[NC][NU], int ng_, int st_) {
-        const int n = ng_ / P.G, g = ng_ - n * P.G;
+        const int n = P.G == 1 ? ng_ : ng_ / P.G, g = ng_ - n * P.G;
         const rsrc_t rx = make_rsrc(const_cast<float *>(x) + (int64_t)n * P.L_in * P.C_in, x_bytes);
-        const int q = (P.st_lo + st_) * 16 + j;
+        const int q0 = (P.st_lo + st_) * 16;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
+        for (int c = 0; c < NC; ++c) {
+            const unsigned su = (unsigned)(q0 - c) * xrow + 4u * (unsigned)(g * CIG);
 #pragma unroll
-            for (int u = 0; u < NU; ++u)
-                xb[c][u] = buf_load4(rx, (unsigned)(q - c) * xrow + 4u * (unsigned)(g * CIG + 16 * u + 4 * g4), 0u);
+            for (int u = 0; u < NU; ++u) xb[c][u] = buf_load4(rx, xl[u] + su, 0u);
+        }
     };
-
-    // Output staging (CONVT_NLC_STAGE): the wave's 16*S outputs x COG channels
-    // of one item, row p = output offset in the item, float4 column c4 stored
-    // at c4 ^ key(p), key(p) = (p/S) mod (COG/4).  The accumulator writes
-    // (lanes j = 0..15 of one g4: rows S*j + r, one column) and the reads
-    // for the stores (16 consecutive float4 of one row) then hit distinct
-    // banks.  Private to the wave: one wave's LDS accesses are performed in
-    // order, so no barrier.
-    constexpr int C4 = COG / 4;
-    constexpr int SROWS = 16 * S;
-    __shared__ __attribute__((aligned(16))) float ostage[CONVT_NLC_STAGE ? 4 : 1][CONVT_NLC_STAGE ? SROWS * COG : 4];
-    float *stg = &ostage[CONVT_NLC_STAGE ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0][0];
 
     float wr[COT][K][NKK]; // A operands: W[g*CIG + ci(kk)][16ct + j][k]
     f4 b4[COT];            // bias of channels 16ct + 4g4 .. +3
-    f4 xa[NC][NU], xb[NC][NU];
-    fetch(xa, ng, st);
-
-    // One item with its inputs in xc; the next item's inputs (the current
-    // one's again after the wave's last item, so that every step issues the
-    // same loads and the compiler's wait counts stay exact) go to xnx.
+    f4 xa[NC][NU], xb[NC][NU], xc[NC][NU];
+    // cursors: the current item (it; ng, st) and the last one whose inputs
+    // were fetched (pit; png, pst), advanced one tile at a time
     int64_t it = it0;
-    auto step = [&](const f4 (&xc)[NC][NU], f4 (&xnx)[NC][NU]) {
-        const int n = ng / P.G, g = ng - n * P.G;
-        int st1 = st + 1, ng1 = ng;
-        if (st1 == P.n_st) { st1 = 0; ++ng1; }
-        const bool has_next = it + 1 < it_end;
-        fetch(xnx, has_next ? ng1 : ng, has_next ? st1 : st);
+    int ng = (int)(it0 / P.n_st), st = (int)(it0 - (int64_t)ng * P.n_st);
+    int64_t pit = it0;
+    int png = ng, pst = st;
+    auto advance = [&](int &ng_, int &st_) {
+        if (++st_ == P.n_st) { st_ = 0; ++ng_; }
+    };
+    fetch(xa, png, pst);
+    if constexpr (PF == 2) {
+        if (pit + 1 < it_end) { ++pit; advance(png, pst); }
+        fetch(xb, png, pst);
+    }
+
+    // One item with its inputs in cur; the inputs of the item PF ahead (the
+    // current one's again past the wave's last item, so that every step
+    // issues the same loads and the compiler's wait counts stay exact) go to
+    // nxt.
+    auto step = [&](const f4 (&cur)[NC][NU], f4 (&nxt)[NC][NU]) {
+        const int n = P.G == 1 ? ng : ng / P.G, g = ng - n * P.G;
+        if (pit + 1 < it_end) { ++pit; advance(png, pst); }
+        fetch(nxt, png, pst);
         // nothing moves across the steps: the scheduler would otherwise pull
         // the next item's MFMAs up to its just-issued loads and wait for them
         __builtin_amdgcn_sched_barrier(0);
@@ -647,7 +664,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_NLC_WAVES_PER_EU))) void k_stream1d_nlc
                 const bool first = k == Ph::first_k(Ph::r_of(k));
 #pragma unroll
                 for (int kk = 0; kk < NKK; ++kk) {
-                    const float bv = xc[c][kk / 4][kk % 4];
+                    const float bv = cur[c][kk / 4][kk % 4];
 #pragma unroll
                     for (int ct = 0; ct < COT; ++ct)
                         acc[sl][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(wr[ct][k][kk], bv,
@@ -657,74 +674,47 @@ __attribute__((amdgpu_waves_per_eu(CONVT_NLC_WAVES_PER_EU))) void k_stream1d_nlc
             }
         }
 
-        // epilogue: phase r of position q0 + j is output o = (q0 + j)*S + r - p
-        const rsrc_t ry = make_rsrc(y + (int64_t)n * P.L_out * P.C_out, y_bytes);
-        const rsrc_t ra = make_rsrc(const_cast<float *>(ADD ? add : y) + (int64_t)n * P.L_out * P.C_out, y_bytes);
-        if constexpr (CONVT_NLC_STAGE != 0) {
+        // stage: phase r of position q0 + j is item row S*j + r
 #pragma unroll
-            for (int r = 0; r < S; ++r)
-#pragma unroll
-                for (int ct = 0; ct < COT; ++ct) {
-                    f4 v = b4[ct];
-                    if constexpr (Ph::count() > 0)
-                        if (Ph::nonempty(r)) v = acc[Ph::slot(r)][ct];
-                    const int c4 = (4 * ct + g4) ^ (j & (C4 - 1));
-                    *reinterpret_cast<f4 *>(stg + (S * j + r) * COG + 4 * c4) = v;
-                }
-            // float4 number f = 64u + lane of the item's outputs: row f / C4,
-            // column f % C4; the stores of one instruction are contiguous
-            const int o0 = (P.st_lo + st) * 16 * S - P.p;
-#pragma unroll
-            for (int u = 0; u < SROWS * C4 / 64; ++u) {
-                const int f = 64 * u + lane;
-                const int row = f / C4, c4 = f % C4;
-                f4 v = *reinterpret_cast<const f4 *>(stg + row * COG + 4 * (c4 ^ ((row / S) & (C4 - 1))));
-                const unsigned off = (unsigned)(o0 + row) * yrow + 4u * (unsigned)(g * COG + 4 * c4);
-                if constexpr (ADD) {
-                    const f4 a = buf_load4(ra, off, 0u);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = finish<EPI>(v[e], a[e]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = activate<EPI>(v[e]);
-                }
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, v),
-                                                       ry, off, 0u, CONVT_NLC_STORE_POLICY);
-            }
-        } else {
-        const int q = (P.st_lo + st) * 16 + j;
-#pragma unroll
-        for (int r = 0; r < S; ++r) {
-            const unsigned o4 = (unsigned)(q * S + r - P.p) * yrow;
+        for (int r = 0; r < S; ++r)
 #pragma unroll
             for (int ct = 0; ct < COT; ++ct) {
-                const unsigned off = o4 + 4u * (unsigned)(g * COG + 16 * ct + 4 * g4);
                 f4 v = b4[ct];
                 if constexpr (Ph::count() > 0)
                     if (Ph::nonempty(r)) v = acc[Ph::slot(r)][ct];
-                if constexpr (ADD) {
-                    const f4 a = buf_load4(ra, off, 0u);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = finish<EPI>(v[e], a[e]);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[e] = activate<EPI>(v[e]);
-                }
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) int, v),
-                                                       ry, off, 0u, CONVT_NLC_STORE_POLICY);
+                const int c4 = (4 * ct + g4) ^ (j & (C4 - 1));
+                *reinterpret_cast<f4 *>(stg + (S * j + r) * COG + 4 * c4) = v;
             }
-        }
+        // store: float4 f = 64u + lane of the item's outputs is row f / C4,
+        // column f % C4; item row p is output o0 + p
+        const rsrc_t ry = make_rsrc(y + (int64_t)n * P.L_out * P.C_out, y_bytes);
+        const rsrc_t ra = make_rsrc(const_cast<float *>(ADD ? add : y) + (int64_t)n * P.L_out * P.C_out, y_bytes);
+        const unsigned so = (unsigned)((P.st_lo + st) * 16 * S - P.p) * yrow + 4u * (unsigned)(g * COG);
+#pragma unroll
+        for (int u = 0; u < NST; ++u) {
+            const int f = 64 * u + lane;
+            const int row = f / C4, c4 = f % C4;
+            f4 v = *reinterpret_cast<const f4 *>(stg + row * COG + 4 * (c4 ^ ((row / S) & (C4 - 1))));
+            const unsigned off = so + (unsigned)row * yrow + 16u * (unsigned)c4;
+            if constexpr (ADD) {
+                const f4 a = buf_load4(ra, off, 0u);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = finish<EPI>(v[e], a[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = activate<EPI>(v[e]);
+            }
+            buf_store4(v, ry, off, 0u);
         }
         __builtin_amdgcn_sched_barrier(0);
-        st = st1;
-        ng = ng1;
         ++it;
+        advance(ng, st);
     };
 
     // Runs of consecutive items of one group share the weights: load them
     // once per run, before the loop that carries the prefetch.
     while (it < it_end) {
-        const int g = ng % P.G;
+        const int g = P.G == 1 ? 0 : ng % P.G;
         const int64_t left = P.G == 1 ? it_end - it : min(it_end - it, (int64_t)(P.n_st - st));
 #pragma unroll
         for (int ct = 0; ct < COT; ++ct) {
@@ -750,17 +740,50 @@ __attribute__((amdgpu_waves_per_eu(CONVT_NLC_WAVES_PER_EU))) void k_stream1d_nlc
             asm volatile("" : "+v"(b4[ct]));
         }
         const int64_t run_end = it + left;
-        // two items per trip with the input buffers swapped (no copies)
-        while (it + 1 < run_end) {
-            step(xa, xb);
-            step(xb, xa);
-        }
-        if (it < run_end) { // an odd item: its prefetch lands in xb; move it
-            step(xa, xb);
+        if constexpr (PF == 1) {
+            // two items per trip with the input sets swapped (no copies)
+            while (it + 1 < run_end) {
+                step(xa, xb);
+                step(xb, xa);
+            }
+            if (it < run_end) { // an odd item: its prefetch lands in xb; move it
+                step(xa, xb);
 #pragma unroll
-            for (int c = 0; c < NC; ++c)
+                for (int c = 0; c < NC; ++c)
 #pragma unroll
-                for (int u = 0; u < NU; ++u) xa[c][u] = xb[c][u];
+                    for (int u = 0; u < NU; ++u) xa[c][u] = xb[c][u];
+            }
+        } else {
+            // three items per trip, the sets rotating: xa and xb hold the next
+            // two items' inputs at every trip start
+            while (it + 2 < run_end) {
+                step(xa, xc);
+                step(xb, xa);
+                step(xc, xb);
+            }
+            // the run's last one or two items; then rotate so that xa and xb
+            // again hold the next two items' inputs (once per run)
+            if (it < run_end) {
+                step(xa, xc);
+                if (it < run_end) {
+                    step(xb, xa);
+#pragma unroll
+                    for (int c = 0; c < NC; ++c)
+#pragma unroll
+                        for (int u = 0; u < NU; ++u) {
+                            xb[c][u] = xa[c][u];
+                            xa[c][u] = xc[c][u];
+                        }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < NC; ++c)
+#pragma unroll
+                        for (int u = 0; u < NU; ++u) {
+                            xa[c][u] = xb[c][u];
+                            xb[c][u] = xc[c][u];
+                        }
+                }
+            }
         }
     }
 }
