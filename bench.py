@@ -120,7 +120,8 @@ def valid_macs(wl, N=None):
 # The source file each kernel is built from; with the headers every kernel
 # includes, it decides whether a stored counter record still describes the
 # kernel that runs.
-KERNEL_SOURCES = {"k_stream1d": "stream1d.hip", "k_igemm3d": "igemm3d.hip", "k_igemm3d_wide": "igemm3d.hip",
+KERNEL_SOURCES = {"k_stream1d": "stream1d.hip", "k_stream1d_nlc": "stream1d.hip", "k_igemm3d": "igemm3d.hip",
+                  "k_igemm3d_wide": "igemm3d.hip", "k_generic_nxc": "generic.hip",
                   "k_generic": "generic.hip", "k_generic_phase": "generic.hip", "k_generic_rows": "generic.hip",
                   "k_generic_pairs": "generic.hip", "k_backward_data": "backward.hip",
                   "k_backward_data_mfma": "backward.hip", "k_backward_data_mfma_row": "backward.hip",
@@ -143,14 +144,18 @@ def source_sha(kernel=None):
     return h.hexdigest()[:16]
 
 
-def traffic_for(wl_name, kernel):
+def traffic_key(wl_name, layout="channels_first"):
+    return wl_name if layout == "channels_first" else f"{wl_name}_{layout}"
+
+
+def traffic_for(wl_name, kernel, layout="channels_first"):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(wl_name)
+        rec = json.load(open(path)).get(traffic_key(wl_name, layout))
     except (OSError, ValueError):
         return None
     if not rec or rec.get("kernel") != kernel or rec.get("source_sha") != source_sha(kernel):
@@ -440,7 +445,7 @@ def measure(wl, op, steps, warmup, path="auto", flushed=20, flusher=None, cpu=Tr
         rate = lambda ms: flops / (ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(rate(ms_launch), 2), "peak": PEAK_FP32_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(rate(ms_launch) / PEAK_FP32_TFLOPS, 4)}
-    roof["traffic"] = traffic_for(wl.name, kernel) if op == "forward" else None
+    roof["traffic"] = traffic_for(wl.name, kernel, layout) if op == "forward" else None
     roof["kernel"] = kernel
     roof["launch_ms"] = round(ms_launch, 5)
     roof["launch_ms_stats"] = stats(launches)
