@@ -140,6 +140,35 @@ __device__ __forceinline__ RowPos decode_row(const Igemm3dParams &P, int cls, in
     return R;
 }
 
+// A row of a class as (sample, D and H input positions relative to the
+// class's first), advanced row by row without dividing.
+struct RowCur {
+    int n, iqd, iqh;
+};
+__device__ __forceinline__ RowCur cursor_at(const Igemm3dParams &P, int cls, int r) {
+    const int nqh = P.cls_nqh[cls], nqd = P.cls_nqd[cls];
+    const int t = r / nqh;
+    return RowCur{t / nqd, t % nqd, r % nqh};
+}
+__device__ __forceinline__ void cursor_next(const Igemm3dParams &P, int cls, RowCur &c) {
+    if (++c.iqh == P.cls_nqh[cls]) {
+        c.iqh = 0;
+        if (++c.iqd == P.cls_nqd[cls]) {
+            c.iqd = 0;
+            ++c.n;
+        }
+    }
+}
+__device__ __forceinline__ RowPos row_at(const Igemm3dParams &P, int cls, const RowCur &c) {
+    RowPos R;
+    R.n = c.n;
+    R.qd = P.cls_qd0[cls] + c.iqd;
+    R.qh = P.cls_qh0[cls] + c.iqh;
+    R.od = P.cls_od0[cls] + c.iqd * P.s_d;
+    R.oh = P.cls_oh0[cls] + c.iqh * P.s_h;
+    return R;
+}
+
 // Buffer resources: a load past num_records returns zeros and a store past it
 // is dropped, so input rows outside the input need no select, and lanes past
 // a row end read harmlessly.  One resource per sample keeps every byte offset
@@ -342,8 +371,8 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     // the compiler's wait counts exact).
     const bool slide_ok = THM == 2 && PER % 2 == 0 && th == 2 && ch1 == ch0 + 1 &&
                           SLOTS * (CIG / 4) * P.W_in == PER * NT;
-    const int nqh = P.cls_nqh[cls];
-    auto slide_of = [&](int k) { return slide_ok && k > r_begin && k % nqh != 0; };
+    // row k (at cursor c) slides unless it starts its chunk or an H run
+    auto slide_of = [&](int k, const RowCur &c) { return slide_ok && k > r_begin && c.iqh != 0; };
     auto fetch_rows = [&](f4 (&rv)[PER], const RowPos &Q, bool slide) {
         unsigned bad = 0xffffffffu; // bit slot clear: the slot's input row exists
 #pragma unroll
@@ -430,10 +459,16 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     f4 pre0[PER], pre1[PER];
     AddRegs av, avn;
     RowPos R = decode_row(P, cls, r_begin);
+    // cursors of rows min(r+1, r_end-1) and min(r+2, r_end-1) of step r, with
+    // their slide flags
+    RowCur c1 = cursor_at(P, cls, min(r_begin + 1, r_end - 1));
+    RowCur c2 = cursor_at(P, cls, min(r_begin + 2, r_end - 1));
+    bool sl1 = slide_of(min(r_begin + 1, r_end - 1), c1);
+    bool sl2 = slide_of(min(r_begin + 2, r_end - 1), c2);
     __syncthreads(); // LDS zeroed before the first row lands
     fetch_rows(pre0, R, false);
     store_rows(lds[0], pre0, false, lds[1]);
-    fetch_rows(pre0, decode_row(P, cls, min(r_begin + 1, r_end - 1)), slide_of(min(r_begin + 1, r_end - 1)));
+    fetch_rows(pre0, row_at(P, cls, c1), sl1);
     if constexpr (FUSED) fetch_add(av, R);
     __syncthreads();
 
@@ -445,11 +480,10 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     // the two buffers), so buffer addresses are immediate offsets.
     auto row_step = [&](const int r, const auto &av, auto &avn, auto &pre, auto &pre2, auto bufc) {
         constexpr int buf = decltype(bufc)::value;
-        const bool has_next = r + 1 < r_end;
         // x rows of row r+2 (into pre2), then add_input of row r+1; pre holds
         // the x rows of row r+1, fetched a row earlier
-        const RowPos Rn = decode_row(P, cls, has_next ? r + 1 : r);
-        fetch_rows(pre2, decode_row(P, cls, min(r + 2, r_end - 1)), slide_of(min(r + 2, r_end - 1)));
+        const RowPos Rn = row_at(P, cls, c1);
+        fetch_rows(pre2, row_at(P, cls, c2), sl2);
         if constexpr (FUSED) fetch_add(avn, Rn);
 
         // The bias enters as the accumulators' start value: the first MFMA of
@@ -515,7 +549,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
         // row's fetch.
 #pragma unroll
         for (int u = 0; u < PER; ++u) asm volatile("" : "+v"(pre[u]));
-        store_rows(lds[buf ^ 1], pre, slide_of(min(r + 1, r_end - 1)), lds[buf]);
+        store_rows(lds[buf ^ 1], pre, sl1, lds[buf]);
 
         // epilogue: lane (g4, j) owns co = 16ct + 4g4 + e, ow = SW*(16t + j) + rr
         const rsrc_t ry = make_rsrc(y + (int64_t)R.n * P.C_out * dhw_out, ybytes);
@@ -589,6 +623,12 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
 
         __syncthreads();
         R = Rn;
+        c1 = c2;
+        sl1 = sl2;
+        if (r + 3 <= r_end - 1) {
+            cursor_next(P, cls, c2);
+            sl2 = slide_of(r + 3, c2);
+        }
     };
     for (int r = r_begin; r < r_end; r += 2) {
         row_step(r, av, avn, pre0, pre1, std::integral_constant<int, 0>{});
