@@ -55,6 +55,15 @@ REDUCED = [
                (1, 1, 1), (1, 1, 1), False, False, wid=3104),
     S.Workload("ig_k3s2_w20", 3, 1, 32, 64, 1, (2, 3, 20), (3, 3, 3), (2, 2, 2), (1, 1, 1),
                (1, 1, 1), (1, 1, 1), True, True, wid=3105),
+    # multi-row steps (classes of one or two D x H taps take 4 or 2 rows along
+    # H per step): every light class multi-row; mixed with single-row classes
+    # whose H runs do not split into whole steps; two taps along D (K_H = 2)
+    S.Workload("ig_multirow_fused", 3, 2, 32, 64, 1, (3, 8, 16), (3, 3, 3), (2, 2, 2), (1, 1, 1),
+               (1, 1, 1), (1, 1, 1), True, True, wid=3106),
+    S.Workload("ig_multirow_mixed", 3, 3, 32, 64, 1, (4, 5, 16), (3, 3, 3), (2, 2, 2), (1, 1, 1),
+               (1, 0, 1), (1, 1, 1), True, False, wid=3107),
+    S.Workload("ig_multirow_kh2", 3, 2, 32, 64, 1, (3, 8, 16), (3, 2, 3), (2, 2, 2), (1, 0, 1),
+               (1, 0, 1), (1, 1, 1), False, True, wid=3108),
     # channel-heavy shapes (weights streamed through LDS): two W-blocks, a
     # ragged last W-block, 64 input channels, fused
     reduced(S.HEAVY_3D, N=1, in_size=(3, 4, 32)),

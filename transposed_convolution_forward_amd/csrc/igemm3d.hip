@@ -60,6 +60,11 @@ __device__ __forceinline__ f4 load4u(const float *p) {
 #define CONVT_IG_XCD_ORDER 1
 #endif
 
+// Tuning knob: classes with one or two D x H taps take 4 or 2 rows per step.
+#ifndef CONVT_IG_MULTIROW
+#define CONVT_IG_MULTIROW 1
+#endif
+
 // Tuning knob: minimum waves per SIMD the register allocation must allow.
 #ifndef CONVT_IG_WAVES_PER_EU
 #define CONVT_IG_WAVES_PER_EU 3
@@ -115,6 +120,7 @@ struct Igemm3dParams {
     int xcd_order;                   // 1: each XCD walks a contiguous range of a class's chunks
     int x_bytes;                     // bytes of x (wide variant: one buffer resource over it)
     int cls_rows[kMaxClasses];
+    int cls_rstep[kMaxClasses]; // output rows per step: 1, or 4 / taps for classes of 1 or 2 D x H taps
     int cls_td[kMaxClasses], cls_th[kMaxClasses];
     int cls_kd[kMaxClasses][kTapMax], cls_cd[kMaxClasses][kTapMax];
     int cls_kh[kMaxClasses][kTapMax], cls_ch[kMaxClasses][kTapMax];
@@ -270,42 +276,68 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     const int r_end = min(r_begin + P.rows_per_block, P.cls_rows[cls]);
     if (r_begin >= r_end) return;
     const int td = P.cls_td[cls], th = P.cls_th[cls];
+    // Rows per step.  A class with one or two D x H taps (set by the host when
+    // its H run length allows) takes 4 or 2 consecutive rows along H per step,
+    // so that its steps issue as many MFMAs as those of a four-tap class and
+    // the per-step costs (row set-up, barrier, waits) are shared.  Its LDS
+    // slot s then holds tap t = s mod taps of row s / taps, and its weights
+    // sit in tap order (tap t at flat slot t, whether the taps lie along D
+    // or H).
+    const int ntaps = td * th;
+    const bool flat = P.cls_rstep[cls] > 1;
+    // flat slot t of a one- or two-tap class -> its (D tap, H tap)
+    auto flat_tap = [&](int t, int &ajd, int &ajh) {
+        ajd = th == 1 ? t : 0;
+        ajh = th == 1 ? 0 : t;
+    };
 
     // zero both buffers once: halo columns and unused slots stay zero
     for (int i = tid; i < 2 * SLOTS * SLOT_SZ; i += NT) (&lds[0][0])[i] = 0.0f;
 
     // the class's weights for this wave's channels: W[4cig + g4][16ct + j][kd][kh][kw]
-    float wr[TDM][THM][KW][NCIG];
+    // The class's weights for this wave's channels, W[4cig + g4][16ct + j][kd]
+    // [kh][kw], into flat tap slots 0 .. NW-1 (each step mode loads its own
+    // set, so that the register allocator sees one set per mode).
+    auto load_weights = [&](float (&wr)[TDM][THM][KW][NCIG], auto nwc) {
+        constexpr int NW = decltype(nwc)::value;
 #pragma unroll
-    for (int jd = 0; jd < TDM; ++jd)
+        for (int jd = 0; jd < TDM; ++jd)
 #pragma unroll
-        for (int jh = 0; jh < THM; ++jh) {
-            const bool used = jd < td && jh < th;
-            const int kd = used ? P.cls_kd[cls][jd] : 0;
-            const int kh = used ? P.cls_kh[cls][jh] : 0;
-#pragma unroll
-            for (int kw = 0; kw < KW; ++kw)
-#pragma unroll
-                for (int cig = 0; cig < NCIG; ++cig) {
-                    const int64_t idx =
-                        ((((int64_t)(4 * cig + g4) * COG + 16 * ct + j) * P.KD + kd) * P.KH + kh) *
-                            KW + kw;
-                    const float v = w[idx];
-                    wr[jd][jh][kw][cig] = used ? v : 0.0f;
+            for (int jh = 0; jh < THM; ++jh) {
+                if (jd * THM + jh >= NW) continue;
+                bool used = jd < td && jh < th;
+                int ajd = jd, ajh = jh;
+                if (flat) {
+                    used = jd * THM + jh < ntaps;
+                    flat_tap(jd * THM + jh, ajd, ajh);
                 }
-        }
+                const int kd = used ? P.cls_kd[cls][ajd] : 0;
+                const int kh = used ? P.cls_kh[cls][ajh] : 0;
+#pragma unroll
+                for (int kw = 0; kw < KW; ++kw)
+#pragma unroll
+                    for (int cig = 0; cig < NCIG; ++cig) {
+                        const int64_t idx =
+                            ((((int64_t)(4 * cig + g4) * COG + 16 * ct + j) * P.KD + kd) * P.KH + kh) *
+                                KW + kw;
+                        const float v = w[idx];
+                        wr[jd][jh][kw][cig] = used ? v : 0.0f;
+                    }
+            }
+        // wait for these here, not inside the row loop (vmcnt is in order)
+#pragma unroll
+        for (int jd = 0; jd < TDM; ++jd)
+#pragma unroll
+            for (int jh = 0; jh < THM; ++jh)
+#pragma unroll
+                for (int kw = 0; kw < KW; ++kw)
+#pragma unroll
+                    for (int cig = 0; cig < NCIG; ++cig)
+                        if (jd * THM + jh < NW) asm volatile("" : "+v"(wr[jd][jh][kw][cig]));
+    };
     float bo[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) bo[e] = bias ? bias[16 * ct + 4 * g4 + e] : 0.0f;
-    // wait for these here, not inside the row loop (vmcnt is in order)
-#pragma unroll
-    for (int jd = 0; jd < TDM; ++jd)
-#pragma unroll
-        for (int jh = 0; jh < THM; ++jh)
-#pragma unroll
-            for (int kw = 0; kw < KW; ++kw)
-#pragma unroll
-                for (int cig = 0; cig < NCIG; ++cig) asm volatile("" : "+v"(wr[jd][jh][kw][cig]));
 #pragma unroll
     for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(bo[e]));
 
@@ -354,8 +386,15 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
             const int ci = rem / W4, c4 = rem - ci * W4;
             const int jh = sq / TDM, jd = sq % TDM;
             const int slot = jd * THM + jh;
-            const int cd = jd == 0 ? cd0 : cd1, ch = jh == 0 ? ch0 : ch1;
-            xo4[u] = 4 * (ci * dhw + 4 * c4 - (cd * P.H_in + ch) * P.W_in);
+            int cd = jd == 0 ? cd0 : cd1, ch = jh == 0 ? ch0 : ch1, q = 0;
+            if (flat) { // tap slot % taps of row slot / taps
+                q = ntaps == 1 ? slot : slot >> 1;
+                int ajd, ajh;
+                flat_tap(slot - q * ntaps, ajd, ajh);
+                cd = ajd == 0 ? cd0 : cd1;
+                ch = ajh == 0 ? ch0 : ch1;
+            }
+            xo4[u] = 4 * (ci * dhw + 4 * c4 - (cd * P.H_in + ch - q) * P.W_in);
             lo[u] = f < nf ? (slot * CIG + ci) * PWM + 4 * c4 - P.iw_lo : -1;
             tb[u] = f < nf ? slot : 31;
         }
@@ -369,21 +408,41 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
     // staged: they are copied from there, and their loads are issued out of
     // range (no traffic; the number of loads per row stays fixed, which keeps
     // the compiler's wait counts exact).
-    const bool slide_ok = THM == 2 && PER % 2 == 0 && th == 2 && ch1 == ch0 + 1 &&
+    const bool slide_ok = !flat && THM == 2 && PER % 2 == 0 && th == 2 && ch1 == ch0 + 1 &&
                           SLOTS * (CIG / 4) * P.W_in == PER * NT;
+    // Per LDS slot s = jd*THM + jh: the input row it holds, relative to the
+    // step's (first) row, at D offset sdd[s] and H offset sdh[s]; bit s of
+    // sused is set when the class uses the slot.
+    int sdd[SLOTS], sdh[SLOTS];
+    unsigned sused = 0;
+#pragma unroll
+    for (int jd = 0; jd < TDM; ++jd)
+#pragma unroll
+        for (int jh = 0; jh < THM; ++jh) {
+            const int sl = jd * THM + jh;
+            int ajd = jd, ajh = jh, q = 0;
+            bool used = jd < td && jh < th;
+            if (flat) {
+                q = ntaps == 1 ? sl : sl >> 1;
+                flat_tap(sl - q * ntaps, ajd, ajh);
+                used = true;
+            }
+            sdd[sl] = -(ajd == 0 ? cd0 : cd1);
+            sdh[sl] = q - (ajh == 0 ? ch0 : ch1);
+            sused |= (unsigned)used << sl;
+        }
     // row k (at cursor c) slides unless it starts its chunk or an H run
     auto slide_of = [&](int k, const RowCur &c) { return slide_ok && k > r_begin && c.iqh != 0; };
     auto fetch_rows = [&](f4 (&rv)[PER], const RowPos &Q, bool slide) {
         unsigned bad = 0xffffffffu; // bit slot clear: the slot's input row exists
 #pragma unroll
-        for (int jd = 0; jd < TDM; ++jd)
-#pragma unroll
-            for (int jh = 0; jh < THM; ++jh) {
-                const int id = Q.qd - (jd == 0 ? cd0 : cd1), ih = Q.qh - (jh == 0 ? ch0 : ch1);
-                if (jd < td && jh < th && id >= 0 && id < P.D_in && ih >= 0 && ih < P.H_in &&
-                    !(slide && jh == 1))
-                    bad &= ~(1u << (jd * THM + jh));
-            }
+        for (int sl = 0; sl < SLOTS; ++sl) {
+            const int id = Q.qd + sdd[sl], ih = Q.qh + sdh[sl];
+            // bitwise, not short-circuit: no branch per condition
+            const bool ok = ((sused >> sl) & 1u) & ((unsigned)id < (unsigned)P.D_in) &
+                            ((unsigned)ih < (unsigned)P.H_in) & !(slide & (sl % THM == 1));
+            bad &= ~((unsigned)ok << sl);
+        }
         const rsrc_t rx = make_rsrc(x + (int64_t)Q.n * P.C_in * dhw, xbytes);
         const int rowx4 = 4 * (Q.qd * P.H_in + Q.qh) * P.W_in * (LAST ? CIG : 1);
 #pragma unroll
@@ -424,15 +483,20 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
             lst[u] = pp < P.W_out ? 4u * (unsigned)(pp * COG + 4 * c4) : kOutOfRange;
         }
     }
+    // add_input registers of one output row; the multi-row modes hold up to 4
     using AddRegs = std::conditional_t<LAST, f4[NSO], float[NWBM][4][SW]>;
-    auto fetch_add = [&](AddRegs &a, const RowPos &Q) {
+    constexpr bool MULTI = !LAST && SLOTS == 4 && NWBM == 1; // multi-row steps compiled in
+    constexpr int RMAX = MULTI ? 4 : 1;
+    // byte offset of the next output row along H (rows of a multi-row step)
+    const unsigned dhy4 = 4u * (unsigned)(P.s_h * P.W_out * (LAST ? COG : 1));
+    auto fetch_add = [&](AddRegs &a, const RowPos &Q, unsigned dq) {
         const rsrc_t ra = make_rsrc(add + (int64_t)Q.n * P.C_out * dhw_out, ybytes);
         if constexpr (LAST) {
 #pragma unroll
-            for (int u = 0; u < NSO; ++u) a[u] = buf_load4nt(ra, row_off4(Q) + lst[u]);
+            for (int u = 0; u < NSO; ++u) a[u] = buf_load4nt(ra, row_off4(Q) + dq + lst[u]);
             return;
         } else {
-        const unsigned vo = lane4 + row_off4(Q);
+        const unsigned vo = lane4 + row_off4(Q) + dq;
 #pragma unroll
         for (int t = 0; t < NWBM; ++t)
 #pragma unroll
@@ -450,165 +514,66 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
         }
     };
 
-    // Input rows are fetched two rows ahead, before the current row's stores:
-    // the vector-memory counter retires in issue order, so the wait for them
-    // then covers only stores issued two rows earlier.  (With rows that
-    // every lane fills, FULLW, each path issues the same stores and the
-    // compiler's wait counts stay exact.)  Past the block's last row the last
-    // row is fetched again, never used.
-    f4 pre0[PER], pre1[PER];
-    AddRegs av, avn;
-    RowPos R = decode_row(P, cls, r_begin);
-    // cursors of rows min(r+1, r_end-1) and min(r+2, r_end-1) of step r, with
-    // their slide flags
-    RowCur c1 = cursor_at(P, cls, min(r_begin + 1, r_end - 1));
-    RowCur c2 = cursor_at(P, cls, min(r_begin + 2, r_end - 1));
-    bool sl1 = slide_of(min(r_begin + 1, r_end - 1), c1);
-    bool sl2 = slide_of(min(r_begin + 2, r_end - 1), c2);
-    __syncthreads(); // LDS zeroed before the first row lands
-    fetch_rows(pre0, R, false);
-    store_rows(lds[0], pre0, false, lds[1]);
-    fetch_rows(pre0, row_at(P, cls, c1), sl1);
-    if constexpr (FUSED) fetch_add(av, R);
-    __syncthreads();
-
     const f4 bias4 = f4{bo[0], bo[1], bo[2], bo[3]};
     static_assert(!SWAP || SW == 2, "the phase swap is for two W phases");
-    // One output row; the loop below runs it twice per trip with the two
-    // add_input register sets swapped, so the prefetched set needs no copy,
-    // and with the LDS buffer as a compile-time index (rows alternate between
-    // the two buffers), so buffer addresses are immediate offsets.
-    auto row_step = [&](const int r, const auto &av, auto &avn, auto &pre, auto &pre2, auto bufc) {
-        constexpr int buf = decltype(bufc)::value;
-        // x rows of row r+2 (into pre2), then add_input of row r+1; pre holds
-        // the x rows of row r+1, fetched a row earlier
-        const RowPos Rn = row_at(P, cls, c1);
-        fetch_rows(pre2, row_at(P, cls, c2), sl2);
-        if constexpr (FUSED) fetch_add(avn, Rn);
 
-        // The bias enters as the accumulators' start value: the first MFMA of
-        // each W phase takes it as its accumulator input.  Rows of a class
-        // without taps keep the bias.
-        f4 acc[NPH][NWBM];
-        if (Ph::count() == 0 || td == 0 || th == 0) {
+    // Epilogue of one output row (its accumulators ac, add_input a, byte
+    // offset dq past row R): lane (g4, j) owns co = 16ct + 4g4 + e,
+    // ow = SW*(16t + j) + rr.  W phase 0 on the odd outputs (swapped) is
+    // fixed for the launch, so a template flag (as a runtime flag the
+    // compiler turns the two orders into per-element selects).
+    auto epi_row = [&](const RowPos &R, const f4 (&ac)[NPH][NWBM], const AddRegs &a, unsigned dq, auto swapped) {
+        const rsrc_t ry = make_rsrc(y + (int64_t)R.n * P.C_out * dhw_out, ybytes);
+        const unsigned vo_row = row_off4(R) + dq;
+        const unsigned vo = lane4 + vo_row;
 #pragma unroll
-            for (int s = 0; s < NPH; ++s)
+        for (int t = 0; t < NWBM; ++t) {
+            const int ow0 = SW * (16 * t + j);
 #pragma unroll
-                for (int t = 0; t < NWBM; ++t) acc[s][t] = bias4;
-        } else if constexpr (Ph::count() > 0) {
-            // per W phase, this lane's B column in LDS: every read below is
-            // then this base plus a compile-time offset
-            // one base per (W phase, tap shift): the reads below are then the
-            // base plus multiples of 64 floats (channel and slot pitches), which
-            // paired LDS reads reach without address arithmetic
-            // (the empty asm hides how the bases relate, or the compiler would pair
-            // reads one float apart and rebuild a base for every pair)
-            typedef const __attribute__((address_space(3))) float *lds_ptr;
-            constexpr int CM = Ph::cmax() + 1;
-            lds_ptr bcol[SW][CM];
+            for (int e = 0; e < 4; ++e) {
+                float v[SW];
+                if constexpr (SW == 2 && NPH == 2) {
+                    v[0] = ac[decltype(swapped)::value ? 1 : 0][t][e];
+                    v[1] = ac[decltype(swapped)::value ? 0 : 1][t][e];
+                } else {
 #pragma unroll
-            for (int rw = 0; rw < SW; ++rw)
+                    for (int rr = 0; rr < SW; ++rr) v[rr] = bo[e];
 #pragma unroll
-                for (int c = 0; c < CM; ++c) {
-                    bcol[rw][c] = LAST ? (lds_ptr)(lds[buf] + (j + P.qw0[rw] - c - P.iw_lo) * PCL + g4)
-                                       : (lds_ptr)(lds[buf] + g4 * PWM - P.iw_lo + j + P.qw0[rw] - c);
-                    asm volatile("" : "+v"(bcol[rw][c]));
-                }
+                    for (int rw = 0; rw < SW; ++rw) {
+                        if constexpr (Ph::count() > 0) {
+                            if (Ph::nonempty(rw)) {
+                                const float av = ac[Ph::slot(rw)][t][e];
 #pragma unroll
-            for (int jd = 0; jd < TDM; ++jd) {
-                if (jd > 0 && jd >= td) break;
-#pragma unroll
-                for (int jh = 0; jh < THM; ++jh) {
-                    if (jh > 0 && jh >= th) break;
-                    const int slot = jd * THM + jh;
-#pragma unroll
-                    for (int cig = 0; cig < NCIG; ++cig) {
-#pragma unroll
-                        for (int kw = 0; kw < KW; ++kw) {
-                            const int rw = Ph::r_of(kw);
-                            const int sl = Ph::slot(rw);
-                            const int c = Ph::c_of(kw);
-#pragma unroll
-                            for (int t = 0; t < NWBM; ++t) {
-                                const float bv = LAST ? bcol[rw][c][slot * SLOT_SZ + 4 * cig + 16 * t * PCL]
-                                                      : bcol[rw][c][(slot * CIG + 4 * cig) * PWM + 16 * t];
-                                const bool first = jd == 0 && jh == 0 && cig == 0 && kw == Ph::first_k(rw);
-                                acc[sl][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                    wr[jd][jh][kw][cig], bv, first ? bias4 : acc[sl][t], 0, 0, 0);
+                                for (int rr = 0; rr < SW; ++rr)
+                                    if (P.sigma[rw] == rr) v[rr] = av;
                             }
                         }
                     }
+                }
+                if constexpr (LAST) { // staged as they are; the epilogue follows the read back
+                    const int c4 = (4 * ct + g4) ^ ((16 * t + j) & (OC4 - 1));
+#pragma unroll
+                    for (int rr = 0; rr < SW; ++rr) ost[(ow0 + rr) * COG + 4 * c4 + e] = v[rr];
+                    continue;
+                } else {
+#pragma unroll
+                    for (int rr = 0; rr < SW; ++rr) v[rr] = finish<EPI>(v[rr], FUSED ? a[t][e][rr] : 0.0f);
+                }
+                const unsigned o = vo + 4 * SW * 16 * t;
+                if (FULLW || ow0 + SW <= P.W_out) {
+                    if constexpr (SW == 2) {
+                        buf_store2(v[0], v[1], ry, o, e * e4);
+                    } else {
+#pragma unroll
+                        for (int rr = 0; rr < SW; ++rr) buf_store1(v[rr], ry, o + 4 * rr, e * e4);
+                    }
+                } else {
+#pragma unroll
+                    for (int rr = 0; rr < SW; ++rr)
+                        if (ow0 + rr < P.W_out) buf_store1(v[rr], ry, o + 4 * rr, e * e4);
                 }
             }
         }
-
-        // The next row's inputs go to the other LDS buffer (free since the last
-        // barrier) before this row's stores: the vector-memory counter retires
-        // in issue order, so the wait for them must not follow the stores.
-        // Unconditional, so that no path leaves them pending into the next
-        // row's fetch.
-#pragma unroll
-        for (int u = 0; u < PER; ++u) asm volatile("" : "+v"(pre[u]));
-        store_rows(lds[buf ^ 1], pre, sl1, lds[buf]);
-
-        // epilogue: lane (g4, j) owns co = 16ct + 4g4 + e, ow = SW*(16t + j) + rr
-        const rsrc_t ry = make_rsrc(y + (int64_t)R.n * P.C_out * dhw_out, ybytes);
-        const unsigned vo = lane4 + row_off4(R);
-        const unsigned vo_row = row_off4(R);
-        auto epi = [&](auto swapped) {
-#pragma unroll
-            for (int t = 0; t < NWBM; ++t) {
-                const int ow0 = SW * (16 * t + j);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float v[SW];
-                    if constexpr (SW == 2 && NPH == 2) {
-                        v[0] = acc[decltype(swapped)::value ? 1 : 0][t][e];
-                        v[1] = acc[decltype(swapped)::value ? 0 : 1][t][e];
-                    } else {
-#pragma unroll
-                        for (int rr = 0; rr < SW; ++rr) v[rr] = bo[e];
-#pragma unroll
-                        for (int rw = 0; rw < SW; ++rw) {
-                            if constexpr (Ph::count() > 0) {
-                                if (Ph::nonempty(rw)) {
-                                    const float a = acc[Ph::slot(rw)][t][e];
-#pragma unroll
-                                    for (int rr = 0; rr < SW; ++rr)
-                                        if (P.sigma[rw] == rr) v[rr] = a;
-                                }
-                            }
-                        }
-                    }
-                    if constexpr (LAST) { // staged as they are; the epilogue follows the read back
-                        const int c4 = (4 * ct + g4) ^ ((16 * t + j) & (OC4 - 1));
-#pragma unroll
-                        for (int rr = 0; rr < SW; ++rr) ost[(ow0 + rr) * COG + 4 * c4 + e] = v[rr];
-                        continue;
-                    } else {
-#pragma unroll
-                    for (int rr = 0; rr < SW; ++rr) v[rr] = finish<EPI>(v[rr], FUSED ? av[t][e][rr] : 0.0f);
-                    }
-                    const unsigned o = vo + 4 * SW * 16 * t;
-                    if (FULLW || ow0 + SW <= P.W_out) {
-                        if constexpr (SW == 2) {
-                            buf_store2(v[0], v[1], ry, o, e * e4);
-                        } else {
-#pragma unroll
-                            for (int rr = 0; rr < SW; ++rr) buf_store1(v[rr], ry, o + 4 * rr, e * e4);
-                        }
-                    } else {
-#pragma unroll
-                        for (int rr = 0; rr < SW; ++rr)
-                            if (ow0 + rr < P.W_out) buf_store1(v[rr], ry, o + 4 * rr, e * e4);
-                    }
-                }
-            }
-        };
-        // W phase 0 on the odd outputs: fixed for the launch, so a template
-        // flag (as a runtime flag the compiler turns the two orders into
-        // per-element selects)
-        epi(std::integral_constant<bool, SWAP>{});
         if constexpr (LAST) {
             __syncthreads();
 #pragma unroll
@@ -616,24 +581,187 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
                 const int f = NT * u + tid, pp = f / OC4, c4 = f % OC4;
                 f4 v = *reinterpret_cast<const f4 *>(&ost[pp * COG + 4 * (c4 ^ ((pp / SW) & (OC4 - 1)))]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = finish<EPI>(v[e], FUSED ? av[u][e] : 0.0f);
+                for (int e = 0; e < 4; ++e) v[e] = finish<EPI>(v[e], FUSED ? a[u][e] : 0.0f);
                 buf_store4(v, ry, vo_row + lst[u]);
             }
         }
+    };
 
+    // Steps of RS rows (template MODE: 0 one row, any taps; 1 or 2 taps per
+    // row, 4 / MODE rows along H).  Input rows are fetched two steps ahead,
+    // before the current step's stores: the vector-memory counter retires in
+    // issue order, so the wait for them then covers only stores issued two
+    // steps earlier.  (With rows that every lane fills, FULLW, each path
+    // issues the same stores and the compiler's wait counts stay exact.)  Past
+    // the block's last step the last step is fetched again, never used.
+    auto run = [&](auto modec) {
+        constexpr int MODE = decltype(modec)::value;
+        constexpr int RS = MODE == 0 ? 1 : 4 / MODE;
+        float wr[TDM][THM][KW][NCIG];
+        load_weights(wr, std::integral_constant<int, MODE == 0 ? TDM * THM : MODE>{});
+        f4 pre0[PER], pre1[PER];
+        AddRegs av[RS], avn[RS];
+        RowPos R = decode_row(P, cls, r_begin);
+        // cursors of the first rows of steps r+RS and r+2RS (clamped to the
+        // last step), with their slide flags
+        RowCur c1 = cursor_at(P, cls, min(r_begin + RS, r_end - RS));
+        RowCur c2 = cursor_at(P, cls, min(r_begin + 2 * RS, r_end - RS));
+        bool sl1 = slide_of(min(r_begin + 1, r_end - 1), c1);
+        bool sl2 = slide_of(min(r_begin + 2, r_end - 1), c2);
+        __syncthreads(); // LDS zeroed before the first row lands
+        fetch_rows(pre0, R, false);
+        store_rows(lds[0], pre0, false, lds[1]);
+        fetch_rows(pre0, row_at(P, cls, c1), sl1);
+        if constexpr (FUSED && MODE == 0) fetch_add(av[0], R, 0);
         __syncthreads();
-        R = Rn;
-        c1 = c2;
-        sl1 = sl2;
-        if (r + 3 <= r_end - 1) {
-            cursor_next(P, cls, c2);
-            sl2 = slide_of(r + 3, c2);
+
+        // One step; the loop below runs it twice per trip with the two
+        // add_input register sets swapped, so the prefetched set needs no
+        // copy, and with the LDS buffer as a compile-time index (steps
+        // alternate between the two buffers), so buffer addresses are
+        // immediate offsets.
+        auto step = [&](const int r, auto &avc, auto &avp, auto &pre, auto &pre2, auto bufc) {
+            constexpr int buf = decltype(bufc)::value;
+            // Single rows: x rows of row r+2 (into pre2), then add_input of
+            // row r+1 (a row ahead).  Multi-row steps: add_input of this
+            // step's rows first (their registers would not fit twice; the
+            // step's MFMAs cover the latency), then x rows of step r+2RS.  pre
+            // holds the x rows of step r+RS, fetched a step earlier.
+            const RowPos Rn = row_at(P, cls, c1);
+            if constexpr (FUSED && MODE > 0) {
+#pragma unroll
+                for (int q = 0; q < RS; ++q) fetch_add(avc[q], R, q * dhy4);
+            }
+            fetch_rows(pre2, row_at(P, cls, c2), sl2);
+            if constexpr (FUSED && MODE == 0) fetch_add(avp[0], Rn, 0);
+
+            // The bias enters as the accumulators' start value: the first MFMA
+            // of each W phase takes it as its accumulator input.  Rows of a
+            // class without taps keep the bias.
+            f4 acc[RS][NPH][NWBM];
+            if (Ph::count() == 0 || td == 0 || th == 0) {
+#pragma unroll
+                for (int q = 0; q < RS; ++q)
+#pragma unroll
+                    for (int s = 0; s < NPH; ++s)
+#pragma unroll
+                        for (int t = 0; t < NWBM; ++t) acc[q][s][t] = bias4;
+            } else if constexpr (Ph::count() > 0) {
+                // one base per (W phase, tap shift): the reads below are then the
+                // base plus multiples of 64 floats (channel and slot pitches), which
+                // paired LDS reads reach without address arithmetic
+                // (the empty asm hides how the bases relate, or the compiler would pair
+                // reads one float apart and rebuild a base for every pair)
+                typedef const __attribute__((address_space(3))) float *lds_ptr;
+                constexpr int CM = Ph::cmax() + 1;
+                lds_ptr bcol[SW][CM];
+#pragma unroll
+                for (int rw = 0; rw < SW; ++rw)
+#pragma unroll
+                    for (int c = 0; c < CM; ++c) {
+                        bcol[rw][c] = LAST ? (lds_ptr)(lds[buf] + (j + P.qw0[rw] - c - P.iw_lo) * PCL + g4)
+                                           : (lds_ptr)(lds[buf] + g4 * PWM - P.iw_lo + j + P.qw0[rw] - c);
+                        asm volatile("" : "+v"(bcol[rw][c]));
+                    }
+                auto bread = [&](int rw, int c, int slot, int cig, int t) {
+                    return LAST ? bcol[rw][c][slot * SLOT_SZ + 4 * cig + 16 * t * PCL]
+                                : bcol[rw][c][(slot * CIG + 4 * cig) * PWM + 16 * t];
+                };
+                if constexpr (MODE == 0) {
+#pragma unroll
+                    for (int jd = 0; jd < TDM; ++jd) {
+                        if (jd > 0 && jd >= td) break;
+#pragma unroll
+                        for (int jh = 0; jh < THM; ++jh) {
+                            if (jh > 0 && jh >= th) break;
+                            const int slot = jd * THM + jh;
+#pragma unroll
+                            for (int cig = 0; cig < NCIG; ++cig) {
+#pragma unroll
+                                for (int kw = 0; kw < KW; ++kw) {
+                                    const int rw = Ph::r_of(kw);
+                                    const int sl = Ph::slot(rw);
+                                    const int c = Ph::c_of(kw);
+#pragma unroll
+                                    for (int t = 0; t < NWBM; ++t) {
+                                        const bool first = jd == 0 && jh == 0 && cig == 0 && kw == Ph::first_k(rw);
+                                        acc[0][sl][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                            wr[jd][jh][kw][cig], bread(rw, c, slot, cig, t),
+                                            first ? bias4 : acc[0][sl][t], 0, 0, 0);
+                                    }
+                                }
+                            }
+                        }
+                    }
+                } else {
+                    // tap t of row q in slot q*MODE + t; the rows' accumulators
+                    // interleave (innermost), so consecutive MFMAs are independent
+#pragma unroll
+                    for (int tp = 0; tp < MODE; ++tp)
+#pragma unroll
+                        for (int cig = 0; cig < NCIG; ++cig)
+#pragma unroll
+                            for (int kw = 0; kw < KW; ++kw) {
+                                const int rw = Ph::r_of(kw);
+                                const int sl = Ph::slot(rw);
+                                const int c = Ph::c_of(kw);
+                                const bool first = tp == 0 && cig == 0 && kw == Ph::first_k(rw);
+#pragma unroll
+                                for (int q = 0; q < RS; ++q)
+#pragma unroll
+                                    for (int t = 0; t < NWBM; ++t)
+                                        acc[q][sl][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                                            wr[tp / THM][tp % THM][kw][cig], bread(rw, c, q * MODE + tp, cig, t),
+                                            first ? bias4 : acc[q][sl][t], 0, 0, 0);
+                            }
+                }
+            }
+
+            // The next step's inputs go to the other LDS buffer (free since the
+            // last barrier) before this step's stores: the vector-memory counter
+            // retires in issue order, so the wait for them must not follow the
+            // stores.  Unconditional, so that no path leaves them pending into
+            // the next step's fetch.
+#pragma unroll
+            for (int u = 0; u < PER; ++u) asm volatile("" : "+v"(pre[u]));
+            store_rows(lds[buf ^ 1], pre, sl1, lds[buf]);
+
+#pragma unroll
+            for (int q = 0; q < RS; ++q) epi_row(R, acc[q], avc[q], q * dhy4, std::integral_constant<bool, SWAP>{});
+
+            __syncthreads();
+            R = Rn;
+            c1 = c2;
+            sl1 = sl2;
+            if (r + 3 * RS <= r_end - RS) {
+                if constexpr (RS == 1) {
+                    cursor_next(P, cls, c2);
+                } else { // a multi-row class's H runs hold whole steps
+                    c2.iqh += RS;
+                    if (c2.iqh == P.cls_nqh[cls]) {
+                        c2.iqh = 0;
+                        if (++c2.iqd == P.cls_nqd[cls]) {
+                            c2.iqd = 0;
+                            ++c2.n;
+                        }
+                    }
+                }
+                sl2 = slide_of(r + 3, c2);
+            }
+        };
+        for (int r = r_begin; r < r_end; r += 2 * RS) {
+            step(r, av, avn, pre0, pre1, std::integral_constant<int, 0>{});
+            if (r + RS < r_end) step(r + RS, avn, av, pre1, pre0, std::integral_constant<int, 1>{});
         }
     };
-    for (int r = r_begin; r < r_end; r += 2) {
-        row_step(r, av, avn, pre0, pre1, std::integral_constant<int, 0>{});
-        if (r + 1 < r_end) row_step(r + 1, avn, av, pre1, pre0, std::integral_constant<int, 1>{});
+    if constexpr (MULTI) {
+        if (flat) {
+            if (ntaps == 1) run(std::integral_constant<int, 1>{});
+            else run(std::integral_constant<int, 2>{});
+            return;
+        }
     }
+    run(std::integral_constant<int, 0>{});
 }
 
 // ---------------------------------------------------------------- wide variant
@@ -1024,6 +1152,7 @@ int64_t fill_params(const convt_plan &Pl, const Layout &L, int SW, Igemm3dParams
         P.cls_oh0[c] = oh0;
         P.cls_nqh[c] = nqh;
         P.cls_rows[c] = (int)(Pl.N * nqd * nqh);
+        P.cls_rstep[c] = 1;
         total_rows += P.cls_rows[c];
     }
     P.n_class = kept;
@@ -1053,7 +1182,22 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
     const int64_t total_rows = fill_params(Pl, L, SW, P);
     // rows per block: enough blocks to fill the CUs several times over
     const int64_t target_blocks = (int64_t)num_cus() * CONVT_IG_BLOCKS_PER_CU;
-    const int rpb = (int)std::max<int64_t>(1, std::min<int64_t>(CONVT_IG_MAX_ROWS, total_rows / target_blocks));
+    int rpb = (int)std::max<int64_t>(1, std::min<int64_t>(CONVT_IG_MAX_ROWS, total_rows / target_blocks));
+    const bool last = Pl.layout == CONVT_LAYOUT_CHANNELS_LAST;
+    // Multi-row steps (the kernel compiles them for channels first, 4 tap
+    // slots and one W-block): a class of 1 or 2 taps whose H runs split into
+    // whole steps; blocks then start on a step (rows per block a multiple of 4).
+    if (CONVT_IG_MULTIROW && !last && TDM * THM == 4 && NWBM == 1) {
+        bool any = false;
+        for (int c = 0; c < P.n_class; ++c) {
+            const int nt = P.cls_td[c] * P.cls_th[c];
+            if ((nt == 1 || nt == 2) && P.cls_nqh[c] % (4 / nt) == 0) {
+                P.cls_rstep[c] = 4 / nt;
+                any = true;
+            }
+        }
+        if (any) rpb = (rpb + 3) / 4 * 4;
+    }
     const int blocks = assign_blocks(P, rpb, CONVT_IG_XCD_ORDER != 0);
     if (blocks == 0) return 0;
     constexpr int NT = COG * 4;
@@ -1062,7 +1206,6 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
     if (need_f > PER * NT) return (int)hipErrorInvalidValue;
     // every lane of every W-block inside the row
     const bool fullw = Pl.ax[2].L_out == SW * 16 * NWBM;
-    const bool last = Pl.layout == CONVT_LAYOUT_CHANNELS_LAST;
     auto launch = [&](auto epi, auto full, auto swap) {
         if (last) { // channels last: the staged epilogue guards the row end itself
             if constexpr (!decltype(full)::value)
