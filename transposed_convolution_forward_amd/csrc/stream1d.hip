@@ -190,6 +190,97 @@ __device__ __forceinline__ void tile_store_lds(float *lds, const f4 (&r)[(CIG * 
     }
 }
 
+// Winograd F(4,3) (Lavin and Gray, "Fast Algorithms for Convolutional Neural
+// Networks", CVPR 2016) for a layer whose one phase has three taps at input
+// shifts 0, 1, 2 (K = 3 and dilation = stride, e.g. stride 2, dilation 2):
+// the four outputs y[q+i] = sum_c w_c x[q+i-c], i = 0..3, are
+// A^T [(G g) . (B^T d)] with d = x[q-2 .. q+3] and g_k = w_{2-k}.  The
+// contraction over input channels then runs on the six transformed
+// components (six MFMAs per 4 channels and 16 tiles of 4 positions, against
+// twelve for the taps directly), the input transform B^T d once per tile when
+// it is staged in LDS, the weight transform G g once per kernel, and the
+// output transform A^T m in registers before the epilogue.  fp32 throughout;
+// the transforms' constants (4, 5, 2, 8, 1/6, 1/12, 1/24) raise the rounding
+// error a few times over the direct sum (about 3e-6 absolute on unit-variance
+// inputs with 96 products per output).
+#ifndef CONVT_S1D_WINOGRAD
+#define CONVT_S1D_WINOGRAD 1
+#endif
+constexpr int kWinoTau = kTileQ / 4; // tiles of 4 positions per work item
+
+// Thread tid stages (channel ci, tile tau) pairs p = tid + u*NT of the item,
+// ci = p / 16, tau = p % 16: inputs q0 + 4tau - 4 .. q0 + 4tau + 3 as two
+// float4 (positions clamped into the row, as in tile_fetch).
+template <int CIG, int NT> constexpr int kWinoPairs = (CIG * kWinoTau + NT - 1) / NT;
+template <int CIG, int NT> using WinoRegs = f4[2 * kWinoPairs<CIG, NT>];
+template <int CIG, int NT> using WinoOffs = unsigned[kWinoPairs<CIG, NT>];
+
+template <int CIG, int NT>
+__device__ __forceinline__ void wino_fetch(WinoRegs<CIG, NT> &r, const float *xrow, int L_in,
+                                           int q0, int tid) {
+#pragma unroll
+    for (int u = 0; u < kWinoPairs<CIG, NT>; ++u) {
+        const int pr = min(tid + u * NT, CIG * kWinoTau - 1);
+        const int ci = pr / kWinoTau, tau = pr % kWinoTau;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int pos = q0 + 4 * tau - 4 + 4 * h;
+            r[2 * u + h] = load4u(xrow + (int64_t)ci * L_in + min(max(pos, 0), L_in - 4));
+        }
+    }
+}
+
+// The same for a tile wholly inside the row: fixed byte offsets xo[u] of the
+// pair's first float4 relative to position q0 - 4.
+template <int CIG, int NT>
+__device__ __forceinline__ void wino_fetch_inner(WinoRegs<CIG, NT> &r, rsrc_t rx,
+                                                 const WinoOffs<CIG, NT> &xo, int q0) {
+#pragma unroll
+    for (int u = 0; u < kWinoPairs<CIG, NT>; ++u) {
+        r[2 * u] = buf_load4(rx, xo[u], 4u * (unsigned)(q0 - 4));
+        r[2 * u + 1] = buf_load4(rx, xo[u] + 16u, 4u * (unsigned)(q0 - 4));
+    }
+}
+
+// Input transform of the staged pairs into LDS: component xi of (ci, tau) at
+// xi*CIG*16 + ci*16 + tau, so the B operand of (component, 4 channels) is 64
+// consecutive floats (lane 16*g4 + j reads channel 4cig + g4, tile j).
+template <int CIG, int NT>
+__device__ __forceinline__ void wino_store_lds(float *lds, const WinoRegs<CIG, NT> &r, int L_in,
+                                               int q0, int tid) {
+    const bool inner = q0 - 4 >= 0 && q0 + kTileQ <= L_in;
+#pragma unroll
+    for (int u = 0; u < kWinoPairs<CIG, NT>; ++u) {
+        const int pr = tid + u * NT;
+        if (pr >= CIG * kWinoTau) continue;
+        const int tau = pr % kWinoTau;
+        f4 h[2] = {r[2 * u], r[2 * u + 1]};
+        if (!inner) { // shift back from the clamped position, zero outside the row
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int pos = q0 + 4 * tau - 4 + 4 * b;
+                const int sh = pos - min(max(pos, 0), L_in - 4);
+                const f4 v = h[b];
+                h[b].x = (pos + 0 >= 0 && pos + 0 < L_in) ? pick4(v, sh + 0) : 0.0f;
+                h[b].y = (pos + 1 >= 0 && pos + 1 < L_in) ? pick4(v, sh + 1) : 0.0f;
+                h[b].z = (pos + 2 >= 0 && pos + 2 < L_in) ? pick4(v, sh + 2) : 0.0f;
+                h[b].w = (pos + 3 >= 0 && pos + 3 < L_in) ? pick4(v, sh + 3) : 0.0f;
+            }
+        }
+        const float d0 = h[0].z, d1 = h[0].w, d2 = h[1].x, d3 = h[1].y, d4 = h[1].z, d5 = h[1].w;
+        // B^T d
+        const float t1 = fmaf(-4.0f, d2, d4), t2 = fmaf(-4.0f, d1, d3);
+        const float t3 = d4 - d2, t4 = 2.0f * (d3 - d1);
+        float *o = lds + pr;
+        o[0 * CIG * kWinoTau] = fmaf(4.0f, d0, fmaf(-5.0f, d2, d4));
+        o[1 * CIG * kWinoTau] = t1 + t2;
+        o[2 * CIG * kWinoTau] = t1 - t2;
+        o[3 * CIG * kWinoTau] = t3 + t4;
+        o[4 * CIG * kWinoTau] = t3 - t4;
+        o[5 * CIG * kWinoTau] = fmaf(4.0f, d1, fmaf(-5.0f, d3, d5));
+    }
+}
+
 // Output lines.  Rows may have any length, so the outputs o_t .. o_t + 64S - 1
 // of a work item start anywhere in a 128-byte cache line, at a different place
 // in every row; stored as they stand, the line at each end of the run is split
@@ -248,10 +339,16 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
     constexpr int NT = COG * 4; // threads per workgroup
     constexpr int NP = Ph::count() > 0 ? Ph::count() : 1;
     constexpr int PER = (CIG * kRowF4 + NT - 1) / NT;
+    // Winograd F(4,3) for one phase of three taps at shifts 0, 1, 2
+    constexpr bool WINO = CONVT_S1D_WINOGRAD && K == 3 && S == D;
+    constexpr int NPAIR = kWinoPairs<CIG, NT>;
+    constexpr int NPRE = WINO ? 2 * NPAIR : PER; // prefetch registers (float4)
+    constexpr int NXO = WINO ? NPAIR : PER;
+    constexpr int NWR = WINO ? 6 : K;             // weight registers per channel group
     static_assert(CIG % 4 == 0 && COG % 16 == 0, "tile shape");
     static_assert(Ph::cmax() <= 4, "input shift beyond the 4-position halo");
 
-    __shared__ __attribute__((aligned(16))) float lds[2][CIG / 4 * kGrpF];
+    __shared__ __attribute__((aligned(16))) float lds[2][WINO ? 6 * CIG * kWinoTau : CIG / 4 * kGrpF];
     __shared__ __attribute__((aligned(16))) float ostage[COT][4][stage_pitch<S>()];
     __shared__ __attribute__((aligned(16))) float ocarry[COT][4][4][kLineF]; // [wave][g4][e][slot]
 
@@ -270,30 +367,49 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
     int ng = (int)(it0 / P.n_st);
     auto xrow_of = [&](int ng_) { return x + (int64_t)ng_ * CIG * P.L_in; }; // (n*G+g)*CIG = n*C_in + g*CIG
 
-    unsigned xo[PER]; // byte offsets of this thread's float4 in a tile wholly inside the row
+    unsigned xo[NXO]; // byte offsets of this thread's float4 (pair) in a tile wholly inside the row
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int f = min(tid + u * NT, CIG * kRowF4 - 1);
-        xo[u] = 4u * (unsigned)((f / kRowF4) * P.L_in + 4 * (f % kRowF4));
+    for (int u = 0; u < NXO; ++u) {
+        if constexpr (WINO) {
+            const int pr = min(tid + u * NT, CIG * kWinoTau - 1);
+            xo[u] = 4u * (unsigned)((pr / kWinoTau) * P.L_in + 4 * (pr % kWinoTau));
+        } else {
+            const int f = min(tid + u * NT, CIG * kRowF4 - 1);
+            xo[u] = 4u * (unsigned)((f / kRowF4) * P.L_in + 4 * (f % kRowF4));
+        }
     }
     int lo[PER]; // LDS offsets of this thread's float4 of the tile
 #pragma unroll
     for (int u = 0; u < PER; ++u) lo[u] = tile_lds_off(min(tid + u * NT, CIG * kRowF4 - 1));
     const int x_bytes = 4 * CIG * P.L_in; // one row set's input rows (below 2 GiB)
     // Tiles inside the row take buffer loads at fixed offsets; the others clamp.
-    auto fetch = [&](f4 (&r)[PER], int ng_, int q0_) {
-        if (q0_ - 4 >= 0 && q0_ + kTileQ <= P.L_in)
-            tile_fetch_inner<CIG, NT>(r, make_rsrc(const_cast<float *>(xrow_of(ng_)), x_bytes), xo, q0_);
-        else
-            tile_fetch<CIG, NT>(r, xrow_of(ng_), P.L_in, q0_, tid);
+    auto fetch = [&](f4 (&r)[NPRE], int ng_, int q0_) {
+        const bool inner = q0_ - 4 >= 0 && q0_ + kTileQ <= P.L_in;
+        if constexpr (WINO) {
+            if (inner)
+                wino_fetch_inner<CIG, NT>(r, make_rsrc(const_cast<float *>(xrow_of(ng_)), x_bytes), xo, q0_);
+            else
+                wino_fetch<CIG, NT>(r, xrow_of(ng_), P.L_in, q0_, tid);
+        } else {
+            if (inner)
+                tile_fetch_inner<CIG, NT>(r, make_rsrc(const_cast<float *>(xrow_of(ng_)), x_bytes), xo, q0_);
+            else
+                tile_fetch<CIG, NT>(r, xrow_of(ng_), P.L_in, q0_, tid);
+        }
+    };
+    auto stage = [&](float *l, const f4 (&r)[NPRE], int q0_) {
+        if constexpr (WINO) wino_store_lds<CIG, NT>(l, r, P.L_in, q0_, tid);
+        else tile_store_lds<CIG, NT>(l, r, lo, P.L_in, q0_, tid);
     };
 
-    f4 pre[PER];
+    f4 pre[NPRE];
     fetch(pre, ng, (P.st_lo + st) * kTileQ);
-    tile_store_lds<CIG, NT>(lds[0], pre, lo, P.L_in, (P.st_lo + st) * kTileQ, tid);
+    stage(lds[0], pre, (P.st_lo + st) * kTileQ);
     __syncthreads();
 
-    float wr[K][NCIG]; // A operands: W[g*CIG + 4*cig + g4][16*ct + j][k]
+    // A operands: W[g*CIG + 4*cig + g4][16*ct + j][k], or with Winograd the
+    // six components of G g for g_k = W[..][2-k]
+    float wr[NWR][NCIG];
     float br[4];       // bias of rows co = 16ct + 4g4 + e
     int buf = 0;
     bool chain = false; // the previous item left its last outputs of each row in ocarry
@@ -323,11 +439,28 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
     for (int ii = 0; ii < n_items;) {
         const int g = ng % P.G;
         const int run = P.G == 1 ? n_items - ii : min(n_items - ii, P.n_st - st);
+        if constexpr (WINO) {
 #pragma unroll
-        for (int k = 0; k < K; ++k)
+            for (int cig = 0; cig < NCIG; ++cig) {
+                const float *wp = w + ((int64_t)(g * CIG + 4 * cig + g4) * COG + 16 * ct + j) * K;
+                const float g0 = wp[2], g1 = wp[1], g2 = wp[0]; // g_k = w_{2-k}
+                // G g, G = [1/4 0 0; -1/6 -1/6 -1/6; -1/6 1/6 -1/6; 1/24 1/12 1/6; 1/24 -1/12 1/6; 0 0 1]
+                const float s02 = g0 + g2;
+                wr[0][cig] = 0.25f * g0;
+                wr[1][cig] = -(s02 + g1) * (1.0f / 6.0f);
+                wr[2][cig] = -(s02 - g1) * (1.0f / 6.0f);
+                const float e02 = fmaf(g0, 1.0f / 24.0f, g2 * (1.0f / 6.0f));
+                wr[3][cig] = fmaf(g1, 1.0f / 12.0f, e02);
+                wr[4][cig] = fmaf(g1, -1.0f / 12.0f, e02);
+                wr[5][cig] = g2;
+            }
+        } else {
 #pragma unroll
-            for (int cig = 0; cig < NCIG; ++cig)
-                wr[k][cig] = w[((int64_t)(g * CIG + 4 * cig + g4) * COG + 16 * ct + j) * K + k];
+            for (int k = 0; k < K; ++k)
+#pragma unroll
+                for (int cig = 0; cig < NCIG; ++cig)
+                    wr[k][cig] = w[((int64_t)(g * CIG + 4 * cig + g4) * COG + 16 * ct + j) * K + k];
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) br[e] = bias ? bias[g * COG + 16 * ct + 4 * g4 + e] : 0.0f;
         // Wait for these loads here, before the loop: an empty asm that reads
@@ -335,7 +468,7 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
         // loop body never waits on them (which, vmcnt being in order, would
         // also wait on the prefetch).
 #pragma unroll
-        for (int k = 0; k < K; ++k)
+        for (int k = 0; k < NWR; ++k)
 #pragma unroll
             for (int cig = 0; cig < NCIG; ++cig) asm volatile("" : "+v"(wr[k][cig]));
 #pragma unroll
@@ -356,6 +489,29 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
         if constexpr (Ph::count() == 0) {
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[0][t] = bias4;
+        } else if constexpr (WINO) {
+            // m_xi[co][tile j] = sum_ci U_xi[co][ci] V_xi[ci][j]; the bias
+            // enters through m_1, whose A^T column is all ones
+            const float *vb = lds[buf] + 16 * g4 + j;
+            const f4 zero4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            f4 m[6];
+#pragma unroll
+            for (int cig = 0; cig < NCIG; ++cig)
+#pragma unroll
+                for (int xi = 0; xi < 6; ++xi)
+                    m[xi] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                        wr[xi][cig], vb[(xi * CIG + 4 * cig) * kWinoTau],
+                        cig == 0 ? (xi == 1 ? bias4 : zero4) : m[xi], 0, 0, 0);
+            // A^T m: positions q0 + 4j + t
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float s12 = m[1][e] + m[2][e], d12 = m[1][e] - m[2][e];
+                const float s34 = m[3][e] + m[4][e], d34 = m[3][e] - m[4][e];
+                acc[0][0][e] = m[0][e] + s12 + s34;
+                acc[0][1][e] = fmaf(2.0f, d34, d12);
+                acc[0][2][e] = fmaf(4.0f, s34, s12);
+                acc[0][3][e] = fmaf(8.0f, d34, d12) + m[5][e];
+            }
         } else {
             // lane j's float4 at q0+4j (row 4cig+g4) and the one before it
             // (the halo float4 for lane 0)
@@ -392,8 +548,8 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
         // pending along the skipping path and wait for it, and with it for every
         // store, before the next fetch.
 #pragma unroll
-        for (int u = 0; u < PER; ++u) asm volatile("" : "+v"(pre[u])); // every prefetch landed here
-        tile_store_lds<CIG, NT>(lds[buf ^ 1], pre, lo, P.L_in, (P.st_lo + st1) * kTileQ, tid);
+        for (int u = 0; u < NPRE; ++u) asm volatile("" : "+v"(pre[u])); // every prefetch landed here
+        stage(lds[buf ^ 1], pre, (P.st_lo + st1) * kTileQ);
 
         // Epilogue (see stage_pitch).  Rows co = g*COG + 16ct + 4g4 + e; the
         // item's outputs of a row are o_t .. o_t + 64S - 1, o_t = q0*S - p.
