@@ -411,7 +411,6 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
     // six components of G g for g_k = W[..][2-k]
     float wr[NWR][NCIG];
     float br[4];       // bias of rows co = 16ct + 4g4 + e
-    int buf = 0;
     bool chain = false; // the previous item left its last outputs of each row in ocarry
     // Per row set (n, g): the sample's y resource, and per row group e the
     // lane's byte offset of its segment relative to the item offset
@@ -434,53 +433,78 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
     const int own = kLineF + (4 * S - 1) * j;
     const f4 *segp = reinterpret_cast<const f4 *>(srow + kLineF + 4 * j);
 
-    // Runs of consecutive items of one group share the weights: load them once
-    // per run, outside the loop that carries the prefetch.
-    for (int ii = 0; ii < n_items;) {
-        const int g = ng % P.G;
-        const int run = P.G == 1 ? n_items - ii : min(n_items - ii, P.n_st - st);
-        if constexpr (WINO) {
+    // The weights of group g (A operands) and its bias.
+    auto load_group = [&](int g) {
+            if constexpr (WINO) {
 #pragma unroll
-            for (int cig = 0; cig < NCIG; ++cig) {
-                const float *wp = w + ((int64_t)(g * CIG + 4 * cig + g4) * COG + 16 * ct + j) * K;
-                const float g0 = wp[2], g1 = wp[1], g2 = wp[0]; // g_k = w_{2-k}
-                // G g, G = [1/4 0 0; -1/6 -1/6 -1/6; -1/6 1/6 -1/6; 1/24 1/12 1/6; 1/24 -1/12 1/6; 0 0 1]
-                const float s02 = g0 + g2;
-                wr[0][cig] = 0.25f * g0;
-                wr[1][cig] = -(s02 + g1) * (1.0f / 6.0f);
-                wr[2][cig] = -(s02 - g1) * (1.0f / 6.0f);
-                const float e02 = fmaf(g0, 1.0f / 24.0f, g2 * (1.0f / 6.0f));
-                wr[3][cig] = fmaf(g1, 1.0f / 12.0f, e02);
-                wr[4][cig] = fmaf(g1, -1.0f / 12.0f, e02);
-                wr[5][cig] = g2;
+                for (int cig = 0; cig < NCIG; ++cig) {
+                    const float *wp = w + ((int64_t)(g * CIG + 4 * cig + g4) * COG + 16 * ct + j) * K;
+                    const float g0 = wp[2], g1 = wp[1], g2 = wp[0]; // g_k = w_{2-k}
+                    // G g, G = [1/4 0 0; -1/6 -1/6 -1/6; -1/6 1/6 -1/6; 1/24 1/12 1/6; 1/24 -1/12 1/6; 0 0 1]
+                    const float s02 = g0 + g2;
+                    wr[0][cig] = 0.25f * g0;
+                    wr[1][cig] = -(s02 + g1) * (1.0f / 6.0f);
+                    wr[2][cig] = -(s02 - g1) * (1.0f / 6.0f);
+                    const float e02 = fmaf(g0, 1.0f / 24.0f, g2 * (1.0f / 6.0f));
+                    wr[3][cig] = fmaf(g1, 1.0f / 12.0f, e02);
+                    wr[4][cig] = fmaf(g1, -1.0f / 12.0f, e02);
+                    wr[5][cig] = g2;
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < K; ++k)
+#pragma unroll
+                    for (int cig = 0; cig < NCIG; ++cig)
+                        wr[k][cig] = w[((int64_t)(g * CIG + 4 * cig + g4) * COG + 16 * ct + j) * K + k];
             }
-        } else {
 #pragma unroll
-            for (int k = 0; k < K; ++k)
+            for (int e = 0; e < 4; ++e) br[e] = bias ? bias[g * COG + 16 * ct + 4 * g4 + e] : 0.0f;
+            // Wait for these loads here: an empty asm that reads and redefines
+            // the registers puts the wait at the group change, so the MFMA
+            // block never waits on them (which, vmcnt being in order, would
+            // also wait on the prefetched tiles).
 #pragma unroll
-                for (int cig = 0; cig < NCIG; ++cig)
-                    wr[k][cig] = w[((int64_t)(g * CIG + 4 * cig + g4) * COG + 16 * ct + j) * K + k];
+            for (int k = 0; k < NWR; ++k)
+#pragma unroll
+                for (int cig = 0; cig < NCIG; ++cig) asm volatile("" : "+v"(wr[k][cig]));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(br[e]));
+    };
+    auto advance = [&](int &st_, int &ng_) {
+        if (++st_ == P.n_st) {
+            st_ = 0;
+            ++ng_;
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) br[e] = bias ? bias[g * COG + 16 * ct + 4 * g4 + e] : 0.0f;
-        // Wait for these loads here, before the loop: an empty asm that reads
-        // and redefines the registers puts the wait in the preheader, so the
-        // loop body never waits on them (which, vmcnt being in order, would
-        // also wait on the prefetch).
-#pragma unroll
-        for (int k = 0; k < NWR; ++k)
-#pragma unroll
-            for (int cig = 0; cig < NCIG; ++cig) asm volatile("" : "+v"(wr[k][cig]));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(br[e]));
+    };
 
-    for (int rr = 0; rr < run; ++rr, ++ii) {
+    // Tiles are fetched two items ahead, into two register sets that swap
+    // roles every item (the loop below runs the item twice per trip with the
+    // sets and the LDS buffers exchanged, all compile-time indices): the wait
+    // before a tile is staged then covers only loads issued an item earlier.
+    // Items ii+1 and ii+2 are (st1, ng1) and (st2, ng2), clamped to the
+    // workgroup's last item (fetched again, never used).
+    int st1 = st, ng1 = ng;
+    if (n_items > 1) advance(st1, ng1);
+    int st2 = st1, ng2 = ng1;
+    if (n_items > 2) advance(st2, ng2);
+    int wg = ng % P.G;
+    load_group(wg);
+    f4 pre2[NPRE];
+    fetch(pre, ng1, (P.st_lo + st1) * kTileQ);
+
+    int ii = 0;
+    auto item = [&](f4 (&preN)[NPRE], f4 (&preF)[NPRE], auto bufc) {
+        constexpr int buf = decltype(bufc)::value;
+        if (P.G > 1 && ng % P.G != wg) { // a new group: its weights
+            wg = ng % P.G;
+            load_group(wg);
+        }
+        const int g = wg;
         const int n = ng / P.G;
         const int q0 = (P.st_lo + st) * kTileQ;
-        int st1 = st + 1, ng1 = ng;
-        if (st1 == P.n_st) { st1 = 0; ++ng1; }
         const bool has_next = ii + 1 < n_items;
-        if (has_next) fetch(pre, ng1, (P.st_lo + st1) * kTileQ);
+        // the tile of item ii+2 (clamped), in flight across this item and the next
+        fetch(preF, ng2, (P.st_lo + st2) * kTileQ);
 
         // The bias enters as the accumulators' start value: the first MFMA of
         // each phase takes it as its accumulator input.
@@ -548,8 +572,8 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
         // pending along the skipping path and wait for it, and with it for every
         // store, before the next fetch.
 #pragma unroll
-        for (int u = 0; u < NPRE; ++u) asm volatile("" : "+v"(pre[u])); // every prefetch landed here
-        stage(lds[buf ^ 1], pre, (P.st_lo + st1) * kTileQ);
+        for (int u = 0; u < NPRE; ++u) asm volatile("" : "+v"(preN[u])); // item ii+1's tile landed here
+        stage(lds[buf ^ 1], preN, (P.st_lo + st1) * kTileQ);
 
         // Epilogue (see stage_pitch).  Rows co = g*COG + 16ct + 4g4 + e; the
         // item's outputs of a row are o_t .. o_t + 64S - 1, o_t = q0*S - p.
@@ -689,10 +713,18 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
         }
 
         __syncthreads();
-        buf ^= 1;
+        ++ii;
         st = st1;
         ng = ng1;
-    }
+        st1 = st2;
+        ng1 = ng2;
+        if (ii + 2 < n_items) advance(st2, ng2);
+    };
+    for (;;) {
+        item(pre, pre2, std::integral_constant<int, 0>{});
+        if (ii >= n_items) break;
+        item(pre2, pre, std::integral_constant<int, 1>{});
+        if (ii >= n_items) break;
     }
 }
 
