@@ -49,7 +49,7 @@ __device__ __forceinline__ f4 load4u(const float *p) {
 // Tuning knobs: workgroups aimed for per CU when sizing the rows per block,
 // and the most rows one block walks.
 #ifndef CONVT_IG_BLOCKS_PER_CU
-#define CONVT_IG_BLOCKS_PER_CU 8
+#define CONVT_IG_BLOCKS_PER_CU 4
 #endif
 #ifndef CONVT_IG_MAX_ROWS
 #define CONVT_IG_MAX_ROWS 256
