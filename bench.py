@@ -123,7 +123,7 @@ def valid_macs(wl, N=None):
 KERNEL_SOURCES = {"k_stream1d": "stream1d.hip", "k_stream1d_nlc": "stream1d.hip", "k_igemm3d": "igemm3d.hip",
                   "k_igemm3d_wide": "igemm3d.hip", "k_generic_nxc": "generic.hip",
                   "k_generic": "generic.hip", "k_generic_phase": "generic.hip", "k_generic_rows": "generic.hip",
-                  "k_generic_pairs": "generic.hip", "k_backward_data": "backward.hip",
+                  "k_generic_pairs": "generic.hip", "k_generic_wpair": "wpair.hip", "k_backward_data": "backward.hip",
                   "k_backward_data_mfma": "backward.hip", "k_backward_data_mfma_row": "backward.hip",
                   "k_backward_weight": "wgrad.hip",
                   "k_backward_weight_lds": "wgrad.hip", "k_backward_weight_row": "wgrad.hip"}

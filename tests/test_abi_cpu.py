@@ -143,7 +143,11 @@ def test_workload_plans_and_paths():
     # few stride-phase classes: the phase-class gather, on the matrix cores with
     # input rows shared along H where the shape has H extent; the tiny 1D layer
     # (two classes, no H) takes the FMA variant
-    assert "kernel=k_generic_pairs" in T.convt_plan_describe(T.plan_for(S.GROUPED_3D))
+    # 8-channel groups with stride 2 along W: the two W phases share a tile
+    assert "kernel=k_generic_wpair" in T.convt_plan_describe(T.plan_for(S.GROUPED_3D))
+    # the same groups with stride 1 along W: row pairs along H
+    w1 = T.Plan(3, 1, 32, 32, 4, (4, 6, 16), (3, 5, 3), (2, 1, 1), (1, 2, 1), (1, 0, 0), (1, 1, 1))
+    assert "kernel=k_generic_pairs" in T.convt_plan_describe(w1)
     assert "kernel=k_generic_phase" in T.convt_plan_describe(T.plan_for(S.TINY_1D))
     # more classes than the table holds (4*3*3 = 36): the per-position gather
     big = T.Plan(3, 1, 2, 2, 1, (4, 4, 4), (4, 3, 3), (4, 3, 3), (0, 0, 0), (0, 0, 0), (1, 1, 1))
@@ -243,7 +247,7 @@ def test_convt_log_names_kernel_and_fallback():
     lines = [l for l in r.stderr.splitlines() if l.startswith("convt: plan:")]
     assert len(lines) == 3, r.stderr
     assert "kernel=k_stream1d" in lines[0] and "fallback" not in lines[0]
-    assert "kernel=k_generic_pairs" in lines[1] and "generic fallback" in lines[1]
+    assert "kernel=k_generic_wpair" in lines[1] and "generic fallback" in lines[1]
     assert "generic fallback" in lines[2]
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
                        env={k: v for k, v in os.environ.items() if k != "CONVT_LOG"})

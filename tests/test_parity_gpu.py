@@ -95,6 +95,18 @@ REDUCED = [
                (1, 0, 1), (1, 2, 1), True, False, wid=3407),
     S.Workload("rows_cig6", 3, 2, 12, 16, 2, (3, 10, 7), (2, 3, 3), (2, 1, 2), (0, 1, 1),
                (1, 0, 1), (1, 1, 1), True, True, wid=3408),
+    # 8-channel groups with stride 2 along W, the two W phases in one tile
+    # (k_generic_wpair): groups of P1's layer at reduced size with a ragged H
+    # run (7 rows), W kernel 4 (one phase's taps all at other shifts), an odd
+    # output width, two groups with bias-only D classes, fused
+    S.Workload("wpair_g1_h7", 3, 1, 8, 8, 1, (3, 7, 8), (3, 5, 7), (2, 1, 2), (1, 2, 3), (1, 0, 1),
+               (1, 1, 1), True, False, wid=3411),
+    S.Workload("wpair_kw4_fused", 3, 2, 8, 8, 1, (2, 7, 16), (2, 3, 4), (1, 2, 2), (0, 1, 1), (0, 1, 0),
+               (1, 1, 1), True, True, wid=3412),
+    S.Workload("wpair_odd_w", 3, 2, 16, 16, 2, (3, 5, 12), (3, 5, 5), (2, 1, 2), (1, 2, 2), (1, 0, 0),
+               (1, 1, 1), False, False, wid=3413),
+    S.Workload("wpair_sd4", 3, 1, 16, 16, 2, (2, 6, 8), (3, 5, 7), (4, 1, 2), (1, 2, 3), (0, 0, 1),
+               (1, 1, 1), True, True, wid=3414),
     # 8-channel groups on 16x16x4 tiles of two output rows: two channel
     # chunks, ragged position and row blocks, fused
     S.Workload("pairs_co16_ragged", 3, 2, 8, 32, 2, (3, 13, 21), (3, 5, 3), (2, 1, 2), (1, 2, 1),

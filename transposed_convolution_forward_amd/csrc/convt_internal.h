@@ -57,6 +57,12 @@ const char *generic_kernel_name(const convt_plan &P);
 int launch_generic(const convt_plan &P, const float *x, const float *w, const float *bias,
                    const float *add, int act, float *y, void *stream);
 
+// Groups of 8 input and 8 output channels with stride 2 and dilation 1 along W
+// (the generic path's first choice when it applies).
+bool wpair_supports(const convt_plan &P);
+int launch_wpair(const convt_plan &P, const float *x, const float *w, const float *bias, const float *add,
+                 int act, float *y, void *stream);
+
 bool stream1d_supports(const convt_plan &P);
 int launch_stream1d(const convt_plan &P, const float *x, const float *w, const float *bias,
                     const float *add, int act, float *y, void *stream);

@@ -974,8 +974,15 @@ int launch_cpt(const convt_plan &Pl, const GenericParams &base, const float *x, 
 
 } // namespace
 
+// The W-pair kernel (wpair.hip) goes first where it applies (CONVT_WPAIR=0
+// builds without it).
+#ifndef CONVT_WPAIR
+#define CONVT_WPAIR 1
+#endif
+
 const char *generic_kernel_name(const convt_plan &Pl) {
     if (Pl.layout == CONVT_LAYOUT_CHANNELS_LAST) return "k_generic_nxc";
+    if (CONVT_WPAIR && wpair_supports(Pl)) return "k_generic_wpair";
     PhaseParams P;
     if (pairs_plan(Pl) > 0) return "k_generic_pairs";
     if (rows_plan(Pl) > 0) return "k_generic_rows";
@@ -1012,6 +1019,7 @@ int launch_generic(const convt_plan &Pl, const float *x, const float *w, const f
         });
         return (int)hipGetLastError();
     }
+    if (CONVT_WPAIR && wpair_supports(Pl)) return launch_wpair(Pl, x, w, bias, add, act, y, stream);
     {
         PhaseParams Q;
         const int thp = pairs_plan(Pl);
