@@ -233,6 +233,11 @@ __global__ __launch_bounds__(kBlockT) __attribute__((amdgpu_waves_per_eu(3))) vo
     {
         const int g = grp;
         const int delta = j >> 3, co = j & 7;
+        int kdv[kTDM], khv[kTHM]; // the class's taps (table entries past td, th are 0)
+#pragma unroll
+        for (int dt = 0; dt < kTDM; ++dt) kdv[dt] = __builtin_amdgcn_readfirstlane(P.cls_kd[cls][dt]);
+#pragma unroll
+        for (int t = 0; t < kTHM; ++t) khv[t] = __builtin_amdgcn_readfirstlane(P.cls_kh[cls][t]);
 #pragma unroll
         for (int dt = 0; dt < kTDM; ++dt)
 #pragma unroll
@@ -245,11 +250,11 @@ __global__ __launch_bounds__(kBlockT) __attribute__((amdgpu_waves_per_eu(3))) vo
                         // entries becomes a per-lane index into scratch)
                         const int kw = (wt[0][sl] & (delta - 1)) | (wt[1][sl] & -delta);
                         const bool used = dt < td && t < th && kw >= 0;
-                        const int kd = used ? P.cls_kd[cls][dt] : 0, kh = used ? P.cls_kh[cls][t] : 0;
-                        const int idx = (((4 * cq + g4) * kCg + co) * P.KD + kd) * P.KH * P.KW + kh * P.KW +
-                                        (used ? kw : 0);
-                        const float v = wl[idx];
-                        wr[dt][t][sl][cq] = used ? v : 0.0f;
+                        // (every operand of the index is valid whatever `used`
+                        // says, so the read needs no branch)
+                        const int idx = (((4 * cq + g4) * kCg + co) * P.KD + kdv[dt]) * P.KH * P.KW + khv[t] * P.KW +
+                                        max(kw, 0);
+                        wr[dt][t][sl][cq] = used ? wl[idx] : 0.0f;
                     }
 #pragma unroll
         for (int e = 0; e < 4; ++e) bo[e] = bias ? bias[g * kCg + 4 * (g4 & 1) + e] : 0.0f;
@@ -275,20 +280,38 @@ __global__ __launch_bounds__(kBlockT) __attribute__((amdgpu_waves_per_eu(3))) vo
     const int ybytes = 4 * P.C_out * dhw_out;
     const int co_l = 4 * (g4 & 1), delta_l = g4 >> 1;
 
+    // Steps k, k + 1 and k + 2 (the last two clamped to the run's last step);
+    // later ones by advancing a cursor, not by dividing
     Step S = step_at(P, cls, grp, k_begin);
+    Step S1 = step_at(P, cls, grp, min(k_begin + 1, k_end - 1));
+    int k2 = min(k_begin + 2, k_end - 1);
+    Step S2 = step_at(P, cls, grp, k2);
+    const int nqh4 = 4 * ((P.cls_nqh[cls] + 3) / 4), nqd = P.cls_nqd[cls];
+    auto advance = [&](Step &T) __attribute__((always_inline)) {
+        if (k2 < k_end - 1) {
+            ++k2;
+            T.iqh0 += 4;
+            if (T.iqh0 == nqh4) {
+                T.iqh0 = 0;
+                if (++T.iqd == nqd) {
+                    T.iqd = 0;
+                    ++T.n;
+                }
+            }
+        }
+    };
     f4 pre0[kPer], pre1[kPer];
     __syncthreads(); // LDS zeroed before the first rows land
     fetch(pre0, S);
     stage(lds[0], pre0);
-    fetch(pre0, step_at(P, cls, grp, min(k_begin + 1, k_end - 1)));
+    fetch(pre0, S1);
     __syncthreads();
 
     // One step; the loop below runs it twice per trip with the prefetch
     // register sets and the LDS buffers exchanged (compile-time indices).
     auto step = [&](const int k, f4 (&pre)[kPer], f4 (&pre2)[kPer], auto bufc) __attribute__((always_inline)) {
         constexpr int buf = decltype(bufc)::value;
-        const Step Sn = step_at(P, cls, grp, min(k + 1, k_end - 1));
-        fetch(pre2, step_at(P, cls, grp, min(k + 2, k_end - 1)));
+        fetch(pre2, S2);
 
         const f4 zero4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
         f4 acc[kNT];
@@ -301,22 +324,36 @@ __global__ __launch_bounds__(kBlockT) __attribute__((amdgpu_waves_per_eu(3))) vo
         typedef const __attribute__((address_space(3))) float *lds_ptr;
         lds_ptr bb = (lds_ptr)(lds[buf] + wv * SLOT + g4 * kPW + P.col0 + j - P.smin - (kNS - 1));
         asm volatile("" : "+v"(bb));
+        // B operands of tap group gi = (D tap, H tap), read one group ahead:
+        // the reads of group gi + 1 are in flight during group gi's MFMAs
+        typedef float BGroup[kCg / 4][kNS][kNT];
+        auto load_b = [&](BGroup &b, const int gi) __attribute__((always_inline)) {
+            const int dt = gi / TH, t = gi % TH;
+#pragma unroll
+            for (int cq = 0; cq < kCg / 4; ++cq)
+#pragma unroll
+                for (int sl = 0; sl < kNS; ++sl)
+#pragma unroll
+                    for (int tl = 0; tl < kNT; ++tl)
+                        b[cq][sl][tl] = bb[(dt * kRows + TH - 1 - t) * SLOT + 4 * cq * kPW + 16 * tl + kNS - 1 - sl];
+        };
         auto contract = [&](auto tdc) __attribute__((always_inline)) {
-            constexpr int TD = decltype(tdc)::value;
+            constexpr int NG = decltype(tdc)::value * TH;
+            BGroup bq[2];
+            load_b(bq[0], 0);
 #pragma unroll
-            for (int dt = 0; dt < TD; ++dt)
+            for (int gi = 0; gi < NG; ++gi) {
+                if (gi + 1 < NG) load_b(bq[(gi + 1) & 1], gi + 1);
+                const int dt = gi / TH, t = gi % TH;
 #pragma unroll
-                for (int t = 0; t < TH; ++t)
+                for (int cq = 0; cq < kCg / 4; ++cq)
 #pragma unroll
-                    for (int cq = 0; cq < kCg / 4; ++cq)
+                    for (int sl = 0; sl < kNS; ++sl)
 #pragma unroll
-                        for (int sl = 0; sl < kNS; ++sl)
-#pragma unroll
-                            for (int tl = 0; tl < kNT; ++tl)
-                                acc[tl] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                                    wr[dt][t][sl][cq],
-                                    bb[(dt * kRows + TH - 1 - t) * SLOT + 4 * cq * kPW + 16 * tl + kNS - 1 - sl],
-                                    acc[tl], 0, 0, 0);
+                        for (int tl = 0; tl < kNT; ++tl)
+                            acc[tl] = __builtin_amdgcn_mfma_f32_16x16x4f32(wr[dt][t][sl][cq], bq[gi & 1][cq][sl][tl],
+                                                                           acc[tl], 0, 0, 0);
+            }
         };
         if (td == 2) contract(std::integral_constant<int, 2>{});
         else if (td == 1) contract(std::integral_constant<int, 1>{});
@@ -349,7 +386,9 @@ __global__ __launch_bounds__(kBlockT) __attribute__((amdgpu_waves_per_eu(3))) vo
             }
         }
         __syncthreads();
-        S = Sn;
+        S = S1;
+        S1 = S2;
+        advance(S2);
     };
     for (int k = k_begin; k < k_end; k += 2) {
         step(k, pre0, pre1, std::integral_constant<int, 0>{});
