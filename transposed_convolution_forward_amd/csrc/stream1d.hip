@@ -42,7 +42,6 @@ __device__ __forceinline__ f4 load4u(const float *p) {
     __builtin_memcpy(&v, p, 16);
     return v;
 }
-__device__ __forceinline__ void store4u(float *p, f4 v) { __builtin_memcpy(p, &v, 16); }
 
 // A buffer resource over one batch sample of y: the common-path stores then
 // take a row-invariant lane offset plus a uniform item offset (no 64-bit
@@ -124,19 +123,23 @@ __device__ __forceinline__ int tile_lds_off(int f) {
 // flight across the contraction of the current tile: every float4 is loaded
 // from a position clamped into the row (needs L_in >= 4); the shift back and
 // the zeroing of positions outside [0, L_in) happen when the tile is written
-// to LDS.
+// to LDS.  Offsets are 32-bit, relative to the thread's fixed offset xo[u]
+// (row and float4 column in a tile wholly inside the row), through the
+// resource over the row set's input rows: per-lane 64-bit addresses would
+// cost registers the contraction needs.
 template <int CIG, int NT>
-__device__ __forceinline__ void tile_fetch(f4 (&r)[(CIG * kRowF4 + NT - 1) / NT], const float *xrow,
-                                           int L_in, int q0, int tid) {
+__device__ __forceinline__ void tile_fetch(f4 (&r)[(CIG * kRowF4 + NT - 1) / NT], rsrc_t rx,
+                                           const unsigned (&xo)[(CIG * kRowF4 + NT - 1) / NT], int L_in,
+                                           int q0, int tid) {
     constexpr int NF = CIG * kRowF4;
     constexpr int PER = (NF + NT - 1) / NT;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int f = min(tid + u * NT, NF - 1);
-        const int row = f / kRowF4, c4 = f % kRowF4;
+        const int c4 = min(tid + u * NT, NF - 1) % kRowF4;
         const int pos = q0 - 4 + 4 * c4;
         const int cp = min(max(pos, 0), L_in - 4);
-        r[u] = load4u(xrow + (int64_t)row * L_in + cp);
+        // xo[u] holds 4*(row*L_in + 4*c4); the sum wraps back into range
+        r[u] = buf_load4(rx, xo[u] + 4u * (unsigned)(cp - 4 * c4), 0);
     }
 }
 
@@ -216,16 +219,17 @@ template <int CIG, int NT> using WinoRegs = f4[2 * kWinoPairs<CIG, NT>];
 template <int CIG, int NT> using WinoOffs = unsigned[kWinoPairs<CIG, NT>];
 
 template <int CIG, int NT>
-__device__ __forceinline__ void wino_fetch(WinoRegs<CIG, NT> &r, const float *xrow, int L_in,
-                                           int q0, int tid) {
+__device__ __forceinline__ void wino_fetch(WinoRegs<CIG, NT> &r, rsrc_t rx, const WinoOffs<CIG, NT> &xo,
+                                           int L_in, int q0, int tid) {
 #pragma unroll
     for (int u = 0; u < kWinoPairs<CIG, NT>; ++u) {
-        const int pr = min(tid + u * NT, CIG * kWinoTau - 1);
-        const int ci = pr / kWinoTau, tau = pr % kWinoTau;
+        const int tau = min(tid + u * NT, CIG * kWinoTau - 1) % kWinoTau;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int pos = q0 + 4 * tau - 4 + 4 * h;
-            r[2 * u + h] = load4u(xrow + (int64_t)ci * L_in + min(max(pos, 0), L_in - 4));
+            const int cp = min(max(pos, 0), L_in - 4);
+            // xo[u] holds 4*(ci*L_in + 4*tau); the sum wraps back into range
+            r[2 * u + h] = buf_load4(rx, xo[u] + 4u * (unsigned)(cp - 4 * tau), 0);
         }
     }
 }
@@ -385,16 +389,13 @@ __attribute__((amdgpu_waves_per_eu(CONVT_S1D_WAVES_PER_EU))) void k_stream1d(con
     // Tiles inside the row take buffer loads at fixed offsets; the others clamp.
     auto fetch = [&](f4 (&r)[NPRE], int ng_, int q0_) {
         const bool inner = q0_ - 4 >= 0 && q0_ + kTileQ <= P.L_in;
+        const rsrc_t rx = make_rsrc(const_cast<float *>(xrow_of(ng_)), x_bytes);
         if constexpr (WINO) {
-            if (inner)
-                wino_fetch_inner<CIG, NT>(r, make_rsrc(const_cast<float *>(xrow_of(ng_)), x_bytes), xo, q0_);
-            else
-                wino_fetch<CIG, NT>(r, xrow_of(ng_), P.L_in, q0_, tid);
+            if (inner) wino_fetch_inner<CIG, NT>(r, rx, xo, q0_);
+            else wino_fetch<CIG, NT>(r, rx, xo, P.L_in, q0_, tid);
         } else {
-            if (inner)
-                tile_fetch_inner<CIG, NT>(r, make_rsrc(const_cast<float *>(xrow_of(ng_)), x_bytes), xo, q0_);
-            else
-                tile_fetch<CIG, NT>(r, xrow_of(ng_), P.L_in, q0_, tid);
+            if (inner) tile_fetch_inner<CIG, NT>(r, rx, xo, q0_);
+            else tile_fetch<CIG, NT>(r, rx, xo, P.L_in, q0_, tid);
         }
     };
     auto stage = [&](float *l, const f4 (&r)[NPRE], int q0_) {
