@@ -230,6 +230,16 @@ def test_layout_selection():
     assert T.lib().convt_plan_get_layout(None) == -1
     T.convt_plan_set_layout(p, "channels_first")
     assert "kernel=k_stream1d\n" in T.convt_plan_describe(p)
+    # the 64-channel streaming variants are compiled for channels first only;
+    # the 32 -> 32 one for both layouts
+    w64 = T.Plan(1, 2, 64, 64, 1, (517,), (3,), (2,), (1,), (0,), (2,))
+    assert "kernel=k_stream1d\n" in T.convt_plan_describe(w64)
+    T.convt_plan_set_layout(w64, "channels_last")
+    assert "kernel=k_generic_nxc" in T.convt_plan_describe(w64)
+    w32 = T.Plan(1, 2, 32, 32, 1, (517,), (3,), (2,), (1,), (0,), (2,))
+    assert "kernel=k_stream1d\n" in T.convt_plan_describe(w32)
+    T.convt_plan_set_layout(w32, "channels_last")
+    assert "kernel=k_stream1d_nlc" in T.convt_plan_describe(w32)
 
 
 def test_convt_log_names_kernel_and_fallback():
@@ -240,7 +250,7 @@ def test_convt_log_names_kernel_and_fallback():
     import sys
     code = ("import transposed_convolution_forward_amd as T; from transposed_convolution_forward_amd import "
             "synthetic as S; T.plan_for(S.LONG_1D); T.plan_for(S.GROUPED_3D); "
-            "T.Plan(1, 1, 64, 64, 1, (100,), (3,), (2,), (1,), (0,), (1,))")
+            "T.Plan(1, 1, 64, 64, 1, (100,), (4,), (2,), (1,), (0,), (1,))")
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
                        env={**os.environ, "CONVT_LOG": "1"})
     assert r.returncode == 0, r.stderr

@@ -85,6 +85,8 @@ NLC_1D = [
     S.Workload("nlc_k5s4d2", 1, 1, 16, 32, 1, (257,), (5,), (4,), (3,), (2,), (2,), True, True, wid=5005),
     S.Workload("nlc_short", 1, 3, 32, 64, 1, (5,), (3,), (2,), (1,), (0,), (2,), True, False, wid=5006),
     S.Workload("nlc_L1", 1, 2, 32, 64, 1, (1,), (3,), (2,), (1,), (0,), (2,), True, False, wid=5007),
+    S.Workload("nlc_32", 1, 2, 32, 32, 1, (4099,), (3,), (2,), (1,), (0,), (2,), True, True, wid=5008),
+    S.Workload("nlc_chain_32", 1, 1, 32, 32, 1, (65553,), (3,), (2,), (2,), (1,), (2,), False, False, wid=5009),
 ]
 
 

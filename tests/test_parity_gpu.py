@@ -43,6 +43,13 @@ REDUCED = [
                wid=3005),
     S.Workload("s1d_short", 1, 3, 32, 64, 1, (5,), (3,), (2,), (1,), (0,), (2,), True, False,
                wid=3006),
+    # the 64- and 32-channel variants (channels first only for 64)
+    S.Workload("s1d_64_k3s2d2", 1, 2, 64, 64, 1, (517,), (3,), (2,), (1,), (0,), (2,), True, True,
+               wid=3011),
+    S.Workload("s1d_g2_64_k3s2d1", 1, 1, 128, 128, 2, (300,), (3,), (2,), (1,), (1,), (1,), True, False,
+               wid=3012),
+    S.Workload("s1d_32_k3s2d2", 1, 2, 32, 32, 1, (1000,), (3,), (2,), (2,), (1,), (2,), False, False,
+               wid=3013),
     # 3D shapes for each implicit-GEMM variant: fused or not, two W-blocks per
     # row, ragged last W-block, other paddings and output paddings
     S.Workload("ig_k3s2_fused_w8", 3, 2, 32, 64, 1, (5, 7, 8), (3, 3, 3), (2, 2, 2), (1, 1, 1),
@@ -212,6 +219,12 @@ CHAINED_1D = [
                wid=3009),
     S.Workload("s1d_chain_d1", 1, 2, 32, 64, 1, (65553,), (3,), (2,), (1,), (1,), (1,), True, False,
                wid=3010),
+    S.Workload("s1d_chain_64", 1, 1, 64, 64, 1, (65553,), (3,), (2,), (1,), (0,), (2,), True, False,
+               wid=3014),
+    S.Workload("s1d_chain_32", 1, 2, 32, 32, 1, (65553,), (3,), (2,), (1,), (0,), (2,), True, False,
+               wid=3015),
+    S.Workload("s1d_chain_64_d1", 1, 1, 64, 64, 1, (65553,), (3,), (2,), (1,), (1,), (1,), True, False,
+               wid=3016),
 ]
 
 

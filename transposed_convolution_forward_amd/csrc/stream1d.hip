@@ -27,6 +27,8 @@
 // Atomic-free: every output element is stored once, by one lane.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "convt_internal.h"
 #include "epilogue.hpp"
 
@@ -980,13 +982,17 @@ __attribute__((amdgpu_waves_per_eu(CONVT_NLC_WAVES_PER_EU))) void k_stream1d_nlc
 // Instantiated shapes: (C_in/g, C_out/g, K, S, D).
 struct Variant {
     int cig, cog, K, S, D;
+    bool nlc; // also compiled for channels last (the 64-channel groups would spill there)
 };
 constexpr Variant kVariants[] = {
-    {32, 64, 3, 2, 2}, // long-sequence layer: N x 32 -> 64, K=3, stride 2, dilation 2
-    {32, 64, 3, 2, 1}, // stride-2 upsampling, K=3
-    {32, 32, 4, 2, 1}, // stride-2 upsampling, K=4 (two phases, two taps each)
-    {16, 16, 3, 3, 2}, // stride 3, dilation 2: three phases, one tap each
-    {16, 32, 5, 4, 2}, // stride 4 > taps per phase: two empty phases
+    {32, 64, 3, 2, 2, true},  // long-sequence layer: N x 32 -> 64, K=3, stride 2, dilation 2
+    {32, 64, 3, 2, 1, true},  // stride-2 upsampling, K=3
+    {32, 32, 4, 2, 1, true},  // stride-2 upsampling, K=4 (two phases, two taps each)
+    {16, 16, 3, 3, 2, true},  // stride 3, dilation 2: three phases, one tap each
+    {16, 32, 5, 4, 2, true},  // stride 4 > taps per phase: two empty phases
+    {64, 64, 3, 2, 2, false}, // the long-sequence layer's pattern with 64-channel groups
+    {32, 32, 3, 2, 2, true},  // ... and with 32 -> 32 channels
+    {64, 64, 3, 2, 1, false}, // stride-2 upsampling, K=3, 64-channel groups
 };
 
 int find_variant(const convt_plan &P) {
@@ -994,7 +1000,8 @@ int find_variant(const convt_plan &P) {
     const AxisPlan &A = P.ax[2];
     for (int i = 0; i < (int)(sizeof(kVariants) / sizeof(kVariants[0])); ++i) {
         const Variant &v = kVariants[i];
-        if (P.Cig == v.cig && P.Cog == v.cog && A.K == v.K && A.s == v.S && A.d == v.D) return i;
+        if (P.Cig == v.cig && P.Cog == v.cog && A.K == v.K && A.s == v.S && A.d == v.D)
+            return P.layout == CONVT_LAYOUT_CHANNELS_LAST && !v.nlc ? -1 : i;
     }
     return -1;
 }
@@ -1030,19 +1037,24 @@ int launch_variant(const convt_plan &Pl, const float *x, const float *w, const f
     P.st_lo = (int)st_lo;
     P.n_st = (int)(st_hi - st_lo);
     P.total = Pl.N * Pl.G * P.n_st;
-    // one round of resident workgroups (see CONVT_S1D_ROUNDS)
-    // workgroups resident per CU: CONVT_S1D_WAVES_PER_EU waves on each of the
-    // 4 SIMDs, COG/16 waves per workgroup
-    const int64_t blocks_target =
-        (int64_t)num_cus() * CONVT_S1D_ROUNDS * (4 * CONVT_S1D_WAVES_PER_EU / (COG / 16));
-    int64_t per_block = (P.total + blocks_target - 1) / blocks_target;
-    if (per_block < 1) per_block = 1;
-    P.per_block = (int)per_block;
-    const unsigned grid = (unsigned)((P.total + per_block - 1) / per_block);
     constexpr int NT = COG * 4;
     with_epi(add != nullptr, act, [&](auto E) {
-        hipLaunchKernelGGL((k_stream1d<CIG, COG, K, S, D, decltype(E)::value>), dim3(grid), dim3(NT), 0, st, P,
-                           x, w, bias, add, y);
+        constexpr auto kern = k_stream1d<CIG, COG, K, S, D, decltype(E)::value>;
+        // one round of resident workgroups (see CONVT_S1D_ROUNDS): CONVT_S1D_WAVES_PER_EU
+        // waves on each of the 4 SIMDs, COG/16 waves per workgroup, or fewer where
+        // the instantiation's registers or LDS allow fewer (queried once)
+        static const int resident = [&] {
+            int nb = 0;
+            const int want = 4 * CONVT_S1D_WAVES_PER_EU / (COG / 16);
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, NT, 0) != hipSuccess || nb < 1) nb = want;
+            return std::min(nb, want);
+        }();
+        const int64_t blocks_target = (int64_t)num_cus() * CONVT_S1D_ROUNDS * resident;
+        int64_t per_block = (P.total + blocks_target - 1) / blocks_target;
+        if (per_block < 1) per_block = 1;
+        P.per_block = (int)per_block;
+        const unsigned grid = (unsigned)((P.total + per_block - 1) / per_block);
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), 0, st, P, x, w, bias, add, y);
     });
     return (int)hipGetLastError();
 }
@@ -1106,6 +1118,7 @@ int launch_stream1d(const convt_plan &Pl, const float *x, const float *w, const 
         case 2: return launch_variant_nlc<32, 32, 4, 2, 1>(Pl, x, w, bias, add, act, y, st);
         case 3: return launch_variant_nlc<16, 16, 3, 3, 2>(Pl, x, w, bias, add, act, y, st);
         case 4: return launch_variant_nlc<16, 32, 5, 4, 2>(Pl, x, w, bias, add, act, y, st);
+        case 6: return launch_variant_nlc<32, 32, 3, 2, 2>(Pl, x, w, bias, add, act, y, st);
         default: return (int)hipErrorInvalidValue;
         }
     }
@@ -1115,6 +1128,9 @@ int launch_stream1d(const convt_plan &Pl, const float *x, const float *w, const 
     case 2: return launch_variant<32, 32, 4, 2, 1>(Pl, x, w, bias, add, act, y, st);
     case 3: return launch_variant<16, 16, 3, 3, 2>(Pl, x, w, bias, add, act, y, st);
     case 4: return launch_variant<16, 32, 5, 4, 2>(Pl, x, w, bias, add, act, y, st);
+    case 5: return launch_variant<64, 64, 3, 2, 2>(Pl, x, w, bias, add, act, y, st);
+    case 6: return launch_variant<32, 32, 3, 2, 2>(Pl, x, w, bias, add, act, y, st);
+    case 7: return launch_variant<64, 64, 3, 2, 1>(Pl, x, w, bias, add, act, y, st);
     default: return (int)hipErrorInvalidValue;
     }
 }
