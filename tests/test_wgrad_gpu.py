@@ -11,7 +11,11 @@ window kernels up to 512 per range of 2048.  With u = 2^-24 and S = the sum
 of |x * dy| over the same terms (the oracle's gradient of |x| and |dy|), the
 rounding error is within (chain length) * u * S; the test allows
   |got - ref| <= 1e-4 + (max(256 + N*ceil(P/1024), 512 + N*ceil(P/2048)) + 12) * 2^-24 * S
-for P input positions, whichever kernel runs.  At full spatial size that
+for P input positions, whichever of those kernels runs.  The shift-pair
+kernel (groups of 8 and 8 channels, stride 2 along W) accumulates in one wave
+at most R * ceil((W_in + 1)/4) steps for R = D_in * H_in input rows, and at
+most N * R partial sums meet by atomic adds, so where it runs the chain is
+R * (ceil((W_in + 1)/4) + N) + 12 if that is longer.  At full spatial size that
 bound is loose (S grows with the positions summed), so the same shapes also
 run on small-integer inputs, where every fp32 partial sum is exact and the
 result must equal the oracle's bit for bit: one dropped or doubled term
@@ -60,6 +64,9 @@ def _check(wl, seed=0):
     in_sp = int(np.prod(wl.in_size))
     out_sp = int(np.prod(out))
     chain_w = max(256 + wl.N * -(-in_sp // 1024), 512 + wl.N * -(-in_sp // 2048)) + 12
+    if "weight gradient: kernel=k_backward_weight_shift" in T.convt_plan_describe(plan):
+        rows = in_sp // wl.in_size[-1]
+        chain_w = max(chain_w, rows * (-(-(wl.in_size[-1] + 1) // 4) + wl.N) + 12)
     chain_b = -(-min(out_sp, 16384) // 4096) + 4 + 8 + wl.N * -(-out_sp // 16384)
     for what, got, ref, s_abs, chain in (("dw", dw, ref_w, abs_w, chain_w), ("db", db, ref_b, abs_b, chain_b)):
         g = got.cpu().numpy().astype(np.float64)
@@ -127,6 +134,29 @@ LEADING_UNIT_AXIS = [
 def test_wgrad_leading_unit_axis(wl):
     assert "_row" not in T.convt_plan_describe(T.plan_for(wl))
     _check(wl)
+
+
+# Shapes for the shift-pair kernel (groups of 8 input and 8 output channels,
+# stride 2 and dilation 1 along W): 1D and 2D, three groups, K_w = 9 (a tile
+# with taps past K), K_w = 1, 40 tiles in three chunks, dilations and strides
+# on D and H, a padding that crops taps, odd W.
+SHIFT = [
+    S.Workload("ws_1d_crop", 1, 2, 8, 8, 1, (101,), (5,), (2,), (6,), (1,), (1,), True, False, 71),
+    S.Workload("ws_2d", 2, 2, 8, 8, 1, (5, 21), (3, 7), (1, 2), (1, 3), (0, 1), (1, 1), True, False, 72),
+    S.Workload("ws_g3_k9", 3, 1, 24, 24, 3, (3, 4, 10), (2, 3, 9), (2, 2, 2), (0, 1, 4), (1, 1, 1), (2, 1, 1),
+               True, False, 73),
+    S.Workload("ws_k1", 3, 2, 8, 8, 1, (2, 3, 7), (1, 1, 1), (1, 1, 2), (0, 0, 0), (0, 0, 1), (1, 1, 1), False,
+               False, 74),
+    S.Workload("ws_40_tiles", 3, 1, 16, 16, 2, (3, 5, 8), (4, 5, 6), (2, 1, 2), (1, 2, 2), (1, 0, 1), (1, 2, 1),
+               True, False, 75),
+]
+
+
+@pytest.mark.parametrize("wl", SHIFT, ids=lambda w: w.name)
+def test_wgrad_shift_pairs(wl):
+    assert "weight gradient: kernel=k_backward_weight_shift" in T.convt_plan_describe(T.plan_for(wl))
+    _check(wl)
+    _check_exact(wl)
 
 
 def _check_exact(wl, seed=0):

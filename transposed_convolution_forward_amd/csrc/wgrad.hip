@@ -21,6 +21,8 @@
 // so it varies in the last bits from run to run.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "wgrad.h"
 
 namespace convt {
@@ -168,6 +170,177 @@ __global__ __launch_bounds__(kWgBlock) void k_backward_weight(const WgradParams 
                 }
             }
     }
+}
+
+// Groups of 8 input and 8 output channels with stride 2 and dilation 1 along
+// W (the grouped 3D layer), where the kernel above would mask three quarters
+// of every 16 x 16 tile.  Here a tile's rows are (sigma, ci), sigma = 0, 1,
+// with A = x[ci][iw + sigma], and its columns (tau, co), tau = 0, 1, with
+// B = dy[co][2 iw - p + T + tau].  With i = iw + sigma, entry ((sigma, ci),
+// (tau, co)) sums x[ci][i] * dy[co][2 i - p + kw] over i for the W tap
+// kw = T + tau - 2 sigma, so with T = 2, 6, 10, ... each W tap lies in exactly
+// one entry of one tile (taps 4t .. 4t+3 in tile t), and a tile is useful work
+// but for taps past K.  The positions iw run over [-1, W_in) four at a time
+// (the MFMA's K), with x zero outside its row.  A wave walks a range of x rows
+// (id, ih) of one (sample, group) for up to kWsTiles (D tap, H tap, T) tiles,
+// skipping a tile whose dy row lies outside the output, then adds its tiles
+// into dw with atomics (so the result varies in the last bits from run to run,
+// as above).
+// Tuning knob: (D tap, H tap, T) tiles per wave.
+#ifndef CONVT_WS_TILES
+#define CONVT_WS_TILES 4
+#endif
+constexpr int kWsTiles = CONVT_WS_TILES;
+
+struct WsParams {
+    AxisPlan ax[kAxes];
+    int C_in, C_out, G, k_vol;
+    int in_sp, out_sp;
+    int nT;            // W tap blocks: taps T-2 .. T+1 for T = 2 + 4t
+    int ntiles;        // KD * KH * nT
+    int tchunks;       // chunks of kWsTiles tiles
+    int rows;          // x rows (id, ih) per sample
+    int rows_per_wave;
+    int rchunks;       // row ranges per (sample, group, chunk)
+    int64_t units;     // waves of work
+};
+
+__global__ __launch_bounds__(kWgBlock) void k_backward_weight_shift(const WsParams P, const float *__restrict__ x,
+                                                                    const float *__restrict__ dy, float *dw) {
+    const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
+    const int lane = threadIdx.x & 63;
+    const int64_t unit =
+        (int64_t)blockIdx.x * (kWgBlock / 64) + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    if (unit >= P.units) return; // no barrier in this kernel: a wave may leave early
+    int64_t t = unit;
+    const int rc = (int)(t % P.rchunks);
+    t /= P.rchunks;
+    const int tc = (int)(t % P.tchunks);
+    t /= P.tchunks;
+    const int g = (int)(t % P.G);
+    const int n = (int)(t / P.G);
+    const int tile0 = tc * kWsTiles, ntl = min(kWsTiles, P.ntiles - tile0);
+    const int r_begin = rc * P.rows_per_wave, r_end = min(r_begin + P.rows_per_wave, P.rows);
+
+    const int i16 = lane & 15, c4 = lane >> 4;
+    const int sig = i16 >> 3, ci = i16 & 7;  // A row
+    const int tau = i16 >> 3, co = i16 & 7;  // B column
+    const wg_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(x + ((int64_t)n * P.C_in + (int64_t)g * 8) * P.in_sp), (short)0, (int)(4 * 8 * P.in_sp),
+        kWgRsrcWord3);
+    const wg_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(dy + ((int64_t)n * P.C_out + (int64_t)g * 8) * P.out_sp), (short)0,
+        (int)(4 * 8 * P.out_sp), kWgRsrcWord3);
+    const int xch = ci * P.in_sp, ych = co * P.out_sp;
+
+    // the chunk's tiles (uniform): D tap, H tap, W tap base T
+    int tkd[kWsTiles], tkh[kWsTiles], tT[kWsTiles];
+#pragma unroll
+    for (int u = 0; u < kWsTiles; ++u) {
+        const int tile = tile0 + min(u, ntl - 1);
+        tT[u] = 2 + 4 * (tile % P.nT);
+        const int kdh = tile / P.nT;
+        tkh[u] = kdh % AH.K;
+        tkd[u] = kdh / AH.K;
+    }
+    wg_v4f acc[kWsTiles];
+#pragma unroll
+    for (int u = 0; u < kWsTiles; ++u) acc[u] = wg_v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Steps k = (row, iw0) flattened, iw0 = -1, 3, 7, ... per row; the operands
+    // of step k + 1 are loaded while step k's MFMAs run.  The loop has no
+    // branch: every load is issued (one outside x's row or the output returns
+    // zero), and every tile's MFMA runs (a dy row outside the output adds
+    // zeros; tiles past the chunk's last repeat it and are not stored), so
+    // the loads stay in flight across the MFMAs.
+    const int spr = (AW.L_in + 4) / 4; // steps per row: iw0 + 3 >= W_in - 1 at the last
+    const int nsteps = (r_end - r_begin) * spr;
+    auto load = [&](int k, float &a, float (&b)[kWsTiles]) __attribute__((always_inline)) {
+        const int rr = k / spr;
+        const int r = r_begin + rr, iw = -1 + 4 * (k - rr * spr) + c4;
+        const int id = r / AH.L_in, ih = r - id * AH.L_in;
+        const int xrow = (id * AH.L_in + ih) * AW.L_in;
+        const int xi = iw + sig;
+        // (& rather than &&: no branch around the loads)
+        const unsigned xo = ((xi >= 0) & (xi < AW.L_in)) ? 4u * (unsigned)(xch + xrow + xi) : kWgOutOfRange;
+        a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, xo, 0, 0));
+        const int ow0 = 2 * iw - AW.p + tau;
+#pragma unroll
+        for (int u = 0; u < kWsTiles; ++u) {
+            const int od = id * AD.s - AD.p + tkd[u] * AD.d, oh = ih * AH.s - AH.p + tkh[u] * AH.d;
+            const int ow = ow0 + tT[u];
+            const bool ok = (od >= 0) & (od < AD.L_out) & (oh >= 0) & (oh < AH.L_out) & (ow >= 0) & (ow < AW.L_out);
+            const unsigned yo = ok ? 4u * (unsigned)(ych + (od * AH.L_out + oh) * AW.L_out + ow) : kWgOutOfRange;
+            b[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdy, yo, 0, 0));
+        }
+    };
+    auto compute = [&](const float a, const float (&b)[kWsTiles]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kWsTiles; ++u) acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b[u], acc[u], 0, 0, 0);
+    };
+    // Two register sets in turn (a copy from one to the other would wait for
+    // the loads in flight); a load past the last step fetches the last again,
+    // unused, and an odd last step runs its second half with A = 0.
+    float a0 = 0.0f, a1, b0[kWsTiles], b1[kWsTiles];
+    if (nsteps > 0) load(0, a0, b0);
+    for (int k = 0; k < nsteps; k += 2) {
+        load(min(k + 1, nsteps - 1), a1, b1);
+        compute(a0, b0);
+        load(min(k + 2, nsteps - 1), a0, b0);
+        compute(k + 1 < nsteps ? a1 : 0.0f, b1);
+    }
+
+    // lane j + 16*c4, register v: row i = 4*c4 + v = (sigma, ci), column j = (tau, co)
+#pragma unroll
+    for (int u = 0; u < kWsTiles; ++u) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = 4 * c4 + v;
+            const int kw = tT[u] + tau - 2 * (i >> 3);
+            if (u < ntl && kw >= 0 && kw < AW.K)
+                atomicAdd(dw + ((int64_t)(g * 8 + (i & 7)) * 8 + co) * P.k_vol + (tkd[u] * AH.K + tkh[u]) * AW.K +
+                              kw,
+                          acc[u][v]);
+        }
+    }
+}
+
+// The shift-pair kernel applies: groups of 8 input and 8 output channels,
+// stride 2 and dilation 1 along W, a group's x and dy below 2 GiB.
+bool weight_shift_applies(const convt_plan &Pl) {
+    return Pl.Cig == 8 && Pl.Cog == 8 && Pl.ax[2].s == 2 && Pl.ax[2].d == 1 && 4 * 8 * Pl.in_sp <= 0x7fffffff &&
+           4 * 8 * Pl.out_sp <= 0x7fffffff;
+}
+
+// Tuning knob: waves the shift-pair kernel's grid aims for (more waves, more
+// atomic adds).
+#ifndef CONVT_WS_WAVES
+#define CONVT_WS_WAVES 4096
+#endif
+
+int launch_weight_shift(const convt_plan &Pl, const float *x, const float *dy, float *dw, hipStream_t st) {
+    WsParams P;
+    for (int a = 0; a < kAxes; ++a) P.ax[a] = Pl.ax[a];
+    P.C_in = (int)Pl.C_in;
+    P.C_out = (int)Pl.C_out;
+    P.G = (int)Pl.G;
+    P.k_vol = (int)Pl.k_vol;
+    P.in_sp = (int)Pl.in_sp;
+    P.out_sp = (int)Pl.out_sp;
+    P.nT = (Pl.ax[2].K + 3) / 4;
+    P.ntiles = Pl.ax[0].K * Pl.ax[1].K * P.nT;
+    P.tchunks = (P.ntiles + kWsTiles - 1) / kWsTiles;
+    P.rows = Pl.ax[0].L_in * Pl.ax[1].L_in;
+    const int64_t lanes = Pl.N * Pl.G * (int64_t)P.tchunks;
+    const int64_t want = (lanes * P.rows + CONVT_WS_WAVES - 1) / CONVT_WS_WAVES;
+    P.rows_per_wave = (int)std::max<int64_t>(1, std::min<int64_t>(want, P.rows));
+    P.rchunks = (P.rows + P.rows_per_wave - 1) / P.rows_per_wave;
+    P.units = lanes * P.rchunks;
+    const int64_t blocks = (P.units + kWgBlock / 64 - 1) / (kWgBlock / 64);
+    if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_backward_weight_shift, dim3((unsigned)blocks), dim3(kWgBlock), 0, st, P, x, dy, dw);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? 0 : (int)e;
 }
 
 // Channel-rich groups (32k input, 64k output channels): the same GEMM with
@@ -492,6 +665,7 @@ int launch_w(const convt_plan &Pl, WgradParams &P, const float *x, const float *
 const char *backward_weight_kernel_name(const convt_plan &P) {
     WrParams R;
     if (weight_row_window(P, R)) return "k_backward_weight_row";
+    if (weight_shift_applies(P)) return "k_backward_weight_shift";
     return P.Cig % 32 == 0 && P.Cog % 64 == 0 ? "k_backward_weight_lds" : "k_backward_weight";
 }
 
@@ -546,6 +720,8 @@ int launch_backward_weight(const convt_plan &Pl, const float *x, const float *dy
         }
         e = hipGetLastError();
         rc = e == hipSuccess ? 0 : (int)e;
+    } else if (weight_shift_applies(Pl)) {
+        rc = launch_weight_shift(Pl, x, dy, dw, st);
     } else {
         rc = (P.CT % 2 == 0 && P.OT % 4 == 0) ? launch_w<2, 4>(Pl, P, x, dy, dw, st)
                                               : launch_w<1, 1>(Pl, P, x, dy, dw, st);
