@@ -170,7 +170,7 @@ def test_gradient_kernel_routing():
     choices follow the kernels' documented conditions."""
     want = {S.TINY_1D.name: ("k_backward_data", "k_backward_weight"),
             S.LONG_1D.name: ("k_backward_data_mfma_row", "k_backward_weight_row"),
-            S.GROUPED_3D.name: ("k_backward_data", "k_backward_weight"),
+            S.GROUPED_3D.name: ("k_backward_data", "k_backward_weight_shift"),
             S.FUSED_3D.name: ("k_backward_data_mfma", "k_backward_weight_lds"),
             S.HEAVY_3D.name: ("k_backward_data_mfma", "k_backward_weight_lds")}
     for wl in S.WORKLOADS:
@@ -196,6 +196,13 @@ def test_gradient_kernel_routing():
     for lead_p, lead_op in ((1, 2), (0, 2)):
         p = T.Plan(2, 2, 32, 64, 1, (1, 1000), (1, 3), (3, 2), (lead_p, 1), (lead_op, 0), (1, 2))
         assert _gradient_kernels(p) == ("k_backward_data_mfma", "k_backward_weight_lds"), (lead_p, lead_op)
+    # the shift-pair weight kernel needs groups of 8 and 8 channels, stride 2 and
+    # dilation 1 along W: stride 1, dilation 2 or 16 output channels per group
+    # take the general kernel
+    for s_w, d_w, cout in ((2, 1, 32), (1, 1, 32), (2, 2, 32), (2, 1, 64)):
+        p = T.Plan(3, 1, 32, cout, 4, (4, 6, 16), (3, 5, 7), (2, 1, s_w), (1, 2, 3), (1, 0, 1), (1, 1, d_w))
+        want = "k_backward_weight_shift" if (s_w, d_w, cout) == (2, 1, 32) else "k_backward_weight"
+        assert _gradient_kernels(p)[1] == want, (s_w, d_w, cout)
 
 
 def test_phase_table_description():
