@@ -95,3 +95,26 @@ LEADING_UNIT_AXIS = [
 def test_backward_leading_unit_axis(wl):
     assert "_row" not in T.convt_plan_describe(T.plan_for(wl))
     _check(wl)
+
+
+# Shapes for the W-pair kernel (groups of 8 input and 8 output channels,
+# stride 2 and dilation 1 along W, stride 1 and dilation 1 along H): W
+# tiles of 32 positions with a partial last one, H not a multiple of the
+# wave's 4 rows, H taps 1, 3 and 7, W taps 1, 4 and 9, three groups, a D
+# stride of 3 with dilation 2, 2D, and a weight volume near the LDS copy's
+# limit (3 x 7 x 9 = 189).
+BWD_WPAIR = [
+    S.Workload("bwp_w33_h6", 3, 2, 8, 8, 1, (2, 6, 33), (2, 3, 4), (1, 1, 2), (0, 1, 1), (0, 0, 1), (1, 1, 1),
+               False, False, 81),
+    S.Workload("bwp_g3_kh7_kw9", 3, 1, 24, 24, 3, (3, 9, 40), (3, 7, 9), (2, 1, 2), (1, 3, 4), (1, 0, 1),
+               (1, 1, 1), False, False, 82),
+    S.Workload("bwp_kh1_kw1_d3", 3, 2, 8, 8, 1, (4, 5, 17), (2, 1, 1), (3, 1, 2), (1, 0, 0), (2, 0, 1), (2, 1, 1),
+               False, False, 83),
+    S.Workload("bwp_2d", 2, 3, 16, 16, 2, (7, 70), (3, 5), (1, 2), (1, 2), (0, 1), (1, 1), False, False, 84),
+]
+
+
+@pytest.mark.parametrize("wl", BWD_WPAIR, ids=lambda w: w.name)
+def test_backward_wpair(wl):
+    assert "input gradient: kernel=k_backward_data_wpair" in T.convt_plan_describe(T.plan_for(wl))
+    _check(wl)

@@ -17,6 +17,8 @@
 // FMAs.  Every dx element is written once by one thread; no atomics.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "backward.h"
 
 namespace convt {
@@ -431,6 +433,192 @@ __global__ __launch_bounds__(kBwdBlock, row_waves_per_simd<MT>()) void k_backwar
     }
 }
 
+// Groups of 8 input and 8 output channels with stride 2 and dilation 1 along
+// W and stride 1, dilation 1 along H (the grouped 3D layer), where the matrix
+// kernel above does not apply and the gather runs on the vector ALUs.  The two
+// W phases of each pair of input positions share one tile, as in the forward
+// W-pair kernel: rows (sigma, ci) hold dx at W position 2j + sigma, columns
+// are 16 pairs j.  Position 2j + sigma meets tap kw at output 4j + 2 sigma -
+// p + kw, so for a dy shift c the B operand dy[co][4j + c] serves row sigma
+// with tap kw = c + p - 2 sigma (zero where that tap does not exist), and
+// c over [-p, K_w - p + 2) covers every tap of both phases.  A wave owns kBpRows
+// consecutive dx rows along H: dy row oh feeds row ih through tap
+// kh = oh - ih + p_h, so each B operand it loads serves up to kBpRows MFMAs.
+// The group's weights are copied to LDS once per workgroup (coalesced) and
+// the A operands read from there.  Steps (kd, c, channel quad) run with the
+// next step's operands loaded during the current step's MFMAs (two register
+// sets, every load issued; out-of-range offsets read zero).  dx is stored
+// once per element, 32 consecutive floats per store instruction.
+constexpr int kBpRows = 4;
+constexpr int kBpMaxKvol = 192; // KD*KH*KW whose group weights fit the LDS copy
+constexpr int kBpWPer = 8 * 8 * kBpMaxKvol / 4 / kBwdBlock; // weight float4 per thread at most
+
+struct BpParams {
+    AxisPlan ax[kAxes];
+    int C_in, C_out, G, kvol;
+    int in_sp, out_sp;
+    int nwt, nhb;      // W tiles of 32 positions, H blocks of kBpRows rows
+    int per_ng;        // wave units per (sample, group): D_in * nhb * nwt
+    int blocks_per_ng; // workgroups per (sample, group)
+};
+
+template <int KH>
+__global__ __launch_bounds__(kBwdBlock) void k_backward_data_wpair(const BpParams P, const float *__restrict__ dy,
+                                                                   const float *__restrict__ w,
+                                                                   float *__restrict__ dx) {
+    constexpr int NR = KH + kBpRows - 1; // dy rows a wave's dx rows reach
+    const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
+    __shared__ __attribute__((aligned(16))) float wl[8 * 8 * kBpMaxKvol];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ng = blockIdx.x / P.blocks_per_ng;
+    const int g = ng % P.G, n = ng / P.G;
+
+    // the group's weights [ci][co][kd][kh][kw], contiguous
+    {
+        const int n4 = 8 * 8 * P.kvol / 4;
+        const bwd_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(w + (int64_t)g * 64 * P.kvol),
+                                                                (short)0, 4 * 64 * P.kvol, kBwdRsrcWord3);
+        bwd_v4f tw[kBpWPer]; // every load in flight before the first write
+#pragma unroll
+        for (int u = 0; u < kBpWPer; ++u) {
+            const int i = tid + u * kBwdBlock;
+            tw[u] = __builtin_bit_cast(bwd_v4f, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rw, i < n4 ? 16u * (unsigned)i : kBwdOutOfRange, 0, 0));
+        }
+#pragma unroll
+        for (int u = 0; u < kBpWPer; ++u) {
+            const int i = tid + u * kBwdBlock;
+            if (i < n4) *reinterpret_cast<bwd_v4f *>(wl + 4 * i) = tw[u];
+        }
+    }
+    __syncthreads();
+    const int unit = (blockIdx.x - ng * P.blocks_per_ng) * 4 + wave;
+    if (unit >= P.per_ng) return; // no barrier after this point
+    const int jt = unit % P.nwt;
+    const int hb = (unit / P.nwt) % P.nhb;
+    const int id = unit / (P.nwt * P.nhb);
+    const int ih0 = hb * kBpRows;
+
+    const int j = lane & 15, c4 = lane >> 4;
+    const int sig = j >> 3, ci = j & 7; // A row (sigma, ci) of this lane: row index j
+    const bwd_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(dy + ((int64_t)n * P.C_out + (int64_t)g * 8) * P.out_sp), (short)0, 4 * 8 * P.out_sp,
+        kBwdRsrcWord3);
+    const int NC = AW.K + 2;
+    const int nsteps = AD.K * NC * 2;
+    const int KW = AW.K;
+
+    // operands of step st = (kd, c, q): A[kh] and B[r]
+    auto load = [&](int st, bool live, float (&a)[KH], float (&b)[NR]) __attribute__((always_inline)) {
+        const int q = st & 1, t = st >> 1;
+        const int kd = t / NC, c = t - kd * NC - AW.p;
+        // A: w[ci][4q + c4][kd][kh][kw], kw = c + p - 2 sigma
+        const int kw = c + AW.p - 2 * sig;
+        const bool aok = live & (kw >= 0) & (kw < KW);
+        const int abase = ((ci * 8 + 4 * q + c4) * AD.K + kd) * KH * KW + (aok ? kw : 0);
+#pragma unroll
+        for (int kh = 0; kh < KH; ++kh) {
+            const float v = wl[abase + kh * KW];
+            a[kh] = aok ? v : 0.0f;
+        }
+        // B: dy[4q + c4][od][ih0 - p_h + r][4(16 jt + j) + c]
+        const int od = id * AD.s - AD.p + kd * AD.d;
+        const int ow = 4 * (16 * jt + j) + c;
+        const bool cok = (od >= 0) & (od < AD.L_out) & (ow >= 0) & (ow < AW.L_out);
+        const int cbase = (4 * q + c4) * P.out_sp + od * AH.L_out * AW.L_out + ow;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            const int oh = ih0 - AH.p + r;
+            const bool ok = cok & (oh >= 0) & (oh < AH.L_out);
+            const unsigned off = ok ? 4u * (unsigned)(cbase + oh * AW.L_out) : kBwdOutOfRange;
+            b[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdy, off, 0, 0));
+        }
+    };
+    bwd_v4f acc[kBpRows];
+#pragma unroll
+    for (int h = 0; h < kBpRows; ++h) acc[h] = bwd_v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    auto compute = [&](const float (&a)[KH], const float (&b)[NR]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+            for (int h = 0; h < kBpRows; ++h)
+                acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kh], b[h + kh], acc[h], 0, 0, 0);
+    };
+    // two register sets in turn; a step past the last loads the last again
+    // with A = 0
+    float a0[KH], a1[KH], b0[NR], b1[NR];
+    load(0, true, a0, b0);
+    for (int st = 0; st < nsteps; st += 2) {
+        load(min(st + 1, nsteps - 1), st + 1 < nsteps, a1, b1);
+        compute(a0, b0);
+        load(min(st + 2, nsteps - 1), st + 2 < nsteps, a0, b0);
+        compute(a1, b1);
+    }
+
+    // lane j + 16 c4, register v: row i = 4 c4 + v = (sigma, ci): dx[ci][ih][2(16 jt + j) + sigma]
+    const bwd_rsrc_t rdx = __builtin_amdgcn_make_buffer_rsrc(dx + ((int64_t)n * P.C_in + (int64_t)g * 8) * P.in_sp,
+                                                             (short)0, 4 * 8 * P.in_sp, kBwdRsrcWord3);
+    const int iw = 2 * (16 * jt + j) + (c4 >> 1);
+#pragma unroll
+    for (int h = 0; h < kBpRows; ++h) {
+        const int ih = ih0 + h;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int cio = 4 * (c4 & 1) + v;
+            const bool ok = (ih < AH.L_in) & (iw < AW.L_in);
+            const unsigned off = ok ? 4u * (unsigned)(cio * P.in_sp + (id * AH.L_in + ih) * AW.L_in + iw)
+                                    : kBwdOutOfRange;
+            // (through a VGPR: passed straight from the accumulator registers,
+            // this compiler stored component 0 for every v)
+            float val = acc[h][v];
+            asm volatile("" : "+v"(val));
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, val), rdx, off, 0, 0);
+        }
+    }
+}
+
+// The W-pair kernel applies: groups of 8 and 8 channels, stride 2 and dilation
+// 1 along W, stride 1 and dilation 1 along H, at most 7 H taps, the group's
+// weights within the LDS copy, and a group's x and dy below 2 GiB.
+bool bwd_wpair_applies(const convt_plan &P) {
+    const AxisPlan &AH = P.ax[1], &AW = P.ax[2];
+    return P.Cig == 8 && P.Cog == 8 && AW.s == 2 && AW.d == 1 && AH.s == 1 && AH.d == 1 && AH.K <= 7 &&
+           P.k_vol <= kBpMaxKvol && 4 * 8 * P.in_sp <= 0x7fffffff && 4 * 8 * P.out_sp <= 0x7fffffff;
+}
+
+int launch_bwd_wpair(const convt_plan &Pl, const float *dy, const float *w, float *dx, hipStream_t st) {
+    BpParams P;
+    for (int a = 0; a < kAxes; ++a) P.ax[a] = Pl.ax[a];
+    P.C_in = (int)Pl.C_in;
+    P.C_out = (int)Pl.C_out;
+    P.G = (int)Pl.G;
+    P.kvol = (int)Pl.k_vol;
+    P.in_sp = (int)Pl.in_sp;
+    P.out_sp = (int)Pl.out_sp;
+    P.nwt = (Pl.ax[2].L_in + 31) / 32;
+    P.nhb = (Pl.ax[1].L_in + kBpRows - 1) / kBpRows;
+    P.per_ng = Pl.ax[0].L_in * P.nhb * P.nwt;
+    P.blocks_per_ng = (P.per_ng + 3) / 4;
+    const int64_t blocks = Pl.N * Pl.G * (int64_t)P.blocks_per_ng;
+    if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
+    auto go = [&](auto khc) {
+        hipLaunchKernelGGL((k_backward_data_wpair<decltype(khc)::value>), dim3((unsigned)blocks), dim3(kBwdBlock), 0,
+                           st, P, dy, w, dx);
+    };
+    switch (Pl.ax[1].K) {
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 3: go(std::integral_constant<int, 3>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    case 5: go(std::integral_constant<int, 5>{}); break;
+    case 6: go(std::integral_constant<int, 6>{}); break;
+    default: go(std::integral_constant<int, 7>{}); break;
+    }
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? 0 : (int)e;
+}
+
 constexpr int kBwdPB = 4; // 16-position blocks per wave
 
 // Row tiles per wave for the matrix kernel (0: it does not apply).  Needs
@@ -545,6 +733,7 @@ const char *backward_data_kernel_name(const convt_plan &P) {
     const int mt = pick_mt(P);
     BwdParams W;
     if (row_window(P, mt, W)) return "k_backward_data_mfma_row";
+    if (mt == 0 && bwd_wpair_applies(P)) return "k_backward_data_wpair";
     return mt > 0 ? "k_backward_data_mfma" : "k_backward_data";
 }
 
@@ -578,6 +767,7 @@ int launch_backward_data(const convt_plan &Pl, const float *dy, const float *w, 
     case 1: return launch_mfma<1>(Pl, P, dy, w, dx, st);
     default: break;
     }
+    if (bwd_wpair_applies(Pl)) return launch_bwd_wpair(Pl, dy, w, dx, st);
     switch (pick_cpi(Pl)) {
     case 16: return launch<16>(Pl, P, dy, w, dx, st);
     case 8: return launch<8>(Pl, P, dy, w, dx, st);
