@@ -170,7 +170,7 @@ def test_gradient_kernel_routing():
     choices follow the kernels' documented conditions."""
     want = {S.TINY_1D.name: ("k_backward_data", "k_backward_weight"),
             S.LONG_1D.name: ("k_backward_data_mfma_row", "k_backward_weight_row"),
-            S.GROUPED_3D.name: ("k_backward_data_wpair", "k_backward_weight_shift"),
+            S.GROUPED_3D.name: ("k_backward_data_wpair", "k_backward_weight_shift_rows"),
             S.FUSED_3D.name: ("k_backward_data_mfma", "k_backward_weight_lds"),
             S.HEAVY_3D.name: ("k_backward_data_mfma", "k_backward_weight_lds")}
     for wl in S.WORKLOADS:
@@ -201,15 +201,19 @@ def test_gradient_kernel_routing():
     # take the general kernel
     for s_w, d_w, cout in ((2, 1, 32), (1, 1, 32), (2, 2, 32), (2, 1, 64)):
         p = T.Plan(3, 1, 32, cout, 4, (4, 6, 16), (3, 5, 7), (2, 1, s_w), (1, 2, 3), (1, 0, 1), (1, 1, d_w))
-        want = "k_backward_weight_shift" if (s_w, d_w, cout) == (2, 1, 32) else "k_backward_weight"
+        want = "k_backward_weight_shift_rows" if (s_w, d_w, cout) == (2, 1, 32) else "k_backward_weight"
         assert _gradient_kernels(p)[1] == want, (s_w, d_w, cout)
         # the input gradient's W-pair kernel has the same conditions (and H
         # stride and dilation 1, which these plans have)
         want = "k_backward_data_wpair" if (s_w, d_w, cout) == (2, 1, 32) else "k_backward_data"
         assert _gradient_kernels(p)[0] == want, (s_w, d_w, cout)
-    # H stride 2: not the W-pair input-gradient kernel
+    # H stride 2: not the W-pair input-gradient kernel, and the weight gradient
+    # without row sharing
     p = T.Plan(3, 1, 32, 32, 4, (4, 6, 16), (3, 5, 7), (2, 2, 2), (1, 2, 3), (1, 1, 1), (1, 1, 1))
     assert _gradient_kernels(p) == ("k_backward_data", "k_backward_weight_shift")
+    # 9 W taps (three T blocks): the weight gradient without row sharing
+    p = T.Plan(3, 1, 32, 32, 4, (4, 6, 16), (3, 5, 9), (2, 1, 2), (1, 2, 4), (1, 0, 1), (1, 1, 1))
+    assert _gradient_kernels(p)[1] == "k_backward_weight_shift"
 
 
 def test_phase_table_description():

@@ -14,8 +14,9 @@ rounding error is within (chain length) * u * S; the test allows
 for P input positions, whichever of those kernels runs.  The shift-pair
 kernel (groups of 8 and 8 channels, stride 2 along W) accumulates in one wave
 at most R * ceil((W_in + 1)/4) steps for R = D_in * H_in input rows, and at
-most N * R partial sums meet by atomic adds, so where it runs the chain is
-R * (ceil((W_in + 1)/4) + N) + 12 if that is longer.  At full spatial size that
+most N * R partial sums meet by atomic adds; its row-sharing variant (H
+stride 1) pads each wave's rows by up to 12, so where either runs the chain is
+R * (ceil((W_in + 1)/4) + N) + 12 * (ceil((W_in + 1)/4) + 1) if that is longer.  At full spatial size that
 bound is loose (S grows with the positions summed), so the same shapes also
 run on small-integer inputs, where every fp32 partial sum is exact and the
 result must equal the oracle's bit for bit: one dropped or doubled term
@@ -66,7 +67,8 @@ def _check(wl, seed=0):
     chain_w = max(256 + wl.N * -(-in_sp // 1024), 512 + wl.N * -(-in_sp // 2048)) + 12
     if "weight gradient: kernel=k_backward_weight_shift" in T.convt_plan_describe(plan):
         rows = in_sp // wl.in_size[-1]
-        chain_w = max(chain_w, rows * (-(-(wl.in_size[-1] + 1) // 4) + wl.N) + 12)
+        spr = -(-(wl.in_size[-1] + 1) // 4)
+        chain_w = max(chain_w, rows * (spr + wl.N) + 12 * (spr + 1))
     chain_b = -(-min(out_sp, 16384) // 4096) + 4 + 8 + wl.N * -(-out_sp // 16384)
     for what, got, ref, s_abs, chain in (("dw", dw, ref_w, abs_w, chain_w), ("db", db, ref_b, abs_b, chain_b)):
         g = got.cpu().numpy().astype(np.float64)
@@ -150,6 +152,26 @@ SHIFT = [
     S.Workload("ws_40_tiles", 3, 1, 16, 16, 2, (3, 5, 8), (4, 5, 6), (2, 1, 2), (1, 2, 2), (1, 0, 1), (1, 2, 1),
                True, False, 75),
 ]
+
+
+# Shapes for the row-sharing variant (H stride 1, dilation 1): H taps 1, 4
+# (an odd number of dy row slots: 10 rows per unrolled trip) and 7, W taps 8
+# (two T blocks) and 3 (one), H lengths that leave a short last row range,
+# several samples and groups, a cropping pad.
+SHIFT_ROWS = [
+    S.Workload("wsr_kh7_kw8", 3, 2, 16, 16, 2, (2, 23, 12), (2, 7, 8), (2, 1, 2), (1, 3, 3), (1, 0, 1),
+               (1, 1, 1), True, False, 76),
+    S.Workload("wsr_kh4_kw3", 3, 3, 8, 8, 1, (3, 31, 9), (3, 4, 3), (1, 1, 2), (1, 1, 1), (0, 0, 1), (2, 1, 1),
+               False, False, 77),
+    S.Workload("wsr_kh1_crop", 2, 2, 8, 8, 1, (13, 40), (1, 5), (1, 2), (0, 6), (0, 1), (1, 1), True, False, 78),
+]
+
+
+@pytest.mark.parametrize("wl", SHIFT_ROWS, ids=lambda w: w.name)
+def test_wgrad_shift_rows(wl):
+    assert "weight gradient: kernel=k_backward_weight_shift_rows" in T.convt_plan_describe(T.plan_for(wl))
+    _check(wl)
+    _check_exact(wl)
 
 
 @pytest.mark.parametrize("wl", SHIFT, ids=lambda w: w.name)

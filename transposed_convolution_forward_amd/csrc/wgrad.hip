@@ -22,6 +22,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "wgrad.h"
 
@@ -305,6 +306,120 @@ __global__ __launch_bounds__(kWgBlock) void k_backward_weight_shift(const WsPara
     }
 }
 
+// The same tiles where H has stride 1 and dilation 1 (the grouped 3D layer),
+// with dy rows shared across x rows: x row ih meets dy row ih - p_h + kh
+// through H tap kh, so the dy row that x row ih + 1 needs for tap kh - 1 is
+// the one row ih used for tap kh.  A wave owns one (sample, group, D tap,
+// D position) and a range of consecutive x rows, with a tile for each (H tap,
+// T) pair; per W step it walks its rows holding the dy rows in KH + 1 slots,
+// each new row loading one dy row per T instead of KH (the slot names rotate
+// with the row, compile-time in a loop unrolled by KH + 1).  The next row's
+// operands are loaded while the current row's MFMAs run.  Rows past the range
+// read x as zero.
+template <int KH, int NTW>
+__global__ __launch_bounds__(kWgBlock) void k_backward_weight_shift_rows(const WsParams P,
+                                                                         const float *__restrict__ x,
+                                                                         const float *__restrict__ dy, float *dw) {
+    constexpr int NSL = KH + 1;                       // dy row slots
+    constexpr int U = NSL % 2 == 0 ? NSL : 2 * NSL;   // rows per unrolled trip (x alternates two registers)
+    const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
+    const int lane = threadIdx.x & 63;
+    const int64_t unit =
+        (int64_t)blockIdx.x * (kWgBlock / 64) + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    if (unit >= P.units) return; // no barrier in this kernel: a wave may leave early
+    int64_t t = unit;
+    const int rri = (int)(t % P.rchunks);
+    t /= P.rchunks;
+    const int id = (int)(t % AD.L_in);
+    t /= AD.L_in;
+    const int kd = (int)(t % AD.K);
+    t /= AD.K;
+    const int g = (int)(t % P.G);
+    const int n = (int)(t / P.G);
+    const int od = id * AD.s - AD.p + kd * AD.d;
+    if (od < 0 || od >= AD.L_out) return; // this D tap reaches no output from this x plane
+    const int ih_b = rri * P.rows_per_wave;
+    const int nrows = min(P.rows_per_wave, AH.L_in - ih_b);
+    const int npad = (nrows + U - 1) / U * U;
+
+    const int i16 = lane & 15, c4 = lane >> 4;
+    const int sig = i16 >> 3, ci = i16 & 7;  // A row
+    const int tau = i16 >> 3, co = i16 & 7;  // B column
+    const wg_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(x + ((int64_t)n * P.C_in + (int64_t)g * 8) * P.in_sp), (short)0, (int)(4 * 8 * P.in_sp),
+        kWgRsrcWord3);
+    const wg_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(dy + ((int64_t)n * P.C_out + (int64_t)g * 8) * P.out_sp), (short)0,
+        (int)(4 * 8 * P.out_sp), kWgRsrcWord3);
+    const int xbase = ci * P.in_sp + (id * AH.L_in + ih_b) * AW.L_in;             // x row ih_b, channel ci
+    const int ybase = co * P.out_sp + (od * AH.L_out + ih_b - AH.p) * AW.L_out;   // dy row R = 0, channel co
+
+    wg_v4f acc[KH][NTW];
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+        for (int tt = 0; tt < NTW; ++tt) acc[kh][tt] = wg_v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const int spr = (AW.L_in + 4) / 4; // W steps: iw = -1 + 4 st + c4
+    // dy relative row R (oh = ih_b - p_h + R) at W step st, every T; zero
+    // outside the output
+    auto load_b = [&](int R, int st, float (&b)[NTW]) __attribute__((always_inline)) {
+        const int oh = ih_b - AH.p + R;
+        const bool rok = (oh >= 0) & (oh < AH.L_out);
+        const int ow0 = 2 * (4 * st + c4 - 1) - AW.p + 2 + tau;
+#pragma unroll
+        for (int tt = 0; tt < NTW; ++tt) {
+            const int ow = ow0 + 4 * tt;
+            const unsigned off = (rok & (ow >= 0) & (ow < AW.L_out)) ? 4u * (unsigned)(ybase + R * AW.L_out + ow)
+                                                                   : kWgOutOfRange;
+            b[tt] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdy, off, 0, 0));
+        }
+    };
+    // x row ih_b + rr at W step st, zero past the wave's rows or the row's ends
+    auto load_x = [&](int rr, int st) __attribute__((always_inline)) {
+        const int xi = 4 * st + c4 - 1 + sig;
+        const unsigned off = ((rr < nrows) & (xi >= 0) & (xi < AW.L_in)) ? 4u * (unsigned)(xbase + rr * AW.L_in + xi)
+                                                                      : kWgOutOfRange;
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
+    };
+    for (int st = 0; st < spr; ++st) {
+        float sl[NSL][NTW];
+        float xa[2];
+#pragma unroll
+        for (int R = 0; R < KH; ++R) load_b(R, st, sl[R]);
+        xa[0] = load_x(0, st);
+        for (int rr0 = 0; rr0 < npad; rr0 += U) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int rr = rr0 + u;
+                // the next row's new dy row (its tap KH - 1) and x row
+                load_b(rr + KH, st, sl[(u + KH) % NSL]);
+                xa[(u + 1) & 1] = load_x(rr + 1, st);
+#pragma unroll
+                for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+                    for (int tt = 0; tt < NTW; ++tt)
+                        acc[kh][tt] =
+                            __builtin_amdgcn_mfma_f32_16x16x4f32(xa[u & 1], sl[(u + kh) % NSL][tt], acc[kh][tt], 0, 0, 0);
+            }
+        }
+    }
+
+    // lane j + 16*c4, register v: row i = 4*c4 + v = (sigma, ci), column j = (tau, co)
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh)
+#pragma unroll
+        for (int tt = 0; tt < NTW; ++tt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = 4 * c4 + v;
+                const int kw = 2 + 4 * tt + tau - 2 * (i >> 3);
+                if (kw >= 0 && kw < AW.K)
+                    atomicAdd(dw + ((int64_t)(g * 8 + (i & 7)) * 8 + co) * P.k_vol + (kd * KH + kh) * AW.K + kw,
+                              acc[kh][tt][v]);
+            }
+}
+
 // The shift-pair kernel applies: groups of 8 input and 8 output channels,
 // stride 2 and dilation 1 along W, a group's x and dy below 2 GiB.
 bool weight_shift_applies(const convt_plan &Pl) {
@@ -317,6 +432,63 @@ bool weight_shift_applies(const convt_plan &Pl) {
 #ifndef CONVT_WS_WAVES
 #define CONVT_WS_WAVES 4096
 #endif
+
+// Tuning knob: waves the row-sharing kernel's grid aims for (fewer waves walk
+// longer row ranges: less warm-up and padding per row, fewer partial sums).
+#ifndef CONVT_WSR_WAVES
+#define CONVT_WSR_WAVES 1024
+#endif
+
+// The row-sharing variant applies as well: H stride 1 and dilation 1, at most
+// 7 H taps and 8 W taps (two T blocks).
+bool weight_shift_rows_applies(const convt_plan &Pl) {
+    return weight_shift_applies(Pl) && Pl.ax[1].s == 1 && Pl.ax[1].d == 1 && Pl.ax[1].K <= 7 && Pl.ax[2].K <= 8;
+}
+
+int launch_weight_shift_rows(const convt_plan &Pl, const float *x, const float *dy, float *dw, hipStream_t st) {
+    WsParams P;
+    for (int a = 0; a < kAxes; ++a) P.ax[a] = Pl.ax[a];
+    P.C_in = (int)Pl.C_in;
+    P.C_out = (int)Pl.C_out;
+    P.G = (int)Pl.G;
+    P.k_vol = (int)Pl.k_vol;
+    P.in_sp = (int)Pl.in_sp;
+    P.out_sp = (int)Pl.out_sp;
+    const int KH = Pl.ax[1].K, NTW = (Pl.ax[2].K + 3) / 4;
+    const int U = (KH + 1) % 2 == 0 ? KH + 1 : 2 * (KH + 1);
+    const int H = Pl.ax[1].L_in;
+    // row ranges: about CONVT_WSR_WAVES waves (at least one range per x
+    // plane), each range a multiple of the unrolled trip (its padding rows add
+    // zeros)
+    const int64_t base = Pl.N * Pl.G * (int64_t)Pl.ax[0].K * Pl.ax[0].L_in;
+    const int64_t want = std::max<int64_t>(1, std::min<int64_t>(H, (CONVT_WSR_WAVES + base - 1) / base));
+    int rpw = (int)((H + want - 1) / want);
+    rpw = (rpw + U - 1) / U * U;
+    P.rows_per_wave = rpw;
+    P.rchunks = (H + rpw - 1) / rpw;
+    P.units = base * P.rchunks;
+    const int64_t blocks = (P.units + kWgBlock / 64 - 1) / (kWgBlock / 64);
+    if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
+    auto go = [&](auto khc, auto ntc) {
+        hipLaunchKernelGGL((k_backward_weight_shift_rows<decltype(khc)::value, decltype(ntc)::value>),
+                           dim3((unsigned)blocks), dim3(kWgBlock), 0, st, P, x, dy, dw);
+    };
+    auto by_nt = [&](auto khc) {
+        if (NTW == 1) go(khc, std::integral_constant<int, 1>{});
+        else go(khc, std::integral_constant<int, 2>{});
+    };
+    switch (KH) {
+    case 1: by_nt(std::integral_constant<int, 1>{}); break;
+    case 2: by_nt(std::integral_constant<int, 2>{}); break;
+    case 3: by_nt(std::integral_constant<int, 3>{}); break;
+    case 4: by_nt(std::integral_constant<int, 4>{}); break;
+    case 5: by_nt(std::integral_constant<int, 5>{}); break;
+    case 6: by_nt(std::integral_constant<int, 6>{}); break;
+    default: by_nt(std::integral_constant<int, 7>{}); break;
+    }
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? 0 : (int)e;
+}
 
 int launch_weight_shift(const convt_plan &Pl, const float *x, const float *dy, float *dw, hipStream_t st) {
     WsParams P;
@@ -665,6 +837,7 @@ int launch_w(const convt_plan &Pl, WgradParams &P, const float *x, const float *
 const char *backward_weight_kernel_name(const convt_plan &P) {
     WrParams R;
     if (weight_row_window(P, R)) return "k_backward_weight_row";
+    if (weight_shift_rows_applies(P)) return "k_backward_weight_shift_rows";
     if (weight_shift_applies(P)) return "k_backward_weight_shift";
     return P.Cig % 32 == 0 && P.Cog % 64 == 0 ? "k_backward_weight_lds" : "k_backward_weight";
 }
@@ -720,6 +893,8 @@ int launch_backward_weight(const convt_plan &Pl, const float *x, const float *dy
         }
         e = hipGetLastError();
         rc = e == hipSuccess ? 0 : (int)e;
+    } else if (weight_shift_rows_applies(Pl)) {
+        rc = launch_weight_shift_rows(Pl, x, dy, dw, st);
     } else if (weight_shift_applies(Pl)) {
         rc = launch_weight_shift(Pl, x, dy, dw, st);
     } else {
