@@ -315,7 +315,9 @@ __global__ __launch_bounds__(kWgBlock) void k_backward_weight_shift(const WsPara
 // each new row loading one dy row per T instead of KH (the slot names rotate
 // with the row, compile-time in a loop unrolled by KH + 1).  The next row's
 // operands are loaded while the current row's MFMAs run.  Rows past the range
-// read x as zero.
+// read x as zero.  The four waves of a workgroup share (sample, group, D tap)
+// and take different (x plane, row range) units; they sum their tiles in LDS
+// and add a quarter of the atomic updates each.
 template <int KH, int NTW>
 __global__ __launch_bounds__(kWgBlock) void k_backward_weight_shift_rows(const WsParams P,
                                                                          const float *__restrict__ x,
@@ -324,20 +326,21 @@ __global__ __launch_bounds__(kWgBlock) void k_backward_weight_shift_rows(const W
     constexpr int U = NSL % 2 == 0 ? NSL : 2 * NSL;   // rows per unrolled trip (x alternates two registers)
     const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
     const int lane = threadIdx.x & 63;
-    const int64_t unit =
-        (int64_t)blockIdx.x * (kWgBlock / 64) + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    if (unit >= P.units) return; // no barrier in this kernel: a wave may leave early
-    int64_t t = unit;
-    const int rri = (int)(t % P.rchunks);
-    t /= P.rchunks;
-    const int id = (int)(t % AD.L_in);
-    t /= AD.L_in;
-    const int kd = (int)(t % AD.K);
-    t /= AD.K;
-    const int g = (int)(t % P.G);
-    const int n = (int)(t / P.G);
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    // workgroup: (sample, group, D tap) and four of its (x plane, row range)
+    // units; a wave past the last unit, or whose D tap reaches no output from
+    // its plane, has no work but joins the reduction
+    const int per = AD.L_in * P.rchunks;
+    const int bpg = (per + 3) / 4;
+    const int64_t ngk = (int64_t)blockIdx.x / bpg;
+    const int sub = (int)((int64_t)blockIdx.x - ngk * bpg) * 4 + wave;
+    const int kd = (int)(ngk % AD.K);
+    const int g = (int)((ngk / AD.K) % P.G);
+    const int n = (int)(ngk / AD.K / P.G);
+    const int rri = sub % P.rchunks;
+    const int id = min(sub / P.rchunks, AD.L_in - 1);
     const int od = id * AD.s - AD.p + kd * AD.d;
-    if (od < 0 || od >= AD.L_out) return; // this D tap reaches no output from this x plane
+    const bool work = sub < per && od >= 0 && od < AD.L_out; // uniform over the wave
     const int ih_b = rri * P.rows_per_wave;
     const int nrows = min(P.rows_per_wave, AH.L_in - ih_b);
     const int npad = (nrows + U - 1) / U * U;
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(kWgBlock) void k_backward_weight_shift_rows(const W
 #pragma unroll
         for (int tt = 0; tt < NTW; ++tt) acc[kh][tt] = wg_v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int spr = (AW.L_in + 4) / 4; // W steps: iw = -1 + 4 st + c4
+    const int spr = work ? (AW.L_in + 4) / 4 : 0; // W steps: iw = -1 + 4 st + c4
     // dy relative row R (oh = ih_b - p_h + R) at W step st, every T; zero
     // outside the output
     auto load_b = [&](int R, int st, float (&b)[NTW]) __attribute__((always_inline)) {
@@ -405,19 +408,28 @@ __global__ __launch_bounds__(kWgBlock) void k_backward_weight_shift_rows(const W
         }
     }
 
-    // lane j + 16*c4, register v: row i = 4*c4 + v = (sigma, ci), column j = (tau, co)
+    // The four waves' tiles meet in LDS ([value e][wave][lane], e = (kh, tt,
+    // v)); wave w then adds values e = w, w + 4, ... of the sum into dw.
+    // Lane j + 16*c4, register v: row i = 4*c4 + v = (sigma, ci), column j =
+    // (tau, co).
+    constexpr int NE = KH * NTW * 4;
+    __shared__ float red[NE * 4 * 64];
 #pragma unroll
     for (int kh = 0; kh < KH; ++kh)
 #pragma unroll
         for (int tt = 0; tt < NTW; ++tt)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int i = 4 * c4 + v;
-                const int kw = 2 + 4 * tt + tau - 2 * (i >> 3);
-                if (kw >= 0 && kw < AW.K)
-                    atomicAdd(dw + ((int64_t)(g * 8 + (i & 7)) * 8 + co) * P.k_vol + (kd * KH + kh) * AW.K + kw,
-                              acc[kh][tt][v]);
-            }
+            for (int v = 0; v < 4; ++v) red[(((kh * NTW + tt) * 4 + v) * 4 + wave) * 64 + lane] = acc[kh][tt][v];
+    __syncthreads();
+    for (int e = wave; e < NE; e += 4) {
+        const float sum = (red[(e * 4 + 0) * 64 + lane] + red[(e * 4 + 1) * 64 + lane]) +
+                          (red[(e * 4 + 2) * 64 + lane] + red[(e * 4 + 3) * 64 + lane]);
+        const int v = e & 3, tt = (e >> 2) % NTW, kh = (e >> 2) / NTW;
+        const int i = 4 * c4 + v;
+        const int kw = 2 + 4 * tt + tau - 2 * (i >> 3);
+        if (kw >= 0 && kw < AW.K)
+            atomicAdd(dw + ((int64_t)(g * 8 + (i & 7)) * 8 + co) * P.k_vol + (kd * KH + kh) * AW.K + kw, sum);
+    }
 }
 
 // The shift-pair kernel applies: groups of 8 input and 8 output channels,
@@ -467,8 +479,10 @@ int launch_weight_shift_rows(const convt_plan &Pl, const float *x, const float *
     P.rows_per_wave = rpw;
     P.rchunks = (H + rpw - 1) / rpw;
     P.units = base * P.rchunks;
-    const int64_t blocks = (P.units + kWgBlock / 64 - 1) / (kWgBlock / 64);
-    if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
+    // workgroups: per (sample, group, D tap), four (x plane, row range) units each
+    const int64_t blocks =
+        Pl.N * Pl.G * (int64_t)Pl.ax[0].K * ((Pl.ax[0].L_in * (int64_t)P.rchunks + 3) / 4);
+    if (blocks > 0x7fffffff || Pl.ax[0].L_in * (int64_t)P.rchunks > 0x7fffffff) return (int)hipErrorInvalidValue;
     auto go = [&](auto khc, auto ntc) {
         hipLaunchKernelGGL((k_backward_weight_shift_rows<decltype(khc)::value, decltype(ntc)::value>),
                            dim3((unsigned)blocks), dim3(kWgBlock), 0, st, P, x, dy, dw);
