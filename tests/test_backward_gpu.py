@@ -118,3 +118,27 @@ BWD_WPAIR = [
 def test_backward_wpair(wl):
     assert "input gradient: kernel=k_backward_data_wpair" in T.convt_plan_describe(T.plan_for(wl))
     _check(wl)
+
+
+# Shapes for the LDS-staged matrix kernel (groups of 32k input and 4k output
+# channels, W_in of 16, 32 or 64, at most 32 taps): a second row block that
+# is partial (H 20 with 16 rows per workgroup) and 27 taps; W 32 with two
+# groups, H dilation 2 and an even tap count (16: the last tap's operand
+# reads run one tap past the end); 2D with W 64, W stride 3 and one channel
+# quad; one D tap with D stride 3, W dilation 3, three quads and two channel
+# chunks.
+BWD_STAGE = [
+    S.Workload("bst_w16_h20", 3, 2, 32, 8, 1, (3, 20, 16), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 0, 1), (1, 1, 1),
+               False, False, 85),
+    S.Workload("bst_w32_g2_dh2", 3, 1, 64, 16, 2, (2, 9, 32), (2, 2, 4), (1, 2, 2), (0, 1, 2), (0, 1, 1),
+               (1, 2, 1), False, False, 86),
+    S.Workload("bst_2d_w64_s3", 2, 2, 32, 4, 1, (7, 64), (3, 2), (1, 3), (1, 0), (0, 2), (1, 1), False, False, 87),
+    S.Workload("bst_kd1_dw3", 3, 1, 64, 12, 1, (4, 5, 16), (1, 3, 2), (3, 1, 3), (0, 1, 2), (2, 0, 1), (1, 1, 3),
+               False, False, 88),
+]
+
+
+@pytest.mark.parametrize("wl", BWD_STAGE, ids=lambda w: w.name)
+def test_backward_stage(wl):
+    assert "input gradient: kernel=k_backward_data_stage" in T.convt_plan_describe(T.plan_for(wl))
+    _check(wl)

@@ -145,6 +145,10 @@ template <int MT> constexpr int stage_depth() { return MT >= 4 ? 1 : 8; }
 // keeps its accumulators in AGPRs instead of holding 168 VGPRs (three waves);
 // channel-heavy shape 3.52 -> 3.36 ms, fused-layer shape unchanged, five no better.
 constexpr int kMfmaWavesPerSimd = 4;
+// Tuning knob: the LDS-staged variant of the matrix kernel where it applies.
+#ifndef CONVT_BWD_STAGE
+#define CONVT_BWD_STAGE 1
+#endif
 constexpr int kRowMaxT = 10; // 64-column steps of the one-axis kernel's dy window (640 columns)
 constexpr int kRowMinWgs = 2048;       // the one-axis kernel's grid, at least (8 per CU)
 constexpr int kRowMaxTilesPerWg = 8;
@@ -431,6 +435,260 @@ __global__ __launch_bounds__(kBwdBlock, row_waves_per_simd<MT>()) void k_backwar
             }
         }
     }
+}
+
+// The matrix kernel above reads its B operands from global memory, tap by
+// tap; where a workgroup's dy rows do not stay in L2 between taps (the fused
+// 3D layer: each dy element is fetched about six times per call), this
+// variant stages them in LDS.  A workgroup owns R = 256 / W_in consecutive dx
+// rows of one (sample, group, chunk of 16*CT input channels, D position):
+// 4*CT waves, wave w holding channel tile w / 4 and 4 blocks of 16 positions
+// ((w % 4) * 64 + 16 pb in the rows' row-major order).  It walks sub-steps
+// (channel quad q, D tap kd); each stages the dy window of that quad and tap,
+// 4 channels x NR rows x NW columns of one dy plane (zero outside the output:
+// rows oh0 .. oh0 + NR - 1, columns -p_w .. -p_w + NW - 1), double buffered,
+// the next window loaded into registers during the current one's MFMAs.  The
+// quad's weights w[ci][4q .. 4q+3][taps] are copied to LDS once per quad
+// (loaded during the previous quad).  Per tap, B (lane j + 16c: dy channel
+// 4q + c at the position's tap output) and A are read from LDS.
+//
+// Thread t stages window elements t + 256*CT*u (u < 18/CT) at those LDS
+// offsets; the buffer holds 4608 floats, so the writes need no bounds test.
+// Each element's byte offset within its plane quad is fixed per workgroup and
+// computed once (out of range where it lies outside the output or the
+// window: the load reads zero); a sub-step adds the plane's offset as the
+// scalar offset, or takes a resource of zero size where its D position lies
+// outside the output.  The weights go the same way, 8 per thread (at most 32
+// taps).
+constexpr int kBsWinCap = 4608; // floats per window buffer
+constexpr int kBsWU = 8;        // weight-slice elements per thread
+
+struct BsParams {
+    AxisPlan ax[kAxes];
+    int C_in, C_out, Cig, Cog, kvol;
+    int in_sp, out_sp;
+    int R, nhb, ccs, NQ;   // rows per workgroup, row blocks, channel chunks, quads
+    int NR, NW;            // window rows, columns (the LDS pitch is NW)
+    int win_sz;            // window floats: 4 * NR * NW <= kBsWinCap
+};
+
+template <int CT>
+__global__ __launch_bounds__(256 * CT) void k_backward_data_stage(const BsParams P, const float *__restrict__ dy,
+                                                                   const float *__restrict__ w,
+                                                                   float *__restrict__ dx) {
+    constexpr int NT = 256 * CT, U = kBsWinCap / NT, PB = 4;
+    static_assert(U * NT == kBsWinCap, "window buffer split evenly over the threads");
+    const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int m = wave >> 2, wq4 = wave & 3;
+    const int j16 = lane & 15, c4 = lane >> 4;
+    int64_t b = blockIdx.x;
+    const int hb = (int)(b % P.nhb);
+    b /= P.nhb;
+    const int id = (int)(b % AD.L_in);
+    b /= AD.L_in;
+    const int cc = (int)(b % P.ccs);
+    b /= P.ccs;
+    const int g = (int)(b % (P.C_in / P.Cig));
+    const int n = (int)(b / (P.C_in / P.Cig));
+    const int ih0 = hb * P.R;
+    const int ci0 = g * P.Cig + cc * 16 * CT;
+    const int od0 = id * AD.s - AD.p, oh0 = ih0 * AH.s - AH.p, ow0 = -AW.p;
+    const int KHW = AH.K * AW.K, nsub = P.NQ * AD.K;
+    const int wq_sz = 16 * CT * 4 * P.kvol;
+
+    extern __shared__ __attribute__((aligned(16))) float lds_bs[];
+    float *win0 = lds_bs, *win1 = lds_bs + kBsWinCap, *wq = lds_bs + 2 * kBsWinCap;
+
+    // window element e = tid + NT*u: channel c, row rr, column col; its byte
+    // offset from the plane quad's start, or out of range
+    unsigned voff[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int e = tid + u * NT;
+        const int c = e / (P.NR * P.NW), rem = e - c * (P.NR * P.NW);
+        const int rr = rem / P.NW, col = rem - rr * P.NW;
+        const int oh = oh0 + rr, ow = ow0 + col;
+        const bool ok = e < P.win_sz && oh >= 0 && oh < AH.L_out && ow >= 0 && ow < AW.L_out;
+        voff[u] = ok ? 4u * (unsigned)(c * P.out_sp + oh * AW.L_out + ow) : kBwdOutOfRange;
+    }
+    const int dy_bytes = 4 * P.C_out * P.out_sp;
+    float *dyn = const_cast<float *>(dy + (int64_t)n * P.C_out * P.out_sp);
+    const bwd_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(dyn, (short)0, dy_bytes, kBwdRsrcWord3);
+    const bwd_rsrc_t rnone = __builtin_amdgcn_make_buffer_rsrc(dyn, (short)0, 0, kBwdRsrcWord3);
+    // window of sub-step ss = (q, kd) into registers (zeros outside the output)
+    auto fetch = [&](float (&pf)[U], int ss) __attribute__((always_inline)) {
+        const int q = ss / AD.K, kd = ss - q * AD.K;
+        const int od = od0 + kd * AD.d;
+        const bool odok = ss < nsub && od >= 0 && od < AD.L_out;
+        const bwd_rsrc_t r = odok ? rdy : rnone;
+        const int soff = odok ? 4 * ((g * P.Cog + 4 * q) * P.out_sp + od * AH.L_out * AW.L_out) : 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            pf[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff[u], soff, 0));
+    };
+    auto stage = [&](float *wb, const float (&pf)[U]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) wb[tid + u * NT] = pf[u];
+    };
+    // weight element e = tid + NT*u: input channel cil, [c][k] index rem of
+    // w[ci0 + cil][4q + c][k]; byte offset from w[ci0][4q][0] (out of range
+    // past the slice)
+    unsigned woff[kBsWU];
+#pragma unroll
+    for (int u = 0; u < kBsWU; ++u) {
+        const int e = tid + u * NT;
+        const int cil = e / (4 * P.kvol), rem = e - cil * (4 * P.kvol);
+        woff[u] = e < wq_sz ? 4u * (unsigned)(cil * P.Cog * P.kvol + rem) : kBwdOutOfRange;
+    }
+    const bwd_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(w + (int64_t)ci0 * P.Cog * P.kvol), (short)0, 4 * 16 * CT * P.Cog * P.kvol, kBwdRsrcWord3);
+    float wpf[kBsWU];
+    auto fetch_w = [&](int q) __attribute__((always_inline)) {
+        const int soff = 16 * min(q, P.NQ - 1) * P.kvol;
+#pragma unroll
+        for (int u = 0; u < kBsWU; ++u)
+            wpf[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, woff[u], soff, 0));
+    };
+    auto stage_w = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < kBsWU; ++u) wq[tid + u * NT] = wpf[u];
+    };
+
+    // per block pb of this wave: row r and first column, so the B address is
+    // bpos[pb] + (kh*dh)*NW + kw*dw within the channel's window
+    int bpos[PB];
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) {
+        const int blk = wq4 * PB + pb;
+        const int r = (blk * 16) / AW.L_in, col0 = (blk * 16) - r * AW.L_in;
+        bpos[pb] = (c4 * P.NR + r * AH.s) * P.NW + (col0 + j16) * AW.s;
+    }
+    const int abase = ((16 * m + j16) * 4 + c4) * P.kvol;
+    bwd_v4f acc[PB];
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) acc[pb] = bwd_v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    float pf[U];
+    fetch_w(0);
+    fetch(pf, 0);
+    stage_w();
+    stage(win0, pf);
+    fetch(pf, 1);
+    fetch_w(1);
+    __syncthreads();
+    for (int ss = 0; ss < nsub; ++ss) {
+        const int kd = ss % AD.K;
+        const float *wb = (ss & 1) ? win1 : win0;
+        // taps (kd, kh, kw) in order, two operand sets: the reads of tap t + 1
+        // are in flight during tap t's products.  (k, kw, toff) walk the taps
+        // with scalar steps.  With an even tap count the last reads are of
+        // the tap after the last (row K_h, column 0; weight index k = kvol at
+        // the last kd), never used: they stay within d_h * NW floats past the
+        // window buffer and one past the weight slice, which the allocation
+        // pads.
+        int k = kd * KHW, kw = 0, toff = 0;
+        auto next = [&]() __attribute__((always_inline)) {
+            const bool row_end = kw == AW.K - 1;
+            toff += row_end ? AH.d * P.NW - (AW.K - 1) * AW.d : AW.d;
+            kw = row_end ? 0 : kw + 1;
+            ++k;
+        };
+        auto rd = [&](float &a, float (&bb)[PB]) __attribute__((always_inline)) {
+            a = wq[abase + k];
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb) bb[pb] = wb[bpos[pb] + toff];
+        };
+        auto mma = [&](const float a, const float (&bb)[PB]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int pb = 0; pb < PB; ++pb)
+                acc[pb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb[pb], acc[pb], 0, 0, 0);
+        };
+        float a0, b0[PB], a1, b1[PB];
+        rd(a0, b0);
+        int t = 0;
+        for (; t + 2 <= KHW; t += 2) {
+            next();
+            rd(a1, b1);
+            mma(a0, b0);
+            next();
+            rd(a0, b0);
+            mma(a1, b1);
+        }
+        if (t < KHW) mma(a0, b0);
+        const bool quad_end = kd == AD.K - 1;
+        if (quad_end) __syncthreads(); // every wave is done with this quad's weights
+        // the next window into the other buffer (read last in sub-step ss - 1)
+        stage((ss & 1) ? win0 : win1, pf);
+        if (quad_end) {
+            stage_w();
+            fetch_w(ss / AD.K + 2);
+        }
+        fetch(pf, ss + 2);
+        __syncthreads();
+    }
+
+    // lane j16 + 16*c4, register v: position j16 of block pb, input channel
+    // 16m + 4*c4 + v
+#pragma unroll
+    for (int pb = 0; pb < PB; ++pb) {
+        const int blk = wq4 * PB + pb;
+        const int r = (blk * 16) / AW.L_in, col0 = (blk * 16) - r * AW.L_in;
+        if (ih0 + r >= AH.L_in) continue;
+        const int sp = (id * AH.L_in + ih0 + r) * AW.L_in + col0 + j16;
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            dx[((int64_t)n * P.C_in + ci0 + 16 * m + 4 * c4 + v) * P.in_sp + sp] = acc[pb][v];
+    }
+}
+
+// LDS floats of one workgroup: two window buffers, the weight slice (NT *
+// kBsWU), and the pad past them that the last tap's unused reads may touch.
+inline size_t stage_lds_floats(int ct, int dh, int NW) {
+    return 2 * (size_t)kBsWinCap + (size_t)256 * ct * kBsWU + (size_t)dh * NW + 1;
+}
+
+// The staged variant applies: 2D or 3D plans with groups of 32k input and 4k
+// output channels (two channel tiles per workgroup; with one, each dy window
+// would be staged once per 16 channels and the matrix kernel is faster),
+// W_in of 16, 32 or 64, at most 32 taps, a window of at most kBsWinCap
+// floats, and the buffers within 64 KB of LDS.  Returns the tile count CT, 0
+// when it does not apply; fills the window fields of P.
+int stage_ct(const convt_plan &Pl, BsParams &P) {
+    const AxisPlan &AH = Pl.ax[1], &AW = Pl.ax[2];
+    if (Pl.ndim < 2 || Pl.Cig % 32 != 0 || Pl.Cog % 4 != 0 || Pl.k_vol > 32) return 0;
+    if (AW.L_in != 16 && AW.L_in != 32 && AW.L_in != 64) return 0;
+    if (4 * Pl.C_out * Pl.out_sp > 0x7fffffff || Pl.N * Pl.C_in * Pl.in_sp > ((int64_t)1 << 40)) return 0;
+    P.R = 256 / AW.L_in;
+    P.NR = (P.R - 1) * AH.s + (AH.K - 1) * AH.d + 1;
+    P.NW = (AW.L_in - 1) * AW.s + (AW.K - 1) * AW.d + 1;
+    P.win_sz = 4 * P.NR * P.NW;
+    if (P.win_sz > kBsWinCap) return 0;
+    const int ct = 2;
+    if (4 * stage_lds_floats(ct, AH.d, P.NW) > 65536) return 0;
+    return ct;
+}
+
+template <int CT>
+int launch_stage(const convt_plan &Pl, BsParams &P, const float *dy, const float *w, float *dx, hipStream_t st) {
+    for (int a = 0; a < kAxes; ++a) P.ax[a] = Pl.ax[a];
+    P.C_in = (int)Pl.C_in;
+    P.C_out = (int)Pl.C_out;
+    P.Cig = (int)Pl.Cig;
+    P.Cog = (int)Pl.Cog;
+    P.kvol = (int)Pl.k_vol;
+    P.in_sp = (int)Pl.in_sp;
+    P.out_sp = (int)Pl.out_sp;
+    P.nhb = (Pl.ax[1].L_in + P.R - 1) / P.R;
+    P.ccs = (int)(Pl.Cig / (16 * CT));
+    P.NQ = (int)(Pl.Cog / 4);
+    const int64_t blocks = Pl.N * Pl.G * (int64_t)P.ccs * Pl.ax[0].L_in * P.nhb;
+    if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
+    const size_t lds = 4 * stage_lds_floats(CT, P.ax[1].d, P.NW);
+    hipLaunchKernelGGL((k_backward_data_stage<CT>), dim3((unsigned)blocks), dim3(256 * CT), lds, st, P, dy, w, dx);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? 0 : (int)e;
 }
 
 // Groups of 8 input and 8 output channels with stride 2 and dilation 1 along
@@ -734,6 +992,8 @@ const char *backward_data_kernel_name(const convt_plan &P) {
     BwdParams W;
     if (row_window(P, mt, W)) return "k_backward_data_mfma_row";
     if (mt == 0 && bwd_wpair_applies(P)) return "k_backward_data_wpair";
+    BsParams S;
+    if (CONVT_BWD_STAGE && mt > 0 && stage_ct(P, S) > 0) return "k_backward_data_stage";
     return mt > 0 ? "k_backward_data_mfma" : "k_backward_data";
 }
 
@@ -761,6 +1021,8 @@ int launch_backward_data(const convt_plan &Pl, const float *dy, const float *w, 
         default: return launch_mfma_row<1>(Pl, P, dy, w, dx, st);
         }
     }
+    BsParams S;
+    if (CONVT_BWD_STAGE && mt > 0 && stage_ct(Pl, S) == 2) return launch_stage<2>(Pl, S, dy, w, dx, st);
     switch (mt) {
     case 4: return launch_mfma<4>(Pl, P, dy, w, dx, st);
     case 2: return launch_mfma<2>(Pl, P, dy, w, dx, st);
