@@ -472,13 +472,20 @@ struct BsParams {
     int win_sz;            // window floats: 4 * NR * NW <= kBsWinCap
 };
 
-template <int CT>
-__global__ __launch_bounds__(256 * CT) void k_backward_data_stage(const BsParams P, const float *__restrict__ dy,
+template <int CT, bool FIX>
+__global__ __launch_bounds__(256 * CT) __attribute__((amdgpu_waves_per_eu(1, 6))) void k_backward_data_stage(const BsParams P, const float *__restrict__ dy,
                                                                    const float *__restrict__ w,
                                                                    float *__restrict__ dx) {
     constexpr int NT = 256 * CT, U = kBsWinCap / NT, PB = 4;
     static_assert(U * NT == kBsWinCap, "window buffer split evenly over the threads");
     const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
+    // H and W geometry; FIX: W_in 16, stride 2, 3 taps and dilation 1 on both
+    // (the fused layer's), as constants, so that every window offset of a tap
+    // is an immediate
+    const int WIN = FIX ? 16 : AW.L_in;
+    const int SH = FIX ? 2 : AH.s, SW = FIX ? 2 : AW.s, KH = FIX ? 3 : AH.K, KW = FIX ? 3 : AW.K;
+    const int DH = FIX ? 1 : AH.d, DW = FIX ? 1 : AW.d;
+    const int NR = FIX ? 33 : P.NR, NW = FIX ? 33 : P.NW;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m = wave >> 2, wq4 = wave & 3;
@@ -494,8 +501,8 @@ __global__ __launch_bounds__(256 * CT) void k_backward_data_stage(const BsParams
     const int n = (int)(b / (P.C_in / P.Cig));
     const int ih0 = hb * P.R;
     const int ci0 = g * P.Cig + cc * 16 * CT;
-    const int od0 = id * AD.s - AD.p, oh0 = ih0 * AH.s - AH.p, ow0 = -AW.p;
-    const int KHW = AH.K * AW.K, nsub = P.NQ * AD.K;
+    const int od0 = id * AD.s - AD.p, oh0 = ih0 * SH - AH.p, ow0 = -AW.p;
+    const int KHW = KH * KW, nsub = P.NQ * AD.K;
     const int wq_sz = 16 * CT * 4 * P.kvol;
 
     extern __shared__ __attribute__((aligned(16))) float lds_bs[];
@@ -507,10 +514,10 @@ __global__ __launch_bounds__(256 * CT) void k_backward_data_stage(const BsParams
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int e = tid + u * NT;
-        const int c = e / (P.NR * P.NW), rem = e - c * (P.NR * P.NW);
-        const int rr = rem / P.NW, col = rem - rr * P.NW;
+        const int c = e / (NR * NW), rem = e - c * (NR * NW);
+        const int rr = rem / NW, col = rem - rr * NW;
         const int oh = oh0 + rr, ow = ow0 + col;
-        const bool ok = e < P.win_sz && oh >= 0 && oh < AH.L_out && ow >= 0 && ow < AW.L_out;
+        const bool ok = e < 4 * NR * NW && oh >= 0 && oh < AH.L_out && ow >= 0 && ow < AW.L_out;
         voff[u] = ok ? 4u * (unsigned)(c * P.out_sp + oh * AW.L_out + ow) : kBwdOutOfRange;
     }
     const int dy_bytes = 4 * P.C_out * P.out_sp;
@@ -562,8 +569,8 @@ __global__ __launch_bounds__(256 * CT) void k_backward_data_stage(const BsParams
 #pragma unroll
     for (int pb = 0; pb < PB; ++pb) {
         const int blk = wq4 * PB + pb;
-        const int r = (blk * 16) / AW.L_in, col0 = (blk * 16) - r * AW.L_in;
-        bpos[pb] = (c4 * P.NR + r * AH.s) * P.NW + (col0 + j16) * AW.s;
+        const int r = (blk * 16) / WIN, col0 = (blk * 16) - r * WIN;
+        bpos[pb] = (c4 * NR + r * SH) * NW + (col0 + j16) * SW;
     }
     const int abase = ((16 * m + j16) * 4 + c4) * P.kvol;
     bwd_v4f acc[PB];
@@ -588,35 +595,65 @@ __global__ __launch_bounds__(256 * CT) void k_backward_data_stage(const BsParams
         // the last kd), never used: they stay within d_h * NW floats past the
         // window buffer and one past the weight slice, which the allocation
         // pads.
-        int k = kd * KHW, kw = 0, toff = 0;
-        auto next = [&]() __attribute__((always_inline)) {
-            const bool row_end = kw == AW.K - 1;
-            toff += row_end ? AH.d * P.NW - (AW.K - 1) * AW.d : AW.d;
-            kw = row_end ? 0 : kw + 1;
-            ++k;
-        };
-        auto rd = [&](float &a, float (&bb)[PB]) __attribute__((always_inline)) {
-            a = wq[abase + k];
-#pragma unroll
-            for (int pb = 0; pb < PB; ++pb) bb[pb] = wb[bpos[pb] + toff];
-        };
         auto mma = [&](const float a, const float (&bb)[PB]) __attribute__((always_inline)) {
 #pragma unroll
             for (int pb = 0; pb < PB; ++pb)
                 acc[pb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb[pb], acc[pb], 0, 0, 0);
         };
-        float a0, b0[PB], a1, b1[PB];
-        rd(a0, b0);
-        int t = 0;
-        for (; t + 2 <= KHW; t += 2) {
-            next();
-            rd(a1, b1);
-            mma(a0, b0);
-            next();
+        if constexpr (FIX) {
+            // 9 taps unrolled (window offsets are constants past bpos[pb]),
+            // the operands of tap t + 1 read before tap t's products
+            float a[9], bb[2][PB];
+#pragma unroll
+            for (int t = 0; t < 9; ++t) a[t] = wq[abase + kd * 9 + t];
+#pragma unroll
+            for (int t = 0; t < 9; ++t) {
+                if (t == 0) {
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb) bb[0][pb] = wb[bpos[pb]];
+                }
+                if (t + 1 < 9) {
+                    const int kh = (t + 1) / 3, kw = (t + 1) - 3 * ((t + 1) / 3);
+#pragma unroll
+                    for (int pb = 0; pb < PB; ++pb) bb[(t + 1) & 1][pb] = wb[bpos[pb] + kh * NW + kw];
+                }
+                mma(a[t], bb[t & 1]);
+            }
+            // issue order: the A reads and tap 0's B reads, then per tap the
+            // two B reads of the next tap before its four products
+            __builtin_amdgcn_sched_group_barrier(0x100, 5 + 2, 0);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        } else {
+            int k = kd * KHW, kw = 0, toff = 0;
+            auto next = [&]() __attribute__((always_inline)) {
+                const bool row_end = kw == KW - 1;
+                toff += row_end ? DH * NW - (KW - 1) * DW : DW;
+                kw = row_end ? 0 : kw + 1;
+                ++k;
+            };
+            auto rd = [&](float &a, float (&bb)[PB]) __attribute__((always_inline)) {
+                a = wq[abase + k];
+#pragma unroll
+                for (int pb = 0; pb < PB; ++pb) bb[pb] = wb[bpos[pb] + toff];
+            };
+            float a0, b0[PB], a1, b1[PB];
             rd(a0, b0);
-            mma(a1, b1);
+            int t = 0;
+            for (; t + 2 <= KHW; t += 2) {
+                next();
+                rd(a1, b1);
+                mma(a0, b0);
+                next();
+                rd(a0, b0);
+                mma(a1, b1);
+            }
+            if (t < KHW) mma(a0, b0);
         }
-        if (t < KHW) mma(a0, b0);
         const bool quad_end = kd == AD.K - 1;
         if (quad_end) __syncthreads(); // every wave is done with this quad's weights
         // the next window into the other buffer (read last in sub-step ss - 1)
@@ -634,9 +671,9 @@ __global__ __launch_bounds__(256 * CT) void k_backward_data_stage(const BsParams
 #pragma unroll
     for (int pb = 0; pb < PB; ++pb) {
         const int blk = wq4 * PB + pb;
-        const int r = (blk * 16) / AW.L_in, col0 = (blk * 16) - r * AW.L_in;
+        const int r = (blk * 16) / WIN, col0 = (blk * 16) - r * WIN;
         if (ih0 + r >= AH.L_in) continue;
-        const int sp = (id * AH.L_in + ih0 + r) * AW.L_in + col0 + j16;
+        const int sp = (id * AH.L_in + ih0 + r) * WIN + col0 + j16;
 #pragma unroll
         for (int v = 0; v < 4; ++v)
             dx[((int64_t)n * P.C_in + ci0 + 16 * m + 4 * c4 + v) * P.in_sp + sp] = acc[pb][v];
@@ -672,6 +709,8 @@ int stage_ct(const convt_plan &Pl, BsParams &P) {
 
 template <int CT>
 int launch_stage(const convt_plan &Pl, BsParams &P, const float *dy, const float *w, float *dx, hipStream_t st) {
+    const AxisPlan &AH = Pl.ax[1], &AW = Pl.ax[2];
+    const bool fix = AW.L_in == 16 && AH.s == 2 && AW.s == 2 && AH.K == 3 && AW.K == 3 && AH.d == 1 && AW.d == 1;
     for (int a = 0; a < kAxes; ++a) P.ax[a] = Pl.ax[a];
     P.C_in = (int)Pl.C_in;
     P.C_out = (int)Pl.C_out;
@@ -686,7 +725,12 @@ int launch_stage(const convt_plan &Pl, BsParams &P, const float *dy, const float
     const int64_t blocks = Pl.N * Pl.G * (int64_t)P.ccs * Pl.ax[0].L_in * P.nhb;
     if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
     const size_t lds = 4 * stage_lds_floats(CT, P.ax[1].d, P.NW);
-    hipLaunchKernelGGL((k_backward_data_stage<CT>), dim3((unsigned)blocks), dim3(256 * CT), lds, st, P, dy, w, dx);
+    if (fix)
+        hipLaunchKernelGGL((k_backward_data_stage<CT, true>), dim3((unsigned)blocks), dim3(256 * CT), lds, st, P, dy, w,
+                           dx);
+    else
+        hipLaunchKernelGGL((k_backward_data_stage<CT, false>), dim3((unsigned)blocks), dim3(256 * CT), lds, st, P, dy, w,
+                           dx);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? 0 : (int)e;
 }
