@@ -125,8 +125,10 @@ KERNEL_SOURCES = {"k_stream1d": "stream1d.hip", "k_stream1d_nlc": "stream1d.hip"
                   "k_generic": "generic.hip", "k_generic_phase": "generic.hip", "k_generic_rows": "generic.hip",
                   "k_generic_pairs": "generic.hip", "k_generic_wpair": "wpair.hip", "k_backward_data": "backward.hip",
                   "k_backward_data_mfma": "backward.hip", "k_backward_data_mfma_row": "backward.hip",
-                  "k_backward_weight": "wgrad.hip",
-                  "k_backward_weight_lds": "wgrad.hip", "k_backward_weight_row": "wgrad.hip"}
+                  "k_backward_data_wpair": "backward.hip", "k_backward_data_stage": "backward.hip",
+                  "k_backward_weight": "wgrad.hip", "k_backward_weight_lds": "wgrad.hip",
+                  "k_backward_weight_row": "wgrad.hip", "k_backward_weight_shift": "wgrad.hip",
+                  "k_backward_weight_shift_rows": "wgrad.hip"}
 SHARED_SOURCES = ("convt_internal.h", "epilogue.hpp")
 
 

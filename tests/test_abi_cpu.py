@@ -287,3 +287,24 @@ def test_convt_log_names_kernel_and_fallback():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
                        env={k: v for k, v in os.environ.items() if k != "CONVT_LOG"})
     assert "convt:" not in r.stderr
+
+
+def test_every_kernel_name_has_a_source():
+    """Every kernel name the library reports (the string literals "k_..." in
+    its sources) maps to its source file in bench.py's table, which decides
+    whether a stored counter record still describes the kernel that runs."""
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    csrc = os.path.join(root, "transposed_convolution_forward_amd", "csrc")
+    names = set()
+    for f in os.listdir(csrc):
+        if f.endswith((".hip", ".cpp")):
+            names |= set(re.findall(r'"(k_[a-z0-9_]+)"', open(os.path.join(csrc, f)).read()))
+    assert names, "no kernel names found"
+    missing = sorted(n for n in names if n not in bench.KERNEL_SOURCES)
+    assert not missing, missing
+    for n, f in bench.KERNEL_SOURCES.items():
+        src = open(os.path.join(csrc, f)).read()
+        assert n in src, (n, f)
