@@ -171,7 +171,7 @@ def test_gradient_kernel_routing():
     want = {S.TINY_1D.name: ("k_backward_data", "k_backward_weight"),
             S.LONG_1D.name: ("k_backward_data_mfma_row", "k_backward_weight_row"),
             S.GROUPED_3D.name: ("k_backward_data_wpair", "k_backward_weight_shift_rows"),
-            S.FUSED_3D.name: ("k_backward_data_stage", "k_backward_weight_lds"),
+            S.FUSED_3D.name: ("k_backward_data_stage", "k_backward_weight_stage"),
             S.HEAVY_3D.name: ("k_backward_data_mfma", "k_backward_weight_lds")}
     for wl in S.WORKLOADS:
         assert _gradient_kernels(T.plan_for(wl)) == want[wl.name], wl.name
@@ -214,6 +214,11 @@ def test_gradient_kernel_routing():
         p = T.Plan(3, 2, cin, 64, 1, (16, 16, w_in), (3, 3, k_w), (2, 2, 2), (1, 1, 1), (1, 1, 1), (1, 1, 1))
         want = "k_backward_data_stage" if (cin, k_w, w_in) == (32, 3, 16) else "k_backward_data_mfma"
         assert _gradient_kernels(p)[0] == want, (cin, k_w, w_in)
+        # the staged weight kernel has the same conditions; otherwise 64 output
+        # channels take the LDS kernel when the input channels fill it
+        want = ("k_backward_weight_stage" if (cin, k_w, w_in) == (32, 3, 16)
+                else "k_backward_weight" if cin == 16 else "k_backward_weight_lds")
+        assert _gradient_kernels(p)[1] == want, (cin, k_w, w_in)
     # H stride 2: not the W-pair input-gradient kernel, and the weight gradient
     # without row sharing
     p = T.Plan(3, 1, 32, 32, 4, (4, 6, 16), (3, 5, 7), (2, 2, 2), (1, 2, 3), (1, 1, 1), (1, 1, 1))

@@ -69,6 +69,12 @@ def _check(wl, seed=0):
         rows = in_sp // wl.in_size[-1]
         spr = -(-(wl.in_size[-1] + 1) // 4)
         chain_w = max(chain_w, rows * (spr + wl.N) + 12 * (spr + 1))
+    if "weight gradient: kernel=k_backward_weight_stage" in T.convt_plan_describe(plan):
+        # one accumulator per workgroup over the sample's blocks of 128
+        # positions (32 K-steps each), then one atomic add per sample
+        lead = in_sp // (wl.in_size[-1] * wl.in_size[-2])
+        nhb = -(-wl.in_size[-2] // (128 // wl.in_size[-1]))
+        chain_w = max(chain_w, lead * nhb * 32 + wl.N + 12)
     chain_b = -(-min(out_sp, 16384) // 4096) + 4 + 8 + wl.N * -(-out_sp // 16384)
     for what, got, ref, s_abs, chain in (("dw", dw, ref_w, abs_w, chain_w), ("db", db, ref_b, abs_b, chain_b)):
         g = got.cpu().numpy().astype(np.float64)
@@ -170,6 +176,32 @@ SHIFT_ROWS = [
 @pytest.mark.parametrize("wl", SHIFT_ROWS, ids=lambda w: w.name)
 def test_wgrad_shift_rows(wl):
     assert "weight gradient: kernel=k_backward_weight_shift_rows" in T.convt_plan_describe(T.plan_for(wl))
+    _check(wl)
+    _check_exact(wl)
+
+
+# Shapes for the LDS-staged weight kernel (groups of 32k input and 4k output
+# channels, W_in of 16, 32 or 64, at most 32 taps): the fused layer's
+# geometry with H 20 (a partial last block of 4 rows); W 32 with two groups,
+# H dilation 2 and 16 taps (four waves without a tap group); 2D with W 64 and
+# W stride 3; one D tap with D stride 3, W dilation 3 and two channel
+# chunks; 32 taps (every wave has a group).
+WT_STAGE = [
+    S.Workload("wst_w16_h20", 3, 2, 32, 8, 1, (2, 20, 16), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 0, 1), (1, 1, 1),
+               True, False, 101),
+    S.Workload("wst_w32_g2_dh2", 3, 1, 64, 8, 2, (2, 5, 32), (2, 2, 4), (1, 2, 2), (0, 1, 2), (0, 1, 1),
+               (1, 2, 1), True, False, 102),
+    S.Workload("wst_2d_w64_s3", 2, 2, 32, 4, 1, (7, 64), (3, 2), (1, 3), (1, 0), (0, 2), (1, 1), False, False, 103),
+    S.Workload("wst_kd1_dw3", 3, 1, 64, 12, 1, (4, 9, 16), (1, 3, 2), (3, 1, 3), (0, 1, 2), (2, 0, 1), (1, 1, 3),
+               True, False, 104),
+    S.Workload("wst_taps32", 3, 1, 32, 8, 1, (3, 8, 16), (2, 4, 4), (1, 1, 1), (1, 2, 1), (0, 0, 0), (1, 1, 1),
+               True, False, 105),
+]
+
+
+@pytest.mark.parametrize("wl", WT_STAGE, ids=lambda w: w.name)
+def test_wgrad_stage(wl):
+    assert "weight gradient: kernel=k_backward_weight_stage" in T.convt_plan_describe(T.plan_for(wl))
     _check(wl)
     _check_exact(wl)
 

@@ -35,6 +35,10 @@ constexpr int kWgRsrcWord3 = 0x00020000; // raw (untyped) buffer access
 constexpr unsigned kWgOutOfRange = 0x80000000u;
 constexpr int kWgBlock = 256;  // four waves, each its own unit
 constexpr int kWgRange = 1024; // input positions per wave (256 steps of 4)
+// Tuning knob: the LDS-staged weight kernel where it applies.
+#ifndef CONVT_WT_STAGE
+#define CONVT_WT_STAGE 1
+#endif
 
 struct WgradParams {
     AxisPlan ax[kAxes];
@@ -790,6 +794,228 @@ bool weight_row_window(const convt_plan &Pl, WrParams &R) {
     return true;
 }
 
+// Groups of 32k input and 4k output channels with W_in of 16, 32 or 64 and at
+// most 32 taps (the fused 3D layer): both operands staged in LDS per block of
+// 128 input positions, as in the staged input gradient.  A workgroup owns the
+// tile dw[32 input channels][output-channel quad q][all taps] of one (sample,
+// group) and walks the sample's blocks (D position, R = 128 / W_in rows).
+// Per block it stages the x tile [ci][position] and, for each D tap, the dy
+// window of the quad: 4 channels x NR rows x NW columns of one dy plane (zero
+// outside the output).  With K = 4 positions of one row, the MFMA's 16
+// columns are (tap t = 4*tg + j/4, channel c = j%4): B (lane j + 16k) is the
+// window value of channel c at position k's tap-t output, A (lane i + 16k)
+// is x[ci0 + 16m + i] at position k.  Wave w owns tap group (w - workgroup)
+// mod 8 (so the waves without a group, when there are fewer than 8, move
+// over the SIMDs from workgroup to workgroup) for both input-channel tiles,
+// and adds its tiles into dw with atomics at the end.  The next block's
+// operands are loaded into registers during the current block's products.
+// Each thread's window elements keep their offset from the block's origin
+// with an index kd*NR + rr (63: never valid) into a per-block mask of the
+// (D tap, row) pairs inside the output.
+constexpr int kWtPos = 128;                       // positions per block
+constexpr int kWtNT = 512;                        // 8 waves
+constexpr int kWtXP = kWtPos + 4;                 // x tile pitch
+constexpr int kWtWinCap = 7168;                   // window floats, all D taps
+constexpr int kWtWU = kWtWinCap / kWtNT;          // window elements per thread
+constexpr int kWtXU = 32 * kWtPos / 4 / kWtNT;    // x float4s per thread
+
+struct WtParams {
+    AxisPlan ax[kAxes];
+    int C_in, C_out, Cig, Cog, kvol;
+    int in_sp, out_sp;
+    int R, nhb, ccs, NQ, NR, NW, TG;
+};
+
+template <bool FIX>
+__global__ __launch_bounds__(kWtNT) void k_backward_weight_stage(const WtParams P, const float *__restrict__ x,
+                                                                 const float *__restrict__ dy,
+                                                                 float *__restrict__ dw) {
+    const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
+    // FIX: the fused layer's geometry (W_in 16, 3 x 3 x 3 taps, H and W stride
+    // 2 and dilation 1) as constants
+    const int WIN = FIX ? 16 : AW.L_in;
+    const int SH = FIX ? 2 : AH.s, SW = FIX ? 2 : AW.s, DH = FIX ? 1 : AH.d, DW = FIX ? 1 : AW.d;
+    const int KD = FIX ? 3 : AD.K, KH = FIX ? 3 : AH.K, KW = FIX ? 3 : AW.K;
+    const int R = FIX ? 8 : P.R, NR = FIX ? 17 : P.NR, NW = FIX ? 33 : P.NW, TG = FIX ? 7 : P.TG;
+    const int win_sz = 4 * NR * NW, kvol = KD * KH * KW, wins = KD * win_sz;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int64_t b = blockIdx.x;
+    const int q = (int)(b % P.NQ);
+    b /= P.NQ;
+    const int cc = (int)(b % P.ccs);
+    b /= P.ccs;
+    const int G = P.C_in / P.Cig;
+    const int g = (int)(b % G);
+    const int n = (int)(b / G);
+    const int ci0 = g * P.Cig + cc * 32;
+    const int tg = (wave + 8 - (int)(blockIdx.x & 7)) & 7;
+    const int HWo = AH.L_out * AW.L_out;
+
+    extern __shared__ __attribute__((aligned(16))) float lds_wt[];
+    float *wl = lds_wt, *xl = lds_wt + kWtWinCap;
+
+    // window elements: offset (bits 0-25) from the block's origin and (D tap,
+    // row) index (bits 26-31)
+    unsigned winfo[kWtWU];
+#pragma unroll
+    for (int u = 0; u < kWtWU; ++u) {
+        const int e = tid + u * kWtNT;
+        const int kd = e / win_sz, r1 = e - kd * win_sz;
+        const int c = r1 / (NR * NW), r2 = r1 - c * (NR * NW);
+        const int rr = r2 / NW, col = r2 - rr * NW;
+        const int ow = col - AW.p;
+        const bool ok = e < wins && ow >= 0 && ow < AW.L_out;
+        const unsigned off = (unsigned)(c * P.out_sp + kd * AD.d * HWo + rr * AW.L_out + col);
+        winfo[u] = off | ((unsigned)(ok ? kd * NR + rr : 63) << 26);
+    }
+    // x float4s: channel ci, position 4*p4 of the block
+    unsigned xoff[kWtXU];
+    int xlo[kWtXU], xp[kWtXU];
+#pragma unroll
+    for (int u = 0; u < kWtXU; ++u) {
+        const int f = tid + u * kWtNT;
+        const int ci = f >> 5, p4 = f & 31;
+        xoff[u] = 4u * (unsigned)(ci * P.in_sp + 4 * p4);
+        xlo[u] = ci * kWtXP + 4 * p4;
+        xp[u] = 4 * p4;
+    }
+    const wg_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(dy + (int64_t)n * P.C_out * P.out_sp), (short)0, 4 * P.C_out * P.out_sp, kWgRsrcWord3);
+    const wg_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(x + (int64_t)n * P.C_in * P.in_sp), (short)0, 4 * P.C_in * P.in_sp, kWgRsrcWord3);
+    const int soff_q = 4 * (g * P.Cog + 4 * q) * P.out_sp;
+    const int nblk = AD.L_in * P.nhb;
+
+    float pf[kWtWU];
+    wg_v4f xpf[kWtXU];
+    // block blk = (id, hb) into registers; past the last block everything
+    // reads zero
+    auto fetch = [&](int blk) __attribute__((always_inline)) {
+        const int id = blk / P.nhb, hb = blk - id * P.nhb;
+        const int ih0 = hb * R;
+        const bool live = blk < nblk;
+        const int od0 = id * AD.s - AD.p, oh0 = ih0 * SH - AH.p;
+        const int base = od0 * HWo + oh0 * AW.L_out - AW.p;
+        // rows of the window inside the output: [lo, hi)
+        const int lo = max(0, -oh0), hi = min(NR, AH.L_out - oh0);
+        const uint64_t rows = hi > lo ? (((uint64_t)1 << hi) - 1) & ~(((uint64_t)1 << lo) - 1) : 0;
+        uint64_t mask = 0;
+        for (int kd = 0; kd < KD; ++kd) {
+            const int od = od0 + kd * AD.d;
+            if (live && od >= 0 && od < AD.L_out) mask |= rows << (kd * NR);
+        }
+#pragma unroll
+        for (int u = 0; u < kWtWU; ++u) {
+            const unsigned idx = winfo[u] >> 26;
+            const bool ok = ((mask >> idx) & 1u) != 0;
+            const unsigned vo = ok ? 4u * (unsigned)((int)(winfo[u] & 0x3ffffffu) + base) : kWgOutOfRange;
+            pf[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdy, vo, soff_q, 0));
+        }
+        const int vlen = live ? min(kWtPos, (AH.L_in - ih0) * WIN) : 0;
+        const int soff_x = live ? 4 * (ci0 * P.in_sp + (id * AH.L_in + ih0) * WIN) : 0;
+#pragma unroll
+        for (int u = 0; u < kWtXU; ++u) {
+            const unsigned vo = xp[u] < vlen ? xoff[u] : kWgOutOfRange;
+            xpf[u] = __builtin_bit_cast(wg_v4f, __builtin_amdgcn_raw_buffer_load_b128(rx, vo, soff_x, 0));
+        }
+    };
+
+    // this lane's B base: tap t of its column (the last tap for padding
+    // columns, which are not stored) and position k of the K-step
+    const int j16 = lane & 15, k4 = lane >> 4;
+    const int t_l = min(4 * tg + (j16 >> 2), kvol - 1);
+    const int kd_l = t_l / (KH * KW), kh_l = (t_l / KW) % KH, kw_l = t_l % KW;
+    const int bbase = kd_l * win_sz + (j16 & 3) * NR * NW + kh_l * DH * NW + kw_l * DW + k4 * SW;
+    const int abase = j16 * kWtXP + k4;
+    wg_v4f acc[2];
+    acc[0] = acc[1] = wg_v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    fetch(0);
+    for (int blk = 0; blk < nblk; ++blk) {
+        __syncthreads(); // every wave is done with the previous block
+#pragma unroll
+        for (int u = 0; u < kWtWU; ++u) wl[tid + u * kWtNT] = pf[u];
+#pragma unroll
+        for (int u = 0; u < kWtXU; ++u) *reinterpret_cast<wg_v4f *>(xl + xlo[u]) = xpf[u];
+        __syncthreads();
+        fetch(blk + 1);
+        if (tg < TG) {
+            // K-step s: positions 4s .. 4s+3 of row 4s / W_in
+            auto kstep = [&](int s) __attribute__((always_inline)) {
+                const int r = (4 * s) / WIN, col0 = 4 * s - r * WIN;
+                const float bv = wl[bbase + r * SH * NW + col0 * SW];
+                const float a0 = xl[abase + 4 * s], a1 = xl[abase + 16 * kWtXP + 4 * s];
+                acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bv, acc[0], 0, 0, 0);
+                acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bv, acc[1], 0, 0, 0);
+            };
+            if constexpr (FIX) {
+#pragma unroll
+                for (int s = 0; s < kWtPos / 4; ++s) kstep(s);
+            } else {
+                for (int s = 0; s < kWtPos / 4; ++s) kstep(s);
+            }
+        }
+    }
+
+    // lane j16 + 16*k4, register v: input channel 16m + 4*k4 + v, column j16
+    const int t_s = 4 * tg + (j16 >> 2);
+    if (tg < TG && t_s < kvol) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                atomicAdd(dw + ((int64_t)(ci0 + 16 * m + 4 * k4 + v) * P.Cog + 4 * q + (j16 & 3)) * kvol + t_s,
+                          acc[m][v]);
+    }
+}
+
+// The staged weight kernel applies: 2D or 3D plans with groups of 32k input
+// and 4k output channels, W_in of 16, 32 or 64, at most 32 taps, the D taps'
+// windows within kWtWinCap floats and their (D tap, row) pairs within 63 mask
+// bits, window offsets within 26 bits, per-sample x and dy below 2 GiB.
+bool weight_stage_applies(const convt_plan &Pl, WtParams &P) {
+    const AxisPlan &AD = Pl.ax[0], &AH = Pl.ax[1], &AW = Pl.ax[2];
+    if (Pl.ndim < 2 || Pl.Cig % 32 != 0 || Pl.Cog % 4 != 0 || Pl.k_vol > 32) return false;
+    if (AW.L_in != 16 && AW.L_in != 32 && AW.L_in != 64) return false;
+    if (4 * Pl.C_out * Pl.out_sp > 0x7fffffff || 4 * Pl.C_in * Pl.in_sp > 0x7fffffff) return false;
+    if (4 * Pl.out_sp + (int64_t)AD.K * AD.d * AH.L_out * AW.L_out >= ((int64_t)1 << 26)) return false;
+    P.R = kWtPos / AW.L_in;
+    P.NR = (P.R - 1) * AH.s + (AH.K - 1) * AH.d + 1;
+    P.NW = (AW.L_in - 1) * AW.s + (AW.K - 1) * AW.d + 1;
+    if (AD.K * P.NR > 63 || AD.K * 4 * P.NR * P.NW > kWtWinCap) return false;
+    return true;
+}
+
+int launch_weight_stage(const convt_plan &Pl, const float *x, const float *dy, float *dw, hipStream_t st) {
+    WtParams P;
+    if (!weight_stage_applies(Pl, P)) return (int)hipErrorInvalidValue;
+    for (int a = 0; a < kAxes; ++a) P.ax[a] = Pl.ax[a];
+    P.C_in = (int)Pl.C_in;
+    P.C_out = (int)Pl.C_out;
+    P.Cig = (int)Pl.Cig;
+    P.Cog = (int)Pl.Cog;
+    P.kvol = (int)Pl.k_vol;
+    P.in_sp = (int)Pl.in_sp;
+    P.out_sp = (int)Pl.out_sp;
+    P.nhb = (Pl.ax[1].L_in + P.R - 1) / P.R;
+    P.ccs = (int)(Pl.Cig / 32);
+    P.NQ = (int)(Pl.Cog / 4);
+    P.TG = (int)((Pl.k_vol + 3) / 4);
+    const int64_t blocks = Pl.N * Pl.G * (int64_t)P.ccs * P.NQ;
+    if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
+    const AxisPlan &AD = Pl.ax[0], &AH = Pl.ax[1], &AW = Pl.ax[2];
+    const bool fix = AW.L_in == 16 && AD.K == 3 && AH.K == 3 && AW.K == 3 && AH.s == 2 && AW.s == 2 && AH.d == 1 &&
+                     AW.d == 1;
+    const size_t lds = sizeof(float) * (kWtWinCap + 32 * kWtXP);
+    if (fix)
+        hipLaunchKernelGGL(k_backward_weight_stage<true>, dim3((unsigned)blocks), dim3(kWtNT), lds, st, P, x, dy, dw);
+    else
+        hipLaunchKernelGGL(k_backward_weight_stage<false>, dim3((unsigned)blocks), dim3(kWtNT), lds, st, P, x, dy, dw);
+    const hipError_t e = hipGetLastError();
+    return e == hipSuccess ? 0 : (int)e;
+}
+
 // db[co] += the sum of dy[n, co, e] over one chunk of kBiasChunk positions e
 // per workgroup, grid (co, chunk, n).  Each thread keeps kBiasDepth partial
 // sums, so that many loads are in flight; a pairwise tree, a wave tree and an
@@ -851,6 +1077,8 @@ int launch_w(const convt_plan &Pl, WgradParams &P, const float *x, const float *
 const char *backward_weight_kernel_name(const convt_plan &P) {
     WrParams R;
     if (weight_row_window(P, R)) return "k_backward_weight_row";
+    WtParams T;
+    if (CONVT_WT_STAGE && weight_stage_applies(P, T)) return "k_backward_weight_stage";
     if (weight_shift_rows_applies(P)) return "k_backward_weight_shift_rows";
     if (weight_shift_applies(P)) return "k_backward_weight_shift";
     return P.Cig % 32 == 0 && P.Cog % 64 == 0 ? "k_backward_weight_lds" : "k_backward_weight";
@@ -887,7 +1115,11 @@ int launch_backward_weight(const convt_plan &Pl, const float *x, const float *dy
     P.OT = (int)((Pl.Cog + 15) / 16);
     P.nranges = (int)((Pl.in_sp + kWgRange - 1) / kWgRange);
     int rc;
-    if (Pl.Cig % 32 == 0 && Pl.Cog % 64 == 0) {
+    WtParams T;
+    WrParams R0;
+    if (CONVT_WT_STAGE && !weight_row_window(Pl, R0) && weight_stage_applies(Pl, T)) {
+        rc = launch_weight_stage(Pl, x, dy, dw, st);
+    } else if (Pl.Cig % 32 == 0 && Pl.Cog % 64 == 0) {
         WlParams L;
         for (int a = 0; a < kAxes; ++a) L.ax[a] = Pl.ax[a];
         L.C_in = P.C_in, L.C_out = P.C_out, L.Cig = P.Cig, L.Cog = P.Cog, L.k_vol = P.k_vol;
