@@ -128,7 +128,8 @@ KERNEL_SOURCES = {"k_stream1d": "stream1d.hip", "k_stream1d_nlc": "stream1d.hip"
                   "k_backward_data_wpair": "backward.hip", "k_backward_data_stage": "backward.hip",
                   "k_backward_weight": "wgrad.hip", "k_backward_weight_lds": "wgrad.hip",
                   "k_backward_weight_row": "wgrad.hip", "k_backward_weight_shift": "wgrad.hip",
-                  "k_backward_weight_shift_rows": "wgrad.hip", "k_backward_weight_stage": "wgrad.hip"}
+                  "k_backward_weight_shift_rows": "wgrad.hip", "k_backward_weight_stage": "wgrad.hip",
+                  "k_backward_bias": "wgrad.hip"}
 SHARED_SOURCES = ("convt_internal.h", "epilogue.hpp")
 
 

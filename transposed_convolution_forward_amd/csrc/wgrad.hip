@@ -826,8 +826,13 @@ struct WtParams {
     int R, nhb, ccs, NQ, NR, NW, TG;
 };
 
+// Tuning knob: waves per SIMD the fused-geometry instance must allow (6: three
+// workgroups per CU, 80 registers).
+#ifndef CONVT_WT_WAVES
+#define CONVT_WT_WAVES 6
+#endif
 template <bool FIX>
-__global__ __launch_bounds__(kWtNT) void k_backward_weight_stage(const WtParams P, const float *__restrict__ x,
+__global__ __launch_bounds__(kWtNT) __attribute__((amdgpu_waves_per_eu(FIX ? CONVT_WT_WAVES : 1))) void k_backward_weight_stage(const WtParams P, const float *__restrict__ x,
                                                                  const float *__restrict__ dy,
                                                                  float *__restrict__ dw) {
     const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
@@ -907,7 +912,10 @@ __global__ __launch_bounds__(kWtNT) void k_backward_weight_stage(const WtParams 
         }
 #pragma unroll
         for (int u = 0; u < kWtWU; ++u) {
-            const unsigned idx = winfo[u] >> 26;
+            // the shift stays in the loop (a 64-bit 1 << idx per element
+            // hoisted out of it would hold two registers each)
+            unsigned idx = winfo[u] >> 26;
+            asm volatile("" : "+v"(idx));
             const bool ok = ((mask >> idx) & 1u) != 0;
             const unsigned vo = ok ? 4u * (unsigned)((int)(winfo[u] & 0x3ffffffu) + base) : kWgOutOfRange;
             pf[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rdy, vo, soff_q, 0));
@@ -952,6 +960,15 @@ __global__ __launch_bounds__(kWtNT) void k_backward_weight_stage(const WtParams 
             if constexpr (FIX) {
 #pragma unroll
                 for (int s = 0; s < kWtPos / 4; ++s) kstep(s);
+                // issue order: the reads of K-steps 0-3, then per pair of
+                // K-steps its four products and the reads two pairs ahead
+                __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+                for (int i = 0; i < kWtPos / 8 - 2; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
             } else {
                 for (int s = 0; s < kWtPos / 4; ++s) kstep(s);
             }
