@@ -172,7 +172,7 @@ def test_gradient_kernel_routing():
             S.LONG_1D.name: ("k_backward_data_mfma_row", "k_backward_weight_row"),
             S.GROUPED_3D.name: ("k_backward_data_wpair", "k_backward_weight_shift_rows"),
             S.FUSED_3D.name: ("k_backward_data_stage", "k_backward_weight_stage"),
-            S.HEAVY_3D.name: ("k_backward_data_mfma", "k_backward_weight_lds")}
+            S.HEAVY_3D.name: ("k_backward_data_mfma", "k_backward_weight_stage")}
     for wl in S.WORKLOADS:
         assert _gradient_kernels(T.plan_for(wl)) == want[wl.name], wl.name
     # one axis, s = 3 and d = 2: the input gradient's full window (765 + 5
@@ -214,8 +214,9 @@ def test_gradient_kernel_routing():
         p = T.Plan(3, 2, cin, 64, 1, (16, 16, w_in), (3, 3, k_w), (2, 2, 2), (1, 1, 1), (1, 1, 1), (1, 1, 1))
         want = "k_backward_data_stage" if (cin, k_w, w_in) == (32, 3, 16) else "k_backward_data_mfma"
         assert _gradient_kernels(p)[0] == want, (cin, k_w, w_in)
-        # the staged weight kernel has the same conditions; otherwise 64 output
-        # channels take the LDS kernel when the input channels fill it
+        # the staged weight kernel has the same conditions but up to 64 taps
+        # (the 72 here take the LDS kernel); otherwise 64 output channels take
+        # the LDS kernel when the input channels fill it
         want = ("k_backward_weight_stage" if (cin, k_w, w_in) == (32, 3, 16)
                 else "k_backward_weight" if cin == 16 else "k_backward_weight_lds")
         assert _gradient_kernels(p)[1] == want, (cin, k_w, w_in)

@@ -196,6 +196,13 @@ WT_STAGE = [
                True, False, 104),
     S.Workload("wst_taps32", 3, 1, 32, 8, 1, (3, 8, 16), (2, 4, 4), (1, 1, 1), (1, 2, 1), (0, 0, 0), (1, 1, 1),
                True, False, 105),
+    # two tap groups per wave: 48 taps (waves 4-7 have no second group) with
+    # W 32; the channel-heavy layer's geometry (64 taps, W 32, stride 2) with a
+    # partial last block of 2 rows, two channel chunks and 8 output channels
+    S.Workload("wst_taps48", 3, 1, 32, 8, 1, (3, 6, 32), (3, 4, 4), (2, 1, 2), (1, 1, 1), (1, 0, 1), (1, 1, 1),
+               True, False, 106),
+    S.Workload("wst_heavy_geo", 3, 1, 64, 8, 1, (3, 6, 32), (4, 4, 4), (2, 2, 2), (1, 1, 1), (0, 0, 0), (1, 1, 1),
+               True, False, 107),
 ]
 
 

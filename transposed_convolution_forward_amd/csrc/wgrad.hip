@@ -815,8 +815,8 @@ bool weight_row_window(const convt_plan &Pl, WrParams &R) {
 constexpr int kWtPos = 128;                       // positions per block
 constexpr int kWtNT = 512;                        // 8 waves
 constexpr int kWtXP = kWtPos + 4;                 // x tile pitch
-constexpr int kWtWinCap = 7168;                   // window floats, all D taps
-constexpr int kWtWU = kWtWinCap / kWtNT;          // window elements per thread
+constexpr int kWtWinCap = 7168;                   // window floats, all D taps (one tap group per wave)
+constexpr int kWtWinCap2 = 10752;                 // the same with two tap groups per wave (33 to 64 taps)
 constexpr int kWtXU = 32 * kWtPos / 4 / kWtNT;    // x float4s per thread
 
 struct WtParams {
@@ -831,17 +831,26 @@ struct WtParams {
 #ifndef CONVT_WT_WAVES
 #define CONVT_WT_WAVES 6
 #endif
-template <bool FIX>
-__global__ __launch_bounds__(kWtNT) __attribute__((amdgpu_waves_per_eu(FIX ? CONVT_WT_WAVES : 1))) void k_backward_weight_stage(const WtParams P, const float *__restrict__ x,
+template <int TGW, int GEO>
+__global__ __launch_bounds__(kWtNT) __attribute__((amdgpu_waves_per_eu(GEO == 1 ? CONVT_WT_WAVES : 1)))
+void k_backward_weight_stage(const WtParams P, const float *__restrict__ x,
                                                                  const float *__restrict__ dy,
                                                                  float *__restrict__ dw) {
     const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
-    // FIX: the fused layer's geometry (W_in 16, 3 x 3 x 3 taps, H and W stride
-    // 2 and dilation 1) as constants
-    const int WIN = FIX ? 16 : AW.L_in;
+    // GEO 1: the fused layer's geometry (W_in 16, 3 x 3 x 3 taps, H and W
+    // stride 2 and dilation 1), GEO 2: the channel-heavy layer's (W_in 32,
+    // 4 x 4 x 4 taps, the same strides), as constants; GEO 0: the plan's
+    constexpr bool FIX = GEO != 0;
+    constexpr int FW = GEO == 2 ? 32 : 16, FK = GEO == 2 ? 4 : 3, FR = 128 / FW;
+    constexpr int FNR = (FR - 1) * 2 + FK, FNW = (FW - 1) * 2 + FK;
+    const int WIN = FIX ? FW : AW.L_in;
     const int SH = FIX ? 2 : AH.s, SW = FIX ? 2 : AW.s, DH = FIX ? 1 : AH.d, DW = FIX ? 1 : AW.d;
-    const int KD = FIX ? 3 : AD.K, KH = FIX ? 3 : AH.K, KW = FIX ? 3 : AW.K;
-    const int R = FIX ? 8 : P.R, NR = FIX ? 17 : P.NR, NW = FIX ? 33 : P.NW, TG = FIX ? 7 : P.TG;
+    const int KD = FIX ? FK : AD.K, KH = FIX ? FK : AH.K, KW = FIX ? FK : AW.K;
+    const int R = FIX ? FR : P.R, NR = FIX ? FNR : P.NR, NW = FIX ? FNW : P.NW;
+    const int TG = FIX ? (FK * FK * FK + 3) / 4 : P.TG;
+    static_assert(!FIX || TGW == (FK * FK * FK > 32 ? 2 : 1), "tap groups per wave of the fixed geometry");
+    constexpr int CAP = TGW == 2 ? kWtWinCap2 : kWtWinCap, WU = CAP / kWtNT;
+    static_assert(WU * kWtNT == CAP, "window buffer split evenly over the threads");
     const int win_sz = 4 * NR * NW, kvol = KD * KH * KW, wins = KD * win_sz;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -854,17 +863,18 @@ __global__ __launch_bounds__(kWtNT) __attribute__((amdgpu_waves_per_eu(FIX ? CON
     const int g = (int)(b % G);
     const int n = (int)(b / G);
     const int ci0 = g * P.Cig + cc * 32;
+    // tap groups tg and tg + 8 (TGW = 2)
     const int tg = (wave + 8 - (int)(blockIdx.x & 7)) & 7;
     const int HWo = AH.L_out * AW.L_out;
 
     extern __shared__ __attribute__((aligned(16))) float lds_wt[];
-    float *wl = lds_wt, *xl = lds_wt + kWtWinCap;
+    float *wl = lds_wt, *xl = lds_wt + CAP;
 
     // window elements: offset (bits 0-25) from the block's origin and (D tap,
     // row) index (bits 26-31)
-    unsigned winfo[kWtWU];
+    unsigned winfo[WU];
 #pragma unroll
-    for (int u = 0; u < kWtWU; ++u) {
+    for (int u = 0; u < WU; ++u) {
         const int e = tid + u * kWtNT;
         const int kd = e / win_sz, r1 = e - kd * win_sz;
         const int c = r1 / (NR * NW), r2 = r1 - c * (NR * NW);
@@ -892,7 +902,7 @@ __global__ __launch_bounds__(kWtNT) __attribute__((amdgpu_waves_per_eu(FIX ? CON
     const int soff_q = 4 * (g * P.Cog + 4 * q) * P.out_sp;
     const int nblk = AD.L_in * P.nhb;
 
-    float pf[kWtWU];
+    float pf[WU];
     wg_v4f xpf[kWtXU];
     // block blk = (id, hb) into registers; past the last block everything
     // reads zero
@@ -911,7 +921,7 @@ __global__ __launch_bounds__(kWtNT) __attribute__((amdgpu_waves_per_eu(FIX ? CON
             if (live && od >= 0 && od < AD.L_out) mask |= rows << (kd * NR);
         }
 #pragma unroll
-        for (int u = 0; u < kWtWU; ++u) {
+        for (int u = 0; u < WU; ++u) {
             // the shift stays in the loop (a 64-bit 1 << idx per element
             // hoisted out of it would hold two registers each)
             unsigned idx = winfo[u] >> 26;
@@ -932,18 +942,23 @@ __global__ __launch_bounds__(kWtNT) __attribute__((amdgpu_waves_per_eu(FIX ? CON
     // this lane's B base: tap t of its column (the last tap for padding
     // columns, which are not stored) and position k of the K-step
     const int j16 = lane & 15, k4 = lane >> 4;
-    const int t_l = min(4 * tg + (j16 >> 2), kvol - 1);
-    const int kd_l = t_l / (KH * KW), kh_l = (t_l / KW) % KH, kw_l = t_l % KW;
-    const int bbase = kd_l * win_sz + (j16 & 3) * NR * NW + kh_l * DH * NW + kw_l * DW + k4 * SW;
+    int bbase[TGW];
+#pragma unroll
+    for (int h = 0; h < TGW; ++h) {
+        const int t_l = min(4 * (tg + 8 * h) + (j16 >> 2), kvol - 1);
+        const int kd_l = t_l / (KH * KW), kh_l = (t_l / KW) % KH, kw_l = t_l % KW;
+        bbase[h] = kd_l * win_sz + (j16 & 3) * NR * NW + kh_l * DH * NW + kw_l * DW + k4 * SW;
+    }
     const int abase = j16 * kWtXP + k4;
-    wg_v4f acc[2];
-    acc[0] = acc[1] = wg_v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    wg_v4f acc[TGW][2];
+#pragma unroll
+    for (int h = 0; h < TGW; ++h) acc[h][0] = acc[h][1] = wg_v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     fetch(0);
     for (int blk = 0; blk < nblk; ++blk) {
         __syncthreads(); // every wave is done with the previous block
 #pragma unroll
-        for (int u = 0; u < kWtWU; ++u) wl[tid + u * kWtNT] = pf[u];
+        for (int u = 0; u < WU; ++u) wl[tid + u * kWtNT] = pf[u];
 #pragma unroll
         for (int u = 0; u < kWtXU; ++u) *reinterpret_cast<wg_v4f *>(xl + xlo[u]) = xpf[u];
         __syncthreads();
@@ -952,12 +967,20 @@ __global__ __launch_bounds__(kWtNT) __attribute__((amdgpu_waves_per_eu(FIX ? CON
             // K-step s: positions 4s .. 4s+3 of row 4s / W_in
             auto kstep = [&](int s) __attribute__((always_inline)) {
                 const int r = (4 * s) / WIN, col0 = 4 * s - r * WIN;
-                const float bv = wl[bbase + r * SH * NW + col0 * SW];
+                float bv[TGW];
+#pragma unroll
+                for (int h = 0; h < TGW; ++h) bv[h] = wl[bbase[h] + r * SH * NW + col0 * SW];
                 const float a0 = xl[abase + 4 * s], a1 = xl[abase + 16 * kWtXP + 4 * s];
-                acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bv, acc[0], 0, 0, 0);
-                acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bv, acc[1], 0, 0, 0);
+#pragma unroll
+                for (int h = 0; h < TGW; ++h) {
+                    acc[h][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0, bv[h], acc[h][0], 0, 0, 0);
+                    acc[h][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1, bv[h], acc[h][1], 0, 0, 0);
+                }
             };
-            if constexpr (FIX) {
+            if constexpr (GEO == 2) {
+#pragma unroll
+                for (int s = 0; s < kWtPos / 4; ++s) kstep(s);
+            } else if constexpr (GEO == 1) {
 #pragma unroll
                 for (int s = 0; s < kWtPos / 4; ++s) kstep(s);
                 // issue order: the reads of K-steps 0-3, then per pair of
@@ -976,31 +999,36 @@ __global__ __launch_bounds__(kWtNT) __attribute__((amdgpu_waves_per_eu(FIX ? CON
     }
 
     // lane j16 + 16*k4, register v: input channel 16m + 4*k4 + v, column j16
-    const int t_s = 4 * tg + (j16 >> 2);
-    if (tg < TG && t_s < kvol) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+    for (int h = 0; h < TGW; ++h) {
+        const int t_s = 4 * (tg + 8 * h) + (j16 >> 2);
+        if (tg < TG && t_s < kvol) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                atomicAdd(dw + ((int64_t)(ci0 + 16 * m + 4 * k4 + v) * P.Cog + 4 * q + (j16 & 3)) * kvol + t_s,
-                          acc[m][v]);
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    atomicAdd(dw + ((int64_t)(ci0 + 16 * m + 4 * k4 + v) * P.Cog + 4 * q + (j16 & 3)) * kvol + t_s,
+                              acc[h][m][v]);
+        }
     }
 }
 
 // The staged weight kernel applies: 2D or 3D plans with groups of 32k input
-// and 4k output channels, W_in of 16, 32 or 64, at most 32 taps, the D taps'
-// windows within kWtWinCap floats and their (D tap, row) pairs within 63 mask
-// bits, window offsets within 26 bits, per-sample x and dy below 2 GiB.
+// and 4k output channels, W_in of 16, 32 or 64, at most 64 taps (one tap group
+// per wave up to 32, two above), the D taps' windows within kWtWinCap floats
+// (kWtWinCap2 with two groups per wave) and their (D tap, row) pairs within 63
+// mask bits, window offsets within 26 bits, per-sample x and dy below 2 GiB.
 bool weight_stage_applies(const convt_plan &Pl, WtParams &P) {
     const AxisPlan &AD = Pl.ax[0], &AH = Pl.ax[1], &AW = Pl.ax[2];
-    if (Pl.ndim < 2 || Pl.Cig % 32 != 0 || Pl.Cog % 4 != 0 || Pl.k_vol > 32) return false;
+    if (Pl.ndim < 2 || Pl.Cig % 32 != 0 || Pl.Cog % 4 != 0 || Pl.k_vol > 64) return false;
     if (AW.L_in != 16 && AW.L_in != 32 && AW.L_in != 64) return false;
     if (4 * Pl.C_out * Pl.out_sp > 0x7fffffff || 4 * Pl.C_in * Pl.in_sp > 0x7fffffff) return false;
     if (4 * Pl.out_sp + (int64_t)AD.K * AD.d * AH.L_out * AW.L_out >= ((int64_t)1 << 26)) return false;
     P.R = kWtPos / AW.L_in;
     P.NR = (P.R - 1) * AH.s + (AH.K - 1) * AH.d + 1;
     P.NW = (AW.L_in - 1) * AW.s + (AW.K - 1) * AW.d + 1;
-    if (AD.K * P.NR > 63 || AD.K * 4 * P.NR * P.NW > kWtWinCap) return false;
+    const int cap = Pl.k_vol > 32 ? kWtWinCap2 : kWtWinCap;
+    if (AD.K * P.NR > 63 || AD.K * 4 * P.NR * P.NW > cap) return false;
     return true;
 }
 
@@ -1024,11 +1052,18 @@ int launch_weight_stage(const convt_plan &Pl, const float *x, const float *dy, f
     const AxisPlan &AD = Pl.ax[0], &AH = Pl.ax[1], &AW = Pl.ax[2];
     const bool fix = AW.L_in == 16 && AD.K == 3 && AH.K == 3 && AW.K == 3 && AH.s == 2 && AW.s == 2 && AH.d == 1 &&
                      AW.d == 1;
-    const size_t lds = sizeof(float) * (kWtWinCap + 32 * kWtXP);
+    const bool fix2 = AW.L_in == 32 && AD.K == 4 && AH.K == 4 && AW.K == 4 && AH.s == 2 && AW.s == 2 && AH.d == 1 &&
+                      AW.d == 1;
+    const bool two = P.TG > 8;
+    const size_t lds = sizeof(float) * ((two ? kWtWinCap2 : kWtWinCap) + 32 * kWtXP);
     if (fix)
-        hipLaunchKernelGGL(k_backward_weight_stage<true>, dim3((unsigned)blocks), dim3(kWtNT), lds, st, P, x, dy, dw);
+        hipLaunchKernelGGL((k_backward_weight_stage<1, 1>), dim3((unsigned)blocks), dim3(kWtNT), lds, st, P, x, dy, dw);
+    else if (fix2)
+        hipLaunchKernelGGL((k_backward_weight_stage<2, 2>), dim3((unsigned)blocks), dim3(kWtNT), lds, st, P, x, dy, dw);
+    else if (two)
+        hipLaunchKernelGGL((k_backward_weight_stage<2, 0>), dim3((unsigned)blocks), dim3(kWtNT), lds, st, P, x, dy, dw);
     else
-        hipLaunchKernelGGL(k_backward_weight_stage<false>, dim3((unsigned)blocks), dim3(kWtNT), lds, st, P, x, dy, dw);
+        hipLaunchKernelGGL((k_backward_weight_stage<1, 0>), dim3((unsigned)blocks), dim3(kWtNT), lds, st, P, x, dy, dw);
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? 0 : (int)e;
 }
