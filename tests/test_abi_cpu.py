@@ -172,7 +172,7 @@ def test_gradient_kernel_routing():
             S.LONG_1D.name: ("k_backward_data_mfma_row", "k_backward_weight_row"),
             S.GROUPED_3D.name: ("k_backward_data_wpair", "k_backward_weight_shift_rows"),
             S.FUSED_3D.name: ("k_backward_data_stage", "k_backward_weight_stage"),
-            S.HEAVY_3D.name: ("k_backward_data_mfma", "k_backward_weight_stage")}
+            S.HEAVY_3D.name: ("k_backward_data_stage", "k_backward_weight_stage")}
     for wl in S.WORKLOADS:
         assert _gradient_kernels(T.plan_for(wl)) == want[wl.name], wl.name
     # one axis, s = 3 and d = 2: the input gradient's full window (765 + 5
@@ -208,8 +208,8 @@ def test_gradient_kernel_routing():
         want = "k_backward_data_wpair" if (s_w, d_w, cout) == (2, 1, 32) else "k_backward_data"
         assert _gradient_kernels(p)[0] == want, (s_w, d_w, cout)
     # the LDS-staged input gradient: 32 input channels per group and at most
-    # 32 taps; 16 channels per group, 64 taps (the heavy layer) or W 48 take
-    # the matrix kernel
+    # 64 taps (16 per D tap above 32); 16 channels per group, 72 taps or W 48
+    # take the matrix kernel
     for cin, k_w, w_in in ((32, 3, 16), (16, 3, 16), (32, 8, 16), (32, 3, 48)):
         p = T.Plan(3, 2, cin, 64, 1, (16, 16, w_in), (3, 3, k_w), (2, 2, 2), (1, 1, 1), (1, 1, 1), (1, 1, 1))
         want = "k_backward_data_stage" if (cin, k_w, w_in) == (32, 3, 16) else "k_backward_data_mfma"

@@ -121,7 +121,7 @@ def test_backward_wpair(wl):
 
 
 # Shapes for the LDS-staged matrix kernel (groups of 32k input and 4k output
-# channels, W_in of 16, 32 or 64, at most 32 taps): a second row block that
+# channels, W_in of 16, 32 or 64, at most 64 taps): a second row block that
 # is partial (H 20 with 16 rows per workgroup) and 27 taps; W 32 with two
 # groups, H dilation 2 and an even tap count (16: the last tap's operand
 # reads run one tap past the end); 2D with W 64, W stride 3 and one channel
@@ -135,6 +135,13 @@ BWD_STAGE = [
     S.Workload("bst_2d_w64_s3", 2, 2, 32, 4, 1, (7, 64), (3, 2), (1, 3), (1, 0), (0, 2), (1, 1), False, False, 87),
     S.Workload("bst_kd1_dw3", 3, 1, 64, 12, 1, (4, 5, 16), (1, 3, 2), (3, 1, 3), (0, 1, 2), (2, 0, 1), (1, 1, 3),
                False, False, 88),
+    # more than 32 taps: the weights staged per (quad, D tap).  The channel-heavy
+    # layer's geometry (W 32, 4 x 4 x 4 taps, stride 2) with a partial second
+    # row block and two channel chunks; 48 taps with 16 per D tap on W 16.
+    S.Workload("bst_heavy_geo", 3, 1, 64, 8, 1, (3, 10, 32), (4, 4, 4), (2, 2, 2), (1, 1, 1), (0, 0, 0), (1, 1, 1),
+               False, False, 89),
+    S.Workload("bst_taps48", 3, 1, 32, 8, 1, (3, 9, 16), (3, 4, 4), (2, 1, 2), (1, 2, 1), (1, 0, 1), (1, 1, 1),
+               False, False, 120),
 ]
 
 

@@ -459,9 +459,13 @@ __global__ __launch_bounds__(kBwdBlock, row_waves_per_simd<MT>()) void k_backwar
 // window: the load reads zero); a sub-step adds the plane's offset as the
 // scalar offset, or takes a resource of zero size where its D position lies
 // outside the output.  The weights go the same way, 8 per thread (at most 32
-// taps).
-constexpr int kBsWinCap = 4608; // floats per window buffer
-constexpr int kBsWU = 8;        // weight-slice elements per thread
+// taps).  Above 32 taps (WSUB) the weights are staged per sub-step instead,
+// w[ci][4q .. 4q+3][kd's K_h x K_w taps] (at most 16), double buffered with
+// the window, and the window buffer holds 5120 floats.
+constexpr int kBsWinCap = 4608;  // floats per window buffer
+constexpr int kBsWinCap2 = 5120; // the same with weights per sub-step
+constexpr int kBsWU = 8;         // weight-slice elements per thread
+constexpr int kBsWsub = 2048;    // weight floats per sub-step buffer: 32 x 4 x 16 taps
 
 struct BsParams {
     AxisPlan ax[kAxes];
@@ -472,20 +476,27 @@ struct BsParams {
     int win_sz;            // window floats: 4 * NR * NW <= kBsWinCap
 };
 
-template <int CT, bool FIX>
+template <int CT, int GEO, bool WSUB>
 __global__ __launch_bounds__(256 * CT) __attribute__((amdgpu_waves_per_eu(1, 6))) void k_backward_data_stage(const BsParams P, const float *__restrict__ dy,
                                                                    const float *__restrict__ w,
                                                                    float *__restrict__ dx) {
-    constexpr int NT = 256 * CT, U = kBsWinCap / NT, PB = 4;
-    static_assert(U * NT == kBsWinCap, "window buffer split evenly over the threads");
+    constexpr int CAP = WSUB ? kBsWinCap2 : kBsWinCap;
+    constexpr int NT = 256 * CT, U = CAP / NT, PB = 4, WSU = kBsWsub / NT;
+    static_assert(U * NT == CAP && WSU * NT == kBsWsub, "buffers split evenly over the threads");
     const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
-    // H and W geometry; FIX: W_in 16, stride 2, 3 taps and dilation 1 on both
-    // (the fused layer's), as constants, so that every window offset of a tap
-    // is an immediate
-    const int WIN = FIX ? 16 : AW.L_in;
-    const int SH = FIX ? 2 : AH.s, SW = FIX ? 2 : AW.s, KH = FIX ? 3 : AH.K, KW = FIX ? 3 : AW.K;
+    // H and W geometry as constants, so that every window offset of a tap is
+    // an immediate: GEO 1, W_in 16, stride 2, 3 taps and dilation 1 on both
+    // (the fused layer's); GEO 2, W_in 32, stride 2, 4 taps and dilation 1
+    // (the channel-heavy layer's); GEO 0, the plan's
+    constexpr bool FIX = GEO != 0;
+    constexpr int FW = GEO == 2 ? 32 : 16, FK = GEO == 2 ? 4 : 3;
+    constexpr int FNR = (256 / FW - 1) * 2 + FK, FNW = (FW - 1) * 2 + FK;
+    static_assert(GEO != 1 || !WSUB, "the fused geometry stages weights per quad");
+    static_assert(GEO != 2 || WSUB, "the channel-heavy geometry stages weights per sub-step");
+    const int WIN = FIX ? FW : AW.L_in;
+    const int SH = FIX ? 2 : AH.s, SW = FIX ? 2 : AW.s, KH = FIX ? FK : AH.K, KW = FIX ? FK : AW.K;
     const int DH = FIX ? 1 : AH.d, DW = FIX ? 1 : AW.d;
-    const int NR = FIX ? 33 : P.NR, NW = FIX ? 33 : P.NW;
+    const int NR = FIX ? FNR : P.NR, NW = FIX ? FNW : P.NW;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m = wave >> 2, wq4 = wave & 3;
@@ -503,10 +514,9 @@ __global__ __launch_bounds__(256 * CT) __attribute__((amdgpu_waves_per_eu(1, 6))
     const int ci0 = g * P.Cig + cc * 16 * CT;
     const int od0 = id * AD.s - AD.p, oh0 = ih0 * SH - AH.p, ow0 = -AW.p;
     const int KHW = KH * KW, nsub = P.NQ * AD.K;
-    const int wq_sz = 16 * CT * 4 * P.kvol;
 
     extern __shared__ __attribute__((aligned(16))) float lds_bs[];
-    float *win0 = lds_bs, *win1 = lds_bs + kBsWinCap, *wq = lds_bs + 2 * kBsWinCap;
+    float *win0 = lds_bs, *win1 = lds_bs + CAP, *wq = lds_bs + 2 * CAP, *wq1 = wq + kBsWsub;
 
     // window element e = tid + NT*u: channel c, row rr, column col; its byte
     // offset from the plane quad's start, or out of range
@@ -540,27 +550,37 @@ __global__ __launch_bounds__(256 * CT) __attribute__((amdgpu_waves_per_eu(1, 6))
         for (int u = 0; u < U; ++u) wb[tid + u * NT] = pf[u];
     };
     // weight element e = tid + NT*u: input channel cil, [c][k] index rem of
-    // w[ci0 + cil][4q + c][k]; byte offset from w[ci0][4q][0] (out of range
-    // past the slice)
-    unsigned woff[kBsWU];
+    // w[ci0 + cil][4q + c][k] (per sub-step: k = kd*KHW + t); byte offset
+    // from w[ci0][4q][0] (out of range past the slice)
+    constexpr int WN = WSUB ? WSU : kBsWU;
+    const int wsl = WSUB ? KHW : P.kvol; // taps per channel in a slice
+    unsigned woff[WN];
 #pragma unroll
-    for (int u = 0; u < kBsWU; ++u) {
+    for (int u = 0; u < WN; ++u) {
         const int e = tid + u * NT;
-        const int cil = e / (4 * P.kvol), rem = e - cil * (4 * P.kvol);
-        woff[u] = e < wq_sz ? 4u * (unsigned)(cil * P.Cog * P.kvol + rem) : kBwdOutOfRange;
+        const int cil = e / (4 * wsl), rem = e - cil * (4 * wsl);
+        const int c = rem / wsl, t = rem - c * wsl;
+        woff[u] = e < 16 * CT * 4 * wsl ? 4u * (unsigned)(cil * P.Cog * P.kvol + c * P.kvol + t) : kBwdOutOfRange;
     }
     const bwd_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float *>(w + (int64_t)ci0 * P.Cog * P.kvol), (short)0, 4 * 16 * CT * P.Cog * P.kvol, kBwdRsrcWord3);
-    float wpf[kBsWU];
+    float wpf[WN];
+    // weights of quad q (per quad) or of sub-step q = (quad, kd) (per sub-step)
     auto fetch_w = [&](int q) __attribute__((always_inline)) {
-        const int soff = 16 * min(q, P.NQ - 1) * P.kvol;
+        int soff;
+        if constexpr (WSUB) {
+            const int qq = min(q, nsub - 1), quad = qq / AD.K, kd = qq - quad * AD.K;
+            soff = 16 * quad * P.kvol + 4 * kd * KHW;
+        } else {
+            soff = 16 * min(q, P.NQ - 1) * P.kvol;
+        }
 #pragma unroll
-        for (int u = 0; u < kBsWU; ++u)
+        for (int u = 0; u < WN; ++u)
             wpf[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, woff[u], soff, 0));
     };
-    auto stage_w = [&]() __attribute__((always_inline)) {
+    auto stage_w = [&](float *wqb) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < kBsWU; ++u) wq[tid + u * NT] = wpf[u];
+        for (int u = 0; u < WN; ++u) wqb[tid + u * NT] = wpf[u];
     };
 
     // per block pb of this wave: row r and first column, so the B address is
@@ -572,7 +592,7 @@ __global__ __launch_bounds__(256 * CT) __attribute__((amdgpu_waves_per_eu(1, 6))
         const int r = (blk * 16) / WIN, col0 = (blk * 16) - r * WIN;
         bpos[pb] = (c4 * NR + r * SH) * NW + (col0 + j16) * SW;
     }
-    const int abase = ((16 * m + j16) * 4 + c4) * P.kvol;
+    const int abase = ((16 * m + j16) * 4 + c4) * (WSUB ? KHW : P.kvol);
     bwd_v4f acc[PB];
 #pragma unroll
     for (int pb = 0; pb < PB; ++pb) acc[pb] = bwd_v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -580,7 +600,7 @@ __global__ __launch_bounds__(256 * CT) __attribute__((amdgpu_waves_per_eu(1, 6))
     float pf[U];
     fetch_w(0);
     fetch(pf, 0);
-    stage_w();
+    stage_w(wq);
     stage(win0, pf);
     fetch(pf, 1);
     fetch_w(1);
@@ -588,6 +608,8 @@ __global__ __launch_bounds__(256 * CT) __attribute__((amdgpu_waves_per_eu(1, 6))
     for (int ss = 0; ss < nsub; ++ss) {
         const int kd = ss % AD.K;
         const float *wb = (ss & 1) ? win1 : win0;
+        // the A operands: this sub-step's buffer, or the quad's slice at kd
+        const float *wqa = WSUB ? ((ss & 1) ? wq1 : wq) : wq + kd * KHW;
         // taps (kd, kh, kw) in order, two operand sets: the reads of tap t + 1
         // are in flight during tap t's products.  (k, kw, toff) walk the taps
         // with scalar steps.  With an even tap count the last reads are of
@@ -601,35 +623,37 @@ __global__ __launch_bounds__(256 * CT) __attribute__((amdgpu_waves_per_eu(1, 6))
                 acc[pb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bb[pb], acc[pb], 0, 0, 0);
         };
         if constexpr (FIX) {
-            // 9 taps unrolled (window offsets are constants past bpos[pb]),
-            // the operands of tap t + 1 read before tap t's products
-            float a[9], bb[2][PB];
+            // FK x FK taps unrolled (window offsets are constants past
+            // bpos[pb]), the operands of tap t + 1 read before tap t's products
+            constexpr int NTAP = FK * FK;
+            float a[NTAP], bb[2][PB];
 #pragma unroll
-            for (int t = 0; t < 9; ++t) a[t] = wq[abase + kd * 9 + t];
+            for (int t = 0; t < NTAP; ++t) a[t] = wqa[abase + t];
 #pragma unroll
-            for (int t = 0; t < 9; ++t) {
+            for (int t = 0; t < NTAP; ++t) {
                 if (t == 0) {
 #pragma unroll
                     for (int pb = 0; pb < PB; ++pb) bb[0][pb] = wb[bpos[pb]];
                 }
-                if (t + 1 < 9) {
-                    const int kh = (t + 1) / 3, kw = (t + 1) - 3 * ((t + 1) / 3);
+                if (t + 1 < NTAP) {
+                    const int kh = (t + 1) / FK, kw = (t + 1) - FK * ((t + 1) / FK);
 #pragma unroll
                     for (int pb = 0; pb < PB; ++pb) bb[(t + 1) & 1][pb] = wb[bpos[pb] + kh * NW + kw];
                 }
                 mma(a[t], bb[t & 1]);
             }
             // issue order: the A reads and tap 0's B reads, then per tap the
-            // two B reads of the next tap before its four products
-            __builtin_amdgcn_sched_group_barrier(0x100, 5 + 2, 0);
+            // two B reads of the next tap before its four products (the A
+            // reads pair up: 5 instructions for 9, 8 for 16)
+            __builtin_amdgcn_sched_group_barrier(0x100, (NTAP + 1) / 2 + 2, 0);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
+            for (int t = 0; t < NTAP - 1; ++t) {
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         } else {
-            int k = kd * KHW, kw = 0, toff = 0;
+            int k = 0, kw = 0, toff = 0;
             auto next = [&]() __attribute__((always_inline)) {
                 const bool row_end = kw == KW - 1;
                 toff += row_end ? DH * NW - (KW - 1) * DW : DW;
@@ -637,7 +661,7 @@ __global__ __launch_bounds__(256 * CT) __attribute__((amdgpu_waves_per_eu(1, 6))
                 ++k;
             };
             auto rd = [&](float &a, float (&bb)[PB]) __attribute__((always_inline)) {
-                a = wq[abase + k];
+                a = wqa[abase + k];
 #pragma unroll
                 for (int pb = 0; pb < PB; ++pb) bb[pb] = wb[bpos[pb] + toff];
             };
@@ -654,13 +678,21 @@ __global__ __launch_bounds__(256 * CT) __attribute__((amdgpu_waves_per_eu(1, 6))
             }
             if (t < KHW) mma(a0, b0);
         }
-        const bool quad_end = kd == AD.K - 1;
-        if (quad_end) __syncthreads(); // every wave is done with this quad's weights
-        // the next window into the other buffer (read last in sub-step ss - 1)
-        stage((ss & 1) ? win0 : win1, pf);
-        if (quad_end) {
-            stage_w();
-            fetch_w(ss / AD.K + 2);
+        if constexpr (WSUB) {
+            // the next window and weights into the other buffers (read last
+            // in sub-step ss - 1)
+            stage((ss & 1) ? win0 : win1, pf);
+            stage_w((ss & 1) ? wq : wq1);
+            fetch_w(ss + 2);
+        } else {
+            const bool quad_end = kd == AD.K - 1;
+            if (quad_end) __syncthreads(); // every wave is done with this quad's weights
+            // the next window into the other buffer (read last in sub-step ss - 1)
+            stage((ss & 1) ? win0 : win1, pf);
+            if (quad_end) {
+                stage_w(wq);
+                fetch_w(ss / AD.K + 2);
+            }
         }
         fetch(pf, ss + 2);
         __syncthreads();
@@ -681,36 +713,43 @@ __global__ __launch_bounds__(256 * CT) __attribute__((amdgpu_waves_per_eu(1, 6))
 }
 
 // LDS floats of one workgroup: two window buffers, the weight slice (NT *
-// kBsWU), and the pad past them that the last tap's unused reads may touch.
-inline size_t stage_lds_floats(int ct, int dh, int NW) {
-    return 2 * (size_t)kBsWinCap + (size_t)256 * ct * kBsWU + (size_t)dh * NW + 1;
+// kBsWU) or the two per-sub-step weight buffers, and the pad past them that
+// the last tap's unused reads may touch.
+inline size_t stage_lds_floats(int ct, bool wsub, int dh, int NW) {
+    return wsub ? 2 * (size_t)kBsWinCap2 + 2 * (size_t)kBsWsub + (size_t)dh * NW + 1
+                : 2 * (size_t)kBsWinCap + (size_t)256 * ct * kBsWU + (size_t)dh * NW + 1;
 }
 
 // The staged variant applies: 2D or 3D plans with groups of 32k input and 4k
 // output channels (two channel tiles per workgroup; with one, each dy window
 // would be staged once per 16 channels and the matrix kernel is faster),
-// W_in of 16, 32 or 64, at most 32 taps, a window of at most kBsWinCap
-// floats, and the buffers within 64 KB of LDS.  Returns the tile count CT, 0
-// when it does not apply; fills the window fields of P.
-int stage_ct(const convt_plan &Pl, BsParams &P) {
+// W_in of 16, 32 or 64, and the buffers within 64 KB of LDS; up to 32 taps
+// with the quad's weights staged once (a window of at most kBsWinCap floats),
+// up to 64 with at most 16 per D tap staged per sub-step (kBsWinCap2).
+// Returns 1 (weights per quad), 2 (per sub-step) or 0 when it does not apply;
+// fills the window fields of P.
+int stage_mode(const convt_plan &Pl, BsParams &P) {
     const AxisPlan &AH = Pl.ax[1], &AW = Pl.ax[2];
-    if (Pl.ndim < 2 || Pl.Cig % 32 != 0 || Pl.Cog % 4 != 0 || Pl.k_vol > 32) return 0;
+    if (Pl.ndim < 2 || Pl.Cig % 32 != 0 || Pl.Cog % 4 != 0 || Pl.k_vol > 64) return 0;
+    const bool wsub = Pl.k_vol > 32;
+    if (wsub && AH.K * AW.K > 16) return 0;
     if (AW.L_in != 16 && AW.L_in != 32 && AW.L_in != 64) return 0;
     if (4 * Pl.C_out * Pl.out_sp > 0x7fffffff || Pl.N * Pl.C_in * Pl.in_sp > ((int64_t)1 << 40)) return 0;
     P.R = 256 / AW.L_in;
     P.NR = (P.R - 1) * AH.s + (AH.K - 1) * AH.d + 1;
     P.NW = (AW.L_in - 1) * AW.s + (AW.K - 1) * AW.d + 1;
     P.win_sz = 4 * P.NR * P.NW;
-    if (P.win_sz > kBsWinCap) return 0;
-    const int ct = 2;
-    if (4 * stage_lds_floats(ct, AH.d, P.NW) > 65536) return 0;
-    return ct;
+    if (P.win_sz > (wsub ? kBsWinCap2 : kBsWinCap)) return 0;
+    if (4 * stage_lds_floats(2, wsub, AH.d, P.NW) > 65536) return 0;
+    return wsub ? 2 : 1;
 }
 
 template <int CT>
-int launch_stage(const convt_plan &Pl, BsParams &P, const float *dy, const float *w, float *dx, hipStream_t st) {
+int launch_stage(const convt_plan &Pl, BsParams &P, bool wsub, const float *dy, const float *w, float *dx,
+                 hipStream_t st) {
     const AxisPlan &AH = Pl.ax[1], &AW = Pl.ax[2];
     const bool fix = AW.L_in == 16 && AH.s == 2 && AW.s == 2 && AH.K == 3 && AW.K == 3 && AH.d == 1 && AW.d == 1;
+    const bool fix2 = AW.L_in == 32 && AH.s == 2 && AW.s == 2 && AH.K == 4 && AW.K == 4 && AH.d == 1 && AW.d == 1;
     for (int a = 0; a < kAxes; ++a) P.ax[a] = Pl.ax[a];
     P.C_in = (int)Pl.C_in;
     P.C_out = (int)Pl.C_out;
@@ -724,13 +763,19 @@ int launch_stage(const convt_plan &Pl, BsParams &P, const float *dy, const float
     P.NQ = (int)(Pl.Cog / 4);
     const int64_t blocks = Pl.N * Pl.G * (int64_t)P.ccs * Pl.ax[0].L_in * P.nhb;
     if (blocks > 0x7fffffff) return (int)hipErrorInvalidValue;
-    const size_t lds = 4 * stage_lds_floats(CT, P.ax[1].d, P.NW);
-    if (fix)
-        hipLaunchKernelGGL((k_backward_data_stage<CT, true>), dim3((unsigned)blocks), dim3(256 * CT), lds, st, P, dy, w,
-                           dx);
-    else
-        hipLaunchKernelGGL((k_backward_data_stage<CT, false>), dim3((unsigned)blocks), dim3(256 * CT), lds, st, P, dy, w,
-                           dx);
+    const size_t lds = 4 * stage_lds_floats(CT, wsub, P.ax[1].d, P.NW);
+    const dim3 grid((unsigned)blocks), blk(256 * CT);
+    if (wsub) {
+        if (fix2)
+            hipLaunchKernelGGL((k_backward_data_stage<CT, 2, true>), grid, blk, lds, st, P, dy, w, dx);
+        else
+            hipLaunchKernelGGL((k_backward_data_stage<CT, 0, true>), grid, blk, lds, st, P, dy, w, dx);
+    } else {
+        if (fix)
+            hipLaunchKernelGGL((k_backward_data_stage<CT, 1, false>), grid, blk, lds, st, P, dy, w, dx);
+        else
+            hipLaunchKernelGGL((k_backward_data_stage<CT, 0, false>), grid, blk, lds, st, P, dy, w, dx);
+    }
     const hipError_t e = hipGetLastError();
     return e == hipSuccess ? 0 : (int)e;
 }
@@ -1037,7 +1082,7 @@ const char *backward_data_kernel_name(const convt_plan &P) {
     if (row_window(P, mt, W)) return "k_backward_data_mfma_row";
     if (mt == 0 && bwd_wpair_applies(P)) return "k_backward_data_wpair";
     BsParams S;
-    if (CONVT_BWD_STAGE && mt > 0 && stage_ct(P, S) > 0) return "k_backward_data_stage";
+    if (CONVT_BWD_STAGE && mt > 0 && stage_mode(P, S) > 0) return "k_backward_data_stage";
     return mt > 0 ? "k_backward_data_mfma" : "k_backward_data";
 }
 
@@ -1066,7 +1111,10 @@ int launch_backward_data(const convt_plan &Pl, const float *dy, const float *w, 
         }
     }
     BsParams S;
-    if (CONVT_BWD_STAGE && mt > 0 && stage_ct(Pl, S) == 2) return launch_stage<2>(Pl, S, dy, w, dx, st);
+    if (CONVT_BWD_STAGE && mt > 0) {
+        const int mode = stage_mode(Pl, S);
+        if (mode > 0) return launch_stage<2>(Pl, S, mode == 2, dy, w, dx, st);
+    }
     switch (mt) {
     case 4: return launch_mfma<4>(Pl, P, dy, w, dx, st);
     case 2: return launch_mfma<2>(Pl, P, dy, w, dx, st);
