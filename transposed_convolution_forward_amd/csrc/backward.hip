@@ -735,6 +735,7 @@ int stage_mode(const convt_plan &Pl, BsParams &P) {
     if (wsub && AH.K * AW.K > 16) return 0;
     if (AW.L_in != 16 && AW.L_in != 32 && AW.L_in != 64) return 0;
     if (4 * Pl.C_out * Pl.out_sp > 0x7fffffff || Pl.N * Pl.C_in * Pl.in_sp > ((int64_t)1 << 40)) return 0;
+    if (4 * 32 * Pl.Cog * Pl.k_vol > 0x7fffffff) return 0; // a chunk's weights in one buffer resource
     P.R = 256 / AW.L_in;
     P.NR = (P.R - 1) * AH.s + (AH.K - 1) * AH.d + 1;
     P.NW = (AW.L_in - 1) * AW.s + (AW.K - 1) * AW.d + 1;
