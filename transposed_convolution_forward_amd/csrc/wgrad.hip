@@ -208,6 +208,7 @@ struct WsParams {
     int rows_per_wave;
     int rchunks;       // row ranges per (sample, group, chunk)
     int64_t units;     // waves of work
+    int wsplit;        // row-sharing kernel: the 4 waves split one unit's W steps
 };
 
 __global__ __launch_bounds__(kWgBlock) void k_backward_weight_shift(const WsParams P, const float *__restrict__ x,
@@ -332,12 +333,15 @@ __global__ __launch_bounds__(kWgBlock) void k_backward_weight_shift_rows(const W
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     // workgroup: (sample, group, D tap) and four of its (x plane, row range)
-    // units; a wave past the last unit, or whose D tap reaches no output from
-    // its plane, has no work but joins the reduction
+    // units, or with wsplit one unit whose W steps the four waves split (they
+    // then read the same x and dy lines at about the same time); a wave past
+    // the last unit, or whose D tap reaches no output from its plane, has no
+    // work but joins the reduction
     const int per = AD.L_in * P.rchunks;
-    const int bpg = (per + 3) / 4;
+    const int bpg = P.wsplit ? per : (per + 3) / 4;
     const int64_t ngk = (int64_t)blockIdx.x / bpg;
-    const int sub = (int)((int64_t)blockIdx.x - ngk * bpg) * 4 + wave;
+    const int sub = P.wsplit ? (int)((int64_t)blockIdx.x - ngk * bpg)
+                             : (int)((int64_t)blockIdx.x - ngk * bpg) * 4 + wave;
     const int kd = (int)(ngk % AD.K);
     const int g = (int)((ngk / AD.K) % P.G);
     const int n = (int)(ngk / AD.K / P.G);
@@ -389,7 +393,8 @@ __global__ __launch_bounds__(kWgBlock) void k_backward_weight_shift_rows(const W
                                                                       : kWgOutOfRange;
         return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
     };
-    for (int st = 0; st < spr; ++st) {
+    const int st0 = P.wsplit ? wave : 0, dst = P.wsplit ? 4 : 1;
+    for (int st = st0; st < spr; st += dst) {
         float sl[NSL][NTW];
         float xa[2];
 #pragma unroll
@@ -454,6 +459,10 @@ bool weight_shift_applies(const convt_plan &Pl) {
 #ifndef CONVT_WSR_WAVES
 #define CONVT_WSR_WAVES 1024
 #endif
+// Tuning knob: the row-sharing kernel's four waves split one unit's W steps.
+#ifndef CONVT_WSR_WSPLIT
+#define CONVT_WSR_WSPLIT 1
+#endif
 
 // The row-sharing variant applies as well: H stride 1 and dilation 1, at most
 // 7 H taps and 8 W taps (two T blocks).
@@ -483,9 +492,11 @@ int launch_weight_shift_rows(const convt_plan &Pl, const float *x, const float *
     P.rows_per_wave = rpw;
     P.rchunks = (H + rpw - 1) / rpw;
     P.units = base * P.rchunks;
-    // workgroups: per (sample, group, D tap), four (x plane, row range) units each
-    const int64_t blocks =
-        Pl.N * Pl.G * (int64_t)Pl.ax[0].K * ((Pl.ax[0].L_in * (int64_t)P.rchunks + 3) / 4);
+    // workgroups: per (sample, group, D tap), four (x plane, row range) units
+    // each, or one with its W steps split over the waves
+    P.wsplit = CONVT_WSR_WSPLIT;
+    const int64_t per = Pl.ax[0].L_in * (int64_t)P.rchunks;
+    const int64_t blocks = Pl.N * Pl.G * (int64_t)Pl.ax[0].K * (P.wsplit ? per : (per + 3) / 4);
     if (blocks > 0x7fffffff || Pl.ax[0].L_in * (int64_t)P.rchunks > 0x7fffffff) return (int)hipErrorInvalidValue;
     auto go = [&](auto khc, auto ntc) {
         hipLaunchKernelGGL((k_backward_weight_shift_rows<decltype(khc)::value, decltype(ntc)::value>),
@@ -510,6 +521,7 @@ int launch_weight_shift_rows(const convt_plan &Pl, const float *x, const float *
 
 int launch_weight_shift(const convt_plan &Pl, const float *x, const float *dy, float *dw, hipStream_t st) {
     WsParams P;
+    P.wsplit = 0;
     for (int a = 0; a < kAxes; ++a) P.ax[a] = Pl.ax[a];
     P.C_in = (int)Pl.C_in;
     P.C_out = (int)Pl.C_out;
