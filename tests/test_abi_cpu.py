@@ -220,6 +220,13 @@ def test_gradient_kernel_routing():
         want = ("k_backward_weight_stage" if (cin, k_w, w_in) == (32, 3, 16)
                 else "k_backward_weight" if cin == 16 else "k_backward_weight_lds")
         assert _gradient_kernels(p)[1] == want, (cin, k_w, w_in)
+    # past the staged kernels' window buffers: H stride 3 on W_in 16 needs 4 x 48
+    # x 33 = 6336 window floats for the input gradient (over 4608); W_in 64 needs
+    # 3 x 4 x 5 x 129 = 7740 for the weight gradient's D taps (over 7168)
+    p = T.Plan(3, 2, 32, 64, 1, (8, 16, 16), (3, 3, 3), (2, 3, 2), (1, 1, 1), (1, 1, 1), (1, 1, 1))
+    assert _gradient_kernels(p)[0] == "k_backward_data_mfma"
+    p = T.Plan(3, 2, 32, 64, 1, (8, 4, 64), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), (1, 1, 1))
+    assert _gradient_kernels(p)[1] == "k_backward_weight_lds"
     # H stride 2: not the W-pair input-gradient kernel, and the weight gradient
     # without row sharing
     p = T.Plan(3, 1, 32, 32, 4, (4, 6, 16), (3, 5, 7), (2, 2, 2), (1, 2, 3), (1, 1, 1), (1, 1, 1))
