@@ -158,7 +158,27 @@ def test_workload_plans_and_paths():
     assert "kernel=k_igemm3d\n" in T.convt_plan_describe(p2)
     p2w = T.Plan(2, 2, 128, 64, 1, (9, 32), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1))
     assert "kernel=k_igemm3d_wide" in T.convt_plan_describe(p2w)
-
+    # kernel 3 or 4 with stride 2 along W (rows of any length that is a
+    # multiple of 4, in segments) streams the weights for any input channel
+    # count that is a multiple of 16 and output channels in blocks of 64 or 32:
+    # 64 -> 64 on the fused layer's geometry,
+    # 128 -> 64 with kernel 3, 32 -> 64 with kernel 4 (no weights-in-VGPR
+    # variant), 64 -> 32, 48 -> 96, 64 -> 128, strides 1 on D and H
+    for cin, cout, k, s_dh in ((64, 64, 3, 2), (128, 64, 3, 2), (32, 64, 4, 2), (64, 64, 4, 2),
+                               (64, 32, 3, 2), (48, 96, 4, 2), (64, 128, 3, 2), (16, 64, 3, 2),
+                               (64, 64, 3, 1), (32, 32, 4, 1)):
+        for w_in in (16, 32, 64, 132):
+            pw = T.Plan(3, 2, cin, cout, 1, (8, 8, w_in), (k,) * 3, (s_dh, s_dh, 2), (1, 1, 1),
+                        (1, 1, 1) if k == 3 and s_dh == 2 else (0, 0, 0), (1, 1, 1))
+            assert "kernel=k_igemm3d_wide" in T.convt_plan_describe(pw), (cin, cout, k, s_dh, w_in)
+    # rows whose length is not a multiple of 4, output channels not in blocks
+    # of 32, input channels not in chunks of 16, more than 4 taps per class on
+    # D do not
+    for a in (((8, 8, 50), 64, 64, (3, 3, 3), (2, 2, 2)), ((8, 8, 16), 64, 48, (3, 3, 3), (2, 2, 2)),
+              ((8, 8, 16), 24, 64, (3, 3, 3), (2, 2, 2)), ((8, 8, 16), 64, 64, (5, 3, 3), (1, 2, 2))):
+        ins, cin, cout, k, st = a
+        text = T.convt_plan_describe(T.Plan(3, 2, cin, cout, 1, ins, k, st, (1, 1, 1), (0, 1, 1), (1, 1, 1)))
+        assert "kernel=k_igemm3d" not in text, a
 
 def _gradient_kernels(plan):
     text = T.convt_plan_describe(plan)

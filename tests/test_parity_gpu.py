@@ -80,6 +80,38 @@ REDUCED = [
                (0, 0, 0), (1, 1, 1), True, True, wid=3202),
     S.Workload("igw_c128_w16_nobias", 3, 1, 128, 64, 1, (5, 2, 16), (4, 4, 4), (2, 2, 2), (1, 1, 1),
                (0, 1, 0), (1, 1, 1), False, False, wid=3203),
+    # kernel 3 along W (12-byte weight loads): the fused layer's geometry with
+    # 64 input channels, 128 input channels on rows of 64 outputs, a ragged
+    # last W-block; kernel 4 with 32 input channels and with 64 on one W-block
+    S.Workload("igw_k3_c64_fused", 3, 2, 64, 64, 1, (3, 5, 16), (3, 3, 3), (2, 2, 2), (1, 1, 1),
+               (1, 1, 1), (1, 1, 1), True, True, wid=3204),
+    S.Workload("igw_k3_c128_w32", 3, 1, 128, 64, 1, (2, 4, 32), (3, 3, 3), (2, 2, 2), (1, 1, 1),
+               (1, 1, 1), (1, 1, 1), True, False, wid=3205),
+    S.Workload("igw_k3_c64_w24", 3, 2, 64, 64, 1, (3, 3, 24), (3, 3, 3), (2, 2, 2), (1, 0, 1),
+               (0, 1, 0), (1, 1, 1), False, True, wid=3206),
+    S.Workload("igw_k4_c32_fused", 3, 2, 32, 64, 1, (3, 4, 32), (4, 4, 4), (2, 2, 2), (1, 1, 1),
+               (0, 0, 0), (1, 1, 1), True, True, wid=3207),
+    S.Workload("igw_k4_c32_w12", 3, 1, 32, 64, 1, (2, 5, 12), (4, 4, 4), (2, 2, 2), (1, 1, 2),
+               (0, 1, 0), (1, 1, 1), True, False, wid=3208),
+    S.Workload("igw_k4_c64_w16", 3, 1, 64, 64, 1, (2, 3, 16), (4, 4, 4), (2, 2, 2), (1, 1, 1),
+               (0, 0, 0), (1, 1, 1), False, False, wid=3209),
+    # output channels in blocks of 32 (64 -> 32, 48 -> 96: three blocks, three
+    # input-channel chunks) and of 64 (64 -> 128: two blocks); 16 input
+    # channels; stride 1 on D and H (3 and 4 taps per class, 12 tap slots)
+    S.Workload("igw_co32_k3_fused", 3, 2, 64, 32, 1, (3, 4, 16), (3, 3, 3), (2, 2, 2), (1, 1, 1),
+               (1, 1, 1), (1, 1, 1), True, True, wid=3210),
+    S.Workload("igw_co128_k4", 3, 1, 64, 128, 1, (2, 3, 32), (4, 4, 4), (2, 2, 2), (1, 1, 1),
+               (0, 0, 0), (1, 1, 1), True, False, wid=3211),
+    S.Workload("igw_co96_c48", 3, 1, 48, 96, 1, (2, 3, 20), (3, 3, 3), (2, 2, 2), (1, 1, 0),
+               (0, 1, 1), (1, 1, 1), True, False, wid=3212),
+    S.Workload("igw_c16_k3_fused", 3, 2, 16, 64, 1, (3, 3, 8), (3, 3, 3), (2, 2, 2), (1, 1, 1),
+               (1, 1, 1), (1, 1, 1), True, True, wid=3213),
+    S.Workload("igw_s1_taps12", 3, 1, 64, 64, 1, (4, 5, 16), (3, 4, 3), (1, 1, 2), (1, 1, 1),
+               (0, 0, 1), (1, 1, 1), False, True, wid=3214),
+    # rows longer than 32 inputs in W segments of 32 (halo staged per
+    # segment): two segments with a ragged last one
+    S.Workload("igw_seg_w44_k4", 3, 1, 64, 64, 1, (2, 3, 44), (4, 4, 4), (2, 2, 2), (1, 1, 2),
+               (0, 0, 0), (1, 1, 1), True, False, wid=3215),
     # generic path on the matrix cores with input rows shared along H (the
     # 4x4x1 rows kernel or, for groups of 8k output and 4k input channels, the
     # 16x16x4 row-pair kernel): two H tap counts (one launch each) and a ragged
@@ -128,6 +160,18 @@ REDUCED = [
                True, False, wid=3302),
     S.Workload("igw2d_c128_k4", 2, 2, 128, 64, 1, (9, 32), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1),
                True, False, wid=3303),
+    S.Workload("igw2d_c64_k3", 2, 2, 64, 64, 1, (10, 20), (3, 3), (2, 2), (1, 1), (1, 0), (1, 1),
+               True, True, wid=3304),
+    S.Workload("igw2d_co32_k4", 2, 2, 32, 32, 1, (12, 32), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1),
+               True, False, wid=3305),
+    # 2D rows in W segments: 64 inputs (two segments), 100 inputs in 32-channel
+    # blocks (four, the last 6 outputs), W padding 3 (later first positions)
+    S.Workload("igw2d_seg_w64_k3", 2, 2, 32, 64, 1, (6, 64), (3, 3), (2, 2), (1, 1), (1, 1), (1, 1),
+               True, True, wid=3306),
+    S.Workload("igw2d_seg_w100_co32", 2, 1, 64, 32, 1, (5, 100), (3, 3), (2, 2), (1, 2), (0, 1),
+               (1, 1), True, True, wid=3307),
+    S.Workload("igw2d_seg_p3", 2, 2, 16, 64, 1, (4, 68), (4, 4), (2, 2), (1, 3), (1, 1), (1, 1),
+               False, False, wid=3308),
 ]
 
 

@@ -39,6 +39,7 @@ namespace convt {
 namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f3 __attribute__((ext_vector_type(3)));
 
 __device__ __forceinline__ f4 load4u(const float *p) {
     f4 v;
@@ -119,6 +120,8 @@ struct Igemm3dParams {
     int cls_chunks[kMaxClasses];     // row chunks (rows_per_block rows each) per class
     int xcd_order;                   // 1: each XCD walks a contiguous range of a class's chunks
     int x_bytes;                     // bytes of x (wide variant: one buffer resource over it)
+    int wseg;                        // wide variant: W segments of 16*NWB input positions per row
+    int wnf;                         // wide variant: float4s staged per input row and segment
     int cls_rows[kMaxClasses];
     int cls_rstep[kMaxClasses]; // output rows per step: 1, or 4 / taps for classes of 1 or 2 D x H taps
     int cls_td[kMaxClasses], cls_th[kMaxClasses];
@@ -767,16 +770,22 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
 // ---------------------------------------------------------------- wide variant
 // Channel-heavy layers: the class's weights (C_in x C_out x taps) do not fit in
 // VGPRs, so they stream through LDS.  A workgroup of 4 waves owns 4 output
-// rows of one class (wave w: row w, all 64 output channels x NWB W-blocks, 16
-// accumulator tiles).  The contraction runs over stages (D/H tap slot x chunk
-// of CC input channels); each stage stages the weight chunk and the 4 rows'
-// input rows, double-buffered.  The weights are staged as [kw][ci][j][m] for
-// channel co = 16m + j, so one 16-byte read gives a lane its four A operands
-// (W^T: 16 co x 4 ci for m = 0..3).  Per (ci quad, kw): 1 A read and NWB B
-// reads feed 4*NWB MFMAs.  Staging offsets are fixed per thread for the
+// rows of one class and one block of COB = 16*MT output channels (wave w: row
+// w, the block's channels x NWB W-blocks, MT*NWB accumulator tiles per W
+// phase); blocks of one row run side by side (channel block fastest), so the
+// rows' inputs are read from L2 after the first.  The contraction runs over
+// stages (D/H tap slot x chunk of CC input channels, C_in/CC chunks); each
+// stage stages the weight chunk and the 4 rows' input rows, double-buffered.
+// The weights are staged as [kw][ci][j][m] for channel co = 16m + j of the
+// block, so one 8- or 16-byte read gives a lane its MT A operands (W^T: 16 co
+// x 4 ci for m < MT); the K_W taps of one (ci, co, kd, kh) are contiguous in
+// the weight tensor and come in one 12- or 16-byte load.  Per (ci quad, kw):
+// 1 A read and NWB B reads feed MT*NWB MFMAs.  Rows longer than 16*NWB input
+// positions split into W segments (a block each): a segment stages its input
+// positions plus the halo its taps reach; positions outside the row are never
+// staged and keep the zeros written at the start.  Staging offsets are fixed per thread for the
 // block; per stage only a uniform offset changes, and input rows outside the
 // input load as zeros through the buffer resource's range check.
-constexpr int kWidePWC = 64; // staged weights per (kw, ci): 64 channels as [j][m]
 // Two workgroups fit a CU's LDS, so two waves per SIMD: the register budget
 // that target allows keeps the accumulators in place across stages.
 #ifndef CONVT_IGW_WAVES_PER_EU
@@ -799,7 +808,7 @@ __device__ __forceinline__ RowPos pick_row(int q, const RowPos &A, const RowPos 
     return o;
 }
 
-template <int CIG, int KW, int SW, int DW, int NWB, int CC, int PWX, int EPI>
+template <int KW, int SW, int DW, int NWB, int MT, int CC, int PWX, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CONVT_IGW_WAVES_PER_EU)))
 void k_igemm3d_wide(const Igemm3dParams P,
                                                       const float *__restrict__ x,
@@ -807,17 +816,18 @@ void k_igemm3d_wide(const Igemm3dParams P,
                                                       const float *__restrict__ bias,
                                                       const float *add, float *y) {
     using Ph = WPhases<KW, SW, DW>;
-    constexpr int COG = 64;
+    constexpr int COB = 16 * MT;           // output channels of a block
     constexpr int NT = 256;
-    constexpr int NCH = CIG / CC;          // channel chunks
     constexpr int NPH = Ph::count() > 0 ? Ph::count() : 1;
-    constexpr int WPAIRS = CC * COG;       // (ci, co) pairs of a weight chunk
+    constexpr int WPAIRS = CC * COB;       // (ci, co) pairs of a weight chunk
     constexpr int WPER = WPAIRS / NT;      // per thread
-    constexpr int XPER = (4 * CC * 8 + NT - 1) / NT; // input rows: 4 rows x CC x (W_in/4 <= 8)
-    static_assert(CIG % CC == 0 && CC % 4 == 0 && WPAIRS % NT == 0, "chunking");
-    static_assert(KW == 4, "one 16-byte weight load covers the W taps");
+    constexpr int XPER = (4 * CC * (PWX / 4) + NT - 1) / NT; // input rows: 4 rows x CC x NF float4s
+    static_assert(CC % 4 == 0 && WPAIRS % NT == 0, "chunking");
+    static_assert(MT == 2 || MT == 4, "one 8- or 16-byte LDS read gives the A operands");
+    static_assert(KW == 3 || KW == 4, "one 12- or 16-byte weight load covers the W taps");
+    typedef float amt __attribute__((ext_vector_type(MT)));
 
-    __shared__ __attribute__((aligned(16))) float Wl[2][KW][CC][kWidePWC];
+    __shared__ __attribute__((aligned(16))) float Wl[2][KW][CC][COB];
     __shared__ __attribute__((aligned(16))) float Xl[2][4][CC][PWX];
 
     const int tid = threadIdx.x;
@@ -826,15 +836,28 @@ void k_igemm3d_wide(const Igemm3dParams P,
     const int j = lane & 15;
     const int g4 = lane >> 4;
 
+    // channel block fastest, then W segment (C_out is a multiple of COB, C_in of
+    // CC: checked on the host)
+    const int ncb = P.C_out / COB;
+    const int rsb = (int)blockIdx.x / ncb;
+    const int cb = (int)blockIdx.x - rsb * ncb;
+    const int rblk = rsb / P.wseg;
+    const int seg = rsb - rblk * P.wseg;
     int cls = 0;
-    while (cls + 1 < P.n_class && (int)blockIdx.x >= P.cls_block0[cls + 1]) ++cls;
-    const int r0 = ((int)blockIdx.x - P.cls_block0[cls]) * 4;
+    while (cls + 1 < P.n_class && rblk >= P.cls_block0[cls + 1]) ++cls;
+    const int r0 = (rblk - P.cls_block0[cls]) * 4;
     const int nrows = min(4, P.cls_rows[cls] - r0);
     if (nrows <= 0) return;
     const int td = P.cls_td[cls], th = P.cls_th[cls];
     const int nslots = td * th;
-    const int nstages = nslots * NCH;
-    const int W4 = P.W_in >> 2;
+    const int nch = P.C_in / CC; // input-channel chunks
+    const int nstages = nslots * nch;
+    const int pos0 = seg * 16 * NWB + P.iw_lo;     // input position at LDS offset 0
+    // staged positions: the segment's P.wnf float4s (<= PWX/4, host) inside the row
+    const int lo = max(pos0, 0), hi = min(pos0 + 4 * P.wnf, P.W_in);
+    const int nfs = max(hi - lo, 0) >> 2;
+    const int fdiv = max(nfs, 1);
+    const int xused = (4 * CC * nfs + NT - 1) / NT; // staging slots in use (uniform)
 
     for (int i = tid; i < 2 * 4 * CC * PWX; i += NT) (&Xl[0][0][0][0])[i] = 0.0f;
 
@@ -846,45 +869,52 @@ void k_igemm3d_wide(const Igemm3dParams P,
     // Per-thread staging offsets, fixed for the block.
     const int KDHW = P.KD * P.KH * KW;
     const int dhw = P.D_in * P.H_in * P.W_in;
-    unsigned wo4[WPER]; // weight byte offset of (ci in chunk, co), tap part excluded
-    int wlo[WPER];      // its LDS index in a [kw] plane: ci*64 + 4*(co mod 16) + co/16
+    unsigned wo4[WPER]; // weight byte offset of (ci in chunk, co in block), tap part excluded
+    int wlo[WPER];      // its LDS index in a [kw] plane: ci*COB + MT*(co mod 16) + co/16
 #pragma unroll
     for (int u = 0; u < WPER; ++u) {
         const int pr = tid + u * NT;
-        const int cil = pr / COG, co = pr - cil * COG;
-        wo4[u] = 4u * (unsigned)((cil * COG + co) * KDHW);
-        wlo[u] = cil * kWidePWC + 4 * (co & 15) + (co >> 4);
+        const int cil = pr / COB, co = pr - cil * COB;
+        wo4[u] = 4u * (unsigned)((cil * P.C_out + cb * COB + co) * KDHW);
+        wlo[u] = cil * COB + MT * (co & 15) + (co >> 4);
     }
     int xo[XPER];  // input element offset of (row, ci in chunk, float4) at the row's (qd, qh)
     int xlo[XPER]; // its LDS index, -1 past the staged float4s
-    int xrw[XPER]; // its row, 31 past the staged float4s
+    int xrw[XPER]; // its row; 31 past the staged float4s or outside the input row (loads zeros)
 #pragma unroll
     for (int u = 0; u < XPER; ++u) {
         const int f = tid + u * NT;
-        const bool in = f < 4 * CC * W4;
-        const int rr = in ? f / (CC * W4) : 3;
-        const int rem = f - rr * (CC * W4);
-        const int cil = rem / W4, c4 = rem - cil * W4;
+        const bool in = f < 4 * CC * nfs;
+        const int rr = in ? f / (CC * fdiv) : 3;
+        const int rem = in ? f - rr * (CC * nfs) : 0;
+        const int cil = rem / fdiv, c4 = rem - cil * nfs;
+        const int pos = lo + 4 * c4;
         const RowPos R = pick_row(rr, R0, R1, R2, R3);
-        xo[u] = (((R.n * P.C_in + cil) * P.D_in + R.qd) * P.H_in + R.qh) * P.W_in + 4 * c4;
-        xlo[u] = in ? (rr * CC + cil) * PWX + 4 * c4 - P.iw_lo : -1;
+        xo[u] = (((R.n * P.C_in + cil) * P.D_in + R.qd) * P.H_in + R.qh) * P.W_in + pos;
+        xlo[u] = in ? (rr * CC + cil) * PWX + pos - pos0 : -1;
         xrw[u] = in ? rr : 31;
     }
-    const rsrc_t rw_ = make_rsrc(w, 4 * P.C_in * COG * KDHW);
+    const rsrc_t rw_ = make_rsrc(w, 4 * P.C_in * P.C_out * KDHW);
     const rsrc_t rx = make_rsrc(x, P.x_bytes);
 
     f4 wpre[WPER];
     f4 xpre[XPER];
 
     auto fetch = [&](int sidx) {
-        const int slot = sidx / NCH, ch = sidx - slot * NCH;
+        const int slot = sidx / nch, ch = sidx - slot * nch;
         const int jd = slot / th, jh = slot - jd * th;
         const int kd = P.cls_kd[cls][jd], kh = P.cls_kh[cls][jh];
         const int cd = P.cls_cd[cls][jd], chh = P.cls_ch[cls][jh];
-        const unsigned wst = 4u * (unsigned)(ch * CC * COG * KDHW + (kd * P.KH + kh) * KW);
+        const unsigned wst = 4u * (unsigned)(ch * CC * P.C_out * KDHW + (kd * P.KH + kh) * KW);
 #pragma unroll
-        for (int u = 0; u < WPER; ++u)
-            wpre[u] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rw_, wo4[u], wst, 0));
+        for (int u = 0; u < WPER; ++u) {
+            if constexpr (KW == 4) {
+                wpre[u] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rw_, wo4[u], wst, 0));
+            } else {
+                const f3 v = __builtin_bit_cast(f3, __builtin_amdgcn_raw_buffer_load_b96(rw_, wo4[u], wst, 0));
+                wpre[u] = f4{v.x, v.y, v.z, 0.0f};
+            }
+        }
         // rows whose input row (qd - cd, qh - ch) lies inside the input: one bit each
         unsigned bad = 0xffffffffu;
 #pragma unroll
@@ -896,8 +926,10 @@ void k_igemm3d_wide(const Igemm3dParams P,
         const int xst = ch * CC * dhw - (cd * P.H_in + chh) * P.W_in;
 #pragma unroll
         for (int u = 0; u < XPER; ++u) {
-            const unsigned off = ((bad >> xrw[u]) << 31) | (4u * (unsigned)(xo[u] + xst));
-            xpre[u] = buf_load4(rx, off);
+            if (u < 2 || u < xused) {
+                const unsigned off = ((bad >> xrw[u]) << 31) | (4u * (unsigned)(xo[u] + xst));
+                xpre[u] = buf_load4(rx, off);
+            }
         }
     };
     auto stash = [&](int b) {
@@ -906,16 +938,16 @@ void k_igemm3d_wide(const Igemm3dParams P,
             (&Wl[b][0][0][0])[wlo[u]] = wpre[u].x;
             (&Wl[b][1][0][0])[wlo[u]] = wpre[u].y;
             (&Wl[b][2][0][0])[wlo[u]] = wpre[u].z;
-            (&Wl[b][3][0][0])[wlo[u]] = wpre[u].w;
+            if constexpr (KW == 4) (&Wl[b][KW - 1][0][0])[wlo[u]] = wpre[u].w;
         }
 #pragma unroll
         for (int u = 0; u < XPER; ++u)
-            if (xlo[u] >= 0) *reinterpret_cast<f4 *>(&Xl[b][0][0][0] + xlo[u]) = xpre[u];
+            if ((u < 2 || u < xused) && xlo[u] >= 0) *reinterpret_cast<f4 *>(&Xl[b][0][0][0] + xlo[u]) = xpre[u];
     };
 
-    f4 acc[4][NPH][NWB];
+    f4 acc[MT][NPH][NWB];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int ph = 0; ph < NPH; ++ph)
 #pragma unroll
@@ -934,8 +966,8 @@ void k_igemm3d_wide(const Igemm3dParams P,
         if (has_next) fetch(sidx + 1);
         if (active && Ph::count() > 0) {
             typedef const __attribute__((address_space(3))) float *lds_ptr;
-            typedef const __attribute__((address_space(3))) f4 *lds_f4ptr;
-            const lds_ptr abase = (lds_ptr)(&Wl[b][0][g4][4 * j]);
+            typedef const __attribute__((address_space(3))) amt *lds_aptr;
+            const lds_ptr abase = (lds_ptr)(&Wl[b][0][g4][MT * j]);
             // one base per (W phase, tap shift), relations hidden (see k_igemm3d)
             constexpr int CM = Ph::cmax() + 1;
             lds_ptr bb[SW][CM];
@@ -953,13 +985,12 @@ void k_igemm3d_wide(const Igemm3dParams P,
                     const int rw = Ph::r_of(kw);
                     const int ph = Ph::slot(rw);
                     const int c = Ph::c_of(kw);
-                    const f4 a4 = *(lds_f4ptr)(abase + (kw * CC + 4 * cig) * kWidePWC);
-                    const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+                    const amt a = *(lds_aptr)(abase + (kw * CC + 4 * cig) * COB);
 #pragma unroll
                     for (int t = 0; t < NWB; ++t) {
                         const float bv = bb[rw][c][4 * cig * PWX + 16 * t];
 #pragma unroll
-                        for (int m = 0; m < 4; ++m)
+                        for (int m = 0; m < MT; ++m)
                             acc[m][ph][t] =
                                 __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], bv, acc[m][ph][t], 0, 0, 0);
                     }
@@ -974,16 +1005,16 @@ void k_igemm3d_wide(const Igemm3dParams P,
     const RowPos R = pick_row(__builtin_amdgcn_readfirstlane(wv), R0, R1, R2, R3);
     const int64_t dhw_out = (int64_t)P.D_out * P.H_out * P.W_out;
     const int64_t row_base =
-        (int64_t)R.n * COG * dhw_out + ((int64_t)R.od * P.H_out + R.oh) * P.W_out;
+        (int64_t)R.n * P.C_out * dhw_out + ((int64_t)R.od * P.H_out + R.oh) * P.W_out;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int co = 16 * m + 4 * g4 + e;
+            const int co = cb * COB + 16 * m + 4 * g4 + e;
             const float bco = bias ? bias[co] : 0.0f;
 #pragma unroll
             for (int t = 0; t < NWB; ++t) {
-                const int ow0 = SW * (16 * t + j);
+                const int ow0 = SW * (16 * (NWB * seg + t) + j);
                 float v[SW];
 #pragma unroll
                 for (int rr = 0; rr < SW; ++rr) v[rr] = 0.0f;
@@ -1235,50 +1266,93 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
     return (int)hipGetLastError();
 }
 
+// Streamed-weight shapes: kernel 3 or 4 along W with stride 2 on rows of any
+// length that is a multiple of 4 (one or two W-blocks per segment), output
+// channels in blocks of 64 (or of 32 when C_out is an odd multiple of 32); C_in
+// is any multiple of the chunk.
 struct WideVariant {
-    int cig, KW, SW, DW, NWB, CC, PWX;
+    int KW, NWB, MT;
 };
 constexpr WideVariant kWide[] = {
-    {128, 4, 2, 1, 2, 16, 48}, // 128 -> 64 channels, kernel 4, stride 2, rows of 64 outputs
-    {128, 4, 2, 1, 1, 16, 48}, // same, rows of 32 outputs
-    {64, 4, 2, 1, 2, 16, 48},  // 64 -> 64 channels
+    {4, 2, 4}, {4, 1, 4}, {3, 2, 4}, {3, 1, 4}, // kernel 4 (the channel-heavy layer) or 3
+    {4, 2, 2}, {4, 1, 2}, {3, 2, 2}, {3, 1, 2}, // 32-channel blocks
 };
 constexpr int kNumWide = (int)(sizeof(kWide) / sizeof(kWide[0]));
+constexpr int kWideCC = 16; // input channels per stage
+constexpr int kWidePWX = 48; // LDS pitch of a staged input row
 
-int find_wide(const convt_plan &P, Layout *Lout) {
-    if (P.ndim < 2 || P.G != 1 || P.Cog != 64 || P.layout != CONVT_LAYOUT_CHANNELS_FIRST) return -1;
-    // one buffer resource spans x (31-bit byte offsets); per-sample y as in the VGPR variant
-    if (4 * P.N * P.C_in * P.in_sp >= INT32_MAX || 4 * P.C_out * P.out_sp >= INT32_MAX) return -1;
+struct WideLayout {
+    Layout L;
+    int nseg; // W segments per row
+    int nf;   // float4s staged per input row and segment
+};
+
+// W layout of the wide variant: two W-blocks per segment when the row has more
+// than 16*S_W outputs, enough segments to cover the row, and the staged input
+// positions of a segment (its 16*NWB positions plus the halo of the taps).
+bool wide_layout(const convt_plan &P, int KW, int NWB, WideLayout &WL) {
+    constexpr int SW = 2, DW = 1;
+    const AxisPlan &A = P.ax[2];
+    if (A.K != KW || A.s != SW || A.d != DW) return false;
+    Layout &L = WL.L;
+    L.cmax = 0;
+    for (int k = 0; k < KW; ++k) L.cmax = std::max(L.cmax, (k * DW) / SW);
+    int qmax = 0;
+    for (int r = 0; r < SW; ++r) {
+        L.qw0[r] = std::max(0, ceil_div(A.p - r, SW));
+        L.sigma[r] = L.qw0[r] * SW + r - A.p;
+        qmax = std::max(qmax, L.qw0[r]);
+    }
+    L.nwb = A.L_out > 16 * SW ? 2 : 1;
+    if (L.nwb != NWB) return false;
+    L.iw_lo = -((L.cmax + 3) / 4) * 4;
+    L.need = qmax + 16 * NWB - L.iw_lo; // LDS positions the B reads of a segment reach
+    WL.nseg = (A.L_out + 16 * SW * NWB - 1) / (16 * SW * NWB);
+    WL.nf = (L.need + 3) / 4;
+    return 4 * WL.nf <= kWidePWX;
+}
+
+int find_wide(const convt_plan &P, WideLayout *out) {
+    if (P.ndim < 2 || P.G != 1 || P.layout != CONVT_LAYOUT_CHANNELS_FIRST) return -1;
+    if (P.C_in % kWideCC != 0 || P.C_out % 32 != 0) return -1;
+    const int mt = P.C_out % 64 == 0 ? 4 : 2;
     const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
-    if (AW.L_in % 4 != 0 || AW.L_in / 4 > 8) return -1;
+    // one buffer resource spans x, one the weights (31-bit byte offsets); per-sample y
+    // as in the VGPR variant
+    if (4 * P.N * P.C_in * P.in_sp >= INT32_MAX || 4 * P.C_out * P.out_sp >= INT32_MAX ||
+        4 * P.C_in * P.C_out * AD.K * AH.K * AW.K >= INT32_MAX)
+        return -1;
+    if (AW.L_in % 4 != 0) return -1; // staged float4s lie wholly inside or outside a row
     if (AD.s * AH.s > kMaxClasses) return -1;
     int tdm = 0, thm = 0;
     for (int r = 0; r < AD.s; ++r) tdm = std::max(tdm, AD.tap_start[r + 1] - AD.tap_start[r]);
     for (int r = 0; r < AH.s; ++r) thm = std::max(thm, AH.tap_start[r + 1] - AH.tap_start[r]);
-    if (tdm > 2 || thm > 2) return -1;
+    if (tdm > kTapMax || thm > kTapMax) return -1;
     for (int i = 0; i < kNumWide; ++i) {
         const WideVariant &v = kWide[i];
-        if (P.Cig != v.cig) continue;
-        const Variant vv = {v.cig, 64, v.KW, v.SW, v.DW, 2, 2, v.NWB, v.PWX, 8};
-        Layout L;
-        if (!w_layout(P, vv, L)) continue;
-        if (Lout) *Lout = L;
+        if (v.MT != mt) continue;
+        WideLayout WL;
+        if (!wide_layout(P, v.KW, v.NWB, WL)) continue;
+        if (out) *out = WL;
         return i;
     }
     return -1;
 }
 
-template <int CIG, int KW, int SW, int DW, int NWB, int CC, int PWX>
-int launch_wide(const convt_plan &Pl, const Layout &L, const float *x, const float *w,
+template <int KW, int NWB, int MT>
+int launch_wide(const convt_plan &Pl, const WideLayout &WL, const float *x, const float *w,
                 const float *bias, const float *add, int act, float *y, hipStream_t st) {
     Igemm3dParams P;
-    fill_params(Pl, L, SW, P);
+    fill_params(Pl, WL.L, 2, P);
     P.x_bytes = (int)(4 * Pl.N * Pl.C_in * Pl.in_sp);
-    const int blocks = assign_blocks(P, 4);
+    P.wseg = WL.nseg;
+    P.wnf = WL.nf;
+    const int64_t blocks = (int64_t)assign_blocks(P, 4) * WL.nseg * (Pl.C_out / (16 * MT));
     if (blocks == 0) return 0;
+    if (blocks > INT32_MAX) return (int)hipErrorInvalidValue;
     with_epi(add != nullptr, act, [&](auto E) {
-        hipLaunchKernelGGL((k_igemm3d_wide<CIG, KW, SW, DW, NWB, CC, PWX, decltype(E)::value>), dim3(blocks),
-                           dim3(256), 0, st, P, x, w, bias, add, y);
+        hipLaunchKernelGGL((k_igemm3d_wide<KW, 2, 1, NWB, MT, kWideCC, kWidePWX, decltype(E)::value>),
+                           dim3((unsigned)blocks), dim3(256), 0, st, P, x, w, bias, add, y);
     });
     return (int)hipGetLastError();
 }
@@ -1288,14 +1362,14 @@ int launch_wide(const convt_plan &Pl, const Layout &L, const float *x, const flo
 bool igemm3d_supports(const convt_plan &P) {
     if (P.ndim < 2) return false;
     Layout L;
-    if (find_variant(P, &L) < 0 && find_wide(P, &L) < 0) return false;
+    if (find_variant(P, &L) < 0 && find_wide(P, nullptr) < 0) return false;
     return P.N * P.ax[0].L_out * P.ax[1].L_out < (int64_t(1) << 31);
 }
 
 const char *igemm3d_kernel_name(const convt_plan &P) {
     Layout L;
     if (find_variant(P, &L) >= 0) return "k_igemm3d";
-    return find_wide(P, &L) >= 0 ? "k_igemm3d_wide" : "none";
+    return find_wide(P, nullptr) >= 0 ? "k_igemm3d_wide" : "none";
 }
 
 int launch_igemm3d(const convt_plan &Pl, const float *x, const float *w, const float *bias,
@@ -1309,10 +1383,16 @@ int launch_igemm3d(const convt_plan &Pl, const float *x, const float *w, const f
     case 2: return launch_variant<16, 32, 4, 2, 1, 2, 2, 2, kPW, 8>(Pl, L, x, w, bias, add, act, y, st);
     default: break;
     }
-    switch (find_wide(Pl, &L)) {
-    case 0: return launch_wide<128, 4, 2, 1, 2, 16, 48>(Pl, L, x, w, bias, add, act, y, st);
-    case 1: return launch_wide<128, 4, 2, 1, 1, 16, 48>(Pl, L, x, w, bias, add, act, y, st);
-    case 2: return launch_wide<64, 4, 2, 1, 2, 16, 48>(Pl, L, x, w, bias, add, act, y, st);
+    WideLayout WL;
+    switch (find_wide(Pl, &WL)) {
+    case 0: return launch_wide<4, 2, 4>(Pl, WL, x, w, bias, add, act, y, st);
+    case 1: return launch_wide<4, 1, 4>(Pl, WL, x, w, bias, add, act, y, st);
+    case 2: return launch_wide<3, 2, 4>(Pl, WL, x, w, bias, add, act, y, st);
+    case 3: return launch_wide<3, 1, 4>(Pl, WL, x, w, bias, add, act, y, st);
+    case 4: return launch_wide<4, 2, 2>(Pl, WL, x, w, bias, add, act, y, st);
+    case 5: return launch_wide<4, 1, 2>(Pl, WL, x, w, bias, add, act, y, st);
+    case 6: return launch_wide<3, 2, 2>(Pl, WL, x, w, bias, add, act, y, st);
+    case 7: return launch_wide<3, 1, 2>(Pl, WL, x, w, bias, add, act, y, st);
     default: return (int)hipErrorInvalidValue;
     }
 }
