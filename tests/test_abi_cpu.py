@@ -171,6 +171,10 @@ def test_workload_plans_and_paths():
             pw = T.Plan(3, 2, cin, cout, 1, (8, 8, w_in), (k,) * 3, (s_dh, s_dh, 2), (1, 1, 1),
                         (1, 1, 1) if k == 3 and s_dh == 2 else (0, 0, 0), (1, 1, 1))
             assert "kernel=k_igemm3d_wide" in T.convt_plan_describe(pw), (cin, cout, k, s_dh, w_in)
+    # groups whose channel counts fit (16k inputs, 32k outputs per group) too
+    for cin, cout, g in ((64, 64, 2), (64, 256, 2), (64, 128, 4)):
+        pg = T.Plan(3, 2, cin, cout, g, (8, 8, 16), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), (1, 1, 1))
+        assert "kernel=k_igemm3d_wide" in T.convt_plan_describe(pg), (cin, cout, g)
     # rows whose length is not a multiple of 4, output channels not in blocks
     # of 32, input channels not in chunks of 16, more than 4 taps per class on
     # D do not
@@ -179,6 +183,8 @@ def test_workload_plans_and_paths():
         ins, cin, cout, k, st = a
         text = T.convt_plan_describe(T.Plan(3, 2, cin, cout, 1, ins, k, st, (1, 1, 1), (0, 1, 1), (1, 1, 1)))
         assert "kernel=k_igemm3d" not in text, a
+    # P1's grouped layer (8 channels per group) keeps its W-pair kernel
+    assert "kernel=k_igemm3d" not in T.convt_plan_describe(T.plan_for(S.GROUPED_3D))
 
 def _gradient_kernels(plan):
     text = T.convt_plan_describe(plan)

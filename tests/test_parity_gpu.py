@@ -108,6 +108,12 @@ REDUCED = [
                (1, 1, 1), (1, 1, 1), True, True, wid=3213),
     S.Workload("igw_s1_taps12", 3, 1, 64, 64, 1, (4, 5, 16), (3, 4, 3), (1, 1, 2), (1, 1, 1),
                (0, 0, 1), (1, 1, 1), False, True, wid=3214),
+    # groups: 32 channels per group (32-channel blocks), 32 -> 128 per group
+    # (two 64-channel blocks per group)
+    S.Workload("igw_g2_co32_fused", 3, 2, 64, 64, 2, (3, 4, 16), (3, 3, 3), (2, 2, 2), (1, 1, 1),
+               (1, 1, 1), (1, 1, 1), True, True, wid=3216),
+    S.Workload("igw_g2_co128_k4", 3, 1, 64, 256, 2, (2, 3, 20), (4, 4, 4), (2, 2, 2), (1, 1, 1),
+               (0, 0, 0), (1, 1, 1), True, False, wid=3217),
     # rows longer than 32 inputs in W segments of 32 (halo staged per
     # segment): two segments with a ragged last one
     S.Workload("igw_seg_w44_k4", 3, 1, 64, 64, 1, (2, 3, 44), (4, 4, 4), (2, 2, 2), (1, 1, 2),
@@ -172,6 +178,8 @@ REDUCED = [
                (1, 1), True, True, wid=3307),
     S.Workload("igw2d_seg_p3", 2, 2, 16, 64, 1, (4, 68), (4, 4), (2, 2), (1, 3), (1, 1), (1, 1),
                False, False, wid=3308),
+    S.Workload("igw2d_g4_seg", 2, 1, 64, 128, 4, (5, 44), (3, 3), (2, 2), (1, 1), (1, 1), (1, 1),
+               True, True, wid=3309),
 ]
 
 

@@ -121,6 +121,7 @@ struct Igemm3dParams {
     int xcd_order;                   // 1: each XCD walks a contiguous range of a class's chunks
     int x_bytes;                     // bytes of x (wide variant: one buffer resource over it)
     int wseg;                        // wide variant: W segments of 16*NWB input positions per row
+    int G, Cig, Cog;                 // wide variant: groups and channels per group
     int wnf;                         // wide variant: float4s staged per input row and segment
     int cls_rows[kMaxClasses];
     int cls_rstep[kMaxClasses]; // output rows per step: 1, or 4 / taps for classes of 1 or 2 D x H taps
@@ -770,10 +771,10 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
 // ---------------------------------------------------------------- wide variant
 // Channel-heavy layers: the class's weights (C_in x C_out x taps) do not fit in
 // VGPRs, so they stream through LDS.  A workgroup of 4 waves owns 4 output
-// rows of one class and one block of COB = 16*MT output channels (wave w: row
-// w, the block's channels x NWB W-blocks, MT*NWB accumulator tiles per W
-// phase); blocks of one row run side by side (channel block fastest), so the
-// rows' inputs are read from L2 after the first.  The contraction runs over
+// rows of one class and one block of COB = 16*MT output channels of one group
+// (wave w: row w, the block's channels x NWB W-blocks, MT*NWB accumulator
+// tiles per W phase); blocks of one row run side by side (channel block
+// fastest), so the rows' inputs are read from L2 after the first.  The contraction runs over
 // stages (D/H tap slot x chunk of CC input channels, C_in/CC chunks); each
 // stage stages the weight chunk and the 4 rows' input rows, double-buffered.
 // The weights are staged as [kw][ci][j][m] for channel co = 16m + j of the
@@ -836,11 +837,13 @@ void k_igemm3d_wide(const Igemm3dParams P,
     const int j = lane & 15;
     const int g4 = lane >> 4;
 
-    // channel block fastest, then W segment (C_out is a multiple of COB, C_in of
-    // CC: checked on the host)
-    const int ncb = P.C_out / COB;
+    // channel block fastest, then W segment (C_out/G is a multiple of COB, C_in/G
+    // of CC: checked on the host)
+    const int cpg = P.Cog / COB; // channel blocks per group
+    const int ncb = P.G * cpg;
     const int rsb = (int)blockIdx.x / ncb;
     const int cb = (int)blockIdx.x - rsb * ncb;
+    const int grp = cb / cpg, cbg = cb - grp * cpg;
     const int rblk = rsb / P.wseg;
     const int seg = rsb - rblk * P.wseg;
     int cls = 0;
@@ -850,7 +853,7 @@ void k_igemm3d_wide(const Igemm3dParams P,
     if (nrows <= 0) return;
     const int td = P.cls_td[cls], th = P.cls_th[cls];
     const int nslots = td * th;
-    const int nch = P.C_in / CC; // input-channel chunks
+    const int nch = P.Cig / CC; // input-channel chunks of the group
     const int nstages = nslots * nch;
     const int pos0 = seg * 16 * NWB + P.iw_lo;     // input position at LDS offset 0
     // staged positions: the segment's P.wnf float4s (<= PWX/4, host) inside the row
@@ -875,7 +878,7 @@ void k_igemm3d_wide(const Igemm3dParams P,
     for (int u = 0; u < WPER; ++u) {
         const int pr = tid + u * NT;
         const int cil = pr / COB, co = pr - cil * COB;
-        wo4[u] = 4u * (unsigned)((cil * P.C_out + cb * COB + co) * KDHW);
+        wo4[u] = 4u * (unsigned)(((grp * P.Cig + cil) * P.Cog + cbg * COB + co) * KDHW);
         wlo[u] = cil * COB + MT * (co & 15) + (co >> 4);
     }
     int xo[XPER];  // input element offset of (row, ci in chunk, float4) at the row's (qd, qh)
@@ -890,11 +893,11 @@ void k_igemm3d_wide(const Igemm3dParams P,
         const int cil = rem / fdiv, c4 = rem - cil * nfs;
         const int pos = lo + 4 * c4;
         const RowPos R = pick_row(rr, R0, R1, R2, R3);
-        xo[u] = (((R.n * P.C_in + cil) * P.D_in + R.qd) * P.H_in + R.qh) * P.W_in + pos;
+        xo[u] = (((R.n * P.C_in + grp * P.Cig + cil) * P.D_in + R.qd) * P.H_in + R.qh) * P.W_in + pos;
         xlo[u] = in ? (rr * CC + cil) * PWX + pos - pos0 : -1;
         xrw[u] = in ? rr : 31;
     }
-    const rsrc_t rw_ = make_rsrc(w, 4 * P.C_in * P.C_out * KDHW);
+    const rsrc_t rw_ = make_rsrc(w, 4 * P.C_in * P.Cog * KDHW);
     const rsrc_t rx = make_rsrc(x, P.x_bytes);
 
     f4 wpre[WPER];
@@ -905,7 +908,7 @@ void k_igemm3d_wide(const Igemm3dParams P,
         const int jd = slot / th, jh = slot - jd * th;
         const int kd = P.cls_kd[cls][jd], kh = P.cls_kh[cls][jh];
         const int cd = P.cls_cd[cls][jd], chh = P.cls_ch[cls][jh];
-        const unsigned wst = 4u * (unsigned)(ch * CC * P.C_out * KDHW + (kd * P.KH + kh) * KW);
+        const unsigned wst = 4u * (unsigned)(ch * CC * P.Cog * KDHW + (kd * P.KH + kh) * KW);
 #pragma unroll
         for (int u = 0; u < WPER; ++u) {
             if constexpr (KW == 4) {
@@ -1010,7 +1013,7 @@ void k_igemm3d_wide(const Igemm3dParams P,
     for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int co = cb * COB + 16 * m + 4 * g4 + e;
+            const int co = grp * P.Cog + cbg * COB + 16 * m + 4 * g4 + e;
             const float bco = bias ? bias[co] : 0.0f;
 #pragma unroll
             for (int t = 0; t < NWB; ++t) {
@@ -1268,8 +1271,8 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
 
 // Streamed-weight shapes: kernel 3 or 4 along W with stride 2 on rows of any
 // length that is a multiple of 4 (one or two W-blocks per segment), output
-// channels in blocks of 64 (or of 32 when C_out is an odd multiple of 32); C_in
-// is any multiple of the chunk.
+// channels of a group in blocks of 64 (or of 32 when C_out/G is an odd multiple
+// of 32); C_in/G is any multiple of the chunk.
 struct WideVariant {
     int KW, NWB, MT;
 };
@@ -1313,14 +1316,14 @@ bool wide_layout(const convt_plan &P, int KW, int NWB, WideLayout &WL) {
 }
 
 int find_wide(const convt_plan &P, WideLayout *out) {
-    if (P.ndim < 2 || P.G != 1 || P.layout != CONVT_LAYOUT_CHANNELS_FIRST) return -1;
-    if (P.C_in % kWideCC != 0 || P.C_out % 32 != 0) return -1;
-    const int mt = P.C_out % 64 == 0 ? 4 : 2;
+    if (P.ndim < 2 || P.layout != CONVT_LAYOUT_CHANNELS_FIRST) return -1;
+    if (P.Cig % kWideCC != 0 || P.Cog % 32 != 0) return -1;
+    const int mt = P.Cog % 64 == 0 ? 4 : 2;
     const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
     // one buffer resource spans x, one the weights (31-bit byte offsets); per-sample y
     // as in the VGPR variant
     if (4 * P.N * P.C_in * P.in_sp >= INT32_MAX || 4 * P.C_out * P.out_sp >= INT32_MAX ||
-        4 * P.C_in * P.C_out * AD.K * AH.K * AW.K >= INT32_MAX)
+        4 * P.C_in * P.Cog * AD.K * AH.K * AW.K >= INT32_MAX)
         return -1;
     if (AW.L_in % 4 != 0) return -1; // staged float4s lie wholly inside or outside a row
     if (AD.s * AH.s > kMaxClasses) return -1;
@@ -1347,6 +1350,9 @@ int launch_wide(const convt_plan &Pl, const WideLayout &WL, const float *x, cons
     P.x_bytes = (int)(4 * Pl.N * Pl.C_in * Pl.in_sp);
     P.wseg = WL.nseg;
     P.wnf = WL.nf;
+    P.G = (int)Pl.G;
+    P.Cig = (int)Pl.Cig;
+    P.Cog = (int)Pl.Cog;
     const int64_t blocks = (int64_t)assign_blocks(P, 4) * WL.nseg * (Pl.C_out / (16 * MT));
     if (blocks == 0) return 0;
     if (blocks > INT32_MAX) return (int)hipErrorInvalidValue;
