@@ -552,8 +552,8 @@ def main():
                                 single_thread=other.name in (S.TINY_1D.name, S.LONG_1D.name, S.GROUPED_3D.name))
             configs[key] = rec
         if args.op == "forward":
-            # the channels-last layout of the long 1D and fused 3D layers
-            for other in (S.LONG_1D, S.FUSED_3D):
+            # the channels-last layout of the long 1D, fused 3D and channel-heavy 3D layers
+            for other in (S.LONG_1D, S.FUSED_3D, S.HEAVY_3D):
                 rec, _, _ = measure(other, args.op, args.steps, args.warmup, "auto", args.flushed, flusher,
                                     cpu=not args.no_cpu_baseline, layout="channels_last")
                 configs[CONFIG_KEYS[other.name] + "_channels_last"] = rec

@@ -289,6 +289,8 @@ def test_layout_selection():
     assert p.x_shape() == (16, 131072, 32) and p.y_shape() == (16, 262145, 64)
     q = T.plan_for(S.GROUPED_3D, "channels_last")
     assert "kernel=k_generic_nxc" in T.convt_plan_describe(q)
+    # the channel-heavy layer streams its weights in either layout
+    assert "kernel=k_igemm3d_wide" in T.convt_plan_describe(T.plan_for(S.HEAVY_3D, "channels_last"))
     assert T.lib().convt_plan_set_layout(q.handle, 2) == T.CONVT_ERR_INVALID_ARG
     assert T.lib().convt_plan_set_layout(None, 1) == T.CONVT_ERR_INVALID_ARG
     assert T.lib().convt_plan_get_layout(None) == -1

@@ -2,7 +2,7 @@
 add_input (N, L_out..., C_out)) through the C ABI against the oracle in the
 same layout, element by element: reduced shapes of every workload and the
 random and degenerate shapes on every path that takes them, every epilogue
-mode, full sizes of the long 1D and fused 3D layers, and the properties that
+mode, full sizes of the long 1D, fused 3D and channel-heavy 3D layers, and the properties that
 every output element is written and the inputs are left as they were.
 Inputs are the seeded channels-first draws with the channel axis moved last.
 Tolerance as the forward: |got - ref| <= 1e-4 + 1e-4 |ref|."""
@@ -124,19 +124,45 @@ def test_channels_last_3d_fast_kernel(wl):
     _check(wl, paths=["igemm3d"])
 
 
+# Shapes for the channels-last streamed-weight kernel: the channel-heavy
+# layer reduced, kernel 3 with 64 input channels, 32-channel blocks, groups,
+# rows in W segments with ragged ends, 2D.
+NDHWC_WIDE = [
+    reduced(S.HEAVY_3D, N=1, in_size=(3, 4, 32)),
+    S.Workload("ndhwc_w_k3_c64_fused", 3, 2, 64, 64, 1, (3, 5, 16), (3, 3, 3), (2, 2, 2), (1, 1, 1),
+               (1, 1, 1), (1, 1, 1), True, True, wid=5301),
+    S.Workload("ndhwc_w_co32_w12", 3, 1, 32, 32, 1, (2, 5, 12), (4, 4, 4), (2, 2, 2), (1, 1, 2),
+               (0, 1, 0), (1, 1, 1), True, False, wid=5302),
+    S.Workload("ndhwc_w_g2_co128", 3, 1, 64, 256, 2, (2, 3, 20), (4, 4, 4), (2, 2, 2), (1, 1, 1),
+               (0, 0, 0), (1, 1, 1), True, False, wid=5303),
+    S.Workload("ndhwc_w_seg_w44", 3, 1, 64, 64, 1, (2, 3, 44), (4, 4, 4), (2, 2, 2), (1, 1, 2),
+               (0, 0, 0), (1, 1, 1), False, True, wid=5304),
+    S.Workload("nhwc_w_seg_w100_co96", 2, 1, 48, 96, 1, (5, 100), (3, 3), (2, 2), (1, 2), (0, 1),
+               (1, 1), True, True, wid=5305),
+]
+
+
+@pytest.mark.parametrize("wl", NDHWC_WIDE, ids=lambda w: f"{w.name}-N{w.N}-in{'x'.join(map(str, w.in_size))}")
+def test_channels_last_wide_kernel(wl):
+    plan = T.plan_for(wl, "channels_last")
+    assert "kernel=k_igemm3d_wide" in T.convt_plan_describe(plan)
+    _check(wl, paths=["igemm3d"])
+
+
 MODES = [(add, act) for add in (False, True) for act in ("none", "hardswish", "x_hardswish")]
 
 
 @pytest.mark.parametrize("wl", [S.Workload("nlc_epi", 1, 2, 32, 64, 1, (20001,), (3,), (2,), (1,), (0,), (2,),
                                            True, False, wid=5101),
                                 reduced(S.FUSED_3D, N=1, in_size=(5, 7, 8)),
-                                reduced(S.GROUPED_3D, N=1, in_size=(4, 8, 16))],
+                                reduced(S.GROUPED_3D, N=1, in_size=(4, 8, 16)),
+                                reduced(S.HEAVY_3D, N=1, in_size=(2, 3, 12))],
                          ids=lambda w: w.name)
 def test_channels_last_epilogue_modes(wl):
     _check(wl, modes=MODES)
 
 
-@pytest.mark.parametrize("wl", [S.LONG_1D, S.FUSED_3D], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [S.LONG_1D, S.FUSED_3D, S.HEAVY_3D], ids=lambda w: w.name)
 def test_channels_last_full_size_every_element(wl):
     """Full size, the planner's channels-last path (the one the bench times),
     every element against the oracle's full forward."""

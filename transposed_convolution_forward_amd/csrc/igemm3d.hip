@@ -781,7 +781,11 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
 // block, so one 8- or 16-byte read gives a lane its MT A operands (W^T: 16 co
 // x 4 ci for m < MT); the K_W taps of one (ci, co, kd, kh) are contiguous in
 // the weight tensor and come in one 12- or 16-byte load.  Per (ci quad, kw):
-// 1 A read and NWB B reads feed MT*NWB MFMAs.  Rows longer than 16*NWB input
+// 1 A read and NWB B reads feed MT*NWB MFMAs.  Channels last (NDHWC, CL): a
+// staged input row is [position][channel] with a pitch of CC + 4 floats (one
+// 16-byte LDS store per 4-channel load; the 16 positions x 4 channels of a B
+// read fall on distinct banks), and a lane stores its 4 consecutive output
+// channels of a position as one float4.  Rows longer than 16*NWB input
 // positions split into W segments (a block each): a segment stages its input
 // positions plus the halo its taps reach; positions outside the row are never
 // staged and keep the zeros written at the start.  Staging offsets are fixed per thread for the
@@ -809,7 +813,7 @@ __device__ __forceinline__ RowPos pick_row(int q, const RowPos &A, const RowPos 
     return o;
 }
 
-template <int KW, int SW, int DW, int NWB, int MT, int CC, int PWX, int EPI>
+template <int KW, int SW, int DW, int NWB, int MT, int CC, int PWX, int EPI, bool CL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CONVT_IGW_WAVES_PER_EU)))
 void k_igemm3d_wide(const Igemm3dParams P,
                                                       const float *__restrict__ x,
@@ -827,9 +831,15 @@ void k_igemm3d_wide(const Igemm3dParams P,
     static_assert(MT == 2 || MT == 4, "one 8- or 16-byte LDS read gives the A operands");
     static_assert(KW == 3 || KW == 4, "one 12- or 16-byte weight load covers the W taps");
     typedef float amt __attribute__((ext_vector_type(MT)));
+    constexpr int XCP = CC + 4;                      // CL: floats per staged position
+    constexpr int XRS = CL ? PWX * XCP : CC * PWX;   // floats per staged row
+    constexpr int XCI = CL ? 4 : 4 * PWX;            // LDS step of 4 input channels
+    constexpr int XT = CL ? 16 * XCP : 16;           // LDS step of 16 positions
+    constexpr int XG = CL ? 1 : PWX;                 // LDS step of one input channel
+    constexpr int XP = CL ? XCP : 1;                 // LDS step of one position
 
     __shared__ __attribute__((aligned(16))) float Wl[2][KW][CC][COB];
-    __shared__ __attribute__((aligned(16))) float Xl[2][4][CC][PWX];
+    __shared__ __attribute__((aligned(16))) float Xl[2][4][XRS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -862,7 +872,7 @@ void k_igemm3d_wide(const Igemm3dParams P,
     const int fdiv = max(nfs, 1);
     const int xused = (4 * CC * nfs + NT - 1) / NT; // staging slots in use (uniform)
 
-    for (int i = tid; i < 2 * 4 * CC * PWX; i += NT) (&Xl[0][0][0][0])[i] = 0.0f;
+    for (int i = tid; i < 2 * 4 * XRS; i += NT) (&Xl[0][0][0])[i] = 0.0f;
 
     const RowPos R0 = decode_row(P, cls, r0);
     const RowPos R1 = decode_row(P, cls, r0 + min(1, nrows - 1));
@@ -881,7 +891,9 @@ void k_igemm3d_wide(const Igemm3dParams P,
         wo4[u] = 4u * (unsigned)(((grp * P.Cig + cil) * P.Cog + cbg * COB + co) * KDHW);
         wlo[u] = cil * COB + MT * (co & 15) + (co >> 4);
     }
-    int xo[XPER];  // input element offset of (row, ci in chunk, float4) at the row's (qd, qh)
+    // Each float4 holds 4 positions of one channel (channels first) or 4
+    // channels of one position (channels last); 4*CC*nfs of them per stage.
+    int xo[XPER];  // input element offset of the float4 at the row's (qd, qh), chunk 0
     int xlo[XPER]; // its LDS index, -1 past the staged float4s
     int xrw[XPER]; // its row; 31 past the staged float4s or outside the input row (loads zeros)
 #pragma unroll
@@ -890,11 +902,18 @@ void k_igemm3d_wide(const Igemm3dParams P,
         const bool in = f < 4 * CC * nfs;
         const int rr = in ? f / (CC * fdiv) : 3;
         const int rem = in ? f - rr * (CC * nfs) : 0;
-        const int cil = rem / fdiv, c4 = rem - cil * nfs;
-        const int pos = lo + 4 * c4;
         const RowPos R = pick_row(rr, R0, R1, R2, R3);
-        xo[u] = (((R.n * P.C_in + grp * P.Cig + cil) * P.D_in + R.qd) * P.H_in + R.qh) * P.W_in + pos;
-        xlo[u] = in ? (rr * CC + cil) * PWX + pos - pos0 : -1;
+        if constexpr (CL) {
+            const int pi = rem / (CC / 4), q = rem - pi * (CC / 4); // position, channel quad
+            const int pos = lo + pi;
+            xo[u] = (((R.n * P.D_in + R.qd) * P.H_in + R.qh) * P.W_in + pos) * P.C_in + grp * P.Cig + 4 * q;
+            xlo[u] = in ? rr * XRS + (pos - pos0) * XCP + 4 * q : -1;
+        } else {
+            const int cil = rem / fdiv, c4 = rem - cil * nfs;
+            const int pos = lo + 4 * c4;
+            xo[u] = (((R.n * P.C_in + grp * P.Cig + cil) * P.D_in + R.qd) * P.H_in + R.qh) * P.W_in + pos;
+            xlo[u] = in ? rr * XRS + cil * PWX + pos - pos0 : -1;
+        }
         xrw[u] = in ? rr : 31;
     }
     const rsrc_t rw_ = make_rsrc(w, 4 * P.C_in * P.Cog * KDHW);
@@ -926,7 +945,8 @@ void k_igemm3d_wide(const Igemm3dParams P,
             const int id = R.qd - cd, ih = R.qh - chh;
             if (q < nrows && id >= 0 && id < P.D_in && ih >= 0 && ih < P.H_in) bad &= ~(1u << q);
         }
-        const int xst = ch * CC * dhw - (cd * P.H_in + chh) * P.W_in;
+        const int xst = CL ? ch * CC - (cd * P.H_in + chh) * P.W_in * P.C_in
+                           : ch * CC * dhw - (cd * P.H_in + chh) * P.W_in;
 #pragma unroll
         for (int u = 0; u < XPER; ++u) {
             if (u < 2 || u < xused) {
@@ -945,7 +965,7 @@ void k_igemm3d_wide(const Igemm3dParams P,
         }
 #pragma unroll
         for (int u = 0; u < XPER; ++u)
-            if ((u < 2 || u < xused) && xlo[u] >= 0) *reinterpret_cast<f4 *>(&Xl[b][0][0][0] + xlo[u]) = xpre[u];
+            if ((u < 2 || u < xused) && xlo[u] >= 0) *reinterpret_cast<f4 *>(&Xl[b][0][0] + xlo[u]) = xpre[u];
     };
 
     f4 acc[MT][NPH][NWB];
@@ -978,7 +998,7 @@ void k_igemm3d_wide(const Igemm3dParams P,
             for (int rw = 0; rw < SW; ++rw)
 #pragma unroll
                 for (int c = 0; c < CM; ++c) {
-                    bb[rw][c] = (lds_ptr)(&Xl[b][wv][g4][0] + P.qw0[rw] + j - c - P.iw_lo);
+                    bb[rw][c] = (lds_ptr)(&Xl[b][wv][0] + g4 * XG + (P.qw0[rw] + j - c - P.iw_lo) * XP);
                     asm volatile("" : "+v"(bb[rw][c]));
                 }
 #pragma unroll
@@ -991,7 +1011,7 @@ void k_igemm3d_wide(const Igemm3dParams P,
                     const amt a = *(lds_aptr)(abase + (kw * CC + 4 * cig) * COB);
 #pragma unroll
                     for (int t = 0; t < NWB; ++t) {
-                        const float bv = bb[rw][c][4 * cig * PWX + 16 * t];
+                        const float bv = bb[rw][c][cig * XCI + t * XT];
 #pragma unroll
                         for (int m = 0; m < MT; ++m)
                             acc[m][ph][t] =
@@ -1006,6 +1026,39 @@ void k_igemm3d_wide(const Igemm3dParams P,
 
     if (!active) return;
     const RowPos R = pick_row(__builtin_amdgcn_readfirstlane(wv), R0, R1, R2, R3);
+    if constexpr (CL) {
+        // lane: 4 consecutive channels of a position, one float4 per (m, W-block, output)
+        const int64_t pbase = (((int64_t)R.n * P.D_out + R.od) * P.H_out + R.oh) * P.W_out;
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            const int co0 = grp * P.Cog + cbg * COB + 16 * m + 4 * g4;
+            float bco[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bco[e] = bias ? bias[co0 + e] : 0.0f;
+#pragma unroll
+            for (int t = 0; t < NWB; ++t) {
+                const int ow0 = SW * (16 * (NWB * seg + t) + j);
+#pragma unroll
+                for (int rr = 0; rr < SW; ++rr) {
+                    if (ow0 + rr >= P.W_out) continue;
+                    f4 v = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int rw = 0; rw < SW; ++rw)
+                        if constexpr (Ph::count() > 0)
+                            if (Ph::nonempty(rw))
+                                if (P.sigma[rw] == rr) v = acc[m][Ph::slot(rw)][t];
+                    const int64_t o = (pbase + ow0 + rr) * P.C_out + co0;
+                    f4 a4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
+                    if constexpr (epi_add(EPI)) a4 = load4u(add + o);
+                    f4 r;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) r[e] = epilogue<EPI>(v[e], bco[e], a4[e]);
+                    __builtin_memcpy(y + o, &r, 16); // 4-byte alignment suffices
+                }
+            }
+        }
+        return;
+    }
     const int64_t dhw_out = (int64_t)P.D_out * P.H_out * P.W_out;
     const int64_t row_base =
         (int64_t)R.n * P.C_out * dhw_out + ((int64_t)R.od * P.H_out + R.oh) * P.W_out;
@@ -1269,8 +1322,8 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
     return (int)hipGetLastError();
 }
 
-// Streamed-weight shapes: kernel 3 or 4 along W with stride 2 on rows of any
-// length that is a multiple of 4 (one or two W-blocks per segment), output
+// Streamed-weight shapes (either layout): kernel 3 or 4 along W with stride 2 on
+// rows of any length that is a multiple of 4 (one or two W-blocks per segment), output
 // channels of a group in blocks of 64 (or of 32 when C_out/G is an odd multiple
 // of 32); C_in/G is any multiple of the chunk.
 struct WideVariant {
@@ -1316,7 +1369,7 @@ bool wide_layout(const convt_plan &P, int KW, int NWB, WideLayout &WL) {
 }
 
 int find_wide(const convt_plan &P, WideLayout *out) {
-    if (P.ndim < 2 || P.layout != CONVT_LAYOUT_CHANNELS_FIRST) return -1;
+    if (P.ndim < 2) return -1;
     if (P.Cig % kWideCC != 0 || P.Cog % 32 != 0) return -1;
     const int mt = P.Cog % 64 == 0 ? 4 : 2;
     const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
@@ -1356,9 +1409,14 @@ int launch_wide(const convt_plan &Pl, const WideLayout &WL, const float *x, cons
     const int64_t blocks = (int64_t)assign_blocks(P, 4) * WL.nseg * (Pl.C_out / (16 * MT));
     if (blocks == 0) return 0;
     if (blocks > INT32_MAX) return (int)hipErrorInvalidValue;
+    const bool last = Pl.layout == CONVT_LAYOUT_CHANNELS_LAST;
     with_epi(add != nullptr, act, [&](auto E) {
-        hipLaunchKernelGGL((k_igemm3d_wide<KW, 2, 1, NWB, MT, kWideCC, kWidePWX, decltype(E)::value>),
-                           dim3((unsigned)blocks), dim3(256), 0, st, P, x, w, bias, add, y);
+        if (last)
+            hipLaunchKernelGGL((k_igemm3d_wide<KW, 2, 1, NWB, MT, kWideCC, kWidePWX, decltype(E)::value, true>),
+                               dim3((unsigned)blocks), dim3(256), 0, st, P, x, w, bias, add, y);
+        else
+            hipLaunchKernelGGL((k_igemm3d_wide<KW, 2, 1, NWB, MT, kWideCC, kWidePWX, decltype(E)::value, false>),
+                               dim3((unsigned)blocks), dim3(256), 0, st, P, x, w, bias, add, y);
     });
     return (int)hipGetLastError();
 }
