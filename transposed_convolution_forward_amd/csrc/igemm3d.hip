@@ -1027,34 +1027,45 @@ void k_igemm3d_wide(const Igemm3dParams P,
     if (!active) return;
     const RowPos R = pick_row(__builtin_amdgcn_readfirstlane(wv), R0, R1, R2, R3);
     if constexpr (CL) {
-        // lane: 4 consecutive channels of a position, one float4 per (m, W-block, output)
+        // lane: 4 consecutive channels of a position, one float4 per (m, W-block,
+        // output); a W-block wholly inside the row (a uniform test) stores without
+        // per-lane guards
         const int64_t pbase = (((int64_t)R.n * P.D_out + R.od) * P.H_out + R.oh) * P.W_out;
+        float bco[MT][4];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const int co0 = grp * P.Cog + cbg * COB + 16 * m + 4 * g4;
-            float bco[4];
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) bco[e] = bias ? bias[co0 + e] : 0.0f;
+            for (int e = 0; e < 4; ++e)
+                bco[m][e] = bias ? bias[grp * P.Cog + cbg * COB + 16 * m + 4 * g4 + e] : 0.0f;
+        auto put = [&](int t, int m, int rr, bool guard) {
+            const int ow0 = SW * (16 * (NWB * seg + t) + j);
+            if (guard && ow0 + rr >= P.W_out) return;
+            f4 v = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int t = 0; t < NWB; ++t) {
-                const int ow0 = SW * (16 * (NWB * seg + t) + j);
+            for (int rw = 0; rw < SW; ++rw)
+                if constexpr (Ph::count() > 0)
+                    if (Ph::nonempty(rw))
+                        if (P.sigma[rw] == rr) v = acc[m][Ph::slot(rw)][t];
+            const int64_t o = (pbase + ow0 + rr) * P.C_out + grp * P.Cog + cbg * COB + 16 * m + 4 * g4;
+            f4 a4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            if constexpr (epi_add(EPI)) a4 = load4u(add + o);
+            f4 r;
 #pragma unroll
-                for (int rr = 0; rr < SW; ++rr) {
-                    if (ow0 + rr >= P.W_out) continue;
-                    f4 v = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int e = 0; e < 4; ++e) r[e] = epilogue<EPI>(v[e], bco[m][e], a4[e]);
+            __builtin_memcpy(y + o, &r, 16); // 4-byte alignment suffices
+        };
 #pragma unroll
-                    for (int rw = 0; rw < SW; ++rw)
-                        if constexpr (Ph::count() > 0)
-                            if (Ph::nonempty(rw))
-                                if (P.sigma[rw] == rr) v = acc[m][Ph::slot(rw)][t];
-                    const int64_t o = (pbase + ow0 + rr) * P.C_out + co0;
-                    f4 a4 = f4{0.0f, 0.0f, 0.0f, 0.0f};
-                    if constexpr (epi_add(EPI)) a4 = load4u(add + o);
-                    f4 r;
+        for (int t = 0; t < NWB; ++t) {
+            if (SW * 16 * (NWB * seg + t + 1) <= P.W_out) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) r[e] = epilogue<EPI>(v[e], bco[e], a4[e]);
-                    __builtin_memcpy(y + o, &r, 16); // 4-byte alignment suffices
-                }
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int rr = 0; rr < SW; ++rr) put(t, m, rr, false);
+            } else {
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int rr = 0; rr < SW; ++rr) put(t, m, rr, true);
             }
         }
         return;
@@ -1062,6 +1073,49 @@ void k_igemm3d_wide(const Igemm3dParams P,
     const int64_t dhw_out = (int64_t)P.D_out * P.H_out * P.W_out;
     const int64_t row_base =
         (int64_t)R.n * P.C_out * dhw_out + ((int64_t)R.od * P.H_out + R.oh) * P.W_out;
+    if constexpr (SW == 2 && Ph::count() == 2) {
+        // a lane's two outputs of a channel are adjacent: one 8-byte store; W
+        // phase 0 lands on the odd outputs when sigma(0) = 1.  A W-block wholly
+        // inside the row (a uniform test) stores without per-lane guards.
+        const bool swp = P.sigma[0] != 0;
+        float bco[MT][4];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                bco[m][e] = bias ? bias[grp * P.Cog + cbg * COB + 16 * m + 4 * g4 + e] : 0.0f;
+        auto put = [&](int t, int m, int e, bool guard) {
+            const int co = grp * P.Cog + cbg * COB + 16 * m + 4 * g4 + e;
+            const int ow0 = 2 * (16 * (NWB * seg + t) + j);
+            const float a0 = acc[m][Ph::slot(0)][t][e], a1 = acc[m][Ph::slot(1)][t][e];
+            const float v0 = swp ? a1 : a0, v1 = swp ? a0 : a1;
+            const int64_t o = row_base + (int64_t)co * dhw_out + ow0;
+            if (!guard || ow0 + 1 < P.W_out) {
+                float ad[2] = {0.0f, 0.0f};
+                if constexpr (epi_add(EPI)) __builtin_memcpy(ad, add + o, 8);
+                const float r[2] = {epilogue<EPI>(v0, bco[m][e], ad[0]), epilogue<EPI>(v1, bco[m][e], ad[1])};
+                __builtin_memcpy(y + o, r, 8); // 4-byte alignment suffices
+            } else if (ow0 < P.W_out) {
+                const float ad = epi_add(EPI) ? add[o] : 0.0f;
+                y[o] = epilogue<EPI>(v0, bco[m][e], ad);
+            }
+        };
+#pragma unroll
+        for (int t = 0; t < NWB; ++t) {
+            if (32 * (NWB * seg + t + 1) <= P.W_out) {
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) put(t, m, e, false);
+            } else {
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) put(t, m, e, true);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
