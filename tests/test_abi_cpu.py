@@ -171,6 +171,11 @@ def test_workload_plans_and_paths():
             pw = T.Plan(3, 2, cin, cout, 1, (8, 8, w_in), (k,) * 3, (s_dh, s_dh, 2), (1, 1, 1),
                         (1, 1, 1) if k == 3 and s_dh == 2 else (0, 0, 0), (1, 1, 1))
             assert "kernel=k_igemm3d_wide" in T.convt_plan_describe(pw), (cin, cout, k, s_dh, w_in)
+    # kernel 3 with stride 1 along W (one W phase, taps at shifts 0..2)
+    for cin, cout in ((64, 64), (32, 32), (128, 64)):
+        for w_in in (12, 32, 100):
+            ps = T.Plan(3, 2, cin, cout, 1, (8, 8, w_in), (3, 3, 3), (2, 2, 1), (1, 1, 1), (1, 1, 0), (1, 1, 1))
+            assert "kernel=k_igemm3d_wide" in T.convt_plan_describe(ps), (cin, cout, w_in)
     # groups whose channel counts fit (16k inputs, 32k outputs per group) too
     for cin, cout, g in ((64, 64, 2), (64, 256, 2), (64, 128, 4)):
         pg = T.Plan(3, 2, cin, cout, g, (8, 8, 16), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), (1, 1, 1))

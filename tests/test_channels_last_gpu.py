@@ -139,6 +139,8 @@ NDHWC_WIDE = [
                (0, 0, 0), (1, 1, 1), False, True, wid=5304),
     S.Workload("nhwc_w_seg_w100_co96", 2, 1, 48, 96, 1, (5, 100), (3, 3), (2, 2), (1, 2), (0, 1),
                (1, 1), True, True, wid=5305),
+    S.Workload("ndhwc_w_s1w_fused", 3, 1, 64, 64, 1, (2, 3, 24), (3, 3, 3), (2, 1, 1), (1, 1, 1),
+               (1, 0, 0), (1, 1, 1), True, True, wid=5306),
 ]
 
 

@@ -114,6 +114,12 @@ REDUCED = [
                (1, 1, 1), (1, 1, 1), True, True, wid=3216),
     S.Workload("igw_g2_co128_k4", 3, 1, 64, 256, 2, (2, 3, 20), (4, 4, 4), (2, 2, 2), (1, 1, 1),
                (0, 0, 0), (1, 1, 1), True, False, wid=3217),
+    # stride 1 along W with kernel 3 (taps at shifts 0..2): two W-blocks, a
+    # ragged one-block row with 3 D taps per class
+    S.Workload("igw_s1w_k3_fused", 3, 2, 64, 64, 1, (3, 4, 20), (3, 3, 3), (2, 2, 1), (1, 1, 1),
+               (1, 1, 0), (1, 1, 1), True, True, wid=3218),
+    S.Workload("igw_s1w_p0_co64", 3, 1, 32, 64, 1, (2, 3, 12), (3, 3, 3), (1, 2, 1), (0, 0, 0),
+               (0, 0, 0), (1, 1, 1), True, False, wid=3219),
     # rows longer than 32 inputs in W segments of 32 (halo staged per
     # segment): two segments with a ragged last one
     S.Workload("igw_seg_w44_k4", 3, 1, 64, 64, 1, (2, 3, 44), (4, 4, 4), (2, 2, 2), (1, 1, 2),
@@ -180,6 +186,8 @@ REDUCED = [
                False, False, wid=3308),
     S.Workload("igw2d_g4_seg", 2, 1, 64, 128, 4, (5, 44), (3, 3), (2, 2), (1, 1), (1, 1), (1, 1),
                True, True, wid=3309),
+    S.Workload("igw2d_s1w_seg_co32", 2, 1, 32, 32, 1, (6, 52), (3, 3), (1, 1), (1, 1), (0, 0), (1, 1),
+               True, False, wid=3310),
 ]
 
 

@@ -1376,16 +1376,18 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
     return (int)hipGetLastError();
 }
 
-// Streamed-weight shapes (either layout): kernel 3 or 4 along W with stride 2 on
-// rows of any length that is a multiple of 4 (one or two W-blocks per segment), output
+// Streamed-weight shapes (either layout): kernel 3 or 4 along W with stride 2, or
+// kernel 3 with stride 1, on rows of any length that is a multiple of 4 (one or
+// two W-blocks per segment), output
 // channels of a group in blocks of 64 (or of 32 when C_out/G is an odd multiple
 // of 32); C_in/G is any multiple of the chunk.
 struct WideVariant {
-    int KW, NWB, MT;
+    int KW, SW, NWB, MT;
 };
 constexpr WideVariant kWide[] = {
-    {4, 2, 4}, {4, 1, 4}, {3, 2, 4}, {3, 1, 4}, // kernel 4 (the channel-heavy layer) or 3
-    {4, 2, 2}, {4, 1, 2}, {3, 2, 2}, {3, 1, 2}, // 32-channel blocks
+    {4, 2, 2, 4}, {4, 2, 1, 4}, {3, 2, 2, 4}, {3, 2, 1, 4}, // kernel 4 (the channel-heavy layer) or 3
+    {4, 2, 2, 2}, {4, 2, 1, 2}, {3, 2, 2, 2}, {3, 2, 1, 2}, // 32-channel blocks
+    {3, 1, 2, 4}, {3, 1, 1, 4}, {3, 1, 2, 2}, {3, 1, 1, 2}, // kernel 3, stride 1
 };
 constexpr int kNumWide = (int)(sizeof(kWide) / sizeof(kWide[0]));
 constexpr int kWideCC = 16; // input channels per stage
@@ -1400,8 +1402,8 @@ struct WideLayout {
 // W layout of the wide variant: two W-blocks per segment when the row has more
 // than 16*S_W outputs, enough segments to cover the row, and the staged input
 // positions of a segment (its 16*NWB positions plus the halo of the taps).
-bool wide_layout(const convt_plan &P, int KW, int NWB, WideLayout &WL) {
-    constexpr int SW = 2, DW = 1;
+bool wide_layout(const convt_plan &P, int KW, int SW, int NWB, WideLayout &WL) {
+    constexpr int DW = 1;
     const AxisPlan &A = P.ax[2];
     if (A.K != KW || A.s != SW || A.d != DW) return false;
     Layout &L = WL.L;
@@ -1442,18 +1444,18 @@ int find_wide(const convt_plan &P, WideLayout *out) {
         const WideVariant &v = kWide[i];
         if (v.MT != mt) continue;
         WideLayout WL;
-        if (!wide_layout(P, v.KW, v.NWB, WL)) continue;
+        if (!wide_layout(P, v.KW, v.SW, v.NWB, WL)) continue;
         if (out) *out = WL;
         return i;
     }
     return -1;
 }
 
-template <int KW, int NWB, int MT>
+template <int KW, int SW, int NWB, int MT>
 int launch_wide(const convt_plan &Pl, const WideLayout &WL, const float *x, const float *w,
                 const float *bias, const float *add, int act, float *y, hipStream_t st) {
     Igemm3dParams P;
-    fill_params(Pl, WL.L, 2, P);
+    fill_params(Pl, WL.L, SW, P);
     P.x_bytes = (int)(4 * Pl.N * Pl.C_in * Pl.in_sp);
     P.wseg = WL.nseg;
     P.wnf = WL.nf;
@@ -1466,10 +1468,10 @@ int launch_wide(const convt_plan &Pl, const WideLayout &WL, const float *x, cons
     const bool last = Pl.layout == CONVT_LAYOUT_CHANNELS_LAST;
     with_epi(add != nullptr, act, [&](auto E) {
         if (last)
-            hipLaunchKernelGGL((k_igemm3d_wide<KW, 2, 1, NWB, MT, kWideCC, kWidePWX, decltype(E)::value, true>),
+            hipLaunchKernelGGL((k_igemm3d_wide<KW, SW, 1, NWB, MT, kWideCC, kWidePWX, decltype(E)::value, true>),
                                dim3((unsigned)blocks), dim3(256), 0, st, P, x, w, bias, add, y);
         else
-            hipLaunchKernelGGL((k_igemm3d_wide<KW, 2, 1, NWB, MT, kWideCC, kWidePWX, decltype(E)::value, false>),
+            hipLaunchKernelGGL((k_igemm3d_wide<KW, SW, 1, NWB, MT, kWideCC, kWidePWX, decltype(E)::value, false>),
                                dim3((unsigned)blocks), dim3(256), 0, st, P, x, w, bias, add, y);
     });
     return (int)hipGetLastError();
@@ -1503,14 +1505,18 @@ int launch_igemm3d(const convt_plan &Pl, const float *x, const float *w, const f
     }
     WideLayout WL;
     switch (find_wide(Pl, &WL)) {
-    case 0: return launch_wide<4, 2, 4>(Pl, WL, x, w, bias, add, act, y, st);
-    case 1: return launch_wide<4, 1, 4>(Pl, WL, x, w, bias, add, act, y, st);
-    case 2: return launch_wide<3, 2, 4>(Pl, WL, x, w, bias, add, act, y, st);
-    case 3: return launch_wide<3, 1, 4>(Pl, WL, x, w, bias, add, act, y, st);
-    case 4: return launch_wide<4, 2, 2>(Pl, WL, x, w, bias, add, act, y, st);
-    case 5: return launch_wide<4, 1, 2>(Pl, WL, x, w, bias, add, act, y, st);
-    case 6: return launch_wide<3, 2, 2>(Pl, WL, x, w, bias, add, act, y, st);
-    case 7: return launch_wide<3, 1, 2>(Pl, WL, x, w, bias, add, act, y, st);
+    case 0: return launch_wide<4, 2, 2, 4>(Pl, WL, x, w, bias, add, act, y, st);
+    case 1: return launch_wide<4, 2, 1, 4>(Pl, WL, x, w, bias, add, act, y, st);
+    case 2: return launch_wide<3, 2, 2, 4>(Pl, WL, x, w, bias, add, act, y, st);
+    case 3: return launch_wide<3, 2, 1, 4>(Pl, WL, x, w, bias, add, act, y, st);
+    case 4: return launch_wide<4, 2, 2, 2>(Pl, WL, x, w, bias, add, act, y, st);
+    case 5: return launch_wide<4, 2, 1, 2>(Pl, WL, x, w, bias, add, act, y, st);
+    case 6: return launch_wide<3, 2, 2, 2>(Pl, WL, x, w, bias, add, act, y, st);
+    case 7: return launch_wide<3, 2, 1, 2>(Pl, WL, x, w, bias, add, act, y, st);
+    case 8: return launch_wide<3, 1, 2, 4>(Pl, WL, x, w, bias, add, act, y, st);
+    case 9: return launch_wide<3, 1, 1, 4>(Pl, WL, x, w, bias, add, act, y, st);
+    case 10: return launch_wide<3, 1, 2, 2>(Pl, WL, x, w, bias, add, act, y, st);
+    case 11: return launch_wide<3, 1, 1, 2>(Pl, WL, x, w, bias, add, act, y, st);
     default: return (int)hipErrorInvalidValue;
     }
 }
