@@ -70,7 +70,7 @@ typedef enum {
     CONVT_PATH_AUTO = 0,     /* let the planner choose (the default) */
     CONVT_PATH_GENERIC = 1,  /* output-stationary phase-table gather, any shape */
     CONVT_PATH_STREAM1D = 2, /* 1D streaming kernel, MFMA channel contraction */
-    CONVT_PATH_IGEMM3D = 3   /* per-phase implicit GEMM on MFMA for 3D */
+    CONVT_PATH_IGEMM3D = 3   /* per-phase implicit GEMM on MFMA for 2D and 3D */
 } convt_path;
 
 /*
