@@ -176,14 +176,19 @@ def test_workload_plans_and_paths():
         for w_in in (12, 32, 100):
             ps = T.Plan(3, 2, cin, cout, 1, (8, 8, w_in), (3, 3, 3), (2, 2, 1), (1, 1, 1), (1, 1, 0), (1, 1, 1))
             assert "kernel=k_igemm3d_wide" in T.convt_plan_describe(ps), (cin, cout, w_in)
+    # 16-channel output blocks with 64 or more input channels; below that the
+    # generic kernels
+    for cin, cout, wide in ((64, 16, True), (64, 48, True), (128, 80, True), (32, 48, False), (16, 16, False)):
+        pc = T.Plan(3, 2, cin, cout, 1, (8, 8, 16), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), (1, 1, 1))
+        assert ("kernel=k_igemm3d_wide" in T.convt_plan_describe(pc)) == wide, (cin, cout)
     # groups whose channel counts fit (16k inputs, 32k outputs per group) too
     for cin, cout, g in ((64, 64, 2), (64, 256, 2), (64, 128, 4)):
         pg = T.Plan(3, 2, cin, cout, g, (8, 8, 16), (3, 3, 3), (2, 2, 2), (1, 1, 1), (1, 1, 1), (1, 1, 1))
         assert "kernel=k_igemm3d_wide" in T.convt_plan_describe(pg), (cin, cout, g)
     # rows whose length is not a multiple of 4, output channels not in blocks
-    # of 32, input channels not in chunks of 16, more than 4 taps per class on
+    # of 16, input channels not in chunks of 16, more than 4 taps per class on
     # D do not
-    for a in (((8, 8, 50), 64, 64, (3, 3, 3), (2, 2, 2)), ((8, 8, 16), 64, 48, (3, 3, 3), (2, 2, 2)),
+    for a in (((8, 8, 50), 64, 64, (3, 3, 3), (2, 2, 2)), ((8, 8, 16), 64, 40, (3, 3, 3), (2, 2, 2)),
               ((8, 8, 16), 24, 64, (3, 3, 3), (2, 2, 2)), ((8, 8, 16), 64, 64, (5, 3, 3), (1, 2, 2))):
         ins, cin, cout, k, st = a
         text = T.convt_plan_describe(T.Plan(3, 2, cin, cout, 1, ins, k, st, (1, 1, 1), (0, 1, 1), (1, 1, 1)))

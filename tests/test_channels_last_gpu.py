@@ -141,6 +141,8 @@ NDHWC_WIDE = [
                (1, 1), True, True, wid=5305),
     S.Workload("ndhwc_w_s1w_fused", 3, 1, 64, 64, 1, (2, 3, 24), (3, 3, 3), (2, 1, 1), (1, 1, 1),
                (1, 0, 0), (1, 1, 1), True, True, wid=5306),
+    S.Workload("ndhwc_w_co48", 3, 1, 64, 48, 1, (2, 3, 44), (3, 3, 3), (2, 2, 2), (1, 1, 1),
+               (1, 1, 1), (1, 1, 1), True, True, wid=5307),
 ]
 
 

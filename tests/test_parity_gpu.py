@@ -120,6 +120,14 @@ REDUCED = [
                (1, 1, 0), (1, 1, 1), True, True, wid=3218),
     S.Workload("igw_s1w_p0_co64", 3, 1, 32, 64, 1, (2, 3, 12), (3, 3, 3), (1, 2, 1), (0, 0, 0),
                (0, 0, 0), (1, 1, 1), True, False, wid=3219),
+    # output channels in blocks of 16 (64 -> 16 on the fused geometry, 64 -> 48
+    # in three blocks with kernel 4, stride 1 with 2 groups of 64 -> 16)
+    S.Workload("igw_co16_fused", 3, 2, 64, 16, 1, (3, 4, 16), (3, 3, 3), (2, 2, 2), (1, 1, 1),
+               (1, 1, 1), (1, 1, 1), True, True, wid=3220),
+    S.Workload("igw_co48_k4_w24", 3, 1, 64, 48, 1, (2, 3, 24), (4, 4, 4), (2, 2, 2), (1, 1, 1),
+               (0, 0, 0), (1, 1, 1), True, False, wid=3221),
+    S.Workload("igw_co16_g2_s1w", 3, 1, 128, 32, 2, (2, 3, 36), (3, 3, 3), (2, 1, 1), (1, 1, 1),
+               (1, 0, 0), (1, 1, 1), False, True, wid=3222),
     # rows longer than 32 inputs in W segments of 32 (halo staged per
     # segment): two segments with a ragged last one
     S.Workload("igw_seg_w44_k4", 3, 1, 64, 64, 1, (2, 3, 44), (4, 4, 4), (2, 2, 2), (1, 1, 2),

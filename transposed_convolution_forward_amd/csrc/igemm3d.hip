@@ -797,6 +797,16 @@ __attribute__((amdgpu_waves_per_eu(CONVT_IG_WAVES_PER_EU))) void k_igemm3d(const
 #define CONVT_IGW_WAVES_PER_EU 2
 #endif
 
+// A operands of a lane: MT floats, read from LDS in one access.
+template <int MT> struct AVec {
+    typedef float t __attribute__((ext_vector_type(MT)));
+};
+template <> struct AVec<1> {
+    typedef float t;
+};
+template <typename V> __device__ __forceinline__ float aget(const V &a, int m) { return a[m]; }
+__device__ __forceinline__ float aget(float a, int) { return a; }
+
 // Row q (0..3) of four held in separate variables, by selects (an array
 // indexed with a per-lane value would live in scratch memory).
 __device__ __forceinline__ int sel4(int q, int a, int b, int c, int d) {
@@ -828,9 +838,9 @@ void k_igemm3d_wide(const Igemm3dParams P,
     constexpr int WPER = WPAIRS / NT;      // per thread
     constexpr int XPER = (4 * CC * (PWX / 4) + NT - 1) / NT; // input rows: 4 rows x CC x NF float4s
     static_assert(CC % 4 == 0 && WPAIRS % NT == 0, "chunking");
-    static_assert(MT == 2 || MT == 4, "one 8- or 16-byte LDS read gives the A operands");
+    static_assert(MT == 1 || MT == 2 || MT == 4, "one 4-, 8- or 16-byte LDS read gives the A operands");
     static_assert(KW == 3 || KW == 4, "one 12- or 16-byte weight load covers the W taps");
-    typedef float amt __attribute__((ext_vector_type(MT)));
+    typedef typename AVec<MT>::t amt;
     constexpr int XCP = CC + 4;                      // CL: floats per staged position
     constexpr int XRS = CL ? PWX * XCP : CC * PWX;   // floats per staged row
     constexpr int XCI = CL ? 4 : 4 * PWX;            // LDS step of 4 input channels
@@ -1015,7 +1025,7 @@ void k_igemm3d_wide(const Igemm3dParams P,
 #pragma unroll
                         for (int m = 0; m < MT; ++m)
                             acc[m][ph][t] =
-                                __builtin_amdgcn_mfma_f32_16x16x4f32(a[m], bv, acc[m][ph][t], 0, 0, 0);
+                                __builtin_amdgcn_mfma_f32_16x16x4f32(aget(a, m), bv, acc[m][ph][t], 0, 0, 0);
                     }
                 }
             }
@@ -1379,8 +1389,8 @@ int launch_variant(const convt_plan &Pl, const Layout &L, const float *x, const 
 // Streamed-weight shapes (either layout): kernel 3 or 4 along W with stride 2, or
 // kernel 3 with stride 1, on rows of any length that is a multiple of 4 (one or
 // two W-blocks per segment), output
-// channels of a group in blocks of 64 (or of 32 when C_out/G is an odd multiple
-// of 32); C_in/G is any multiple of the chunk.
+// channels of a group in blocks of 64, 32 or 16 (the largest that divides
+// C_out/G; 16 only with C_in/G >= 64); C_in/G is any multiple of the chunk.
 struct WideVariant {
     int KW, SW, NWB, MT;
 };
@@ -1388,6 +1398,8 @@ constexpr WideVariant kWide[] = {
     {4, 2, 2, 4}, {4, 2, 1, 4}, {3, 2, 2, 4}, {3, 2, 1, 4}, // kernel 4 (the channel-heavy layer) or 3
     {4, 2, 2, 2}, {4, 2, 1, 2}, {3, 2, 2, 2}, {3, 2, 1, 2}, // 32-channel blocks
     {3, 1, 2, 4}, {3, 1, 1, 4}, {3, 1, 2, 2}, {3, 1, 1, 2}, // kernel 3, stride 1
+    {4, 2, 2, 1}, {4, 2, 1, 1}, {3, 2, 2, 1}, {3, 2, 1, 1}, // 16-channel blocks
+    {3, 1, 2, 1}, {3, 1, 1, 1},
 };
 constexpr int kNumWide = (int)(sizeof(kWide) / sizeof(kWide[0]));
 constexpr int kWideCC = 16; // input channels per stage
@@ -1426,8 +1438,11 @@ bool wide_layout(const convt_plan &P, int KW, int SW, int NWB, WideLayout &WL) {
 
 int find_wide(const convt_plan &P, WideLayout *out) {
     if (P.ndim < 2) return -1;
-    if (P.Cig % kWideCC != 0 || P.Cog % 32 != 0) return -1;
-    const int mt = P.Cog % 64 == 0 ? 4 : 2;
+    if (P.Cig % kWideCC != 0 || P.Cog % 16 != 0) return -1;
+    const int mt = P.Cog % 64 == 0 ? 4 : P.Cog % 32 == 0 ? 2 : 1;
+    // 16-channel blocks pay the staging of 16 input channels per 8 MFMAs of a
+    // W-block: ahead of the generic kernels only with 64 or more input channels
+    if (mt == 1 && P.Cig < 64) return -1;
     const AxisPlan &AD = P.ax[0], &AH = P.ax[1], &AW = P.ax[2];
     // one buffer resource spans x, one the weights (31-bit byte offsets); per-sample y
     // as in the VGPR variant
@@ -1517,6 +1532,12 @@ int launch_igemm3d(const convt_plan &Pl, const float *x, const float *w, const f
     case 9: return launch_wide<3, 1, 1, 4>(Pl, WL, x, w, bias, add, act, y, st);
     case 10: return launch_wide<3, 1, 2, 2>(Pl, WL, x, w, bias, add, act, y, st);
     case 11: return launch_wide<3, 1, 1, 2>(Pl, WL, x, w, bias, add, act, y, st);
+    case 12: return launch_wide<4, 2, 2, 1>(Pl, WL, x, w, bias, add, act, y, st);
+    case 13: return launch_wide<4, 2, 1, 1>(Pl, WL, x, w, bias, add, act, y, st);
+    case 14: return launch_wide<3, 2, 2, 1>(Pl, WL, x, w, bias, add, act, y, st);
+    case 15: return launch_wide<3, 2, 1, 1>(Pl, WL, x, w, bias, add, act, y, st);
+    case 16: return launch_wide<3, 1, 2, 1>(Pl, WL, x, w, bias, add, act, y, st);
+    case 17: return launch_wide<3, 1, 1, 1>(Pl, WL, x, w, bias, add, act, y, st);
     default: return (int)hipErrorInvalidValue;
     }
 }
